@@ -1,0 +1,156 @@
+/*
+ * va_varlen.h -- exact scaled-dot-product attention over packed variable-length
+ * sequences on AMD Instinct MI355X (gfx950).  Plain C ABI: no C++ or PyTorch
+ * types cross it, so a caller needs neither libtorch nor a matching compiler.
+ *
+ * What is computed.  Sequences are concatenated into one token stream; the
+ * boundaries of sequence b are rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of
+ * Q (and of O) and rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of K and V
+ * (the FlashAttention-2 varlen layout on the TorchEasyRec pull request 663
+ * page: one packed stream with explicit cumulative boundaries).  For every
+ * sequence b, query head h and KV head g = h / (num_heads_q / num_heads_kv)
+ * (contiguous GQA/MQA groups):
+ *
+ *     S   = softmax_scale * Q_bh K_bg^T + Bias_bh
+ *     S[i][j] = -inf   if causal and j > i + (Lk_b - Lq_b)    (bottom-right)
+ *     O_bh = softmax(S) V_bg,    LSE_bh[i] = ln sum_j exp(S[i][j])
+ *
+ * A query row that sees no key (causal with Lq_b > Lk_b, or Lk_b = 0) gets
+ * O = 0 and LSE = -inf.  With Lq_b = 1 causal equals non-causal, as the FDMA
+ * pull request 118 page notes for single-token decode (section "Key
+ * Implementation Points").  No dropout (that page assumes dropout 0).
+ *
+ * Layouts (all row-major, contiguous, element strides implied):
+ *   q, out, dout, dq    [total_q, num_heads_q, head_dim]
+ *   k, v, dk, dv        [total_k, num_heads_kv, head_dim]
+ *   lse                 [num_heads_q, total_q]  float32, natural log
+ *   cu_seqlens_q/_k     [batch + 1] int32, device memory, cu[0] = 0,
+ *                       non-decreasing, cu[batch] = total_q / total_k
+ *   bias                optional; element (b, h, r, c) -- r, c local to the
+ *                       sequence -- at bias[b*s0 + h*s1 + r*s2 + c*s3], with
+ *                       bias_stride = {s0, s1, s2, s3} a HOST int64[4] of
+ *                       element strides >= 0.  A per-key bias is s2 = 0; a
+ *                       head-shared bias is s1 = 0; any permuted view is just
+ *                       other strides.  This is the strided per-sequence view of
+ *                       the GiGL pull request 858 page (section "Approach": the
+ *                       bias of sequence i sits at i * stride(0)).  The bias has
+ *                       the input dtype, is added after scaling, and only
+ *                       elements with r < Lq_b and c < Lk_b are ever read.
+ *
+ * Ownership and synchronisation.  The caller allocates every buffer, inputs,
+ * outputs and workspace, in device memory (except bias_stride, on the host).
+ * The library allocates nothing per call, frees nothing, never reads device
+ * memory on the host and never synchronises: each call only enqueues kernels
+ * on `stream` and returns (the per-step host sync the TorchEasyRec page's
+ * review flags is avoided by construction).  Outputs are fully overwritten
+ * (zeros for empty rows); they are valid for later work on `stream`.
+ *
+ * Errors.  A non-VA_OK return means nothing was enqueued; va_last_error()
+ * then holds a message for the calling thread.  Invalid device metadata
+ * (cu_seqlens not monotone, cu[batch] != total, a length above max_seqlen)
+ * is not detected: results are then unspecified, but every index is clamped
+ * so no access leaves the buffers the other arguments describe.
+ */
+#ifndef VA_VARLEN_H
+#define VA_VARLEN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VA_OK = 0,
+  VA_ERR_INVALID = 1,     /* null pointer, zero/negative size, Hq % Hkv != 0, bad stride */
+  VA_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, unknown dtype, bf16 grads of fp32 inputs */
+  VA_ERR_WORKSPACE = 3,   /* workspace smaller than va_varlen_bwd_workspace_size() */
+  VA_ERR_HIP = 4          /* the HIP runtime reported an error; text in va_last_error() */
+} va_status;
+
+typedef enum {
+  VA_F32 = 0,  /* IEEE float32; products and sums in float32 (no reduced-precision shortcut) */
+  VA_BF16 = 1  /* bfloat16 storage; matrix products on bf16 MFMA with float32 accumulation */
+} va_dtype;
+
+/* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
+typedef void* va_stream;
+
+/*
+ * Forward.  Writes out [total_q, num_heads_q, head_dim] in `dtype` and lse
+ * [num_heads_q, total_q] in float32.
+ *   q, k, v            device, `dtype`, layouts above
+ *   cu_seqlens_q/_k    device int32 [batch + 1]
+ *   max_seqlen_q/_k    host upper bounds on Lq_b / Lk_b (>= 1); they size the
+ *                      tile schedule, never the results
+ *   softmax_scale      multiplies Q K^T (callers usually pass 1/sqrt(head_dim))
+ *   causal             0 or 1; 1 = bottom-right aligned causal mask
+ *   bias, bias_stride  both NULL (no bias) or both non-NULL
+ *   head_dim           64 or 128
+ * Returns VA_ERR_INVALID for a NULL required pointer, exactly one of
+ * bias/bias_stride NULL, batch/total/heads/head_dim <= 0, Hq % Hkv != 0,
+ * max_seqlen <= 0, a negative stride; VA_ERR_UNSUPPORTED for head_dim not in
+ * {64, 128} or an unknown dtype; VA_ERR_HIP if the launch fails.
+ */
+va_status va_varlen_fwd(const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int32_t max_seqlen_q, int32_t max_seqlen_k,
+                        float softmax_scale, int causal,
+                        const void* bias, const int64_t* bias_stride,
+                        void* out, float* lse,
+                        int32_t batch, int32_t total_q, int32_t total_k,
+                        int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                        va_dtype dtype, va_stream stream);
+
+/*
+ * Bytes of device workspace va_varlen_bwd needs for these sizes (256-byte
+ * aligned pointer required).  Returns 0 for arguments va_varlen_bwd would
+ * reject.  Pure host arithmetic.
+ */
+size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t total_k,
+                                    int32_t num_heads_q, int32_t num_heads_kv,
+                                    int32_t head_dim, va_dtype dtype, va_dtype grad_dtype);
+
+/*
+ * Backward: dq, dk, dv of sum(dout * out) for the forward above, recomputing
+ * the softmax from `lse` (the forward's own output) instead of storing it.
+ * The bias, if given, is treated as a constant (no bias gradient).
+ *   dout, out          device, `dtype`, [total_q, num_heads_q, head_dim]
+ *   lse                device float32 [num_heads_q, total_q] from va_varlen_fwd
+ *   dq                 [total_q, num_heads_q, head_dim] in grad_dtype
+ *   dk, dv             [total_k, num_heads_kv, head_dim] in grad_dtype; the
+ *                      query heads of a GQA group are summed
+ *   workspace          device scratch of at least va_varlen_bwd_workspace_size()
+ *                      bytes, 256-byte aligned; contents need no initialisation
+ *   grad_dtype         VA_F32, or VA_BF16 when dtype is VA_BF16
+ * Deterministic: a call's results do not depend on scheduling (no atomics on
+ * values).  Errors as for the forward, plus VA_ERR_WORKSPACE, and
+ * VA_ERR_UNSUPPORTED for grad_dtype = VA_BF16 with dtype = VA_F32.
+ */
+va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const void* v,
+                        const void* out, const float* lse,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int32_t max_seqlen_q, int32_t max_seqlen_k,
+                        float softmax_scale, int causal,
+                        const void* bias, const int64_t* bias_stride,
+                        void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        int32_t batch, int32_t total_q, int32_t total_k,
+                        int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                        va_dtype dtype, va_dtype grad_dtype, va_stream stream);
+
+/* Static text for a status code (never NULL). */
+const char* va_status_string(va_status s);
+
+/* Message for the last non-VA_OK return on the calling thread ("" if none). */
+const char* va_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int va_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VA_VARLEN_H */

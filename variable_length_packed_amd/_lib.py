@@ -1,0 +1,59 @@
+"""ctypes view of libva_varlen.so (the C ABI declared in include/va_varlen.h)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libva_varlen.so")
+
+VA_OK, VA_ERR_INVALID, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP = range(5)
+VA_F32, VA_BF16 = 0, 1
+
+# Every symbol include/va_varlen.h declares.
+EXPORTS = ("va_varlen_fwd", "va_varlen_bwd", "va_varlen_bwd_workspace_size", "va_status_string",
+           "va_last_error", "va_version")
+
+_lib = None
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_f = ctypes.c_float
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def load() -> ctypes.CDLL:
+    """Load the library once.  Raises if it has not been built: there is no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m variable_length_packed_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.va_varlen_fwd.restype = ctypes.c_int
+    lib.va_varlen_fwd.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p, _i64p, _p,
+                                  _p, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p]
+    lib.va_varlen_bwd.restype = ctypes.c_int
+    lib.va_varlen_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p,
+                                  _i64p, _p, _p, _p, _p, ctypes.c_size_t, _i32, _i32, _i32, _i32,
+                                  _i32, _i32, ctypes.c_int, ctypes.c_int, _p]
+    lib.va_varlen_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.va_varlen_bwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                                 ctypes.c_int]
+    lib.va_status_string.restype = ctypes.c_char_p
+    lib.va_status_string.argtypes = [ctypes.c_int]
+    lib.va_last_error.restype = ctypes.c_char_p
+    lib.va_last_error.argtypes = []
+    lib.va_version.restype = ctypes.c_int
+    lib.va_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def strides_arg(strides):
+    """HOST int64[4] for bias_stride, or None."""
+    if strides is None:
+        return None
+    arr = (ctypes.c_int64 * 4)(*[int(s) for s in strides])
+    return arr

@@ -1,0 +1,245 @@
+"""Torch-facing marshalling over the C ABI (include/va_varlen.h).
+
+Tensors are checked for device, dtype, rank and contiguity, outputs are
+allocated with torch, pointers and the current HIP stream are handed to the
+library.  Nothing here computes attention.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+
+
+class VaError(RuntimeError):
+    """The HIP runtime reported an error inside the library."""
+
+
+_DTYPES = {torch.float32: _lib.VA_F32, torch.bfloat16: _lib.VA_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise ValueError(f"dtype {t.dtype} not supported (float32 or bfloat16)") from None
+
+
+def _raise(status: int, lib) -> None:
+    if status == _lib.VA_OK:
+        return
+    msg = (lib.va_last_error() or b"").decode(errors="replace")
+    name = (lib.va_status_string(status) or b"").decode()
+    if status == _lib.VA_ERR_HIP:
+        raise VaError(f"{name}: {msg}")
+    raise ValueError(f"{name}: {msg}")
+
+
+def _need_dev(name: str, t: torch.Tensor, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _bias_args(bias, bias_stride, q, batch, hq, max_q, max_k):
+    if bias is None:
+        if bias_stride is not None:
+            raise ValueError("bias_stride given without bias")
+        return None, None
+    if bias.device != q.device:
+        raise ValueError("bias must be on the same device as q")
+    if bias.dtype != q.dtype:
+        raise ValueError(f"bias dtype {bias.dtype} must equal the input dtype {q.dtype}")
+    if bias_stride is None:
+        if bias.dim() != 4:
+            raise ValueError("a bias without bias_stride must be 4-D [batch, heads, rows, cols]")
+        s = list(bias.stride())
+        if bias.shape[1] == 1:
+            s[1] = 0
+        if bias.shape[2] == 1:
+            s[2] = 0
+        bias_stride = s
+    bias_stride = [int(x) for x in bias_stride]
+    if len(bias_stride) != 4 or min(bias_stride) < 0:
+        raise ValueError("bias_stride must be 4 non-negative element strides")
+    # every element a valid (b, h, r < max_q, c < max_k) may address lies in the storage
+    s0, s1, s2, s3 = bias_stride
+    hi = (batch - 1) * s0 + (hq - 1) * s1 + (max_q - 1) * s2 + (max_k - 1) * s3
+    avail = bias.untyped_storage().nbytes() // bias.element_size() - bias.storage_offset()
+    if hi >= avail:
+        raise ValueError(f"bias view reaches element {hi} but only {avail} exist")
+    return bias.data_ptr(), _lib.strides_arg(bias_stride)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def va_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                  max_seqlen_q: int, max_seqlen_k: int,
+                  softmax_scale: Optional[float] = None, causal: bool = False,
+                  bias: Optional[torch.Tensor] = None,
+                  bias_stride: Optional[Sequence[int]] = None,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Forward.  Returns (out [Tq, Hq, d] in q's dtype, lse [Hq, Tq] float32)."""
+    lib = _lib.load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
+                 ("cu_seqlens_k", cu_seqlens_k)):
+        _need_dev(n, t, q.device)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [tokens, heads, head_dim]")
+    if k.shape != v.shape or k.shape[2] != q.shape[2]:
+        raise ValueError("k and v must be [total_k, Hkv, d] with q's head_dim")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be 1-D of equal length")
+    dt = _dt(q)
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    batch = cu_seqlens_q.numel() - 1
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    bptr, bstr = _bias_args(bias, bias_stride, q, batch, hq, int(max_seqlen_q), int(max_seqlen_k))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _need_dev("out", out, q.device)
+    _need_dev("lse", lse, q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or lse.shape != (hq, tq) or \
+            lse.dtype != torch.float32:
+        raise ValueError("out/lse have the wrong shape or dtype")
+    st = lib.va_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+                           cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
+                           int(bool(causal)), bptr, bstr, out.data_ptr(), lse.data_ptr(), batch,
+                           tq, tk, hq, hkv, d, dt, _stream(q.device))
+    _raise(st, lib)
+    return out, lse
+
+
+def va_varlen_bwd_workspace_size(batch: int, total_q: int, total_k: int, num_heads_q: int,
+                                 num_heads_kv: int, head_dim: int, dtype: torch.dtype,
+                                 grad_dtype: torch.dtype) -> int:
+    lib = _lib.load()
+    return int(lib.va_varlen_bwd_workspace_size(batch, total_q, total_k, num_heads_q, num_heads_kv,
+                                                head_dim, _DTYPES.get(dtype, -1),
+                                                _DTYPES.get(grad_dtype, -1)))
+
+
+def va_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  out: torch.Tensor, lse: torch.Tensor,
+                  cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                  max_seqlen_q: int, max_seqlen_k: int,
+                  softmax_scale: Optional[float] = None, causal: bool = False,
+                  bias: Optional[torch.Tensor] = None,
+                  bias_stride: Optional[Sequence[int]] = None,
+                  grad_dtype: torch.dtype = torch.float32,
+                  dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                  dv: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Backward.  Returns (dq, dk, dv) in ``grad_dtype``."""
+    lib = _lib.load()
+    for n, t in (("dout", dout), ("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse),
+                 ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        _need_dev(n, t, q.device)
+    if q.dim() != 3 or k.shape != v.shape or dout.shape != q.shape or out.shape != q.shape:
+        raise ValueError("shape mismatch among dout, q, k, v, out")
+    if any(t.dtype != q.dtype for t in (k, v, dout, out)):
+        raise ValueError("dout, q, k, v, out must share one dtype")
+    if lse.dtype != torch.float32 or lse.shape != (q.shape[1], q.shape[0]):
+        raise ValueError("lse must be float32 [Hq, total_q]")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32 or \
+            cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens must be int32 of equal length")
+    dt = _dt(q)
+    gdt = _DTYPES.get(grad_dtype)
+    if gdt is None:
+        raise ValueError(f"grad_dtype {grad_dtype} not supported")
+    tq, hq, d = q.shape
+    tk, hkv, _ = k.shape
+    batch = cu_seqlens_q.numel() - 1
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    bptr, bstr = _bias_args(bias, bias_stride, q, batch, hq, int(max_seqlen_q), int(max_seqlen_k))
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=grad_dtype, device=q.device)
+    for n, t, shp in (("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, v.shape)):
+        _need_dev(n, t, q.device)
+        if t.shape != shp or t.dtype != grad_dtype:
+            raise ValueError(f"{n} has the wrong shape or dtype")
+    need = lib.va_varlen_bwd_workspace_size(batch, tq, tk, hq, hkv, d, dt, gdt)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
+    _need_dev("workspace", workspace, q.device)
+    st = lib.va_varlen_bwd(dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           out.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
+                           cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
+                           int(bool(causal)), bptr, bstr, dq.data_ptr(), dk.data_ptr(),
+                           dv.data_ptr(), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), batch, tq, tk, hq, hkv,
+                           d, dt, gdt, _stream(q.device))
+    _raise(st, lib)
+    return dq, dk, dv
+
+
+class _VarlenAttn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_q, cu_k, max_q, max_k, scale, causal, bias, bias_stride,
+                grad_dtype):
+        out, lse = va_varlen_fwd(q, k, v, cu_q, cu_k, max_q, max_k, scale, causal, bias,
+                                 bias_stride)
+        ctx.save_for_backward(q, k, v, out, lse, cu_q, cu_k)
+        ctx.mark_non_differentiable(lse)
+        ctx.bias = bias
+        ctx.args = (max_q, max_k, scale, causal, bias_stride, grad_dtype)
+        return out, lse
+
+    @staticmethod
+    def backward(ctx, dout, dlse):
+        q, k, v, out, lse, cu_q, cu_k = ctx.saved_tensors
+        max_q, max_k, scale, causal, bias_stride, grad_dtype = ctx.args
+        dq, dk, dv = va_varlen_bwd(dout.contiguous(), q, k, v, out, lse, cu_q, cu_k, max_q, max_k,
+                                   scale, causal, ctx.bias, bias_stride, grad_dtype)
+        return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None, None,
+                None, None, None, None)
+
+
+def varlen_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                softmax_scale=None, causal=False, bias=None, bias_stride=None,
+                grad_dtype=torch.float32):
+    """Differentiable packed attention: returns (out, lse); gradients flow to q, k, v.
+
+    The bias is a constant: a bias that requires grad raises ValueError (the
+    kernel has no bias gradient).  The LSE output carries no gradient.
+    """
+    if bias is not None and bias.requires_grad:
+        raise ValueError("bias gradients are not supported: pass a bias that does not require grad")
+    return _VarlenAttn.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                             softmax_scale, causal, bias, bias_stride, grad_dtype)
+
+
+def va_status_string(status: int) -> str:
+    return _lib.load().va_status_string(status).decode()
+
+
+def va_last_error() -> str:
+    return _lib.load().va_last_error().decode(errors="replace")
+
+
+def va_version() -> int:
+    return int(_lib.load().va_version())
