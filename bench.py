@@ -1,0 +1,264 @@
+"""Benchmark: packed varlen attention on one MI355X.
+
+One step = one pass of the whole hot path over one synthetic batch: the
+forward (scores, bias, mask, online softmax, PV, LSE) and the backward
+(rowsum(dO*O), dK/dV, dQ) of the long-row bf16 causal GQA workload: 16
+sequences with lengths log-uniform in [128, 2048] (one of exactly 2048), 14
+query heads, 2 KV heads, head_dim 64, gradients stored float32.  Inputs are
+resident in HBM before the timed region.  The metric is non-padded TFLOP/s:
+4*d FLOPs per visible (query, key) pair and query head forward, 10*d
+backward; padding and recomputation are not counted.
+
+Prints ONE JSON line.  Besides the contract fields it carries the
+per-pass breakdown, the Qwen2.5-0.5B-shaped forward (20 sequences of
+64..1024 tokens) as a second forward figure, the live per-kernel roofline of
+the dominant kernel, and the CPU oracle's rate on the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import config, count  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_F32_TFLOPS = 157.3     # dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0       # HBM3E
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "variable_length_packed_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_flops(w, kernel: str) -> int:
+    """Non-padded FLOPs one launch of `kernel` must do (recomputation not counted)."""
+    pairs = count.workload_pairs(w.lens_q, w.lens_k, w.causal)
+    unit = 2 * w.d * w.hq * pairs  # one contraction over all visible pairs
+    if kernel.startswith("fwd"):
+        return 2 * unit          # S = QK^T, O = PV
+    if kernel.startswith("bwd_dkdv") and not kernel.endswith("reduce"):
+        return 4 * unit          # S (counted once), dP, dV, dK
+    if kernel.startswith("bwd_dq"):
+        return 1 * unit          # dQ only; its S and dP recompute are not counted
+    return 0
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None  # kernels changed since the counters were taken
+    e = t.get("kernels", {}).get(workload, {}).get(kernel)
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, min_seconds: float = 10.0, max_reps: int = 3):
+    """The fp64 oracle (forward + backward of every sequence) timed on the host cores."""
+    import oracle  # test infrastructure: only this leg of the bench uses it
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    flops = count.fwd_flops(w) + count.bwd_flops(w)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal, w.bias, w.bias_strides)
+        oracle.backward(w.dout, w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal, w.bias,
+                        w.bias_strides)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= max_reps:
+            break
+    rate = flops * reps / el / 1e12
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            m = re.search(r"model name\s*:\s*(.*)", f.read())
+            model = m.group(1).strip() if m else ""
+    except OSError:
+        pass
+    return {"value": rate, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the whole workload, forward + backward, {reps} time(s), {el:.1f} s, "
+                      f"numpy float64 with {threads} BLAS threads on {model or 'the host CPU'}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="3", help="config id for the step (default 3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; every box here has one "
+                                   "GPU, so --gpus must be 1"}))
+        return 2
+
+    import torch
+    import variable_length_packed_amd as va
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def dev_inputs(w, with_dout=True):
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(dt).contiguous()
+        d = dict(q=t(w.q), k=t(w.k), v=t(w.v), cu_q=torch.from_numpy(w.cu_q).to(dev),
+                 cu_k=torch.from_numpy(w.cu_k).to(dev))
+        d["bias"] = t(w.bias) if w.bias is not None else None
+        d["dout"] = t(w.dout) if (with_dout and w.dout is not None) else None
+        return d
+
+    w = config(int(args.workload), with_dout=True)
+    x = dev_inputs(w)
+    bstr = w.bias_strides if w.bias is not None else None
+    out = torch.empty_like(x["q"])
+    lse = torch.empty((w.hq, w.total_q), dtype=torch.float32, device=dev)
+    dq = torch.empty(x["q"].shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(x["k"].shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(x["v"].shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(va.va_varlen_bwd_workspace_size(w.batch, w.total_q, w.total_k, w.hq, w.hkv,
+                                                     w.d, x["q"].dtype, torch.float32),
+                     dtype=torch.uint8, device=dev)
+
+    def fwd():
+        va.va_varlen_fwd(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], w.max_q, w.max_k, w.scale,
+                         w.causal, x["bias"], bstr, out=out, lse=lse)
+
+    def bwd():
+        va.va_varlen_bwd(x["dout"], x["q"], x["k"], x["v"], out, lse, x["cu_q"], x["cu_k"],
+                         w.max_q, w.max_k, w.scale, w.causal, x["bias"], bstr,
+                         grad_dtype=torch.float32, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    def step():
+        fwd()
+        bwd()
+
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(k):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / k
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps)
+    flops_fwd, flops_bwd = count.fwd_flops(w), count.bwd_flops(w)
+    value = (flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12
+    ms_fwd = timed(fwd, args.steps)
+    ms_bwd = timed(bwd, args.steps)
+
+    # per-kernel HIP-event timing on the stream the kernels run on
+    va.va_timing_start(64 * args.steps + 64)
+    for _ in range(args.steps):
+        step()
+    kt = va.va_timing_stop()
+    kernels = {}
+    for name, (n, tot) in kt.items():
+        avg = tot / max(n, 1)
+        fl = algorithmic_flops(w, name)
+        kernels[name] = {"launches": n, "avg_ms": round(avg, 5),
+                         "tflops": round(fl / (avg * 1e-3) / 1e12, 2) if fl else None}
+    dom = max(kt.items(), key=lambda kv: kv[1][1])[0] if kt else None
+    roof = None
+    if dom is not None:
+        n, tot = kt[dom]
+        avg_s = tot / n * 1e-3
+        fl = algorithmic_flops(w, dom)
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        ach = fl / avg_s / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "traffic": measured_traffic(dom, f"config{args.workload}"),
+                "algorithmic_flops_per_launch": fl, "avg_launch_ms": round(tot / n, 5)}
+
+    # the Qwen2.5-0.5B-shaped forward (20 sequences U[64, 1024]) as a second forward figure
+    w2 = config(2, with_dout=False)
+    x2 = dev_inputs(w2, with_dout=False)
+    o2 = torch.empty_like(x2["q"])
+    l2 = torch.empty((w2.hq, w2.total_q), dtype=torch.float32, device=dev)
+
+    def fwd2():
+        va.va_varlen_fwd(x2["q"], x2["k"], x2["v"], x2["cu_q"], x2["cu_k"], w2.max_q, w2.max_k,
+                         w2.scale, True, out=o2, lse=l2)
+
+    for _ in range(args.warmup):
+        fwd2()
+    ms_fwd2 = timed(fwd2, args.steps)
+    tf2 = count.fwd_flops(w2) / (ms_fwd2 * 1e-3) / 1e12
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": "varlen attention TFLOP/s (non-padded FLOPs), fwd+bwd step, bf16 MFMA",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded PCG64 draws, N(0,1), bf16 round-to-nearest-even)",
+        "config": {"workload": "long-row bf16 causal GQA fwd+bwd: 16 seqs logU[128,2048] incl. "
+                               "one of 2048, 14 q heads / 2 kv heads, head_dim 64, fp32 grads",
+                   "total_tokens": w.total_q, "batch": w.batch, "max_seqlen": w.max_q,
+                   "visible_pairs_per_head": count.workload_pairs(w.lens_q, w.lens_k, True),
+                   "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "passes": {
+            "fwd": {"ms": round(ms_fwd, 5), "tflops": round(flops_fwd / (ms_fwd * 1e-3) / 1e12, 2),
+                    "pct_bf16_peak": round(100 * flops_fwd / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
+            "bwd": {"ms": round(ms_bwd, 5), "tflops": round(flops_bwd / (ms_bwd * 1e-3) / 1e12, 2),
+                    "pct_bf16_peak": round(100 * flops_bwd / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
+        },
+        "qwen_shaped_fwd": {"workload": "20 seqs U[64,1024], 14/2 heads, d64, causal, bf16",
+                            "total_tokens": w2.total_q, "ms": round(ms_fwd2, 5),
+                            "tflops": round(tf2, 2), "pct_bf16_peak": round(100 * tf2 / PEAK_BF16_TFLOPS, 2)},
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

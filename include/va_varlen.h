@@ -140,6 +140,27 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
                         int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                         va_dtype dtype, va_dtype grad_dtype, va_stream stream);
 
+/*
+ * Measurement.  The metric of this library is non-padded attention TFLOP/s
+ * per kernel against the MI355X roofline, so a caller can time each kernel a
+ * call launches.  After va_timing_start(n), the calling thread's library
+ * calls record a HIP event pair around each kernel they launch, on that
+ * call's stream, for up to n launches (events are created here, not per
+ * call).  va_timing_stop() waits for the recorded events, writes up to
+ * max_entries per-kernel aggregates (name, launches, total milliseconds) and
+ * returns how many kernels were seen (or -1 on a HIP error), then releases
+ * the events.  Timing adds an event record between launches; it is off by
+ * default.
+ */
+typedef struct {
+  const char* name; /* static string naming the kernel */
+  int launches;
+  double total_ms;
+} va_kernel_time;
+
+va_status va_timing_start(int max_launches);
+int va_timing_stop(va_kernel_time* out, int max_entries);
+
 /* Static text for a status code (never NULL). */
 const char* va_status_string(va_status s);
 

@@ -24,6 +24,8 @@ from .api import (  # noqa: F401
     va_varlen_fwd,
     va_last_error,
     va_status_string,
+    va_timing_start,
+    va_timing_stop,
     va_version,
     varlen_attn,
 )

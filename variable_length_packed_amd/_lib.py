@@ -12,7 +12,11 @@ VA_F32, VA_BF16 = 0, 1
 
 # Every symbol include/va_varlen.h declares.
 EXPORTS = ("va_varlen_fwd", "va_varlen_bwd", "va_varlen_bwd_workspace_size", "va_status_string",
-           "va_last_error", "va_version")
+           "va_last_error", "va_version", "va_timing_start", "va_timing_stop")
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
 
 _lib = None
 
@@ -47,6 +51,10 @@ def load() -> ctypes.CDLL:
     lib.va_last_error.argtypes = []
     lib.va_version.restype = ctypes.c_int
     lib.va_version.argtypes = []
+    lib.va_timing_start.restype = ctypes.c_int
+    lib.va_timing_start.argtypes = [ctypes.c_int]
+    lib.va_timing_stop.restype = ctypes.c_int
+    lib.va_timing_stop.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int]
     _lib = lib
     return lib
 

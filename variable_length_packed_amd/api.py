@@ -233,6 +233,23 @@ def varlen_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                              softmax_scale, causal, bias, bias_stride, grad_dtype)
 
 
+def va_timing_start(max_launches: int = 4096) -> None:
+    """Record a HIP event pair around each kernel this thread's later calls launch."""
+    lib = _lib.load()
+    _raise(lib.va_timing_start(int(max_launches)), lib)
+
+
+def va_timing_stop() -> dict:
+    """Stop timing; returns {kernel name: (launches, total milliseconds)}."""
+    lib = _lib.load()
+    buf = (_lib.KernelTime * 64)()
+    n = lib.va_timing_stop(buf, 64)
+    if n < 0:
+        raise VaError("event timing failed")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms))
+            for i in range(min(n, 64))}
+
+
 def va_status_string(status: int) -> str:
     return _lib.load().va_status_string(status).decode()
 

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <string>
+#include <vector>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -224,7 +226,75 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
 
 }  // extern "C"
 
+namespace {
+
+struct Timing {
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // 2 per launch
+  std::vector<const char*> names;
+  int used = 0;
+};
+thread_local Timing g_timing;
+
+}  // namespace
+
+extern "C" va_status va_timing_start(int max_launches) {
+  Timing& t = g_timing;
+  if (max_launches <= 0) return fail(VA_ERR_INVALID, "max_launches must be > 0");
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+  t.ev.assign(2 * (size_t)max_launches, nullptr);
+  t.names.assign((size_t)max_launches, nullptr);
+  for (auto& e : t.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      t.on = false;
+      return hip_fail(r, "hipEventCreate");
+    }
+  }
+  t.used = 0;
+  t.on = true;
+  return VA_OK;
+}
+
+extern "C" int va_timing_stop(va_kernel_time* out, int max_entries) {
+  Timing& t = g_timing;
+  t.on = false;
+  std::vector<va_kernel_time> agg;
+  int rc = 0;
+  for (int i = 0; i < t.used && rc == 0; ++i) {
+    if (hipEventSynchronize(t.ev[2 * i + 1]) != hipSuccess) { rc = -1; break; }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]) != hipSuccess) { rc = -1; break; }
+    size_t j = 0;
+    while (j < agg.size() && std::string(agg[j].name) != t.names[i]) ++j;
+    if (j == agg.size()) agg.push_back({t.names[i], 0, 0.0});
+    agg[j].launches += 1;
+    agg[j].total_ms += ms;
+  }
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+  t.ev.clear();
+  t.names.clear();
+  t.used = 0;
+  if (rc != 0) return -1;
+  for (int j = 0; j < (int)agg.size() && j < max_entries; ++j) out[j] = agg[j];
+  return (int)agg.size();
+}
+
 namespace va {
+
+void timing_before(hipStream_t st, const char* name) {
+  Timing& t = g_timing;
+  if (!t.on || t.used >= (int)t.names.size()) return;
+  t.names[t.used] = name;
+  (void)hipEventRecord(t.ev[2 * t.used], st);
+}
+
+void timing_after(hipStream_t st) {
+  Timing& t = g_timing;
+  if (!t.on || t.used >= (int)t.names.size() || t.names[t.used] == nullptr) return;
+  (void)hipEventRecord(t.ev[2 * t.used + 1], st);
+  t.used += 1;
+}
 
 // Resident workgroups of `kernel` on the current device, capped by the work.
 int resident_grid(const void* kernel, int threads, int64_t max_items) {

@@ -569,7 +569,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, int64_t q_items, int64_t k_items, hipS
     constexpr int EPV = BF16 ? 8 : 4;
     const int64_t threads = (int64_t)a.total_q * a.hq * (D / EPV);
     const int64_t grid = (threads + NT - 1) / NT;
+    timing_before(st, "bwd_dsum");
     hipLaunchKernelGGL((dsum_kernel<BF16, D>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+    timing_after(st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -578,15 +580,19 @@ hipError_t launch_bwd_t(const BwdArgs& a, int64_t q_items, int64_t k_items, hipS
     const int hsplit = a.hsplit;
     const int grid = resident_grid((const void*)kern, NT, k_items * hsplit);
     if (grid <= 0) return hipErrorInvalidConfiguration;
+    timing_before(st, BF16 ? "bwd_dkdv_bf16" : "bwd_dkdv_f32");
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a, hsplit, a.part);
+    timing_after(st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (hsplit > 1) {
       const size_t n4 = (size_t)a.total_k * a.hkv * D / 4;
       int64_t g = (int64_t)((n4 + NT - 1) / NT);
       if (g > 4096) g = 4096;
+      timing_before(st, "bwd_dkdv_reduce");
       hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)g), dim3(NT), 0, st, a, hsplit,
                          (const float*)a.part);
+      timing_after(st);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -595,7 +601,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, int64_t q_items, int64_t k_items, hipS
     auto kern = dq_kernel<BF16, D, CAUSAL, HAS_BIAS>;
     const int grid = resident_grid((const void*)kern, NT, q_items);
     if (grid <= 0) return hipErrorInvalidConfiguration;
+    timing_before(st, BF16 ? "bwd_dq_bf16" : "bwd_dq_f32");
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
+    timing_after(st);
   }
   return hipGetLastError();
 }

@@ -383,7 +383,9 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int64_t items, hipStream_t st) 
   auto kern = fwd_kernel<BF16, D, CAUSAL, HAS_BIAS>;
   const int grid = resident_grid((const void*)kern, NT, items);
   if (grid <= 0) return hipErrorInvalidConfiguration;
+  timing_before(st, BF16 ? "fwd_bf16" : "fwd_f32");
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
+  timing_after(st);
   return hipGetLastError();
 }
 

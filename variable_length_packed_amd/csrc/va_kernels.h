@@ -53,6 +53,10 @@ struct BwdArgs {
   int32_t grad_bf16;
 };
 
+// Optional per-kernel event timing (see va_timing_start); no-ops when off.
+void timing_before(hipStream_t st, const char* name);
+void timing_after(hipStream_t st);
+
 // Persistent grids: min(max_items, resident workgroups per device).
 int resident_grid(const void* kernel, int threads, int64_t max_items);
 
