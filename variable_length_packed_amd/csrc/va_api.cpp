@@ -146,7 +146,7 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
   a.out = out; a.lse = lse;
   a.batch = batch; a.total_q = total_q; a.total_k = total_k;
   a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = num_heads_q / num_heads_kv; a.d = head_dim;
-  const int bm = va::fwd_block_m();
+  const int bm = va::fwd_block_m(dtype == VA_BF16, head_dim);
   sched_dims(max_seqlen_q, bm, a.tcap, a.stride, a.nlev);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.causal = causal;

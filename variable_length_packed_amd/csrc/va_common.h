@@ -43,9 +43,42 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __builtin_bit_cast(float, (uint32_t)x << 16);
 }
 
+// Raw buffer resources: loads past `bytes` (or at a negative offset, seen as
+// a huge unsigned one) return zero and stores there are dropped, so ragged
+// tiles need no branches.  Word 3 = 0x00020000: 32-bit data format, the
+// setting for raw (unstructured) buffers on CDNA.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+__device__ __forceinline__ u32x2_t buf_load8(rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(u32x4_t v, rsrc_t r, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(u32x2_t v, rsrc_t r, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(uint32_t v, rsrc_t r, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, byte_off, 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Value of the same register in lane l ^ 32 (v_permlane32_swap: a VALU op,
+// no LDS round trip).  For lanes < 32 the partner's value is the second
+// result, for lanes >= 32 the first.
+__device__ __forceinline__ float xor32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -74,13 +107,14 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int b, int total, 
 // that share a KV head run together and share its K/V in L2).
 // ---------------------------------------------------------------------------
 constexpr int kMaxLevels = 512;
+// Per-sequence tile counts cached in LDS when the batch fits (uint16 each).
+constexpr int kMaxSeqCached = 2048;
 
 struct SchedShared {
   int level_start[kMaxLevels + 1];
   int full[kMaxLevels + 1];
   int part[kMaxLevels + 1];
-  int scan[4];
-  int found_b, found_t, found;
+  uint16_t ntiles[kMaxSeqCached];
   int total_tiles;
 };
 
@@ -89,7 +123,7 @@ __device__ __forceinline__ int seq_tiles(int len, int bm, int tcap) {
   return min(n, tcap);
 }
 
-// Called once per workgroup by all 256 threads.
+// Called once per workgroup by all threads.
 __device__ inline void sched_build(SchedShared& s, const int32_t* cu, int batch, int total,
                                    int bm, int tcap, int stride, int nlev) {
   const int tid = threadIdx.x;
@@ -101,8 +135,9 @@ __device__ inline void sched_build(SchedShared& s, const int32_t* cu, int batch,
   for (int b = tid; b < batch; b += blockDim.x) {
     int q0, q1;
     seq_bounds(cu, b, total, q0, q1);
-    int n = seq_tiles(q1 - q0, bm, tcap);
-    int f = n / stride, rem = n - f * stride;
+    const int n = seq_tiles(q1 - q0, bm, tcap);
+    if (b < kMaxSeqCached) s.ntiles[b] = (uint16_t)min(n, 65535);
+    const int f = n / stride, rem = n - f * stride;
     if (f > 0) atomicAdd(&s.full[f - 1], 1);
     if (rem > 0) atomicAdd(&s.part[f], rem);
   }
@@ -125,59 +160,68 @@ __device__ inline void sched_build(SchedShared& s, const int32_t* cu, int batch,
   __syncthreads();
 }
 
-// Maps a tile index to (sequence b, tile t).  All threads call it; returns
-// through shared memory (uniform).
-__device__ inline void sched_find(SchedShared& s, const int32_t* cu, int batch, int total, int bm,
-                                  int tcap, int stride, int nlev, int tile, int& b_out,
+__device__ __forceinline__ int sched_ntiles(const SchedShared& s, const int32_t* cu, int b,
+                                            int total, int bm, int tcap) {
+  if (b < kMaxSeqCached) return s.ntiles[b];
+  int q0, q1;
+  seq_bounds(cu, b, total, q0, q1);
+  return seq_tiles(q1 - q0, bm, tcap);
+}
+
+// Maps a tile index to (sequence b, tile t).  Every wave decodes on its own
+// (no barrier, nothing written): within level `lev` the tiles are ordered by
+// sequence, so b is found by counting, 64 sequences per step, the sequences
+// that own tiles in that level.
+__device__ inline void sched_find(const SchedShared& s, const int32_t* cu, int batch, int total,
+                                  int bm, int tcap, int stride, int nlev, int tile, int& b_out,
                                   int& t_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  int lev = 0;
-  {
-    int lo = 0, hi = nlev - 1;  // largest lev with level_start[lev] <= tile
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (s.level_start[mid] <= tile) lo = mid; else hi = mid - 1;
-    }
-    lev = lo;
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = nlev - 1;  // largest lev with level_start[lev] <= tile
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s.level_start[mid] <= tile) lo = mid; else hi = mid - 1;
   }
+  const int lev = lo;
   const int u = tile - s.level_start[lev];
   const int lo_t = lev * stride;
-  int base = 0;
-  for (int chunk = 0; chunk < batch; chunk += blockDim.x) {
-    const int b = chunk + tid;
+  int base = 0, fb = 0, ft = lo_t;
+  for (int chunk = 0; chunk < batch; chunk += 64) {
+    const int b = chunk + lane;
     int c = 0;
-    if (b < batch) {
-      int q0, q1;
-      seq_bounds(cu, b, total, q0, q1);
-      int n = seq_tiles(q1 - q0, bm, tcap);
-      c = min(max(n - lo_t, 0), stride);
-    }
-    // inclusive scan inside the wave
-    int x = c;
+    if (b < batch) c = min(max(sched_ntiles(s, cu, b, total, bm, tcap) - lo_t, 0), stride);
+    if (stride == 1) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(c > 0);
+      const int cnt = __builtin_popcountll(m);
+      if (u < base + cnt) {
+        // the (u - base)-th set bit of m
+        const int excl = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(c > 0 && excl == u - base);
+        fb = chunk + (int)__builtin_ctzll(hit);
+        ft = lo_t;
+        break;
+      }
+      base += cnt;
+    } else {
+      int x = c;  // inclusive scan across the wave
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      const int tot = __shfl(x, 63, 64);
+      if (u < base + tot) {
+        const int excl = base + x - c;
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(c > 0 && u >= excl && u < excl + c);
+        const int l = (int)__builtin_ctzll(hit);
+        fb = chunk + l;
+        ft = lo_t + (u - (base + __shfl(x, l, 64) - __shfl(c, l, 64)));
+        break;
+      }
+      base += tot;
     }
-    if (lane == 63) s.scan[wid] = x;
-    __syncthreads();
-    int wbase = 0, tot = 0;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-      if (w < wid) wbase += s.scan[w];
-      tot += s.scan[w];
-    }
-    const int excl = base + wbase + x - c;
-    if (c > 0 && u >= excl && u < excl + c) {
-      s.found_b = b;
-      s.found_t = lo_t + (u - excl);
-    }
-    base += tot;
-    __syncthreads();
-    if (base > u) break;  // uniform: every thread has the same base
   }
-  b_out = uniform(s.found_b);
-  t_out = uniform(s.found_t);
-  __syncthreads();
+  b_out = uniform(fb);
+  t_out = uniform(ft);
 }
 
 }  // namespace va

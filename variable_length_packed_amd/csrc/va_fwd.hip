@@ -25,18 +25,17 @@ namespace va {
 
 namespace {
 
-constexpr int BM = 128;  // query rows per workgroup
 constexpr int NT = 256;  // threads per workgroup
 
 // keys per block: 64 for bf16 (two 32-key score tiles), 32 for f32 (LDS size)
-template <bool BF16>
+template <bool BF16, int D>
 struct BlockN {
   static constexpr int value = BF16 ? 64 : 32;
 };
 
 template <bool BF16, int D>
 struct FwdSmem {
-  static constexpr int BN = BlockN<BF16>::value;
+  static constexpr int BN = BlockN<BF16, D>::value;
   using T = typename std::conditional<BF16, uint16_t, float>::type;
   // K block: [BN][D] row-major, row pitch padded by 16 bytes.
   static constexpr int KP = D + 16 / (int)sizeof(T);
@@ -49,14 +48,22 @@ struct FwdSmem {
   T v[2][VROWS * VP];
 };
 
-// Position of key j (0..BN-1) inside a transposed bf16 V row.
+// Position of key j (0..BN-1) inside a transposed bf16 V row before the
+// swizzle: bits 2 and 3 of j swapped, so the 8 k-slots of a lane half are
+// contiguous.
 __device__ __forceinline__ int vpos(int j) {
   return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
 }
 
+// The 16-byte chunks of transposed row d are XOR-swizzled by (d >> 3) modulo
+// the chunk count: the transposing stores (8 rows apart per lane) and the
+// fragment reads (consecutive rows per lane) then spread over the LDS banks.
+template <int BN>
+__device__ __forceinline__ int vswz(int d) { return ((d >> 3) & (BN / 8 - 1)) << 3; }
+
 template <bool BF16, int D>
 struct Loader {
-  static constexpr int BN = BlockN<BF16>::value;
+  static constexpr int BN = BlockN<BF16, D>::value;
   using T = typename std::conditional<BF16, uint16_t, float>::type;
   static constexpr int EPV = 16 / sizeof(T);           // elements per 16-byte vector
   static constexpr int KVEC = BN * D / EPV;            // 16-byte vectors per K block
@@ -67,97 +74,101 @@ struct Loader {
   u32x4_t kr[KPT];
   u32x4_t vr[BF16 ? 2 * VPT : VPT];
 
-  __device__ __forceinline__ void load(const T* __restrict__ kbase, const T* __restrict__ vbase,
-                                       size_t row_stride, int kb, int klo, int khi) {
-    const int tid = threadIdx.x;
+  // Block of keys kb .. kb+BN-1 of one (sequence, KV head).  The resources
+  // cover keys [0, kv_hi); other rows (negative offsets included) read 0.
+  __device__ __forceinline__ void load_k(rsrc_t kres, int row_bytes, int kb) {
+    static_assert(KVEC % NT == 0 && VTASK % NT == 0, "loader tasks must tile the workgroup");
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      int u = tid + i * NT;
-      int key = u / (D / EPV), c = u % (D / EPV);
-      int j = kb + key;
-      u32x4_t z = {0, 0, 0, 0};
-      if (u < KVEC && j >= klo && j < khi)
-        z = *(const u32x4_t*)(kbase + (size_t)j * row_stride + c * EPV);
-      kr[i] = z;
+      const int u = threadIdx.x + i * NT;
+      const int key = u / (D / EPV), c = u % (D / EPV);
+      kr[i] = buf_load16(kres, (kb + key) * row_bytes + c * 16);
     }
+  }
+  __device__ __forceinline__ void load_v(rsrc_t vres, int row_bytes, int kb) {
     if constexpr (BF16) {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
-        int u = tid + i * NT;
-        int dc = u % (D / 8), kp = u / (D / 8);
+        const int u = threadIdx.x + i * NT;
+        const int dc = u % (D / 8), kp = u / (D / 8);
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          int j = kb + 2 * kp + r;
-          u32x4_t z = {0, 0, 0, 0};
-          if (u < VTASK && j >= klo && j < khi)
-            z = *(const u32x4_t*)(vbase + (size_t)j * row_stride + dc * 8);
-          vr[2 * i + r] = z;
-        }
+        for (int r = 0; r < 2; ++r) vr[2 * i + r] = buf_load16(vres, (kb + 2 * kp + r) * row_bytes + dc * 16);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
-        int u = tid + i * NT;
-        int key = u / (D / EPV), c = u % (D / EPV);
-        int j = kb + key;
-        u32x4_t z = {0, 0, 0, 0};
-        if (u < KVEC && j >= klo && j < khi)
-          z = *(const u32x4_t*)(vbase + (size_t)j * row_stride + c * EPV);
-        vr[i] = z;
+        const int u = threadIdx.x + i * NT;
+        const int key = u / (D / EPV), c = u % (D / EPV);
+        vr[i] = buf_load16(vres, (kb + key) * row_bytes + c * 16);
       }
     }
   }
 
-  __device__ __forceinline__ void store(FwdSmem<BF16, D>& sm, int buf) {
+  __device__ __forceinline__ void store_k(FwdSmem<BF16, D>& sm, int buf) {
     using S = FwdSmem<BF16, D>;
-    const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      int u = tid + i * NT;
-      if (u < KVEC) {
-        int key = u / (D / EPV), c = u % (D / EPV);
-        *(u32x4_t*)(&sm.k[buf][key * S::KP + c * EPV]) = kr[i];
-      }
+      const int u = threadIdx.x + i * NT;
+      const int key = u / (D / EPV), c = u % (D / EPV);
+      *(u32x4_t*)(&sm.k[buf][key * S::KP + c * EPV]) = kr[i];
     }
+  }
+  __device__ __forceinline__ void store_v(FwdSmem<BF16, D>& sm, int buf) {
+    using S = FwdSmem<BF16, D>;
     if constexpr (BF16) {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
-        int u = tid + i * NT;
-        if (u < VTASK) {
-          int dc = u % (D / 8), kp = u / (D / 8);
-          const int pos = vpos(2 * kp);
-          u32x4_t a = vr[2 * i], b = vr[2 * i + 1];
-          // a holds dims dc*8..+8 of key 2kp, b of key 2kp+1; write pairs (key, key+1) per dim
+        const int u = threadIdx.x + i * NT;
+        const int dc = u % (D / 8), kp = u / (D / 8);
+        const int pos = vpos(2 * kp) ^ vswz<BN>(dc * 8);  // rows dc*8 .. dc*8+7 share the swizzle
+        const u32x4_t a = vr[2 * i], b = vr[2 * i + 1];
+        // a holds dims dc*8..+8 of key 2kp, b of key 2kp+1; write pairs (key, key+1) per dim
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            uint32_t lo = (a[e] & 0xFFFFu) | (b[e] << 16);
-            uint32_t hi = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
-            *(uint32_t*)(&sm.v[buf][(dc * 8 + 2 * e) * S::VP + pos]) = lo;
-            *(uint32_t*)(&sm.v[buf][(dc * 8 + 2 * e + 1) * S::VP + pos]) = hi;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = (a[e] & 0xFFFFu) | (b[e] << 16);
+          const uint32_t hi = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
+          *(uint32_t*)(&sm.v[buf][(dc * 8 + 2 * e) * S::VP + pos]) = lo;
+          *(uint32_t*)(&sm.v[buf][(dc * 8 + 2 * e + 1) * S::VP + pos]) = hi;
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < VPT; ++i) {
-        int u = tid + i * NT;
-        if (u < KVEC) {
-          int key = u / (D / EPV), c = u % (D / EPV);
-          *(u32x4_t*)(&sm.v[buf][key * S::VP + c * EPV]) = vr[i];
-        }
+        const int u = threadIdx.x + i * NT;
+        const int key = u / (D / EPV), c = u % (D / EPV);
+        *(u32x4_t*)(&sm.v[buf][key * S::VP + c * EPV]) = vr[i];
       }
     }
   }
 };
 
+// Query tiles of 32 rows per wave.  Two tiles halve LDS reads per MFMA (each
+// K and V^T fragment feeds two MFMAs) but need the whole register file, i.e.
+// one wave per SIMD; measured on gfx950 that loses more to exposed latency
+// than it saves, so one tile per wave (two waves per SIMD) is used.
+template <bool BF16, int D>
+struct WaveTiles {
+  static constexpr int value = 1;
+};
+template <bool BF16, int D>
+constexpr int block_m() { return 4 * 32 * WaveTiles<BF16, D>::value; }
+
+// d = 64: two workgroups per CU (256 registers per lane); d = 128: one, with
+// the accumulators free to use the whole 512-entry register file.
+template <bool BF16, int D>
+constexpr int min_blocks() { return D == 64 ? 2 : 1; }
+
 template <bool BF16, int D, bool CAUSAL, bool HAS_BIAS>
-__global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArgs a) {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
   using S = FwdSmem<BF16, D>;
-  constexpr int BN = BlockN<BF16>::value;
+  constexpr int BN = BlockN<BF16, D>::value;
   constexpr int NS = BN / 32;                // 32-key score tiles per block
   constexpr int DT = D / 32;                 // 32-wide output tiles along head_dim
   constexpr int QF = BF16 ? D / 16 : D / 2;  // Q fragments (MFMA k-steps) per lane
+  constexpr int QT = WaveTiles<BF16, D>::value;  // 32-row query tiles per wave
+  constexpr int BM = block_m<BF16, D>();
+  constexpr int WR = 32 * QT;                 // rows per wave
 
   __shared__ SchedShared sched;
   __shared__ S sm;
@@ -191,186 +202,294 @@ __global__ __launch_bounds__(NT, 2) void fwd_kernel(FwdArgs a) {
     const int off = Lk - Lq;
     const int g = h / a.n_rep;
     const int r1 = Lq - t * BM;
-    const int w0 = r1 - BM + 32 * wid;  // first row of this wave
-    const int rq = w0 + r32;            // this lane's query row
-    const bool row_ok = rq >= 0;
+    const int w0 = r1 - BM + WR * wid;  // first row of this wave
+    int rq[QT];                          // this lane's query row in each query tile
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) rq[qt] = w0 + 32 * qt + r32;
     // keys the whole tile may see, and this wave's last visible key + 1
     const int kv_hi = CAUSAL ? min(Lk, r1 + off) : Lk;
-    const int wave_hi = CAUSAL ? min(Lk, w0 + 32 + off) : Lk;
-    const bool wave_on = (w0 + 31 >= 0) && wave_hi > 0;
+    const int wave_hi = CAUSAL ? min(Lk, w0 + WR + off) : Lk;
+    const bool wave_on = (w0 + WR - 1 >= 0) && wave_hi > 0;
     const int nblk = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
-    // causal: blocks end exactly at kv_hi (the ragged block holds keys near 0);
-    // otherwise blocks start at 0 (the ragged block is the last)
-    const int kb0 = CAUSAL ? kv_hi - nblk * BN : 0;
+    // blocks start at key 0; the ragged block (if any) is the last, and with a
+    // causal mask the blocks crossing the diagonal are the last ones too, so
+    // every masked block comes after every unmasked one.  Blocks before
+    // n_plain are unmasked for every wave of the workgroup: the smallest row
+    // of the tile sees keys <= r1 - BM + off.
+    const int kb0 = 0;
+    const int n_plain = CAUSAL ? min(max(r1 - BM + off + 1, 0) / BN, kv_hi / BN) : kv_hi / BN;
 
-    // ---- Q fragment (B operand of S^T = K Q^T)
-    u32x4_t qf4[BF16 ? QF : 1];
-    float qff[BF16 ? 1 : QF];
-    {
-      const T* qrow = qg + (size_t)(q0 + max(rq, 0)) * qstride + (size_t)h * D;
+    // ---- resources: this sequence's rows of Q/O for head h and of K/V for head g
+    constexpr int ELT = (int)sizeof(T);
+    const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
+    const size_t qoff = (size_t)q0 * qstride + (size_t)h * D;
+    const int64_t qbytes = Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0;
+    const rsrc_t qres = make_rsrc(qg + qoff, qbytes);
+    const rsrc_t ores = make_rsrc(og + qoff, qbytes);
+    const size_t koff = (size_t)k0 * kstride + (size_t)g * D;
+    const int64_t kbytes = kv_hi > 0 ? (int64_t)(kv_hi - 1) * krow_bytes + D * ELT : 0;
+    const rsrc_t kres = make_rsrc(kg + koff, kbytes);
+    const rsrc_t vres = make_rsrc(vg + koff, kbytes);
+
+    // ---- Q fragments (B operand of S^T = K Q^T); rows < 0 read as zero
+    u32x4_t qf4[QT][BF16 ? QF : 1];
+    float qff[QT][BF16 ? 1 : QF];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
       if constexpr (BF16) {
 #pragma unroll
-        for (int ks = 0; ks < QF; ++ks) {
-          u32x4_t z = {0, 0, 0, 0};
-          if (row_ok) z = *(const u32x4_t*)(qrow + 16 * ks + 8 * hh);
-          qf4[ks] = z;
-        }
+        for (int ks = 0; ks < QF; ++ks)
+          qf4[qt][ks] = buf_load16(qres, rq[qt] * qrow_bytes + (16 * ks + 8 * hh) * 2);
       } else {
         // k-slot (group G, step j) of lane half hh reads dim 8G + 4hh + j
 #pragma unroll
         for (int G = 0; G < D / 8; ++G) {
-          f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-          if (row_ok) z = *(const f32x4_t*)(qrow + 8 * G + 4 * hh);
+          const u32x4_t z = buf_load16(qres, rq[qt] * qrow_bytes + (8 * G + 4 * hh) * 4);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) qff[4 * G + j] = z[j];
+          for (int j = 0; j < 4; ++j) qff[qt][4 * G + j] = __uint_as_float(z[j]);
         }
       }
     }
 
-    f32x16_t acc[DT];
+    f32x16_t acc[QT][DT];
+    float m_run[QT], l_run[QT];  // running max (log2 units) and this half's partial row sum
 #pragma unroll
-    for (int i = 0; i < DT; ++i) acc[i] = (f32x16_t){};
-    float m_run = -INFINITY;  // running max of log2-domain scores
-    float l_run = 0.f;        // this half's partial row sum
+    for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+      for (int i = 0; i < DT; ++i) acc[qt][i] = (f32x16_t){};
+      m_run[qt] = -INFINITY;
+      l_run[qt] = 0.f;
+    }
 
-    const T* kbase = kg + (size_t)k0 * kstride + (size_t)g * D;
-    const T* vbase = vg + (size_t)k0 * kstride + (size_t)g * D;
-    const T* bias_bh = nullptr;
+    const T* bias_bh[QT];
     if constexpr (HAS_BIAS)
-      bias_bh = (const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1 +
-                (int64_t)max(rq, 0) * a.bs2;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        bias_bh[qt] = (const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1 +
+                      (int64_t)max(rq[qt], 0) * a.bs2;
 
     Loader<BF16, D> ld;
-    if (nblk > 0) {
-      ld.load(kbase, vbase, kstride, kb0, 0, kv_hi);
-      ld.store(sm, 0);
-    }
-    __syncthreads();
 
-    for (int n = 0; n < nblk; ++n) {
-      const int kb = kb0 + n * BN;
-      const int buf = n & 1;
-      if (n + 1 < nblk) ld.load(kbase, vbase, kstride, kb + BN, 0, kv_hi);
+    // Visible keys of a row: kj in [0, hi_row]; kj is kb + c_i + 4*hh with
+    // c_i = 32*st + 8*(i/4) + i%4 a compile-time constant, so the mask of a
+    // score is one unsigned range test on c_i.
+    int hi_row[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) hi_row[qt] = CAUSAL ? min(kv_hi - 1, rq[qt] + off) : kv_hi - 1;
 
-      if (wave_on && kb < wave_hi) {
-        // ---- S^T = K Q^T for two 32-key tiles
-        f32x16_t s[NS];
+    // ---- S^T = K Q^T of the block in K buffer `kbuf`: each K fragment read
+    // from LDS feeds the QT query tiles
+    auto qk = [&](int kbuf, f32x16_t (&s)[QT][NS]) {
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          s[st] = (f32x16_t){};
-          const T* krow = &sm.k[buf][(32 * st + r32) * S::KP];
-          if constexpr (BF16) {
+      for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-            for (int ks = 0; ks < QF; ++ks) {
-              u32x4_t ka = *(const u32x4_t*)(krow + 16 * ks + 8 * hh);
-              s[st] = mfma32_bf16(ka, qf4[ks], s[st]);
-            }
-          } else {
+        for (int st = 0; st < NS; ++st) s[qt][st] = (f32x16_t){};
+      if constexpr (BF16) {
 #pragma unroll
-            for (int G = 0; G < D / 8; ++G) {
-              f32x4_t ka = *(const f32x4_t*)(krow + 8 * G + 4 * hh);
+        for (int ks = 0; ks < QF; ++ks)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) s[st] = mfma32_f32(ka[j], qff[4 * G + j], s[st]);
-            }
+          for (int st = 0; st < NS; ++st) {
+            const u32x4_t ka = *(const u32x4_t*)(&sm.k[kbuf][(32 * st + r32) * S::KP + 16 * ks + 8 * hh]);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) s[qt][st] = mfma32_bf16(ka, qf4[qt][ks], s[qt][st]);
           }
-        }
-        // ---- scale, bias, mask (log2 domain)
-        const bool need_mask = (kb < 0) || (kb + BN > kv_hi) ||
-                               (CAUSAL && (kb + BN - 1 > w0 + off));
-        float x[16 * NS];
+      } else {
+#pragma unroll
+        for (int G = 0; G < D / 8; ++G)
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            const f32x4_t ka = *(const f32x4_t*)(&sm.k[kbuf][(32 * st + r32) * S::KP + 8 * G + 4 * hh]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int qt = 0; qt < QT; ++qt) s[qt][st] = mfma32_f32(ka[j], qff[qt][4 * G + j], s[qt][st]);
+          }
+      }
+    };
+
+    // ---- softmax of one block's scores and O^T += V^T P^T.  MASK: some
+    // score of the wave's tile is invisible.  Scores are rewritten in place.
+    auto softmax_pv = [&](auto mask_tag, int kb, int vbuf, f32x16_t (&s)[QT][NS]) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      // bias (log2 units) and mask; without a bias the scores stay raw and the
+      // scale is applied inside the exponent's FMA
+      const int lo_rel = -kb - 4 * hh;  // c_i >= lo_rel  <=>  kj >= 0
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const unsigned span = (unsigned)max(hi_row[qt] + 1, 0);  // kj <= hi_row (none if < 0)
 #pragma unroll
         for (int st = 0; st < NS; ++st)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int kj = kb + 32 * st + 8 * (i >> 2) + 4 * hh + (i & 3);
-            float v = s[st][i] * a.scale_log2;
+            const int ci = 32 * st + 8 * (i >> 2) + (i & 3);
+            float v = s[qt][st][i];
             if constexpr (HAS_BIAS) {
-              if (row_ok && kj >= 0 && kj < Lk) {
-                T bv = bias_bh[(int64_t)kj * a.bs3];
+              const int kj = kb + ci + 4 * hh;
+              v *= a.scale_log2;
+              if (rq[qt] >= 0 && kj >= 0 && kj < Lk) {
                 float bf;
-                if constexpr (BF16) bf = bf16_to_f32(bv); else bf = bv;
+                if constexpr (BF16) bf = bf16_to_f32(bias_bh[qt][(int64_t)kj * a.bs3]);
+                else bf = bias_bh[qt][(int64_t)kj * a.bs3];
                 v = __builtin_fmaf(bf, kLog2e, v);
               }
             }
-            if (need_mask) {
-              bool ok = kj >= 0 && kj < kv_hi && (!CAUSAL || kj <= rq + off);
-              v = ok ? v : -INFINITY;
-            }
-            x[16 * st + i] = v;
+            if constexpr (MASK) v = ((unsigned)(ci - lo_rel) < span) ? v : -INFINITY;
+            s[qt][st][i] = v;
           }
-        // ---- online softmax
-        float mx = x[0];
+      }
+      // online softmax with a lazily moved reference max (log2 units): keep the
+      // reference unless a row's max exceeds it by more than 8 (then p <= 2^8:
+      // exact algebra, no overflow); moving it rescales O
+      float mx[QT];
+      bool move = false;
 #pragma unroll
-        for (int i = 1; i < 16 * NS; ++i) mx = fmaxf(mx, x[i]);
-        mx = fmaxf(mx, xor32(mx));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
-        float psum = 0.f;
+      for (int qt = 0; qt < QT; ++qt) {
+        float m = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16 * NS; ++i) {
-          x[i] = fast_exp2(x[i] - m_use);
-          psum += x[i];
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) m = max3f(m, s[qt][st][i], s[qt][st][i + 1]);
+        m = fmaxf(m, xor32(m));
+        if constexpr (!HAS_BIAS) m *= a.scale_log2;  // raw scores: scale the max once (scale > 0)
+        mx[qt] = m;
+        move = move || (m > m_run[qt] + 8.f);
+      }
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const float m_new = fmaxf(m_run[qt], mx[qt]);
+          const float alpha = fast_exp2(m_run[qt] - (m_new == -INFINITY ? 0.f : m_new));
+          m_run[qt] = m_new;
+          l_run[qt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[qt][dt][i] *= alpha;
         }
-        l_run = l_run * alpha + psum;
+      }
+      float m_use[QT], psum[QT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+      for (int qt = 0; qt < QT; ++qt) {
+        m_use[qt] = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
+        psum[qt] = 0.f;
+      }
+      auto p_of = [&](float v, int qt) {
+        if constexpr (HAS_BIAS) return fast_exp2(v - m_use[qt]);
+        else return fast_exp2(__builtin_fmaf(v, a.scale_log2, -m_use[qt]));
+      };
+      if constexpr (BF16) {
+        // 16-key chunks kc: P^T chunk = registers 8*(kc%2) .. +8 of score tile kc/2.
+        // The V^T fragments of chunk kc+1 are read while chunk kc computes.
+        u32x4_t vnext[DT];
+        auto read_v = [&](int kc, u32x4_t (&dst)[DT]) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
-        // ---- O^T += V^T P^T
-        if constexpr (BF16) {
+          for (int dt = 0; dt < DT; ++dt) {
+            const int d = 32 * dt + r32;
+            dst[dt] = *(const u32x4_t*)(&sm.v[vbuf][d * S::VP + ((16 * kc + 8 * hh) ^ vswz<BN>(d))]);
+          }
+        };
+        read_v(0, vnext);
 #pragma unroll
-          for (int kc = 0; kc < 2 * NS; ++kc) {  // 16-key chunks
+        for (int kc = 0; kc < 2 * NS; ++kc) {
+          u32x4_t vcur[DT];
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) vcur[dt] = vnext[dt];
+          if (kc + 1 < 2 * NS) read_v(kc + 1, vnext);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
             u32x4_t pb;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pb[e] = pack_bf16x2(x[8 * kc + 2 * e], x[8 * kc + 2 * e + 1]);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-              u32x4_t va = *(const u32x4_t*)(&sm.v[buf][(32 * dt + r32) * S::VP + 16 * kc + 8 * hh]);
-              acc[dt] = mfma32_bf16(va, pb, acc[dt]);
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = p_of(s[qt][kc >> 1][8 * (kc & 1) + 2 * e], qt);
+              const float p1 = p_of(s[qt][kc >> 1][8 * (kc & 1) + 2 * e + 1], qt);
+              psum[qt] += p0 + p1;
+              pb[e] = pack_bf16x2(p0, p1);
             }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = mfma32_bf16(vcur[dt], pb, acc[qt][dt]);
           }
-        } else {
+        }
+      } else {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
           for (int st = 0; st < NS; ++st)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
+              const float p = p_of(s[qt][st][i], qt);
+              psum[qt] += p;
               const int key = 32 * st + 8 * (i >> 2) + 4 * hh + (i & 3);
 #pragma unroll
               for (int dt = 0; dt < DT; ++dt) {
-                float va = sm.v[buf][key * S::VP + 32 * dt + r32];
-                acc[dt] = mfma32_f32(va, x[16 * st + i], acc[dt]);
+                const float va = sm.v[vbuf][key * S::VP + 32 * dt + r32];
+                acc[qt][dt] = mfma32_f32(va, p, acc[qt][dt]);
               }
             }
-        }
       }
-      if (n + 1 < nblk) ld.store(sm, buf ^ 1);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) l_run[qt] += psum[qt];
+    };
+
+    // Pipeline: K runs one block ahead of V.  Iteration n computes S of block
+    // n+1 (MFMA) while it runs the softmax of block n (VALU), then PV of block
+    // n; it stages K(n+2) into the K buffer block n used and V(n+1) into the V
+    // buffer block n-1 used, so one barrier per block suffices.
+    auto active = [&](int n) { return n < nblk && wave_on && kb0 + n * BN < wave_hi; };
+    ld.load_k(kres, krow_bytes, kb0);
+    ld.load_v(vres, krow_bytes, kb0);
+    ld.store_k(sm, 0);
+    ld.store_v(sm, 0);
+    ld.load_k(kres, krow_bytes, kb0 + BN);
+    ld.store_k(sm, 1);
+    __syncthreads();
+    f32x16_t s_cur[QT][NS];
+    if (active(0)) qk(0, s_cur);
+    __syncthreads();  // every wave has read K(0) before K(2) replaces it
+
+    auto step = [&](auto mask_tag, int n) {
+      const int kb = kb0 + n * BN;
+      ld.load_k(kres, krow_bytes, kb + 2 * BN);  // past the last block every row reads as zero
+      ld.load_v(vres, krow_bytes, kb + BN);
+      f32x16_t s_nxt[QT][NS];
+      if (active(n + 1)) qk((n + 1) & 1, s_nxt);
+      if (active(n)) softmax_pv(mask_tag, kb, n & 1, s_cur);
+      ld.store_k(sm, n & 1);
+      ld.store_v(sm, (n + 1) & 1);
       __syncthreads();
-    }
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int st = 0; st < NS; ++st) s_cur[qt][st] = s_nxt[qt][st];
+    };
+    // unmasked blocks, then the (at most a few) masked ones: two loops, so the
+    // accumulators never merge from two code paths inside a loop
+    int n = 0;
+    for (; n < n_plain; ++n) step(std::integral_constant<bool, false>(), n);
+    for (; n < nblk; ++n) step(std::integral_constant<bool, true>(), n);
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
-    const float l_tot = l_run + xor32(l_run);
-    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (row_ok) {
-      T* orow = og + (size_t)(q0 + rq) * qstride + (size_t)h * D;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const float l_tot = l_run[qt] + xor32(l_run[qt]);
+      const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const int d0 = 32 * dt + 8 * a4 + 4 * hh;
-          float o0 = acc[dt][4 * a4 + 0] * inv_l, o1 = acc[dt][4 * a4 + 1] * inv_l;
-          float o2 = acc[dt][4 * a4 + 2] * inv_l, o3 = acc[dt][4 * a4 + 3] * inv_l;
+          const float o0 = acc[qt][dt][4 * a4 + 0] * inv_l, o1 = acc[qt][dt][4 * a4 + 1] * inv_l;
+          const float o2 = acc[qt][dt][4 * a4 + 2] * inv_l, o3 = acc[qt][dt][4 * a4 + 3] * inv_l;
+          // rows < 0 fall outside the resource: the store is dropped
           if constexpr (BF16) {
-            u32x2_t w = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-            *(u32x2_t*)(orow + d0) = w;
+            buf_store8((u32x2_t){pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)}, ores, rq[qt] * qrow_bytes + d0 * 2);
           } else {
-            *(f32x4_t*)(orow + d0) = (f32x4_t){o0, o1, o2, o3};
+            buf_store16((u32x4_t){__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2),
+                                  __float_as_uint(o3)}, ores, rq[qt] * qrow_bytes + d0 * 4);
           }
         }
-      if (hh == 0) {
-        const float lse = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
-        a.lse[(size_t)h * a.total_q + q0 + rq] = lse;
+      if (rq[qt] >= 0 && hh == 0) {
+        const float lse = l_tot > 0.f ? (m_run[qt] + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+        a.lse[(size_t)h * a.total_q + q0 + rq[qt]] = lse;
       }
     }
   }
@@ -399,7 +518,10 @@ static hipError_t launch_fwd_d(const FwdArgs& a, int64_t grid, hipStream_t st) {
                   : launch_fwd_t<BF16, D, false, false>(a, grid, st);
 }
 
-int fwd_block_m() { return BM; }
+int fwd_block_m(bool bf16, int d) {
+  if (bf16) return d == 64 ? block_m<true, 64>() : block_m<true, 128>();
+  return d == 64 ? block_m<false, 64>() : block_m<false, 128>();
+}
 
 hipError_t launch_fwd(const FwdArgs& a, int64_t grid, hipStream_t st) {
   if (a.bf16) return a.d == 64 ? launch_fwd_d<true, 64>(a, grid, st) : launch_fwd_d<true, 128>(a, grid, st);

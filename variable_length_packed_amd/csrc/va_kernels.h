@@ -60,7 +60,7 @@ void timing_after(hipStream_t st);
 // Persistent grids: min(max_items, resident workgroups per device).
 int resident_grid(const void* kernel, int threads, int64_t max_items);
 
-int fwd_block_m();
+int fwd_block_m(bool bf16, int d);
 hipError_t launch_fwd(const FwdArgs& a, int64_t max_items, hipStream_t st);
 
 int bwd_block_q();
