@@ -7,17 +7,27 @@
 //   dV  = P^T dO,  dK = scale * dS^T Q,  dQ = scale * dS K
 //
 // dK/dV kernel: a workgroup owns 128 keys (32 per wave) of one sequence and
-// KV head; K and V stay in registers, and the workgroup walks the query
+// KV head; K and V stay in registers while the workgroup walks the 32-query
 // blocks (and the query heads of its GQA group) that see those keys, staging
-// Q and dO in LDS both as rows and transposed (for the contractions over
-// queries).  When the group's heads are split over several workgroups, each
-// writes float32 partial sums to the workspace and a reduce kernel adds them
-// in a fixed order, so results never depend on scheduling.
+// Q and dO in LDS both as rows (for S and dP) and transposed (for the
+// contractions over queries).  When the group's heads are split over several
+// workgroups, each writes float32 partial sums to the workspace and a reduce
+// kernel adds them in a fixed order, so results never depend on scheduling.
 //
 // dQ kernel: shaped like the forward.  A workgroup owns 128 query rows of one
-// head; Q and dO stay in registers; the score tile is computed transposed
-// (keys x queries) so each lane holds one query row, and dS^T feeds the dQ^T
+// head; Q and dO stay in registers; score tiles are computed transposed (keys
+// x queries) so each lane holds one query row and dS^T feeds the dQ^T
 // contraction straight from registers.
+//
+// No mask is needed for a key past the sequence (its K and V read as zero and
+// its dK/dV row is never stored; in dQ its zero K row adds nothing) or for a
+// query row past it (its staged LSE is +inf, so its P is 0).  Only tiles that
+// cross the causal diagonal take the masked path, in a loop of their own.
+//
+// bf16: P and dS are rounded to bf16 for the MFMA.  For dV and dK the rounding
+// error of that operand is carried by a second bf16 operand (the residual
+// x - bf16(x)), so those two contractions are exact to float32 accumulation;
+// dQ uses the plain rounding.
 #include "va_common.h"
 #include "va_kernels.h"
 
@@ -26,47 +36,46 @@ namespace va {
 namespace {
 
 constexpr int NT = 256;
-constexpr int BNK = 128;  // keys per dK/dV workgroup
+constexpr int BNK = 128;     // keys per dK/dV workgroup
 constexpr int BMQ_DQ = 128;  // query rows per dQ workgroup
 
 template <bool BF16>
 using elem_t = typename std::conditional<BF16, uint16_t, float>::type;
 
-// Row r (0..) position inside a transposed bf16 LDS row: bits 2 and 3 of r
-// swapped, so the 8 k-slots of a lane half are contiguous (see va_fwd.hip).
+// Row r's position inside a transposed bf16 LDS row (bits 2 and 3 swapped so
+// the 8 k-slots of a lane half are contiguous), and the XOR swizzle of the
+// 16-byte chunks of transposed row d (spreads the transposing stores and the
+// fragment reads over the LDS banks).
 __device__ __forceinline__ int tpos(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
+template <int ROWS>
+__device__ __forceinline__ int tswz(int d) { return ((d >> 3) & (ROWS / 8 - 1)) << 3; }
 
-// Stages a [ROWS][D] block of a token-major tensor into LDS: as rows
-// ([ROWS][D + pad]) and, for bf16, transposed ([D][ROWS + pad], rows permuted
-// by tpos).  Each thread owns pairs of consecutive rows of one 16-byte column
-// chunk so the transposed store can pair them.
+// Stages a [ROWS][D] block (rows row0 .. of a buffer resource; rows outside
+// read as zero) into LDS as rows ([ROWS][D + pad]) and, for bf16, transposed
+// ([D][ROWS + pad], swizzled).  Each thread owns pairs of consecutive rows of
+// one 16-byte chunk, so the transposed store can pair them.
 template <bool BF16, int ROWS, int D, bool TRANS>
 struct Stager {
   using T = elem_t<BF16>;
   static constexpr int EPV = 16 / sizeof(T);
-  static constexpr int CH = D / EPV;                 // 16-byte chunks per row
-  static constexpr int PAIRS = (ROWS / 2) * CH;      // tasks
-  static constexpr int TPT = (PAIRS + NT - 1) / NT;  // tasks per thread
+  static constexpr int CH = D / EPV;                     // 16-byte chunks per row
+  static constexpr int PAIRS = (ROWS / 2) * CH;          // tasks
+  static constexpr int TPT = (PAIRS + NT - 1) / NT;      // tasks per thread
   static constexpr int NP = D + 16 / (int)sizeof(T);     // row pitch (elements)
   static constexpr int TP = ROWS + 16 / (int)sizeof(T);  // transposed pitch
+  static_assert(PAIRS % NT == 0 || PAIRS < NT, "stager tasks");
   u32x4_t r[2 * TPT];
 
-  __device__ __forceinline__ void load(const T* __restrict__ base, size_t row_stride, int row0,
-                                       int rhi) {
+  __device__ __forceinline__ void load(rsrc_t res, int row_bytes, int row0) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int u = threadIdx.x + i * NT;
+      if (PAIRS < NT && u >= PAIRS) continue;
       const int c = u % CH, p = u / CH;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int row = row0 + 2 * p + e;
-        u32x4_t z = {0, 0, 0, 0};
-        if (u < PAIRS && row >= 0 && row < rhi)
-          z = *(const u32x4_t*)(base + (size_t)row * row_stride + c * EPV);
-        r[2 * i + e] = z;
-      }
+      for (int e = 0; e < 2; ++e) r[2 * i + e] = buf_load16(res, (row0 + 2 * p + e) * row_bytes + c * 16);
     }
   }
 
@@ -74,17 +83,17 @@ struct Stager {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int u = threadIdx.x + i * NT;
-      if (u >= PAIRS) continue;
+      if (PAIRS < NT && u >= PAIRS) continue;
       const int c = u % CH, p = u / CH;
       *(u32x4_t*)(dn + (2 * p) * NP + c * EPV) = r[2 * i];
       *(u32x4_t*)(dn + (2 * p + 1) * NP + c * EPV) = r[2 * i + 1];
       if constexpr (BF16 && TRANS) {
-        const int pos = tpos(2 * p);
+        const int pos = tpos(2 * p) ^ tswz<ROWS>(c * 8);  // rows c*8 .. c*8+7 share the swizzle
         const u32x4_t a = r[2 * i], b = r[2 * i + 1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          uint32_t lo = (a[e] & 0xFFFFu) | (b[e] << 16);
-          uint32_t hi = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
+          const uint32_t lo = (a[e] & 0xFFFFu) | (b[e] << 16);
+          const uint32_t hi = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
           *(uint32_t*)(dt + (c * 8 + 2 * e) * TP + pos) = lo;
           *(uint32_t*)(dt + (c * 8 + 2 * e + 1) * TP + pos) = hi;
         }
@@ -93,29 +102,30 @@ struct Stager {
   }
 };
 
-// Register fragment of one row (this lane's row) for the "other" operand of
-// a 32x32 MFMA contracting over head_dim: bf16 -> D/16 vectors of 8; f32 ->
-// D/2 scalars with k-slot (group G, step j) of lane half hh = dim 8G+4hh+j.
+// 16-byte fragment of transposed row d (k-slot chunk kc of lane half hh).
+template <int ROWS, int TP>
+__device__ __forceinline__ u32x4_t tfrag(const uint16_t* t, int d, int kc, int hh) {
+  return *(const u32x4_t*)(t + d * TP + ((16 * kc + 8 * hh) ^ tswz<ROWS>(d)));
+}
+
+// Register fragment of this lane's row for the "other" operand of a 32x32
+// MFMA contracting over head_dim: bf16 -> D/16 vectors of 8; f32 -> D/2
+// scalars with k-slot (group G, step j) of lane half hh = dim 8G+4hh+j.
 template <bool BF16, int D>
 struct RowFrag {
   static constexpr int N = BF16 ? D / 16 : D / 2;
   u32x4_t b[BF16 ? N : 1];
   float f[BF16 ? 1 : N];
-  __device__ __forceinline__ void load(const elem_t<BF16>* row, bool ok, int hh) {
+  __device__ __forceinline__ void load(rsrc_t res, int row_bytes, int row, int hh) {
     if constexpr (BF16) {
 #pragma unroll
-      for (int ks = 0; ks < N; ++ks) {
-        u32x4_t z = {0, 0, 0, 0};
-        if (ok) z = *(const u32x4_t*)(row + 16 * ks + 8 * hh);
-        b[ks] = z;
-      }
+      for (int ks = 0; ks < N; ++ks) b[ks] = buf_load16(res, row * row_bytes + (16 * ks + 8 * hh) * 2);
     } else {
 #pragma unroll
       for (int G = 0; G < D / 8; ++G) {
-        f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        if (ok) z = *(const f32x4_t*)(row + 8 * G + 4 * hh);
+        const u32x4_t z = buf_load16(res, row * row_bytes + (8 * G + 4 * hh) * 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) f[4 * G + j] = z[j];
+        for (int j = 0; j < 4; ++j) f[4 * G + j] = __uint_as_float(z[j]);
       }
     }
   }
@@ -129,13 +139,13 @@ __device__ __forceinline__ f32x16_t mm_rows(const elem_t<BF16>* lrow, const RowF
   if constexpr (BF16) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      u32x4_t a = *(const u32x4_t*)(lrow + 16 * ks + 8 * hh);
+      const u32x4_t a = *(const u32x4_t*)(lrow + 16 * ks + 8 * hh);
       acc = mfma32_bf16(a, fr.b[ks], acc);
     }
   } else {
 #pragma unroll
     for (int G = 0; G < D / 8; ++G) {
-      f32x4_t a = *(const f32x4_t*)(lrow + 8 * G + 4 * hh);
+      const f32x4_t a = *(const f32x4_t*)(lrow + 8 * G + 4 * hh);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc = mfma32_f32(a[j], fr.f[4 * G + j], acc);
     }
@@ -145,6 +155,19 @@ __device__ __forceinline__ f32x16_t mm_rows(const elem_t<BF16>* lrow, const RowF
 
 __device__ __forceinline__ float ld_bias(const uint16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float ld_bias(const float* p) { return *p; }
+
+// bf16 operand of 8 values and, optionally, the bf16 residual of the same 8.
+__device__ __forceinline__ void pack8(const float* v, u32x4_t& hi, u32x4_t* lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+    if (lo) {
+      const float r0 = v[2 * e] - __uint_as_float(hi[e] << 16);
+      const float r1 = v[2 * e + 1] - __uint_as_float(hi[e] & 0xFFFF0000u);
+      (*lo)[e] = pack_bf16x2(r0, r1);
+    }
+  }
+}
 
 // ---------------------------------------------------------------- preprocess
 template <bool BF16, int D>
@@ -182,10 +205,11 @@ __global__ __launch_bounds__(NT) void dsum_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK / dV
+constexpr int BMQ = 32;  // queries per dK/dV block
+
 template <bool BF16, int D>
 struct DkdvSmem {
   using T = elem_t<BF16>;
-  static constexpr int BMQ = D == 128 ? 32 : 64;
   using St = Stager<BF16, BMQ, D, true>;
   T qn[2][BMQ * St::NP];
   T dn[2][BMQ * St::NP];
@@ -195,14 +219,16 @@ struct DkdvSmem {
   float dsum[2][BMQ];
 };
 
+template <bool BF16, int D>
+constexpr int dkdv_min_blocks() { return D == 64 ? 2 : 1; }
+
 template <bool BF16, int D, bool CAUSAL, bool HAS_BIAS>
-__global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a, int hsplit, float* part) {
+__global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(BwdArgs a, int hsplit, float* part) {
   using T = elem_t<BF16>;
   using SM = DkdvSmem<BF16, D>;
-  constexpr int BMQ = SM::BMQ;
-  constexpr int NQ = BMQ / 32;  // 32-query score tiles per block
-  constexpr int DT = D / 32;
   using St = typename SM::St;
+  constexpr int DT = D / 32;
+  constexpr int ELT = (int)sizeof(T);
 
   __shared__ SchedShared sched;
   __shared__ SM sm;
@@ -214,6 +240,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a, int hsplit, floa
   const int per_tile = a.hkv * hsplit;
   const int total_items = sched.total_tiles * per_tile;
   const size_t qstride = (size_t)a.hq * D, kstride = (size_t)a.hkv * D;
+  const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
   const int hpw = a.n_rep / hsplit;  // query heads per workgroup
 
   for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
@@ -230,39 +257,47 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a, int hsplit, floa
     const int kt0 = t * BNK;
     const int wk0 = kt0 + 32 * wid;  // first key of this wave
     const int kj = wk0 + r32;        // this lane's key (columns of the score tile)
-    const bool key_ok = kj < Lk;
     const bool wave_keys = wk0 < Lk;
 
+    const size_t koff = (size_t)k0 * kstride + (size_t)g * D;
+    const int64_t kbytes = Lk > 0 ? (int64_t)(Lk - 1) * krow_bytes + D * ELT : 0;
     RowFrag<BF16, D> kf, vf;
-    {
-      const T* krow = (const T*)a.k + (size_t)(k0 + min(kj, max(Lk - 1, 0))) * kstride + (size_t)g * D;
-      const T* vrow = (const T*)a.v + (size_t)(k0 + min(kj, max(Lk - 1, 0))) * kstride + (size_t)g * D;
-      kf.load(krow, key_ok, hh);
-      vf.load(vrow, key_ok, hh);
-    }
+    kf.load(make_rsrc((const T*)a.k + koff, kbytes), krow_bytes, kj, hh);
+    vf.load(make_rsrc((const T*)a.v + koff, kbytes), krow_bytes, kj, hh);
     f32x16_t dk[DT], dv[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) { dk[i] = (f32x16_t){}; dv[i] = (f32x16_t){}; }
 
-    // queries that can see key kt0: i + off >= kt0
+    // query blocks that can see a key of the tile: i + off >= kt0 (causal)
     const int qs = CAUSAL ? max(0, kt0 - off) : 0;
     const int nqb = qs < Lq ? (Lq - qs + BMQ - 1) / BMQ : 0;
-    const int niter = nqb * hpw;
+    // blocks crossing the diagonal for some wave: qb + off < kt0 + BNK - 1
+    const int n_diag = CAUSAL ? min(nqb, max(0, (kt0 + BNK - 1 - off - qs + BMQ - 1) / BMQ)) : 0;
+    const int k_masked = hpw * n_diag, k_total = hpw * nqb;
     const int h_first = g * a.n_rep + sp * hpw;
+    auto tile_of = [&](int k, int& r, int& n) {
+      if (k < k_masked) { r = k / n_diag; n = k - r * n_diag; }
+      else { const int nu = nqb - n_diag, kk = k - k_masked; r = kk / nu; n = n_diag + (kk - r * nu); }
+    };
 
     St sq, sd;
-    float pl = 0.f, pd = 0.f;  // staged lse2 / dsum for thread tid < BMQ
-    auto issue = [&](int it) {
-      const int r = it / nqb, n = it - r * nqb;
+    float pl = 0.f, pd = 0.f;  // staged lse2 / dsum of query tid (tid < BMQ)
+    auto issue = [&](int k) {
+      int r, n;
+      tile_of(k, r, n);
       const int h = h_first + r;
       const int qb = qs + n * BMQ;
-      sq.load((const T*)a.q + (size_t)q0 * qstride + (size_t)h * D, qstride, qb, Lq);
-      sd.load((const T*)a.dout + (size_t)q0 * qstride + (size_t)h * D, qstride, qb, Lq);
+      const size_t qoff = (size_t)q0 * qstride + (size_t)h * D;
+      const int64_t qbytes = Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0;
+      sq.load(make_rsrc((const T*)a.q + qoff, qbytes), qrow_bytes, qb);
+      sd.load(make_rsrc((const T*)a.dout + qoff, qbytes), qrow_bytes, qb);
       if (tid < BMQ) {
         const int i = qb + tid;
-        pl = 0.f; pd = 0.f;
+        pl = INFINITY;  // rows past the sequence: P = exp2(x - inf) = 0
+        pd = 0.f;
         if (i < Lq) {
-          pl = a.lse[(size_t)h * a.total_q + q0 + i] * kLog2e;
+          const float l = a.lse[(size_t)h * a.total_q + q0 + i];
+          pl = l == -INFINITY ? INFINITY : l * kLog2e;  // a row that sees nothing adds nothing
           pd = a.dsum[(size_t)h * a.total_q + q0 + i];
         }
       }
@@ -273,96 +308,93 @@ __global__ __launch_bounds__(NT, 1) void dkdv_kernel(BwdArgs a, int hsplit, floa
       if (tid < BMQ) { sm.lse2[buf][tid] = pl; sm.dsum[buf][tid] = pd; }
     };
 
-    if (niter > 0) { issue(0); commit(0); }
-    __syncthreads();
-    for (int it = 0; it < niter; ++it) {
-      const int buf = it & 1;
-      const int r = it / nqb, n = it - r * nqb;
+    auto step = [&](auto mask_tag, int k) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int buf = k & 1;
+      int r, n;
+      tile_of(k, r, n);
       const int h = h_first + r;
       const int qb = qs + n * BMQ;
-      if (it + 1 < niter) issue(it + 1);
+      if (k + 1 < k_total) issue(k + 1);
       // this wave's keys are seen by queries i >= wk0 - off
       const bool active = wave_keys && (!CAUSAL || qb + BMQ - 1 + off >= wk0);
       if (active) {
-        const bool need_mask = (qb + BMQ > Lq) || (wk0 + 32 > Lk) || (CAUSAL && qb + off < wk0 + 31);
+        // S = Q K^T and dP = dO V^T: C[query][key], lane = key
+        f32x16_t s = mm_rows<BF16, D>(&sm.qn[buf][r32 * St::NP], kf, (f32x16_t){}, hh);
+        f32x16_t dp = mm_rows<BF16, D>(&sm.dn[buf][r32 * St::NP], vf, (f32x16_t){}, hh);
         const T* bias_h = nullptr;
         if constexpr (HAS_BIAS)
           bias_h = (const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1 + (int64_t)kj * a.bs3;
-        f32x16_t p[NQ], ds[NQ];
+        // causal: key kj is visible to query qb + ql iff ql >= kj - off - qb
+        const int thr = kj - off - qb - 4 * hh;
+        float p[16], ds[16];
 #pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) {
-          // S = Q K^T and dP = dO V^T: C[query][key], lane = key
-          f32x16_t s = mm_rows<BF16, D>(&sm.qn[buf][(32 * qt + r32) * St::NP], kf, (f32x16_t){}, hh);
-          f32x16_t dp = mm_rows<BF16, D>(&sm.dn[buf][(32 * qt + r32) * St::NP], vf, (f32x16_t){}, hh);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int ql = 32 * qt + 8 * (i >> 2) + 4 * hh + (i & 3);  // query inside block
+        for (int i = 0; i < 16; ++i) {
+          const int cl = 8 * (i >> 2) + (i & 3);  // query inside the block is cl + 4*hh
+          const int ql = cl + 4 * hh;
+          float x = s[i] * a.scale_log2;
+          if constexpr (HAS_BIAS) {
             const int qi = qb + ql;
-            float x = s[i] * a.scale_log2;
-            if constexpr (HAS_BIAS) {
-              if (qi < Lq && key_ok) x = __builtin_fmaf(ld_bias(bias_h + (int64_t)qi * a.bs2), kLog2e, x);
-            }
-            float pv = fast_exp2(x - sm.lse2[buf][ql]);
-            if (need_mask) {
-              const bool ok = qi < Lq && key_ok && (!CAUSAL || kj <= qi + off);
-              pv = ok ? pv : 0.f;
-            }
-            p[qt][i] = pv;
-            ds[qt][i] = pv * (dp[i] - sm.dsum[buf][ql]);
+            if (qi < Lq && kj < Lk) x = __builtin_fmaf(ld_bias(bias_h + (int64_t)qi * a.bs2), kLog2e, x);
           }
+          float pv = fast_exp2(x - sm.lse2[buf][ql]);
+          if constexpr (MASK) pv = cl >= thr ? pv : 0.f;
+          p[i] = pv;
+          ds[i] = pv * (dp[i] - sm.dsum[buf][ql]);
         }
         // dV += P^T dO, dK += dS^T Q: C[key][d], lane = d
         if constexpr (BF16) {
 #pragma unroll
-          for (int qt = 0; qt < NQ; ++qt)
+          for (int c = 0; c < 2; ++c) {
+            u32x4_t pa, pa_lo, da, da_lo;
+            pack8(&p[8 * c], pa, &pa_lo);
+            pack8(&ds[8 * c], da, &da_lo);
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-              u32x4_t pa, da;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                pa[e] = pack_bf16x2(p[qt][8 * c + 2 * e], p[qt][8 * c + 2 * e + 1]);
-                da[e] = pack_bf16x2(ds[qt][8 * c + 2 * e], ds[qt][8 * c + 2 * e + 1]);
-              }
-              const int col = 32 * qt + 16 * c + 8 * hh;
-#pragma unroll
-              for (int dt = 0; dt < DT; ++dt) {
-                u32x4_t ob = *(const u32x4_t*)(&sm.dt[buf][(32 * dt + r32) * St::TP + col]);
-                u32x4_t qb4 = *(const u32x4_t*)(&sm.qt[buf][(32 * dt + r32) * St::TP + col]);
-                dv[dt] = mfma32_bf16(pa, ob, dv[dt]);
-                dk[dt] = mfma32_bf16(da, qb4, dk[dt]);
-              }
+            for (int dt_ = 0; dt_ < DT; ++dt_) {
+              const int d = 32 * dt_ + r32;
+              const u32x4_t ob = tfrag<BMQ, St::TP>(sm.dt[buf], d, c, hh);
+              const u32x4_t qb4 = tfrag<BMQ, St::TP>(sm.qt[buf], d, c, hh);
+              dv[dt_] = mfma32_bf16(pa, ob, dv[dt_]);
+              dv[dt_] = mfma32_bf16(pa_lo, ob, dv[dt_]);
+              dk[dt_] = mfma32_bf16(da, qb4, dk[dt_]);
+              dk[dt_] = mfma32_bf16(da_lo, qb4, dk[dt_]);
             }
+          }
         } else {
 #pragma unroll
-          for (int qt = 0; qt < NQ; ++qt)
+          for (int i = 0; i < 16; ++i) {
+            const int ql = 8 * (i >> 2) + 4 * hh + (i & 3);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int ql = 32 * qt + 8 * (i >> 2) + 4 * hh + (i & 3);
-#pragma unroll
-              for (int dt = 0; dt < DT; ++dt) {
-                const float ob = sm.dn[buf][ql * St::NP + 32 * dt + r32];
-                const float qv = sm.qn[buf][ql * St::NP + 32 * dt + r32];
-                dv[dt] = mfma32_f32(p[qt][i], ob, dv[dt]);
-                dk[dt] = mfma32_f32(ds[qt][i], qv, dk[dt]);
-              }
+            for (int dt_ = 0; dt_ < DT; ++dt_) {
+              const float ob = sm.dn[buf][ql * St::NP + 32 * dt_ + r32];
+              const float qv = sm.qn[buf][ql * St::NP + 32 * dt_ + r32];
+              dv[dt_] = mfma32_f32(p[i], ob, dv[dt_]);
+              dk[dt_] = mfma32_f32(ds[i], qv, dk[dt_]);
             }
+          }
         }
       }
-      if (it + 1 < niter) commit(buf ^ 1);
+      if (k + 1 < k_total) commit(buf ^ 1);
       __syncthreads();
-    }
+    };
+
+    if (k_total > 0) { issue(0); commit(0); }
+    __syncthreads();
+    int k = 0;
+    for (; k < k_masked; ++k) step(std::integral_constant<bool, true>(), k);
+    for (; k < k_total; ++k) step(std::integral_constant<bool, false>(), k);
 
     // ---- epilogue: rows = keys 8(i/4)+4hh+i%4 of the wave, column d = 32dt + r32
+    const size_t plane = (size_t)a.total_k * kstride;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt_ = 0; dt_ < DT; ++dt_)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = wk0 + 8 * (i >> 2) + 4 * hh + (i & 3);
         if (key >= Lk) continue;
-        const size_t o = (size_t)(k0 + key) * kstride + (size_t)g * D + 32 * dt + r32;
-        const float kv = dk[dt][i], vv = dv[dt][i];
+        const size_t o = koff + (size_t)key * kstride + 32 * dt_ + r32;
+        const float kv = dk[dt_][i], vv = dv[dt_][i];
         if (hsplit > 1) {
-          const size_t plane = (size_t)a.total_k * kstride;
           part[(size_t)(2 * sp) * plane + o] = kv;
           part[(size_t)(2 * sp + 1) * plane + o] = vv;
         } else if (a.grad_bf16) {
@@ -416,6 +448,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   constexpr int BN = SM::BN;
   constexpr int NS = BN / 32;
   constexpr int DT = D / 32;
+  constexpr int ELT = (int)sizeof(T);
   using St = typename SM::St;
   using Sv = typename SM::Sv;
 
@@ -428,6 +461,8 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   sched_build(sched, a.cu_q, a.batch, a.total_q, BMQ_DQ, a.tcap_q, a.stride_q, a.nlev_q);
   const int total_items = sched.total_tiles * a.hq;
   const size_t qstride = (size_t)a.hq * D, kstride = (size_t)a.hkv * D;
+  const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
+  const int gelt = a.grad_bf16 ? 2 : 4;
 
   for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
     const int tile = item / a.hq;
@@ -448,65 +483,61 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     const int wave_hi = CAUSAL ? min(Lk, w0 + 32 + off) : Lk;
     const bool wave_on = (w0 + 31 >= 0) && wave_hi > 0;
     const int nblk = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
-    const int kb0 = CAUSAL ? kv_hi - nblk * BN : 0;
+    // blocks start at key 0; those before n_plain are fully visible to every
+    // row of the tile (the smallest row sees keys <= r1 - BMQ_DQ + off)
+    const int n_plain = CAUSAL ? min(max(r1 - BMQ_DQ + off + 1, 0) / BN, nblk) : nblk;
 
+    const size_t qoff = (size_t)q0 * qstride + (size_t)h * D;
+    const int64_t qbytes = Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0;
     RowFrag<BF16, D> qf, of;
-    {
-      const size_t ro = (size_t)(q0 + max(rq, 0)) * qstride + (size_t)h * D;
-      qf.load((const T*)a.q + ro, row_ok, hh);
-      of.load((const T*)a.dout + ro, row_ok, hh);
-    }
+    qf.load(make_rsrc((const T*)a.q + qoff, qbytes), qrow_bytes, rq, hh);
+    of.load(make_rsrc((const T*)a.dout + qoff, qbytes), qrow_bytes, rq, hh);
     float lse2 = 0.f, dsum = 0.f;
     if (row_ok) {
-      lse2 = a.lse[(size_t)h * a.total_q + q0 + rq] * kLog2e;
+      const float l = a.lse[(size_t)h * a.total_q + q0 + rq];
+      lse2 = l == -INFINITY ? INFINITY : l * kLog2e;  // a row that sees nothing adds nothing
       dsum = a.dsum[(size_t)h * a.total_q + q0 + rq];
     }
     f32x16_t acc[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) acc[i] = (f32x16_t){};
 
-    const T* kbase = (const T*)a.k + (size_t)k0 * kstride + (size_t)g * D;
-    const T* vbase = (const T*)a.v + (size_t)k0 * kstride + (size_t)g * D;
+    const size_t koff = (size_t)k0 * kstride + (size_t)g * D;
+    const int64_t kbytes = kv_hi > 0 ? (int64_t)(kv_hi - 1) * krow_bytes + D * ELT : 0;
+    const rsrc_t kres = make_rsrc((const T*)a.k + koff, kbytes);
+    const rsrc_t vres = make_rsrc((const T*)a.v + koff, kbytes);
     const T* bias_bh = nullptr;
     if constexpr (HAS_BIAS)
       bias_bh = (const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1 + (int64_t)max(rq, 0) * a.bs2;
+    const int hi_row = CAUSAL ? min(kv_hi - 1, rq + off) : kv_hi - 1;
 
     St sk;
     Sv sv;
-    if (nblk > 0) {
-      sk.load(kbase, kstride, kb0, kv_hi);
-      sv.load(vbase, kstride, kb0, kv_hi);
-      sk.store(sm.kn[0], sm.kt[0]);
-      sv.store(sm.vn[0], nullptr);
-    }
-    __syncthreads();
-    for (int n = 0; n < nblk; ++n) {
-      const int kb = kb0 + n * BN;
+    auto step = [&](auto mask_tag, int n) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int kb = n * BN;
       const int buf = n & 1;
       if (n + 1 < nblk) {
-        sk.load(kbase, kstride, kb + BN, kv_hi);
-        sv.load(vbase, kstride, kb + BN, kv_hi);
+        sk.load(kres, krow_bytes, kb + BN);
+        sv.load(vres, krow_bytes, kb + BN);
       }
       if (wave_on && kb < wave_hi) {
-        const bool need_mask = (kb < 0) || (kb + BN > kv_hi) || (CAUSAL && (kb + BN - 1 > w0 + off));
         float dsv[16 * NS];
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           // S^T = K Q^T, dP^T = V dO^T: C[key][query], lane = query
-          f32x16_t s = mm_rows<BF16, D>(&sm.kn[buf][(32 * st + r32) * St::NP], qf, (f32x16_t){}, hh);
-          f32x16_t dp = mm_rows<BF16, D>(&sm.vn[buf][(32 * st + r32) * St::NP], of, (f32x16_t){}, hh);
+          const f32x16_t s = mm_rows<BF16, D>(&sm.kn[buf][(32 * st + r32) * St::NP], qf, (f32x16_t){}, hh);
+          const f32x16_t dp = mm_rows<BF16, D>(&sm.vn[buf][(32 * st + r32) * St::NP], of, (f32x16_t){}, hh);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int kj = kb + 32 * st + 8 * (i >> 2) + 4 * hh + (i & 3);
+            const int ci = 32 * st + 8 * (i >> 2) + (i & 3);
+            const int kj = kb + ci + 4 * hh;
             float x = s[i] * a.scale_log2;
             if constexpr (HAS_BIAS) {
-              if (row_ok && kj >= 0 && kj < Lk) x = __builtin_fmaf(ld_bias(bias_bh + (int64_t)kj * a.bs3), kLog2e, x);
+              if (row_ok && kj < Lk) x = __builtin_fmaf(ld_bias(bias_bh + (int64_t)kj * a.bs3), kLog2e, x);
             }
             float pv = fast_exp2(x - lse2);
-            if (need_mask) {
-              const bool ok = row_ok && kj >= 0 && kj < kv_hi && (!CAUSAL || kj <= rq + off);
-              pv = ok ? pv : 0.f;
-            }
+            if constexpr (MASK) pv = kj <= hi_row ? pv : 0.f;
             dsv[16 * st + i] = pv * (dp[i] - dsum);
           }
         }
@@ -515,13 +546,10 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int kc = 0; kc < 2 * NS; ++kc) {
             u32x4_t pb;
+            pack8(&dsv[8 * kc], pb, nullptr);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pb[e] = pack_bf16x2(dsv[8 * kc + 2 * e], dsv[8 * kc + 2 * e + 1]);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-              u32x4_t ka = *(const u32x4_t*)(&sm.kt[buf][(32 * dt + r32) * St::TP + 16 * kc + 8 * hh]);
-              acc[dt] = mfma32_bf16(ka, pb, acc[dt]);
-            }
+            for (int dt_ = 0; dt_ < DT; ++dt_)
+              acc[dt_] = mfma32_bf16(tfrag<BN, St::TP>(sm.kt[buf], 32 * dt_ + r32, kc, hh), pb, acc[dt_]);
           }
         } else {
 #pragma unroll
@@ -530,9 +558,9 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
             for (int i = 0; i < 16; ++i) {
               const int key = 32 * st + 8 * (i >> 2) + 4 * hh + (i & 3);
 #pragma unroll
-              for (int dt = 0; dt < DT; ++dt) {
-                const float ka = sm.kn[buf][key * St::NP + 32 * dt + r32];
-                acc[dt] = mfma32_f32(ka, dsv[16 * st + i], acc[dt]);
+              for (int dt_ = 0; dt_ < DT; ++dt_) {
+                const float ka = sm.kn[buf][key * St::NP + 32 * dt_ + r32];
+                acc[dt_] = mfma32_f32(ka, dsv[16 * st + i], acc[dt_]);
               }
             }
         }
@@ -542,24 +570,37 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
         sv.store(sm.vn[buf ^ 1], nullptr);
       }
       __syncthreads();
-    }
+    };
 
-    if (row_ok) {
-      const size_t ro = (size_t)(q0 + rq) * qstride + (size_t)h * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int d0 = 32 * dt + 8 * a4 + 4 * hh;
-          const float o0 = acc[dt][4 * a4 + 0] * a.scale, o1 = acc[dt][4 * a4 + 1] * a.scale;
-          const float o2 = acc[dt][4 * a4 + 2] * a.scale, o3 = acc[dt][4 * a4 + 3] * a.scale;
-          if (a.grad_bf16) {
-            *(u32x2_t*)((uint16_t*)a.dq + ro + d0) = (u32x2_t){pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-          } else {
-            *(f32x4_t*)((float*)a.dq + ro + d0) = (f32x4_t){o0, o1, o2, o3};
-          }
-        }
+    if (nblk > 0) {
+      sk.load(kres, krow_bytes, 0);
+      sv.load(vres, krow_bytes, 0);
+      sk.store(sm.kn[0], sm.kt[0]);
+      sv.store(sm.vn[0], nullptr);
     }
+    __syncthreads();
+    int n = 0;
+    for (; n < n_plain; ++n) step(std::integral_constant<bool, false>(), n);
+    for (; n < nblk; ++n) step(std::integral_constant<bool, true>(), n);
+
+    // rows < 0 fall outside the resource: their stores are dropped
+    const int dq_row_bytes = (int)qstride * gelt;
+    const rsrc_t dqres = make_rsrc((uint8_t*)a.dq + qoff * gelt,
+                                   Lq > 0 ? (int64_t)(Lq - 1) * dq_row_bytes + D * gelt : 0);
+#pragma unroll
+    for (int dt_ = 0; dt_ < DT; ++dt_)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = 32 * dt_ + 8 * a4 + 4 * hh;
+        const float o0 = acc[dt_][4 * a4 + 0] * a.scale, o1 = acc[dt_][4 * a4 + 1] * a.scale;
+        const float o2 = acc[dt_][4 * a4 + 2] * a.scale, o3 = acc[dt_][4 * a4 + 3] * a.scale;
+        if (a.grad_bf16) {
+          buf_store8((u32x2_t){pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)}, dqres, rq * dq_row_bytes + d0 * 2);
+        } else {
+          buf_store16((u32x4_t){__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2),
+                                __float_as_uint(o3)}, dqres, rq * dq_row_bytes + d0 * 4);
+        }
+      }
   }
 }
 
