@@ -52,13 +52,13 @@ def algorithmic_flops(w, kernel: str) -> int:
     """Non-padded FLOPs one launch of `kernel` must do (recomputation not counted)."""
     pairs = count.workload_pairs(w.lens_q, w.lens_k, w.causal)
     unit = 2 * w.d * w.hq * pairs  # one contraction over all visible pairs
-    if kernel.startswith("fwd"):
+    if kernel in ("fwd_bf16", "fwd_f32"):
         return 2 * unit          # S = QK^T, O = PV
-    if kernel.startswith("bwd_dkdv") and not kernel.endswith("reduce"):
+    if kernel in ("bwd_dkdv_bf16", "bwd_dkdv_f32"):
         return 4 * unit          # S (counted once), dP, dV, dK
-    if kernel.startswith("bwd_dq"):
+    if kernel in ("bwd_dq_bf16", "bwd_dq_f32"):
         return 1 * unit          # dQ only; its S and dP recompute are not counted
-    return 0
+    return 0                     # planner, merges, D = rowsum(dO * O)
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -146,13 +146,17 @@ def main() -> int:
     dq = torch.empty(x["q"].shape, dtype=torch.float32, device=dev)
     dk = torch.empty(x["k"].shape, dtype=torch.float32, device=dev)
     dv = torch.empty(x["v"].shape, dtype=torch.float32, device=dev)
-    ws = torch.empty(va.va_varlen_bwd_workspace_size(w.batch, w.total_q, w.total_k, w.hq, w.hkv,
-                                                     w.d, x["q"].dtype, torch.float32),
+    ws = torch.empty(va.va_varlen_bwd_workspace_size(w.batch, w.total_q, w.total_k, w.max_q,
+                                                     w.max_k, w.hq, w.hkv, w.d, x["q"].dtype,
+                                                     torch.float32),
                      dtype=torch.uint8, device=dev)
+    wsf = torch.empty(va.va_varlen_fwd_workspace_size(w.batch, w.total_q, w.total_k, w.max_q,
+                                                      w.max_k, w.hq, w.hkv, w.d, x["q"].dtype),
+                      dtype=torch.uint8, device=dev)
 
     def fwd():
         va.va_varlen_fwd(x["q"], x["k"], x["v"], x["cu_q"], x["cu_k"], w.max_q, w.max_k, w.scale,
-                         w.causal, x["bias"], bstr, out=out, lse=lse)
+                         w.causal, x["bias"], bstr, out=out, lse=lse, workspace=wsf)
 
     def bwd():
         va.va_varlen_bwd(x["dout"], x["q"], x["k"], x["v"], out, lse, x["cu_q"], x["cu_k"],
@@ -193,7 +197,8 @@ def main() -> int:
         fl = algorithmic_flops(w, name)
         kernels[name] = {"launches": n, "avg_ms": round(avg, 5),
                          "tflops": round(fl / (avg * 1e-3) / 1e12, 2) if fl else None}
-    dom = max(kt.items(), key=lambda kv: kv[1][1])[0] if kt else None
+    timed_kernels = {k: v for k, v in kt.items() if algorithmic_flops(w, k) > 0}
+    dom = max(timed_kernels.items(), key=lambda kv: kv[1][1])[0] if timed_kernels else None
     roof = None
     if dom is not None:
         n, tot = kt[dom]

@@ -45,6 +45,18 @@
  * review flags is avoided by construction).  Outputs are fully overwritten
  * (zeros for empty rows); they are valid for later work on `stream`.
  *
+ * Workspace.  Each call first runs a planner kernel that reads cu_seqlens on
+ * the device and writes, into the workspace, the list of work units of each
+ * pass sorted by cost, so that the persistent workgroups take the heaviest
+ * units first.  A query tile that sees more than 1024 keys (a key tile seen
+ * by more than 768 query-row x head pairs in the backward) is split into
+ * units whose float32 partial results are merged in a fixed order.  The rule
+ * depends only on the tile's own sequence, so results are deterministic and a
+ * sequence's results do not depend on the other sequences of the batch --
+ * unless the batch would need more partial slots than the workspace's fixed
+ * budget, in which case it is planned without splitting.  Contents need no
+ * initialisation; a workspace must not be shared by calls that may overlap.
+ *
  * Errors.  A non-VA_OK return means nothing was enqueued; va_last_error()
  * then holds a message for the calling thread.  Invalid device metadata
  * (cu_seqlens not monotone, cu[batch] != total, a length above max_seqlen)
@@ -65,7 +77,7 @@ typedef enum {
   VA_OK = 0,
   VA_ERR_INVALID = 1,     /* null pointer, zero/negative size, Hq % Hkv != 0, bad stride */
   VA_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, unknown dtype, bf16 grads of fp32 inputs */
-  VA_ERR_WORKSPACE = 3,   /* workspace smaller than va_varlen_bwd_workspace_size() */
+  VA_ERR_WORKSPACE = 3,   /* workspace smaller than va_varlen_{fwd,bwd}_workspace_size() */
   VA_ERR_HIP = 4          /* the HIP runtime reported an error; text in va_last_error() */
 } va_status;
 
@@ -83,15 +95,21 @@ typedef void* va_stream;
  *   q, k, v            device, `dtype`, layouts above
  *   cu_seqlens_q/_k    device int32 [batch + 1]
  *   max_seqlen_q/_k    host upper bounds on Lq_b / Lk_b (>= 1); they size the
- *                      tile schedule, never the results
- *   softmax_scale      multiplies Q K^T (callers usually pass 1/sqrt(head_dim))
+ *                      workspace, never the results (a bound that is too small
+ *                      only disables splitting)
+ *   softmax_scale      multiplies Q K^T (callers usually pass 1/sqrt(head_dim));
+ *                      must be finite and > 0
  *   causal             0 or 1; 1 = bottom-right aligned causal mask
  *   bias, bias_stride  both NULL (no bias) or both non-NULL
+ *   workspace          device scratch of at least va_varlen_fwd_workspace_size()
+ *                      bytes, 256-byte aligned
  *   head_dim           64 or 128
  * Returns VA_ERR_INVALID for a NULL required pointer, exactly one of
  * bias/bias_stride NULL, batch/total/heads/head_dim <= 0, Hq % Hkv != 0,
- * max_seqlen <= 0, a negative stride; VA_ERR_UNSUPPORTED for head_dim not in
- * {64, 128} or an unknown dtype; VA_ERR_HIP if the launch fails.
+ * max_seqlen <= 0, a negative stride, a scale that is not finite and > 0, a
+ * misaligned workspace; VA_ERR_UNSUPPORTED for head_dim not in {64, 128} or
+ * an unknown dtype; VA_ERR_WORKSPACE for too small a workspace; VA_ERR_HIP
+ * if a launch fails.
  */
 va_status va_varlen_fwd(const void* q, const void* k, const void* v,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -99,16 +117,22 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
                         float softmax_scale, int causal,
                         const void* bias, const int64_t* bias_stride,
                         void* out, float* lse,
+                        void* workspace, size_t workspace_bytes,
                         int32_t batch, int32_t total_q, int32_t total_k,
                         int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                         va_dtype dtype, va_stream stream);
 
 /*
- * Bytes of device workspace va_varlen_bwd needs for these sizes (256-byte
- * aligned pointer required).  Returns 0 for arguments va_varlen_bwd would
- * reject.  Pure host arithmetic.
+ * Bytes of device workspace va_varlen_fwd / va_varlen_bwd need for these
+ * sizes (256-byte aligned pointer required).  Return 0 for arguments the call
+ * would reject.  Pure host arithmetic.
  */
+size_t va_varlen_fwd_workspace_size(int32_t batch, int32_t total_q, int32_t total_k,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t num_heads_q, int32_t num_heads_kv,
+                                    int32_t head_dim, va_dtype dtype);
 size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t total_k,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
                                     int32_t num_heads_q, int32_t num_heads_kv,
                                     int32_t head_dim, va_dtype dtype, va_dtype grad_dtype);
 
@@ -122,10 +146,10 @@ size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
  *   dk, dv             [total_k, num_heads_kv, head_dim] in grad_dtype; the
  *                      query heads of a GQA group are summed
  *   workspace          device scratch of at least va_varlen_bwd_workspace_size()
- *                      bytes, 256-byte aligned; contents need no initialisation
+ *                      bytes, 256-byte aligned
  *   grad_dtype         VA_F32, or VA_BF16 when dtype is VA_BF16
  * Deterministic: a call's results do not depend on scheduling (no atomics on
- * values).  Errors as for the forward, plus VA_ERR_WORKSPACE, and
+ * values; split tiles are summed in a fixed order).  Errors as for the forward, plus VA_ERR_WORKSPACE, and
  * VA_ERR_UNSUPPORTED for grad_dtype = VA_BF16 with dtype = VA_F32.
  */
 va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const void* v,

@@ -58,12 +58,13 @@ def test_status_strings_and_version(lib):
 
 def _fwd(lib, **kw):
     a = dict(q=P, k=P, v=P, cq=P, ck=P, mq=8, mk=8, scale=0.125, causal=1, bias=None,
-             bstr=None, out=P, lse=P, batch=2, tq=16, tk=16, hq=4, hkv=2, d=64, dt=BF16)
+             bstr=None, out=P, lse=P, ws=0x100000, wsb=1 << 30, batch=2, tq=16, tk=16, hq=4,
+             hkv=2, d=64, dt=BF16)
     a.update(kw)
     bstr = _lib.strides_arg(a["bstr"]) if a["bstr"] is not None else None
     return lib.va_varlen_fwd(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["mq"], a["mk"], a["scale"],
-                             a["causal"], a["bias"], bstr, a["out"], a["lse"], a["batch"], a["tq"],
-                             a["tk"], a["hq"], a["hkv"], a["d"], a["dt"], None)
+                             a["causal"], a["bias"], bstr, a["out"], a["lse"], a["ws"], a["wsb"],
+                             a["batch"], a["tq"], a["tk"], a["hq"], a["hkv"], a["d"], a["dt"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -84,9 +85,12 @@ def _fwd(lib, **kw):
     (dict(bias=P), INVALID),           # bias without strides
     (dict(bstr=(1, 1, 1, 1)), INVALID),  # strides without bias
     (dict(bias=P, bstr=(1, -1, 1, 1)), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(ws=0x100040), INVALID),      # misaligned workspace
     (dict(d=96), UNSUPPORTED),
     (dict(d=256), UNSUPPORTED),
     (dict(dt=7), UNSUPPORTED),
+    (dict(wsb=16), WORKSPACE),
 ])
 def test_fwd_validation(lib, kw, code):
     assert _fwd(lib, **kw) == code
@@ -120,16 +124,48 @@ def test_bwd_validation(lib, kw, code):
     assert _bwd(lib, **kw) == code
 
 
-def test_workspace_size(lib):
+def _r(x):
+    return (x + 255) // 256 * 256
+
+
+def _plan_bytes(units, splits):
+    return 256 + 2 * _r(16 * units) + _r(16 * max(splits, 1))
+
+
+def test_fwd_workspace_size(lib):
+    f = lib.va_varlen_fwd_workspace_size
+    assert f(0, 16, 16, 8, 8, 4, 2, 64, BF16) == 0
+    assert f(2, 16, 16, 0, 8, 4, 2, 64, BF16) == 0
+    assert f(2, 16, 16, 8, 8, 4, 3, 64, BF16) == 0
+    assert f(2, 16, 16, 8, 8, 4, 2, 96, BF16) == 0
+    # no tile can see more than 1024 keys: only the plan (<= total/128 + batch units)
+    assert f(2, 16, 16, 8, 8, 4, 2, 64, BF16) == _plan_bytes(2, 0)
+    assert f(20, 10459, 10459, 1024, 1024, 14, 2, 64, BF16) == _plan_bytes(10459 // 128 + 20, 0)
+    # longer keys: partial slots of hq * 128 rows * (d + 1) floats, two per tile at most
+    tiles = 9687 // 128 + 16
+    slot = 14 * 128 * 65 * 4
+    slots = min(2 * tiles, (64 << 20) // slot)
+    assert f(16, 9687, 9687, 2048, 2048, 14, 2, 64, BF16) == \
+        _plan_bytes(tiles + slots, slots // 2) + _r(slots * slot)
+    # float32 steps are 32 keys, so the same 1024-key chunk is 32 steps
+    assert f(2, 16, 16, 1024, 1024, 4, 2, 64, F32) == _plan_bytes(2, 0)
+
+
+def test_bwd_workspace_size(lib):
     f = lib.va_varlen_bwd_workspace_size
-    assert f(0, 16, 16, 4, 2, 64, BF16, F32) == 0
-    assert f(2, 16, 16, 4, 3, 64, BF16, F32) == 0
-    assert f(2, 16, 16, 4, 2, 96, BF16, F32) == 0
-    assert f(2, 16, 16, 4, 2, 64, F32, BF16) == 0
-    n = f(2, 16, 16, 4, 4, 64, BF16, F32)  # no GQA: only D = rowsum(dO * O)
-    assert n == 256  # 4 heads * 16 rows * 4 bytes, rounded up to 256
-    g = f(2, 16, 16, 4, 2, 64, BF16, F32)  # GQA on a small problem: per-head partial dK/dV
-    assert g == 256 + 2 * 2 * 16 * 2 * 64 * 4
+    assert f(0, 16, 16, 8, 8, 4, 2, 64, BF16, F32) == 0
+    assert f(2, 16, 16, 8, 8, 4, 3, 64, BF16, F32) == 0
+    assert f(2, 16, 16, 8, 8, 4, 2, 96, BF16, F32) == 0
+    assert f(2, 16, 16, 8, 8, 4, 2, 64, F32, BF16) == 0
+    # short sequences: D = rowsum(dO * O) and the two plans (dK/dV and dQ)
+    n = f(2, 16, 16, 8, 8, 4, 4, 64, BF16, F32)
+    assert n == _r(4 * 16 * 4) + 2 * _plan_bytes(2, 0)
+    # GQA 4/2: a dK/dV unit holds at most 768 (query row, head) pairs = 12 blocks of 32
+    assert f(2, 16, 16, 384, 8, 4, 2, 64, BF16, F32) == n
+    big = f(2, 16, 16, 416, 8, 4, 2, 64, BF16, F32)
+    slots_k = 2 * 2  # two tiles, ceil(13 / 12) = 2 chunks each
+    assert big == _r(4 * 16 * 4) + _plan_bytes(2 + slots_k, slots_k // 2) + _plan_bytes(2, 0) + \
+        _r(slots_k * 2 * 2 * 128 * 64 * 4)
 
 
 def test_python_layer_rejects_cpu_tensors_and_bias_grad():

@@ -19,7 +19,7 @@ from . import _gpu
 
 pytestmark = pytest.mark.gpu
 
-LENS = [37, 300, 129, 64, 1000, 5]
+LENS = [37, 300, 129, 64, 1500, 5]  # 1500: split work units in every pass
 
 
 def _run_all(w):
@@ -30,6 +30,9 @@ def _run_all(w):
     return [x.detach().clone() for x in (out, lse, dq, dk, dv)]
 
 
+LENS_BIAS = [37, 300, 129, 64, 1000, 5]  # keeps the per-pair bias grid at 1024 x 1024
+
+
 def _case(seed, lens_q, lens_k=None, bias=False, dtype="bf16"):
     return make_case(seed, lens_q, lens_k=lens_k, hq=14, hkv=2, d=64, causal=True, dtype=dtype,
                      bias="per_pair" if bias else "none", with_dout=True, bias_std=0.5,
@@ -38,10 +41,11 @@ def _case(seed, lens_q, lens_k=None, bias=False, dtype="bf16"):
 
 @pytest.mark.parametrize("bias", [False, True])
 def test_isolation_rewrite_values(bias):
-    w = _case(60, LENS, bias=bias)
+    lens = LENS_BIAS if bias else LENS
+    w = _case(60, lens, bias=bias)
     base = _run_all(w)
-    w2 = _case(61, LENS, bias=bias)  # every value differs ...
-    n0 = LENS[0]
+    w2 = _case(61, lens, bias=bias)  # every value differs ...
+    n0 = lens[0]
     for a, b in ((w2.q, w.q), (w2.k, w.k), (w2.v, w.v), (w2.dout, w.dout)):
         a[n0:] = b[n0:]  # ... except sequences 1.. are copied back
     if bias:

@@ -10,7 +10,9 @@ request 118 page (section "Recommended Automated Tests": lengths such as
 off, causal decode with q_len 1) and the CUDA tests listed on the GiGL pull
 request 858 page (section "Verification": per-key on and off, max_seq_len
 not a multiple of 8, one head with full sequences, permuted-view bias) are
-covered by these cases.
+covered by these cases.  Long sequences exercise the split work units and
+their merges; a max_seqlen hint below the true length must leave results
+unchanged (it only turns splitting off).
 """
 
 import pytest
@@ -51,6 +53,17 @@ for dt in ("f32", "bf16"):
     CASES.append((f"fdma-shapes-{dt}", dict(seed=45, lens_q=[37, 37, 512, 512, 512, 512], hq=2,
                                             hkv=2, d=64, causal=False, dtype=dt, with_dout=True,
                                             bias="per_pair", bias_std=0.5)))
+    # tiles long enough to be split into several work units (forward and dQ:
+    # more than 1024 keys; dK/dV: more than 768 query-row x head pairs),
+    # merged by the merge kernels
+    CASES.append((f"split-long-{dt}", dict(seed=46, lens_q=[1500, 40, 2100], hq=4, hkv=1, d=64,
+                                           causal=True, dtype=dt, with_dout=True)))
+    CASES.append((f"split-cross-bias-{dt}", dict(seed=47, lens_q=[300, 1100], lens_k=[1300, 2000],
+                                                 hq=2, hkv=2, d=64, causal=False, dtype=dt,
+                                                 with_dout=True, bias="per_pair", bias_std=0.5)))
+    CASES.append((f"split-decode-d128-{dt}", dict(seed=48, lens_q=[1, 3, 1200], lens_k=[3000, 1500, 2500],
+                                                  hq=8, hkv=2, d=128, causal=True, dtype=dt,
+                                                  with_dout=True)))
 
 
 @pytest.mark.parametrize("name,c", CASES, ids=[c[0] for c in CASES])
@@ -90,3 +103,28 @@ def test_autograd_matches_direct_calls():
     assert torch.equal(out, o2) and torch.equal(lse, l2)
     assert torch.equal(q.grad, g2[0].to(q.dtype))
     assert torch.equal(k.grad, g2[1].to(k.dtype)) and torch.equal(v.grad, g2[2].to(v.dtype))
+
+
+def test_small_max_seqlen_hint_disables_splitting_only():
+    """max_seqlen is a sizing hint: passing one below the true maximum plans no split units
+    and must give the same (oracle-exact) results."""
+    import variable_length_packed_amd as va
+    w = make_case(49, [2100, 33], hq=4, hkv=2, d=64, causal=True, dtype="bf16", with_dout=True)
+    print("[case] small max_seqlen hint", flush=True)
+    inp = _gpu.device_inputs(w)
+    out, lse = va.va_varlen_fwd(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_k"], 64, 64,
+                                w.scale, True)
+    dq, dk, dv = va.va_varlen_bwd(inp["dout"], inp["q"], inp["k"], inp["v"], out, lse, inp["cu_q"],
+                                  inp["cu_k"], 64, 64, w.scale, True)
+    out2, lse2 = _gpu.run_fwd(w, inp)
+    g2 = _gpu.run_bwd(w, out2, lse2, inp)
+    torch.cuda.synchronize()
+    import oracle
+    o_ref, l_ref = oracle.forward(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, True)
+    ref = oracle.backward(w.dout, w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, True)
+    for got in ((out, lse, dq, dk, dv), (out2, lse2) + tuple(g2)):
+        _gpu.check("out", _gpu.host(got[0]), o_ref, w.dtype)
+        _gpu.check_lse(_gpu.host(got[1]), l_ref, w.dtype)
+        for n, g, r in zip(("dq", "dk", "dv"), got[2:], ref):
+            _gpu.check(n, _gpu.host(g), r, w.dtype, grad=True,
+                       abs_tol=_gpu.grad_abs_tol(w.dtype, r, False))

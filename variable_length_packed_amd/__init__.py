@@ -22,6 +22,7 @@ from .api import (  # noqa: F401
     va_varlen_bwd,
     va_varlen_bwd_workspace_size,
     va_varlen_fwd,
+    va_varlen_fwd_workspace_size,
     va_last_error,
     va_status_string,
     va_timing_start,

@@ -11,8 +11,9 @@ VA_OK, VA_ERR_INVALID, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP = range(
 VA_F32, VA_BF16 = 0, 1
 
 # Every symbol include/va_varlen.h declares.
-EXPORTS = ("va_varlen_fwd", "va_varlen_bwd", "va_varlen_bwd_workspace_size", "va_status_string",
-           "va_last_error", "va_version", "va_timing_start", "va_timing_stop")
+EXPORTS = ("va_varlen_fwd", "va_varlen_bwd", "va_varlen_fwd_workspace_size",
+           "va_varlen_bwd_workspace_size", "va_status_string", "va_last_error", "va_version",
+           "va_timing_start", "va_timing_stop")
 
 
 class KernelTime(ctypes.Structure):
@@ -37,14 +38,18 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     lib.va_varlen_fwd.restype = ctypes.c_int
     lib.va_varlen_fwd.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p, _i64p, _p,
-                                  _p, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p]
+                                  _p, _p, ctypes.c_size_t, _i32, _i32, _i32, _i32, _i32, _i32,
+                                  ctypes.c_int, _p]
     lib.va_varlen_bwd.restype = ctypes.c_int
     lib.va_varlen_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p,
                                   _i64p, _p, _p, _p, _p, ctypes.c_size_t, _i32, _i32, _i32, _i32,
                                   _i32, _i32, ctypes.c_int, ctypes.c_int, _p]
-    lib.va_varlen_bwd_workspace_size.restype = ctypes.c_size_t
-    lib.va_varlen_bwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
+    lib.va_varlen_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.va_varlen_fwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                  ctypes.c_int]
+    lib.va_varlen_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.va_varlen_bwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                 ctypes.c_int, ctypes.c_int]
     lib.va_status_string.restype = ctypes.c_char_p
     lib.va_status_string.argtypes = [ctypes.c_int]
     lib.va_last_error.restype = ctypes.c_char_p

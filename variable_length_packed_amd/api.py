@@ -90,7 +90,8 @@ def va_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   softmax_scale: Optional[float] = None, causal: bool = False,
                   bias: Optional[torch.Tensor] = None,
                   bias_stride: Optional[Sequence[int]] = None,
-                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
     """Forward.  Returns (out [Tq, Hq, d] in q's dtype, lse [Hq, Tq] float32)."""
     lib = _lib.load()
     for n, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
@@ -121,20 +122,37 @@ def va_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if out.shape != q.shape or out.dtype != q.dtype or lse.shape != (hq, tq) or \
             lse.dtype != torch.float32:
         raise ValueError("out/lse have the wrong shape or dtype")
+    need = lib.va_varlen_fwd_workspace_size(batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k),
+                                            hq, hkv, d, dt)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
+    _need_dev("workspace", workspace, q.device)
     st = lib.va_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
                            cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
-                           int(bool(causal)), bptr, bstr, out.data_ptr(), lse.data_ptr(), batch,
-                           tq, tk, hq, hkv, d, dt, _stream(q.device))
+                           int(bool(causal)), bptr, bstr, out.data_ptr(), lse.data_ptr(),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           batch, tq, tk, hq, hkv, d, dt, _stream(q.device))
     _raise(st, lib)
     return out, lse
 
 
-def va_varlen_bwd_workspace_size(batch: int, total_q: int, total_k: int, num_heads_q: int,
-                                 num_heads_kv: int, head_dim: int, dtype: torch.dtype,
+def va_varlen_fwd_workspace_size(batch: int, total_q: int, total_k: int, max_seqlen_q: int,
+                                 max_seqlen_k: int, num_heads_q: int, num_heads_kv: int,
+                                 head_dim: int, dtype: torch.dtype) -> int:
+    lib = _lib.load()
+    return int(lib.va_varlen_fwd_workspace_size(batch, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                                                num_heads_q, num_heads_kv, head_dim,
+                                                _DTYPES.get(dtype, -1)))
+
+
+def va_varlen_bwd_workspace_size(batch: int, total_q: int, total_k: int, max_seqlen_q: int,
+                                 max_seqlen_k: int, num_heads_q: int, num_heads_kv: int,
+                                 head_dim: int, dtype: torch.dtype,
                                  grad_dtype: torch.dtype) -> int:
     lib = _lib.load()
-    return int(lib.va_varlen_bwd_workspace_size(batch, total_q, total_k, num_heads_q, num_heads_kv,
-                                                head_dim, _DTYPES.get(dtype, -1),
+    return int(lib.va_varlen_bwd_workspace_size(batch, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                                                num_heads_q, num_heads_kv, head_dim,
+                                                _DTYPES.get(dtype, -1),
                                                 _DTYPES.get(grad_dtype, -1)))
 
 
@@ -182,7 +200,8 @@ def va_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch
         _need_dev(n, t, q.device)
         if t.shape != shp or t.dtype != grad_dtype:
             raise ValueError(f"{n} has the wrong shape or dtype")
-    need = lib.va_varlen_bwd_workspace_size(batch, tq, tk, hq, hkv, d, dt, gdt)
+    need = lib.va_varlen_bwd_workspace_size(batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k),
+                                            hq, hkv, d, dt, gdt)
     if workspace is None:
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
     _need_dev("workspace", workspace, q.device)

@@ -27,8 +27,6 @@ va_status fail(va_status s, const char* fmt, ...) {
   return s;
 }
 
-constexpr int kMaxLevels = 512;  // matches the device schedule's level table
-
 struct Common {
   int batch, total_q, total_k, hq, hkv, d, max_q, max_k;
   int causal;
@@ -62,42 +60,108 @@ va_status check_common(const Common& c, float scale, const void* bias, const int
   return VA_OK;
 }
 
-// Schedule sizing: tiles of bm rows per sequence, capped by max_seqlen; at
-// most kMaxLevels schedule levels.
-void sched_dims(int max_len, int bm, int& tcap, int& stride, int& nlev) {
-  tcap = (max_len + bm - 1) / bm;
-  if (tcap < 1) tcap = 1;
-  stride = (tcap + kMaxLevels - 1) / kMaxLevels;
-  nlev = (tcap + stride - 1) / stride;
-}
-
-int64_t max_tiles(int total, int batch, int bm, int tcap) {
-  int64_t a = (int64_t)total / bm + batch;  // each sequence adds at most one ragged tile
-  int64_t b = (int64_t)batch * tcap;
-  return a < b ? a : b;
-}
-
-// Backward workspace: D = rowsum(dO * O) as [hq, total_q] float32, then,
-// when the query heads of a GQA group are spread over several workgroups,
-// float32 dK/dV partial sums [2 * hsplit][total_k, hkv, d].
+// ---------------------------------------------------------------------------
+// Workspace.  Every pass gets a work plan (a header, the unit list and the
+// split-tile list) and, when some tile can be split, float32 partial-result
+// slots.  Sizes are bounds from host arguments only: at most total/tile +
+// batch tiles (each sequence adds at most one ragged tile), and a tile of
+// s steps splits into ceil(s / chunk) units.  Partial slots are capped by a
+// byte budget; a batch that would need more is planned without splitting.
+// ---------------------------------------------------------------------------
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Split a GQA group's heads over workgroups when the unsplit dK/dV grid
-// would be too small to fill the device: at most 2048 work items.
-int choose_hsplit(int batch, int total_k, int hkv, int n_rep, int bnk, int tcap_k) {
-  if (n_rep <= 1) return 1;
-  return max_tiles(total_k, batch, bnk, tcap_k) * hkv < 2048 ? n_rep : 1;
+constexpr int kChunkKeys = 1024;      // forward / dQ: most keys per unit
+constexpr int kDkdvUnitRows = 768;    // dK/dV: most (query row, head) pairs per unit
+constexpr size_t kFwdPartBudget = (size_t)64 << 20;
+constexpr size_t kDkdvPartBudget = (size_t)128 << 20;
+constexpr size_t kDqPartBudget = (size_t)64 << 20;
+
+struct PlanLayout {
+  int unit_cap = 0, slot_cap = 0, split_cap = 0, chunk = 1;
+  size_t plan_bytes = 0;   // header + lists
+  size_t slot_bytes = 0;   // bytes of one partial slot
+};
+
+PlanLayout plan_layout(int total_t, int batch, int tile, int max_other, int step, int chunk,
+                       size_t slot_bytes, size_t budget) {
+  PlanLayout L;
+  const int64_t tiles = (int64_t)total_t / tile + batch;
+  const int64_t max_steps = ((int64_t)max_other + step - 1) / step;
+  int64_t slots = 0;
+  if (max_steps > chunk) {
+    slots = tiles * ((max_steps + chunk - 1) / chunk);
+    const int64_t cap = (int64_t)(budget / slot_bytes);
+    if (slots > cap) slots = cap;
+    if (slots < 2) slots = 0;
+  }
+  L.slot_cap = (int)slots;
+  L.split_cap = (int)(slots / 2);
+  L.unit_cap = (int)(tiles + slots);
+  L.chunk = chunk;
+  L.slot_bytes = slot_bytes;
+  L.plan_bytes = round_up(256) + 2 * round_up((size_t)L.unit_cap * 16) +
+                 round_up((size_t)(L.split_cap > 0 ? L.split_cap : 1) * 16);
+  return L;
 }
 
-size_t bwd_workspace(int batch, int total_q, int total_k, int hq, int hkv, int d, int max_k,
-                     int& hsplit) {
-  int tcap, stride, nlev;
-  sched_dims(max_k, va::bwd_block_k(), tcap, stride, nlev);
-  hsplit = choose_hsplit(batch, total_k, hkv, hq / hkv, va::bwd_block_k(), tcap);
-  size_t ws = round_up((size_t)hq * total_q * sizeof(float));
-  if (hsplit > 1) ws += round_up((size_t)2 * hsplit * total_k * hkv * d * sizeof(float));
-  return ws;
+// Carves a plan out of the workspace at `p`; returns the bytes used.
+size_t carve_plan(char* p, const PlanLayout& L, va::Plan& plan) {
+  plan.hdr = (int*)p;
+  size_t o = round_up(256);
+  plan.units = (int4*)(p + o);
+  o += round_up((size_t)L.unit_cap * 16);
+  plan.uinfo = (int4*)(p + o);
+  o += round_up((size_t)L.unit_cap * 16);
+  plan.splits = (int4*)(p + o);
+  o += round_up((size_t)(L.split_cap > 0 ? L.split_cap : 1) * 16);
+  return o;
+}
+
+va::PlanArgs plan_args(const va::Plan& plan, const PlanLayout& L, const int32_t* cu_t,
+                       const int32_t* cu_o, int total_t, int total_o, int batch, int tile,
+                       int step, int kside, int causal) {
+  va::PlanArgs a{};
+  a.plan = plan;
+  a.cu_t = cu_t; a.cu_o = cu_o;
+  a.total_t = total_t; a.total_o = total_o; a.batch = batch;
+  a.tile = tile; a.step = step; a.kside = kside; a.causal = causal;
+  a.chunk = L.chunk;
+  a.unit_cap = L.unit_cap; a.slot_cap = L.slot_cap; a.split_cap = L.split_cap;
+  return a;
+}
+
+PlanLayout fwd_plan(int batch, int total_q, int max_k, int hq, int d, bool bf16) {
+  const int bm = va::fwd_block_m(), bn = va::fwd_block_n(bf16, d);
+  return plan_layout(total_q, batch, bm, max_k, bn, kChunkKeys / bn,
+                     (size_t)hq * bm * (d + 1) * sizeof(float), kFwdPartBudget);
+}
+
+size_t fwd_workspace(int batch, int total_q, int max_k, int hq, int d, bool bf16) {
+  const PlanLayout L = fwd_plan(batch, total_q, max_k, hq, d, bf16);
+  return L.plan_bytes + round_up(L.slot_bytes * L.slot_cap);
+}
+
+PlanLayout dkdv_plan(int batch, int total_k, int max_q, int hkv, int n_rep, int d) {
+  const int bnk = va::bwd_block_k(), bmq = va::bwd_dkdv_block_q();
+  int chunk = kDkdvUnitRows / (bmq * n_rep);
+  if (chunk < 1) chunk = 1;
+  return plan_layout(total_k, batch, bnk, max_q, bmq, chunk,
+                     (size_t)hkv * 2 * bnk * d * sizeof(float), kDkdvPartBudget);
+}
+
+PlanLayout dq_plan(int batch, int total_q, int max_k, int hq, int d, bool bf16) {
+  const int bm = va::bwd_block_q(), bn = va::bwd_dq_block_n(bf16, d);
+  return plan_layout(total_q, batch, bm, max_k, bn, kChunkKeys / bn,
+                     (size_t)hq * bm * d * sizeof(float), kDqPartBudget);
+}
+
+size_t bwd_workspace(int batch, int total_q, int total_k, int max_q, int max_k, int hq, int hkv,
+                     int d, bool bf16) {
+  const PlanLayout K = dkdv_plan(batch, total_k, max_q, hkv, hq / hkv, d);
+  const PlanLayout Q = dq_plan(batch, total_q, max_k, hq, d, bf16);
+  return round_up((size_t)hq * total_q * sizeof(float)) + K.plan_bytes + Q.plan_bytes +
+         round_up(K.slot_bytes * K.slot_cap) + round_up(Q.slot_bytes * Q.slot_cap);
 }
 
 va_status hip_fail(hipError_t e, const char* what) {
@@ -123,20 +187,38 @@ const char* va_status_string(va_status s) {
 
 const char* va_last_error(void) { return g_err; }
 
+size_t va_varlen_fwd_workspace_size(int32_t batch, int32_t total_q, int32_t total_k,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                    va_dtype dtype) {
+  if (batch <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 ||
+      num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0 ||
+      (head_dim != 64 && head_dim != 128) || (dtype != VA_F32 && dtype != VA_BF16))
+    return 0;
+  return fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, dtype == VA_BF16);
+}
+
 va_status va_varlen_fwd(const void* q, const void* k, const void* v,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                         int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
                         int causal, const void* bias, const int64_t* bias_stride, void* out,
-                        float* lse, int32_t batch, int32_t total_q, int32_t total_k,
-                        int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
-                        va_dtype dtype, va_stream stream) {
+                        float* lse, void* workspace, size_t workspace_bytes, int32_t batch,
+                        int32_t total_q, int32_t total_k, int32_t num_heads_q,
+                        int32_t num_heads_kv, int32_t head_dim, va_dtype dtype,
+                        va_stream stream) {
   g_err[0] = 0;
-  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse)
+  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse || !workspace)
     return fail(VA_ERR_INVALID, "a required pointer is NULL");
   Common c{batch, total_q, total_k, num_heads_q, num_heads_kv, head_dim, max_seqlen_q,
            max_seqlen_k, causal, dtype};
   va_status s = check_common(c, softmax_scale, bias, bias_stride);
   if (s != VA_OK) return s;
+  if (((uintptr_t)workspace) % kAlign != 0)
+    return fail(VA_ERR_INVALID, "workspace must be 256-byte aligned");
+  const bool bf16 = dtype == VA_BF16;
+  const size_t need = fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16);
+  if (workspace_bytes < need)
+    return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
 
   va::FwdArgs a{};
   a.q = q; a.k = k; a.v = v;
@@ -146,28 +228,38 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
   a.out = out; a.lse = lse;
   a.batch = batch; a.total_q = total_q; a.total_k = total_k;
   a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = num_heads_q / num_heads_kv; a.d = head_dim;
-  const int bm = va::fwd_block_m(dtype == VA_BF16, head_dim);
-  sched_dims(max_seqlen_q, bm, a.tcap, a.stride, a.nlev);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.causal = causal;
-  a.bf16 = dtype == VA_BF16;
-  const int64_t items = max_tiles(total_q, batch, bm, a.tcap) * num_heads_q;
-  hipError_t e = va::launch_fwd(a, items, (hipStream_t)stream);
+  a.bf16 = bf16;
+  const PlanLayout L = fwd_plan(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16);
+  char* w = (char*)workspace;
+  const size_t used = carve_plan(w, L, a.plan);
+  a.part_o = (float*)(w + used);
+  a.part_lse = a.part_o + (size_t)L.slot_cap * num_heads_q * va::fwd_block_m() * head_dim;
+  a.split_cap = L.split_cap;
+  va::PlanSet ps{};
+  ps.p[0] = plan_args(a.plan, L, cu_seqlens_q, cu_seqlens_k, total_q, total_k, batch,
+                      va::fwd_block_m(), va::fwd_block_n(bf16, head_dim), 0, causal);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = va::launch_plan(ps, 1, st);
+  if (e != hipSuccess) return hip_fail(e, "forward plan launch");
+  e = va::launch_fwd(a, (int64_t)L.unit_cap * num_heads_q, st);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return VA_OK;
 }
 
 size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t total_k,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
                                     int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                                     va_dtype dtype, va_dtype grad_dtype) {
-  if (batch <= 0 || total_q <= 0 || total_k <= 0 || num_heads_q <= 0 || num_heads_kv <= 0 ||
+  if (batch <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 ||
+      num_heads_q <= 0 || num_heads_kv <= 0 ||
       num_heads_q % num_heads_kv != 0 || (head_dim != 64 && head_dim != 128) ||
       (dtype != VA_F32 && dtype != VA_BF16) || (grad_dtype != VA_F32 && grad_dtype != VA_BF16) ||
       (dtype == VA_F32 && grad_dtype == VA_BF16))
     return 0;
-  int hsplit;
-  // the dK/dV tile cap only bounds the grid estimate; use the largest possible
-  return bwd_workspace(batch, total_q, total_k, num_heads_q, num_heads_kv, head_dim, total_k, hsplit);
+  return bwd_workspace(batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q,
+                       num_heads_kv, head_dim, dtype == VA_BF16);
 }
 
 va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const void* v,
@@ -192,9 +284,10 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
     return fail(VA_ERR_UNSUPPORTED, "bf16 gradients of float32 inputs are not supported");
   if (((uintptr_t)workspace) % kAlign != 0)
     return fail(VA_ERR_INVALID, "workspace must be 256-byte aligned");
-  int hsplit = 1;
-  const size_t need = bwd_workspace(batch, total_q, total_k, num_heads_q, num_heads_kv, head_dim,
-                                    total_k, hsplit);
+  const bool bf16 = dtype == VA_BF16;
+  const int n_rep = num_heads_q / num_heads_kv;
+  const size_t need = bwd_workspace(batch, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                                    num_heads_q, num_heads_kv, head_dim, bf16);
   if (workspace_bytes < need)
     return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
 
@@ -204,22 +297,34 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
   a.bias = bias;
   if (bias) { a.bs0 = bias_stride[0]; a.bs1 = bias_stride[1]; a.bs2 = bias_stride[2]; a.bs3 = bias_stride[3]; }
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.dsum = (float*)workspace;
-  a.hsplit = hsplit;
-  a.part = hsplit > 1 ? (float*)((char*)workspace + round_up((size_t)num_heads_q * total_q * sizeof(float)))
-                      : nullptr;
   a.batch = batch; a.total_q = total_q; a.total_k = total_k;
-  a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = num_heads_q / num_heads_kv; a.d = head_dim;
-  sched_dims(max_seqlen_q, va::bwd_block_q(), a.tcap_q, a.stride_q, a.nlev_q);
-  sched_dims(max_seqlen_k, va::bwd_block_k(), a.tcap_k, a.stride_k, a.nlev_k);
+  a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = n_rep; a.d = head_dim;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.causal = causal;
-  a.bf16 = dtype == VA_BF16;
+  a.bf16 = bf16;
   a.grad_bf16 = grad_dtype == VA_BF16;
-  const int64_t q_items = max_tiles(total_q, batch, va::bwd_block_q(), a.tcap_q) * num_heads_q;
-  const int64_t k_items = max_tiles(total_k, batch, va::bwd_block_k(), a.tcap_k) * num_heads_kv;
-  hipError_t e = va::launch_bwd(a, q_items, k_items, (hipStream_t)stream);
+
+  const PlanLayout K = dkdv_plan(batch, total_k, max_seqlen_q, num_heads_kv, n_rep, head_dim);
+  const PlanLayout Q = dq_plan(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16);
+  char* w = (char*)workspace;
+  a.dsum = (float*)w;
+  size_t o = round_up((size_t)num_heads_q * total_q * sizeof(float));
+  o += carve_plan(w + o, K, a.plan_k);
+  o += carve_plan(w + o, Q, a.plan_q);
+  a.part_kv = (float*)(w + o);
+  o += round_up(K.slot_bytes * K.slot_cap);
+  a.part_q = (float*)(w + o);
+  a.split_cap_k = K.split_cap;
+  a.split_cap_q = Q.split_cap;
+
+  va::PlanSet ps{};
+  ps.p[0] = plan_args(a.plan_k, K, cu_seqlens_k, cu_seqlens_q, total_k, total_q, batch,
+                      va::bwd_block_k(), va::bwd_dkdv_block_q(), 1, causal);
+  ps.p[1] = plan_args(a.plan_q, Q, cu_seqlens_q, cu_seqlens_k, total_q, total_k, batch,
+                      va::bwd_block_q(), va::bwd_dq_block_n(bf16, head_dim), 0, causal);
+  hipError_t e = va::launch_bwd(a, ps, (int64_t)Q.unit_cap * num_heads_q,
+                                (int64_t)K.unit_cap * num_heads_kv, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return VA_OK;
 }

@@ -6,18 +6,23 @@
 //   dP  = dO V^T,  dS = P * (dP - D)
 //   dV  = P^T dO,  dK = scale * dS^T Q,  dQ = scale * dS K
 //
-// dK/dV kernel: a workgroup owns 128 keys (32 per wave) of one sequence and
-// KV head; K and V stay in registers while the workgroup walks the 32-query
-// blocks (and the query heads of its GQA group) that see those keys, staging
+// dK/dV kernel: a work unit is 128 keys (32 per wave) of one sequence and KV
+// head; K and V stay in registers while the workgroup walks the 32-query
+// blocks that see those keys, for every query head of the GQA group, staging
 // Q and dO in LDS both as rows (for S and dP) and transposed (for the
-// contractions over queries).  When the group's heads are split over several
-// workgroups, each writes float32 partial sums to the workspace and a reduce
-// kernel adds them in a fixed order, so results never depend on scheduling.
+// contractions over queries).  A key tile seen by many query blocks is split
+// into units over ranges of query blocks; those write float32 partial sums
+// and a merge kernel adds them in chunk order, so results never depend on
+// scheduling.
 //
-// dQ kernel: shaped like the forward.  A workgroup owns 128 query rows of one
-// head; Q and dO stay in registers; score tiles are computed transposed (keys
-// x queries) so each lane holds one query row and dS^T feeds the dQ^T
-// contraction straight from registers.
+// dQ kernel: shaped like the forward.  A unit is 128 query rows of one head
+// (or a range of key blocks of them, merged the same way); Q and dO stay in
+// registers; score tiles are computed transposed (keys x queries) so each
+// lane holds one query row and dS^T feeds the dQ^T contraction straight from
+// registers.
+//
+// Both take their units from the planner's list through an atomic queue,
+// heaviest first.
 //
 // No mask is needed for a key past the sequence (its K and V read as zero and
 // its dK/dV row is never stored; in dQ its zero K row adds nothing) or for a
@@ -30,6 +35,7 @@
 // dQ uses the plain rounding.
 #include "va_common.h"
 #include "va_kernels.h"
+#include "va_plan.h"
 
 namespace va {
 
@@ -170,13 +176,20 @@ __device__ __forceinline__ void pack8(const float* v, u32x4_t& hi, u32x4_t* lo) 
 }
 
 // ---------------------------------------------------------------- preprocess
+// One launch: workgroups 0 and 1 build the dK/dV and dQ work plans while the
+// others compute D = rowsum(dO * O) for every (query row, head).
 template <bool BF16, int D>
-__global__ __launch_bounds__(NT) void dsum_kernel(BwdArgs a) {
+__global__ __launch_bounds__(plan::PT) void plan_dsum_kernel(BwdArgs a, PlanSet ps) {
+  __shared__ plan::PlanShared sh;
+  if (blockIdx.x < 2) {
+    plan::plan_body(ps.p[blockIdx.x], sh);
+    return;
+  }
   using T = elem_t<BF16>;
   constexpr int EPV = 16 / sizeof(T);
   constexpr int TPR = D / EPV;  // threads per (token, head) row
   const int64_t rows = (int64_t)a.total_q * a.hq;
-  const int64_t row = ((int64_t)blockIdx.x * NT + threadIdx.x) / TPR;
+  const int64_t row = ((int64_t)(blockIdx.x - 2) * plan::PT + threadIdx.x) / TPR;
   const int c = threadIdx.x % TPR;
   float s = 0.f;
   if (row < rows) {
@@ -223,32 +236,35 @@ template <bool BF16, int D>
 constexpr int dkdv_min_blocks() { return D == 64 ? 2 : 1; }
 
 template <bool BF16, int D, bool CAUSAL, bool HAS_BIAS>
-__global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(BwdArgs a, int hsplit, float* part) {
+__global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(BwdArgs a) {
   using T = elem_t<BF16>;
   using SM = DkdvSmem<BF16, D>;
   using St = typename SM::St;
   constexpr int DT = D / 32;
   constexpr int ELT = (int)sizeof(T);
 
-  __shared__ SchedShared sched;
   __shared__ SM sm;
+  __shared__ int s_item;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
   const int hh = lane >> 5, r32 = lane & 31;
 
-  sched_build(sched, a.cu_k, a.batch, a.total_k, BNK, a.tcap_k, a.stride_k, a.nlev_k);
-  const int per_tile = a.hkv * hsplit;
-  const int total_items = sched.total_tiles * per_tile;
+  const int total_items = uniform(a.plan_k.hdr[1]) * a.hkv;
   const size_t qstride = (size_t)a.hq * D, kstride = (size_t)a.hkv * D;
   const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
-  const int hpw = a.n_rep / hsplit;  // query heads per workgroup
+  const int hpw = a.n_rep;  // every query head of the group
 
-  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
-    const int tile = item / per_tile;
-    const int rem = item - tile * per_tile;
-    const int g = rem / hsplit, sp = rem - g * hsplit;
-    int b, t;
-    sched_find(sched, a.cu_k, a.batch, a.total_k, BNK, a.tcap_k, a.stride_k, a.nlev_k, tile, b, t);
+  if (tid == 0) s_item = queue_take(a.plan_k.hdr);
+  __syncthreads();
+  for (int item = uniform(s_item); item < total_items; item = uniform(s_item)) {
+    __syncthreads();  // every thread has read s_item
+    int next_item = 0;
+    if (tid == 0) next_item = queue_take(a.plan_k.hdr);  // published at the end of this item
+    const int unit = item / a.hkv;
+    const int g = item - unit * a.hkv;
+    const int4 un = a.plan_k.units[unit];
+    const int b = uniform(un.x), t = uniform(un.y), u0 = uniform(un.z), u1 = uniform(un.w);
+    const int slot = uniform(a.plan_k.uinfo[unit].x);  // >= 0: a chunk of a split tile
     int q0, q1, k0, k1;
     seq_bounds(a.cu_q, b, a.total_q, q0, q1);
     seq_bounds(a.cu_k, b, a.total_k, k0, k1);
@@ -268,16 +284,19 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
 #pragma unroll
     for (int i = 0; i < DT; ++i) { dk[i] = (f32x16_t){}; dv[i] = (f32x16_t){}; }
 
-    // query blocks that can see a key of the tile: i + off >= kt0 (causal)
+    // query blocks that can see a key of the tile: i + off >= kt0 (causal);
+    // this unit runs blocks [u0, u1) of them, for every head of the group
     const int qs = CAUSAL ? max(0, kt0 - off) : 0;
     const int nqb = qs < Lq ? (Lq - qs + BMQ - 1) / BMQ : 0;
     // blocks crossing the diagonal for some wave: qb + off < kt0 + BNK - 1
     const int n_diag = CAUSAL ? min(nqb, max(0, (kt0 + BNK - 1 - off - qs + BMQ - 1) / BMQ)) : 0;
-    const int k_masked = hpw * n_diag, k_total = hpw * nqb;
-    const int h_first = g * a.n_rep + sp * hpw;
+    const int nb = u1 - u0;
+    const int nm = min(max(n_diag - u0, 0), nb);  // masked blocks of the unit (its first ones)
+    const int k_masked = hpw * nm, k_total = hpw * nb;
+    const int h_first = g * a.n_rep;
     auto tile_of = [&](int k, int& r, int& n) {
-      if (k < k_masked) { r = k / n_diag; n = k - r * n_diag; }
-      else { const int nu = nqb - n_diag, kk = k - k_masked; r = kk / nu; n = n_diag + (kk - r * nu); }
+      if (k < k_masked) { r = k / nm; n = u0 + (k - r * nm); }
+      else { const int nu = nb - nm, kk = k - k_masked; r = kk / nu; n = u0 + nm + (kk - r * nu); }
     };
 
     St sq, sd;
@@ -385,46 +404,86 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
     for (; k < k_total; ++k) step(std::integral_constant<bool, false>(), k);
 
     // ---- epilogue: rows = keys 8(i/4)+4hh+i%4 of the wave, column d = 32dt + r32
-    const size_t plane = (size_t)a.total_k * kstride;
+    if (slot < 0) {
 #pragma unroll
-    for (int dt_ = 0; dt_ < DT; ++dt_)
+      for (int dt_ = 0; dt_ < DT; ++dt_)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = wk0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (key >= Lk) continue;
-        const size_t o = koff + (size_t)key * kstride + 32 * dt_ + r32;
-        const float kv = dk[dt_][i], vv = dv[dt_][i];
-        if (hsplit > 1) {
-          part[(size_t)(2 * sp) * plane + o] = kv;
-          part[(size_t)(2 * sp + 1) * plane + o] = vv;
-        } else if (a.grad_bf16) {
-          ((uint16_t*)a.dk)[o] = (uint16_t)(pack_bf16x2(kv * a.scale, 0.f) & 0xFFFF);
-          ((uint16_t*)a.dv)[o] = (uint16_t)(pack_bf16x2(vv, 0.f) & 0xFFFF);
-        } else {
-          ((float*)a.dk)[o] = kv * a.scale;
-          ((float*)a.dv)[o] = vv;
+        for (int i = 0; i < 16; ++i) {
+          const int key = wk0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (key >= Lk) continue;
+          const size_t o = koff + (size_t)key * kstride + 32 * dt_ + r32;
+          const float kv = dk[dt_][i] * a.scale, vv = dv[dt_][i];
+          if (a.grad_bf16) {
+            ((uint16_t*)a.dk)[o] = (uint16_t)(pack_bf16x2(kv, 0.f) & 0xFFFF);
+            ((uint16_t*)a.dv)[o] = (uint16_t)(pack_bf16x2(vv, 0.f) & 0xFFFF);
+          } else {
+            ((float*)a.dk)[o] = kv;
+            ((float*)a.dv)[o] = vv;
+          }
         }
-      }
+    } else {
+      float* pk = a.part_kv + ((size_t)slot * a.hkv + g) * 2 * BNK * D;
+      float* pv = pk + BNK * D;
+#pragma unroll
+      for (int dt_ = 0; dt_ < DT; ++dt_)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kl = 32 * wid + 8 * (i >> 2) + 4 * hh + (i & 3);  // key inside the tile
+          pk[kl * D + 32 * dt_ + r32] = dk[dt_][i];
+          pv[kl * D + 32 * dt_ + r32] = dv[dt_][i];
+        }
+    }
+    if (tid == 0) s_item = next_item;
+    __syncthreads();
   }
 }
 
-// Adds the head-split partial sums of dK and dV in a fixed order.
-__global__ __launch_bounds__(NT) void dkdv_reduce_kernel(BwdArgs a, int hsplit, const float* part) {
-  const size_t plane = (size_t)a.total_k * a.hkv * a.d;
-  const size_t n4 = plane / 4;
-  for (size_t i = (size_t)blockIdx.x * NT + threadIdx.x; i < n4; i += (size_t)gridDim.x * NT) {
-    f32x4_t sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < hsplit; ++s) {
-      sk += ((const f32x4_t*)(part + (size_t)(2 * s) * plane))[i];
-      sv += ((const f32x4_t*)(part + (size_t)(2 * s + 1) * plane))[i];
+// Sums the chunks of split dK/dV tiles in chunk order (deterministic) and
+// writes the gradients.  A work item is 16 keys of one (split tile, KV
+// head); sixteen threads per key.
+constexpr int kMergeKeys = 16;
+
+template <int D>
+__global__ __launch_bounds__(NT) void dkdv_merge_kernel(BwdArgs a) {
+  constexpr int SLABS = BNK / kMergeKeys;
+  constexpr int TPR = NT / kMergeKeys;
+  constexpr int SEG = D / TPR;
+  const int total = uniform(a.plan_k.hdr[2]) * a.hkv * SLABS;
+  const int ks = threadIdx.x / TPR, seg = threadIdx.x % TPR;
+  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+    const int slab = it % SLABS, sg = it / SLABS;
+    const int si = sg / a.hkv, g = sg - si * a.hkv;
+    const int4 sp = a.plan_k.splits[si];
+    const int b = uniform(sp.x), t = uniform(sp.y), sb = uniform(sp.z), nch = uniform(sp.w);
+    int k0, k1;
+    seq_bounds(a.cu_k, b, a.total_k, k0, k1);
+    const int kl = slab * kMergeKeys + ks;  // key inside the tile
+    const int key = t * BNK + kl;
+    if (key >= k1 - k0) continue;
+    f32x4_t sk[SEG / 4], sv[SEG / 4];
+#pragma unroll
+    for (int e = 0; e < SEG / 4; ++e) { sk[e] = (f32x4_t){0.f, 0.f, 0.f, 0.f}; sv[e] = sk[e]; }
+#pragma unroll 4
+    for (int c = 0; c < nch; ++c) {
+      const float* pk = a.part_kv + ((size_t)(sb + c) * a.hkv + g) * 2 * BNK * D + kl * D + seg * SEG;
+      const float* pv = pk + BNK * D;
+#pragma unroll
+      for (int e = 0; e < SEG / 4; ++e) {
+        sk[e] += ((const f32x4_t*)pk)[e];
+        sv[e] += ((const f32x4_t*)pv)[e];
+      }
     }
-    sk *= a.scale;
-    if (a.grad_bf16) {
-      ((u32x2_t*)a.dk)[i] = (u32x2_t){pack_bf16x2(sk[0], sk[1]), pack_bf16x2(sk[2], sk[3])};
-      ((u32x2_t*)a.dv)[i] = (u32x2_t){pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
-    } else {
-      ((f32x4_t*)a.dk)[i] = sk;
-      ((f32x4_t*)a.dv)[i] = sv;
+    const size_t o = ((size_t)(k0 + key) * a.hkv + g) * D + seg * SEG;
+#pragma unroll
+    for (int e = 0; e < SEG / 4; ++e) {
+      const f32x4_t k4 = sk[e] * a.scale, v4 = sv[e];
+      if (a.grad_bf16) {
+        ((u32x2_t*)((uint16_t*)a.dk + o))[e] = (u32x2_t){pack_bf16x2(k4[0], k4[1]), pack_bf16x2(k4[2], k4[3])};
+        ((u32x2_t*)((uint16_t*)a.dv + o))[e] = (u32x2_t){pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
+      } else {
+        ((f32x4_t*)((float*)a.dk + o))[e] = k4;
+        ((f32x4_t*)((float*)a.dv + o))[e] = v4;
+      }
     }
   }
 }
@@ -452,23 +511,28 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   using St = typename SM::St;
   using Sv = typename SM::Sv;
 
-  __shared__ SchedShared sched;
   __shared__ SM sm;
+  __shared__ int s_item;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
   const int hh = lane >> 5, r32 = lane & 31;
 
-  sched_build(sched, a.cu_q, a.batch, a.total_q, BMQ_DQ, a.tcap_q, a.stride_q, a.nlev_q);
-  const int total_items = sched.total_tiles * a.hq;
+  const int total_items = uniform(a.plan_q.hdr[1]) * a.hq;
   const size_t qstride = (size_t)a.hq * D, kstride = (size_t)a.hkv * D;
   const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
   const int gelt = a.grad_bf16 ? 2 : 4;
 
-  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
-    const int tile = item / a.hq;
-    const int h = item - tile * a.hq;
-    int b, t;
-    sched_find(sched, a.cu_q, a.batch, a.total_q, BMQ_DQ, a.tcap_q, a.stride_q, a.nlev_q, tile, b, t);
+  if (tid == 0) s_item = queue_take(a.plan_q.hdr);
+  __syncthreads();
+  for (int item = uniform(s_item); item < total_items; item = uniform(s_item)) {
+    __syncthreads();  // every thread has read s_item
+    int next_item = 0;
+    if (tid == 0) next_item = queue_take(a.plan_q.hdr);  // published at the end of this item
+    const int unit = item / a.hq;
+    const int h = item - unit * a.hq;
+    const int4 un = a.plan_q.units[unit];
+    const int b = uniform(un.x), t = uniform(un.y), n0 = uniform(un.z), n1 = uniform(un.w);
+    const int slot = uniform(a.plan_q.uinfo[unit].x);  // >= 0: a chunk of a split tile
     int q0, q1, k0, k1;
     seq_bounds(a.cu_q, b, a.total_q, q0, q1);
     seq_bounds(a.cu_k, b, a.total_k, k0, k1);
@@ -482,10 +546,11 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     const int kv_hi = CAUSAL ? min(Lk, r1 + off) : Lk;
     const int wave_hi = CAUSAL ? min(Lk, w0 + 32 + off) : Lk;
     const bool wave_on = (w0 + 31 >= 0) && wave_hi > 0;
-    const int nblk = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
     // blocks start at key 0; those before n_plain are fully visible to every
-    // row of the tile (the smallest row sees keys <= r1 - BMQ_DQ + off)
-    const int n_plain = CAUSAL ? min(max(r1 - BMQ_DQ + off + 1, 0) / BN, nblk) : nblk;
+    // row of the tile (the smallest row sees keys <= r1 - BMQ_DQ + off); this
+    // unit runs blocks [n0, n1)
+    const int n_plain = CAUSAL ? max(r1 - BMQ_DQ + off + 1, 0) / BN : kv_hi / BN;
+    const int kv_end = min(kv_hi, n1 * BN);  // keys this unit may read
 
     const size_t qoff = (size_t)q0 * qstride + (size_t)h * D;
     const int64_t qbytes = Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0;
@@ -503,7 +568,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     for (int i = 0; i < DT; ++i) acc[i] = (f32x16_t){};
 
     const size_t koff = (size_t)k0 * kstride + (size_t)g * D;
-    const int64_t kbytes = kv_hi > 0 ? (int64_t)(kv_hi - 1) * krow_bytes + D * ELT : 0;
+    const int64_t kbytes = kv_end > 0 ? (int64_t)(kv_end - 1) * krow_bytes + D * ELT : 0;
     const rsrc_t kres = make_rsrc((const T*)a.k + koff, kbytes);
     const rsrc_t vres = make_rsrc((const T*)a.v + koff, kbytes);
     const T* bias_bh = nullptr;
@@ -516,8 +581,8 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     auto step = [&](auto mask_tag, int n) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int kb = n * BN;
-      const int buf = n & 1;
-      if (n + 1 < nblk) {
+      const int buf = (n - n0) & 1;
+      if (n + 1 < n1) {
         sk.load(kres, krow_bytes, kb + BN);
         sv.load(vres, krow_bytes, kb + BN);
       }
@@ -565,74 +630,130 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
             }
         }
       }
-      if (n + 1 < nblk) {
+      if (n + 1 < n1) {
         sk.store(sm.kn[buf ^ 1], sm.kt[buf ^ 1]);
         sv.store(sm.vn[buf ^ 1], nullptr);
       }
       __syncthreads();
     };
 
-    if (nblk > 0) {
-      sk.load(kres, krow_bytes, 0);
-      sv.load(vres, krow_bytes, 0);
+    if (n1 > n0) {
+      sk.load(kres, krow_bytes, n0 * BN);
+      sv.load(vres, krow_bytes, n0 * BN);
       sk.store(sm.kn[0], sm.kt[0]);
       sv.store(sm.vn[0], nullptr);
     }
     __syncthreads();
-    int n = 0;
-    for (; n < n_plain; ++n) step(std::integral_constant<bool, false>(), n);
-    for (; n < nblk; ++n) step(std::integral_constant<bool, true>(), n);
+    int n = n0;
+    for (; n < min(n_plain, n1); ++n) step(std::integral_constant<bool, false>(), n);
+    for (; n < n1; ++n) step(std::integral_constant<bool, true>(), n);
 
-    // rows < 0 fall outside the resource: their stores are dropped
-    const int dq_row_bytes = (int)qstride * gelt;
-    const rsrc_t dqres = make_rsrc((uint8_t*)a.dq + qoff * gelt,
-                                   Lq > 0 ? (int64_t)(Lq - 1) * dq_row_bytes + D * gelt : 0);
+    if (slot < 0) {
+      // rows < 0 fall outside the resource: their stores are dropped
+      const int dq_row_bytes = (int)qstride * gelt;
+      const rsrc_t dqres = make_rsrc((uint8_t*)a.dq + qoff * gelt,
+                                     Lq > 0 ? (int64_t)(Lq - 1) * dq_row_bytes + D * gelt : 0);
 #pragma unroll
-    for (int dt_ = 0; dt_ < DT; ++dt_)
+      for (int dt_ = 0; dt_ < DT; ++dt_)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int d0 = 32 * dt_ + 8 * a4 + 4 * hh;
-        const float o0 = acc[dt_][4 * a4 + 0] * a.scale, o1 = acc[dt_][4 * a4 + 1] * a.scale;
-        const float o2 = acc[dt_][4 * a4 + 2] * a.scale, o3 = acc[dt_][4 * a4 + 3] * a.scale;
-        if (a.grad_bf16) {
-          buf_store8((u32x2_t){pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)}, dqres, rq * dq_row_bytes + d0 * 2);
-        } else {
-          buf_store16((u32x4_t){__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2),
-                                __float_as_uint(o3)}, dqres, rq * dq_row_bytes + d0 * 4);
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int d0 = 32 * dt_ + 8 * a4 + 4 * hh;
+          const float o0 = acc[dt_][4 * a4 + 0] * a.scale, o1 = acc[dt_][4 * a4 + 1] * a.scale;
+          const float o2 = acc[dt_][4 * a4 + 2] * a.scale, o3 = acc[dt_][4 * a4 + 3] * a.scale;
+          if (a.grad_bf16) {
+            buf_store8((u32x2_t){pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)}, dqres, rq * dq_row_bytes + d0 * 2);
+          } else {
+            buf_store16((u32x4_t){__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2),
+                                  __float_as_uint(o3)}, dqres, rq * dq_row_bytes + d0 * 4);
+          }
         }
-      }
+    } else {
+      const int rl = rq - (r1 - BMQ_DQ);  // 0 .. BMQ_DQ-1
+      float* pq = a.part_q + ((size_t)slot * a.hq + h) * BMQ_DQ * D + (size_t)rl * D;
+#pragma unroll
+      for (int dt_ = 0; dt_ < DT; ++dt_)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int d0 = 32 * dt_ + 8 * a4 + 4 * hh;
+          *(f32x4_t*)(pq + d0) = (f32x4_t){acc[dt_][4 * a4], acc[dt_][4 * a4 + 1], acc[dt_][4 * a4 + 2],
+                                           acc[dt_][4 * a4 + 3]};
+        }
+    }
+    if (tid == 0) s_item = next_item;
+    __syncthreads();
+  }
+}
+
+// Sums the chunks of split dQ tiles in chunk order (deterministic).  A work
+// item is 32 rows of one (split tile, head); eight threads per row.
+constexpr int kMergeRows = 32;
+
+template <int D>
+__global__ __launch_bounds__(NT) void dq_merge_kernel(BwdArgs a) {
+  constexpr int SLABS = BMQ_DQ / kMergeRows;
+  constexpr int TPR = NT / kMergeRows;
+  constexpr int SEG = D / TPR;
+  const int total = uniform(a.plan_q.hdr[2]) * a.hq * SLABS;
+  const int rs = threadIdx.x / TPR, seg = threadIdx.x % TPR;
+  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+    const int slab = it % SLABS, sh = it / SLABS;
+    const int si = sh / a.hq, h = sh - si * a.hq;
+    const int4 sp = a.plan_q.splits[si];
+    const int b = uniform(sp.x), t = uniform(sp.y), sb = uniform(sp.z), nch = uniform(sp.w);
+    int q0, q1;
+    seq_bounds(a.cu_q, b, a.total_q, q0, q1);
+    const int row = slab * kMergeRows + rs;
+    const int rq = (q1 - q0) - (t + 1) * BMQ_DQ + row;
+    if (rq < 0) continue;
+    f32x4_t acc[SEG / 4];
+#pragma unroll
+    for (int e = 0; e < SEG / 4; ++e) acc[e] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int c = 0; c < nch; ++c) {
+      const f32x4_t* src =
+          (const f32x4_t*)(a.part_q + (((size_t)(sb + c) * a.hq + h) * BMQ_DQ + row) * D + seg * SEG);
+#pragma unroll
+      for (int e = 0; e < SEG / 4; ++e) acc[e] += src[e];
+    }
+    const size_t o = ((size_t)(q0 + rq) * a.hq + h) * D + seg * SEG;
+#pragma unroll
+    for (int e = 0; e < SEG / 4; ++e) {
+      const f32x4_t x = acc[e] * a.scale;
+      if (a.grad_bf16)
+        ((u32x2_t*)((uint16_t*)a.dq + o))[e] = (u32x2_t){pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      else
+        ((f32x4_t*)((float*)a.dq + o))[e] = x;
+    }
   }
 }
 
 template <bool BF16, int D, bool CAUSAL, bool HAS_BIAS>
-hipError_t launch_bwd_t(const BwdArgs& a, int64_t q_items, int64_t k_items, hipStream_t st) {
+hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, int64_t k_items,
+                        hipStream_t st) {
   {
     constexpr int EPV = BF16 ? 8 : 4;
     const int64_t threads = (int64_t)a.total_q * a.hq * (D / EPV);
-    const int64_t grid = (threads + NT - 1) / NT;
-    timing_before(st, "bwd_dsum");
-    hipLaunchKernelGGL((dsum_kernel<BF16, D>), dim3((unsigned)grid), dim3(NT), 0, st, a);
+    const int64_t grid = 2 + (threads + plan::PT - 1) / plan::PT;
+    timing_before(st, "bwd_plan_dsum");
+    hipLaunchKernelGGL((plan_dsum_kernel<BF16, D>), dim3((unsigned)grid), dim3(plan::PT), 0, st, a, ps);
     timing_after(st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     auto kern = dkdv_kernel<BF16, D, CAUSAL, HAS_BIAS>;
-    const int hsplit = a.hsplit;
-    const int grid = resident_grid((const void*)kern, NT, k_items * hsplit);
+    const int grid = resident_grid((const void*)kern, NT, k_items);
     if (grid <= 0) return hipErrorInvalidConfiguration;
     timing_before(st, BF16 ? "bwd_dkdv_bf16" : "bwd_dkdv_f32");
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a, hsplit, a.part);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
     timing_after(st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (hsplit > 1) {
-      const size_t n4 = (size_t)a.total_k * a.hkv * D / 4;
-      int64_t g = (int64_t)((n4 + NT - 1) / NT);
+    if (a.split_cap_k > 0) {
+      int64_t g = (int64_t)a.split_cap_k * a.hkv * (BNK / kMergeKeys);
       if (g > 4096) g = 4096;
-      timing_before(st, "bwd_dkdv_reduce");
-      hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)g), dim3(NT), 0, st, a, hsplit,
-                         (const float*)a.part);
+      timing_before(st, "bwd_dkdv_merge");
+      hipLaunchKernelGGL(dkdv_merge_kernel<D>, dim3((unsigned)g), dim3(NT), 0, st, a);
       timing_after(st);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -645,31 +766,47 @@ hipError_t launch_bwd_t(const BwdArgs& a, int64_t q_items, int64_t k_items, hipS
     timing_before(st, BF16 ? "bwd_dq_bf16" : "bwd_dq_f32");
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
     timing_after(st);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.split_cap_q > 0) {
+      int64_t g = (int64_t)a.split_cap_q * a.hq * (BMQ_DQ / kMergeRows);
+      if (g > 4096) g = 4096;
+      timing_before(st, "bwd_dq_merge");
+      hipLaunchKernelGGL(dq_merge_kernel<D>, dim3((unsigned)g), dim3(NT), 0, st, a);
+      timing_after(st);
+    }
   }
   return hipGetLastError();
 }
 
 template <bool BF16, int D>
-hipError_t launch_bwd_d(const BwdArgs& a, int64_t q_items, int64_t k_items, hipStream_t st) {
+hipError_t launch_bwd_d(const BwdArgs& a, const PlanSet& ps, int64_t q_items, int64_t k_items,
+                        hipStream_t st) {
   const bool hb = a.bias != nullptr;
   if (a.causal)
-    return hb ? launch_bwd_t<BF16, D, true, true>(a, q_items, k_items, st)
-              : launch_bwd_t<BF16, D, true, false>(a, q_items, k_items, st);
-  return hb ? launch_bwd_t<BF16, D, false, true>(a, q_items, k_items, st)
-            : launch_bwd_t<BF16, D, false, false>(a, q_items, k_items, st);
+    return hb ? launch_bwd_t<BF16, D, true, true>(a, ps, q_items, k_items, st)
+              : launch_bwd_t<BF16, D, true, false>(a, ps, q_items, k_items, st);
+  return hb ? launch_bwd_t<BF16, D, false, true>(a, ps, q_items, k_items, st)
+            : launch_bwd_t<BF16, D, false, false>(a, ps, q_items, k_items, st);
 }
 
 }  // namespace
 
 int bwd_block_q() { return BMQ_DQ; }
 int bwd_block_k() { return BNK; }
+int bwd_dkdv_block_q() { return BMQ; }
+int bwd_dq_block_n(bool bf16, int d) {
+  if (bf16) return d == 64 ? DqSmem<true, 64>::BN : DqSmem<true, 128>::BN;
+  return d == 64 ? DqSmem<false, 64>::BN : DqSmem<false, 128>::BN;
+}
 
-hipError_t launch_bwd(const BwdArgs& a, int64_t q_items, int64_t k_items, hipStream_t st) {
+hipError_t launch_bwd(const BwdArgs& a, const PlanSet& ps, int64_t q_items, int64_t k_items,
+                      hipStream_t st) {
   if (a.bf16)
-    return a.d == 64 ? launch_bwd_d<true, 64>(a, q_items, k_items, st)
-                     : launch_bwd_d<true, 128>(a, q_items, k_items, st);
-  return a.d == 64 ? launch_bwd_d<false, 64>(a, q_items, k_items, st)
-                   : launch_bwd_d<false, 128>(a, q_items, k_items, st);
+    return a.d == 64 ? launch_bwd_d<true, 64>(a, ps, q_items, k_items, st)
+                     : launch_bwd_d<true, 128>(a, ps, q_items, k_items, st);
+  return a.d == 64 ? launch_bwd_d<false, 64>(a, ps, q_items, k_items, st)
+                   : launch_bwd_d<false, 128>(a, ps, q_items, k_items, st);
 }
 
 }  // namespace va

@@ -95,133 +95,13 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int b, int total, 
 }
 
 // ---------------------------------------------------------------------------
-// Tile schedule over (sequence, q-tile, head), built on the device from
-// cu_seqlens so no padded tile is computed and the host never reads device
-// memory.  Tiles are end-aligned: tile t of sequence b covers query rows
-// [Lq - (t+1)*BM, Lq - t*BM) (rows < 0 are absent), so the ragged tile holds
-// the first rows, which see the fewest keys under a bottom-right causal mask.
-// Tiles are ordered heaviest first: level t = 0 (the last rows of every
-// sequence) first, then t = 1, ...; within a level by sequence.  With
-// `stride` > 1, a level groups `stride` consecutive t of a sequence.  The
-// work item index is tile * heads + head (heads fastest, so the query heads
-// that share a KV head run together and share its K/V in L2).
+// Work queue.  A planner kernel writes, per pass, a list of work units sorted
+// by cost (heaviest first) and zeroes hdr[0]; the pass's persistent
+// workgroups then take items in list order with one atomic each, so the
+// heavy units start first and the light ones fill in behind them.
 // ---------------------------------------------------------------------------
-constexpr int kMaxLevels = 512;
-// Per-sequence tile counts cached in LDS when the batch fits (uint16 each).
-constexpr int kMaxSeqCached = 2048;
-
-struct SchedShared {
-  int level_start[kMaxLevels + 1];
-  int full[kMaxLevels + 1];
-  int part[kMaxLevels + 1];
-  uint16_t ntiles[kMaxSeqCached];
-  int total_tiles;
-};
-
-__device__ __forceinline__ int seq_tiles(int len, int bm, int tcap) {
-  int n = (len + bm - 1) / bm;
-  return min(n, tcap);
-}
-
-// Called once per workgroup by all threads.
-__device__ inline void sched_build(SchedShared& s, const int32_t* cu, int batch, int total,
-                                   int bm, int tcap, int stride, int nlev) {
-  const int tid = threadIdx.x;
-  for (int i = tid; i <= nlev; i += blockDim.x) {
-    s.full[i] = 0;
-    s.part[i] = 0;
-  }
-  __syncthreads();
-  for (int b = tid; b < batch; b += blockDim.x) {
-    int q0, q1;
-    seq_bounds(cu, b, total, q0, q1);
-    const int n = seq_tiles(q1 - q0, bm, tcap);
-    if (b < kMaxSeqCached) s.ntiles[b] = (uint16_t)min(n, 65535);
-    const int f = n / stride, rem = n - f * stride;
-    if (f > 0) atomicAdd(&s.full[f - 1], 1);
-    if (rem > 0) atomicAdd(&s.part[f], rem);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    // C(level) = stride * #{b : full levels of b > level} + partial(level)
-    int above = 0;
-    for (int l = nlev - 1; l >= 0; --l) {
-      above += s.full[l];
-      s.full[l] = above;  // now #{b : f_b > l}
-    }
-    int acc = 0;
-    for (int l = 0; l < nlev; ++l) {
-      s.level_start[l] = acc;
-      acc += stride * s.full[l] + s.part[l];
-    }
-    s.level_start[nlev] = acc;
-    s.total_tiles = acc;
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ int sched_ntiles(const SchedShared& s, const int32_t* cu, int b,
-                                            int total, int bm, int tcap) {
-  if (b < kMaxSeqCached) return s.ntiles[b];
-  int q0, q1;
-  seq_bounds(cu, b, total, q0, q1);
-  return seq_tiles(q1 - q0, bm, tcap);
-}
-
-// Maps a tile index to (sequence b, tile t).  Every wave decodes on its own
-// (no barrier, nothing written): within level `lev` the tiles are ordered by
-// sequence, so b is found by counting, 64 sequences per step, the sequences
-// that own tiles in that level.
-__device__ inline void sched_find(const SchedShared& s, const int32_t* cu, int batch, int total,
-                                  int bm, int tcap, int stride, int nlev, int tile, int& b_out,
-                                  int& t_out) {
-  const int lane = threadIdx.x & 63;
-  int lo = 0, hi = nlev - 1;  // largest lev with level_start[lev] <= tile
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s.level_start[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int lev = lo;
-  const int u = tile - s.level_start[lev];
-  const int lo_t = lev * stride;
-  int base = 0, fb = 0, ft = lo_t;
-  for (int chunk = 0; chunk < batch; chunk += 64) {
-    const int b = chunk + lane;
-    int c = 0;
-    if (b < batch) c = min(max(sched_ntiles(s, cu, b, total, bm, tcap) - lo_t, 0), stride);
-    if (stride == 1) {
-      const uint64_t m = __builtin_amdgcn_ballot_w64(c > 0);
-      const int cnt = __builtin_popcountll(m);
-      if (u < base + cnt) {
-        // the (u - base)-th set bit of m
-        const int excl = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(c > 0 && excl == u - base);
-        fb = chunk + (int)__builtin_ctzll(hit);
-        ft = lo_t;
-        break;
-      }
-      base += cnt;
-    } else {
-      int x = c;  // inclusive scan across the wave
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-      }
-      const int tot = __shfl(x, 63, 64);
-      if (u < base + tot) {
-        const int excl = base + x - c;
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(c > 0 && u >= excl && u < excl + c);
-        const int l = (int)__builtin_ctzll(hit);
-        fb = chunk + l;
-        ft = lo_t + (u - (base + __shfl(x, l, 64) - __shfl(c, l, 64)));
-        break;
-      }
-      base += tot;
-    }
-  }
-  b_out = uniform(fb);
-  t_out = uniform(ft);
+__device__ __forceinline__ int queue_take(int* hdr) {
+  return __hip_atomic_fetch_add(hdr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace va

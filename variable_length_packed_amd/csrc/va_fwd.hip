@@ -170,8 +170,8 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
   constexpr int BM = block_m<BF16, D>();
   constexpr int WR = 32 * QT;                 // rows per wave
 
-  __shared__ SchedShared sched;
   __shared__ S sm;
+  __shared__ int s_item;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -179,8 +179,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
   const int hh = lane >> 5;
   const int r32 = lane & 31;
 
-  sched_build(sched, a.cu_q, a.batch, a.total_q, BM, a.tcap, a.stride, a.nlev);
-  const int total_items = sched.total_tiles * a.hq;
+  const int total_items = uniform(a.plan.hdr[1]) * a.hq;
 
   const T* __restrict__ qg = (const T*)a.q;
   const T* __restrict__ kg = (const T*)a.k;
@@ -189,11 +188,17 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
   const size_t qstride = (size_t)a.hq * D;
   const size_t kstride = (size_t)a.hkv * D;
 
-  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
-    const int tile = item / a.hq;
-    const int h = item - tile * a.hq;
-    int b, t;
-    sched_find(sched, a.cu_q, a.batch, a.total_q, BM, a.tcap, a.stride, a.nlev, tile, b, t);
+  if (tid == 0) s_item = queue_take(a.plan.hdr);
+  __syncthreads();
+  for (int item = uniform(s_item); item < total_items; item = uniform(s_item)) {
+    __syncthreads();  // every thread has read s_item
+    int next_item = 0;
+    if (tid == 0) next_item = queue_take(a.plan.hdr);  // published at the end of this item
+    const int unit = item / a.hq;
+    const int h = item - unit * a.hq;
+    const int4 un = a.plan.units[unit];
+    const int b = uniform(un.x), t = uniform(un.y), n0 = uniform(un.z), n1 = uniform(un.w);
+    const int slot = uniform(a.plan.uinfo[unit].x);  // >= 0: a chunk of a split tile
     int q0, q1, k0, k1;
     seq_bounds(a.cu_q, b, a.total_q, q0, q1);
     seq_bounds(a.cu_k, b, a.total_k, k0, k1);
@@ -210,14 +215,17 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     const int kv_hi = CAUSAL ? min(Lk, r1 + off) : Lk;
     const int wave_hi = CAUSAL ? min(Lk, w0 + WR + off) : Lk;
     const bool wave_on = (w0 + WR - 1 >= 0) && wave_hi > 0;
-    const int nblk = kv_hi > 0 ? (kv_hi + BN - 1) / BN : 0;
     // blocks start at key 0; the ragged block (if any) is the last, and with a
     // causal mask the blocks crossing the diagonal are the last ones too, so
     // every masked block comes after every unmasked one.  Blocks before
     // n_plain are unmasked for every wave of the workgroup: the smallest row
-    // of the tile sees keys <= r1 - BM + off.
-    const int kb0 = 0;
+    // of the tile sees keys <= r1 - BM + off.  This unit runs blocks
+    // [n0, n1) of the tile's ceil(kv_hi / BN).
+    const int kb0 = n0 * BN;
+    const int nb = n1 - n0;
     const int n_plain = CAUSAL ? min(max(r1 - BM + off + 1, 0) / BN, kv_hi / BN) : kv_hi / BN;
+    const int j_plain = min(max(n_plain - n0, 0), nb);
+    const int kv_end = min(kv_hi, n1 * BN);  // keys this unit may read
 
     // ---- resources: this sequence's rows of Q/O for head h and of K/V for head g
     constexpr int ELT = (int)sizeof(T);
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     const rsrc_t qres = make_rsrc(qg + qoff, qbytes);
     const rsrc_t ores = make_rsrc(og + qoff, qbytes);
     const size_t koff = (size_t)k0 * kstride + (size_t)g * D;
-    const int64_t kbytes = kv_hi > 0 ? (int64_t)(kv_hi - 1) * krow_bytes + D * ELT : 0;
+    const int64_t kbytes = kv_end > 0 ? (int64_t)(kv_end - 1) * krow_bytes + D * ELT : 0;
     const rsrc_t kres = make_rsrc(kg + koff, kbytes);
     const rsrc_t vres = make_rsrc(vg + koff, kbytes);
 
@@ -434,7 +442,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     // n+1 (MFMA) while it runs the softmax of block n (VALU), then PV of block
     // n; it stages K(n+2) into the K buffer block n used and V(n+1) into the V
     // buffer block n-1 used, so one barrier per block suffices.
-    auto active = [&](int n) { return n < nblk && wave_on && kb0 + n * BN < wave_hi; };
+    auto active = [&](int j) { return j < nb && wave_on && kb0 + j * BN < wave_hi; };
     ld.load_k(kres, krow_bytes, kb0);
     ld.load_v(vres, krow_bytes, kb0);
     ld.store_k(sm, 0);
@@ -446,7 +454,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     if (active(0)) qk(0, s_cur);
     __syncthreads();  // every wave has read K(0) before K(2) replaces it
 
-    auto step = [&](auto mask_tag, int n) {
+    auto step = [&](auto mask_tag, int n) {  // n: block index inside the unit
       const int kb = kb0 + n * BN;
       ld.load_k(kres, krow_bytes, kb + 2 * BN);  // past the last block every row reads as zero
       ld.load_v(vres, krow_bytes, kb + BN);
@@ -463,35 +471,109 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     };
     // unmasked blocks, then the (at most a few) masked ones: two loops, so the
     // accumulators never merge from two code paths inside a loop
-    int n = 0;
-    for (; n < n_plain; ++n) step(std::integral_constant<bool, false>(), n);
-    for (; n < nblk; ++n) step(std::integral_constant<bool, true>(), n);
+    int j = 0;
+    for (; j < j_plain; ++j) step(std::integral_constant<bool, false>(), j);
+    for (; j < nb; ++j) step(std::integral_constant<bool, true>(), j);
 
-    // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
+    // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; a chunk of a split
+    // tile stores O and the base-2 LSE in float32 to its slot instead
+    const int row_base = r1 - BM;  // tile row 0
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float l_tot = l_run[qt] + xor32(l_run[qt]);
       const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float lse2 = l_tot > 0.f ? m_run[qt] + __builtin_log2f(l_tot) : -INFINITY;
+      if (slot < 0) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int d0 = 32 * dt + 8 * a4 + 4 * hh;
-          const float o0 = acc[qt][dt][4 * a4 + 0] * inv_l, o1 = acc[qt][dt][4 * a4 + 1] * inv_l;
-          const float o2 = acc[qt][dt][4 * a4 + 2] * inv_l, o3 = acc[qt][dt][4 * a4 + 3] * inv_l;
-          // rows < 0 fall outside the resource: the store is dropped
-          if constexpr (BF16) {
-            buf_store8((u32x2_t){pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)}, ores, rq[qt] * qrow_bytes + d0 * 2);
-          } else {
-            buf_store16((u32x4_t){__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2),
-                                  __float_as_uint(o3)}, ores, rq[qt] * qrow_bytes + d0 * 4);
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const int d0 = 32 * dt + 8 * a4 + 4 * hh;
+            const float o0 = acc[qt][dt][4 * a4 + 0] * inv_l, o1 = acc[qt][dt][4 * a4 + 1] * inv_l;
+            const float o2 = acc[qt][dt][4 * a4 + 2] * inv_l, o3 = acc[qt][dt][4 * a4 + 3] * inv_l;
+            // rows < 0 fall outside the resource: the store is dropped
+            if constexpr (BF16) {
+              buf_store8((u32x2_t){pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)}, ores, rq[qt] * qrow_bytes + d0 * 2);
+            } else {
+              buf_store16((u32x4_t){__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2),
+                                    __float_as_uint(o3)}, ores, rq[qt] * qrow_bytes + d0 * 4);
+            }
           }
-        }
-      if (rq[qt] >= 0 && hh == 0) {
-        const float lse = l_tot > 0.f ? (m_run[qt] + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
-        a.lse[(size_t)h * a.total_q + q0 + rq[qt]] = lse;
+        if (rq[qt] >= 0 && hh == 0) a.lse[(size_t)h * a.total_q + q0 + rq[qt]] = lse2 * kLn2;
+      } else {
+        const int rl = rq[qt] - row_base;  // 0 .. BM-1
+        float* po = a.part_o + ((size_t)slot * a.hq + h) * BM * D + (size_t)rl * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int a4 = 0; a4 < 4; ++a4) {
+            const int d0 = 32 * dt + 8 * a4 + 4 * hh;
+            *(f32x4_t*)(po + d0) = (f32x4_t){acc[qt][dt][4 * a4 + 0] * inv_l, acc[qt][dt][4 * a4 + 1] * inv_l,
+                                             acc[qt][dt][4 * a4 + 2] * inv_l, acc[qt][dt][4 * a4 + 3] * inv_l};
+          }
+        if (hh == 0) a.part_lse[((size_t)slot * a.hq + h) * BM + rl] = lse2;
       }
     }
+    if (tid == 0) s_item = next_item;
+    __syncthreads();
+  }
+}
+
+// Merges the chunks of split tiles: per query row, LSE = log2 sum_c 2^LSE_c
+// and O = sum_c 2^(LSE_c - LSE) O_c, summed in chunk order (deterministic).
+// A work item is 32 rows of one (split tile, head); eight threads per row.
+constexpr int kMergeRows = 32;
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(NT) void fwd_merge_kernel(FwdArgs a) {
+  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int BM = block_m<BF16, D>();
+  constexpr int SLABS = BM / kMergeRows;
+  constexpr int TPR = NT / kMergeRows;  // threads per row
+  constexpr int SEG = D / TPR;          // dims per thread
+  const int total = uniform(a.plan.hdr[2]) * a.hq * SLABS;
+  const int rs = threadIdx.x / TPR, seg = threadIdx.x % TPR;
+  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+    const int slab = it % SLABS, sh = it / SLABS;
+    const int si = sh / a.hq, h = sh - si * a.hq;
+    const int4 sp = a.plan.splits[si];
+    const int b = uniform(sp.x), t = uniform(sp.y), sb = uniform(sp.z), nch = uniform(sp.w);
+    int q0, q1;
+    seq_bounds(a.cu_q, b, a.total_q, q0, q1);
+    const int row = slab * kMergeRows + rs;         // row inside the tile
+    const int rq = (q1 - q0) - (t + 1) * BM + row;  // row inside the sequence
+    if (rq < 0) continue;
+    const size_t pi0 = (size_t)sb * a.hq + h;       // slot of chunk c: pi0 + c * hq
+    float mx = -INFINITY;
+#pragma unroll 4
+    for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.part_lse[(pi0 + (size_t)c * a.hq) * BM + row]);
+    f32x4_t acc[SEG / 4];
+#pragma unroll
+    for (int e = 0; e < SEG / 4; ++e) acc[e] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll 4
+      for (int c = 0; c < nch; ++c) {
+        const size_t pi = pi0 + (size_t)c * a.hq;
+        const float w = fast_exp2(a.part_lse[pi * BM + row] - mx);
+        wsum += w;
+        const f32x4_t* src = (const f32x4_t*)(a.part_o + (pi * BM + row) * D + seg * SEG);
+#pragma unroll
+        for (int e = 0; e < SEG / 4; ++e) acc[e] += w * src[e];
+      }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    T* dst = (T*)a.out + ((size_t)(q0 + rq) * a.hq + h) * D + seg * SEG;
+#pragma unroll
+    for (int e = 0; e < SEG / 4; ++e) {
+      const f32x4_t x = acc[e] * inv;
+      if constexpr (BF16)
+        *(u32x2_t*)(dst + 4 * e) = (u32x2_t){pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      else
+        *(f32x4_t*)(dst + 4 * e) = x;
+    }
+    if (seg == 0)
+      a.lse[(size_t)h * a.total_q + q0 + rq] = wsum > 0.f ? (mx + __builtin_log2f(wsum)) * kLn2 : -INFINITY;
   }
 }
 
@@ -504,6 +586,13 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int64_t items, hipStream_t st) 
   if (grid <= 0) return hipErrorInvalidConfiguration;
   timing_before(st, BF16 ? "fwd_bf16" : "fwd_f32");
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
+  timing_after(st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.split_cap <= 0) return e;
+  int64_t mg = (int64_t)a.split_cap * a.hq * (block_m<BF16, D>() / kMergeRows);
+  if (mg > 4096) mg = 4096;
+  timing_before(st, "fwd_merge");
+  hipLaunchKernelGGL((fwd_merge_kernel<BF16, D>), dim3((unsigned)mg), dim3(NT), 0, st, a);
   timing_after(st);
   return hipGetLastError();
 }
@@ -518,9 +607,10 @@ static hipError_t launch_fwd_d(const FwdArgs& a, int64_t grid, hipStream_t st) {
                   : launch_fwd_t<BF16, D, false, false>(a, grid, st);
 }
 
-int fwd_block_m(bool bf16, int d) {
-  if (bf16) return d == 64 ? block_m<true, 64>() : block_m<true, 128>();
-  return d == 64 ? block_m<false, 64>() : block_m<false, 128>();
+int fwd_block_m() { return block_m<true, 64>(); }
+int fwd_block_n(bool bf16, int d) {
+  if (bf16) return d == 64 ? BlockN<true, 64>::value : BlockN<true, 128>::value;
+  return d == 64 ? BlockN<false, 64>::value : BlockN<false, 128>::value;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int64_t grid, hipStream_t st) {

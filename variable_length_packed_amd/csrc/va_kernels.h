@@ -7,6 +7,43 @@
 
 namespace va {
 
+// ---------------------------------------------------------------------------
+// Work plans.  A pass tiles one side of every sequence (query rows for the
+// forward and dQ, key rows for dK/dV) and walks the other side in steps (key
+// blocks, or query blocks).  A tile with more steps than `chunk` is split
+// into nch = ceil(steps / chunk) units of near-equal step ranges; each unit
+// of a split tile writes float32 partial results to its own slot and a merge
+// kernel combines the nch slots in chunk order.  The split rule depends only
+// on the tile's own sequence, so a sequence's results never depend on the
+// rest of the batch.  Units are listed by step count, largest first.
+// ---------------------------------------------------------------------------
+struct Plan {
+  int* hdr;        // [0] queue cursor (zeroed by the planner), [1] units, [2] split tiles
+  int4* units;     // [unit_cap] {sequence, tile, first step, end step}
+  int4* uinfo;     // [unit_cap] {partial slot or -1, split index, chunk, chunks}
+  int4* splits;    // [split_cap] {sequence, tile, first slot, chunks}
+};
+
+struct PlanArgs {
+  Plan plan;
+  const int32_t* cu_t;  // cu_seqlens of the tiled side
+  const int32_t* cu_o;  // cu_seqlens of the stepped side
+  int32_t total_t, total_o, batch;
+  int32_t tile;    // rows per tile
+  int32_t step;    // rows of the other side per step
+  int32_t kside;   // 0: query tiles, end-aligned, steps over keys [0, kv_hi)
+                   // 1: key tiles, start-aligned, steps over queries [qs, Lq)
+  int32_t causal;
+  int32_t chunk;   // most steps per unit
+  int32_t unit_cap, slot_cap, split_cap;
+};
+
+struct PlanSet {
+  PlanArgs p[2];
+};
+
+hipError_t launch_plan(const PlanSet& s, int nplans, hipStream_t st);
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -17,10 +54,11 @@ struct FwdArgs {
   int64_t bs0, bs1, bs2, bs3;
   void* out;
   float* lse;
+  Plan plan;
+  float* part_o;    // [slot][hq][BM][d]  normalised partial outputs of split tiles
+  float* part_lse;  // [slot][hq][BM]     their base-2 log-sum-exp
   int32_t batch, total_q, total_k, hq, hkv, n_rep, d;
-  int32_t tcap;    // q-tiles per sequence considered (from max_seqlen_q)
-  int32_t stride;  // q-tiles per schedule level
-  int32_t nlev;    // schedule levels
+  int32_t split_cap;
   float scale_log2;
   int32_t causal;
   int32_t bf16;
@@ -40,12 +78,13 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;  // workspace [hq, total_q]: rowsum(dO * O)
-  float* part;  // workspace [2 * hsplit][total_k, hkv, d]: dK/dV partial sums (hsplit > 1)
-  int32_t hsplit;  // workgroups sharing one GQA group's query heads (1 or n_rep)
+  float* dsum;     // workspace [hq, total_q]: rowsum(dO * O)
+  Plan plan_k;     // dK/dV pass: key tiles
+  Plan plan_q;     // dQ pass: query tiles
+  float* part_kv;  // [slot][hkv][2][BNK][d]  dK (unscaled) and dV partial sums
+  float* part_q;   // [slot][hq][BMQ][d]      dQ (unscaled) partial sums
   int32_t batch, total_q, total_k, hq, hkv, n_rep, d;
-  int32_t tcap_q, stride_q, nlev_q;  // schedule over q-tiles (dQ kernel)
-  int32_t tcap_k, stride_k, nlev_k;  // schedule over k-tiles (dK/dV kernel)
+  int32_t split_cap_k, split_cap_q;
   float scale;
   float scale_log2;
   int32_t causal;
@@ -60,11 +99,17 @@ void timing_after(hipStream_t st);
 // Persistent grids: min(max_items, resident workgroups per device).
 int resident_grid(const void* kernel, int threads, int64_t max_items);
 
-int fwd_block_m(bool bf16, int d);
+// Tile and step sizes of each pass (the planner and the kernels must agree).
+int fwd_block_m();
+int fwd_block_n(bool bf16, int d);
 hipError_t launch_fwd(const FwdArgs& a, int64_t max_items, hipStream_t st);
 
-int bwd_block_q();
-int bwd_block_k();
-hipError_t launch_bwd(const BwdArgs& a, int64_t max_q_items, int64_t max_k_items, hipStream_t st);
+int bwd_block_q();                   // query rows per dQ tile
+int bwd_block_k();                   // key rows per dK/dV tile
+int bwd_dq_block_n(bool bf16, int d);  // keys per dQ step
+int bwd_dkdv_block_q();              // queries per dK/dV step
+// Launches the fused planner + D preprocess (plans ps.p[0] = dK/dV, ps.p[1] = dQ), then the passes.
+hipError_t launch_bwd(const BwdArgs& a, const PlanSet& ps, int64_t max_q_items, int64_t max_k_items,
+                      hipStream_t st);
 
 }  // namespace va

@@ -1,0 +1,202 @@
+// Planner body (see va_plan.hip): device code shared by the forward's
+// planner kernel and the backward's fused planner + preprocess kernel.  Must
+// run in a workgroup of PT threads.
+#pragma once
+#include <limits.h>
+
+#include "va_common.h"
+#include "va_kernels.h"
+
+namespace va {
+namespace plan {
+
+constexpr int PT = 1024;    // planner threads
+constexpr int NBIN = 2048;  // step-count bins (larger counts share the last bin)
+
+// Steps of tile t of a sequence (Lt rows on the tiled side, Lo on the other).
+__device__ __forceinline__ int tile_steps(const PlanArgs& p, int Lt, int Lo, int t) {
+  if (p.kside == 0) {
+    // query tile t covers rows [Lq - (t+1)*tile, Lq - t*tile); with the
+    // bottom-right causal mask its last row sees keys < r1 + Lk - Lq
+    const int Lq = Lt, Lk = Lo;
+    const int r1 = Lq - t * p.tile;
+    int hi = p.causal ? min(Lk, r1 + (Lk - Lq)) : Lk;
+    hi = max(hi, 0);
+    return (hi + p.step - 1) / p.step;
+  }
+  // key tile t covers keys [t*tile, (t+1)*tile); causal: query i sees key j
+  // iff j <= i + Lk - Lq, so the first query that sees the tile is kt0 - off
+  const int Lk = Lt, Lq = Lo;
+  const int kt0 = t * p.tile;
+  const int qs = p.causal ? max(0, kt0 - (Lk - Lq)) : 0;
+  return qs < Lq ? (Lq - qs + p.step - 1) / p.step : 0;
+}
+
+__device__ __forceinline__ int chunks_of(int steps, int chunk) {
+  return steps > chunk ? (steps + chunk - 1) / chunk : 1;
+}
+
+// Chunk c of a tile of s = q * nch + r steps (0 <= r < nch): the first r
+// chunks have q + 1 steps, the others q.
+__device__ __forceinline__ void chunk_range(int q, int r, int c, int& n0, int& n1) {
+  n0 = c * q + min(c, r);
+  n1 = n0 + q + (c < r ? 1 : 0);
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// Visits every tile of the plan's sequences, spread over the threads: the
+// sequences are taken MAXB at a time; their tile counts are scanned in LDS
+// and each thread finds the sequence of its tile by binary search.
+constexpr int MAXB = 2048;
+
+struct PlanShared {
+  int bins[NBIN];
+  int tstart[MAXB + 1];  // exclusive scan of the tile counts of the current block of sequences
+  int lt[MAXB];          // tiled-side length
+  int lo[MAXB];          // other-side length
+  int wsum[PT / 64];
+  int n_units, n_slots, n_splits, slot_ctr, split_ctr;
+};
+
+// Block-wide exclusive scan of one int per thread; returns the total.
+__device__ inline int block_scan(int x, int* wsum, int& excl) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < PT / 64; ++w) {
+    const int v = wsum[w];
+    if (w < wid) before += v;
+    total += v;
+  }
+  excl = before + incl - x;
+  __syncthreads();
+  return total;
+}
+
+template <typename F>
+__device__ void for_each_tile(const PlanArgs& p, PlanShared& sh, F&& f) {
+  for (int b0 = 0; b0 < p.batch; b0 += MAXB) {
+    const int nb = min(MAXB, p.batch - b0);
+    // two sequences per thread (PT * 2 == MAXB)
+    int cnt[2] = {0, 0};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * threadIdx.x + e;
+      if (i < nb) {
+        int t0, t1, o0, o1;
+        seq_bounds(p.cu_t, b0 + i, p.total_t, t0, t1);
+        seq_bounds(p.cu_o, b0 + i, p.total_o, o0, o1);
+        sh.lt[i] = t1 - t0;
+        sh.lo[i] = o1 - o0;
+        cnt[e] = (t1 - t0 + p.tile - 1) / p.tile;
+      }
+    }
+    int excl;
+    const int ntiles = block_scan(cnt[0] + cnt[1], sh.wsum, excl);
+    if (2 * threadIdx.x < nb) sh.tstart[2 * threadIdx.x] = excl;
+    if (2 * threadIdx.x + 1 < nb) sh.tstart[2 * threadIdx.x + 1] = excl + cnt[0];
+    if (threadIdx.x == 0) sh.tstart[nb] = ntiles;
+    __syncthreads();
+    for (int i = threadIdx.x; i < ntiles; i += PT) {
+      int lo_ = 0, hi_ = nb - 1;  // last sequence with tstart <= i
+      while (lo_ < hi_) {
+        const int mid = (lo_ + hi_ + 1) >> 1;
+        if (sh.tstart[mid] <= i) lo_ = mid; else hi_ = mid - 1;
+      }
+      f(b0 + lo_, i - sh.tstart[lo_], sh.lt[lo_], sh.lo[lo_]);
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
+  static_assert(2 * PT == MAXB, "two sequences per thread");
+  const int tid = threadIdx.x;
+
+  // (1) count, at most twice
+  int chunk = max(p.chunk, 1);
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int i = tid; i < NBIN; i += PT) sh.bins[i] = 0;
+    if (tid == 0) { sh.n_units = 0; sh.n_slots = 0; sh.n_splits = 0; }
+    __syncthreads();
+    int mu = 0, ms = 0, mp = 0;
+    for_each_tile(p, sh, [&](int b, int t, int Lt, int Lo) {
+      const int s = tile_steps(p, Lt, Lo, t);
+      const int nch = chunks_of(s, chunk);
+      mu += nch;
+      if (nch > 1) { ms += nch; mp += 1; }
+      const int q = s / nch, r = s - q * nch;  // r chunks of q + 1 steps, nch - r of q
+      if (r > 0) atomicAdd(&sh.bins[min(q + 1, NBIN - 1)], r);
+      atomicAdd(&sh.bins[min(q, NBIN - 1)], nch - r);
+    });
+    mu = wave_sum(mu);
+    ms = wave_sum(ms);
+    mp = wave_sum(mp);
+    if ((tid & 63) == 0) {
+      atomicAdd(&sh.n_units, mu);
+      atomicAdd(&sh.n_slots, ms);
+      atomicAdd(&sh.n_splits, mp);
+    }
+    __syncthreads();
+    const bool fits = sh.n_slots <= p.slot_cap && sh.n_splits <= p.split_cap && sh.n_units <= p.unit_cap;
+    __syncthreads();
+    if (fits || chunk == INT_MAX) break;
+    chunk = INT_MAX;  // no split at all
+  }
+
+  // (2) exclusive scan from the top bin down: thread i owns bins
+  // NBIN-1-2i and NBIN-2-2i
+  static_assert(2 * PT == NBIN, "two bins per thread");
+  const int hiB = NBIN - 1 - 2 * tid, loB = hiB - 1;
+  const int c_hi = sh.bins[hiB], c_lo = sh.bins[loB];
+  int excl;
+  block_scan(c_hi + c_lo, sh.wsum, excl);
+  sh.bins[hiB] = excl;
+  sh.bins[loB] = excl + c_hi;
+  if (tid == 0) { sh.slot_ctr = 0; sh.split_ctr = 0; }
+  __syncthreads();
+
+  // (3) place
+  for_each_tile(p, sh, [&](int b, int t, int Lt, int Lo) {
+    const int s = tile_steps(p, Lt, Lo, t);
+    const int nch = chunks_of(s, chunk);
+    int sp = -1, sb = -1;
+    if (nch > 1) {
+      sp = atomicAdd(&sh.split_ctr, 1);
+      sb = atomicAdd(&sh.slot_ctr, nch);
+      if (sp < p.split_cap) p.plan.splits[sp] = make_int4(b, t, sb, nch);
+    }
+    const int q = s / nch, r = s - q * nch;
+    int pos_hi = r > 0 ? atomicAdd(&sh.bins[min(q + 1, NBIN - 1)], r) : 0;
+    int pos_lo = atomicAdd(&sh.bins[min(q, NBIN - 1)], nch - r);
+    for (int c = 0; c < nch; ++c) {
+      int n0, n1;
+      chunk_range(q, r, c, n0, n1);
+      const int pos = c < r ? pos_hi++ : pos_lo++;
+      if (pos < p.unit_cap) {
+        p.plan.units[pos] = make_int4(b, t, n0, n1);
+        p.plan.uinfo[pos] = make_int4(nch > 1 ? sb + c : -1, sp, c, nch);
+      }
+    }
+  });
+  if (tid == 0) {
+    p.plan.hdr[0] = 0;
+    p.plan.hdr[1] = min(sh.n_units, p.unit_cap);
+    p.plan.hdr[2] = min(sh.n_splits, p.split_cap);
+  }
+}
+
+}  // namespace plan
+}  // namespace va
