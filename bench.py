@@ -115,6 +115,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="3", help="config id for the step (default 3)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run 3 device-to-device copies of MIB MiB (a kernel of known HBM "
+                         "traffic, to scale hardware byte counters against)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; every box here has one "
@@ -216,10 +219,14 @@ def main() -> int:
     x2 = dev_inputs(w2, with_dout=False)
     o2 = torch.empty_like(x2["q"])
     l2 = torch.empty((w2.hq, w2.total_q), dtype=torch.float32, device=dev)
+    ws2 = torch.empty(va.va_varlen_fwd_workspace_size(w2.batch, w2.total_q, w2.total_k, w2.max_q,
+                                                      w2.max_k, w2.hq, w2.hkv, w2.d,
+                                                      torch.bfloat16),
+                      dtype=torch.uint8, device=dev)
 
     def fwd2():
         va.va_varlen_fwd(x2["q"], x2["k"], x2["v"], x2["cu_q"], x2["cu_k"], w2.max_q, w2.max_k,
-                         w2.scale, True, out=o2, lse=l2)
+                         w2.scale, True, out=o2, lse=l2, workspace=ws2)
 
     for _ in range(args.warmup):
         fwd2()
@@ -261,6 +268,15 @@ def main() -> int:
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = nbytes
     print(json.dumps(line), flush=True)
     return 0
 
