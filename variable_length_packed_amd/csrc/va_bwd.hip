@@ -29,10 +29,10 @@
 // query row past it (its staged LSE is +inf, so its P is 0).  Only tiles that
 // cross the causal diagonal take the masked path, in a loop of their own.
 //
-// bf16: P and dS are rounded to bf16 for the MFMA.  For dV and dK the rounding
-// error of that operand is carried by a second bf16 operand (the residual
-// x - bf16(x)), so those two contractions are exact to float32 accumulation;
-// dQ uses the plain rounding.
+// bf16: P and dS are rounded to bf16 for the MFMA.  For dK the rounding error
+// of dS is carried by a second bf16 operand (the residual dS - bf16(dS)), so
+// that contraction is exact to float32 accumulation; dV (P >= 0, errors of
+// both signs cancel) and dQ use the plain rounding.
 #include "va_common.h"
 #include "va_kernels.h"
 #include "va_plan.h"
@@ -294,16 +294,25 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
     const int nm = min(max(n_diag - u0, 0), nb);  // masked blocks of the unit (its first ones)
     const int k_masked = hpw * nm, k_total = hpw * nb;
     const int h_first = g * a.n_rep;
-    auto tile_of = [&](int k, int& r, int& n) {
-      if (k < k_masked) { r = k / nm; n = u0 + (k - r * nm); }
-      else { const int nu = nb - nm, kk = k - k_masked; r = kk / nu; n = u0 + nm + (kk - r * nu); }
+    // block k of the unit is (head r, query block n): the masked blocks first
+    // (heads outer), then the unmasked ones; next_of() gives block k from
+    // block k - 1 (values only, so the cursor stays in scalar registers)
+    auto next_of = [&](int k, int2 c) -> int2 {
+      if (k == k_masked) return make_int2(0, u0 + nm);
+      int r = c.x, n = c.y + 1;
+      if (k < k_masked) {
+        if (n == u0 + nm) { n = u0; ++r; }
+      } else if (n == u1) {
+        n = u0 + nm;
+        ++r;
+      }
+      return make_int2(r, n);
     };
 
     St sq, sd;
     float pl = 0.f, pd = 0.f;  // staged lse2 / dsum of query tid (tid < BMQ)
-    auto issue = [&](int k) {
-      int r, n;
-      tile_of(k, r, n);
+    auto issue = [&](int2 rn) {
+      const int r = rn.x, n = rn.y;
       const int h = h_first + r;
       const int qb = qs + n * BMQ;
       const size_t qoff = (size_t)q0 * qstride + (size_t)h * D;
@@ -327,14 +336,13 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
       if (tid < BMQ) { sm.lse2[buf][tid] = pl; sm.dsum[buf][tid] = pd; }
     };
 
-    auto step = [&](auto mask_tag, int k) {
+    auto step = [&](auto mask_tag, int k, int2 rn, int2 rn_next) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int buf = k & 1;
-      int r, n;
-      tile_of(k, r, n);
+      const int r = rn.x, n = rn.y;
       const int h = h_first + r;
       const int qb = qs + n * BMQ;
-      if (k + 1 < k_total) issue(k + 1);
+      if (k + 1 < k_total) issue(rn_next);
       // this wave's keys are seen by queries i >= wk0 - off
       const bool active = wave_keys && (!CAUSAL || qb + BMQ - 1 + off >= wk0);
       if (active) {
@@ -365,8 +373,8 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
         if constexpr (BF16) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            u32x4_t pa, pa_lo, da, da_lo;
-            pack8(&p[8 * c], pa, &pa_lo);
+            u32x4_t pa, da, da_lo;
+            pack8(&p[8 * c], pa, nullptr);
             pack8(&ds[8 * c], da, &da_lo);
 #pragma unroll
             for (int dt_ = 0; dt_ < DT; ++dt_) {
@@ -374,7 +382,6 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
               const u32x4_t ob = tfrag<BMQ, St::TP>(sm.dt[buf], d, c, hh);
               const u32x4_t qb4 = tfrag<BMQ, St::TP>(sm.qt[buf], d, c, hh);
               dv[dt_] = mfma32_bf16(pa, ob, dv[dt_]);
-              dv[dt_] = mfma32_bf16(pa_lo, ob, dv[dt_]);
               dk[dt_] = mfma32_bf16(da, qb4, dk[dt_]);
               dk[dt_] = mfma32_bf16(da_lo, qb4, dk[dt_]);
             }
@@ -397,40 +404,58 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
       __syncthreads();
     };
 
-    if (k_total > 0) { issue(0); commit(0); }
+    int2 rn = make_int2(0, u0);
+    if (k_total > 0) { issue(rn); commit(0); }
     __syncthreads();
     int k = 0;
-    for (; k < k_masked; ++k) step(std::integral_constant<bool, true>(), k);
-    for (; k < k_total; ++k) step(std::integral_constant<bool, false>(), k);
+    for (; k < k_masked; ++k) {
+      const int2 nx = next_of(k + 1, rn);
+      step(std::integral_constant<bool, true>(), k, rn, nx);
+      rn = nx;
+    }
+    for (; k < k_total; ++k) {
+      const int2 nx = next_of(k + 1, rn);
+      step(std::integral_constant<bool, false>(), k, rn, nx);
+      rn = nx;
+    }
 
-    // ---- epilogue: rows = keys 8(i/4)+4hh+i%4 of the wave, column d = 32dt + r32
+    // ---- epilogue.  Register i of tile dt holds key wk0 + 8(i/4) + 4hh + i%4,
+    // dim 32dt + r32.  Whole tiles: buffer stores whose resource ends at the
+    // sequence's last key (rows past it are dropped).  A chunk of a split tile
+    // stores the registers as they lie (16 bytes per lane, [dt][i/4][lane][4])
+    // into its slot; the merge kernel undoes the layout.
     if (slot < 0) {
+      const int gelt = a.grad_bf16 ? 2 : 4;
+      const int krow = (int)kstride * gelt;
+      const size_t base = (koff + (size_t)max(wk0, 0) * kstride) * gelt;
+      const int64_t nbytes = Lk > wk0 ? (int64_t)(Lk - wk0 - 1) * krow + D * gelt : 0;
+      const rsrc_t rk = make_rsrc((const uint8_t*)a.dk + base, nbytes);
+      const rsrc_t rv = make_rsrc((const uint8_t*)a.dv + base, nbytes);
+      const int lane_off = 4 * hh * krow + r32 * gelt;
 #pragma unroll
       for (int dt_ = 0; dt_ < DT; ++dt_)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = wk0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (key >= Lk) continue;
-          const size_t o = koff + (size_t)key * kstride + 32 * dt_ + r32;
+          const int off = lane_off + (8 * (i >> 2) + (i & 3)) * krow + 32 * dt_ * gelt;
           const float kv = dk[dt_][i] * a.scale, vv = dv[dt_][i];
           if (a.grad_bf16) {
-            ((uint16_t*)a.dk)[o] = (uint16_t)(pack_bf16x2(kv, 0.f) & 0xFFFF);
-            ((uint16_t*)a.dv)[o] = (uint16_t)(pack_bf16x2(vv, 0.f) & 0xFFFF);
+            buf_store2((uint16_t)(pack_bf16x2(kv, 0.f) & 0xFFFF), rk, off);
+            buf_store2((uint16_t)(pack_bf16x2(vv, 0.f) & 0xFFFF), rv, off);
           } else {
-            ((float*)a.dk)[o] = kv;
-            ((float*)a.dv)[o] = vv;
+            buf_store4(__float_as_uint(kv), rk, off);
+            buf_store4(__float_as_uint(vv), rv, off);
           }
         }
     } else {
-      float* pk = a.part_kv + ((size_t)slot * a.hkv + g) * 2 * BNK * D;
+      float* pk = a.part_kv + ((size_t)slot * a.hkv + g) * 2 * BNK * D + (size_t)wid * 32 * D;
       float* pv = pk + BNK * D;
 #pragma unroll
       for (int dt_ = 0; dt_ < DT; ++dt_)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kl = 32 * wid + 8 * (i >> 2) + 4 * hh + (i & 3);  // key inside the tile
-          pk[kl * D + 32 * dt_ + r32] = dk[dt_][i];
-          pv[kl * D + 32 * dt_ + r32] = dv[dt_][i];
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int o = ((dt_ * 4 + i4) * 64 + lane) * 4;
+          *(f32x4_t*)(pk + o) = (f32x4_t){dk[dt_][4 * i4], dk[dt_][4 * i4 + 1], dk[dt_][4 * i4 + 2], dk[dt_][4 * i4 + 3]};
+          *(f32x4_t*)(pv + o) = (f32x4_t){dv[dt_][4 * i4], dv[dt_][4 * i4 + 1], dv[dt_][4 * i4 + 2], dv[dt_][4 * i4 + 3]};
         }
     }
     if (tid == 0) s_item = next_item;
@@ -439,50 +464,49 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
 }
 
 // Sums the chunks of split dK/dV tiles in chunk order (deterministic) and
-// writes the gradients.  A work item is 16 keys of one (split tile, KV
-// head); sixteen threads per key.
-constexpr int kMergeKeys = 16;
-
+// writes the gradients.  A work item is one wave's 32 keys of one (split
+// tile, KV head); a thread owns 16-byte pieces of the partials' register
+// layout [dt][i/4][lane][4], i.e. 4 consecutive keys of one dim.
 template <int D>
 __global__ __launch_bounds__(NT) void dkdv_merge_kernel(BwdArgs a) {
-  constexpr int SLABS = BNK / kMergeKeys;
-  constexpr int TPR = NT / kMergeKeys;
-  constexpr int SEG = D / TPR;
-  const int total = uniform(a.plan_k.hdr[2]) * a.hkv * SLABS;
-  const int ks = threadIdx.x / TPR, seg = threadIdx.x % TPR;
+  constexpr int DT = D / 32;
+  constexpr int PIECES = DT * 4 * 64;       // 16-byte pieces per wave block
+  constexpr int PPT = PIECES / NT;          // per thread
+  const int total = uniform(a.plan_k.hdr[2]) * a.hkv * 4;
   for (int it = blockIdx.x; it < total; it += gridDim.x) {
-    const int slab = it % SLABS, sg = it / SLABS;
+    const int w = it & 3, sg = it >> 2;
     const int si = sg / a.hkv, g = sg - si * a.hkv;
     const int4 sp = a.plan_k.splits[si];
     const int b = uniform(sp.x), t = uniform(sp.y), sb = uniform(sp.z), nch = uniform(sp.w);
     int k0, k1;
     seq_bounds(a.cu_k, b, a.total_k, k0, k1);
-    const int kl = slab * kMergeKeys + ks;  // key inside the tile
-    const int key = t * BNK + kl;
-    if (key >= k1 - k0) continue;
-    f32x4_t sk[SEG / 4], sv[SEG / 4];
+    const int Lk = k1 - k0;
 #pragma unroll
-    for (int e = 0; e < SEG / 4; ++e) { sk[e] = (f32x4_t){0.f, 0.f, 0.f, 0.f}; sv[e] = sk[e]; }
+    for (int pp = 0; pp < PPT; ++pp) {
+      const int piece = threadIdx.x + pp * NT;
+      const int lane = piece & 63, i4 = (piece >> 6) & 3, dt = piece >> 8;
+      const int hh = lane >> 5, r32 = lane & 31;
+      f32x4_t sk = {0.f, 0.f, 0.f, 0.f}, sv = sk;
 #pragma unroll 4
-    for (int c = 0; c < nch; ++c) {
-      const float* pk = a.part_kv + ((size_t)(sb + c) * a.hkv + g) * 2 * BNK * D + kl * D + seg * SEG;
-      const float* pv = pk + BNK * D;
-#pragma unroll
-      for (int e = 0; e < SEG / 4; ++e) {
-        sk[e] += ((const f32x4_t*)pk)[e];
-        sv[e] += ((const f32x4_t*)pv)[e];
+      for (int c = 0; c < nch; ++c) {
+        const float* pk = a.part_kv + ((size_t)(sb + c) * a.hkv + g) * 2 * BNK * D + (size_t)w * 32 * D;
+        sk += *(const f32x4_t*)(pk + piece * 4);
+        sv += *(const f32x4_t*)(pk + BNK * D + piece * 4);
       }
-    }
-    const size_t o = ((size_t)(k0 + key) * a.hkv + g) * D + seg * SEG;
+      const int key0 = t * BNK + 32 * w + 8 * i4 + 4 * hh;  // keys key0 .. key0+3
+      const int d = 32 * dt + r32;
 #pragma unroll
-    for (int e = 0; e < SEG / 4; ++e) {
-      const f32x4_t k4 = sk[e] * a.scale, v4 = sv[e];
-      if (a.grad_bf16) {
-        ((u32x2_t*)((uint16_t*)a.dk + o))[e] = (u32x2_t){pack_bf16x2(k4[0], k4[1]), pack_bf16x2(k4[2], k4[3])};
-        ((u32x2_t*)((uint16_t*)a.dv + o))[e] = (u32x2_t){pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3])};
-      } else {
-        ((f32x4_t*)((float*)a.dk + o))[e] = k4;
-        ((f32x4_t*)((float*)a.dv + o))[e] = v4;
+      for (int j = 0; j < 4; ++j) {
+        if (key0 + j >= Lk) break;
+        const size_t o = ((size_t)(k0 + key0 + j) * a.hkv + g) * D + d;
+        const float kv = sk[j] * a.scale, vv = sv[j];
+        if (a.grad_bf16) {
+          ((uint16_t*)a.dk)[o] = (uint16_t)(pack_bf16x2(kv, 0.f) & 0xFFFF);
+          ((uint16_t*)a.dv)[o] = (uint16_t)(pack_bf16x2(vv, 0.f) & 0xFFFF);
+        } else {
+          ((float*)a.dk)[o] = kv;
+          ((float*)a.dv)[o] = vv;
+        }
       }
     }
   }
@@ -750,7 +774,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.split_cap_k > 0) {
-      int64_t g = (int64_t)a.split_cap_k * a.hkv * (BNK / kMergeKeys);
+      int64_t g = (int64_t)a.split_cap_k * a.hkv * 4;
       if (g > 4096) g = 4096;
       timing_before(st, "bwd_dkdv_merge");
       hipLaunchKernelGGL(dkdv_merge_kernel<D>, dim3((unsigned)g), dim3(NT), 0, st, a);

@@ -68,6 +68,9 @@ __device__ __forceinline__ void buf_store8(u32x2_t v, rsrc_t r, int byte_off) {
 __device__ __forceinline__ void buf_store4(uint32_t v, rsrc_t r, int byte_off) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, byte_off, 0, 0);
 }
+__device__ __forceinline__ void buf_store2(uint16_t v, rsrc_t r, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, byte_off, 0, 0);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
