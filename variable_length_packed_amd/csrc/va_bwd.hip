@@ -263,8 +263,9 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
     const int unit = item / a.hkv;
     const int g = item - unit * a.hkv;
     const int4 un = a.plan_k.units[unit];
-    const int b = uniform(un.x), t = uniform(un.y), u0 = uniform(un.z), u1 = uniform(un.w);
-    const int slot = uniform(a.plan_k.uinfo[unit].x);  // >= 0: a chunk of a split tile
+    const int b = uniform(un.x), t = uniform(un.y);
+    const int u0 = uniform(un.z), u1 = uniform(un.w);
+    const int slot = uniform(a.plan_k.slots[unit]);  // >= 0: a chunk of a split tile
     int q0, q1, k0, k1;
     seq_bounds(a.cu_q, b, a.total_q, q0, q1);
     seq_bounds(a.cu_k, b, a.total_k, k0, k1);
@@ -555,8 +556,9 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     const int unit = item / a.hq;
     const int h = item - unit * a.hq;
     const int4 un = a.plan_q.units[unit];
-    const int b = uniform(un.x), t = uniform(un.y), n0 = uniform(un.z), n1 = uniform(un.w);
-    const int slot = uniform(a.plan_q.uinfo[unit].x);  // >= 0: a chunk of a split tile
+    const int b = uniform(un.x), t = uniform(un.y);
+    const int n0 = uniform(un.z), n1 = uniform(un.w);
+    const int slot = uniform(a.plan_q.slots[unit]);  // >= 0: a chunk of a split tile
     int q0, q1, k0, k1;
     seq_bounds(a.cu_q, b, a.total_q, q0, q1);
     seq_bounds(a.cu_k, b, a.total_k, k0, k1);

@@ -197,8 +197,9 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     const int unit = item / a.hq;
     const int h = item - unit * a.hq;
     const int4 un = a.plan.units[unit];
-    const int b = uniform(un.x), t = uniform(un.y), n0 = uniform(un.z), n1 = uniform(un.w);
-    const int slot = uniform(a.plan.uinfo[unit].x);  // >= 0: a chunk of a split tile
+    const int b = uniform(un.x), t = uniform(un.y);
+    const int n0 = uniform(un.z), n1 = uniform(un.w);
+    const int slot = uniform(a.plan.slots[unit]);  // >= 0: a chunk of a split tile
     int q0, q1, k0, k1;
     seq_bounds(a.cu_q, b, a.total_q, q0, q1);
     seq_bounds(a.cu_k, b, a.total_k, k0, k1);

@@ -20,7 +20,7 @@ namespace va {
 struct Plan {
   int* hdr;        // [0] queue cursor (zeroed by the planner), [1] units, [2] split tiles
   int4* units;     // [unit_cap] {sequence, tile, first step, end step}
-  int4* uinfo;     // [unit_cap] {partial slot or -1, split index, chunk, chunks}
+  int* slots;      // [unit_cap] partial slot of a chunk of a split tile, or -1
   int4* splits;    // [split_cap] {sequence, tile, first slot, chunks}
 };
 

@@ -43,16 +43,16 @@ __device__ __forceinline__ void chunk_range(int q, int r, int c, int& n0, int& n
   n1 = n0 + q + (c < r ? 1 : 0);
 }
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
 
-// Visits every tile of the plan's sequences, spread over the threads: the
-// sequences are taken MAXB at a time; their tile counts are scanned in LDS
-// and each thread finds the sequence of its tile by binary search.
+// Tiles are visited spread over the threads: the sequences are taken MAXB at
+// a time, their tile counts scanned in LDS, and each thread finds the
+// sequence of its tile by binary search.  When the batch fits one such
+// block and has at most TPT * PT tiles (the usual case), every thread keeps
+// its tiles (sequence, tile, steps) in registers, so the later passes
+// neither reload cu_seqlens nor search again.
 constexpr int MAXB = 2048;
+constexpr int TPT = 4;    // cached tiles per thread
+constexpr int NCAND = 6;  // chunk candidates: chunk << 0 .. chunk << 5
 
 struct PlanShared {
   int bins[NBIN];
@@ -60,7 +60,8 @@ struct PlanShared {
   int lt[MAXB];          // tiled-side length
   int lo[MAXB];          // other-side length
   int wsum[PT / 64];
-  int n_units, n_slots, n_splits, slot_ctr, split_ctr;
+  int cnt[NCAND];        // partial slots per chunk candidate
+  int slot_ctr, split_ctr;
 };
 
 // Block-wide exclusive scan of one int per thread; returns the total.
@@ -85,92 +86,152 @@ __device__ inline int block_scan(int x, int* wsum, int& excl) {
   return total;
 }
 
+// Loads the lengths of sequences b0 .. b0+nb-1 and scans their tile counts;
+// returns the number of tiles.
+__device__ inline int load_block(const PlanArgs& p, PlanShared& sh, int b0, int nb) {
+  int cnt[2] = {0, 0};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int i = 2 * threadIdx.x + e;
+    if (i < nb) {
+      int t0, t1, o0, o1;
+      seq_bounds(p.cu_t, b0 + i, p.total_t, t0, t1);
+      seq_bounds(p.cu_o, b0 + i, p.total_o, o0, o1);
+      sh.lt[i] = t1 - t0;
+      sh.lo[i] = o1 - o0;
+      cnt[e] = (t1 - t0 + p.tile - 1) / p.tile;
+    }
+  }
+  int excl;
+  const int ntiles = block_scan(cnt[0] + cnt[1], sh.wsum, excl);
+  if (2 * threadIdx.x < nb) sh.tstart[2 * threadIdx.x] = excl;
+  if (2 * threadIdx.x + 1 < nb) sh.tstart[2 * threadIdx.x + 1] = excl + cnt[0];
+  if (threadIdx.x == 0) sh.tstart[nb] = ntiles;
+  __syncthreads();
+  return ntiles;
+}
+
+// Sequence (inside the block) of tile i: the last one with tstart <= i.
+__device__ __forceinline__ int find_seq(const PlanShared& sh, int nb, int i) {
+  int lo_ = 0, hi_ = nb - 1;
+  while (lo_ < hi_) {
+    const int mid = (lo_ + hi_ + 1) >> 1;
+    if (sh.tstart[mid] <= i) lo_ = mid; else hi_ = mid - 1;
+  }
+  return lo_;
+}
+
+// f(sequence, tile, steps) for every tile (the general path).
 template <typename F>
 __device__ void for_each_tile(const PlanArgs& p, PlanShared& sh, F&& f) {
   for (int b0 = 0; b0 < p.batch; b0 += MAXB) {
     const int nb = min(MAXB, p.batch - b0);
-    // two sequences per thread (PT * 2 == MAXB)
-    int cnt[2] = {0, 0};
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int i = 2 * threadIdx.x + e;
-      if (i < nb) {
-        int t0, t1, o0, o1;
-        seq_bounds(p.cu_t, b0 + i, p.total_t, t0, t1);
-        seq_bounds(p.cu_o, b0 + i, p.total_o, o0, o1);
-        sh.lt[i] = t1 - t0;
-        sh.lo[i] = o1 - o0;
-        cnt[e] = (t1 - t0 + p.tile - 1) / p.tile;
-      }
-    }
-    int excl;
-    const int ntiles = block_scan(cnt[0] + cnt[1], sh.wsum, excl);
-    if (2 * threadIdx.x < nb) sh.tstart[2 * threadIdx.x] = excl;
-    if (2 * threadIdx.x + 1 < nb) sh.tstart[2 * threadIdx.x + 1] = excl + cnt[0];
-    if (threadIdx.x == 0) sh.tstart[nb] = ntiles;
-    __syncthreads();
+    const int ntiles = load_block(p, sh, b0, nb);
     for (int i = threadIdx.x; i < ntiles; i += PT) {
-      int lo_ = 0, hi_ = nb - 1;  // last sequence with tstart <= i
-      while (lo_ < hi_) {
-        const int mid = (lo_ + hi_ + 1) >> 1;
-        if (sh.tstart[mid] <= i) lo_ = mid; else hi_ = mid - 1;
-      }
-      f(b0 + lo_, i - sh.tstart[lo_], sh.lt[lo_], sh.lo[lo_]);
+      const int q = find_seq(sh, nb, i);
+      const int t = i - sh.tstart[q];
+      f(b0 + q, t, tile_steps(p, sh.lt[q], sh.lo[q], t));
     }
     __syncthreads();
   }
 }
 
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
 __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
   static_assert(2 * PT == MAXB, "two sequences per thread");
+  static_assert(2 * PT == NBIN, "two bins per thread");
   const int tid = threadIdx.x;
 
-  // (1) count, at most twice
-  int chunk = max(p.chunk, 1);
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int i = tid; i < NBIN; i += PT) sh.bins[i] = 0;
-    if (tid == 0) { sh.n_units = 0; sh.n_slots = 0; sh.n_splits = 0; }
-    __syncthreads();
-    int mu = 0, ms = 0, mp = 0;
-    for_each_tile(p, sh, [&](int b, int t, int Lt, int Lo) {
-      const int s = tile_steps(p, Lt, Lo, t);
-      const int nch = chunks_of(s, chunk);
-      mu += nch;
-      if (nch > 1) { ms += nch; mp += 1; }
-      const int q = s / nch, r = s - q * nch;  // r chunks of q + 1 steps, nch - r of q
-      if (r > 0) atomicAdd(&sh.bins[min(q + 1, NBIN - 1)], r);
-      atomicAdd(&sh.bins[min(q, NBIN - 1)], nch - r);
-    });
-    mu = wave_sum(mu);
-    ms = wave_sum(ms);
-    mp = wave_sum(mp);
-    if ((tid & 63) == 0) {
-      atomicAdd(&sh.n_units, mu);
-      atomicAdd(&sh.n_slots, ms);
-      atomicAdd(&sh.n_splits, mp);
+  // tile cache (fast path)
+  int cb[TPT], ct[TPT], cs[TPT];
+  bool fast = p.batch <= MAXB;
+  if (fast) {
+    const int ntiles = load_block(p, sh, 0, p.batch);
+    fast = ntiles <= TPT * PT;
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const int i = tid + j * PT;
+      cs[j] = -1;
+      if (fast && i < ntiles) {
+        const int q = find_seq(sh, p.batch, i);
+        cb[j] = q;
+        ct[j] = i - sh.tstart[q];
+        cs[j] = tile_steps(p, sh.lt[q], sh.lo[q], ct[j]);
+      }
     }
     __syncthreads();
-    const bool fits = sh.n_slots <= p.slot_cap && sh.n_splits <= p.split_cap && sh.n_units <= p.unit_cap;
-    __syncthreads();
-    if (fits || chunk == INT_MAX) break;
-    chunk = INT_MAX;  // no split at all
   }
+  auto visit = [&](auto&& f) {
+    if (fast) {
+#pragma unroll
+      for (int j = 0; j < TPT; ++j)
+        if (cs[j] >= 0) f(cb[j], ct[j], cs[j]);
+    } else {
+      for_each_tile(p, sh, f);
+    }
+  };
 
-  // (2) exclusive scan from the top bin down: thread i owns bins
-  // NBIN-1-2i and NBIN-2-2i
-  static_assert(2 * PT == NBIN, "two bins per thread");
+  // (1) partial slots each chunk candidate needs (a split tile of nch chunks
+  // takes nch slots); only lanes with a split tile join the reductions
+  if (tid < NCAND) sh.cnt[tid] = 0;
+  __syncthreads();
+  const int chunk0 = max(p.chunk, 1);
+  {
+    int sl[NCAND];
+#pragma unroll
+    for (int j = 0; j < NCAND; ++j) sl[j] = 0;
+    visit([&](int, int, int s) {
+      // ceil(s / (chunk0 << j)) = ceil(ceil(s / chunk0) / 2^j): one division
+      const int n = (s + chunk0 - 1) / chunk0;
+#pragma unroll
+      for (int j = 0; j < NCAND; ++j) {
+        const int nch = (n + (1 << j) - 1) >> j;
+        if (nch > 1) sl[j] += nch;
+      }
+    });
+#pragma unroll
+    for (int j = 0; j < NCAND; ++j)
+      if (sl[j] > 0) {
+        const int v = (int)__builtin_amdgcn_wave_reduce_add_u32((unsigned)sl[j], 0);
+        const uint64_t m = __builtin_amdgcn_read_exec();
+        if ((int)(threadIdx.x & 63) == (int)__builtin_ctzll(m)) atomicAdd(&sh.cnt[j], v);
+      }
+  }
+  __syncthreads();
+  // the smallest chunk whose partial results fit the workspace (each split
+  // tile takes >= 2 slots, so the split list fits too)
+  int pick = NCAND;
+  for (int j = NCAND - 1; j >= 0; --j)
+    if (sh.cnt[j] <= p.slot_cap) pick = j;
+  const int chunk = pick < NCAND ? chunk0 << pick : INT_MAX;
+
+  // (2) histogram by step count, scanned from the top bin down: thread i
+  // owns bins NBIN-1-2i and NBIN-2-2i
+  for (int i = tid; i < NBIN; i += PT) sh.bins[i] = 0;
+  __syncthreads();
+  visit([&](int, int, int s) {
+    const int nch = chunks_of(s, chunk);
+    const int q = s / nch, r = s - q * nch;  // r chunks of q + 1 steps, nch - r of q
+    if (r > 0) atomicAdd(&sh.bins[min(q + 1, NBIN - 1)], r);
+    atomicAdd(&sh.bins[min(q, NBIN - 1)], nch - r);
+  });
+  __syncthreads();
   const int hiB = NBIN - 1 - 2 * tid, loB = hiB - 1;
   const int c_hi = sh.bins[hiB], c_lo = sh.bins[loB];
   int excl;
-  block_scan(c_hi + c_lo, sh.wsum, excl);
+  const int n_units = block_scan(c_hi + c_lo, sh.wsum, excl);
   sh.bins[hiB] = excl;
   sh.bins[loB] = excl + c_hi;
   if (tid == 0) { sh.slot_ctr = 0; sh.split_ctr = 0; }
   __syncthreads();
 
   // (3) place
-  for_each_tile(p, sh, [&](int b, int t, int Lt, int Lo) {
-    const int s = tile_steps(p, Lt, Lo, t);
+  visit([&](int b, int t, int s) {
     const int nch = chunks_of(s, chunk);
     int sp = -1, sb = -1;
     if (nch > 1) {
@@ -187,14 +248,15 @@ __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
       const int pos = c < r ? pos_hi++ : pos_lo++;
       if (pos < p.unit_cap) {
         p.plan.units[pos] = make_int4(b, t, n0, n1);
-        p.plan.uinfo[pos] = make_int4(nch > 1 ? sb + c : -1, sp, c, nch);
+        p.plan.slots[pos] = nch > 1 ? sb + c : -1;
       }
     }
   });
+  __syncthreads();
   if (tid == 0) {
     p.plan.hdr[0] = 0;
-    p.plan.hdr[1] = min(sh.n_units, p.unit_cap);
-    p.plan.hdr[2] = min(sh.n_splits, p.split_cap);
+    p.plan.hdr[1] = min(n_units, p.unit_cap);
+    p.plan.hdr[2] = min(sh.split_ctr, p.split_cap);
   }
 }
 

@@ -3,11 +3,13 @@
 // on the same stream; it also zeroes the pass's queue cursor, so a call
 // needs no memset and no host read of device memory.
 //
-// Steps: (1) count the units of every tile (tiles spread over the threads)
-// and histogram them by step count; if the split units would not
-// fit the workspace's partial slots, count again without splitting (all or
-// nothing, so the split rule stays per tile); (2) scan the histogram from
-// the largest step count down; (3) place every unit at its bin's cursor.
+// Steps: (1) count, for the fixed chunk and for 2x, 4x, ... 32x it, the units,
+// partial slots and split tiles every tile needs, and take the smallest
+// chunk whose partials fit the workspace (normally the fixed one, so the
+// split of a tile depends on its own sequence only; a batch too large for
+// the workspace gets coarser chunks, or none, rather than failing);
+// (2) histogram the units by step count and scan it from the largest count
+// down; (3) place every unit at its bin's cursor.
 // Within a bin the order is whatever the atomics give: the units of a bin
 // are independent, and a unit's results do not depend on its position.
 #include "va_plan.h"
