@@ -129,7 +129,7 @@ def _r(x):
 
 
 def _plan_bytes(units, splits):
-    return 256 + _r(16 * units) + _r(4 * units) + _r(16 * max(splits, 1))
+    return 256 + 2 * _r(16 * units) + _r(4 * units) + _r(16 * max(splits, 1))
 
 
 def test_fwd_workspace_size(lib):

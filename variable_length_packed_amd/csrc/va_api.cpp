@@ -100,7 +100,7 @@ PlanLayout plan_layout(int total_t, int batch, int tile, int max_other, int step
   L.unit_cap = (int)(tiles + slots);
   L.chunk = chunk;
   L.slot_bytes = slot_bytes;
-  L.plan_bytes = round_up(256) + round_up((size_t)L.unit_cap * 16) + round_up((size_t)L.unit_cap * 4) +
+  L.plan_bytes = round_up(256) + 2 * round_up((size_t)L.unit_cap * 16) + round_up((size_t)L.unit_cap * 4) +
                  round_up((size_t)(L.split_cap > 0 ? L.split_cap : 1) * 16);
   return L;
 }
@@ -110,6 +110,8 @@ size_t carve_plan(char* p, const PlanLayout& L, va::Plan& plan) {
   plan.hdr = (int*)p;
   size_t o = round_up(256);
   plan.units = (int4*)(p + o);
+  o += round_up((size_t)L.unit_cap * 16);
+  plan.bounds = (int4*)(p + o);
   o += round_up((size_t)L.unit_cap * 16);
   plan.slots = (int*)(p + o);
   o += round_up((size_t)L.unit_cap * 4);

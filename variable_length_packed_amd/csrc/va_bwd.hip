@@ -244,7 +244,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
   constexpr int ELT = (int)sizeof(T);
 
   __shared__ SM sm;
-  __shared__ int s_item;
+  __shared__ int s_info[2][10];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
   const int hh = lane >> 5, r32 = lane & 31;
@@ -254,22 +254,20 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
   const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
   const int hpw = a.n_rep;  // every query head of the group
 
-  if (tid == 0) s_item = queue_take(a.plan_k.hdr);
+  if (tid == 0) item_store(s_info[0], item_load(a.plan_k, queue_take(a.plan_k.hdr), a.hkv, total_items));
   __syncthreads();
-  for (int item = uniform(s_item); item < total_items; item = uniform(s_item)) {
-    __syncthreads();  // every thread has read s_item
+  for (int cur = 0;; cur ^= 1) {
+    const int* inf = s_info[cur];
+    const int item = uniform(inf[0]);
+    if (item >= total_items) break;
     int next_item = 0;
-    if (tid == 0) next_item = queue_take(a.plan_k.hdr);  // published at the end of this item
+    if (tid == 0) next_item = queue_take(a.plan_k.hdr);  // its entries are loaded during this item
     const int unit = item / a.hkv;
     const int g = item - unit * a.hkv;
-    const int4 un = a.plan_k.units[unit];
-    const int b = uniform(un.x), t = uniform(un.y);
-    const int u0 = uniform(un.z), u1 = uniform(un.w);
-    const int slot = uniform(a.plan_k.slots[unit]);  // >= 0: a chunk of a split tile
-    int q0, q1, k0, k1;
-    seq_bounds(a.cu_q, b, a.total_q, q0, q1);
-    seq_bounds(a.cu_k, b, a.total_k, k0, k1);
-    q0 = uniform(q0); q1 = uniform(q1); k0 = uniform(k0); k1 = uniform(k1);
+    const int b = uniform(inf[1]), t = uniform(inf[2]);
+    const int u0 = uniform(inf[3]), u1 = uniform(inf[4]);
+    const int k0 = uniform(inf[5]), k1 = uniform(inf[6]), q0 = uniform(inf[7]), q1 = uniform(inf[8]);
+    const int slot = uniform(inf[9]);  // >= 0: a chunk of a split tile
     const int Lq = q1 - q0, Lk = k1 - k0, off = Lk - Lq;
     const int kt0 = t * BNK;
     const int wk0 = kt0 + 32 * wid;  // first key of this wave
@@ -408,6 +406,8 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
     int2 rn = make_int2(0, u0);
     if (k_total > 0) { issue(rn); commit(0); }
     __syncthreads();
+    ItemInfo nxt;
+    if (tid == 0) nxt = item_load(a.plan_k, next_item, a.hkv, total_items);
     int k = 0;
     for (; k < k_masked; ++k) {
       const int2 nx = next_of(k + 1, rn);
@@ -419,6 +419,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
       step(std::integral_constant<bool, false>(), k, rn, nx);
       rn = nx;
     }
+    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
 
     // ---- epilogue.  Register i of tile dt holds key wk0 + 8(i/4) + 4hh + i%4,
     // dim 32dt + r32.  Whole tiles: buffer stores whose resource ends at the
@@ -459,7 +460,6 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
           *(f32x4_t*)(pv + o) = (f32x4_t){dv[dt_][4 * i4], dv[dt_][4 * i4 + 1], dv[dt_][4 * i4 + 2], dv[dt_][4 * i4 + 3]};
         }
     }
-    if (tid == 0) s_item = next_item;
     __syncthreads();
   }
 }
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   using Sv = typename SM::Sv;
 
   __shared__ SM sm;
-  __shared__ int s_item;
+  __shared__ int s_info[2][10];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
   const int hh = lane >> 5, r32 = lane & 31;
@@ -547,22 +547,20 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
   const int gelt = a.grad_bf16 ? 2 : 4;
 
-  if (tid == 0) s_item = queue_take(a.plan_q.hdr);
+  if (tid == 0) item_store(s_info[0], item_load(a.plan_q, queue_take(a.plan_q.hdr), a.hq, total_items));
   __syncthreads();
-  for (int item = uniform(s_item); item < total_items; item = uniform(s_item)) {
-    __syncthreads();  // every thread has read s_item
+  for (int cur = 0;; cur ^= 1) {
+    const int* inf = s_info[cur];
+    const int item = uniform(inf[0]);
+    if (item >= total_items) break;
     int next_item = 0;
-    if (tid == 0) next_item = queue_take(a.plan_q.hdr);  // published at the end of this item
+    if (tid == 0) next_item = queue_take(a.plan_q.hdr);  // its entries are loaded during this item
     const int unit = item / a.hq;
     const int h = item - unit * a.hq;
-    const int4 un = a.plan_q.units[unit];
-    const int b = uniform(un.x), t = uniform(un.y);
-    const int n0 = uniform(un.z), n1 = uniform(un.w);
-    const int slot = uniform(a.plan_q.slots[unit]);  // >= 0: a chunk of a split tile
-    int q0, q1, k0, k1;
-    seq_bounds(a.cu_q, b, a.total_q, q0, q1);
-    seq_bounds(a.cu_k, b, a.total_k, k0, k1);
-    q0 = uniform(q0); q1 = uniform(q1); k0 = uniform(k0); k1 = uniform(k1);
+    const int b = uniform(inf[1]), t = uniform(inf[2]);
+    const int n0 = uniform(inf[3]), n1 = uniform(inf[4]);
+    const int q0 = uniform(inf[5]), q1 = uniform(inf[6]), k0 = uniform(inf[7]), k1 = uniform(inf[8]);
+    const int slot = uniform(inf[9]);  // >= 0: a chunk of a split tile
     const int Lq = q1 - q0, Lk = k1 - k0, off = Lk - Lq;
     const int g = h / a.n_rep;
     const int r1 = Lq - t * BMQ_DQ;
@@ -670,9 +668,12 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
       sv.store(sm.vn[0], nullptr);
     }
     __syncthreads();
+    ItemInfo nxt;
+    if (tid == 0) nxt = item_load(a.plan_q, next_item, a.hq, total_items);
     int n = n0;
     for (; n < min(n_plain, n1); ++n) step(std::integral_constant<bool, false>(), n);
     for (; n < n1; ++n) step(std::integral_constant<bool, true>(), n);
+    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
 
     if (slot < 0) {
       // rows < 0 fall outside the resource: their stores are dropped
@@ -705,7 +706,6 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
                                            acc[dt_][4 * a4 + 3]};
         }
     }
-    if (tid == 0) s_item = next_item;
     __syncthreads();
   }
 }

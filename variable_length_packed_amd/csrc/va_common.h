@@ -97,6 +97,19 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int b, int total, 
   e = z;
 }
 
+// Transposed V in LDS (the A operand of O^T += V^T P^T).  A lane's 8 MFMA
+// k-slots must be the 8 keys whose scores it holds, which are keys
+// {4hh .. 4hh+3, 8+4hh .. 8+4hh+3} of each 16-key chunk; storing key j of a
+// chunk at position vpos(j) (bits 2 and 3 swapped) makes them contiguous.
+// The 16-byte chunks of transposed row d are XOR-swizzled by (d >> 3) modulo
+// the chunk count, spreading the transposing stores (8 rows apart per lane)
+// and the fragment reads (consecutive rows per lane) over the LDS banks.
+__device__ __forceinline__ int vpos(int j) {
+  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+}
+template <int BN>
+__device__ __forceinline__ int vswz(int d) { return ((d >> 3) & (BN / 8 - 1)) << 3; }
+
 // ---------------------------------------------------------------------------
 // Work queue.  A planner kernel writes, per pass, a list of work units sorted
 // by cost (heaviest first) and zeroes hdr[0]; the pass's persistent
@@ -105,6 +118,32 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int b, int total, 
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int queue_take(int* hdr) {
   return __hip_atomic_fetch_add(hdr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A work item and its unit's plan entries.  Thread 0 takes the next item
+// from the queue and loads its entries while the current item computes, and
+// publishes them in LDS (double-buffered by item parity) before the current
+// item's output stores, so an item starts without a dependent chain of
+// global loads.
+struct ItemInfo {
+  int v[10];  // item, sequence, tile, first step, end step, tiled start/end, other start/end, slot
+};
+template <typename PlanT>
+__device__ __forceinline__ ItemInfo item_load(const PlanT& pl, int item, int per_unit, int total_items) {
+  ItemInfo r;
+  r.v[0] = item;
+  if (item < total_items) {
+    const int unit = item / per_unit;
+    const int4 un = pl.units[unit], bd = pl.bounds[unit];
+    r.v[1] = un.x; r.v[2] = un.y; r.v[3] = un.z; r.v[4] = un.w;
+    r.v[5] = bd.x; r.v[6] = bd.y; r.v[7] = bd.z; r.v[8] = bd.w;
+    r.v[9] = pl.slots[unit];
+  }
+  return r;
+}
+__device__ __forceinline__ void item_store(int* dst, const ItemInfo& r) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) dst[i] = r.v[i];
 }
 
 }  // namespace va

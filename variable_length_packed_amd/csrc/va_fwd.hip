@@ -48,19 +48,6 @@ struct FwdSmem {
   T v[2][VROWS * VP];
 };
 
-// Position of key j (0..BN-1) inside a transposed bf16 V row before the
-// swizzle: bits 2 and 3 of j swapped, so the 8 k-slots of a lane half are
-// contiguous.
-__device__ __forceinline__ int vpos(int j) {
-  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
-}
-
-// The 16-byte chunks of transposed row d are XOR-swizzled by (d >> 3) modulo
-// the chunk count: the transposing stores (8 rows apart per lane) and the
-// fragment reads (consecutive rows per lane) then spread over the LDS banks.
-template <int BN>
-__device__ __forceinline__ int vswz(int d) { return ((d >> 3) & (BN / 8 - 1)) << 3; }
-
 template <bool BF16, int D>
 struct Loader {
   static constexpr int BN = BlockN<BF16, D>::value;
@@ -171,7 +158,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
   constexpr int WR = 32 * QT;                 // rows per wave
 
   __shared__ S sm;
-  __shared__ int s_item;
+  __shared__ int s_info[2][10];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -188,22 +175,20 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
   const size_t qstride = (size_t)a.hq * D;
   const size_t kstride = (size_t)a.hkv * D;
 
-  if (tid == 0) s_item = queue_take(a.plan.hdr);
+  if (tid == 0) item_store(s_info[0], item_load(a.plan, queue_take(a.plan.hdr), a.hq, total_items));
   __syncthreads();
-  for (int item = uniform(s_item); item < total_items; item = uniform(s_item)) {
-    __syncthreads();  // every thread has read s_item
+  for (int cur = 0;; cur ^= 1) {
+    const int* inf = s_info[cur];
+    const int item = uniform(inf[0]);
+    if (item >= total_items) break;
     int next_item = 0;
-    if (tid == 0) next_item = queue_take(a.plan.hdr);  // published at the end of this item
+    if (tid == 0) next_item = queue_take(a.plan.hdr);  // its entries are loaded during this item
     const int unit = item / a.hq;
     const int h = item - unit * a.hq;
-    const int4 un = a.plan.units[unit];
-    const int b = uniform(un.x), t = uniform(un.y);
-    const int n0 = uniform(un.z), n1 = uniform(un.w);
-    const int slot = uniform(a.plan.slots[unit]);  // >= 0: a chunk of a split tile
-    int q0, q1, k0, k1;
-    seq_bounds(a.cu_q, b, a.total_q, q0, q1);
-    seq_bounds(a.cu_k, b, a.total_k, k0, k1);
-    q0 = uniform(q0); q1 = uniform(q1); k0 = uniform(k0); k1 = uniform(k1);
+    const int b = uniform(inf[1]), t = uniform(inf[2]);
+    const int n0 = uniform(inf[3]), n1 = uniform(inf[4]);
+    const int q0 = uniform(inf[5]), q1 = uniform(inf[6]), k0 = uniform(inf[7]), k1 = uniform(inf[8]);
+    const int slot = uniform(inf[9]);  // >= 0: a chunk of a split tile
     const int Lq = q1 - q0, Lk = k1 - k0;
     const int off = Lk - Lq;
     const int g = h / a.n_rep;
@@ -288,6 +273,29 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
 
     // ---- S^T = K Q^T of the block in K buffer `kbuf`: each K fragment read
     // from LDS feeds the QT query tiles
+    // bf16: the K fragments of a block, read from LDS ahead of their MFMAs
+    constexpr int KFN = BF16 ? QF * NS : 1;
+    auto read_k = [&](int kbuf, u32x4_t (&kfr)[KFN]) __attribute__((always_inline)) {
+      if constexpr (BF16) {
+#pragma unroll
+        for (int ks = 0; ks < QF; ++ks)
+#pragma unroll
+          for (int st = 0; st < NS; ++st)
+            kfr[ks * NS + st] = *(const u32x4_t*)(&sm.k[kbuf][(32 * st + r32) * S::KP + 16 * ks + 8 * hh]);
+      }
+    };
+    auto qk_frag = [&](const u32x4_t (&kfr)[KFN], f32x16_t (&s)[QT][NS]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int st = 0; st < NS; ++st) s[qt][st] = (f32x16_t){};
+#pragma unroll
+      for (int ks = 0; ks < QF; ++ks)
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) s[qt][st] = mfma32_bf16(kfr[ks * NS + st], qf4[qt][ks], s[qt][st]);
+    };
     auto qk = [&](int kbuf, f32x16_t (&s)[QT][NS]) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
@@ -316,9 +324,10 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
       }
     };
 
-    // ---- softmax of one block's scores and O^T += V^T P^T.  MASK: some
-    // score of the wave's tile is invisible.  Scores are rewritten in place.
-    auto softmax_pv = [&](auto mask_tag, int kb, int vbuf, f32x16_t (&s)[QT][NS]) {
+    // ---- softmax of one block's scores, in two parts: mask / bias, row max
+    // and the lazy rescale; then P and O^T += V^T P^T.  MASK: some score of
+    // the wave's tile is invisible.  Scores are rewritten in place.
+    auto softmax_max = [&](auto mask_tag, int kb, f32x16_t (&s)[QT][NS]) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
       // bias (log2 units) and mask; without a bias the scores stay raw and the
       // scale is applied inside the exponent's FMA
@@ -376,6 +385,8 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
             for (int i = 0; i < 16; ++i) acc[qt][dt][i] *= alpha;
         }
       }
+    };
+    auto exp_pv = [&](int vbuf, f32x16_t (&s)[QT][NS]) __attribute__((always_inline)) {
       float m_use[QT], psum[QT];
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
@@ -444,24 +455,68 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     // n; it stages K(n+2) into the K buffer block n used and V(n+1) into the V
     // buffer block n-1 used, so one barrier per block suffices.
     auto active = [&](int j) { return j < nb && wave_on && kb0 + j * BN < wave_hi; };
-    ld.load_k(kres, krow_bytes, kb0);
-    ld.load_v(vres, krow_bytes, kb0);
-    ld.store_k(sm, 0);
-    ld.store_v(sm, 0);
-    ld.load_k(kres, krow_bytes, kb0 + BN);
-    ld.store_k(sm, 1);
+    {
+      Loader<BF16, D> ld1;  // K(1) in flight with K(0) and V(0)
+      ld.load_k(kres, krow_bytes, kb0);
+      ld.load_v(vres, krow_bytes, kb0);
+      ld1.load_k(kres, krow_bytes, kb0 + BN);
+      ld.store_k(sm, 0);
+      ld.store_v(sm, 0);
+      ld1.store_k(sm, 1);
+    }
     __syncthreads();
     f32x16_t s_cur[QT][NS];
     if (active(0)) qk(0, s_cur);
     __syncthreads();  // every wave has read K(0) before K(2) replaces it
+    ItemInfo nxt;
+    if (tid == 0) nxt = item_load(a.plan, next_item, a.hq, total_items);
 
     auto step = [&](auto mask_tag, int n) {  // n: block index inside the unit
+      constexpr bool MASK = decltype(mask_tag)::value;
       const int kb = kb0 + n * BN;
       ld.load_k(kres, krow_bytes, kb + 2 * BN);  // past the last block every row reads as zero
       ld.load_v(vres, krow_bytes, kb + BN);
       f32x16_t s_nxt[QT][NS];
-      if (active(n + 1)) qk((n + 1) & 1, s_nxt);
-      if (active(n)) softmax_pv(mask_tag, kb, n & 1, s_cur);
+      if constexpr (!MASK) {
+        // every wave with rows in the sequence sees all of block n; S of
+        // block n + 1 needs no guard either (a block past the unit reads as
+        // zeros and is never used), so the MFMAs of S(n + 1) and the
+        // exponentials and PV of block n share one straight-line region and
+        // are interleaved there
+        if constexpr (BF16) {
+          u32x4_t kfr[KFN];
+          read_k((n + 1) & 1, kfr);  // in flight during the row max
+          softmax_max(mask_tag, kb, s_cur);
+          qk_frag(kfr, s_nxt);
+          exp_pv(n & 1, s_cur);
+          if constexpr (!HAS_BIAS) {
+            // S(n + 1) MFMAs between the exponentials of block n, then the PV
+            // MFMAs between the rest
+#pragma unroll
+            for (int i = 0; i < QF * NS * QT; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);  // transcendental
+              __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+            }
+#pragma unroll
+            for (int i = 0; i < 2 * NS * DT * QT; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+              __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+            }
+          }
+        } else {
+          softmax_max(mask_tag, kb, s_cur);
+          qk((n + 1) & 1, s_nxt);
+          exp_pv(n & 1, s_cur);
+        }
+      } else {
+        if (active(n + 1)) qk((n + 1) & 1, s_nxt);
+        if (active(n)) {
+          softmax_max(mask_tag, kb, s_cur);
+          exp_pv(n & 1, s_cur);
+        }
+      }
       ld.store_k(sm, n & 1);
       ld.store_v(sm, (n + 1) & 1);
       __syncthreads();
@@ -475,6 +530,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     int j = 0;
     for (; j < j_plain; ++j) step(std::integral_constant<bool, false>(), j);
     for (; j < nb; ++j) step(std::integral_constant<bool, true>(), j);
+    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; a chunk of a split
     // tile stores O and the base-2 LSE in float32 to its slot instead
@@ -515,7 +571,6 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
         if (hh == 0) a.part_lse[((size_t)slot * a.hq + h) * BM + rl] = lse2;
       }
     }
-    if (tid == 0) s_item = next_item;
     __syncthreads();
   }
 }
@@ -588,7 +643,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int64_t items, hipStream_t st) 
   timing_before(st, BF16 ? "fwd_bf16" : "fwd_f32");
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
   timing_after(st);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split_cap <= 0) return e;
   int64_t mg = (int64_t)a.split_cap * a.hq * (block_m<BF16, D>() / kMergeRows);
   if (mg > 4096) mg = 4096;

@@ -20,6 +20,7 @@ namespace va {
 struct Plan {
   int* hdr;        // [0] queue cursor (zeroed by the planner), [1] units, [2] split tiles
   int4* units;     // [unit_cap] {sequence, tile, first step, end step}
+  int4* bounds;    // [unit_cap] the sequence's rows: {tiled start, end, other start, end}
   int* slots;      // [unit_cap] partial slot of a chunk of a split tile, or -1
   int4* splits;    // [split_cap] {sequence, tile, first slot, chunks}
 };

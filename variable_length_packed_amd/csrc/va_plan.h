@@ -57,7 +57,9 @@ constexpr int NCAND = 6;  // chunk candidates: chunk << 0 .. chunk << 5
 struct PlanShared {
   int bins[NBIN];
   int tstart[MAXB + 1];  // exclusive scan of the tile counts of the current block of sequences
+  int st[MAXB];          // tiled-side first row
   int lt[MAXB];          // tiled-side length
+  int so[MAXB];          // other-side first row
   int lo[MAXB];          // other-side length
   int wsum[PT / 64];
   int cnt[NCAND];        // partial slots per chunk candidate
@@ -97,7 +99,9 @@ __device__ inline int load_block(const PlanArgs& p, PlanShared& sh, int b0, int 
       int t0, t1, o0, o1;
       seq_bounds(p.cu_t, b0 + i, p.total_t, t0, t1);
       seq_bounds(p.cu_o, b0 + i, p.total_o, o0, o1);
+      sh.st[i] = t0;
       sh.lt[i] = t1 - t0;
+      sh.so[i] = o0;
       sh.lo[i] = o1 - o0;
       cnt[e] = (t1 - t0 + p.tile - 1) / p.tile;
     }
@@ -121,7 +125,8 @@ __device__ __forceinline__ int find_seq(const PlanShared& sh, int nb, int i) {
   return lo_;
 }
 
-// f(sequence, tile, steps) for every tile (the general path).
+// f(sequence, tile, steps, q) for every tile (the general path); q indexes
+// the sequence's entries in sh during the call.
 template <typename F>
 __device__ void for_each_tile(const PlanArgs& p, PlanShared& sh, F&& f) {
   for (int b0 = 0; b0 < p.batch; b0 += MAXB) {
@@ -130,7 +135,7 @@ __device__ void for_each_tile(const PlanArgs& p, PlanShared& sh, F&& f) {
     for (int i = threadIdx.x; i < ntiles; i += PT) {
       const int q = find_seq(sh, nb, i);
       const int t = i - sh.tstart[q];
-      f(b0 + q, t, tile_steps(p, sh.lt[q], sh.lo[q], t));
+      f(b0 + q, t, tile_steps(p, sh.lt[q], sh.lo[q], t), q);
     }
     __syncthreads();
   }
@@ -170,7 +175,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
     if (fast) {
 #pragma unroll
       for (int j = 0; j < TPT; ++j)
-        if (cs[j] >= 0) f(cb[j], ct[j], cs[j]);
+        if (cs[j] >= 0) f(cb[j], ct[j], cs[j], cb[j]);
     } else {
       for_each_tile(p, sh, f);
     }
@@ -185,7 +190,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
     int sl[NCAND];
 #pragma unroll
     for (int j = 0; j < NCAND; ++j) sl[j] = 0;
-    visit([&](int, int, int s) {
+    visit([&](int, int, int s, int) {
       // ceil(s / (chunk0 << j)) = ceil(ceil(s / chunk0) / 2^j): one division
       const int n = (s + chunk0 - 1) / chunk0;
 #pragma unroll
@@ -214,7 +219,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
   // owns bins NBIN-1-2i and NBIN-2-2i
   for (int i = tid; i < NBIN; i += PT) sh.bins[i] = 0;
   __syncthreads();
-  visit([&](int, int, int s) {
+  visit([&](int, int, int s, int) {
     const int nch = chunks_of(s, chunk);
     const int q = s / nch, r = s - q * nch;  // r chunks of q + 1 steps, nch - r of q
     if (r > 0) atomicAdd(&sh.bins[min(q + 1, NBIN - 1)], r);
@@ -231,8 +236,9 @@ __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
   __syncthreads();
 
   // (3) place
-  visit([&](int b, int t, int s) {
+  visit([&](int b, int t, int s, int qs) {
     const int nch = chunks_of(s, chunk);
+    const int4 bd = make_int4(sh.st[qs], sh.st[qs] + sh.lt[qs], sh.so[qs], sh.so[qs] + sh.lo[qs]);
     int sp = -1, sb = -1;
     if (nch > 1) {
       sp = atomicAdd(&sh.split_ctr, 1);
@@ -248,6 +254,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
       const int pos = c < r ? pos_hi++ : pos_lo++;
       if (pos < p.unit_cap) {
         p.plan.units[pos] = make_int4(b, t, n0, n1);
+        p.plan.bounds[pos] = bd;
         p.plan.slots[pos] = nch > 1 ? sb + c : -1;
       }
     }
