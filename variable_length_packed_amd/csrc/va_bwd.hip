@@ -254,14 +254,17 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
   const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
   const int hpw = a.n_rep;  // every query head of the group
 
-  if (tid == 0) item_store(s_info[0], item_load(a.plan_k, queue_take(a.plan_k.hdr), a.hkv, total_items));
+  int ticket = 0;  // thread 0: ticket of the item after the current one
+  if (tid == 0) {
+    const int first = (int)blockIdx.x;
+    item_store(s_info[0], item_load(a.plan_k, first, a.hkv, total_items));
+    if (first < total_items) ticket = queue_take(a.plan_k.hdr);
+  }
   __syncthreads();
   for (int cur = 0;; cur ^= 1) {
     const int* inf = s_info[cur];
     const int item = uniform(inf[0]);
     if (item >= total_items) break;
-    int next_item = 0;
-    if (tid == 0) next_item = queue_take(a.plan_k.hdr);  // its entries are loaded during this item
     const int unit = item / a.hkv;
     const int g = item - unit * a.hkv;
     const int b = uniform(inf[1]), t = uniform(inf[2]);
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
     if (k_total > 0) { issue(rn); commit(0); }
     __syncthreads();
     ItemInfo nxt;
-    if (tid == 0) nxt = item_load(a.plan_k, next_item, a.hkv, total_items);
+    if (tid == 0) nxt = item_load(a.plan_k, (int)gridDim.x + ticket, a.hkv, total_items);
     int k = 0;
     for (; k < k_masked; ++k) {
       const int2 nx = next_of(k + 1, rn);
@@ -419,7 +422,10 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
       step(std::integral_constant<bool, false>(), k, rn, nx);
       rn = nx;
     }
-    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
+    if (tid == 0) {
+      item_store(s_info[cur ^ 1], nxt);  // before the output stores
+      ticket = queue_take(a.plan_k.hdr);  // waited for in the next item's prologue
+    }
 
     // ---- epilogue.  Register i of tile dt holds key wk0 + 8(i/4) + 4hh + i%4,
     // dim 32dt + r32.  Whole tiles: buffer stores whose resource ends at the
@@ -547,14 +553,17 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
   const int gelt = a.grad_bf16 ? 2 : 4;
 
-  if (tid == 0) item_store(s_info[0], item_load(a.plan_q, queue_take(a.plan_q.hdr), a.hq, total_items));
+  int ticket = 0;  // thread 0: ticket of the item after the current one
+  if (tid == 0) {
+    const int first = (int)blockIdx.x;
+    item_store(s_info[0], item_load(a.plan_q, first, a.hq, total_items));
+    if (first < total_items) ticket = queue_take(a.plan_q.hdr);
+  }
   __syncthreads();
   for (int cur = 0;; cur ^= 1) {
     const int* inf = s_info[cur];
     const int item = uniform(inf[0]);
     if (item >= total_items) break;
-    int next_item = 0;
-    if (tid == 0) next_item = queue_take(a.plan_q.hdr);  // its entries are loaded during this item
     const int unit = item / a.hq;
     const int h = item - unit * a.hq;
     const int b = uniform(inf[1]), t = uniform(inf[2]);
@@ -669,11 +678,14 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     }
     __syncthreads();
     ItemInfo nxt;
-    if (tid == 0) nxt = item_load(a.plan_q, next_item, a.hq, total_items);
+    if (tid == 0) nxt = item_load(a.plan_q, (int)gridDim.x + ticket, a.hq, total_items);
     int n = n0;
     for (; n < min(n_plain, n1); ++n) step(std::integral_constant<bool, false>(), n);
     for (; n < n1; ++n) step(std::integral_constant<bool, true>(), n);
-    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
+    if (tid == 0) {
+      item_store(s_info[cur ^ 1], nxt);  // before the output stores
+      ticket = queue_take(a.plan_q.hdr);  // waited for in the next item's prologue
+    }
 
     if (slot < 0) {
       // rows < 0 fall outside the resource: their stores are dropped

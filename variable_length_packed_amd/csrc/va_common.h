@@ -113,18 +113,27 @@ __device__ __forceinline__ int vswz(int d) { return ((d >> 3) & (BN / 8 - 1)) <<
 // ---------------------------------------------------------------------------
 // Work queue.  A planner kernel writes, per pass, a list of work units sorted
 // by cost (heaviest first) and zeroes hdr[0]; the pass's persistent
-// workgroups then take items in list order with one atomic each, so the
-// heavy units start first and the light ones fill in behind them.
+// workgroups then take items in list order, so the heavy units start first
+// and the light ones fill in behind them.  Workgroup w starts with item w;
+// later items are gridDim.x + a ticket from one device-scope atomic, taken
+// by thread 0 one item ahead (a workgroup takes a ticket only while it holds
+// a valid item, and tickets grow, so every valid item is run exactly once).
+// The atomic's address goes through a register the compiler must treat as
+// per-lane: a uniform address would be rewritten into a one-lane atomic plus
+// an immediate broadcast, i.e. a wait for the atomic's full round trip (which
+// also drains every store still in flight) at the point of the call.  This
+// way the wait happens where the ticket is first used.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int queue_take(int* hdr) {
-  return __hip_atomic_fetch_add(hdr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ int queue_take(int* hdr) {  // the ticket; its item is gridDim.x + ticket
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return __hip_atomic_fetch_add(hdr + z, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A work item and its unit's plan entries.  Thread 0 takes the next item
-// from the queue and loads its entries while the current item computes, and
-// publishes them in LDS (double-buffered by item parity) before the current
-// item's output stores, so an item starts without a dependent chain of
-// global loads.
+// A work item and its unit's plan entries.  Thread 0 loads the entries of
+// the next item while the current item computes and publishes them in LDS
+// (double-buffered by item parity) before the current item's output stores,
+// so an item starts without a dependent chain of global loads.
 struct ItemInfo {
   int v[10];  // item, sequence, tile, first step, end step, tiled start/end, other start/end, slot
 };

@@ -175,14 +175,17 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
   const size_t qstride = (size_t)a.hq * D;
   const size_t kstride = (size_t)a.hkv * D;
 
-  if (tid == 0) item_store(s_info[0], item_load(a.plan, queue_take(a.plan.hdr), a.hq, total_items));
+  int ticket = 0;  // thread 0: ticket of the item after the current one
+  if (tid == 0) {
+    const int first = (int)blockIdx.x;
+    item_store(s_info[0], item_load(a.plan, first, a.hq, total_items));
+    if (first < total_items) ticket = queue_take(a.plan.hdr);
+  }
   __syncthreads();
   for (int cur = 0;; cur ^= 1) {
     const int* inf = s_info[cur];
     const int item = uniform(inf[0]);
     if (item >= total_items) break;
-    int next_item = 0;
-    if (tid == 0) next_item = queue_take(a.plan.hdr);  // its entries are loaded during this item
     const int unit = item / a.hq;
     const int h = item - unit * a.hq;
     const int b = uniform(inf[1]), t = uniform(inf[2]);
@@ -469,7 +472,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     if (active(0)) qk(0, s_cur);
     __syncthreads();  // every wave has read K(0) before K(2) replaces it
     ItemInfo nxt;
-    if (tid == 0) nxt = item_load(a.plan, next_item, a.hq, total_items);
+    if (tid == 0) nxt = item_load(a.plan, (int)gridDim.x + ticket, a.hq, total_items);
 
     auto step = [&](auto mask_tag, int n) {  // n: block index inside the unit
       constexpr bool MASK = decltype(mask_tag)::value;
@@ -530,7 +533,10 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     int j = 0;
     for (; j < j_plain; ++j) step(std::integral_constant<bool, false>(), j);
     for (; j < nb; ++j) step(std::integral_constant<bool, true>(), j);
-    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
+    if (tid == 0) {
+      item_store(s_info[cur ^ 1], nxt);  // before the output stores
+      ticket = queue_take(a.plan.hdr);  // waited for in the next item's prologue
+    }
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; a chunk of a split
     // tile stores O and the base-2 LSE in float32 to its slot instead
