@@ -39,6 +39,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// acc + lo + hi of a packed bf16 pair (one v_dot2 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair),
+                                         __builtin_bit_cast(bf16x2_t, 0x3F803F80u), acc, false);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __builtin_bit_cast(float, (uint32_t)x << 16);
 }
@@ -97,18 +103,16 @@ __device__ __forceinline__ void seq_bounds(const int32_t* cu, int b, int total, 
   e = z;
 }
 
-// Transposed V in LDS (the A operand of O^T += V^T P^T).  A lane's 8 MFMA
-// k-slots must be the 8 keys whose scores it holds, which are keys
-// {4hh .. 4hh+3, 8+4hh .. 8+4hh+3} of each 16-key chunk; storing key j of a
-// chunk at position vpos(j) (bits 2 and 3 swapped) makes them contiguous.
-// The 16-byte chunks of transposed row d are XOR-swizzled by (d >> 3) modulo
-// the chunk count, spreading the transposing stores (8 rows apart per lane)
-// and the fragment reads (consecutive rows per lane) over the LDS banks.
-__device__ __forceinline__ int vpos(int j) {
-  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+// Transposing LDS read of 16-bit data (ds_read_b64_tr_b16).  In each group of
+// 16 lanes, lane s gives the address of 4 consecutive elements; lane i of the
+// group receives, in slot j, element i % 4 of lane 4j + i / 4.  So if lane s
+// points at row s / 4, columns 4(s % 4) .. +4 of a 4 x 16 tile, lane i gets
+// column i of the tile's 4 rows: a 16 x 4 transpose per group.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p));
 }
-template <int BN>
-__device__ __forceinline__ int vswz(int d) { return ((d >> 3) & (BN / 8 - 1)) << 3; }
 
 // ---------------------------------------------------------------------------
 // Work queue.  A planner kernel writes, per pass, a list of work units sorted

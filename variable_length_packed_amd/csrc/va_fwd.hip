@@ -37,15 +37,12 @@ template <bool BF16, int D>
 struct FwdSmem {
   static constexpr int BN = BlockN<BF16, D>::value;
   using T = typename std::conditional<BF16, uint16_t, float>::type;
-  // K block: [BN][D] row-major, row pitch padded by 16 bytes.
+  // K and V blocks: [BN][D] row-major as in memory, row pitch padded by 16
+  // bytes.  bf16 V^T fragments come from transposing LDS reads.
   static constexpr int KP = D + 16 / (int)sizeof(T);
-  // V block: bf16 -> transposed [D][BN] with keys permuted inside each group
-  // of 16 (bits 2 and 3 of the key swapped) so a lane's 8 MFMA k-slots are
-  // contiguous; f32 -> [BN][D] like K.
-  static constexpr int VROWS = BF16 ? D : BN;
-  static constexpr int VP = (BF16 ? BN : D) + 16 / (int)sizeof(T);
+  static constexpr int VP = KP;
   T k[2][BN * KP];
-  T v[2][VROWS * VP];
+  T v[2][BN * VP];
 };
 
 template <bool BF16, int D>
@@ -55,16 +52,13 @@ struct Loader {
   static constexpr int EPV = 16 / sizeof(T);           // elements per 16-byte vector
   static constexpr int KVEC = BN * D / EPV;            // 16-byte vectors per K block
   static constexpr int KPT = (KVEC + NT - 1) / NT;     // per thread
-  // V (bf16): tasks of 2 keys x 8 dims; (f32): same as K
-  static constexpr int VTASK = BF16 ? (BN / 2) * (D / 8) : KVEC;
-  static constexpr int VPT = (VTASK + NT - 1) / NT;
   u32x4_t kr[KPT];
-  u32x4_t vr[BF16 ? 2 * VPT : VPT];
+  u32x4_t vr[KPT];
 
   // Block of keys kb .. kb+BN-1 of one (sequence, KV head).  The resources
   // cover keys [0, kv_hi); other rows (negative offsets included) read 0.
   __device__ __forceinline__ void load_k(rsrc_t kres, int row_bytes, int kb) {
-    static_assert(KVEC % NT == 0 && VTASK % NT == 0, "loader tasks must tile the workgroup");
+    static_assert(KVEC % NT == 0, "loader tasks must tile the workgroup");
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int u = threadIdx.x + i * NT;
@@ -73,21 +67,11 @@ struct Loader {
     }
   }
   __device__ __forceinline__ void load_v(rsrc_t vres, int row_bytes, int kb) {
-    if constexpr (BF16) {
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int u = threadIdx.x + i * NT;
-        const int dc = u % (D / 8), kp = u / (D / 8);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) vr[2 * i + r] = buf_load16(vres, (kb + 2 * kp + r) * row_bytes + dc * 16);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int u = threadIdx.x + i * NT;
-        const int key = u / (D / EPV), c = u % (D / EPV);
-        vr[i] = buf_load16(vres, (kb + key) * row_bytes + c * 16);
-      }
+    for (int i = 0; i < KPT; ++i) {
+      const int u = threadIdx.x + i * NT;
+      const int key = u / (D / EPV), c = u % (D / EPV);
+      vr[i] = buf_load16(vres, (kb + key) * row_bytes + c * 16);
     }
   }
 
@@ -102,29 +86,11 @@ struct Loader {
   }
   __device__ __forceinline__ void store_v(FwdSmem<BF16, D>& sm, int buf) {
     using S = FwdSmem<BF16, D>;
-    if constexpr (BF16) {
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int u = threadIdx.x + i * NT;
-        const int dc = u % (D / 8), kp = u / (D / 8);
-        const int pos = vpos(2 * kp) ^ vswz<BN>(dc * 8);  // rows dc*8 .. dc*8+7 share the swizzle
-        const u32x4_t a = vr[2 * i], b = vr[2 * i + 1];
-        // a holds dims dc*8..+8 of key 2kp, b of key 2kp+1; write pairs (key, key+1) per dim
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (a[e] & 0xFFFFu) | (b[e] << 16);
-          const uint32_t hi = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
-          *(uint32_t*)(&sm.v[buf][(dc * 8 + 2 * e) * S::VP + pos]) = lo;
-          *(uint32_t*)(&sm.v[buf][(dc * 8 + 2 * e + 1) * S::VP + pos]) = hi;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const int u = threadIdx.x + i * NT;
-        const int key = u / (D / EPV), c = u % (D / EPV);
-        *(u32x4_t*)(&sm.v[buf][key * S::VP + c * EPV]) = vr[i];
-      }
+    for (int i = 0; i < KPT; ++i) {
+      const int u = threadIdx.x + i * NT;
+      const int key = u / (D / EPV), c = u % (D / EPV);
+      *(u32x4_t*)(&sm.v[buf][key * S::VP + c * EPV]) = vr[i];
     }
   }
 };
@@ -327,6 +293,24 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
       }
     };
 
+    // bf16 V^T fragment of 16-key chunk kc (A operand of O^T += V^T P^T).  Its
+    // k-slots must be the keys of the lane's P^T slots, i.e. of its score
+    // registers: keys 4hh .. 4hh+3 and 8+4hh .. 8+4hh+3 of the chunk.  Lane l
+    // holds dim 32*dt + l%32 of those keys, from two transposing reads of 4
+    // keys each; in each group of 16 lanes, lane s points at key s/4 of the
+    // four, dims 4*(s%4) .. +4 of the group's 16.
+    const int vlane = (4 * hh + ((lane >> 2) & 3)) * S::VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto read_vfrag = [&](int vbuf, int kc, u32x4_t (&dst)[DT]) __attribute__((always_inline)) {
+      if constexpr (BF16) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const T* p = &sm.v[vbuf][vlane + 16 * kc * S::VP + 32 * dt];
+          const u32x2_t lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * S::VP);
+          dst[dt] = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+    };
+
     // ---- softmax of one block's scores, in two parts: mask / bias, row max
     // and the lazy rescale; then P and O^T += V^T P^T.  MASK: some score of
     // the wave's tile is invisible.  Scores are rewritten in place.
@@ -404,13 +388,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
         // 16-key chunks kc: P^T chunk = registers 8*(kc%2) .. +8 of score tile kc/2.
         // The V^T fragments of chunk kc+1 are read while chunk kc computes.
         u32x4_t vnext[DT];
-        auto read_v = [&](int kc, u32x4_t (&dst)[DT]) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const int d = 32 * dt + r32;
-            dst[dt] = *(const u32x4_t*)(&sm.v[vbuf][d * S::VP + ((16 * kc + 8 * hh) ^ vswz<BN>(d))]);
-          }
-        };
+        auto read_v = [&](int kc, u32x4_t (&dst)[DT]) { read_vfrag(vbuf, kc, dst); };
         read_v(0, vnext);
 #pragma unroll
         for (int kc = 0; kc < 2 * NS; ++kc) {
@@ -451,6 +429,97 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
       }
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) l_run[qt] += psum[qt];
+    };
+
+    // ---- bf16 without bias, a block every row of the wave sees in full: the
+    // MFMAs of S(n+1) and PV(n) and the exponentials of block n in an explicit
+    // order.  Round kc (one per 16-key chunk) issues the S(n+1) MFMAs of its
+    // k-steps and the PV MFMAs of chunk kc-1, each followed by a share of the
+    // vector work of chunk kc (exponentials, bf16 packing, row sums), so the
+    // matrix unit and the vector unit of the SIMD both have work that waits
+    // on neither.  The row sums add the bf16-rounded P that the PV MFMAs use.
+    constexpr int NCH = 2 * NS;  // 16-key chunks per block
+    auto step_fast = [&](int n, f32x16_t (&sc)[QT][NS], f32x16_t (&sn)[QT][NS]) __attribute__((always_inline)) {
+      if constexpr (QT == 1 && BF16 && !HAS_BIAS) {
+      static_assert(QF % NCH == 0, "whole k-steps per round");
+      constexpr int KPR = QF / NCH;  // S k-steps per round
+      const int kb = kb0 + n * BN;
+      const int kbuf = (n + 1) & 1, vbuf = n & 1;
+      ld.load_k(kres, krow_bytes, kb + 2 * BN);  // past the last block every row reads as zero
+      ld.load_v(vres, krow_bytes, kb + BN);
+      u32x4_t kfr[KFN];
+      read_k(kbuf, kfr);
+      u32x4_t vf[NCH][DT];
+      read_vfrag(vbuf, 0, vf[0]);
+      // row max of block n (raw scores, four independent chains)
+      float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const int c = (8 * st + i / 2) & 3;
+          m4[c] = max3f(m4[c], sc[0][st][i], sc[0][st][i + 1]);
+        }
+      float m = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      m = fmaxf(m, xor32(m)) * a.scale_log2;
+      if (__builtin_amdgcn_ballot_w64(m > m_run[0] + 8.f) != 0) {
+        const float m_new = fmaxf(m_run[0], m);
+        const float alpha = fast_exp2(m_run[0] - (m_new == -INFINITY ? 0.f : m_new));
+        m_run[0] = m_new;
+        l_run[0] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[0][dt][i] *= alpha;
+      }
+      const float nmu = m_run[0] == -INFINITY ? 0.f : -m_run[0];
+#pragma unroll
+      for (int st = 0; st < NS; ++st) sn[0][st] = (f32x16_t){};
+      float ps0 = 0.f, ps1 = 0.f;
+      u32x4_t pb[NCH];
+#pragma unroll
+      for (int kc = 0; kc <= NCH; ++kc) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (kc < NCH) {
+#pragma unroll
+          for (int r = 0; r < KPR; ++r)
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+              const int ks = kc * KPR + r;
+              sn[0][st] = mfma32_bf16(kfr[ks * NS + st], qf4[0][ks], sn[0][st]);
+            }
+        }
+        if (kc > 0) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[0][dt] = mfma32_bf16(vf[kc - 1][dt], pb[kc - 1], acc[0][dt]);
+        }
+        if (kc + 1 < NCH) read_vfrag(vbuf, kc + 1, vf[kc + 1]);
+        if (kc < NCH) {
+          const int st = kc >> 1, i0 = 8 * (kc & 1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(__builtin_fmaf(sc[0][st][i0 + 2 * e], a.scale_log2, nmu));
+            const float p1 = fast_exp2(__builtin_fmaf(sc[0][st][i0 + 2 * e + 1], a.scale_log2, nmu));
+            pb[kc][e] = pack_bf16x2(p0, p1);
+          }
+          ps0 = add_bf16x2(pb[kc][0], ps0);
+          ps1 = add_bf16x2(pb[kc][1], ps1);
+          ps0 = add_bf16x2(pb[kc][2], ps0);
+          ps1 = add_bf16x2(pb[kc][3], ps1);
+          // one MFMA, then a share of the vector work, in turn
+#pragma unroll
+          for (int g = 0; g < (kc > 0 ? DT : 0) + KPR * NS; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      l_run[0] += ps0 + ps1;
+      ld.store_k(sm, n & 1);
+      ld.store_v(sm, (n + 1) & 1);
+      __syncthreads();
+      }
     };
 
     // Pipeline: K runs one block ahead of V.  Iteration n computes S of block
@@ -531,7 +600,21 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     // unmasked blocks, then the (at most a few) masked ones: two loops, so the
     // accumulators never merge from two code paths inside a loop
     int j = 0;
-    for (; j < j_plain; ++j) step(std::integral_constant<bool, false>(), j);
+    if constexpr (BF16 && !HAS_BIAS && QT == 1) {
+      f32x16_t s_alt[QT][NS];
+      for (; j + 1 < j_plain; j += 2) {
+        step_fast(j, s_cur, s_alt);
+        step_fast(j + 1, s_alt, s_cur);
+      }
+      if (j < j_plain) {
+        step_fast(j, s_cur, s_alt);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) s_cur[0][st] = s_alt[0][st];
+        ++j;
+      }
+    } else {
+      for (; j < j_plain; ++j) step(std::integral_constant<bool, false>(), j);
+    }
     for (; j < nb; ++j) step(std::integral_constant<bool, true>(), j);
     if (tid == 0) {
       item_store(s_info[cur ^ 1], nxt);  // before the output stores
