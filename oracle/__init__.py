@@ -18,3 +18,4 @@ from .attention import (  # noqa: F401
     visible,
 )
 from .brute import brute_forward  # noqa: F401
+from .packing import pack_metadata, pad, unpad  # noqa: F401
