@@ -12,7 +12,8 @@ import pytest
 from variable_length_packed_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "va_varlen.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = range(5)
 F32, BF16 = 0, 1
@@ -20,9 +21,11 @@ P = 0x1000  # a non-NULL pointer that validation rejects before any use
 
 
 def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(va_[a-z0-9_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(va_[a-z0-9_]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -178,3 +181,54 @@ def test_python_layer_rejects_cpu_tensors_and_bias_grad():
     b = torch.zeros(1, 2, 4, 4, requires_grad=True)
     with pytest.raises(ValueError):
         va.varlen_attn(q, q, q, cu, cu, 4, 4, bias=b)
+
+
+# ---------------------------------------------------------------- packing (include/va_pack.h)
+def _tensors(n=1, rb=128, padded=P, packed=P):
+    arr = (_lib.PackTensor * max(n, 1))()
+    for i in range(max(n, 1)):
+        arr[i].padded = padded
+        arr[i].packed = packed
+        arr[i].row_bytes = rb
+    return arr
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=None), INVALID),
+    (dict(cu=None), INVALID),
+    (dict(inv=None), INVALID),
+    (dict(batch=0), INVALID),
+    (dict(seqlen=-1), INVALID),
+    (dict(batch=1 << 16, seqlen=1 << 15), INVALID),
+])
+def test_pack_metadata_validation(lib, kw, code):
+    a = dict(mask=P, batch=4, seqlen=8, cu=P, mx=P, idx=P, pos=P, inv=P)
+    a.update(kw)
+    assert lib.va_pack_metadata(a["mask"], a["batch"], a["seqlen"], a["cu"], a["mx"], a["idx"], a["pos"],
+                                a["inv"], None) == code
+    assert lib.va_last_error()
+
+
+@pytest.mark.parametrize("which", ["unpad", "pad"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), INVALID),
+    (dict(n=5), INVALID),
+    (dict(tensors=None), INVALID),
+    (dict(rb=0), INVALID),
+    (dict(padded=0), INVALID),
+    (dict(packed=0), INVALID),
+    (dict(batch=0), INVALID),
+    (dict(seqlen=0), INVALID),
+    (dict(rows=-1), INVALID),
+    (dict(index=None), INVALID),
+])
+def test_unpad_pad_validation(lib, which, kw, code):
+    a = dict(n=2, rb=128, padded=P, packed=P, batch=4, seqlen=8, rows=32, index=P, tensors="x")
+    a.update(kw)
+    arr = None if a["tensors"] is None else _tensors(a["n"], a["rb"], a["padded"], a["packed"])
+    if which == "unpad":
+        r = lib.va_unpad(arr, a["n"], a["index"], P, a["batch"], a["seqlen"], a["rows"], None)
+    else:
+        r = lib.va_pad(arr, a["n"], a["index"], a["batch"], a["seqlen"], a["rows"], None)
+    assert r == code
+    assert lib.va_last_error()

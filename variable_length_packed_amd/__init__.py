@@ -19,6 +19,9 @@ it is 4-D ``[batch, Hq, rows, cols]``; a per-key bias is rows stride 0).
 
 from .api import (  # noqa: F401
     VaError,
+    pack_metadata,
+    pad,
+    unpad,
     va_varlen_bwd,
     va_varlen_bwd_workspace_size,
     va_varlen_fwd,

@@ -1,4 +1,4 @@
-"""ctypes view of libva_varlen.so (the C ABI declared in include/va_varlen.h)."""
+"""ctypes view of libva_varlen.so (the C ABI declared in include/va_varlen.h and include/va_pack.h)."""
 
 from __future__ import annotations
 
@@ -10,14 +10,19 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libva_varle
 VA_OK, VA_ERR_INVALID, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP = range(5)
 VA_F32, VA_BF16 = 0, 1
 
-# Every symbol include/va_varlen.h declares.
+# Every symbol include/va_varlen.h and include/va_pack.h declare.
 EXPORTS = ("va_varlen_fwd", "va_varlen_bwd", "va_varlen_fwd_workspace_size",
            "va_varlen_bwd_workspace_size", "va_status_string", "va_last_error", "va_version",
-           "va_timing_start", "va_timing_stop")
+           "va_timing_start", "va_timing_stop", "va_pack_metadata", "va_unpad", "va_pad")
+VA_PACK_MAX_TENSORS = 4
 
 
 class KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int), ("total_ms", ctypes.c_double)]
+
+
+class PackTensor(ctypes.Structure):
+    _fields_ = [("padded", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("row_bytes", ctypes.c_int64)]
 
 _lib = None
 
@@ -60,6 +65,12 @@ def load() -> ctypes.CDLL:
     lib.va_timing_start.argtypes = [ctypes.c_int]
     lib.va_timing_stop.restype = ctypes.c_int
     lib.va_timing_stop.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int]
+    lib.va_pack_metadata.restype = ctypes.c_int
+    lib.va_pack_metadata.argtypes = [_p, _i32, _i32, _p, _p, _p, _p, _p, _p]
+    lib.va_unpad.restype = ctypes.c_int
+    lib.va_unpad.argtypes = [ctypes.POINTER(PackTensor), _i32, _p, _p, _i32, _i32, ctypes.c_int64, _p]
+    lib.va_pad.restype = ctypes.c_int
+    lib.va_pad.argtypes = [ctypes.POINTER(PackTensor), _i32, _p, _i32, _i32, ctypes.c_int64, _p]
     _lib = lib
     return lib
 

@@ -1,4 +1,4 @@
-"""Torch-facing marshalling over the C ABI (include/va_varlen.h).
+"""Torch-facing marshalling over the C ABI (include/va_varlen.h, include/va_pack.h).
 
 Tensors are checked for device, dtype, rank and contiguity, outputs are
 allocated with torch, pointers and the current HIP stream are handed to the
@@ -279,3 +279,79 @@ def va_last_error() -> str:
 
 def va_version() -> int:
     return int(_lib.load().va_version())
+
+
+# ---------------------------------------------------------------- packing (include/va_pack.h)
+def pack_metadata(mask: torch.Tensor):
+    """Packing metadata of a padding mask [batch, seqlen] (nonzero = real token), on its device.
+
+    Returns (cu_seqlens int32 [batch+1], max_seqlen int32 [1], indices int32 [batch*seqlen],
+    position_ids int32 [batch*seqlen], inverse int32 [batch*seqlen]); only the first
+    cu_seqlens[-1] entries of indices and position_ids are meaningful.  No host sync.
+    """
+    lib = _lib.load()
+    _need_dev("mask", mask, None)
+    if mask.dim() != 2:
+        raise ValueError("mask must be 2-D [batch, seqlen]")
+    m = mask if mask.dtype == torch.uint8 else (mask != 0).to(torch.uint8)
+    batch, seqlen = m.shape
+    dev = m.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    cu = torch.empty(batch + 1, **i32)
+    mx = torch.empty(1, **i32)
+    idx = torch.empty(batch * seqlen, **i32)
+    pos = torch.empty(batch * seqlen, **i32)
+    inv = torch.empty(batch * seqlen, **i32)
+    _raise(lib.va_pack_metadata(m.data_ptr(), batch, seqlen, cu.data_ptr(), mx.data_ptr(), idx.data_ptr(),
+                                pos.data_ptr(), inv.data_ptr(), _stream(dev)), lib)
+    return cu, mx, idx, pos, inv
+
+
+def _pack_tensors(padded, packed, batch, seqlen):
+    if not 1 <= len(padded) <= _lib.VA_PACK_MAX_TENSORS:
+        raise ValueError(f"1..{_lib.VA_PACK_MAX_TENSORS} tensors per call")
+    arr = (_lib.PackTensor * len(padded))()
+    for i, (x, y) in enumerate(zip(padded, packed)):
+        _need_dev(f"padded[{i}]", x, padded[0].device)
+        _need_dev(f"packed[{i}]", y, padded[0].device)
+        if x.shape[0] != batch or x.shape[1] != seqlen:
+            raise ValueError(f"padded[{i}] must be [batch, seqlen, ...]")
+        if y.shape[1:] != x.shape[2:] or y.dtype != x.dtype:
+            raise ValueError(f"packed[{i}] must be [rows, ...] with the padded tensor's row shape and dtype")
+        arr[i].padded = x.data_ptr()
+        arr[i].packed = y.data_ptr()
+        arr[i].row_bytes = x[0, 0].numel() * x.element_size()
+    return arr
+
+
+def unpad(padded: Sequence[torch.Tensor], indices: torch.Tensor, cu_seqlens: torch.Tensor,
+          packed_rows: Optional[int] = None):
+    """Gather the real tokens of padded [batch, seqlen, ...] tensors into packed [rows, ...] ones.
+
+    Rows past cu_seqlens[-1] of the outputs are left unwritten; ``packed_rows`` defaults
+    to batch * seqlen (pass the known total to get exact-size outputs).
+    """
+    lib = _lib.load()
+    padded = list(padded)
+    batch, seqlen = padded[0].shape[:2]
+    rows = batch * seqlen if packed_rows is None else int(packed_rows)
+    packed = [torch.empty((rows,) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device) for x in padded]
+    arr = _pack_tensors(padded, packed, batch, seqlen)
+    _need_dev("indices", indices, padded[0].device)
+    _need_dev("cu_seqlens", cu_seqlens, padded[0].device)
+    _raise(lib.va_unpad(arr, len(padded), indices.data_ptr(), cu_seqlens.data_ptr(), batch, seqlen, rows,
+                        _stream(padded[0].device)), lib)
+    return packed
+
+
+def pad(packed: Sequence[torch.Tensor], inverse: torch.Tensor, batch: int, seqlen: int):
+    """Scatter packed [rows, ...] tensors back to padded [batch, seqlen, ...] ones (zeros elsewhere)."""
+    lib = _lib.load()
+    packed = list(packed)
+    padded = [torch.empty((batch, seqlen) + tuple(y.shape[1:]), dtype=y.dtype, device=y.device)
+              for y in packed]
+    arr = _pack_tensors(padded, packed, batch, seqlen)
+    _need_dev("inverse", inverse, packed[0].device)
+    _raise(lib.va_pad(arr, len(packed), inverse.data_ptr(), batch, seqlen, packed[0].shape[0],
+                      _stream(packed[0].device)), lib)
+    return padded

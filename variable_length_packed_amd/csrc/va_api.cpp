@@ -1,7 +1,9 @@
 // C ABI of the packed varlen attention library: argument validation (host
 // only, no device reads), schedule sizing and kernel launch.  Declarations
-// and the contract of every entry point are in include/va_varlen.h.
+// and the contract of every entry point are in include/va_varlen.h and
+// include/va_pack.h.
 #include "va_varlen.h"
+#include "va_pack.h"
 
 #include <hip/hip_runtime.h>
 
@@ -328,6 +330,82 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
   hipError_t e = va::launch_bwd(a, ps, (int64_t)Q.unit_cap * num_heads_q,
                                 (int64_t)K.unit_cap * num_heads_kv, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return VA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Packing (include/va_pack.h)
+// ---------------------------------------------------------------------------
+va_status va_pack_metadata(const uint8_t* mask, int32_t batch, int32_t seqlen,
+                           int32_t* cu_seqlens, int32_t* max_seqlen,
+                           int32_t* indices, int32_t* position_ids, int32_t* inverse,
+                           va_stream stream) {
+  if (!mask || !cu_seqlens || !max_seqlen || !indices || !position_ids || !inverse)
+    return fail(VA_ERR_INVALID, "NULL pointer argument");
+  if (batch <= 0 || seqlen <= 0)
+    return fail(VA_ERR_INVALID, "batch and seqlen must be > 0 (got %d, %d)", batch, seqlen);
+  if ((int64_t)batch * seqlen >= ((int64_t)1 << 31))
+    return fail(VA_ERR_INVALID, "batch * seqlen must be < 2^31");
+  const hipError_t e = va::launch_pack_metadata(mask, batch, seqlen, cu_seqlens, max_seqlen, indices,
+                                                position_ids, inverse, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "packing metadata launch");
+  return VA_OK;
+}
+
+static va_status pack_args(const va_pack_tensor* tensors, int32_t n, int32_t batch, int32_t seqlen,
+                           int64_t packed_rows, va::PackArgs& a, int& width) {
+  if (!tensors) return fail(VA_ERR_INVALID, "NULL tensors");
+  if (n < 1 || n > VA_PACK_MAX_TENSORS)
+    return fail(VA_ERR_INVALID, "n_tensors must be 1..%d (got %d)", VA_PACK_MAX_TENSORS, n);
+  if (batch <= 0 || seqlen <= 0)
+    return fail(VA_ERR_INVALID, "batch and seqlen must be > 0 (got %d, %d)", batch, seqlen);
+  if ((int64_t)batch * seqlen >= ((int64_t)1 << 31))
+    return fail(VA_ERR_INVALID, "batch * seqlen must be < 2^31");
+  if (packed_rows < 0) return fail(VA_ERR_INVALID, "packed_rows must be >= 0");
+  a = va::PackArgs{};
+  a.n = n;
+  a.batch = batch;
+  a.padded_rows = (int64_t)batch * seqlen;
+  a.packed_rows = packed_rows;
+  // the widest copy that divides every row size and base address
+  uint64_t g = 16;
+  for (int i = 0; i < n; ++i) {
+    const va_pack_tensor& t = tensors[i];
+    if (!t.padded || !t.packed) return fail(VA_ERR_INVALID, "NULL pointer in tensor %d", i);
+    if (t.row_bytes <= 0) return fail(VA_ERR_INVALID, "row_bytes of tensor %d must be > 0", i);
+    a.padded[i] = t.padded;
+    a.packed[i] = t.packed;
+    a.row_bytes[i] = t.row_bytes;
+    const uint64_t bits = (uint64_t)t.row_bytes | (uint64_t)(uintptr_t)t.padded | (uint64_t)(uintptr_t)t.packed;
+    while (g > 1 && (bits & (g - 1)) != 0) g >>= 1;
+  }
+  width = (int)g;
+  return VA_OK;
+}
+
+va_status va_unpad(const va_pack_tensor* tensors, int32_t n_tensors,
+                   const int32_t* indices, const int32_t* cu_seqlens,
+                   int32_t batch, int32_t seqlen, int64_t packed_rows, va_stream stream) {
+  if (!indices || !cu_seqlens) return fail(VA_ERR_INVALID, "NULL pointer argument");
+  va::PackArgs a;
+  int width = 1;
+  const va_status st = pack_args(tensors, n_tensors, batch, seqlen, packed_rows, a, width);
+  if (st != VA_OK) return st;
+  if (packed_rows == 0) return VA_OK;
+  const hipError_t e = va::launch_unpad(a, width, indices, cu_seqlens, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "unpad launch");
+  return VA_OK;
+}
+
+va_status va_pad(const va_pack_tensor* tensors, int32_t n_tensors, const int32_t* inverse,
+                 int32_t batch, int32_t seqlen, int64_t packed_rows, va_stream stream) {
+  if (!inverse) return fail(VA_ERR_INVALID, "NULL pointer argument");
+  va::PackArgs a;
+  int width = 1;
+  const va_status st = pack_args(tensors, n_tensors, batch, seqlen, packed_rows, a, width);
+  if (st != VA_OK) return st;
+  const hipError_t e = va::launch_pad(a, width, inverse, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "pad launch");
   return VA_OK;
 }
 

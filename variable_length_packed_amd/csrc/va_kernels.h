@@ -113,4 +113,23 @@ int bwd_dkdv_block_q();              // queries per dK/dV step
 hipError_t launch_bwd(const BwdArgs& a, const PlanSet& ps, int64_t max_q_items, int64_t max_k_items,
                       hipStream_t st);
 
+// ---------------------------------------------------------------------------
+// Packing: metadata from a padding mask, unpad (gather) and pad (scatter).
+// ---------------------------------------------------------------------------
+constexpr int kPackMaxTensors = 4;
+struct PackArgs {
+  void* padded[kPackMaxTensors];  // [padded_rows][row_bytes] each
+  void* packed[kPackMaxTensors];  // [packed_rows][row_bytes] each
+  int64_t row_bytes[kPackMaxTensors];
+  int32_t n;                      // tensors in use
+  int32_t batch;
+  int64_t padded_rows;            // batch * seqlen
+  int64_t packed_rows;            // rows the packed buffers hold
+};
+hipError_t launch_pack_metadata(const uint8_t* mask, int batch, int seqlen, int32_t* cu, int32_t* max_len,
+                                int32_t* indices, int32_t* position_ids, int32_t* inverse, hipStream_t st);
+// width: bytes per copy (16, 8, 4, 2 or 1), dividing every row size and base address
+hipError_t launch_unpad(const PackArgs& a, int width, const int32_t* indices, const int32_t* cu, hipStream_t st);
+hipError_t launch_pad(const PackArgs& a, int width, const int32_t* inverse, hipStream_t st);
+
 }  // namespace va

@@ -13,6 +13,7 @@ from .generate import (  # noqa: F401
     bf16_round,
     config,
     make_case,
+    padding_mask,
     CONFIG_IDS,
 )
 from .count import (  # noqa: F401

@@ -291,3 +291,27 @@ def make_case(seed: int, lens_q: Sequence[int], lens_k: Optional[Sequence[int]] 
                     lens_q=lens_q, lens_k=lens_k, hq=hq, hkv=hkv, d=d, scale=sc,
                     q=q, k=k, v=v, dout=dout, bias=b_arr, bias_strides=b_str,
                     bias_kind=bias, notes={"seed": seed, "bias_layout": bias_layout})
+
+
+def padding_mask(seed: int, batch: int, seqlen: int, kind: str = "random",
+                 lengths: Optional[Sequence[int]] = None) -> np.ndarray:
+    """uint8 [batch, seqlen] padding mask (1 = real token) of a padded batch.
+
+    kind "right" / "left": each row holds ``lengths[b]`` real tokens (drawn
+    uniform in [0, seqlen] when not given) at its start / end; "random": every
+    position is real with probability 0.6 (interior padding).
+    """
+    rng = _rng(seed, batch, seqlen, 7)
+    m = np.zeros((batch, seqlen), dtype=np.uint8)
+    if kind == "random":
+        m[:] = rng.random((batch, seqlen)) < 0.6
+        return m
+    lens = list(lengths) if lengths is not None else list(rng.integers(0, seqlen + 1, size=batch))
+    for b, L in enumerate(lens):
+        if kind == "right":
+            m[b, :L] = 1
+        elif kind == "left":
+            m[b, seqlen - L:] = 1
+        else:
+            raise ValueError(kind)
+    return m
