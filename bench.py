@@ -33,7 +33,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import config, count  # noqa: E402
+from workloads import config, count, padding_mask  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_F32_TFLOPS = 157.3     # dense fp32 MFMA
@@ -233,6 +233,53 @@ def main() -> int:
     ms_fwd2 = timed(fwd2, args.steps)
     tf2 = count.fwd_flops(w2) / (ms_fwd2 * 1e-3) / 1e12
 
+    # the packing steps either side of the path: config 3's rows right-padded to 2048
+    S = 2048
+    mask = padding_mask(0, w.batch, S, "right", lengths=list(w.lens_q))
+    dmask = torch.from_numpy(mask).to(dev)
+    pq = torch.randn(w.batch, S, w.hq, w.d, device=dev).to(torch.bfloat16)
+    pk = torch.randn(w.batch, S, w.hkv, w.d, device=dev).to(torch.bfloat16)
+    pv = torch.randn(w.batch, S, w.hkv, w.d, device=dev).to(torch.bfloat16)
+    meta = va.pack_metadata(dmask)
+    cu_p, _, idx_p, _, inv_p = meta
+    T = w.total_q
+    packed = va.unpad([pq, pk, pv], idx_p, cu_p, packed_rows=T)
+
+    def do_meta():
+        va.pack_metadata(dmask)
+
+    def do_unpad():
+        va.unpad([pq, pk, pv], idx_p, cu_p, packed_rows=T)
+
+    def do_pad():
+        va.pad([packed[0]], inv_p, w.batch, S)
+
+    for f in (do_meta, do_unpad, do_pad):
+        f()
+    torch.cuda.synchronize()
+    # kernel time by the library's event timing (the Python marshalling of a call
+    # takes longer than these kernels, so wall time per call would measure the host)
+    va.va_timing_start(16 * args.steps + 16)
+    for _ in range(args.steps):
+        do_meta()
+        do_unpad()
+        do_pad()
+    pt = va.va_timing_stop()
+    kavg = lambda *names: sum(pt[n][1] / pt[n][0] for n in names if n in pt)
+    ms_meta = kavg("pack_count", "pack_scan", "pack_index")
+    ms_unpad, ms_pad = kavg("unpad"), kavg("pad")
+    row_q, row_kv = w.hq * w.d * 2, w.hkv * w.d * 2
+    b_unpad = T * (row_q + 2 * row_kv) * 2 + T * 4          # rows read and written, indices read
+    b_pad = T * row_q + w.batch * S * row_q + w.batch * S * 4  # packed rows read, padded rows and inverse
+    gbs = lambda b, ms: round(b / (ms * 1e-3) / 1e9, 1)
+    packing = {"workload": f"config-3 rows right-padded to {S}: Q [16,{S},14,64], K/V [16,{S},2,64] bf16",
+               "timing": "library HIP events around each kernel, averaged over the timed calls",
+               "metadata_ms": round(ms_meta, 5),
+               "unpad_qkv": {"ms": round(ms_unpad, 5), "bytes": b_unpad, "GB_s": gbs(b_unpad, ms_unpad),
+                             "frac_hbm": round(b_unpad / (ms_unpad * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+               "pad_out": {"ms": round(ms_pad, 5), "bytes": b_pad, "GB_s": gbs(b_pad, ms_pad),
+                           "frac_hbm": round(b_pad / (ms_pad * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     props = torch.cuda.get_device_properties(dev)
     line = {
@@ -264,6 +311,7 @@ def main() -> int:
                             "total_tokens": w2.total_q, "ms": round(ms_fwd2, 5),
                             "tflops": round(tf2, 2), "pct_bf16_peak": round(100 * tf2 / PEAK_BF16_TFLOPS, 2)},
         "kernels": kernels,
+        "packing": packing,
         "roofline": roof,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
