@@ -8,10 +8,12 @@ never imports them.
 
 from .attention import (  # noqa: F401
     backward,
+    bias_grad,
     bias_tile,
     forward,
     head_backward,
     head_forward,
+    head_logit_grad,
     head_probs,
     sequence_group_backward,
     sequence_head_forward,

@@ -32,7 +32,10 @@ Gradients (given dO), the analytic chain rule through the softmax:
     dQ = scale * dS K;  dK = scale * dS^T Q;  dV = P^T dO
 
 with dK and dV summed over the query heads that share a KV head.  The bias
-is treated as a constant (no bias gradient).
+is added to the logits, so its gradient is dS itself, summed over every axis
+the bias is broadcast along (``bias_grad``).  The GiGL pull request 858 page
+(section "Approach") notes that the varlen kernel it calls has no backward for
+a per-sequence bias, which sends biased training to the padded path.
 
 Pins: ``tests/test_oracle_pins.py`` checks every function here against brute
 force, a library SDPA in float64, closed forms, invariants and finite
@@ -113,13 +116,21 @@ def head_probs(qb, kb, scale: float, causal: bool, bias_bh=None) -> np.ndarray:
     return p
 
 
-def head_backward(qb, kb, vb, dob, scale: float, causal: bool, bias_bh=None):
-    """One sequence, one query head.  Returns (dQ [lq, d], dK [lk, d], dV [lk, d])."""
+def head_logit_grad(qb, kb, vb, dob, scale: float, causal: bool, bias_bh=None):
+    """dS (lq, lk): the gradient of sum(dO * O) w.r.t. the logits S = scale Q K^T + bias of
+    one sequence and head (zero where the mask hides a pair)."""
     qb, kb, vb, dob = _f64(qb), _f64(kb), _f64(vb), _f64(dob)
     p = head_probs(qb, kb, scale, causal, bias_bh)
     dp = dob @ vb.T
     dsum = (p * dp).sum(axis=1, keepdims=True)
     ds = p * (dp - dsum)
+    return p, ds
+
+
+def head_backward(qb, kb, vb, dob, scale: float, causal: bool, bias_bh=None):
+    """One sequence, one query head.  Returns (dQ [lq, d], dK [lk, d], dV [lk, d])."""
+    qb, kb, vb, dob = _f64(qb), _f64(kb), _f64(vb), _f64(dob)
+    p, ds = head_logit_grad(qb, kb, vb, dob, scale, causal, bias_bh)
     dq = float(scale) * (ds @ kb)
     dk = float(scale) * (ds.T @ qb)
     dv = p.T @ dob
@@ -211,3 +222,31 @@ def backward(dout, q, k, v, cu_q, cu_k, scale, causal, bias=None, bias_strides=N
             dk[k0:k1, g] = bk
             dv[k0:k1, g] = bv
     return dq, dk, dv
+
+
+def bias_grad(dout, q, k, v, cu_q, cu_k, scale, causal, bias, bias_strides, size: int,
+              grad_strides=None):
+    """Gradient of sum(dout * out) w.r.t. a bias buffer of `size` elements read through the
+    strided view (b, h, r, c) -> b*t0 + h*t1 + r*t2 + c*t3 (t = grad_strides, default the
+    bias strides).  The bias enters the logits additively, so its gradient is dS, summed
+    into every buffer element that several (b, h, r, c) read (a stride-0 axis, e.g. the
+    rows of a per-key bias).  Elements no valid (b, h, r < Lq, c < Lk) reads stay 0."""
+    q, k, v, cu_q, cu_k, n_rep = _check(q, k, v, cu_q, cu_k)
+    dout = np.asarray(dout)
+    t0, t1, t2, t3 = (int(x) for x in (grad_strides if grad_strides is not None else bias_strides))
+    grad = np.zeros(size)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        lq, lk = q1 - q0, k1 - k0
+        if lq == 0 or lk == 0:
+            continue
+        r = np.arange(lq, dtype=np.int64)[:, None]
+        c = np.arange(lk, dtype=np.int64)[None, :]
+        for h in range(q.shape[1]):
+            g = h // n_rep
+            bb = bias_tile(bias, bias_strides, b, h, lq, lk)
+            _, ds = head_logit_grad(q[q0:q1, h], k[k0:k1, g], v[k0:k1, g], dout[q0:q1, h],
+                                    scale, causal, bb)
+            idx = b * t0 + h * t1 + r * t2 + c * t3
+            np.add.at(grad, idx.ravel(), ds.ravel())
+    return grad
