@@ -54,8 +54,9 @@
  * depends only on the tile's own sequence, so results are deterministic and a
  * sequence's results do not depend on the other sequences of the batch --
  * unless the batch would need more partial slots than the workspace's fixed
- * budget, in which case it is planned without splitting.  Contents need no
- * initialisation; a workspace must not be shared by calls that may overlap.
+ * budget, in which case the planner doubles the split length (up to 32x, then
+ * no splitting) until they fit.  Contents need no initialisation; a workspace
+ * must not be shared by calls that may overlap.
  *
  * Errors.  A non-VA_OK return means nothing was enqueued; va_last_error()
  * then holds a message for the calling thread.  Invalid device metadata
@@ -138,13 +139,29 @@ size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
 
 /*
  * Backward: dq, dk, dv of sum(dout * out) for the forward above, recomputing
- * the softmax from `lse` (the forward's own output) instead of storing it.
- * The bias, if given, is treated as a constant (no bias gradient).
+ * the softmax from `lse` (the forward's own output) instead of storing it,
+ * and optionally the bias gradient.
  *   dout, out          device, `dtype`, [total_q, num_heads_q, head_dim]
  *   lse                device float32 [num_heads_q, total_q] from va_varlen_fwd
  *   dq                 [total_q, num_heads_q, head_dim] in grad_dtype
  *   dk, dv             [total_k, num_heads_kv, head_dim] in grad_dtype; the
  *                      query heads of a GQA group are summed
+ *   dbias, dbias_stride  both NULL (no bias gradient) or both non-NULL, and then
+ *                      a bias is required.  The bias enters the logits additively,
+ *                      so its gradient is dS = P * (dP - D) (the GiGL pull request
+ *                      858 page, section "Approach", notes the varlen kernel it
+ *                      calls has no such backward).  dbias is float32, written at
+ *                      element b*t0 + h*t1 + r*t2 + c*t3 with dbias_stride = {t0,
+ *                      t1, t2, t3} (HOST int64[4]); a stride of 0 sums over that
+ *                      axis.  Supported: t0 > 0 (or batch 1) and t3 > 0;
+ *                      per pair (t2 > 0): t1 > 0 (or one query head) -- the
+ *                      elements of pairs in key blocks the causal mask skips
+ *                      entirely are NOT written (zero the buffer first); per key
+ *                      (t2 = 0): summed over rows, every (b, h, c < Lk) written,
+ *                      with t1 > 0 and at most 32 query heads per KV head, or
+ *                      t1 = 0 (summed over heads too) with one KV head.  Other
+ *                      layouts return VA_ERR_UNSUPPORTED.  Typically dbias_stride
+ *                      equals bias_stride of a float32 buffer shaped like the bias.
  *   workspace          device scratch of at least va_varlen_bwd_workspace_size()
  *                      bytes, 256-byte aligned
  *   grad_dtype         VA_F32, or VA_BF16 when dtype is VA_BF16
@@ -159,6 +176,7 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
                         float softmax_scale, int causal,
                         const void* bias, const int64_t* bias_stride,
                         void* dq, void* dk, void* dv,
+                        float* dbias, const int64_t* dbias_stride,
                         void* workspace, size_t workspace_bytes,
                         int32_t batch, int32_t total_q, int32_t total_k,
                         int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,

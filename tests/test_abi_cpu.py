@@ -102,14 +102,15 @@ def test_fwd_validation(lib, kw, code):
 
 def _bwd(lib, **kw):
     a = dict(do=P, q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, mq=8, mk=8, scale=0.125, causal=1,
-             bias=None, bstr=None, dq=P, dk=P, dv=P, ws=0x100000, wsb=1 << 30, batch=2, tq=16,
-             tk=16, hq=4, hkv=2, d=64, dt=BF16, gdt=F32)
+             bias=None, bstr=None, dq=P, dk=P, dv=P, db=None, dbstr=None, ws=0x100000, wsb=1 << 30,
+             batch=2, tq=16, tk=16, hq=4, hkv=2, d=64, dt=BF16, gdt=F32)
     a.update(kw)
     bstr = _lib.strides_arg(a["bstr"]) if a["bstr"] is not None else None
+    dbstr = _lib.strides_arg(a["dbstr"]) if a["dbstr"] is not None else None
     return lib.va_varlen_bwd(a["do"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
                              a["mq"], a["mk"], a["scale"], a["causal"], a["bias"], bstr, a["dq"],
-                             a["dk"], a["dv"], a["ws"], a["wsb"], a["batch"], a["tq"], a["tk"],
-                             a["hq"], a["hkv"], a["d"], a["dt"], a["gdt"], None)
+                             a["dk"], a["dv"], a["db"], dbstr, a["ws"], a["wsb"], a["batch"], a["tq"],
+                             a["tk"], a["hq"], a["hkv"], a["d"], a["dt"], a["gdt"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -122,6 +123,15 @@ def _bwd(lib, **kw):
     (dict(dt=F32, gdt=BF16), UNSUPPORTED),
     (dict(gdt=5), UNSUPPORTED),
     (dict(wsb=16), WORKSPACE),
+    # bias gradient
+    (dict(db=P), INVALID),                                              # no dbias_stride
+    (dict(db=P, dbstr=(64, 16, 4, 1)), INVALID),                        # no bias
+    (dict(bias=P, bstr=(64, 16, 4, 1), db=P, dbstr=(64, 16, -4, 1)), INVALID),
+    (dict(bias=P, bstr=(64, 16, 4, 1), db=P, dbstr=(0, 16, 4, 1)), UNSUPPORTED),   # summed over sequences
+    (dict(bias=P, bstr=(64, 16, 4, 1), db=P, dbstr=(64, 16, 4, 0)), UNSUPPORTED),  # summed over keys
+    (dict(bias=P, bstr=(64, 16, 4, 1), db=P, dbstr=(64, 0, 4, 1)), UNSUPPORTED),   # per pair, summed over heads
+    (dict(bias=P, bstr=(16, 4, 0, 1), db=P, dbstr=(16, 0, 0, 1)), UNSUPPORTED),    # per key over heads, 2 KV heads
+    (dict(bias=P, bstr=(16, 4, 0, 1), db=P, dbstr=(16, 4, 0, 1), hq=66, hkv=2), UNSUPPORTED),  # 33 heads per KV head
 ])
 def test_bwd_validation(lib, kw, code):
     assert _bwd(lib, **kw) == code
@@ -162,13 +172,13 @@ def test_bwd_workspace_size(lib):
     assert f(2, 16, 16, 8, 8, 4, 2, 64, F32, BF16) == 0
     # short sequences: D = rowsum(dO * O) and the two plans (dK/dV and dQ)
     n = f(2, 16, 16, 8, 8, 4, 4, 64, BF16, F32)
-    assert n == _r(4 * 16 * 4) + 2 * _plan_bytes(2, 0)
+    assert n == _r(4 * 16 * 4) + 2 * _plan_bytes(2, 0)  # no partial slots (per-key bias sums: none)
     # GQA 4/2: a dK/dV unit holds at most 768 (query row, head) pairs = 12 blocks of 32
     assert f(2, 16, 16, 384, 8, 4, 2, 64, BF16, F32) == n
     big = f(2, 16, 16, 416, 8, 4, 2, 64, BF16, F32)
     slots_k = 2 * 2  # two tiles, ceil(13 / 12) = 2 chunks each
     assert big == _r(4 * 16 * 4) + _plan_bytes(2 + slots_k, slots_k // 2) + _plan_bytes(2, 0) + \
-        _r(slots_k * 2 * 2 * 128 * 64 * 4)
+        _r(slots_k * 2 * 2 * 128 * 64 * 4) + _r(slots_k * 4 * 128 * 4)  # + per-key bias sums per slot
 
 
 def test_python_layer_rejects_cpu_tensors_and_bias_grad():
@@ -179,8 +189,8 @@ def test_python_layer_rejects_cpu_tensors_and_bias_grad():
     with pytest.raises(ValueError):
         va.va_varlen_fwd(q, q, q, cu, cu, 4, 4)
     b = torch.zeros(1, 2, 4, 4, requires_grad=True)
-    with pytest.raises(ValueError):
-        va.varlen_attn(q, q, q, cu, cu, 4, 4, bias=b)
+    with pytest.raises(ValueError):  # a bias through an explicit strided view cannot require grad
+        va.varlen_attn(q, q, q, cu, cu, 4, 4, bias=b, bias_stride=(32, 16, 4, 1))
 
 
 # ---------------------------------------------------------------- packing (include/va_pack.h)

@@ -136,8 +136,9 @@ def test_python_errors_on_gpu_tensors():
     with pytest.raises(ValueError):  # non-contiguous input
         va.va_varlen_fwd(inp["q"].transpose(0, 1), inp["k"], inp["v"], inp["cu_q"], inp["cu_k"], 7, 7)
     b = torch.zeros(2, 2, 7, 7, dtype=torch.bfloat16, device=_gpu.DEV, requires_grad=True)
-    with pytest.raises(ValueError):  # a bias that needs a gradient
-        va.varlen_attn(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_k"], 7, 7, bias=b)
+    with pytest.raises(ValueError):  # a bias that needs a gradient, read through an explicit view
+        va.varlen_attn(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_k"], 7, 7, bias=b,
+                       bias_stride=(98, 49, 7, 1))
     with pytest.raises(ValueError):  # bias view reaching past its storage
         small = torch.zeros(2, 2, 3, 3, dtype=torch.bfloat16, device=_gpu.DEV)
         va.va_varlen_fwd(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_k"], 7, 7, bias=small)

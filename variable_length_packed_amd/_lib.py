@@ -47,8 +47,8 @@ def load() -> ctypes.CDLL:
                                   ctypes.c_int, _p]
     lib.va_varlen_bwd.restype = ctypes.c_int
     lib.va_varlen_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p,
-                                  _i64p, _p, _p, _p, _p, ctypes.c_size_t, _i32, _i32, _i32, _i32,
-                                  _i32, _i32, ctypes.c_int, ctypes.c_int, _p]
+                                  _i64p, _p, _p, _p, _p, _i64p, _p, ctypes.c_size_t, _i32, _i32,
+                                  _i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int, _p]
     lib.va_varlen_fwd_workspace_size.restype = ctypes.c_size_t
     lib.va_varlen_fwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                  ctypes.c_int]

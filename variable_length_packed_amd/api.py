@@ -166,8 +166,16 @@ def va_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch
                   grad_dtype: torch.dtype = torch.float32,
                   dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                   dv: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None):
-    """Backward.  Returns (dq, dk, dv) in ``grad_dtype``."""
+                  workspace: Optional[torch.Tensor] = None,
+                  dbias: Optional[torch.Tensor] = None,
+                  dbias_stride: Optional[Sequence[int]] = None):
+    """Backward.  Returns (dq, dk, dv) in ``grad_dtype``.
+
+    With ``dbias`` (a float32 device tensor) and ``dbias_stride`` (4 element
+    strides relative to ``dbias``'s first element; 0 sums over that axis), the
+    bias gradient is written into ``dbias`` as include/va_varlen.h describes
+    (elements of pairs in key blocks a causal mask skips are left as they are).
+    """
     lib = _lib.load()
     for n, t in (("dout", dout), ("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse),
                  ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
@@ -200,6 +208,22 @@ def va_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch
         _need_dev(n, t, q.device)
         if t.shape != shp or t.dtype != grad_dtype:
             raise ValueError(f"{n} has the wrong shape or dtype")
+    dbptr, dbstr = None, None
+    if (dbias is None) != (dbias_stride is None):
+        raise ValueError("dbias and dbias_stride go together")
+    if dbias is not None:
+        if bias is None:
+            raise ValueError("dbias needs a bias")
+        if dbias.device != q.device or dbias.dtype != torch.float32:
+            raise ValueError("dbias must be a float32 tensor on q's device")
+        t = [int(x) for x in dbias_stride]
+        if len(t) != 4 or min(t) < 0:
+            raise ValueError("dbias_stride must be 4 non-negative element strides")
+        hi = (batch - 1) * t[0] + (hq - 1) * t[1] + (int(max_seqlen_q) - 1) * t[2] + (int(max_seqlen_k) - 1) * t[3]
+        avail = dbias.untyped_storage().nbytes() // 4 - dbias.storage_offset()
+        if hi >= avail:
+            raise ValueError(f"dbias view reaches element {hi} but only {avail} exist")
+        dbptr, dbstr = dbias.data_ptr(), _lib.strides_arg(t)
     need = lib.va_varlen_bwd_workspace_size(batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k),
                                             hq, hkv, d, dt, gdt)
     if workspace is None:
@@ -209,7 +233,7 @@ def va_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch
                            out.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
                            cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
                            int(bool(causal)), bptr, bstr, dq.data_ptr(), dk.data_ptr(),
-                           dv.data_ptr(), workspace.data_ptr(),
+                           dv.data_ptr(), dbptr, dbstr, workspace.data_ptr(),
                            workspace.numel() * workspace.element_size(), batch, tq, tk, hq, hkv,
                            d, dt, gdt, _stream(q.device))
     _raise(st, lib)
@@ -232,22 +256,35 @@ class _VarlenAttn(torch.autograd.Function):
     def backward(ctx, dout, dlse):
         q, k, v, out, lse, cu_q, cu_k = ctx.saved_tensors
         max_q, max_k, scale, causal, bias_stride, grad_dtype = ctx.args
+        bias = ctx.bias
+        db, dbs = None, None
+        if bias is not None and ctx.needs_input_grad[9]:
+            # a dense float32 gradient shaped like the bias; its size-1 head or row axis
+            # (a head-shared or per-key bias) is summed over by a zero stride
+            db = torch.zeros(bias.shape, dtype=torch.float32, device=bias.device)
+            dbs = list(db.stride())
+            for ax in (1, 2):
+                if bias.shape[ax] == 1:
+                    dbs[ax] = 0
         dq, dk, dv = va_varlen_bwd(dout.contiguous(), q, k, v, out, lse, cu_q, cu_k, max_q, max_k,
-                                   scale, causal, ctx.bias, bias_stride, grad_dtype)
+                                   scale, causal, bias, bias_stride, grad_dtype, dbias=db,
+                                   dbias_stride=dbs)
         return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None, None,
-                None, None, None, None)
+                None, db.to(bias.dtype) if db is not None else None, None, None)
 
 
 def varlen_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                 softmax_scale=None, causal=False, bias=None, bias_stride=None,
                 grad_dtype=torch.float32):
-    """Differentiable packed attention: returns (out, lse); gradients flow to q, k, v.
+    """Differentiable packed attention: returns (out, lse); gradients flow to q, k, v and
+    to a 4-D bias [batch, heads or 1, rows or 1, cols] given without ``bias_stride``.
 
-    The bias is a constant: a bias that requires grad raises ValueError (the
-    kernel has no bias gradient).  The LSE output carries no gradient.
+    A bias read through an explicit ``bias_stride`` view cannot require grad
+    (call va_varlen_bwd with dbias for that).  The LSE output carries no gradient.
     """
-    if bias is not None and bias.requires_grad:
-        raise ValueError("bias gradients are not supported: pass a bias that does not require grad")
+    if bias is not None and bias.requires_grad and bias_stride is not None:
+        raise ValueError("a bias read through bias_stride cannot require grad here: use "
+                         "va_varlen_bwd(..., dbias=, dbias_stride=)")
     return _VarlenAttn.apply(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                              softmax_scale, causal, bias, bias_stride, grad_dtype)
 

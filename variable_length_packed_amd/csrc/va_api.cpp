@@ -160,12 +160,16 @@ PlanLayout dq_plan(int batch, int total_q, int max_k, int hq, int d, bool bf16) 
                      (size_t)hq * bm * d * sizeof(float), kDqPartBudget);
 }
 
+// per-key bias-gradient sums of one dK/dV partial slot: [Hkv][n_rep][128 keys] floats
+size_t dbias_slot_bytes(int hq) { return (size_t)hq * va::bwd_block_k() * sizeof(float); }
+
 size_t bwd_workspace(int batch, int total_q, int total_k, int max_q, int max_k, int hq, int hkv,
                      int d, bool bf16) {
   const PlanLayout K = dkdv_plan(batch, total_k, max_q, hkv, hq / hkv, d);
   const PlanLayout Q = dq_plan(batch, total_q, max_k, hq, d, bf16);
   return round_up((size_t)hq * total_q * sizeof(float)) + K.plan_bytes + Q.plan_bytes +
-         round_up(K.slot_bytes * K.slot_cap) + round_up(Q.slot_bytes * Q.slot_cap);
+         round_up(K.slot_bytes * K.slot_cap) + round_up(Q.slot_bytes * Q.slot_cap) +
+         round_up(dbias_slot_bytes(hq) * K.slot_cap);
 }
 
 va_status hip_fail(hipError_t e, const char* what) {
@@ -270,7 +274,8 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
                         const void* out, const float* lse, const int32_t* cu_seqlens_q,
                         const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
                         float softmax_scale, int causal, const void* bias,
-                        const int64_t* bias_stride, void* dq, void* dk, void* dv, void* workspace,
+                        const int64_t* bias_stride, void* dq, void* dk, void* dv, float* dbias,
+                        const int64_t* dbias_stride, void* workspace,
                         size_t workspace_bytes, int32_t batch, int32_t total_q, int32_t total_k,
                         int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                         va_dtype dtype, va_dtype grad_dtype, va_stream stream) {
@@ -286,6 +291,29 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
     return fail(VA_ERR_UNSUPPORTED, "unknown grad_dtype %d", (int)grad_dtype);
   if (dtype == VA_F32 && grad_dtype == VA_BF16)
     return fail(VA_ERR_UNSUPPORTED, "bf16 gradients of float32 inputs are not supported");
+  int dbias_mode = 0;
+  if ((dbias == nullptr) != (dbias_stride == nullptr))
+    return fail(VA_ERR_INVALID, "dbias and dbias_stride must both be NULL or both non-NULL");
+  if (dbias) {
+    if (!bias) return fail(VA_ERR_INVALID, "dbias requires a bias");
+    const int64_t* t = dbias_stride;
+    for (int i = 0; i < 4; ++i)
+      if (t[i] < 0) return fail(VA_ERR_INVALID, "dbias_stride[%d] is negative", i);
+    const int n_rep_ = num_heads_q / num_heads_kv;
+    if ((t[0] == 0 && batch > 1) || t[3] == 0)
+      return fail(VA_ERR_UNSUPPORTED, "a bias gradient summed over sequences or keys is not supported");
+    if (t[2] != 0) {  // per pair: every (b, h, r, c) its own element
+      if (t[1] == 0 && num_heads_q > 1)
+        return fail(VA_ERR_UNSUPPORTED, "a per-pair bias gradient summed over heads is not supported");
+      dbias_mode = 1;
+    } else {  // per key: summed over rows (and over heads when t1 = 0)
+      if (t[1] == 0 ? num_heads_kv != 1 : n_rep_ > 32)
+        return fail(VA_ERR_UNSUPPORTED,
+                    "a per-key bias gradient needs a head stride with at most 32 query heads per "
+                    "KV head, or one KV head when summed over heads");
+      dbias_mode = 2;
+    }
+  }
   if (((uintptr_t)workspace) % kAlign != 0)
     return fail(VA_ERR_INVALID, "workspace must be 256-byte aligned");
   const bool bf16 = dtype == VA_BF16;
@@ -319,6 +347,11 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
   a.part_kv = (float*)(w + o);
   o += round_up(K.slot_bytes * K.slot_cap);
   a.part_q = (float*)(w + o);
+  o += round_up(Q.slot_bytes * Q.slot_cap);
+  a.part_db = (float*)(w + o);
+  a.dbias = dbias;
+  a.dbias_mode = dbias_mode;
+  if (dbias) { a.ds0 = dbias_stride[0]; a.ds1 = dbias_stride[1]; a.ds2 = dbias_stride[2]; a.ds3 = dbias_stride[3]; }
   a.split_cap_k = K.split_cap;
   a.split_cap_q = Q.split_cap;
 

@@ -43,6 +43,7 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int BNK = 128;     // keys per dK/dV workgroup
+constexpr int kDbiasMaxHeads = 32;  // query heads per KV head with a per-key bias gradient
 constexpr int BMQ_DQ = 128;  // query rows per dQ workgroup
 
 template <bool BF16>
@@ -245,6 +246,8 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
 
   __shared__ SM sm;
   __shared__ int s_info[2][10];
+  // per-key bias gradient sums [head of the group][key of the tile] (bias kernels only)
+  __shared__ float db_acc[HAS_BIAS ? kDbiasMaxHeads * BNK : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
   const int hh = lane >> 5, r32 = lane & 31;
@@ -371,6 +374,25 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
           p[i] = pv;
           ds[i] = pv * (dp[i] - sm.dsum[buf][ql]);
         }
+        if constexpr (HAS_BIAS) {
+          // bias gradient = dS (the bias enters the logits additively)
+          if (a.dbias_mode == 1) {
+            if (kj < Lk) {
+              float* db = a.dbias + (int64_t)b * a.ds0 + (int64_t)h * a.ds1 + (int64_t)kj * a.ds3;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int qi = qb + 8 * (i >> 2) + 4 * hh + (i & 3);
+                if (qi < Lq) db[(int64_t)qi * a.ds2] = ds[i];
+              }
+            }
+          } else if (a.dbias_mode == 2) {
+            float cs = 0.f;  // this lane's key over its 16 rows, then over both lane halves
+#pragma unroll
+            for (int i = 0; i < 16; ++i) cs += ds[i];
+            cs += xor32(cs);
+            if (hh == 0) db_acc[(a.ds1 == 0 ? 0 : r) * BNK + 32 * wid + r32] += cs;
+          }
+        }
         // dV += P^T dO, dK += dS^T Q: C[key][d], lane = d
         if constexpr (BF16) {
 #pragma unroll
@@ -406,6 +428,11 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
       __syncthreads();
     };
 
+    if constexpr (HAS_BIAS) {
+      // per-key bias gradient: each wave sums into its own 32 columns (no barrier needed)
+      if (a.dbias_mode == 2 && hh == 0)
+        for (int r = 0; r < (a.ds1 == 0 ? 1 : hpw); ++r) db_acc[r * BNK + 32 * wid + r32] = 0.f;
+    }
     int2 rn = make_int2(0, u0);
     if (k_total > 0) { issue(rn); commit(0); }
     __syncthreads();
@@ -425,6 +452,21 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
     if (tid == 0) {
       item_store(s_info[cur ^ 1], nxt);  // before the output stores
       ticket = queue_take(a.plan_k.hdr);  // waited for in the next item's prologue
+    }
+
+    if constexpr (HAS_BIAS) {
+      if (a.dbias_mode == 2 && hh == 0) {
+        const int nacc = a.ds1 == 0 ? 1 : hpw;
+        if (slot < 0) {
+          if (kj < Lk)
+            for (int r = 0; r < nacc; ++r)
+              a.dbias[(int64_t)b * a.ds0 + (int64_t)(h_first + r) * a.ds1 + (int64_t)kj * a.ds3] =
+                  db_acc[r * BNK + 32 * wid + r32];
+        } else {
+          float* pd = a.part_db + ((size_t)slot * a.hkv + g) * hpw * BNK;
+          for (int r = 0; r < nacc; ++r) pd[r * BNK + 32 * wid + r32] = db_acc[r * BNK + 32 * wid + r32];
+        }
+      }
     }
 
     // ---- epilogue.  Register i of tile dt holds key wk0 + 8(i/4) + 4hh + i%4,
@@ -514,6 +556,16 @@ __global__ __launch_bounds__(NT) void dkdv_merge_kernel(BwdArgs a) {
           ((float*)a.dk)[o] = kv;
           ((float*)a.dv)[o] = vv;
         }
+      }
+    }
+    if (a.dbias_mode == 2) {  // per-key bias gradient: chunk sums in chunk order
+      const int nacc = a.ds1 == 0 ? 1 : a.n_rep;
+      for (int e = threadIdx.x; e < nacc * 32; e += NT) {
+        const int r = e >> 5, kk = 32 * w + (e & 31), key = t * BNK + kk;
+        if (key >= Lk) continue;
+        float s = 0.f;
+        for (int c = 0; c < nch; ++c) s += a.part_db[(((size_t)(sb + c) * a.hkv + g) * a.n_rep + r) * BNK + kk];
+        a.dbias[(int64_t)b * a.ds0 + (int64_t)(g * a.n_rep + r) * a.ds1 + (int64_t)key * a.ds3] = s;
       }
     }
   }

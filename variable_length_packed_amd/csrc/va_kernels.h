@@ -84,6 +84,13 @@ struct BwdArgs {
   Plan plan_q;     // dQ pass: query tiles
   float* part_kv;  // [slot][hkv][2][BNK][d]  dK (unscaled) and dV partial sums
   float* part_q;   // [slot][hq][BMQ][d]      dQ (unscaled) partial sums
+  // bias gradient (dbias_mode 0: none; 1: per pair, dS stored at element
+  // b*ds0 + h*ds1 + r*ds2 + c*ds3; 2: per key (ds2 = 0), dS summed over rows,
+  // and over the heads too when ds1 = 0 (one KV head))
+  float* dbias;
+  int64_t ds0, ds1, ds2, ds3;
+  int32_t dbias_mode;
+  float* part_db;  // [slot][hkv][n_rep][BNK]  per-key sums of split key tiles
   int32_t batch, total_q, total_k, hq, hkv, n_rep, d;
   int32_t split_cap_k, split_cap_q;
   float scale;
