@@ -280,6 +280,46 @@ def main() -> int:
                "pad_out": {"ms": round(ms_pad, 5), "bytes": b_pad, "GB_s": gbs(b_pad, ms_pad),
                            "frac_hbm": round(b_pad / (ms_pad * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
 
+    # bias gradient: the graph-encoder workload (512 seqs U[1,256], 8/8 heads, d64, non-causal,
+    # bf16) with a per-pair bias grid [512, 8, 256, 256], forward + backward with dbias
+    w4 = config(4, dtype="bf16", bias="per_key", with_dout=True)  # Q/K/V/dO; the grid is drawn on device
+    x4 = dev_inputs(w4)
+    G = 256
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    grid = (0.5 * torch.randn(w4.batch * w4.hq * G * G, generator=gen, device=dev)).to(torch.bfloat16)
+    gstr = (w4.hq * G * G, G * G, G, 1)
+    dgrid = torch.zeros(grid.numel(), dtype=torch.float32, device=dev)
+    o4 = torch.empty_like(x4["q"])
+    l4 = torch.empty((w4.hq, w4.total_q), dtype=torch.float32, device=dev)
+    g4 = [torch.empty(x4[n].shape, dtype=torch.float32, device=dev) for n in "qkv"]
+    wf4 = torch.empty(va.va_varlen_fwd_workspace_size(w4.batch, w4.total_q, w4.total_k, w4.max_q, w4.max_k,
+                                                      w4.hq, w4.hkv, w4.d, torch.bfloat16),
+                      dtype=torch.uint8, device=dev)
+    wb4 = torch.empty(va.va_varlen_bwd_workspace_size(w4.batch, w4.total_q, w4.total_k, w4.max_q, w4.max_k,
+                                                      w4.hq, w4.hkv, w4.d, torch.bfloat16, torch.float32),
+                      dtype=torch.uint8, device=dev)
+
+    def step4():
+        va.va_varlen_fwd(x4["q"], x4["k"], x4["v"], x4["cu_q"], x4["cu_k"], w4.max_q, w4.max_k, w4.scale,
+                         False, grid, gstr, out=o4, lse=l4, workspace=wf4)
+        va.va_varlen_bwd(x4["dout"], x4["q"], x4["k"], x4["v"], o4, l4, x4["cu_q"], x4["cu_k"], w4.max_q,
+                         w4.max_k, w4.scale, False, grid, gstr, dq=g4[0], dk=g4[1], dv=g4[2], workspace=wb4,
+                         dbias=dgrid, dbias_stride=gstr)
+
+    for _ in range(2):
+        step4()
+    ms4 = timed(step4, max(3, args.steps // 4))
+    valid = int(sum(int(L) * int(L) for L in w4.lens_q)) * w4.hq
+    fl4 = count.fwd_flops(w4) + count.bwd_flops(w4)
+    bias_bytes = valid * (2 + 2 + 2 + 4)  # bias read by the forward, dK/dV and dQ passes; dbias written
+    bias_grad = {"workload": "graph encoder, 512 seqs U[1,256], 8/8 heads, d64, non-causal, bf16, per-pair "
+                             "bias grid [512,8,256,256], fwd + bwd with dbias (float32, same layout)",
+                 "ms_per_step": round(ms4, 5), "tflops": round(fl4 / (ms4 * 1e-3) / 1e12, 2),
+                 "valid_bias_elements": valid, "bias_stream_bytes": bias_bytes,
+                 "bias_stream_GB_s": round(bias_bytes / (ms4 * 1e-3) / 1e9, 1)}
+    del grid, dgrid
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     props = torch.cuda.get_device_properties(dev)
     line = {
@@ -312,6 +352,7 @@ def main() -> int:
                             "tflops": round(tf2, 2), "pct_bf16_peak": round(100 * tf2 / PEAK_BF16_TFLOPS, 2)},
         "kernels": kernels,
         "packing": packing,
+        "bias_grad": bias_grad,
         "roofline": roof,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
