@@ -108,9 +108,11 @@ typedef void* va_stream;
  * Returns VA_ERR_INVALID for a NULL required pointer, exactly one of
  * bias/bias_stride NULL, batch/total/heads/head_dim <= 0, Hq % Hkv != 0,
  * max_seqlen <= 0, a negative stride, a scale that is not finite and > 0, a
- * misaligned workspace; VA_ERR_UNSUPPORTED for head_dim not in {64, 128} or
- * an unknown dtype; VA_ERR_WORKSPACE for too small a workspace; VA_ERR_HIP
- * if a launch fails.
+ * misaligned workspace; VA_ERR_UNSUPPORTED for head_dim not in {64, 128}, an
+ * unknown dtype, or a bias view spanning 2 GiB or more inside one (sequence,
+ * head); VA_ERR_WORKSPACE for too small a workspace; VA_ERR_HIP if a launch
+ * fails.  A bias with contiguous keys (bias_stride[3] = 1), strides that are
+ * multiples of 4 and a base aligned to 4 elements is read 4 keys per load.
  */
 va_status va_varlen_fwd(const void* q, const void* k, const void* v,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

@@ -224,12 +224,18 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
       l_run[qt] = 0.f;
     }
 
-    const T* bias_bh[QT];
-    if constexpr (HAS_BIAS)
+    // this (sequence, head)'s bias view (element (r, c) at r*bs2 + c*bs3) and the byte
+    // offset of this lane's row and key half in it
+    rsrc_t bres = make_rsrc(a.bias, 0);
+    int boff[QT];
+    if constexpr (HAS_BIAS) {
+      // the resource ends after the last element a valid (r, c) reads, rounded up to a
+      // whole dword; loads past it (rows before the sequence, keys past its end) read 0
+      const int64_t last = Lq > 0 && Lk > 0 ? ((int64_t)(Lq - 1) * a.bs2 + (int64_t)(Lk - 1) * a.bs3 + 1) * ELT : 0;
+      bres = make_rsrc((const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1, (last + 3) & ~(int64_t)3);
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-        bias_bh[qt] = (const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1 +
-                      (int64_t)max(rq[qt], 0) * a.bs2;
+      for (int qt = 0; qt < QT; ++qt) boff[qt] = (int)(((int64_t)rq[qt] * a.bs2 + 4 * hh * a.bs3) * ELT);
+    }
 
     Loader<BF16, D> ld;
 
@@ -322,22 +328,50 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) {
         const unsigned span = (unsigned)max(hi_row[qt] + 1, 0);  // kj <= hi_row (none if < 0)
+        float bv[HAS_BIAS ? NS : 1][16];
+        if constexpr (HAS_BIAS) {
+          if (a.bias_vec) {
+            // registers 4j .. 4j+3 of a score tile are 4 consecutive keys: one 8-byte
+            // (bf16) or 16-byte (f32) load each; keys past the sequence are masked
+            // below, rows outside it are never stored
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int off = boff[qt] + (kb + 32 * st + 8 * j) * ELT;
+                if constexpr (BF16) {
+                  const u32x2_t x = buf_load8(bres, off);
+                  bv[st][4 * j + 0] = __uint_as_float(x[0] << 16);
+                  bv[st][4 * j + 1] = __uint_as_float(x[0] & 0xFFFF0000u);
+                  bv[st][4 * j + 2] = __uint_as_float(x[1] << 16);
+                  bv[st][4 * j + 3] = __uint_as_float(x[1] & 0xFFFF0000u);
+                } else {
+                  const u32x4_t x = buf_load16(bres, off);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) bv[st][4 * j + e] = __uint_as_float(x[e]);
+                }
+              }
+          } else {
+            // any other layout: one element per load, same resource
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int off = boff[qt] + (kb + 32 * st + 8 * (i >> 2) + (i & 3)) * (int)a.bs3 * ELT;
+                if constexpr (BF16)
+                  bv[st][i] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(bres, off, 0, 0) << 16);
+                else
+                  bv[st][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bres, off, 0, 0));
+              }
+          }
+        }
 #pragma unroll
         for (int st = 0; st < NS; ++st)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int ci = 32 * st + 8 * (i >> 2) + (i & 3);
             float v = s[qt][st][i];
-            if constexpr (HAS_BIAS) {
-              const int kj = kb + ci + 4 * hh;
-              v *= a.scale_log2;
-              if (rq[qt] >= 0 && kj >= 0 && kj < Lk) {
-                float bf;
-                if constexpr (BF16) bf = bf16_to_f32(bias_bh[qt][(int64_t)kj * a.bs3]);
-                else bf = bias_bh[qt][(int64_t)kj * a.bs3];
-                v = __builtin_fmaf(bf, kLog2e, v);
-              }
-            }
+            if constexpr (HAS_BIAS) v = __builtin_fmaf(bv[st][i], kLog2e, v * a.scale_log2);
             if constexpr (MASK) v = ((unsigned)(ci - lo_rel) < span) ? v : -INFINITY;
             s[qt][st][i] = v;
           }

@@ -63,6 +63,7 @@ struct FwdArgs {
   float scale_log2;
   int32_t causal;
   int32_t bf16;
+  int32_t bias_vec;  // keys contiguous (bs3 = 1), 4-key groups aligned: vector bias loads
 };
 
 struct BwdArgs {
