@@ -337,7 +337,15 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
   a.dout = dout; a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
   a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
   a.bias = bias;
-  if (bias) { a.bs0 = bias_stride[0]; a.bs1 = bias_stride[1]; a.bs2 = bias_stride[2]; a.bs3 = bias_stride[3]; }
+  if (bias) {
+    a.bs0 = bias_stride[0]; a.bs1 = bias_stride[1]; a.bs2 = bias_stride[2]; a.bs3 = bias_stride[3];
+    const int elt = bf16 ? 2 : 4;
+    const int64_t span = ((int64_t)max_seqlen_q * a.bs2 + ((int64_t)max_seqlen_k + 64) * a.bs3 + 8) * elt;
+    if (span >= ((int64_t)1 << 31))
+      return fail(VA_ERR_UNSUPPORTED, "a bias view spanning 2 GiB or more per sequence and head");
+    a.bias_vec = a.bs3 == 1 && a.bs0 % 4 == 0 && a.bs1 % 4 == 0 && a.bs2 % 4 == 0 &&
+                 ((uintptr_t)bias) % (4 * elt) == 0;
+  }
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.batch = batch; a.total_q = total_q; a.total_k = total_k;
   a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = n_rep; a.d = head_dim;

@@ -160,8 +160,6 @@ __device__ __forceinline__ f32x16_t mm_rows(const elem_t<BF16>* lrow, const RowF
   return acc;
 }
 
-__device__ __forceinline__ float ld_bias(const uint16_t* p) { return bf16_to_f32(*p); }
-__device__ __forceinline__ float ld_bias(const float* p) { return *p; }
 
 // bf16 operand of 8 values and, optionally, the bf16 residual of the same 8.
 __device__ __forceinline__ void pack8(const float* v, u32x4_t& hi, u32x4_t* lo) {
@@ -354,9 +352,16 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
         // S = Q K^T and dP = dO V^T: C[query][key], lane = key
         f32x16_t s = mm_rows<BF16, D>(&sm.qn[buf][r32 * St::NP], kf, (f32x16_t){}, hh);
         f32x16_t dp = mm_rows<BF16, D>(&sm.dn[buf][r32 * St::NP], vf, (f32x16_t){}, hh);
-        const T* bias_h = nullptr;
-        if constexpr (HAS_BIAS)
-          bias_h = (const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1 + (int64_t)kj * a.bs3;
+        // the bias of head h through a resource that ends after the last element a valid
+        // (row, key) reads (rounded up to a dword); rows past the sequence read 0 or are
+        // zeroed below, so garbage never meets a row whose P must be 0
+        rsrc_t bres = make_rsrc(a.bias, 0);
+        int brow = 0;
+        if constexpr (HAS_BIAS) {
+          const int64_t last = ((int64_t)(Lq - 1) * a.bs2 + (int64_t)(Lk - 1) * a.bs3 + 1) * ELT;
+          bres = make_rsrc((const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1, (last + 3) & ~(int64_t)3);
+          brow = (int)(((int64_t)kj * a.bs3 + (int64_t)(qb + 4 * hh) * a.bs2) * ELT);
+        }
         // causal: key kj is visible to query qb + ql iff ql >= kj - off - qb
         const int thr = kj - off - qb - 4 * hh;
         float p[16], ds[16];
@@ -366,8 +371,11 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
           const int ql = cl + 4 * hh;
           float x = s[i] * a.scale_log2;
           if constexpr (HAS_BIAS) {
-            const int qi = qb + ql;
-            if (qi < Lq && kj < Lk) x = __builtin_fmaf(ld_bias(bias_h + (int64_t)qi * a.bs2), kLog2e, x);
+            const int off = brow + cl * (int)a.bs2 * ELT;
+            float bf;
+            if constexpr (BF16) bf = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(bres, off, 0, 0) << 16);
+            else bf = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bres, off, 0, 0));
+            x = __builtin_fmaf(qb + ql < Lq ? bf : 0.f, kLog2e, x);
           }
           float pv = fast_exp2(x - sm.lse2[buf][ql]);
           if constexpr (MASK) pv = cl >= thr ? pv : 0.f;
@@ -583,8 +591,10 @@ struct DqSmem {
   T vn[2][BN * St::NP];
 };
 
-template <bool BF16, int D, bool CAUSAL, bool HAS_BIAS>
+// BIAS: 0 none; 1 any layout (one element per load); 2 contiguous keys (four per load)
+template <bool BF16, int D, bool CAUSAL, int BIAS>
 __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
+  constexpr bool HAS_BIAS = BIAS != 0;
   using T = elem_t<BF16>;
   using SM = DqSmem<BF16, D>;
   constexpr int BN = SM::BN;
@@ -656,9 +666,16 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     const int64_t kbytes = kv_end > 0 ? (int64_t)(kv_end - 1) * krow_bytes + D * ELT : 0;
     const rsrc_t kres = make_rsrc((const T*)a.k + koff, kbytes);
     const rsrc_t vres = make_rsrc((const T*)a.v + koff, kbytes);
-    const T* bias_bh = nullptr;
-    if constexpr (HAS_BIAS)
-      bias_bh = (const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1 + (int64_t)max(rq, 0) * a.bs2;
+    // this (sequence, head)'s bias view (element (r, c) at r*bs2 + c*bs3), ending after the
+    // last element a valid (row, key) reads; rows before the sequence read 0, keys past
+    // it are masked
+    rsrc_t bres = make_rsrc(a.bias, 0);
+    int boff = 0;
+    if constexpr (HAS_BIAS) {
+      const int64_t last = Lq > 0 && Lk > 0 ? ((int64_t)(Lq - 1) * a.bs2 + (int64_t)(Lk - 1) * a.bs3 + 1) * ELT : 0;
+      bres = make_rsrc((const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1, (last + 3) & ~(int64_t)3);
+      boff = (int)(((int64_t)rq * a.bs2 + 4 * hh * a.bs3) * ELT);
+    }
     const int hi_row = CAUSAL ? min(kv_hi - 1, rq + off) : kv_hi - 1;
 
     St sk;
@@ -678,14 +695,48 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
           // S^T = K Q^T, dP^T = V dO^T: C[key][query], lane = query
           const f32x16_t s = mm_rows<BF16, D>(&sm.kn[buf][(32 * st + r32) * St::NP], qf, (f32x16_t){}, hh);
           const f32x16_t dp = mm_rows<BF16, D>(&sm.vn[buf][(32 * st + r32) * St::NP], of, (f32x16_t){}, hh);
+          float bv[HAS_BIAS ? 16 : 1];
+          if constexpr (HAS_BIAS) {
+            // registers 4j .. 4j+3 are 4 consecutive keys: one load each when keys are
+            // contiguous, else four element loads packed the same way
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int key = kb + 32 * st + 8 * j;
+              if constexpr (BF16) {
+                u32x2_t x;
+                if constexpr (BIAS == 2) {
+                  x = buf_load8(bres, boff + key * ELT);
+                } else {
+                  uint32_t e[4];
+#pragma unroll
+                  for (int c = 0; c < 4; ++c)
+                    e[c] = __builtin_amdgcn_raw_buffer_load_b16(bres, boff + (key + c) * (int)a.bs3 * ELT, 0, 0);
+                  x = (u32x2_t){e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+                }
+                bv[4 * j + 0] = __uint_as_float(x[0] << 16);
+                bv[4 * j + 1] = __uint_as_float(x[0] & 0xFFFF0000u);
+                bv[4 * j + 2] = __uint_as_float(x[1] << 16);
+                bv[4 * j + 3] = __uint_as_float(x[1] & 0xFFFF0000u);
+              } else {
+                u32x4_t x;
+                if constexpr (BIAS == 2) {
+                  x = buf_load16(bres, boff + key * ELT);
+                } else {
+#pragma unroll
+                  for (int c = 0; c < 4; ++c)
+                    x[c] = __builtin_amdgcn_raw_buffer_load_b32(bres, boff + (key + c) * (int)a.bs3 * ELT, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[4 * j + e] = __uint_as_float(x[e]);
+              }
+            }
+          }
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int ci = 32 * st + 8 * (i >> 2) + (i & 3);
             const int kj = kb + ci + 4 * hh;
             float x = s[i] * a.scale_log2;
-            if constexpr (HAS_BIAS) {
-              if (row_ok && kj < Lk) x = __builtin_fmaf(ld_bias(bias_bh + (int64_t)kj * a.bs3), kLog2e, x);
-            }
+            if constexpr (HAS_BIAS) x = __builtin_fmaf(bv[i], kLog2e, x);
             float pv = fast_exp2(x - lse2);
             if constexpr (MASK) pv = kj <= hi_row ? pv : 0.f;
             dsv[16 * st + i] = pv * (dp[i] - dsum);
@@ -850,7 +901,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
     }
   }
   {
-    auto kern = dq_kernel<BF16, D, CAUSAL, HAS_BIAS>;
+    auto kern = !HAS_BIAS ? dq_kernel<BF16, D, CAUSAL, 0>
+                          : (a.bias_vec ? dq_kernel<BF16, D, CAUSAL, 2> : dq_kernel<BF16, D, CAUSAL, 1>);
     const int grid = resident_grid((const void*)kern, NT, q_items);
     if (grid <= 0) return hipErrorInvalidConfiguration;
     timing_before(st, BF16 ? "bwd_dq_bf16" : "bwd_dq_f32");

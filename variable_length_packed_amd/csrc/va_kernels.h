@@ -99,6 +99,7 @@ struct BwdArgs {
   int32_t causal;
   int32_t bf16;
   int32_t grad_bf16;
+  int32_t bias_vec;  // keys contiguous (bs3 = 1), 4-key groups aligned: vector bias loads
 };
 
 // Optional per-kernel event timing (see va_timing_start); no-ops when off.
