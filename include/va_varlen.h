@@ -84,7 +84,8 @@ typedef enum {
 
 typedef enum {
   VA_F32 = 0,  /* IEEE float32; products and sums in float32 (no reduced-precision shortcut) */
-  VA_BF16 = 1  /* bfloat16 storage; matrix products on bf16 MFMA with float32 accumulation */
+  VA_BF16 = 1, /* bfloat16 storage; matrix products on bf16 MFMA with float32 accumulation */
+  VA_F16 = 2   /* float16 storage; matrix products on f16 MFMA with float32 accumulation */
 } va_dtype;
 
 /* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
@@ -166,10 +167,10 @@ size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
  *                      equals bias_stride of a float32 buffer shaped like the bias.
  *   workspace          device scratch of at least va_varlen_bwd_workspace_size()
  *                      bytes, 256-byte aligned
- *   grad_dtype         VA_F32, or VA_BF16 when dtype is VA_BF16
+ *   grad_dtype         VA_F32, or the input dtype when that is VA_BF16 or VA_F16
  * Deterministic: a call's results do not depend on scheduling (no atomics on
  * values; split tiles are summed in a fixed order).  Errors as for the forward, plus VA_ERR_WORKSPACE, and
- * VA_ERR_UNSUPPORTED for grad_dtype = VA_BF16 with dtype = VA_F32.
+ * VA_ERR_UNSUPPORTED for a 16-bit grad_dtype other than the input dtype.
  */
 va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const void* v,
                         const void* out, const float* lse,

@@ -7,6 +7,9 @@ relative L2 <= 5e-3 on every tensor (gradients stored float32).  On shapes other
 the five named workloads, a bf16 gradient's max-abs bound is max(2e-2, 2^-8 * max|ref|):
 the kernels round P and dS to bf16 (relative error <= 2^-9 per term) before the
 contractions, so the error of the largest gradients grows with their magnitude.
+float16 runs take the bf16 bounds scaled by 2^-3, the ratio of the two formats' unit
+roundoffs (10 against 7 fraction bits): max-abs <= 2.5e-3, relative L2 <= 6.25e-4, and
+max(2.5e-3, 2^-11 * max|ref|) for gradients off the named workloads.
 """
 
 from __future__ import annotations
@@ -17,11 +20,13 @@ import torch
 import oracle
 
 DEV = torch.device("cuda:0")
-TOL = {"f32": dict(abs=1e-5), "bf16": dict(abs=2e-2, rel=5e-3)}
+TOL = {"f32": dict(abs=1e-5), "bf16": dict(abs=2e-2, rel=5e-3), "f16": dict(abs=2.5e-3, rel=6.25e-4)}
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+_UNIT = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}  # unit roundoff of each 16-bit format
 
 
 def tdtype(w):
-    return torch.float32 if w.dtype == "f32" else torch.bfloat16
+    return _TORCH[w.dtype]
 
 
 def to_dev(x, dt):
@@ -96,7 +101,7 @@ def grad_abs_tol(dtype, ref, named_workload):
     if dtype == "f32" or named_workload:
         return None
     big = float(np.max(np.abs(ref))) if np.size(ref) else 0.0
-    return max(TOL["bf16"]["abs"], 2.0 ** -8 * big)
+    return max(TOL[dtype]["abs"], _UNIT[dtype] * big)
 
 
 def full_parity(w, backward=None, grad_dtype=torch.float32, named_workload=False):

@@ -16,7 +16,7 @@ HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.j
            if h.endswith(".h")]
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = range(5)
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 P = 0x1000  # a non-NULL pointer that validation rejects before any use
 
 
@@ -93,6 +93,7 @@ def _fwd(lib, **kw):
     (dict(d=96), UNSUPPORTED),
     (dict(d=256), UNSUPPORTED),
     (dict(dt=7), UNSUPPORTED),
+    (dict(dt=3), UNSUPPORTED),
     (dict(wsb=16), WORKSPACE),
 ])
 def test_fwd_validation(lib, kw, code):
@@ -121,6 +122,8 @@ def _bwd(lib, **kw):
     (dict(hq=3, hkv=2), INVALID),
     (dict(d=32), UNSUPPORTED),
     (dict(dt=F32, gdt=BF16), UNSUPPORTED),
+    (dict(dt=BF16, gdt=F16), UNSUPPORTED),     # 16-bit gradients only in the input's format
+    (dict(dt=F16, gdt=BF16), UNSUPPORTED),
     (dict(gdt=5), UNSUPPORTED),
     (dict(wsb=16), WORKSPACE),
     # bias gradient
@@ -160,6 +163,7 @@ def test_fwd_workspace_size(lib):
     slots = min(2 * tiles, (64 << 20) // slot)
     assert f(16, 9687, 9687, 2048, 2048, 14, 2, 64, BF16) == \
         _plan_bytes(tiles + slots, slots // 2) + _r(slots * slot)
+    assert f(16, 9687, 9687, 2048, 2048, 14, 2, 64, F16) == f(16, 9687, 9687, 2048, 2048, 14, 2, 64, BF16)
     # float32 steps are 32 keys, so the same 1024-key chunk is 32 steps
     assert f(2, 16, 16, 1024, 1024, 4, 2, 64, F32) == _plan_bytes(2, 0)
 
@@ -170,6 +174,9 @@ def test_bwd_workspace_size(lib):
     assert f(2, 16, 16, 8, 8, 4, 3, 64, BF16, F32) == 0
     assert f(2, 16, 16, 8, 8, 4, 2, 96, BF16, F32) == 0
     assert f(2, 16, 16, 8, 8, 4, 2, 64, F32, BF16) == 0
+    assert f(2, 16, 16, 8, 8, 4, 2, 64, BF16, F16) == 0
+    # float16 plans exactly as bf16 (same 64-key steps, same unit sizes)
+    assert f(2, 16, 16, 416, 8, 4, 2, 64, F16, F16) == f(2, 16, 16, 416, 8, 4, 2, 64, BF16, BF16)
     # short sequences: D = rowsum(dO * O) and the two plans (dK/dV and dQ)
     n = f(2, 16, 16, 8, 8, 4, 4, 64, BF16, F32)
     assert n == _r(4 * 16 * 4) + 2 * _plan_bytes(2, 0)  # no partial slots (per-key bias sums: none)

@@ -8,7 +8,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libva_varlen.so")
 
 VA_OK, VA_ERR_INVALID, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP = range(5)
-VA_F32, VA_BF16 = 0, 1
+VA_F32, VA_BF16, VA_F16 = 0, 1, 2
 
 # Every symbol include/va_varlen.h and include/va_pack.h declare.
 EXPORTS = ("va_varlen_fwd", "va_varlen_bwd", "va_varlen_fwd_workspace_size",

@@ -19,14 +19,14 @@ class VaError(RuntimeError):
     """The HIP runtime reported an error inside the library."""
 
 
-_DTYPES = {torch.float32: _lib.VA_F32, torch.bfloat16: _lib.VA_BF16}
+_DTYPES = {torch.float32: _lib.VA_F32, torch.bfloat16: _lib.VA_BF16, torch.float16: _lib.VA_F16}
 
 
 def _dt(t: torch.Tensor) -> int:
     try:
         return _DTYPES[t.dtype]
     except KeyError:
-        raise ValueError(f"dtype {t.dtype} not supported (float32 or bfloat16)") from None
+        raise ValueError(f"dtype {t.dtype} not supported (float32, bfloat16 or float16)") from None
 
 
 def _raise(status: int, lib) -> None:

@@ -54,7 +54,8 @@ va_status check_common(const Common& c, float scale, const void* bias, const int
   if (bstride)
     for (int i = 0; i < 4; ++i)
       if (bstride[i] < 0) return fail(VA_ERR_INVALID, "bias_stride[%d] is negative", i);
-  if (c.dtype != VA_F32 && c.dtype != VA_BF16) return fail(VA_ERR_UNSUPPORTED, "unknown dtype %d", (int)c.dtype);
+  if (c.dtype != VA_F32 && c.dtype != VA_BF16 && c.dtype != VA_F16)
+    return fail(VA_ERR_UNSUPPORTED, "unknown dtype %d", (int)c.dtype);
   if (c.d != 64 && c.d != 128) return fail(VA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", c.d);
   if ((int64_t)c.total_q * c.hq * c.d >= ((int64_t)1 << 40) ||
       (int64_t)c.total_k * c.hkv * c.d >= ((int64_t)1 << 40))
@@ -172,6 +173,9 @@ size_t bwd_workspace(int batch, int total_q, int total_k, int max_q, int max_k, 
          round_up(dbias_slot_bytes(hq) * K.slot_cap);
 }
 
+// kernel element code: 0 float32, 1 bfloat16, 2 float16
+int elem_code(va_dtype t) { return t == VA_BF16 ? 1 : (t == VA_F16 ? 2 : 0); }
+
 va_status hip_fail(hipError_t e, const char* what) {
   return fail(VA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -201,9 +205,9 @@ size_t va_varlen_fwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
                                     va_dtype dtype) {
   if (batch <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 ||
       num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0 ||
-      (head_dim != 64 && head_dim != 128) || (dtype != VA_F32 && dtype != VA_BF16))
+      (head_dim != 64 && head_dim != 128) || (dtype != VA_F32 && dtype != VA_BF16 && dtype != VA_F16))
     return 0;
-  return fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, dtype == VA_BF16);
+  return fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, dtype != VA_F32);
 }
 
 va_status va_varlen_fwd(const void* q, const void* k, const void* v,
@@ -223,7 +227,7 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
   if (s != VA_OK) return s;
   if (((uintptr_t)workspace) % kAlign != 0)
     return fail(VA_ERR_INVALID, "workspace must be 256-byte aligned");
-  const bool bf16 = dtype == VA_BF16;
+  const bool bf16 = dtype != VA_F32;  // a 16-bit kind (bf16 or f16)
   const size_t need = fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16);
   if (workspace_bytes < need)
     return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
@@ -248,7 +252,7 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
   a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = num_heads_q / num_heads_kv; a.d = head_dim;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.causal = causal;
-  a.bf16 = bf16;
+  a.bf16 = elem_code(dtype);
   const PlanLayout L = fwd_plan(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16);
   char* w = (char*)workspace;
   const size_t used = carve_plan(w, L, a.plan);
@@ -273,11 +277,11 @@ size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
   if (batch <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 ||
       num_heads_q <= 0 || num_heads_kv <= 0 ||
       num_heads_q % num_heads_kv != 0 || (head_dim != 64 && head_dim != 128) ||
-      (dtype != VA_F32 && dtype != VA_BF16) || (grad_dtype != VA_F32 && grad_dtype != VA_BF16) ||
-      (dtype == VA_F32 && grad_dtype == VA_BF16))
+      (dtype != VA_F32 && dtype != VA_BF16 && dtype != VA_F16) ||
+      (grad_dtype != VA_F32 && grad_dtype != dtype))
     return 0;
   return bwd_workspace(batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q,
-                       num_heads_kv, head_dim, dtype == VA_BF16);
+                       num_heads_kv, head_dim, dtype != VA_F32);
 }
 
 va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const void* v,
@@ -297,10 +301,10 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
            max_seqlen_k, causal, dtype};
   va_status s = check_common(c, softmax_scale, bias, bias_stride);
   if (s != VA_OK) return s;
-  if (grad_dtype != VA_F32 && grad_dtype != VA_BF16)
+  if (grad_dtype != VA_F32 && grad_dtype != VA_BF16 && grad_dtype != VA_F16)
     return fail(VA_ERR_UNSUPPORTED, "unknown grad_dtype %d", (int)grad_dtype);
-  if (dtype == VA_F32 && grad_dtype == VA_BF16)
-    return fail(VA_ERR_UNSUPPORTED, "bf16 gradients of float32 inputs are not supported");
+  if (grad_dtype != VA_F32 && grad_dtype != dtype)
+    return fail(VA_ERR_UNSUPPORTED, "gradients are float32 or the input dtype");
   int dbias_mode = 0;
   if ((dbias == nullptr) != (dbias_stride == nullptr))
     return fail(VA_ERR_INVALID, "dbias and dbias_stride must both be NULL or both non-NULL");
@@ -326,7 +330,7 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
   }
   if (((uintptr_t)workspace) % kAlign != 0)
     return fail(VA_ERR_INVALID, "workspace must be 256-byte aligned");
-  const bool bf16 = dtype == VA_BF16;
+  const bool bf16 = dtype != VA_F32;  // a 16-bit kind (bf16 or f16)
   const int n_rep = num_heads_q / num_heads_kv;
   const size_t need = bwd_workspace(batch, total_q, total_k, max_seqlen_q, max_seqlen_k,
                                     num_heads_q, num_heads_kv, head_dim, bf16);
@@ -352,8 +356,8 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.causal = causal;
-  a.bf16 = bf16;
-  a.grad_bf16 = grad_dtype == VA_BF16;
+  a.bf16 = elem_code(dtype);
+  a.grad_bf16 = grad_dtype == VA_F32 ? 0 : elem_code(grad_dtype);
 
   const PlanLayout K = dkdv_plan(batch, total_k, max_seqlen_q, num_heads_kv, n_rep, head_dim);
   const PlanLayout Q = dq_plan(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16);

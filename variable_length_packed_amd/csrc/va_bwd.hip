@@ -46,8 +46,8 @@ constexpr int BNK = 128;     // keys per dK/dV workgroup
 constexpr int kDbiasMaxHeads = 32;  // query heads per KV head with a per-key bias gradient
 constexpr int BMQ_DQ = 128;  // query rows per dQ workgroup
 
-template <bool BF16>
-using elem_t = typename std::conditional<BF16, uint16_t, float>::type;
+template <int H16>
+using elem_t = typename std::conditional<(H16 != 0), uint16_t, float>::type;
 
 // Row r's position inside a transposed bf16 LDS row (bits 2 and 3 swapped so
 // the 8 k-slots of a lane half are contiguous), and the XOR swizzle of the
@@ -63,9 +63,9 @@ __device__ __forceinline__ int tswz(int d) { return ((d >> 3) & (ROWS / 8 - 1)) 
 // read as zero) into LDS as rows ([ROWS][D + pad]) and, for bf16, transposed
 // ([D][ROWS + pad], swizzled).  Each thread owns pairs of consecutive rows of
 // one 16-byte chunk, so the transposed store can pair them.
-template <bool BF16, int ROWS, int D, bool TRANS>
+template <int H16, int ROWS, int D, bool TRANS>
 struct Stager {
-  using T = elem_t<BF16>;
+  using T = elem_t<H16>;
   static constexpr int EPV = 16 / sizeof(T);
   static constexpr int CH = D / EPV;                     // 16-byte chunks per row
   static constexpr int PAIRS = (ROWS / 2) * CH;          // tasks
@@ -94,7 +94,7 @@ struct Stager {
       const int c = u % CH, p = u / CH;
       *(u32x4_t*)(dn + (2 * p) * NP + c * EPV) = r[2 * i];
       *(u32x4_t*)(dn + (2 * p + 1) * NP + c * EPV) = r[2 * i + 1];
-      if constexpr (BF16 && TRANS) {
+      if constexpr (H16 && TRANS) {
         const int pos = tpos(2 * p) ^ tswz<ROWS>(c * 8);  // rows c*8 .. c*8+7 share the swizzle
         const u32x4_t a = r[2 * i], b = r[2 * i + 1];
 #pragma unroll
@@ -118,13 +118,13 @@ __device__ __forceinline__ u32x4_t tfrag(const uint16_t* t, int d, int kc, int h
 // Register fragment of this lane's row for the "other" operand of a 32x32
 // MFMA contracting over head_dim: bf16 -> D/16 vectors of 8; f32 -> D/2
 // scalars with k-slot (group G, step j) of lane half hh = dim 8G+4hh+j.
-template <bool BF16, int D>
+template <int H16, int D>
 struct RowFrag {
-  static constexpr int N = BF16 ? D / 16 : D / 2;
-  u32x4_t b[BF16 ? N : 1];
-  float f[BF16 ? 1 : N];
+  static constexpr int N = H16 ? D / 16 : D / 2;
+  u32x4_t b[H16 ? N : 1];
+  float f[H16 ? 1 : N];
   __device__ __forceinline__ void load(rsrc_t res, int row_bytes, int row, int hh) {
-    if constexpr (BF16) {
+    if constexpr (H16) {
 #pragma unroll
       for (int ks = 0; ks < N; ++ks) b[ks] = buf_load16(res, row * row_bytes + (16 * ks + 8 * hh) * 2);
     } else {
@@ -140,14 +140,14 @@ struct RowFrag {
 
 // acc += (32 rows of an LDS row-major tile, from `lrow` = this lane's row) x
 // frag^T, contracting over head_dim.  Result: C[lds row][fragment row].
-template <bool BF16, int D>
-__device__ __forceinline__ f32x16_t mm_rows(const elem_t<BF16>* lrow, const RowFrag<BF16, D>& fr,
+template <int H16, int D>
+__device__ __forceinline__ f32x16_t mm_rows(const elem_t<H16>* lrow, const RowFrag<H16, D>& fr,
                                             f32x16_t acc, int hh) {
-  if constexpr (BF16) {
+  if constexpr (H16) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const u32x4_t a = *(const u32x4_t*)(lrow + 16 * ks + 8 * hh);
-      acc = mfma32_bf16(a, fr.b[ks], acc);
+      acc = mfma16<H16>(a, fr.b[ks], acc);
     }
   } else {
 #pragma unroll
@@ -161,15 +161,16 @@ __device__ __forceinline__ f32x16_t mm_rows(const elem_t<BF16>* lrow, const RowF
 }
 
 
-// bf16 operand of 8 values and, optionally, the bf16 residual of the same 8.
+// 16-bit operand of 8 values and, optionally, the 16-bit residual of the same 8.
+template <int H16>
 __device__ __forceinline__ void pack8(const float* v, u32x4_t& hi, u32x4_t* lo) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    hi[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+    hi[e] = pack16<H16>(v[2 * e], v[2 * e + 1]);
     if (lo) {
-      const float r0 = v[2 * e] - __uint_as_float(hi[e] << 16);
-      const float r1 = v[2 * e + 1] - __uint_as_float(hi[e] & 0xFFFF0000u);
-      (*lo)[e] = pack_bf16x2(r0, r1);
+      const float r0 = v[2 * e] - lo16<H16>(hi[e]);
+      const float r1 = v[2 * e + 1] - hi16<H16>(hi[e]);
+      (*lo)[e] = pack16<H16>(r0, r1);
     }
   }
 }
@@ -177,14 +178,14 @@ __device__ __forceinline__ void pack8(const float* v, u32x4_t& hi, u32x4_t* lo) 
 // ---------------------------------------------------------------- preprocess
 // One launch: workgroups 0 and 1 build the dK/dV and dQ work plans while the
 // others compute D = rowsum(dO * O) for every (query row, head).
-template <bool BF16, int D>
+template <int H16, int D>
 __global__ __launch_bounds__(plan::PT) void plan_dsum_kernel(BwdArgs a, PlanSet ps) {
   __shared__ plan::PlanShared sh;
   if (blockIdx.x < 2) {
     plan::plan_body(ps.p[blockIdx.x], sh);
     return;
   }
-  using T = elem_t<BF16>;
+  using T = elem_t<H16>;
   constexpr int EPV = 16 / sizeof(T);
   constexpr int TPR = D / EPV;  // threads per (token, head) row
   const int64_t rows = (int64_t)a.total_q * a.hq;
@@ -194,12 +195,12 @@ __global__ __launch_bounds__(plan::PT) void plan_dsum_kernel(BwdArgs a, PlanSet 
   if (row < rows) {
     const T* o = (const T*)a.out + row * D + c * EPV;
     const T* g = (const T*)a.dout + row * D + c * EPV;
-    if constexpr (BF16) {
+    if constexpr (H16) {
       const u32x4_t x = *(const u32x4_t*)o, y = *(const u32x4_t*)g;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        s = __builtin_fmaf(bf16_to_f32(x[e] & 0xFFFF), bf16_to_f32(y[e] & 0xFFFF), s);
-        s = __builtin_fmaf(bf16_to_f32(x[e] >> 16), bf16_to_f32(y[e] >> 16), s);
+        s = __builtin_fmaf(lo16<H16>(x[e]), lo16<H16>(y[e]), s);
+        s = __builtin_fmaf(hi16<H16>(x[e]), hi16<H16>(y[e]), s);
       }
     } else {
       // float vectors are loaded as such (no bit casts of vector elements)
@@ -219,25 +220,25 @@ __global__ __launch_bounds__(plan::PT) void plan_dsum_kernel(BwdArgs a, PlanSet 
 // ---------------------------------------------------------------- dK / dV
 constexpr int BMQ = 32;  // queries per dK/dV block
 
-template <bool BF16, int D>
+template <int H16, int D>
 struct DkdvSmem {
-  using T = elem_t<BF16>;
-  using St = Stager<BF16, BMQ, D, true>;
+  using T = elem_t<H16>;
+  using St = Stager<H16, BMQ, D, true>;
   T qn[2][BMQ * St::NP];
   T dn[2][BMQ * St::NP];
-  T qt[2][BF16 ? D * St::TP : 1];
-  T dt[2][BF16 ? D * St::TP : 1];
+  T qt[2][H16 ? D * St::TP : 1];
+  T dt[2][H16 ? D * St::TP : 1];
   float lse2[2][BMQ];
   float dsum[2][BMQ];
 };
 
-template <bool BF16, int D>
+template <int H16, int D>
 constexpr int dkdv_min_blocks() { return D == 64 ? 2 : 1; }
 
-template <bool BF16, int D, bool CAUSAL, bool HAS_BIAS>
-__global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(BwdArgs a) {
-  using T = elem_t<BF16>;
-  using SM = DkdvSmem<BF16, D>;
+template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
+__global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(BwdArgs a) {
+  using T = elem_t<H16>;
+  using SM = DkdvSmem<H16, D>;
   using St = typename SM::St;
   constexpr int DT = D / 32;
   constexpr int ELT = (int)sizeof(T);
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
 
     const size_t koff = (size_t)k0 * kstride + (size_t)g * D;
     const int64_t kbytes = Lk > 0 ? (int64_t)(Lk - 1) * krow_bytes + D * ELT : 0;
-    RowFrag<BF16, D> kf, vf;
+    RowFrag<H16, D> kf, vf;
     kf.load(make_rsrc((const T*)a.k + koff, kbytes), krow_bytes, kj, hh);
     vf.load(make_rsrc((const T*)a.v + koff, kbytes), krow_bytes, kj, hh);
     f32x16_t dk[DT], dv[DT];
@@ -350,8 +351,8 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
       const bool active = wave_keys && (!CAUSAL || qb + BMQ - 1 + off >= wk0);
       if (active) {
         // S = Q K^T and dP = dO V^T: C[query][key], lane = key
-        f32x16_t s = mm_rows<BF16, D>(&sm.qn[buf][r32 * St::NP], kf, (f32x16_t){}, hh);
-        f32x16_t dp = mm_rows<BF16, D>(&sm.dn[buf][r32 * St::NP], vf, (f32x16_t){}, hh);
+        f32x16_t s = mm_rows<H16, D>(&sm.qn[buf][r32 * St::NP], kf, (f32x16_t){}, hh);
+        f32x16_t dp = mm_rows<H16, D>(&sm.dn[buf][r32 * St::NP], vf, (f32x16_t){}, hh);
         // the bias of head h through a resource that ends after the last element a valid
         // (row, key) reads (rounded up to a dword); rows past the sequence read 0 or are
         // zeroed below, so garbage never meets a row whose P must be 0
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
           if constexpr (HAS_BIAS) {
             const int off = brow + cl * (int)a.bs2 * ELT;
             float bf;
-            if constexpr (BF16) bf = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(bres, off, 0, 0) << 16);
+            if constexpr (H16) bf = lo16<H16>(__builtin_amdgcn_raw_buffer_load_b16(bres, off, 0, 0));
             else bf = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bres, off, 0, 0));
             x = __builtin_fmaf(qb + ql < Lq ? bf : 0.f, kLog2e, x);
           }
@@ -402,20 +403,20 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
           }
         }
         // dV += P^T dO, dK += dS^T Q: C[key][d], lane = d
-        if constexpr (BF16) {
+        if constexpr (H16) {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             u32x4_t pa, da, da_lo;
-            pack8(&p[8 * c], pa, nullptr);
-            pack8(&ds[8 * c], da, &da_lo);
+            pack8<H16>(&p[8 * c], pa, nullptr);
+            pack8<H16>(&ds[8 * c], da, &da_lo);
 #pragma unroll
             for (int dt_ = 0; dt_ < DT; ++dt_) {
               const int d = 32 * dt_ + r32;
               const u32x4_t ob = tfrag<BMQ, St::TP>(sm.dt[buf], d, c, hh);
               const u32x4_t qb4 = tfrag<BMQ, St::TP>(sm.qt[buf], d, c, hh);
-              dv[dt_] = mfma32_bf16(pa, ob, dv[dt_]);
-              dk[dt_] = mfma32_bf16(da, qb4, dk[dt_]);
-              dk[dt_] = mfma32_bf16(da_lo, qb4, dk[dt_]);
+              dv[dt_] = mfma16<H16>(pa, ob, dv[dt_]);
+              dk[dt_] = mfma16<H16>(da, qb4, dk[dt_]);
+              dk[dt_] = mfma16<H16>(da_lo, qb4, dk[dt_]);
             }
           }
         } else {
@@ -497,8 +498,8 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<BF16, D>())) void dkdv_kernel(
           const int off = lane_off + (8 * (i >> 2) + (i & 3)) * krow + 32 * dt_ * gelt;
           const float kv = dk[dt_][i] * a.scale, vv = dv[dt_][i];
           if (a.grad_bf16) {
-            buf_store2((uint16_t)(pack_bf16x2(kv, 0.f) & 0xFFFF), rk, off);
-            buf_store2((uint16_t)(pack_bf16x2(vv, 0.f) & 0xFFFF), rv, off);
+            buf_store2((uint16_t)(pack16<H16>(kv, 0.f) & 0xFFFF), rk, off);
+            buf_store2((uint16_t)(pack16<H16>(vv, 0.f) & 0xFFFF), rv, off);
           } else {
             buf_store4(__float_as_uint(kv), rk, off);
             buf_store4(__float_as_uint(vv), rv, off);
@@ -558,8 +559,8 @@ __global__ __launch_bounds__(NT) void dkdv_merge_kernel(BwdArgs a) {
         const size_t o = ((size_t)(k0 + key0 + j) * a.hkv + g) * D + d;
         const float kv = sk[j] * a.scale, vv = sv[j];
         if (a.grad_bf16) {
-          ((uint16_t*)a.dk)[o] = (uint16_t)(pack_bf16x2(kv, 0.f) & 0xFFFF);
-          ((uint16_t*)a.dv)[o] = (uint16_t)(pack_bf16x2(vv, 0.f) & 0xFFFF);
+          ((uint16_t*)a.dk)[o] = (uint16_t)(pack16_rt(kv, 0.f, a.grad_bf16) & 0xFFFF);
+          ((uint16_t*)a.dv)[o] = (uint16_t)(pack16_rt(vv, 0.f, a.grad_bf16) & 0xFFFF);
         } else {
           ((float*)a.dk)[o] = kv;
           ((float*)a.dv)[o] = vv;
@@ -580,23 +581,23 @@ __global__ __launch_bounds__(NT) void dkdv_merge_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dQ
-template <bool BF16, int D>
+template <int H16, int D>
 struct DqSmem {
-  using T = elem_t<BF16>;
-  static constexpr int BN = (BF16 && D == 64) ? 64 : 32;
-  using St = Stager<BF16, BN, D, true>;
-  using Sv = Stager<BF16, BN, D, false>;
+  using T = elem_t<H16>;
+  static constexpr int BN = (H16 && D == 64) ? 64 : 32;
+  using St = Stager<H16, BN, D, true>;
+  using Sv = Stager<H16, BN, D, false>;
   T kn[2][BN * St::NP];
-  T kt[2][BF16 ? D * St::TP : 1];
+  T kt[2][H16 ? D * St::TP : 1];
   T vn[2][BN * St::NP];
 };
 
 // BIAS: 0 none; 1 any layout (one element per load); 2 contiguous keys (four per load)
-template <bool BF16, int D, bool CAUSAL, int BIAS>
+template <int H16, int D, bool CAUSAL, int BIAS>
 __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   constexpr bool HAS_BIAS = BIAS != 0;
-  using T = elem_t<BF16>;
-  using SM = DqSmem<BF16, D>;
+  using T = elem_t<H16>;
+  using SM = DqSmem<H16, D>;
   constexpr int BN = SM::BN;
   constexpr int NS = BN / 32;
   constexpr int DT = D / 32;
@@ -649,7 +650,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
 
     const size_t qoff = (size_t)q0 * qstride + (size_t)h * D;
     const int64_t qbytes = Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0;
-    RowFrag<BF16, D> qf, of;
+    RowFrag<H16, D> qf, of;
     qf.load(make_rsrc((const T*)a.q + qoff, qbytes), qrow_bytes, rq, hh);
     of.load(make_rsrc((const T*)a.dout + qoff, qbytes), qrow_bytes, rq, hh);
     float lse2 = 0.f, dsum = 0.f;
@@ -693,8 +694,8 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
           // S^T = K Q^T, dP^T = V dO^T: C[key][query], lane = query
-          const f32x16_t s = mm_rows<BF16, D>(&sm.kn[buf][(32 * st + r32) * St::NP], qf, (f32x16_t){}, hh);
-          const f32x16_t dp = mm_rows<BF16, D>(&sm.vn[buf][(32 * st + r32) * St::NP], of, (f32x16_t){}, hh);
+          const f32x16_t s = mm_rows<H16, D>(&sm.kn[buf][(32 * st + r32) * St::NP], qf, (f32x16_t){}, hh);
+          const f32x16_t dp = mm_rows<H16, D>(&sm.vn[buf][(32 * st + r32) * St::NP], of, (f32x16_t){}, hh);
           float bv[HAS_BIAS ? 16 : 1];
           if constexpr (HAS_BIAS) {
             // registers 4j .. 4j+3 are 4 consecutive keys: one load each when keys are
@@ -702,7 +703,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int key = kb + 32 * st + 8 * j;
-              if constexpr (BF16) {
+              if constexpr (H16) {
                 u32x2_t x;
                 if constexpr (BIAS == 2) {
                   x = buf_load8(bres, boff + key * ELT);
@@ -713,10 +714,10 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
                     e[c] = __builtin_amdgcn_raw_buffer_load_b16(bres, boff + (key + c) * (int)a.bs3 * ELT, 0, 0);
                   x = (u32x2_t){e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
                 }
-                bv[4 * j + 0] = __uint_as_float(x[0] << 16);
-                bv[4 * j + 1] = __uint_as_float(x[0] & 0xFFFF0000u);
-                bv[4 * j + 2] = __uint_as_float(x[1] << 16);
-                bv[4 * j + 3] = __uint_as_float(x[1] & 0xFFFF0000u);
+                bv[4 * j + 0] = lo16<H16>(x[0]);
+                bv[4 * j + 1] = hi16<H16>(x[0]);
+                bv[4 * j + 2] = lo16<H16>(x[1]);
+                bv[4 * j + 3] = hi16<H16>(x[1]);
               } else {
                 u32x4_t x;
                 if constexpr (BIAS == 2) {
@@ -743,14 +744,14 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
           }
         }
         // dQ^T += K^T dS^T
-        if constexpr (BF16) {
+        if constexpr (H16) {
 #pragma unroll
           for (int kc = 0; kc < 2 * NS; ++kc) {
             u32x4_t pb;
-            pack8(&dsv[8 * kc], pb, nullptr);
+            pack8<H16>(&dsv[8 * kc], pb, nullptr);
 #pragma unroll
             for (int dt_ = 0; dt_ < DT; ++dt_)
-              acc[dt_] = mfma32_bf16(tfrag<BN, St::TP>(sm.kt[buf], 32 * dt_ + r32, kc, hh), pb, acc[dt_]);
+              acc[dt_] = mfma16<H16>(tfrag<BN, St::TP>(sm.kt[buf], 32 * dt_ + r32, kc, hh), pb, acc[dt_]);
           }
         } else {
 #pragma unroll
@@ -803,7 +804,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
           const float o0 = acc[dt_][4 * a4 + 0] * a.scale, o1 = acc[dt_][4 * a4 + 1] * a.scale;
           const float o2 = acc[dt_][4 * a4 + 2] * a.scale, o3 = acc[dt_][4 * a4 + 3] * a.scale;
           if (a.grad_bf16) {
-            buf_store8((u32x2_t){pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)}, dqres, rq * dq_row_bytes + d0 * 2);
+            buf_store8((u32x2_t){pack16<H16>(o0, o1), pack16<H16>(o2, o3)}, dqres, rq * dq_row_bytes + d0 * 2);
           } else {
             buf_store16((u32x4_t){__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2),
                                   __float_as_uint(o3)}, dqres, rq * dq_row_bytes + d0 * 4);
@@ -861,31 +862,32 @@ __global__ __launch_bounds__(NT) void dq_merge_kernel(BwdArgs a) {
     for (int e = 0; e < SEG / 4; ++e) {
       const f32x4_t x = acc[e] * a.scale;
       if (a.grad_bf16)
-        ((u32x2_t*)((uint16_t*)a.dq + o))[e] = (u32x2_t){pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        ((u32x2_t*)((uint16_t*)a.dq + o))[e] = (u32x2_t){pack16_rt(x[0], x[1], a.grad_bf16),
+                                                        pack16_rt(x[2], x[3], a.grad_bf16)};
       else
         ((f32x4_t*)((float*)a.dq + o))[e] = x;
     }
   }
 }
 
-template <bool BF16, int D, bool CAUSAL, bool HAS_BIAS>
+template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
 hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, int64_t k_items,
                         hipStream_t st) {
   {
-    constexpr int EPV = BF16 ? 8 : 4;
+    constexpr int EPV = H16 ? 8 : 4;
     const int64_t threads = (int64_t)a.total_q * a.hq * (D / EPV);
     const int64_t grid = 2 + (threads + plan::PT - 1) / plan::PT;
     timing_before(st, "bwd_plan_dsum");
-    hipLaunchKernelGGL((plan_dsum_kernel<BF16, D>), dim3((unsigned)grid), dim3(plan::PT), 0, st, a, ps);
+    hipLaunchKernelGGL((plan_dsum_kernel<H16, D>), dim3((unsigned)grid), dim3(plan::PT), 0, st, a, ps);
     timing_after(st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    auto kern = dkdv_kernel<BF16, D, CAUSAL, HAS_BIAS>;
+    auto kern = dkdv_kernel<H16, D, CAUSAL, HAS_BIAS>;
     const int grid = resident_grid((const void*)kern, NT, k_items);
     if (grid <= 0) return hipErrorInvalidConfiguration;
-    timing_before(st, BF16 ? "bwd_dkdv_bf16" : "bwd_dkdv_f32");
+    timing_before(st, H16 == 2 ? "bwd_dkdv_f16" : H16 ? "bwd_dkdv_bf16" : "bwd_dkdv_f32");
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
     timing_after(st);
     e = hipGetLastError();
@@ -901,11 +903,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
     }
   }
   {
-    auto kern = !HAS_BIAS ? dq_kernel<BF16, D, CAUSAL, 0>
-                          : (a.bias_vec ? dq_kernel<BF16, D, CAUSAL, 2> : dq_kernel<BF16, D, CAUSAL, 1>);
+    auto kern = !HAS_BIAS ? dq_kernel<H16, D, CAUSAL, 0>
+                          : (a.bias_vec ? dq_kernel<H16, D, CAUSAL, 2> : dq_kernel<H16, D, CAUSAL, 1>);
     const int grid = resident_grid((const void*)kern, NT, q_items);
     if (grid <= 0) return hipErrorInvalidConfiguration;
-    timing_before(st, BF16 ? "bwd_dq_bf16" : "bwd_dq_f32");
+    timing_before(st, H16 == 2 ? "bwd_dq_f16" : H16 ? "bwd_dq_bf16" : "bwd_dq_f32");
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
     timing_after(st);
     e = hipGetLastError();
@@ -921,15 +923,15 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
   return hipGetLastError();
 }
 
-template <bool BF16, int D>
+template <int H16, int D>
 hipError_t launch_bwd_d(const BwdArgs& a, const PlanSet& ps, int64_t q_items, int64_t k_items,
                         hipStream_t st) {
   const bool hb = a.bias != nullptr;
   if (a.causal)
-    return hb ? launch_bwd_t<BF16, D, true, true>(a, ps, q_items, k_items, st)
-              : launch_bwd_t<BF16, D, true, false>(a, ps, q_items, k_items, st);
-  return hb ? launch_bwd_t<BF16, D, false, true>(a, ps, q_items, k_items, st)
-            : launch_bwd_t<BF16, D, false, false>(a, ps, q_items, k_items, st);
+    return hb ? launch_bwd_t<H16, D, true, true>(a, ps, q_items, k_items, st)
+              : launch_bwd_t<H16, D, true, false>(a, ps, q_items, k_items, st);
+  return hb ? launch_bwd_t<H16, D, false, true>(a, ps, q_items, k_items, st)
+            : launch_bwd_t<H16, D, false, false>(a, ps, q_items, k_items, st);
 }
 
 }  // namespace
@@ -944,11 +946,14 @@ int bwd_dq_block_n(bool bf16, int d) {
 
 hipError_t launch_bwd(const BwdArgs& a, const PlanSet& ps, int64_t q_items, int64_t k_items,
                       hipStream_t st) {
+  if (a.bf16 == 2)
+    return a.d == 64 ? launch_bwd_d<2, 64>(a, ps, q_items, k_items, st)
+                     : launch_bwd_d<2, 128>(a, ps, q_items, k_items, st);
   if (a.bf16)
-    return a.d == 64 ? launch_bwd_d<true, 64>(a, ps, q_items, k_items, st)
-                     : launch_bwd_d<true, 128>(a, ps, q_items, k_items, st);
-  return a.d == 64 ? launch_bwd_d<false, 64>(a, ps, q_items, k_items, st)
-                   : launch_bwd_d<false, 128>(a, ps, q_items, k_items, st);
+    return a.d == 64 ? launch_bwd_d<1, 64>(a, ps, q_items, k_items, st)
+                     : launch_bwd_d<1, 128>(a, ps, q_items, k_items, st);
+  return a.d == 64 ? launch_bwd_d<0, 64>(a, ps, q_items, k_items, st)
+                   : launch_bwd_d<0, 128>(a, ps, q_items, k_items, st);
 }
 
 }  // namespace va

@@ -49,6 +49,60 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __builtin_bit_cast(float, (uint32_t)x << 16);
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit element kinds.  Kernels take H16 = 0 (float32), 1 (bfloat16) or
+// 2 (float16); every 16-bit-path helper below picks the instruction of its
+// kind.  Both kinds share one storage layout (16 bits per element) and one
+// MFMA operand layout (v_mfma_f32_32x32x16_bf16 / _f16).
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+template <int H16>
+__device__ __forceinline__ f32x16_t mfma16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  if constexpr (H16 == 2)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return mfma32_bf16(a, b, c);
+}
+
+// Two floats to two 16-bit values (round to nearest even), low half = lo.
+template <int H16>
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+  if constexpr (H16 == 2)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+  else
+    return pack_bf16x2(lo, hi);
+}
+
+// acc + lo + hi of a packed pair.
+template <int H16>
+__device__ __forceinline__ float sum16(uint32_t pair, float acc) {
+  if constexpr (H16 == 2)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pair), __builtin_bit_cast(f16x2_t, 0x3C003C00u),
+                                  acc, false);
+  else
+    return add_bf16x2(pair, acc);
+}
+
+// The value in the low / high 16 bits of a word.
+template <int H16>
+__device__ __forceinline__ float lo16(uint32_t x) {
+  if constexpr (H16 == 2) return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xFFFFu));
+  else return __uint_as_float(x << 16);
+}
+template <int H16>
+__device__ __forceinline__ float hi16(uint32_t x) {
+  if constexpr (H16 == 2) return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16));
+  else return __uint_as_float(x & 0xFFFF0000u);
+}
+
+// The same at run time, for kernels that serve both kinds (merges).
+__device__ __forceinline__ uint32_t pack16_rt(float lo, float hi, int h16) {
+  return h16 == 2 ? pack16<2>(lo, hi) : pack16<1>(lo, hi);
+}
+
 // Raw buffer resources: loads past `bytes` (or at a negative offset, seen as
 // a huge unsigned one) return zero and stores there are dropped, so ragged
 // tiles need no branches.  Word 3 = 0x00020000: 32-bit data format, the

@@ -28,15 +28,15 @@ namespace {
 constexpr int NT = 256;  // threads per workgroup
 
 // keys per block: 64 for bf16 (two 32-key score tiles), 32 for f32 (LDS size)
-template <bool BF16, int D>
+template <int H16, int D>
 struct BlockN {
-  static constexpr int value = BF16 ? 64 : 32;
+  static constexpr int value = H16 ? 64 : 32;
 };
 
-template <bool BF16, int D>
+template <int H16, int D>
 struct FwdSmem {
-  static constexpr int BN = BlockN<BF16, D>::value;
-  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  static constexpr int BN = BlockN<H16, D>::value;
+  using T = typename std::conditional<(H16 != 0), uint16_t, float>::type;
   // K and V blocks: [BN][D] row-major as in memory, row pitch padded by 16
   // bytes.  bf16 V^T fragments come from transposing LDS reads.
   static constexpr int KP = D + 16 / (int)sizeof(T);
@@ -45,10 +45,10 @@ struct FwdSmem {
   T v[2][BN * VP];
 };
 
-template <bool BF16, int D>
+template <int H16, int D>
 struct Loader {
-  static constexpr int BN = BlockN<BF16, D>::value;
-  using T = typename std::conditional<BF16, uint16_t, float>::type;
+  static constexpr int BN = BlockN<H16, D>::value;
+  using T = typename std::conditional<(H16 != 0), uint16_t, float>::type;
   static constexpr int EPV = 16 / sizeof(T);           // elements per 16-byte vector
   static constexpr int KVEC = BN * D / EPV;            // 16-byte vectors per K block
   static constexpr int KPT = (KVEC + NT - 1) / NT;     // per thread
@@ -75,8 +75,8 @@ struct Loader {
     }
   }
 
-  __device__ __forceinline__ void store_k(FwdSmem<BF16, D>& sm, int buf) {
-    using S = FwdSmem<BF16, D>;
+  __device__ __forceinline__ void store_k(FwdSmem<H16, D>& sm, int buf) {
+    using S = FwdSmem<H16, D>;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int u = threadIdx.x + i * NT;
@@ -84,8 +84,8 @@ struct Loader {
       *(u32x4_t*)(&sm.k[buf][key * S::KP + c * EPV]) = kr[i];
     }
   }
-  __device__ __forceinline__ void store_v(FwdSmem<BF16, D>& sm, int buf) {
-    using S = FwdSmem<BF16, D>;
+  __device__ __forceinline__ void store_v(FwdSmem<H16, D>& sm, int buf) {
+    using S = FwdSmem<H16, D>;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int u = threadIdx.x + i * NT;
@@ -99,28 +99,28 @@ struct Loader {
 // K and V^T fragment feeds two MFMAs) but need the whole register file, i.e.
 // one wave per SIMD; measured on gfx950 that loses more to exposed latency
 // than it saves, so one tile per wave (two waves per SIMD) is used.
-template <bool BF16, int D>
+template <int H16, int D>
 struct WaveTiles {
   static constexpr int value = 1;
 };
-template <bool BF16, int D>
-constexpr int block_m() { return 4 * 32 * WaveTiles<BF16, D>::value; }
+template <int H16, int D>
+constexpr int block_m() { return 4 * 32 * WaveTiles<H16, D>::value; }
 
 // d = 64: two workgroups per CU (256 registers per lane); d = 128: one, with
 // the accumulators free to use the whole 512-entry register file.
-template <bool BF16, int D>
+template <int H16, int D>
 constexpr int min_blocks() { return D == 64 ? 2 : 1; }
 
-template <bool BF16, int D, bool CAUSAL, bool HAS_BIAS>
-__global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArgs a) {
-  using T = typename std::conditional<BF16, uint16_t, float>::type;
-  using S = FwdSmem<BF16, D>;
-  constexpr int BN = BlockN<BF16, D>::value;
+template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
+__global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs a) {
+  using T = typename std::conditional<(H16 != 0), uint16_t, float>::type;
+  using S = FwdSmem<H16, D>;
+  constexpr int BN = BlockN<H16, D>::value;
   constexpr int NS = BN / 32;                // 32-key score tiles per block
   constexpr int DT = D / 32;                 // 32-wide output tiles along head_dim
-  constexpr int QF = BF16 ? D / 16 : D / 2;  // Q fragments (MFMA k-steps) per lane
-  constexpr int QT = WaveTiles<BF16, D>::value;  // 32-row query tiles per wave
-  constexpr int BM = block_m<BF16, D>();
+  constexpr int QF = H16 ? D / 16 : D / 2;  // Q fragments (MFMA k-steps) per lane
+  constexpr int QT = WaveTiles<H16, D>::value;  // 32-row query tiles per wave
+  constexpr int BM = block_m<H16, D>();
   constexpr int WR = 32 * QT;                 // rows per wave
 
   __shared__ S sm;
@@ -195,11 +195,11 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     const rsrc_t vres = make_rsrc(vg + koff, kbytes);
 
     // ---- Q fragments (B operand of S^T = K Q^T); rows < 0 read as zero
-    u32x4_t qf4[QT][BF16 ? QF : 1];
-    float qff[QT][BF16 ? 1 : QF];
+    u32x4_t qf4[QT][H16 ? QF : 1];
+    float qff[QT][H16 ? 1 : QF];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      if constexpr (BF16) {
+      if constexpr (H16) {
 #pragma unroll
         for (int ks = 0; ks < QF; ++ks)
           qf4[qt][ks] = buf_load16(qres, rq[qt] * qrow_bytes + (16 * ks + 8 * hh) * 2);
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
       for (int qt = 0; qt < QT; ++qt) boff[qt] = (int)(((int64_t)rq[qt] * a.bs2 + 4 * hh * a.bs3) * ELT);
     }
 
-    Loader<BF16, D> ld;
+    Loader<H16, D> ld;
 
     // Visible keys of a row: kj in [0, hi_row]; kj is kb + c_i + 4*hh with
     // c_i = 32*st + 8*(i/4) + i%4 a compile-time constant, so the mask of a
@@ -249,9 +249,9 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     // ---- S^T = K Q^T of the block in K buffer `kbuf`: each K fragment read
     // from LDS feeds the QT query tiles
     // bf16: the K fragments of a block, read from LDS ahead of their MFMAs
-    constexpr int KFN = BF16 ? QF * NS : 1;
+    constexpr int KFN = H16 ? QF * NS : 1;
     auto read_k = [&](int kbuf, u32x4_t (&kfr)[KFN]) __attribute__((always_inline)) {
-      if constexpr (BF16) {
+      if constexpr (H16) {
 #pragma unroll
         for (int ks = 0; ks < QF; ++ks)
 #pragma unroll
@@ -269,21 +269,21 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
 #pragma unroll
         for (int st = 0; st < NS; ++st)
 #pragma unroll
-          for (int qt = 0; qt < QT; ++qt) s[qt][st] = mfma32_bf16(kfr[ks * NS + st], qf4[qt][ks], s[qt][st]);
+          for (int qt = 0; qt < QT; ++qt) s[qt][st] = mfma16<H16>(kfr[ks * NS + st], qf4[qt][ks], s[qt][st]);
     };
     auto qk = [&](int kbuf, f32x16_t (&s)[QT][NS]) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int st = 0; st < NS; ++st) s[qt][st] = (f32x16_t){};
-      if constexpr (BF16) {
+      if constexpr (H16) {
 #pragma unroll
         for (int ks = 0; ks < QF; ++ks)
 #pragma unroll
           for (int st = 0; st < NS; ++st) {
             const u32x4_t ka = *(const u32x4_t*)(&sm.k[kbuf][(32 * st + r32) * S::KP + 16 * ks + 8 * hh]);
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt) s[qt][st] = mfma32_bf16(ka, qf4[qt][ks], s[qt][st]);
+            for (int qt = 0; qt < QT; ++qt) s[qt][st] = mfma16<H16>(ka, qf4[qt][ks], s[qt][st]);
           }
       } else {
 #pragma unroll
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     // four, dims 4*(s%4) .. +4 of the group's 16.
     const int vlane = (4 * hh + ((lane >> 2) & 3)) * S::VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     auto read_vfrag = [&](int vbuf, int kc, u32x4_t (&dst)[DT]) __attribute__((always_inline)) {
-      if constexpr (BF16) {
+      if constexpr (H16) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const T* p = &sm.v[vbuf][vlane + 16 * kc * S::VP + 32 * dt];
@@ -339,12 +339,12 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const int off = boff[qt] + (kb + 32 * st + 8 * j) * ELT;
-                if constexpr (BF16) {
+                if constexpr (H16) {
                   const u32x2_t x = buf_load8(bres, off);
-                  bv[st][4 * j + 0] = __uint_as_float(x[0] << 16);
-                  bv[st][4 * j + 1] = __uint_as_float(x[0] & 0xFFFF0000u);
-                  bv[st][4 * j + 2] = __uint_as_float(x[1] << 16);
-                  bv[st][4 * j + 3] = __uint_as_float(x[1] & 0xFFFF0000u);
+                  bv[st][4 * j + 0] = lo16<H16>(x[0]);
+                  bv[st][4 * j + 1] = hi16<H16>(x[0]);
+                  bv[st][4 * j + 2] = lo16<H16>(x[1]);
+                  bv[st][4 * j + 3] = hi16<H16>(x[1]);
                 } else {
                   const u32x4_t x = buf_load16(bres, off);
 #pragma unroll
@@ -358,8 +358,8 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
                 const int off = boff[qt] + (kb + 32 * st + 8 * (i >> 2) + (i & 3)) * (int)a.bs3 * ELT;
-                if constexpr (BF16)
-                  bv[st][i] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(bres, off, 0, 0) << 16);
+                if constexpr (H16)
+                  bv[st][i] = lo16<H16>(__builtin_amdgcn_raw_buffer_load_b16(bres, off, 0, 0));
                 else
                   bv[st][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bres, off, 0, 0));
               }
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
         if constexpr (HAS_BIAS) return fast_exp2(v - m_use[qt]);
         else return fast_exp2(__builtin_fmaf(v, a.scale_log2, -m_use[qt]));
       };
-      if constexpr (BF16) {
+      if constexpr (H16) {
         // 16-key chunks kc: P^T chunk = registers 8*(kc%2) .. +8 of score tile kc/2.
         // The V^T fragments of chunk kc+1 are read while chunk kc computes.
         u32x4_t vnext[DT];
@@ -438,10 +438,10 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
               const float p0 = p_of(s[qt][kc >> 1][8 * (kc & 1) + 2 * e], qt);
               const float p1 = p_of(s[qt][kc >> 1][8 * (kc & 1) + 2 * e + 1], qt);
               psum[qt] += p0 + p1;
-              pb[e] = pack_bf16x2(p0, p1);
+              pb[e] = pack16<H16>(p0, p1);
             }
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = mfma32_bf16(vcur[dt], pb, acc[qt][dt]);
+            for (int dt = 0; dt < DT; ++dt) acc[qt][dt] = mfma16<H16>(vcur[dt], pb, acc[qt][dt]);
           }
         }
       } else {
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     // on neither.  The row sums add the bf16-rounded P that the PV MFMAs use.
     constexpr int NCH = 2 * NS;  // 16-key chunks per block
     auto step_fast = [&](int n, f32x16_t (&sc)[QT][NS], f32x16_t (&sn)[QT][NS]) __attribute__((always_inline)) {
-      if constexpr (QT == 1 && BF16 && !HAS_BIAS) {
+      if constexpr (QT == 1 && H16 && !HAS_BIAS) {
       static_assert(QF % NCH == 0, "whole k-steps per round");
       constexpr int KPR = QF / NCH;  // S k-steps per round
       const int kb = kb0 + n * BN;
@@ -520,12 +520,12 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
               const int ks = kc * KPR + r;
-              sn[0][st] = mfma32_bf16(kfr[ks * NS + st], qf4[0][ks], sn[0][st]);
+              sn[0][st] = mfma16<H16>(kfr[ks * NS + st], qf4[0][ks], sn[0][st]);
             }
         }
         if (kc > 0) {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) acc[0][dt] = mfma32_bf16(vf[kc - 1][dt], pb[kc - 1], acc[0][dt]);
+          for (int dt = 0; dt < DT; ++dt) acc[0][dt] = mfma16<H16>(vf[kc - 1][dt], pb[kc - 1], acc[0][dt]);
         }
         if (kc + 1 < NCH) read_vfrag(vbuf, kc + 1, vf[kc + 1]);
         if (kc < NCH) {
@@ -534,12 +534,12 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
           for (int e = 0; e < 4; ++e) {
             const float p0 = fast_exp2(__builtin_fmaf(sc[0][st][i0 + 2 * e], a.scale_log2, nmu));
             const float p1 = fast_exp2(__builtin_fmaf(sc[0][st][i0 + 2 * e + 1], a.scale_log2, nmu));
-            pb[kc][e] = pack_bf16x2(p0, p1);
+            pb[kc][e] = pack16<H16>(p0, p1);
           }
-          ps0 = add_bf16x2(pb[kc][0], ps0);
-          ps1 = add_bf16x2(pb[kc][1], ps1);
-          ps0 = add_bf16x2(pb[kc][2], ps0);
-          ps1 = add_bf16x2(pb[kc][3], ps1);
+          ps0 = sum16<H16>(pb[kc][0], ps0);
+          ps1 = sum16<H16>(pb[kc][1], ps1);
+          ps0 = sum16<H16>(pb[kc][2], ps0);
+          ps1 = sum16<H16>(pb[kc][3], ps1);
           // one MFMA, then a share of the vector work, in turn
 #pragma unroll
           for (int g = 0; g < (kc > 0 ? DT : 0) + KPR * NS; ++g) {
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     // buffer block n-1 used, so one barrier per block suffices.
     auto active = [&](int j) { return j < nb && wave_on && kb0 + j * BN < wave_hi; };
     {
-      Loader<BF16, D> ld1;  // K(1) in flight with K(0) and V(0)
+      Loader<H16, D> ld1;  // K(1) in flight with K(0) and V(0)
       ld.load_k(kres, krow_bytes, kb0);
       ld.load_v(vres, krow_bytes, kb0);
       ld1.load_k(kres, krow_bytes, kb0 + BN);
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
         // zeros and is never used), so the MFMAs of S(n + 1) and the
         // exponentials and PV of block n share one straight-line region and
         // are interleaved there
-        if constexpr (BF16) {
+        if constexpr (H16) {
           u32x4_t kfr[KFN];
           read_k((n + 1) & 1, kfr);  // in flight during the row max
           softmax_max(mask_tag, kb, s_cur);
@@ -634,7 +634,7 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
     // unmasked blocks, then the (at most a few) masked ones: two loops, so the
     // accumulators never merge from two code paths inside a loop
     int j = 0;
-    if constexpr (BF16 && !HAS_BIAS && QT == 1) {
+    if constexpr (H16 && !HAS_BIAS && QT == 1) {
       f32x16_t s_alt[QT][NS];
       for (; j + 1 < j_plain; j += 2) {
         step_fast(j, s_cur, s_alt);
@@ -672,8 +672,8 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
             const float o0 = acc[qt][dt][4 * a4 + 0] * inv_l, o1 = acc[qt][dt][4 * a4 + 1] * inv_l;
             const float o2 = acc[qt][dt][4 * a4 + 2] * inv_l, o3 = acc[qt][dt][4 * a4 + 3] * inv_l;
             // rows < 0 fall outside the resource: the store is dropped
-            if constexpr (BF16) {
-              buf_store8((u32x2_t){pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)}, ores, rq[qt] * qrow_bytes + d0 * 2);
+            if constexpr (H16) {
+              buf_store8((u32x2_t){pack16<H16>(o0, o1), pack16<H16>(o2, o3)}, ores, rq[qt] * qrow_bytes + d0 * 2);
             } else {
               buf_store16((u32x4_t){__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2),
                                     __float_as_uint(o3)}, ores, rq[qt] * qrow_bytes + d0 * 4);
@@ -703,10 +703,10 @@ __global__ __launch_bounds__(NT, (min_blocks<BF16, D>())) void fwd_kernel(FwdArg
 // A work item is 32 rows of one (split tile, head); eight threads per row.
 constexpr int kMergeRows = 32;
 
-template <bool BF16, int D>
+template <int H16, int D>
 __global__ __launch_bounds__(NT) void fwd_merge_kernel(FwdArgs a) {
-  using T = typename std::conditional<BF16, uint16_t, float>::type;
-  constexpr int BM = block_m<BF16, D>();
+  using T = typename std::conditional<(H16 != 0), uint16_t, float>::type;
+  constexpr int BM = block_m<H16, D>();
   constexpr int SLABS = BM / kMergeRows;
   constexpr int TPR = NT / kMergeRows;  // threads per row
   constexpr int SEG = D / TPR;          // dims per thread
@@ -746,8 +746,8 @@ __global__ __launch_bounds__(NT) void fwd_merge_kernel(FwdArgs a) {
 #pragma unroll
     for (int e = 0; e < SEG / 4; ++e) {
       const f32x4_t x = acc[e] * inv;
-      if constexpr (BF16)
-        *(u32x2_t*)(dst + 4 * e) = (u32x2_t){pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+      if constexpr (H16)
+        *(u32x2_t*)(dst + 4 * e) = (u32x2_t){pack16<H16>(x[0], x[1]), pack16<H16>(x[2], x[3])};
       else
         *(f32x4_t*)(dst + 4 * e) = x;
     }
@@ -758,32 +758,32 @@ __global__ __launch_bounds__(NT) void fwd_merge_kernel(FwdArgs a) {
 
 }  // namespace
 
-template <bool BF16, int D, bool CAUSAL, bool HAS_BIAS>
+template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
 static hipError_t launch_fwd_t(const FwdArgs& a, int64_t items, hipStream_t st) {
-  auto kern = fwd_kernel<BF16, D, CAUSAL, HAS_BIAS>;
+  auto kern = fwd_kernel<H16, D, CAUSAL, HAS_BIAS>;
   const int grid = resident_grid((const void*)kern, NT, items);
   if (grid <= 0) return hipErrorInvalidConfiguration;
-  timing_before(st, BF16 ? "fwd_bf16" : "fwd_f32");
+  timing_before(st, H16 == 2 ? "fwd_f16" : H16 ? "fwd_bf16" : "fwd_f32");
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
   timing_after(st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split_cap <= 0) return e;
-  int64_t mg = (int64_t)a.split_cap * a.hq * (block_m<BF16, D>() / kMergeRows);
+  int64_t mg = (int64_t)a.split_cap * a.hq * (block_m<H16, D>() / kMergeRows);
   if (mg > 4096) mg = 4096;
   timing_before(st, "fwd_merge");
-  hipLaunchKernelGGL((fwd_merge_kernel<BF16, D>), dim3((unsigned)mg), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((fwd_merge_kernel<H16, D>), dim3((unsigned)mg), dim3(NT), 0, st, a);
   timing_after(st);
   return hipGetLastError();
 }
 
-template <bool BF16, int D>
+template <int H16, int D>
 static hipError_t launch_fwd_d(const FwdArgs& a, int64_t grid, hipStream_t st) {
   const bool has_bias = a.bias != nullptr;
   if (a.causal)
-    return has_bias ? launch_fwd_t<BF16, D, true, true>(a, grid, st)
-                    : launch_fwd_t<BF16, D, true, false>(a, grid, st);
-  return has_bias ? launch_fwd_t<BF16, D, false, true>(a, grid, st)
-                  : launch_fwd_t<BF16, D, false, false>(a, grid, st);
+    return has_bias ? launch_fwd_t<H16, D, true, true>(a, grid, st)
+                    : launch_fwd_t<H16, D, true, false>(a, grid, st);
+  return has_bias ? launch_fwd_t<H16, D, false, true>(a, grid, st)
+                  : launch_fwd_t<H16, D, false, false>(a, grid, st);
 }
 
 int fwd_block_m() { return block_m<true, 64>(); }
@@ -793,8 +793,9 @@ int fwd_block_n(bool bf16, int d) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int64_t grid, hipStream_t st) {
-  if (a.bf16) return a.d == 64 ? launch_fwd_d<true, 64>(a, grid, st) : launch_fwd_d<true, 128>(a, grid, st);
-  return a.d == 64 ? launch_fwd_d<false, 64>(a, grid, st) : launch_fwd_d<false, 128>(a, grid, st);
+  if (a.bf16 == 2) return a.d == 64 ? launch_fwd_d<2, 64>(a, grid, st) : launch_fwd_d<2, 128>(a, grid, st);
+  if (a.bf16) return a.d == 64 ? launch_fwd_d<1, 64>(a, grid, st) : launch_fwd_d<1, 128>(a, grid, st);
+  return a.d == 64 ? launch_fwd_d<0, 64>(a, grid, st) : launch_fwd_d<0, 128>(a, grid, st);
 }
 
 }  // namespace va

@@ -62,7 +62,7 @@ struct FwdArgs {
   int32_t split_cap;
   float scale_log2;
   int32_t causal;
-  int32_t bf16;
+  int32_t bf16;      // element kind: 0 float32, 1 bfloat16, 2 float16
   int32_t bias_vec;  // keys contiguous (bs3 = 1), 4-key groups aligned: vector bias loads
 };
 
@@ -97,8 +97,8 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   int32_t causal;
-  int32_t bf16;
-  int32_t grad_bf16;
+  int32_t bf16;       // element kind: 0 float32, 1 bfloat16, 2 float16
+  int32_t grad_bf16;  // gradients in float32 (0) or in the input's 16-bit kind (its code)
   int32_t bias_vec;  // keys contiguous (bs3 = 1), 4-key groups aligned: vector bias loads
 };
 

@@ -66,6 +66,17 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return bits.view(np.float32).reshape(np.shape(x))
 
 
+def f16_round(x: np.ndarray) -> np.ndarray:
+    """float32 array whose values are the IEEE binary16 rounding of ``x`` (nearest, ties to even).
+
+    Inputs must be finite and below the binary16 overflow threshold (65520).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if not np.all(np.abs(x) < 65520.0):
+        raise ValueError("f16_round expects finite values below 65520")
+    return x.astype(np.float16).astype(np.float32)
+
+
 def _cu(lengths: Sequence[int]) -> np.ndarray:
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
@@ -84,7 +95,7 @@ class Workload:
     """
 
     name: str
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "f16"
     causal: bool
     lens_q: np.ndarray
     lens_k: np.ndarray
@@ -150,7 +161,11 @@ def _draw(rng: np.random.Generator, shape, dtype: str, std: float = 1.0) -> np.n
     x = rng.standard_normal(size=shape, dtype=np.float32)
     if std != 1.0:
         x *= np.float32(std)
-    return bf16_round(x) if dtype == "bf16" else x
+    if dtype == "bf16":
+        return bf16_round(x)
+    if dtype == "f16":
+        return f16_round(x)
+    return x
 
 
 def _lengths(cfg_id: int) -> tuple:
@@ -208,7 +223,7 @@ def config(cfg_id: int, dtype: Optional[str] = None, bias: str = "none",
     """
     hq, hkv, d, causal, dt0, has_bwd = _SHAPES[cfg_id]
     dtype = dtype or dt0
-    if dtype not in ("f32", "bf16"):
+    if dtype not in ("f32", "bf16", "f16"):
         raise ValueError(dtype)
     lq, lk = _lengths(cfg_id)
     tq, tk = int(lq.sum()), int(lk.sum())
@@ -253,6 +268,8 @@ def make_case(seed: int, lens_q: Sequence[int], lens_k: Optional[Sequence[int]] 
     stride is 1 on the key axis), or ``"head_shared"`` (head stride 0).
     ``grid`` = (R, C) fixes the bias grid edge (default: the max lengths).
     """
+    if dtype not in ("f32", "bf16", "f16"):
+        raise ValueError(dtype)
     lens_q = np.asarray(list(lens_q), dtype=np.int64)
     lens_k = lens_q.copy() if lens_k is None else np.asarray(list(lens_k), dtype=np.int64)
     if len(lens_q) != len(lens_k):
