@@ -20,4 +20,5 @@ from .attention import (  # noqa: F401
     visible,
 )
 from .brute import brute_forward  # noqa: F401
+from .kvcache import gather_pages, kvcache_forward  # noqa: F401
 from .packing import pack_metadata, pad, unpad  # noqa: F401

@@ -54,9 +54,9 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     if not np.all(np.isfinite(x)):
         raise ValueError("bf16_bits expects finite values")
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) & 0xFFFF
+    # finite patterns are at most 0xFF7FFFFF, so the sum stays below 2^32
+    u = x.view(np.uint32)
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
     return r.astype(np.uint16)
 
 
