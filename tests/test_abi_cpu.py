@@ -249,3 +249,59 @@ def test_unpad_pad_validation(lib, which, kw, code):
         r = lib.va_pad(arr, a["n"], a["index"], a["batch"], a["seqlen"], a["rows"], None)
     assert r == code
     assert lib.va_last_error()
+
+
+# ---------------------------------------------------------------- decode steps (include/va_kvcache.h)
+def _kv(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, cq=P, sk=P, bt=P, bts=8, ps=16, np_=64, mq=1, mk=128, scale=0.125, causal=1,
+             out=P, lse=P, ws=0x100000, wsb=1 << 30, batch=2, tq=2, hq=8, hkv=2, d=128, dt=BF16)
+    a.update(kw)
+    return lib.va_kvcache_fwd(a["q"], a["kc"], a["vc"], a["cq"], a["sk"], a["bt"], a["bts"], a["ps"], a["np_"],
+                              a["mq"], a["mk"], a["scale"], a["causal"], a["out"], a["lse"], a["ws"], a["wsb"],
+                              a["batch"], a["tq"], a["hq"], a["hkv"], a["d"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID),
+    (dict(bt=None), INVALID),
+    (dict(sk=None), INVALID),
+    (dict(lse=None), INVALID),
+    (dict(batch=0), INVALID),
+    (dict(tq=0), INVALID),
+    (dict(hq=6, hkv=4), INVALID),
+    (dict(mq=0), INVALID),
+    (dict(mk=-1), INVALID),
+    (dict(ps=0), INVALID),
+    (dict(ps=24), INVALID),            # not a power of two
+    (dict(ps=1 << 21), INVALID),
+    (dict(np_=0), INVALID),
+    (dict(bts=7), INVALID),            # 7 pages of 16 keys do not reach max_seqlen_k = 128
+    (dict(causal=2), INVALID),
+    (dict(scale=0.0), INVALID),
+    (dict(kc=P + 8), INVALID),         # misaligned cache
+    (dict(dt=F32), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED),
+    (dict(mq=1 << 20, hq=64, hkv=8), UNSUPPORTED),  # a sequence's queries span 2^31 bytes
+])
+def test_kvcache_validation(lib, kw, code):
+    assert _kv(lib, **kw) == code
+    assert lib.va_last_error()
+
+
+def test_kvcache_workspace_size(lib):
+    f = lib.va_kvcache_fwd_workspace_size
+    assert f(0, 1, 128, 8, 2, 128, BF16) == 0
+    assert f(2, 1, 128, 8, 2, 128, F32) == 0         # not a decode dtype
+    assert f(2, 1, 128, 8, 3, 128, BF16) == 0
+    # chunks of at least 256 keys: a cache that fits one chunk needs no partials
+    assert f(2, 1, 256, 8, 2, 128, BF16) == 0
+    assert f(2, 1, 0, 8, 2, 128, F16) == 0
+    # 4 KV heads x 2 sequences = 8 row blocks want 1024 chunks each: 512 keys split into
+    # two of 256; partial rows per slot = n_rep * max_q = 4
+    slots = 2 * 4 * 1 * 2
+    assert f(2, 1, 512, 16, 4, 128, BF16) == _r(slots * 4 * 128 * 4) + _r(slots * 4 * 4)
+    # 12 new tokens x 4 heads per KV head = 48 rows: two row blocks of 32 rows
+    slots = 2 * 4 * 2 * 2
+    assert f(2, 12, 512, 16, 4, 64, F16) == _r(slots * 32 * 64 * 4) + _r(slots * 32 * 4)
+    # a large batch keeps whole caches in one chunk when that already gives 8192 waves
+    assert f(8192, 1, 4000, 8, 1, 128, BF16) == 0

@@ -9,6 +9,7 @@ library is missing, calls raise.
                              softmax_scale, causal, bias=None, bias_stride=None)
     dq, dk, dv = va_varlen_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, ...)
     out = varlen_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, ...)
+    out, lse = kvcache_fwd(q, k_cache, v_cache, cu_seqlens_q, seqlens_k, block_table, ...)
 
 Layouts: q/out [total_q, Hq, d], k/v [total_k, Hkv, d], lse [Hq, total_q]
 float32, cu_seqlens int32 [batch + 1] on the device, bias a device tensor of
@@ -19,6 +20,8 @@ it is 4-D ``[batch, Hq, rows, cols]``; a per-key bias is rows stride 0).
 
 from .api import (  # noqa: F401
     VaError,
+    kvcache_fwd,
+    kvcache_fwd_workspace_size,
     pack_metadata,
     pad,
     unpad,

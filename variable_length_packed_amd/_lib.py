@@ -1,4 +1,5 @@
-"""ctypes view of libva_varlen.so (the C ABI declared in include/va_varlen.h and include/va_pack.h)."""
+"""ctypes view of libva_varlen.so (the C ABI declared in include/va_varlen.h, include/va_kvcache.h
+and include/va_pack.h)."""
 
 from __future__ import annotations
 
@@ -10,10 +11,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libva_varle
 VA_OK, VA_ERR_INVALID, VA_ERR_UNSUPPORTED, VA_ERR_WORKSPACE, VA_ERR_HIP = range(5)
 VA_F32, VA_BF16, VA_F16 = 0, 1, 2
 
-# Every symbol include/va_varlen.h and include/va_pack.h declare.
+# Every symbol the headers under include/ declare.
 EXPORTS = ("va_varlen_fwd", "va_varlen_bwd", "va_varlen_fwd_workspace_size",
            "va_varlen_bwd_workspace_size", "va_status_string", "va_last_error", "va_version",
-           "va_timing_start", "va_timing_stop", "va_pack_metadata", "va_unpad", "va_pad")
+           "va_timing_start", "va_timing_stop", "va_pack_metadata", "va_unpad", "va_pad",
+           "va_kvcache_fwd", "va_kvcache_fwd_workspace_size")
 VA_PACK_MAX_TENSORS = 4
 
 
@@ -69,6 +71,12 @@ def load() -> ctypes.CDLL:
     lib.va_pack_metadata.argtypes = [_p, _i32, _i32, _p, _p, _p, _p, _p, _p]
     lib.va_unpad.restype = ctypes.c_int
     lib.va_unpad.argtypes = [ctypes.POINTER(PackTensor), _i32, _p, _p, _i32, _i32, ctypes.c_int64, _p]
+    lib.va_kvcache_fwd.restype = ctypes.c_int
+    lib.va_kvcache_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f, ctypes.c_int,
+                                   _p, _p, _p, ctypes.c_size_t, _i32, _i32, _i32, _i32, _i32,
+                                   ctypes.c_int, _p]
+    lib.va_kvcache_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.va_kvcache_fwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int]
     lib.va_pad.restype = ctypes.c_int
     lib.va_pad.argtypes = [ctypes.POINTER(PackTensor), _i32, _p, _i32, _i32, ctypes.c_int64, _p]
     _lib = lib

@@ -136,6 +136,66 @@ def va_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return out, lse
 
 
+def kvcache_fwd_workspace_size(batch: int, max_seqlen_q: int, max_seqlen_k: int, num_heads_q: int,
+                               num_heads_kv: int, head_dim: int, dtype: torch.dtype) -> int:
+    lib = _lib.load()
+    return int(lib.va_kvcache_fwd_workspace_size(batch, max_seqlen_q, max_seqlen_k, num_heads_q,
+                                                 num_heads_kv, head_dim, _DTYPES.get(dtype, -1)))
+
+
+def kvcache_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                cu_seqlens_q: torch.Tensor, seqlens_k: torch.Tensor, block_table: torch.Tensor,
+                max_seqlen_q: int, max_seqlen_k: int, softmax_scale: Optional[float] = None,
+                causal: bool = True, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Decode step against a paged KV cache (include/va_kvcache.h).
+
+    q [total_q, Hq, d] (the new tokens, packed by cu_seqlens_q), k_cache / v_cache
+    [num_pages, page_size, Hkv, d], seqlens_k int32 [batch], block_table int32
+    [batch, pages_per_seq].  Returns (out [total_q, Hq, d], lse [Hq, total_q] float32).
+    """
+    lib = _lib.load()
+    for n, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("cu_seqlens_q", cu_seqlens_q),
+                 ("seqlens_k", seqlens_k), ("block_table", block_table)):
+        _need_dev(n, t, q.device)
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [tokens, heads, d] and the caches [pages, page_size, heads, d]")
+    if k_cache.shape[3] != q.shape[2] or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("the caches must share q's head_dim and dtype")
+    if cu_seqlens_q.dtype != torch.int32 or seqlens_k.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise ValueError("cu_seqlens_q, seqlens_k and block_table must be int32")
+    batch = cu_seqlens_q.numel() - 1
+    if cu_seqlens_q.dim() != 1 or seqlens_k.shape != (batch,) or block_table.dim() != 2 or \
+            block_table.shape[0] != batch:
+        raise ValueError("seqlens_k must be [batch] and block_table [batch, pages_per_seq]")
+    dt = _dt(q)
+    tq, hq, d = q.shape
+    n_pages, page_size, hkv, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _need_dev("out", out, q.device)
+    _need_dev("lse", lse, q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or lse.shape != (hq, tq) or lse.dtype != torch.float32:
+        raise ValueError("out/lse have the wrong shape or dtype")
+    need = lib.va_kvcache_fwd_workspace_size(batch, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
+    wptr, wbytes = (0, 0) if workspace is None else (workspace.data_ptr(),
+                                                     workspace.numel() * workspace.element_size())
+    if workspace is not None:
+        _need_dev("workspace", workspace, q.device)
+    st = lib.va_kvcache_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens_q.data_ptr(),
+                            seqlens_k.data_ptr(), block_table.data_ptr(), block_table.shape[1], page_size,
+                            n_pages, int(max_seqlen_q), int(max_seqlen_k), scale, int(bool(causal)),
+                            out.data_ptr(), lse.data_ptr(), wptr or None, wbytes, batch, tq, hq, hkv, d, dt,
+                            _stream(q.device))
+    _raise(st, lib)
+    return out, lse
+
+
 def va_varlen_fwd_workspace_size(batch: int, total_q: int, total_k: int, max_seqlen_q: int,
                                  max_seqlen_k: int, num_heads_q: int, num_heads_kv: int,
                                  head_dim: int, dtype: torch.dtype) -> int:

@@ -25,7 +25,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", f"-I{INCLUDE}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]
 
-SOURCES = ["va_api.cpp", "va_plan.hip", "va_fwd.hip", "va_bwd.hip", "va_pack.hip"]
+SOURCES = ["va_api.cpp", "va_plan.hip", "va_fwd.hip", "va_bwd.hip", "va_pack.hip", "va_kvcache.hip"]
 
 
 def _hipcc() -> str:

@@ -1,8 +1,9 @@
 // C ABI of the packed varlen attention library: argument validation (host
 // only, no device reads), schedule sizing and kernel launch.  Declarations
-// and the contract of every entry point are in include/va_varlen.h and
-// include/va_pack.h.
+// and the contract of every entry point are in include/va_varlen.h,
+// include/va_kvcache.h and include/va_pack.h.
 #include "va_varlen.h"
+#include "va_kvcache.h"
 #include "va_pack.h"
 
 #include <hip/hip_runtime.h>
@@ -171,6 +172,44 @@ size_t bwd_workspace(int batch, int total_q, int total_k, int max_q, int max_k, 
   return round_up((size_t)hq * total_q * sizeof(float)) + K.plan_bytes + Q.plan_bytes +
          round_up(K.slot_bytes * K.slot_cap) + round_up(Q.slot_bytes * Q.slot_cap) +
          round_up(dbias_slot_bytes(hq) * K.slot_cap);
+}
+
+// Decode steps: 32-row blocks of (new token, query head) pairs per (sequence,
+// KV head), and key chunks sized so the grid holds about kKvWaves waves (at
+// least 256 keys per chunk, so the partial results of a chunk stay a few
+// percent of the K/V bytes it reads).
+constexpr int64_t kKvWaves = 8192;
+struct KvLayout {
+  int rblocks = 1, rows = 1, chunk = 1, nchunk = 1;
+  size_t part_o_bytes = 0, part_lse_bytes = 0;
+};
+KvLayout kv_layout(int batch, int max_q, int max_k, int hq, int hkv, int d) {
+  KvLayout L;
+  const int64_t R = (int64_t)max_q * (hq / hkv);
+  L.rblocks = (int)((R + 31) / 32);
+  L.rows = (int)(R < 32 ? R : 32);
+  const int kb = va::kv_block_n(d);
+  const int64_t blocks = (int64_t)batch * hkv * L.rblocks;
+  const int64_t want = (kKvWaves + blocks - 1) / blocks;  // chunks wanted per row block
+  const int64_t steps = ((int64_t)max_k + kb - 1) / kb;
+  int64_t cs = (steps + want - 1) / want;
+  if (cs < 256 / kb) cs = 256 / kb;
+  L.chunk = (int)(cs * kb);
+  L.nchunk = (int)(((int64_t)max_k + L.chunk - 1) / L.chunk);
+  if (L.nchunk < 1) L.nchunk = 1;
+  if (L.nchunk > 1) {
+    const size_t slots = (size_t)blocks * L.nchunk;
+    L.part_o_bytes = round_up(slots * L.rows * d * sizeof(float));
+    L.part_lse_bytes = round_up(slots * L.rows * sizeof(float));
+  }
+  return L;
+}
+
+bool kv_args_ok(int32_t batch, int32_t max_q, int32_t max_k, int32_t hq, int32_t hkv, int32_t d,
+                va_dtype dtype) {
+  return batch > 0 && max_q > 0 && max_k >= 0 && hq > 0 && hkv > 0 && hq % hkv == 0 &&
+         (d == 64 || d == 128) && (dtype == VA_BF16 || dtype == VA_F16) &&
+         (int64_t)max_q * hq * d * 2 < ((int64_t)1 << 31);
 }
 
 // kernel element code: 0 float32, 1 bfloat16, 2 float16
@@ -391,6 +430,81 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
 // ---------------------------------------------------------------------------
 // Packing (include/va_pack.h)
 // ---------------------------------------------------------------------------
+size_t va_kvcache_fwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                     int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                     va_dtype dtype) {
+  if (!kv_args_ok(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, dtype)) return 0;
+  const KvLayout L = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
+  return L.part_o_bytes + L.part_lse_bytes;
+}
+
+va_status va_kvcache_fwd(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* cu_seqlens_q, const int32_t* seqlens_k,
+                         const int32_t* block_table, int32_t block_table_stride,
+                         int32_t page_size, int32_t num_pages,
+                         int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                         int causal, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, int32_t batch, int32_t total_q,
+                         int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                         va_dtype dtype, va_stream stream) {
+  g_err[0] = 0;
+  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !seqlens_k || !block_table || !out || !lse)
+    return fail(VA_ERR_INVALID, "a required pointer is NULL");
+  if (batch <= 0 || total_q <= 0) return fail(VA_ERR_INVALID, "batch and total_q must be > 0");
+  if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0)
+    return fail(VA_ERR_INVALID, "head counts must be > 0, num_heads_q a multiple of num_heads_kv");
+  if (head_dim <= 0) return fail(VA_ERR_INVALID, "head_dim must be > 0");
+  if (max_seqlen_q <= 0 || max_seqlen_k < 0)
+    return fail(VA_ERR_INVALID, "max_seqlen_q must be > 0 and max_seqlen_k >= 0");
+  if (page_size <= 0 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+    return fail(VA_ERR_INVALID, "page_size must be a power of two in [1, 2^20] (got %d)", page_size);
+  if (num_pages <= 0) return fail(VA_ERR_INVALID, "num_pages must be > 0");
+  if (block_table_stride <= 0 || (int64_t)block_table_stride * page_size < max_seqlen_k)
+    return fail(VA_ERR_INVALID, "block_table_stride * page_size must cover max_seqlen_k");
+  if (causal != 0 && causal != 1) return fail(VA_ERR_INVALID, "causal must be 0 or 1");
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f))
+    return fail(VA_ERR_INVALID, "softmax_scale must be finite and > 0");
+  if ((((uintptr_t)q) | ((uintptr_t)k_cache) | ((uintptr_t)v_cache) | ((uintptr_t)out)) % 16 != 0)
+    return fail(VA_ERR_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (dtype != VA_BF16 && dtype != VA_F16)
+    return fail(VA_ERR_UNSUPPORTED, "decode steps take bf16 or float16 (got dtype %d)", (int)dtype);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(VA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (!kv_args_ok(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, dtype))
+    return fail(VA_ERR_UNSUPPORTED, "max_seqlen_q * num_heads_q * head_dim * 2 must be < 2^31");
+  const KvLayout L = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
+  const size_t need = L.part_o_bytes + L.part_lse_bytes;
+  if (need > 0) {
+    if (!workspace) return fail(VA_ERR_INVALID, "workspace is NULL but %zu bytes are needed", need);
+    if (((uintptr_t)workspace) % kAlign != 0)
+      return fail(VA_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  }
+  va::KvArgs a{};
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.cu_q = cu_seqlens_q; a.seqlens_k = seqlens_k; a.block_table = block_table;
+  a.out = out; a.lse = lse;
+  a.part_o = need > 0 ? (float*)workspace : nullptr;
+  a.part_lse = need > 0 ? (float*)((char*)workspace + L.part_o_bytes) : nullptr;
+  a.batch = batch; a.total_q = total_q;
+  a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = num_heads_q / num_heads_kv; a.d = head_dim;
+  a.bt_stride = block_table_stride;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  a.page_shift = shift;
+  a.num_pages = num_pages;
+  const int64_t reach = (int64_t)block_table_stride * page_size;
+  a.max_k = (int)(reach < max_seqlen_k ? reach : max_seqlen_k);
+  a.rblocks = L.rblocks; a.rows = L.rows; a.chunk = L.chunk; a.nchunk = L.nchunk;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.causal = causal;
+  a.h16 = elem_code(dtype);
+  const hipError_t e = va::launch_kvcache(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return VA_OK;
+}
+
 va_status va_pack_metadata(const uint8_t* mask, int32_t batch, int32_t seqlen,
                            int32_t* cu_seqlens, int32_t* max_seqlen,
                            int32_t* indices, int32_t* position_ids, int32_t* inverse,

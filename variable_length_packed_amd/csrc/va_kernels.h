@@ -123,6 +123,38 @@ hipError_t launch_bwd(const BwdArgs& a, const PlanSet& ps, int64_t max_q_items, 
                       hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// Decode steps against a paged KV cache.  A work item (one wave) is one
+// (sequence, KV head, row block, key chunk): 32 rows = (new token, query
+// head of the KV head's group) pairs, keys [chunk * c, chunk * (c + 1)).
+// Items are numbered ((b * hkv + g) * rblocks + rb) * nchunk + c.  A
+// sequence with more than one chunk writes float32 partials to the slot of
+// its item, [slot][rows][d] and [slot][rows], and the merge kernel combines
+// its chunks in order.
+// ---------------------------------------------------------------------------
+struct KvArgs {
+  const void* q;             // [total_q, hq, d]
+  const void* k_cache;       // [num_pages, page_size, hkv, d]
+  const void* v_cache;
+  const int32_t* cu_q;       // [batch + 1]
+  const int32_t* seqlens_k;  // [batch]
+  const int32_t* block_table;  // [batch][bt_stride]
+  void* out;                 // [total_q, hq, d]
+  float* lse;                // [hq, total_q]
+  float* part_o;
+  float* part_lse;
+  int32_t batch, total_q, hq, hkv, n_rep, d;
+  int32_t bt_stride, page_shift, num_pages;
+  int32_t max_k;             // keys of a sequence are capped here (max_seqlen_k and the table's reach)
+  int32_t rblocks, rows;     // 32-row blocks per (sequence, KV head); partial rows per slot
+  int32_t chunk, nchunk;     // keys per item (a multiple of the step), chunks per row block
+  float scale_log2;
+  int32_t causal;
+  int32_t h16;               // 1 bfloat16, 2 float16
+};
+int kv_block_n(int d);  // keys per step of the decode kernel
+hipError_t launch_kvcache(const KvArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Packing: metadata from a padding mask, unpad (gather) and pad (scatter).
 // ---------------------------------------------------------------------------
 constexpr int kPackMaxTensors = 4;

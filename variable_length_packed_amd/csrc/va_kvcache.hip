@@ -1,0 +1,353 @@
+// Decode steps: attention of a few new query tokens per sequence against the
+// sequence's paged KV cache.
+//
+// A decode step reads every cached key and value once and does little
+// arithmetic per byte (2 * n_rep * q_len flops per byte of K/V at 16 bits), so
+// this kernel is bound by HBM, not by the matrix cores.  Its shape follows
+// from that:
+//
+// * A work item is ONE wave: 32 rows, each a (new token, query head) pair of
+//   one KV head's GQA group, against a chunk of the sequence's keys.  The
+//   n_rep query heads that share a KV head sit in one tile, so K and V are
+//   read once per KV head, not once per query head.
+// * Each lane owns one key of every 32-key score tile and loads that key's K
+//   row straight into the A operand of S^T = K Q^T (no LDS), and the same
+//   key's V row, which goes through a wave-private LDS slice so that the
+//   transposing LDS read (ds_read_b64_tr_b16) can hand out V^T fragments for
+//   O^T += V^T P^T, exactly as in the packed forward kernel.
+// * The page of a key is one block-table lookup per lane and tile; the page
+//   index is clamped into the pool and keys past the chunk's end are clamped
+//   to its last key (their scores are masked), so no address ever leaves the
+//   cache, whatever the table holds.
+// * Long caches are split into chunks of `chunk` keys so that the grid has
+//   thousands of waves; a chunk writes its normalised partial O and base-2
+//   LSE, and a merge kernel combines a sequence's chunks in chunk order
+//   (deterministic).
+//
+// Semantics (the packed forward's): bottom-right causal alignment, so query
+// i of Lq sees keys j <= i + Lk - Lq; a row with no visible key gives O = 0
+// and LSE = -inf.
+#include "va_common.h"
+#include "va_kernels.h"
+
+namespace va {
+
+namespace {
+
+constexpr int KNT = 256;  // 4 independent waves per workgroup
+
+template <int D>
+struct KvShape {
+  static constexpr int KB = 4096 / D;  // keys per step: 8 KB of K and 8 KB of V per wave
+  static constexpr int NS = KB / 32;   // 32-key score tiles per step
+  static constexpr int VP = D + 8;     // LDS row pitch of the staged V block (elements)
+  static constexpr int KS = D / 16;    // MFMA k-steps over head_dim
+  static constexpr int DT = D / 32;    // 32-wide tiles of head_dim in O^T
+};
+
+template <int H16, int D, bool CAUSAL, bool BIGPAGE>
+__global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
+  using SH = KvShape<D>;
+  constexpr int KB = SH::KB, NS = SH::NS, VP = SH::VP, KS = SH::KS, DT = SH::DT;
+  __shared__ uint16_t sk_all[4][KB * VP];
+  __shared__ uint16_t sv_all[4][KB * VP];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = uniform(threadIdx.x >> 6);
+  const int hh = lane >> 5;
+  const int r32 = lane & 31;
+  uint16_t* sk = sk_all[wid];
+  uint16_t* sv = sv_all[wid];
+
+  // ---- items: (sequence, KV head, row block, chunk), taken by each wave with a
+  // grid stride; waves never synchronise, so each runs its items alone
+  const int NC = a.nchunk, RB = a.rblocks;
+  const int n_items = a.batch * a.hkv * RB * NC;
+  for (int item = (int)blockIdx.x * 4 + wid; item < n_items; item += (int)gridDim.x * 4) {
+  const int c = item % NC;
+  int t = item / NC;
+  const int rb = t % RB;
+  t /= RB;
+  const int g = t % a.hkv;
+  const int b = t / a.hkv;
+
+  int q0, q1;
+  seq_bounds(a.cu_q, b, a.total_q, q0, q1);
+  const int Lq = q1 - q0;
+  if (32 * rb >= Lq * a.n_rep) continue;  // no rows in this block
+  const int Lk = min(max(a.seqlens_k[b], 0), a.max_k);
+  const int nch = max(1, (Lk + a.chunk - 1) / a.chunk);
+  if (c >= nch) continue;
+  const int off = Lk - Lq;
+
+  // this lane's row: new token qpos, query head h
+  const int r = 32 * rb + r32;
+  const int qpos = r / a.n_rep;
+  const int h = g * a.n_rep + (r - qpos * a.n_rep);
+  const bool row_ok = qpos < Lq;
+  // keys of the chunk that some row of the block sees, and the steps that
+  // every valid row of the block sees in full
+  const int qpos_first = (32 * rb) / a.n_rep;
+  const int qpos_last = min(Lq - 1, (32 * rb + 31) / a.n_rep);
+  const int kbeg = c * a.chunk;
+  int kend = min(Lk, kbeg + a.chunk);
+  if (CAUSAL) kend = min(kend, qpos_last + off + 1);
+  const int nsteps = kend > kbeg ? (kend - kbeg + KB - 1) / KB : 0;
+  int plain_end = kend;
+  if (CAUSAL) plain_end = min(plain_end, qpos_first + off + 1);
+  const int nplain = plain_end > kbeg ? (plain_end - kbeg) / KB : 0;
+  const int hi = !row_ok ? -1 : (CAUSAL ? min(kend - 1, qpos + off) : kend - 1);
+
+  // ---- Q fragments (B operand of S^T = K Q^T); rows past the sequence read 0
+  constexpr int ELT = 2;
+  const size_t qrow = (size_t)a.hq * D;
+  const rsrc_t qres = make_rsrc((const uint16_t*)a.q + (size_t)q0 * qrow, (int64_t)Lq * qrow * ELT);
+  u32x4_t qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = buf_load16(qres, ((qpos * a.hq + h) * D + 16 * ks + 8 * hh) * ELT);
+
+  // ---- cache rows.  Loads are coalesced: in each 16-byte load instruction LPR
+  // consecutive lanes read one key's row of this KV head (D * 2 bytes), so the
+  // wave reads RPI whole rows per instruction and NI instructions per step for
+  // each of K and V.  Both go through the wave's LDS slices: K is read back in
+  // the MFMA operand layout, V through the transposing read.
+  constexpr int LPR = D / 8;     // lanes per row
+  constexpr int RPI = 64 / LPR;  // rows per load instruction
+  constexpr int NI = KB / RPI;   // load instructions per step and tensor
+  const int lrow = lane / LPR, lcol = (lane % LPR) * 8;
+  const uint16_t* __restrict__ kc = (const uint16_t*)a.k_cache;
+  const uint16_t* __restrict__ vc = (const uint16_t*)a.v_cache;
+  const int32_t* __restrict__ bt = a.block_table + (size_t)b * a.bt_stride;
+  const int pmask = (1 << a.page_shift) - 1;
+  // key of load i of step n (clamped to the chunk's last key)
+  auto key_of = [&](int n, int i) { return min(kbeg + n * KB + RPI * i + lrow, kend - 1); };
+  // pages of the next step to load, fetched a step ahead: with pages of at
+  // least KB keys a step lies in one page (steps start at multiples of KB),
+  // so one uniform lookup per step; otherwise one per load and lane
+  constexpr int NPG = BIGPAGE ? 1 : NI;
+  int pg[NPG];
+  auto fetch_pages = [&](int n) __attribute__((always_inline)) {
+    if constexpr (BIGPAGE) {
+      pg[0] = bt[uniform(kbeg + n * KB) >> a.page_shift];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) pg[i] = bt[key_of(n, i) >> a.page_shift];
+    }
+  };
+  u32x4_t kr[NI], vr[NI];
+  auto load_kv = [&](int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int page = min(max(pg[BIGPAGE ? 0 : i], 0), a.num_pages - 1);
+      const int64_t row = ((int64_t)page << a.page_shift) + (key_of(n, i) & pmask);
+      const int64_t o = (row * a.hkv + g) * D + lcol;
+      kr[i] = __builtin_nontemporal_load((const u32x4_t*)(kc + o));
+      vr[i] = __builtin_nontemporal_load((const u32x4_t*)(vc + o));
+    }
+  };
+
+  f32x16_t acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x16_t){};
+  float m_run = -INFINITY, l_run = 0.f;  // running max (log2 units), this lane's half of the row sum
+
+  // V^T fragments: lane l reads dim 32 dt + l % 32 of the keys its P^T slots
+  // hold (4hh .. 4hh+3 and 8+4hh .. 8+4hh+3 of each 16-key chunk), two
+  // transposing reads of four keys each
+  const int vlane = (4 * hh + ((lane >> 2) & 3)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  if (nsteps > 0) {
+    fetch_pages(0);
+    load_kv(0);
+  }
+  if (nsteps > 1) fetch_pages(1);
+  for (int n = 0; n < nsteps; ++n) {
+    // K(n) and V(n) into the wave's LDS slices (the previous step's reads of
+    // them are done: one wave's LDS operations complete in order)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      *(u32x4_t*)(sk + (RPI * i + lrow) * VP + lcol) = kr[i];
+      *(u32x4_t*)(sv + (RPI * i + lrow) * VP + lcol) = vr[i];
+    }
+    // the next step's K and V are in flight during all of this step's work
+    // (their pages were fetched a step ago); then the pages of the step after
+    if (n + 1 < nsteps) load_kv(n + 1);
+    if (n + 2 < nsteps) fetch_pages(n + 2);
+    // S^T = K Q^T, K fragments from LDS
+    f32x16_t s[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      s[st] = (f32x16_t){};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4_t kf = *(const u32x4_t*)(sk + (32 * st + r32) * VP + 16 * ks + 8 * hh);
+        s[st] = mfma16<H16>(kf, qf[ks], s[st]);
+      }
+    }
+
+    // ---- online softmax (base 2); masked steps test every key against the row's last
+    const int kb = kbeg + n * KB;
+    const bool masked = n >= nplain;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = s[st][i] * a.scale_log2;
+        if (masked) {
+          const int kj = kb + 32 * st + 8 * (i >> 2) + 4 * hh + (i & 3);
+          v = kj <= hi ? v : -INFINITY;
+        }
+        s[st][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);  // 0 while m_run is -inf
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+
+    // ---- P (rounded to the input kind) and O^T += V^T P^T, 16 keys at a time
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int kc16 = 0; kc16 < 2; ++kc16) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = fast_exp2(s[st][8 * kc16 + 2 * j] - m_use);
+          const float p1 = fast_exp2(s[st][8 * kc16 + 2 * j + 1] - m_use);
+          w[j] = pack16<H16>(p0, p1);
+          l_run = sum16<H16>(w[j], l_run);
+        }
+        const u32x4_t bop = (u32x4_t){w[0], w[1], w[2], w[3]};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint16_t* p = sv + vlane + (32 * st + 16 * kc16) * VP + 32 * dt;
+          const u32x2_t lo = lds_read_tr16(p), hi2 = lds_read_tr16(p + 8 * VP);
+          acc[dt] = mfma16<H16>((u32x4_t){lo[0], lo[1], hi2[0], hi2[1]}, bop, acc[dt]);
+        }
+      }
+  }
+
+  // ---- epilogue: O = acc / l and LSE, or this chunk's partials
+  const float l_tot = l_run + xor32(l_run);
+  const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse2 = l_tot > 0.f ? m_run + __builtin_log2f(l_tot) : -INFINITY;
+  if (nch == 1) {
+    const rsrc_t ores = make_rsrc((uint16_t*)a.out + (size_t)q0 * qrow, (int64_t)Lq * qrow * ELT);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = 32 * dt + 8 * a4 + 4 * hh;
+        const float o0 = acc[dt][4 * a4 + 0] * inv_l, o1 = acc[dt][4 * a4 + 1] * inv_l;
+        const float o2 = acc[dt][4 * a4 + 2] * inv_l, o3 = acc[dt][4 * a4 + 3] * inv_l;
+        // rows past the sequence fall outside the resource: the store is dropped
+        buf_store8((u32x2_t){pack16<H16>(o0, o1), pack16<H16>(o2, o3)}, ores, ((qpos * a.hq + h) * D + d0) * ELT);
+      }
+    if (row_ok && hh == 0) a.lse[(size_t)h * a.total_q + q0 + qpos] = lse2 * kLn2;
+  } else if (row_ok && r32 < a.rows) {
+    const size_t slot = (size_t)item;  // ((b * hkv + g) * rblocks + rb) * nchunk + c
+    float* po = a.part_o + (slot * a.rows + r32) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = 32 * dt + 8 * a4 + 4 * hh;
+        *(f32x4_t*)(po + d0) = (f32x4_t){acc[dt][4 * a4 + 0] * inv_l, acc[dt][4 * a4 + 1] * inv_l,
+                                         acc[dt][4 * a4 + 2] * inv_l, acc[dt][4 * a4 + 3] * inv_l};
+      }
+    if (hh == 0) a.part_lse[slot * a.rows + r32] = lse2;
+  }
+  }
+}
+
+// Combines the chunks of every row block whose sequence has more than one:
+// LSE = log2 sum_c 2^LSE_c and O = sum_c 2^(LSE_c - LSE) O_c, in chunk order.
+// A workgroup is one (sequence, KV head, row block); eight threads per row.
+template <int H16, int D>
+__global__ __launch_bounds__(KNT) void kv_merge_kernel(KvArgs a) {
+  constexpr int TPR = 8, SEG = D / TPR;
+  const int item = (int)blockIdx.x;  // (b * hkv + g) * rblocks + rb
+  const int rb = item % a.rblocks;
+  const int g = (item / a.rblocks) % a.hkv;
+  const int b = item / a.rblocks / a.hkv;
+  int q0, q1;
+  seq_bounds(a.cu_q, b, a.total_q, q0, q1);
+  const int Lq = q1 - q0;
+  const int Lk = min(max(a.seqlens_k[b], 0), a.max_k);
+  const int nch = max(1, (Lk + a.chunk - 1) / a.chunk);
+  if (nch == 1) return;
+  const int row = threadIdx.x / TPR, seg = threadIdx.x % TPR;
+  const int r = 32 * rb + row;
+  const int qpos = r / a.n_rep;
+  if (qpos >= Lq || row >= a.rows) return;
+  const int h = g * a.n_rep + (r - qpos * a.n_rep);
+  const size_t slot0 = (size_t)item * a.nchunk;
+  float mx = -INFINITY;
+  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.part_lse[(slot0 + c) * a.rows + row]);
+  f32x4_t acc[SEG / 4];
+#pragma unroll
+  for (int e = 0; e < SEG / 4; ++e) acc[e] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (mx != -INFINITY) {
+    for (int c = 0; c < nch; ++c) {
+      const size_t sl = slot0 + c;
+      const float w = fast_exp2(a.part_lse[sl * a.rows + row] - mx);
+      wsum += w;
+      const f32x4_t* src = (const f32x4_t*)(a.part_o + (sl * a.rows + row) * D + seg * SEG);
+#pragma unroll
+      for (int e = 0; e < SEG / 4; ++e) acc[e] += w * src[e];
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  uint16_t* dst = (uint16_t*)a.out + ((size_t)(q0 + qpos) * a.hq + h) * D + seg * SEG;
+#pragma unroll
+  for (int e = 0; e < SEG / 4; ++e) {
+    const f32x4_t x = acc[e] * inv;
+    *(u32x2_t*)(dst + 4 * e) = (u32x2_t){pack16<H16>(x[0], x[1]), pack16<H16>(x[2], x[3])};
+  }
+  if (seg == 0)
+    a.lse[(size_t)h * a.total_q + q0 + qpos] = wsum > 0.f ? (mx + __builtin_log2f(wsum)) * kLn2 : -INFINITY;
+}
+
+template <int H16, int D, bool CAUSAL>
+hipError_t launch_kv_t(const KvArgs& a, hipStream_t st) {
+  const int64_t items = (int64_t)a.batch * a.hkv * a.rblocks * a.nchunk;
+  auto kern = (1 << a.page_shift) >= KvShape<D>::KB ? kv_decode_kernel<H16, D, CAUSAL, true>
+                                                    : kv_decode_kernel<H16, D, CAUSAL, false>;
+  const int grid = resident_grid((const void*)kern, KNT, (items + 3) / 4);
+  if (grid <= 0) return hipErrorInvalidConfiguration;
+  timing_before(st, H16 == 2 ? "kvcache_f16" : "kvcache_bf16");
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(KNT), 0, st, a);
+  timing_after(st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nchunk <= 1) return e;
+  timing_before(st, "kvcache_merge");
+  hipLaunchKernelGGL((kv_merge_kernel<H16, D>), dim3((unsigned)(items / a.nchunk)), dim3(KNT), 0, st, a);
+  timing_after(st);
+  return hipGetLastError();
+}
+
+template <int H16, int D>
+hipError_t launch_kv_d(const KvArgs& a, hipStream_t st) {
+  return a.causal ? launch_kv_t<H16, D, true>(a, st) : launch_kv_t<H16, D, false>(a, st);
+}
+
+}  // namespace
+
+int kv_block_n(int d) { return d == 64 ? KvShape<64>::KB : KvShape<128>::KB; }
+
+hipError_t launch_kvcache(const KvArgs& a, hipStream_t st) {
+  if (a.h16 == 2) return a.d == 64 ? launch_kv_d<2, 64>(a, st) : launch_kv_d<2, 128>(a, st);
+  return a.d == 64 ? launch_kv_d<1, 64>(a, st) : launch_kv_d<1, 128>(a, st);
+}
+
+}  // namespace va

@@ -140,3 +140,31 @@ def decode_lengths(seed: int = 11, batch: int = DECODE_BATCH, max_k: int = DECOD
 
 
 DECODE_SHAPE = dict(hq=32, hkv=8, d=128, causal=True, page_size=64)
+
+
+def decode_device_inputs(device, seed: int = 11) -> dict:
+    """The decode-step workload on ``device``: lengths and pages from the seeded layout, Q and
+    the caches N(0, 1) drawn on the device from a seeded generator and rounded to bf16, the
+    slots past each sequence's last key set to NaN.  Keys: lens_k, bt (host), n_pages, q, kc,
+    vc, cu, sk, btd (device)."""
+    import torch
+
+    lens_k = decode_lengths(seed)
+    B = len(lens_k)
+    sh = DECODE_SHAPE
+    ps = sh["page_size"]
+    bt, n_pages = page_layout(seed, lens_k, ps, 0)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    q = torch.randn((B, sh["hq"], sh["d"]), generator=g, device=device).to(torch.bfloat16)
+    caches = [torch.randn((n_pages, ps, sh["hkv"], sh["d"]), generator=g, device=device).to(torch.bfloat16)
+              for _ in range(2)]
+    for b in range(B):
+        n = int(lens_k[b])
+        if n % ps:
+            for cache in caches:
+                cache[int(bt[b, n // ps]), n % ps:] = float("nan")
+    return dict(lens_k=lens_k, bt=bt, n_pages=n_pages, q=q, kc=caches[0], vc=caches[1],
+                cu=torch.arange(B + 1, dtype=torch.int32, device=device),
+                sk=torch.from_numpy(lens_k.astype(np.int32)).to(device),
+                btd=torch.from_numpy(bt).to(device))
