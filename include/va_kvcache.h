@@ -27,8 +27,9 @@
  * How.  One wave per (sequence, KV head, 32 rows of (new token, query head),
  * chunk of keys): every K/V byte of a KV head is read once for all the query
  * heads of its group; long caches are split over chunks whose partial
- * results a second kernel merges in chunk order (deterministic).  The step
- * is bound by HBM bandwidth (K and V read once).
+ * results a last kernel merges in chunk order (deterministic).  A first
+ * one-workgroup kernel lists the chunks that have work.  The step is bound
+ * by HBM bandwidth (K and V read once).
  *
  * Memory safety against bad metadata: a sequence's length is clamped to
  * [0, min(max_seqlen_k, block_table_stride * page_size)], page indices to
@@ -51,8 +52,10 @@ extern "C" {
 #endif
 
 /*
- * Bytes of device workspace va_kvcache_fwd needs (0: none; then `workspace`
- * may be NULL).  The split of long caches into chunks, and so this size,
+ * Bytes of device workspace va_kvcache_fwd needs: the work list (a planner
+ * kernel lists the (sequence, key chunk) pairs that have work, so the waves
+ * share them evenly) and, when caches can be longer than one chunk, float32
+ * partial results.  The split of long caches into chunks, and so this size,
  * depends only on these arguments.  Returns 0 for arguments the call would
  * reject.
  */
@@ -68,6 +71,7 @@ size_t va_kvcache_fwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_
  *                     max_seqlen_k: stride * page_size >= max_seqlen_k
  *   page_size         a power of two, 1 .. 2^20;  num_pages > 0
  *   dtype             VA_BF16 or VA_F16 (VA_F32: VA_ERR_UNSUPPORTED); head_dim 64 or 128
+ *   workspace         device memory, 256-byte aligned, of at least the size above
  * Returns VA_ERR_INVALID for a NULL required pointer, a misaligned buffer,
  * a non-positive size, Hq % Hkv != 0, a bad page_size / num_pages / stride,
  * a non-finite or non-positive scale, causal not 0/1; VA_ERR_UNSUPPORTED for

@@ -279,6 +279,9 @@ def _kv(lib, **kw):
     (dict(causal=2), INVALID),
     (dict(scale=0.0), INVALID),
     (dict(kc=P + 8), INVALID),         # misaligned cache
+    (dict(ws=None), INVALID),
+    (dict(ws=P + 64), INVALID),        # misaligned workspace
+    (dict(wsb=16), WORKSPACE),
     (dict(dt=F32), UNSUPPORTED),
     (dict(d=96), UNSUPPORTED),
     (dict(mq=1 << 20, hq=64, hkv=8), UNSUPPORTED),  # a sequence's queries span 2^31 bytes
@@ -293,15 +296,18 @@ def test_kvcache_workspace_size(lib):
     assert f(0, 1, 128, 8, 2, 128, BF16) == 0
     assert f(2, 1, 128, 8, 2, 128, F32) == 0         # not a decode dtype
     assert f(2, 1, 128, 8, 3, 128, BF16) == 0
+
+    def plan(batch, nchunk):  # planner header + a 32-byte entry per possible chunk
+        return 256 + _r(batch * nchunk * 32)
     # chunks of at least 256 keys: a cache that fits one chunk needs no partials
-    assert f(2, 1, 256, 8, 2, 128, BF16) == 0
-    assert f(2, 1, 0, 8, 2, 128, F16) == 0
+    assert f(2, 1, 256, 8, 2, 128, BF16) == plan(2, 1)
+    assert f(2, 1, 0, 8, 2, 128, F16) == plan(2, 1)
     # 4 KV heads x 2 sequences = 8 row blocks want 1024 chunks each: 512 keys split into
     # two of 256; partial rows per slot = n_rep * max_q = 4
     slots = 2 * 4 * 1 * 2
-    assert f(2, 1, 512, 16, 4, 128, BF16) == _r(slots * 4 * 128 * 4) + _r(slots * 4 * 4)
+    assert f(2, 1, 512, 16, 4, 128, BF16) == plan(2, 2) + _r(slots * 4 * 128 * 4) + _r(slots * 4 * 4)
     # 12 new tokens x 4 heads per KV head = 48 rows: two row blocks of 32 rows
     slots = 2 * 4 * 2 * 2
-    assert f(2, 12, 512, 16, 4, 64, F16) == _r(slots * 32 * 64 * 4) + _r(slots * 32 * 4)
+    assert f(2, 12, 512, 16, 4, 64, F16) == plan(2, 2) + _r(slots * 32 * 64 * 4) + _r(slots * 32 * 4)
     # a large batch keeps whole caches in one chunk when that already gives 8192 waves
-    assert f(8192, 1, 4000, 8, 1, 128, BF16) == 0
+    assert f(8192, 1, 4000, 8, 1, 128, BF16) == plan(8192, 1)

@@ -181,16 +181,14 @@ def kvcache_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if out.shape != q.shape or out.dtype != q.dtype or lse.shape != (hq, tq) or lse.dtype != torch.float32:
         raise ValueError("out/lse have the wrong shape or dtype")
     need = lib.va_kvcache_fwd_workspace_size(batch, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, dt)
-    if workspace is None and need > 0:
-        workspace = torch.empty(int(need), dtype=torch.uint8, device=q.device)
-    wptr, wbytes = (0, 0) if workspace is None else (workspace.data_ptr(),
-                                                     workspace.numel() * workspace.element_size())
-    if workspace is not None:
-        _need_dev("workspace", workspace, q.device)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
+    _need_dev("workspace", workspace, q.device)
     st = lib.va_kvcache_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cu_seqlens_q.data_ptr(),
                             seqlens_k.data_ptr(), block_table.data_ptr(), block_table.shape[1], page_size,
                             n_pages, int(max_seqlen_q), int(max_seqlen_k), scale, int(bool(causal)),
-                            out.data_ptr(), lse.data_ptr(), wptr or None, wbytes, batch, tq, hq, hkv, d, dt,
+                            out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), batch, tq, hq, hkv, d, dt,
                             _stream(q.device))
     _raise(st, lib)
     return out, lse

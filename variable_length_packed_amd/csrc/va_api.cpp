@@ -181,7 +181,8 @@ size_t bwd_workspace(int batch, int total_q, int total_k, int max_q, int max_k, 
 constexpr int64_t kKvWaves = 8192;
 struct KvLayout {
   int rblocks = 1, rows = 1, chunk = 1, nchunk = 1;
-  size_t part_o_bytes = 0, part_lse_bytes = 0;
+  size_t plan_bytes = 0, part_o_bytes = 0, part_lse_bytes = 0;
+  size_t total() const { return plan_bytes + part_o_bytes + part_lse_bytes; }
 };
 KvLayout kv_layout(int batch, int max_q, int max_k, int hq, int hkv, int d) {
   KvLayout L;
@@ -202,6 +203,8 @@ KvLayout kv_layout(int batch, int max_q, int max_k, int hq, int hkv, int d) {
     L.part_o_bytes = round_up(slots * L.rows * d * sizeof(float));
     L.part_lse_bytes = round_up(slots * L.rows * sizeof(float));
   }
+  // the planner's header and chunk list (at most nchunk entries per sequence)
+  L.plan_bytes = round_up(256) + round_up((size_t)batch * L.nchunk * sizeof(va::KvChunk));
   return L;
 }
 
@@ -435,7 +438,7 @@ size_t va_kvcache_fwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_
                                      va_dtype dtype) {
   if (!kv_args_ok(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, dtype)) return 0;
   const KvLayout L = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
-  return L.part_o_bytes + L.part_lse_bytes;
+  return L.total();
 }
 
 va_status va_kvcache_fwd(const void* q, const void* k_cache, const void* v_cache,
@@ -473,20 +476,20 @@ va_status va_kvcache_fwd(const void* q, const void* k_cache, const void* v_cache
   if (!kv_args_ok(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, dtype))
     return fail(VA_ERR_UNSUPPORTED, "max_seqlen_q * num_heads_q * head_dim * 2 must be < 2^31");
   const KvLayout L = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
-  const size_t need = L.part_o_bytes + L.part_lse_bytes;
-  if (need > 0) {
-    if (!workspace) return fail(VA_ERR_INVALID, "workspace is NULL but %zu bytes are needed", need);
-    if (((uintptr_t)workspace) % kAlign != 0)
-      return fail(VA_ERR_INVALID, "workspace must be 256-byte aligned");
-    if (workspace_bytes < need)
-      return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
-  }
+  const size_t need = L.total();
+  if (!workspace) return fail(VA_ERR_INVALID, "workspace is NULL");
+  if (((uintptr_t)workspace) % kAlign != 0) return fail(VA_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
   va::KvArgs a{};
   a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
   a.cu_q = cu_seqlens_q; a.seqlens_k = seqlens_k; a.block_table = block_table;
   a.out = out; a.lse = lse;
-  a.part_o = need > 0 ? (float*)workspace : nullptr;
-  a.part_lse = need > 0 ? (float*)((char*)workspace + L.part_o_bytes) : nullptr;
+  char* w = (char*)workspace;
+  a.plan = (int32_t*)w;
+  a.chunks = (va::KvChunk*)(w + round_up(256));
+  a.part_o = L.part_o_bytes > 0 ? (float*)(w + L.plan_bytes) : nullptr;
+  a.part_lse = L.part_lse_bytes > 0 ? (float*)(w + L.plan_bytes + L.part_o_bytes) : nullptr;
   a.batch = batch; a.total_q = total_q;
   a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = num_heads_q / num_heads_kv; a.d = head_dim;
   a.bt_stride = block_table_stride;

@@ -126,11 +126,15 @@ hipError_t launch_bwd(const BwdArgs& a, const PlanSet& ps, int64_t max_q_items, 
 // Decode steps against a paged KV cache.  A work item (one wave) is one
 // (sequence, KV head, row block, key chunk): 32 rows = (new token, query
 // head of the KV head's group) pairs, keys [chunk * c, chunk * (c + 1)).
-// Items are numbered ((b * hkv + g) * rblocks + rb) * nchunk + c.  A
-// sequence with more than one chunk writes float32 partials to the slot of
-// its item, [slot][rows][d] and [slot][rows], and the merge kernel combines
-// its chunks in order.
+// A planner kernel lists the (sequence, chunk) pairs that have work; items
+// are (list entry, row block, KV head), KV heads fastest.  A sequence with
+// more than one chunk writes float32 partials to slot
+// ((b * hkv + g) * rblocks + rb) * nchunk + c, [slot][rows][d] and
+// [slot][rows], and the merge kernel combines its chunks in order.
 // ---------------------------------------------------------------------------
+struct KvChunk {
+  int32_t b, c, q0, q1, lk, pad0, pad1, pad2;  // sequence, chunk, its query rows, its cached keys
+};
 struct KvArgs {
   const void* q;             // [total_q, hq, d]
   const void* k_cache;       // [num_pages, page_size, hkv, d]
@@ -142,6 +146,8 @@ struct KvArgs {
   float* lse;                // [hq, total_q]
   float* part_o;
   float* part_lse;
+  int32_t* plan;             // [0] = entries in `chunks` (written by the planner)
+  KvChunk* chunks;           // [batch * nchunk] at most
   int32_t batch, total_q, hq, hkv, n_rep, d;
   int32_t bt_stride, page_shift, num_pages;
   int32_t max_k;             // keys of a sequence are capped here (max_seqlen_k and the table's reach)

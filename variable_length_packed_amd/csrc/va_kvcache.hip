@@ -59,25 +59,31 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
   uint16_t* sk = sk_all[wid];
   uint16_t* sv = sv_all[wid];
 
-  // ---- items: (sequence, KV head, row block, chunk), taken by each wave with a
-  // grid stride; waves never synchronise, so each runs its items alone
-  const int NC = a.nchunk, RB = a.rblocks;
-  const int n_items = a.batch * a.hkv * RB * NC;
-  for (int item = (int)blockIdx.x * 4 + wid; item < n_items; item += (int)gridDim.x * 4) {
-  const int c = item % NC;
-  int t = item / NC;
-  const int rb = t % RB;
-  t /= RB;
-  const int g = t % a.hkv;
-  const int b = t / a.hkv;
-
-  int q0, q1;
-  seq_bounds(a.cu_q, b, a.total_q, q0, q1);
+  // ---- items: (chunk of the planner's list, row block, KV head), KV heads
+  // fastest, so the waves of a workgroup read the same keys of neighbouring
+  // heads (adjacent in each cache row) at the same time.  The list holds
+  // only real chunks, so a static round robin gives every wave nearly the
+  // same work; a wave prefetches its next item's entry during the current one.
+  // Waves never synchronise: each runs its items alone.
+  const int RB = a.rblocks;
+  const int per_chunk = RB * a.hkv;
+  const int n_items = uniform(a.plan[0]) * per_chunk;
+  const int n_waves = (int)gridDim.x * 4;
+  auto entry = [&](int it) {
+    return it < n_items ? a.chunks[it / per_chunk] : (KvChunk){0, 0, 0, 0, 0, 0, 0, 0};
+  };
+  KvChunk nxt = entry((int)blockIdx.x * 4 + wid);
+  for (int item = (int)blockIdx.x * 4 + wid; item < n_items; item += n_waves) {
+  const KvChunk ent = nxt;
+  nxt = entry(item + n_waves);
+  const int g = item % a.hkv;
+  const int rb = (item / a.hkv) % RB;
+  const int b = uniform(ent.b), c = uniform(ent.c);
+  const int q0 = uniform(ent.q0), q1 = uniform(ent.q1), Lk = uniform(ent.lk);
+  const size_t slot = (((size_t)b * a.hkv + g) * RB + rb) * a.nchunk + c;  // partial slot of this chunk
   const int Lq = q1 - q0;
   if (32 * rb >= Lq * a.n_rep) continue;  // no rows in this block
-  const int Lk = min(max(a.seqlens_k[b], 0), a.max_k);
   const int nch = max(1, (Lk + a.chunk - 1) / a.chunk);
-  if (c >= nch) continue;
   const int off = Lk - Lq;
 
   // this lane's row: new token qpos, query head h
@@ -254,7 +260,6 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
       }
     if (row_ok && hh == 0) a.lse[(size_t)h * a.total_q + q0 + qpos] = lse2 * kLn2;
   } else if (row_ok && r32 < a.rows) {
-    const size_t slot = (size_t)item;  // ((b * hkv + g) * rblocks + rb) * nchunk + c
     float* po = a.part_o + (slot * a.rows + r32) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -267,6 +272,44 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
     if (hh == 0) a.part_lse[slot * a.rows + r32] = lse2;
   }
   }
+}
+
+// The planner: one workgroup lists every (sequence, chunk) pair that has
+// work, in sequence order, with the sequence's bounds (clamped as in the
+// decode kernel), and stores the count in plan[0].  A sequence with new
+// tokens has max(1, ceil(Lk / chunk)) chunks (an empty cache still owes its
+// rows O = 0 and LSE = -inf); one without has none.
+constexpr int kPlanThreads = 1024;
+__global__ __launch_bounds__(kPlanThreads) void kv_plan_kernel(KvArgs a) {
+  __shared__ int scan[kPlanThreads];
+  __shared__ int s_base;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_base = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < a.batch; b0 += kPlanThreads) {
+    const int b = b0 + tid;
+    int q0 = 0, q1 = 0, lk = 0, cnt = 0;
+    if (b < a.batch) {
+      seq_bounds(a.cu_q, b, a.total_q, q0, q1);
+      lk = min(max(a.seqlens_k[b], 0), a.max_k);
+      cnt = q1 > q0 ? max(1, (lk + a.chunk - 1) / a.chunk) : 0;
+    }
+    // inclusive scan of the counts (Hillis-Steele over the workgroup)
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int o = 1; o < kPlanThreads; o <<= 1) {
+      const int add = tid >= o ? scan[tid - o] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    const int base = s_base + scan[tid] - cnt;
+    for (int c = 0; c < cnt; ++c) a.chunks[base + c] = (KvChunk){b, c, q0, q1, lk, 0, 0, 0};
+    __syncthreads();
+    if (tid == kPlanThreads - 1) s_base += scan[tid];
+    __syncthreads();
+  }
+  if (tid == 0) a.plan[0] = s_base;
 }
 
 // Combines the chunks of every row block whose sequence has more than one:
@@ -325,10 +368,15 @@ hipError_t launch_kv_t(const KvArgs& a, hipStream_t st) {
                                                     : kv_decode_kernel<H16, D, CAUSAL, false>;
   const int grid = resident_grid((const void*)kern, KNT, (items + 3) / 4);
   if (grid <= 0) return hipErrorInvalidConfiguration;
+  timing_before(st, "kvcache_plan");
+  hipLaunchKernelGGL(kv_plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+  timing_after(st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   timing_before(st, H16 == 2 ? "kvcache_f16" : "kvcache_bf16");
   hipLaunchKernelGGL(kern, dim3(grid), dim3(KNT), 0, st, a);
   timing_after(st);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess || a.nchunk <= 1) return e;
   timing_before(st, "kvcache_merge");
   hipLaunchKernelGGL((kv_merge_kernel<H16, D>), dim3((unsigned)(items / a.nchunk)), dim3(KNT), 0, st, a);
