@@ -77,7 +77,7 @@ def measured_traffic(kernel: str, workload: str):
     return None if e is None else e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, min_seconds: float = 10.0, max_reps: int = 3):
+def cpu_baseline(w, min_seconds: float = 10.0, max_reps: int = 10):
     """The fp64 oracle (forward + backward of every sequence) timed on the host cores."""
     import oracle  # test infrastructure: only this leg of the bench uses it
     try:
@@ -115,6 +115,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="3", help="config id for the step (default 3)")
+    ap.add_argument("--sections", default="qwen,packing,bias,decode",
+                    help="comma list of the sections to run besides the main step "
+                         "(qwen, packing, bias, decode; default all)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 3 device-to-device copies of MIB MiB (a kernel of known HBM "
                          "traffic, to scale hardware byte counters against)")
@@ -140,6 +143,10 @@ def main() -> int:
         d["bias"] = t(w.bias) if w.bias is not None else None
         d["dout"] = t(w.dout) if (with_dout and w.dout is not None) else None
         return d
+
+    secs = {t for t in args.sections.split(",") if t}
+    ms_fwd2 = tf2 = w2 = None
+    packing = bias_grad = kvcache_decode = None
 
     w = config(int(args.workload), with_dout=True)
     x = dev_inputs(w)
@@ -215,110 +222,156 @@ def main() -> int:
                 "algorithmic_flops_per_launch": fl, "avg_launch_ms": round(tot / n, 5)}
 
     # the Qwen2.5-0.5B-shaped forward (20 sequences U[64, 1024]) as a second forward figure
-    w2 = config(2, with_dout=False)
-    x2 = dev_inputs(w2, with_dout=False)
-    o2 = torch.empty_like(x2["q"])
-    l2 = torch.empty((w2.hq, w2.total_q), dtype=torch.float32, device=dev)
-    ws2 = torch.empty(va.va_varlen_fwd_workspace_size(w2.batch, w2.total_q, w2.total_k, w2.max_q,
-                                                      w2.max_k, w2.hq, w2.hkv, w2.d,
-                                                      torch.bfloat16),
-                      dtype=torch.uint8, device=dev)
+    if "qwen" in secs:
+        w2 = config(2, with_dout=False)
+        x2 = dev_inputs(w2, with_dout=False)
+        o2 = torch.empty_like(x2["q"])
+        l2 = torch.empty((w2.hq, w2.total_q), dtype=torch.float32, device=dev)
+        ws2 = torch.empty(va.va_varlen_fwd_workspace_size(w2.batch, w2.total_q, w2.total_k, w2.max_q,
+                                                          w2.max_k, w2.hq, w2.hkv, w2.d,
+                                                          torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
 
-    def fwd2():
-        va.va_varlen_fwd(x2["q"], x2["k"], x2["v"], x2["cu_q"], x2["cu_k"], w2.max_q, w2.max_k,
-                         w2.scale, True, out=o2, lse=l2, workspace=ws2)
+        def fwd2():
+            va.va_varlen_fwd(x2["q"], x2["k"], x2["v"], x2["cu_q"], x2["cu_k"], w2.max_q, w2.max_k,
+                             w2.scale, True, out=o2, lse=l2, workspace=ws2)
 
-    for _ in range(args.warmup):
-        fwd2()
-    ms_fwd2 = timed(fwd2, args.steps)
-    tf2 = count.fwd_flops(w2) / (ms_fwd2 * 1e-3) / 1e12
+        for _ in range(args.warmup):
+            fwd2()
+        ms_fwd2 = timed(fwd2, args.steps)
+        tf2 = count.fwd_flops(w2) / (ms_fwd2 * 1e-3) / 1e12
 
-    # the packing steps either side of the path: config 3's rows right-padded to 2048
-    S = 2048
-    mask = padding_mask(0, w.batch, S, "right", lengths=list(w.lens_q))
-    dmask = torch.from_numpy(mask).to(dev)
-    pq = torch.randn(w.batch, S, w.hq, w.d, device=dev).to(torch.bfloat16)
-    pk = torch.randn(w.batch, S, w.hkv, w.d, device=dev).to(torch.bfloat16)
-    pv = torch.randn(w.batch, S, w.hkv, w.d, device=dev).to(torch.bfloat16)
-    meta = va.pack_metadata(dmask)
-    cu_p, _, idx_p, _, inv_p = meta
-    T = w.total_q
-    packed = va.unpad([pq, pk, pv], idx_p, cu_p, packed_rows=T)
+    if "packing" in secs:
+        # the packing steps either side of the path: config 3's rows right-padded to 2048
+        S = 2048
+        mask = padding_mask(0, w.batch, S, "right", lengths=list(w.lens_q))
+        dmask = torch.from_numpy(mask).to(dev)
+        pq = torch.randn(w.batch, S, w.hq, w.d, device=dev).to(torch.bfloat16)
+        pk = torch.randn(w.batch, S, w.hkv, w.d, device=dev).to(torch.bfloat16)
+        pv = torch.randn(w.batch, S, w.hkv, w.d, device=dev).to(torch.bfloat16)
+        meta = va.pack_metadata(dmask)
+        cu_p, _, idx_p, _, inv_p = meta
+        T = w.total_q
+        packed = va.unpad([pq, pk, pv], idx_p, cu_p, packed_rows=T)
 
-    def do_meta():
-        va.pack_metadata(dmask)
+        def do_meta():
+            va.pack_metadata(dmask)
 
-    def do_unpad():
-        va.unpad([pq, pk, pv], idx_p, cu_p, packed_rows=T)
+        def do_unpad():
+            va.unpad([pq, pk, pv], idx_p, cu_p, packed_rows=T)
 
-    def do_pad():
-        va.pad([packed[0]], inv_p, w.batch, S)
+        def do_pad():
+            va.pad([packed[0]], inv_p, w.batch, S)
 
-    for f in (do_meta, do_unpad, do_pad):
-        f()
-    torch.cuda.synchronize()
-    # kernel time by the library's event timing (the Python marshalling of a call
-    # takes longer than these kernels, so wall time per call would measure the host)
-    va.va_timing_start(16 * args.steps + 16)
-    for _ in range(args.steps):
-        do_meta()
-        do_unpad()
-        do_pad()
-    pt = va.va_timing_stop()
-    kavg = lambda *names: sum(pt[n][1] / pt[n][0] for n in names if n in pt)
-    ms_meta = kavg("pack_count", "pack_scan", "pack_index")
-    ms_unpad, ms_pad = kavg("unpad"), kavg("pad")
-    row_q, row_kv = w.hq * w.d * 2, w.hkv * w.d * 2
-    b_unpad = T * (row_q + 2 * row_kv) * 2 + T * 4          # rows read and written, indices read
-    b_pad = T * row_q + w.batch * S * row_q + w.batch * S * 4  # packed rows read, padded rows and inverse
-    gbs = lambda b, ms: round(b / (ms * 1e-3) / 1e9, 1)
-    packing = {"workload": f"config-3 rows right-padded to {S}: Q [16,{S},14,64], K/V [16,{S},2,64] bf16",
-               "timing": "library HIP events around each kernel, averaged over the timed calls",
-               "metadata_ms": round(ms_meta, 5),
-               "unpad_qkv": {"ms": round(ms_unpad, 5), "bytes": b_unpad, "GB_s": gbs(b_unpad, ms_unpad),
-                             "frac_hbm": round(b_unpad / (ms_unpad * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-               "pad_out": {"ms": round(ms_pad, 5), "bytes": b_pad, "GB_s": gbs(b_pad, ms_pad),
-                           "frac_hbm": round(b_pad / (ms_pad * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+        for f in (do_meta, do_unpad, do_pad):
+            f()
+        torch.cuda.synchronize()
+        # kernel time by the library's event timing (the Python marshalling of a call
+        # takes longer than these kernels, so wall time per call would measure the host)
+        va.va_timing_start(16 * args.steps + 16)
+        for _ in range(args.steps):
+            do_meta()
+            do_unpad()
+            do_pad()
+        pt = va.va_timing_stop()
+        kavg = lambda *names: sum(pt[n][1] / pt[n][0] for n in names if n in pt)
+        ms_meta = kavg("pack_count", "pack_scan", "pack_index")
+        ms_unpad, ms_pad = kavg("unpad"), kavg("pad")
+        row_q, row_kv = w.hq * w.d * 2, w.hkv * w.d * 2
+        b_unpad = T * (row_q + 2 * row_kv) * 2 + T * 4          # rows read and written, indices read
+        b_pad = T * row_q + w.batch * S * row_q + w.batch * S * 4  # packed rows read, padded rows and inverse
+        gbs = lambda b, ms: round(b / (ms * 1e-3) / 1e9, 1)
+        packing = {"workload": f"config-3 rows right-padded to {S}: Q [16,{S},14,64], K/V [16,{S},2,64] bf16",
+                   "timing": "library HIP events around each kernel, averaged over the timed calls",
+                   "metadata_ms": round(ms_meta, 5),
+                   "unpad_qkv": {"ms": round(ms_unpad, 5), "bytes": b_unpad, "GB_s": gbs(b_unpad, ms_unpad),
+                                 "frac_hbm": round(b_unpad / (ms_unpad * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+                   "pad_out": {"ms": round(ms_pad, 5), "bytes": b_pad, "GB_s": gbs(b_pad, ms_pad),
+                               "frac_hbm": round(b_pad / (ms_pad * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
 
-    # bias gradient: the graph-encoder workload (512 seqs U[1,256], 8/8 heads, d64, non-causal,
-    # bf16) with a per-pair bias grid [512, 8, 256, 256], forward + backward with dbias
-    w4 = config(4, dtype="bf16", bias="per_key", with_dout=True)  # Q/K/V/dO; the grid is drawn on device
-    x4 = dev_inputs(w4)
-    G = 256
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(4)
-    grid = (0.5 * torch.randn(w4.batch * w4.hq * G * G, generator=gen, device=dev)).to(torch.bfloat16)
-    gstr = (w4.hq * G * G, G * G, G, 1)
-    dgrid = torch.zeros(grid.numel(), dtype=torch.float32, device=dev)
-    o4 = torch.empty_like(x4["q"])
-    l4 = torch.empty((w4.hq, w4.total_q), dtype=torch.float32, device=dev)
-    g4 = [torch.empty(x4[n].shape, dtype=torch.float32, device=dev) for n in "qkv"]
-    wf4 = torch.empty(va.va_varlen_fwd_workspace_size(w4.batch, w4.total_q, w4.total_k, w4.max_q, w4.max_k,
-                                                      w4.hq, w4.hkv, w4.d, torch.bfloat16),
-                      dtype=torch.uint8, device=dev)
-    wb4 = torch.empty(va.va_varlen_bwd_workspace_size(w4.batch, w4.total_q, w4.total_k, w4.max_q, w4.max_k,
-                                                      w4.hq, w4.hkv, w4.d, torch.bfloat16, torch.float32),
-                      dtype=torch.uint8, device=dev)
+    if "bias" in secs:
+        # bias gradient: the graph-encoder workload (512 seqs U[1,256], 8/8 heads, d64, non-causal,
+        # bf16) with a per-pair bias grid [512, 8, 256, 256], forward + backward with dbias
+        w4 = config(4, dtype="bf16", bias="per_key", with_dout=True)  # Q/K/V/dO; the grid is drawn on device
+        x4 = dev_inputs(w4)
+        G = 256
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(4)
+        grid = (0.5 * torch.randn(w4.batch * w4.hq * G * G, generator=gen, device=dev)).to(torch.bfloat16)
+        gstr = (w4.hq * G * G, G * G, G, 1)
+        dgrid = torch.zeros(grid.numel(), dtype=torch.float32, device=dev)
+        o4 = torch.empty_like(x4["q"])
+        l4 = torch.empty((w4.hq, w4.total_q), dtype=torch.float32, device=dev)
+        g4 = [torch.empty(x4[n].shape, dtype=torch.float32, device=dev) for n in "qkv"]
+        wf4 = torch.empty(va.va_varlen_fwd_workspace_size(w4.batch, w4.total_q, w4.total_k, w4.max_q, w4.max_k,
+                                                          w4.hq, w4.hkv, w4.d, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+        wb4 = torch.empty(va.va_varlen_bwd_workspace_size(w4.batch, w4.total_q, w4.total_k, w4.max_q, w4.max_k,
+                                                          w4.hq, w4.hkv, w4.d, torch.bfloat16, torch.float32),
+                          dtype=torch.uint8, device=dev)
 
-    def step4():
-        va.va_varlen_fwd(x4["q"], x4["k"], x4["v"], x4["cu_q"], x4["cu_k"], w4.max_q, w4.max_k, w4.scale,
-                         False, grid, gstr, out=o4, lse=l4, workspace=wf4)
-        va.va_varlen_bwd(x4["dout"], x4["q"], x4["k"], x4["v"], o4, l4, x4["cu_q"], x4["cu_k"], w4.max_q,
-                         w4.max_k, w4.scale, False, grid, gstr, dq=g4[0], dk=g4[1], dv=g4[2], workspace=wb4,
-                         dbias=dgrid, dbias_stride=gstr)
+        def step4():
+            va.va_varlen_fwd(x4["q"], x4["k"], x4["v"], x4["cu_q"], x4["cu_k"], w4.max_q, w4.max_k, w4.scale,
+                             False, grid, gstr, out=o4, lse=l4, workspace=wf4)
+            va.va_varlen_bwd(x4["dout"], x4["q"], x4["k"], x4["v"], o4, l4, x4["cu_q"], x4["cu_k"], w4.max_q,
+                             w4.max_k, w4.scale, False, grid, gstr, dq=g4[0], dk=g4[1], dv=g4[2], workspace=wb4,
+                             dbias=dgrid, dbias_stride=gstr)
 
-    for _ in range(2):
-        step4()
-    ms4 = timed(step4, max(3, args.steps // 4))
-    valid = int(sum(int(L) * int(L) for L in w4.lens_q)) * w4.hq
-    fl4 = count.fwd_flops(w4) + count.bwd_flops(w4)
-    bias_bytes = valid * (2 + 2 + 2 + 4)  # bias read by the forward, dK/dV and dQ passes; dbias written
-    bias_grad = {"workload": "graph encoder, 512 seqs U[1,256], 8/8 heads, d64, non-causal, bf16, per-pair "
-                             "bias grid [512,8,256,256], fwd + bwd with dbias (float32, same layout)",
-                 "ms_per_step": round(ms4, 5), "tflops": round(fl4 / (ms4 * 1e-3) / 1e12, 2),
-                 "valid_bias_elements": valid, "bias_stream_bytes": bias_bytes,
-                 "bias_stream_GB_s": round(bias_bytes / (ms4 * 1e-3) / 1e9, 1)}
-    del grid, dgrid
+        for _ in range(2):
+            step4()
+        ms4 = timed(step4, max(3, args.steps // 4))
+        valid = int(sum(int(L) * int(L) for L in w4.lens_q)) * w4.hq
+        fl4 = count.fwd_flops(w4) + count.bwd_flops(w4)
+        bias_bytes = valid * (2 + 2 + 2 + 4)  # bias read by the forward, dK/dV and dQ passes; dbias written
+        bias_grad = {"workload": "graph encoder, 512 seqs U[1,256], 8/8 heads, d64, non-causal, bf16, per-pair "
+                                 "bias grid [512,8,256,256], fwd + bwd with dbias (float32, same layout)",
+                     "ms_per_step": round(ms4, 5), "tflops": round(fl4 / (ms4 * 1e-3) / 1e12, 2),
+                     "valid_bias_elements": valid, "bias_stream_bytes": bias_bytes,
+                     "bias_stream_GB_s": round(bias_bytes / (ms4 * 1e-3) / 1e9, 1)}
+        del grid, dgrid
+
+    if "decode" in secs:
+        # decode step against a paged KV cache: 128 sequences x 1 new token, cached lengths
+        # U[1, 4096], 32/8 heads, d128, bf16, pages of 64 keys in random order (HBM-bound)
+        from workloads.kvcache import DECODE_SHAPE, decode_device_inputs
+        kv = decode_device_inputs(dev)
+        shk = DECODE_SHAPE
+        Bk = len(kv["lens_k"])
+        mk = int(kv["lens_k"].max())
+        ok = torch.empty_like(kv["q"])
+        lk = torch.empty((shk["hq"], Bk), dtype=torch.float32, device=dev)
+        wk = torch.empty(va.kvcache_fwd_workspace_size(Bk, 1, mk, shk["hq"], shk["hkv"], shk["d"], torch.bfloat16),
+                         dtype=torch.uint8, device=dev)
+        sc_k = 1.0 / float(np.sqrt(shk["d"]))
+
+        def decode():
+            va.kvcache_fwd(kv["q"], kv["kc"], kv["vc"], kv["cu"], kv["sk"], kv["btd"], 1, mk, sc_k, True,
+                           out=ok, lse=lk, workspace=wk)
+
+        for _ in range(3):
+            decode()
+        ms_dec = timed(decode, args.steps)
+        va.va_timing_start(8 * args.steps + 8)
+        for _ in range(args.steps):
+            decode()
+        kt = va.va_timing_stop()
+        kv_bytes = int(kv["lens_k"].sum()) * shk["hkv"] * shk["d"] * 2 * 2  # K and V of every cached key, once
+        io_bytes = 2 * kv["q"].numel() * 2 + lk.numel() * 4                  # Q read, O and LSE written
+        dec_ms = kt["kvcache_bf16"][1] / kt["kvcache_bf16"][0]
+        dec_gbs = (kv_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
+        kvcache_decode = {
+            "workload": "decode step: 128 seqs x 1 new token, cached lengths U[1,4096], 32 q / 8 kv heads, d128, "
+                        "bf16, paged KV (pages of 64 keys, random order)",
+            "ms_per_step": round(ms_dec, 5),
+            "kernels_ms": {k: round(v[1] / v[0], 5) for k, v in kt.items()},
+            "kv_bytes": kv_bytes,
+            "step_GB_s": round((kv_bytes + io_bytes) / (ms_dec * 1e-3) / 1e9, 1),
+            "roofline": {"kernel": "kvcache_bf16", "bound": "hbm", "achieved": round(dec_gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes": kv_bytes + io_bytes,
+                         "traffic": measured_traffic("kvcache_bf16", "decode")},
+        }
+        del kv
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     props = torch.cuda.get_device_properties(dev)
@@ -347,12 +400,14 @@ def main() -> int:
             "bwd": {"ms": round(ms_bwd, 5), "tflops": round(flops_bwd / (ms_bwd * 1e-3) / 1e12, 2),
                     "pct_bf16_peak": round(100 * flops_bwd / (ms_bwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
         },
-        "qwen_shaped_fwd": {"workload": "20 seqs U[64,1024], 14/2 heads, d64, causal, bf16",
-                            "total_tokens": w2.total_q, "ms": round(ms_fwd2, 5),
-                            "tflops": round(tf2, 2), "pct_bf16_peak": round(100 * tf2 / PEAK_BF16_TFLOPS, 2)},
+        "qwen_shaped_fwd": None if w2 is None else {
+            "workload": "20 seqs U[64,1024], 14/2 heads, d64, causal, bf16",
+            "total_tokens": w2.total_q, "ms": round(ms_fwd2, 5),
+            "tflops": round(tf2, 2), "pct_bf16_peak": round(100 * tf2 / PEAK_BF16_TFLOPS, 2)},
         "kernels": kernels,
         "packing": packing,
         "bias_grad": bias_grad,
+        "kvcache_decode": kvcache_decode,
         "roofline": roof,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
