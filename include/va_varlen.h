@@ -20,9 +20,20 @@
  * pull request 118 page notes for single-token decode (section "Key
  * Implementation Points").  No dropout (that page assumes dropout 0).
  *
- * Layouts (all row-major, contiguous, element strides implied):
- *   q, out, dout, dq    [total_q, num_heads_q, head_dim]
- *   k, v, dk, dv        [total_k, num_heads_kv, head_dim]
+ * Layouts (row-major; heads and head_dim elements dense):
+ *   q                   [total_q, num_heads_q, head_dim], token stride qkv_row_stride[0]
+ *   k, v                [total_k, num_heads_kv, head_dim], token strides qkv_row_stride[1], [2]
+ *   out, dout, dq       [total_q, num_heads_q, head_dim], contiguous
+ *   dk, dv              [total_k, num_heads_kv, head_dim], contiguous
+ *   qkv_row_stride      optional HOST int64[3]: elements from one token's row
+ *                       of q (k, v) to the next; NULL = contiguous (num_heads
+ *                       * head_dim).  Each must be >= num_heads * head_dim and
+ *                       keep rows 16-byte aligned (q, k, v bases too), so the
+ *                       Q, K and V slices of one fused projection output
+ *                       [total, (Hq + 2 Hkv) * head_dim] -- the QKV-packed
+ *                       input of the flash_attn_qkvpacked_func call the noether
+ *                       pull request 236 page lists (section "module") -- are
+ *                       read in place, without a copy.
  *   lse                 [num_heads_q, total_q]  float32, natural log
  *   cu_seqlens_q/_k     [batch + 1] int32, device memory, cu[0] = 0,
  *                       non-decreasing, cu[batch] = total_q / total_k
@@ -103,16 +114,19 @@ typedef void* va_stream;
  *                      must be finite and > 0
  *   causal             0 or 1; 1 = bottom-right aligned causal mask
  *   bias, bias_stride  both NULL (no bias) or both non-NULL
+ *   qkv_row_stride     NULL or HOST int64[3] token strides of q, k, v (above)
  *   workspace          device scratch of at least va_varlen_fwd_workspace_size()
  *                      bytes, 256-byte aligned
  *   head_dim           64 or 128
  * Returns VA_ERR_INVALID for a NULL required pointer, exactly one of
  * bias/bias_stride NULL, batch/total/heads/head_dim <= 0, Hq % Hkv != 0,
  * max_seqlen <= 0, a negative stride, a scale that is not finite and > 0, a
- * misaligned workspace; VA_ERR_UNSUPPORTED for head_dim not in {64, 128}, an
- * unknown dtype, or a bias view spanning 2 GiB or more inside one (sequence,
- * head); VA_ERR_WORKSPACE for too small a workspace; VA_ERR_HIP if a launch
- * fails.  A bias with contiguous keys (bias_stride[3] = 1), strides that are
+ * misaligned workspace, a row stride below num_heads * head_dim or rows or
+ * bases of q/k/v not 16-byte aligned; VA_ERR_UNSUPPORTED for head_dim not in
+ * {64, 128}, an unknown dtype, a bias view spanning 2 GiB or more inside one
+ * (sequence, head), or max_seqlen * row stride reaching 2 GiB (the kernels
+ * address one sequence's rows with 32-bit byte offsets); VA_ERR_WORKSPACE for
+ * too small a workspace; VA_ERR_HIP if a launch fails.  A bias with contiguous keys (bias_stride[3] = 1), strides that are
  * multiples of 4 and a base aligned to 4 elements is read 4 keys per load.
  */
 va_status va_varlen_fwd(const void* q, const void* k, const void* v,
@@ -120,6 +134,7 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
                         int32_t max_seqlen_q, int32_t max_seqlen_k,
                         float softmax_scale, int causal,
                         const void* bias, const int64_t* bias_stride,
+                        const int64_t* qkv_row_stride,
                         void* out, float* lse,
                         void* workspace, size_t workspace_bytes,
                         int32_t batch, int32_t total_q, int32_t total_k,
@@ -144,7 +159,8 @@ size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
  * Backward: dq, dk, dv of sum(dout * out) for the forward above, recomputing
  * the softmax from `lse` (the forward's own output) instead of storing it,
  * and optionally the bias gradient.
- *   dout, out          device, `dtype`, [total_q, num_heads_q, head_dim]
+ *   dout, out          device, `dtype`, [total_q, num_heads_q, head_dim], contiguous
+ *   q, k, v            as for the forward, with the same qkv_row_stride
  *   lse                device float32 [num_heads_q, total_q] from va_varlen_fwd
  *   dq                 [total_q, num_heads_q, head_dim] in grad_dtype
  *   dk, dv             [total_k, num_heads_kv, head_dim] in grad_dtype; the
@@ -178,6 +194,7 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
                         int32_t max_seqlen_q, int32_t max_seqlen_k,
                         float softmax_scale, int causal,
                         const void* bias, const int64_t* bias_stride,
+                        const int64_t* qkv_row_stride,
                         void* dq, void* dk, void* dv,
                         float* dbias, const int64_t* dbias_stride,
                         void* workspace, size_t workspace_bytes,

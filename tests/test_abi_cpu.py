@@ -61,12 +61,13 @@ def test_status_strings_and_version(lib):
 
 def _fwd(lib, **kw):
     a = dict(q=P, k=P, v=P, cq=P, ck=P, mq=8, mk=8, scale=0.125, causal=1, bias=None,
-             bstr=None, out=P, lse=P, ws=0x100000, wsb=1 << 30, batch=2, tq=16, tk=16, hq=4,
+             bstr=None, rs=None, out=P, lse=P, ws=0x100000, wsb=1 << 30, batch=2, tq=16, tk=16, hq=4,
              hkv=2, d=64, dt=BF16)
     a.update(kw)
     bstr = _lib.strides_arg(a["bstr"]) if a["bstr"] is not None else None
+    rs = _lib.strides_arg(a["rs"]) if a["rs"] is not None else None
     return lib.va_varlen_fwd(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["mq"], a["mk"], a["scale"],
-                             a["causal"], a["bias"], bstr, a["out"], a["lse"], a["ws"], a["wsb"],
+                             a["causal"], a["bias"], bstr, rs, a["out"], a["lse"], a["ws"], a["wsb"],
                              a["batch"], a["tq"], a["tk"], a["hq"], a["hkv"], a["d"], a["dt"], None)
 
 
@@ -95,6 +96,13 @@ def _fwd(lib, **kw):
     (dict(dt=7), UNSUPPORTED),
     (dict(dt=3), UNSUPPORTED),
     (dict(wsb=16), WORKSPACE),
+    # token strides of q, k, v
+    (dict(rs=(255, 128, 128)), INVALID),       # q rows overlap (below Hq * d = 256)
+    (dict(rs=(256, 128, 100)), INVALID),
+    (dict(rs=(260, 128, 128)), INVALID),       # 520-byte rows: not 16-byte aligned
+    (dict(rs=(258, 128, 128), dt=F32), INVALID),  # float32: 1032-byte rows
+    (dict(k=P + 8), INVALID),                  # misaligned base
+    (dict(rs=(1 << 28, 128, 128), mq=8), UNSUPPORTED),  # 8 rows of 2^29 bytes: past 32-bit offsets
 ])
 def test_fwd_validation(lib, kw, code):
     assert _fwd(lib, **kw) == code
@@ -103,13 +111,14 @@ def test_fwd_validation(lib, kw, code):
 
 def _bwd(lib, **kw):
     a = dict(do=P, q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, mq=8, mk=8, scale=0.125, causal=1,
-             bias=None, bstr=None, dq=P, dk=P, dv=P, db=None, dbstr=None, ws=0x100000, wsb=1 << 30,
-             batch=2, tq=16, tk=16, hq=4, hkv=2, d=64, dt=BF16, gdt=F32)
+             bias=None, bstr=None, rs=None, dq=P, dk=P, dv=P, db=None, dbstr=None, ws=0x100000,
+             wsb=1 << 30, batch=2, tq=16, tk=16, hq=4, hkv=2, d=64, dt=BF16, gdt=F32)
     a.update(kw)
     bstr = _lib.strides_arg(a["bstr"]) if a["bstr"] is not None else None
     dbstr = _lib.strides_arg(a["dbstr"]) if a["dbstr"] is not None else None
+    rs = _lib.strides_arg(a["rs"]) if a["rs"] is not None else None
     return lib.va_varlen_bwd(a["do"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
-                             a["mq"], a["mk"], a["scale"], a["causal"], a["bias"], bstr, a["dq"],
+                             a["mq"], a["mk"], a["scale"], a["causal"], a["bias"], bstr, rs, a["dq"],
                              a["dk"], a["dv"], a["db"], dbstr, a["ws"], a["wsb"], a["batch"], a["tq"],
                              a["tk"], a["hq"], a["hkv"], a["d"], a["dt"], a["gdt"], None)
 
@@ -126,6 +135,8 @@ def _bwd(lib, **kw):
     (dict(dt=F16, gdt=BF16), UNSUPPORTED),
     (dict(gdt=5), UNSUPPORTED),
     (dict(wsb=16), WORKSPACE),
+    (dict(rs=(256, 64, 128)), INVALID),        # k rows overlap (below Hkv * d = 128)
+    (dict(v=P + 4), INVALID),
     # bias gradient
     (dict(db=P), INVALID),                                              # no dbias_stride
     (dict(db=P, dbstr=(64, 16, 4, 1)), INVALID),                        # no bias

@@ -44,12 +44,12 @@ def load() -> ctypes.CDLL:
                           "`python -m variable_length_packed_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     lib.va_varlen_fwd.restype = ctypes.c_int
-    lib.va_varlen_fwd.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p, _i64p, _p,
-                                  _p, _p, ctypes.c_size_t, _i32, _i32, _i32, _i32, _i32, _i32,
+    lib.va_varlen_fwd.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p, _i64p, _i64p,
+                                  _p, _p, _p, ctypes.c_size_t, _i32, _i32, _i32, _i32, _i32, _i32,
                                   ctypes.c_int, _p]
     lib.va_varlen_bwd.restype = ctypes.c_int
     lib.va_varlen_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p,
-                                  _i64p, _p, _p, _p, _p, _i64p, _p, ctypes.c_size_t, _i32, _i32,
+                                  _i64p, _i64p, _p, _p, _p, _p, _i64p, _p, ctypes.c_size_t, _i32, _i32,
                                   _i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int, _p]
     lib.va_varlen_fwd_workspace_size.restype = ctypes.c_size_t
     lib.va_varlen_fwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -84,8 +84,8 @@ def load() -> ctypes.CDLL:
 
 
 def strides_arg(strides):
-    """HOST int64[4] for bias_stride, or None."""
+    """HOST int64[n] for bias_stride (4) or qkv_row_stride (3), or None."""
     if strides is None:
         return None
-    arr = (ctypes.c_int64 * 4)(*[int(s) for s in strides])
+    arr = (ctypes.c_int64 * len(strides))(*[int(s) for s in strides])
     return arr

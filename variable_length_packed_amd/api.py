@@ -39,15 +39,29 @@ def _raise(status: int, lib) -> None:
     raise ValueError(f"{name}: {msg}")
 
 
-def _need_dev(name: str, t: torch.Tensor, device) -> None:
+def _need_dev(name: str, t: torch.Tensor, device, rows: bool = False) -> None:
+    """A device tensor on `device`, contiguous -- or, with ``rows``, a [tokens, heads, d]
+    view whose heads and elements are dense (its token stride goes to the library)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on the GPU (got {t.device})")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
-    if not t.is_contiguous():
+    if rows and t.dim() == 3:
+        if t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
+            raise ValueError(f"{name} must have dense heads and head_dim (any token stride)")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _row_strides(q, k, v):
+    """HOST int64[3] token strides of q, k, v, or None when all three are contiguous."""
+    if q.is_contiguous() and k.is_contiguous() and v.is_contiguous():
+        return None
+    return _lib.strides_arg([q.stride(0) if q.shape[0] > 1 else q.shape[1] * q.shape[2],
+                             k.stride(0) if k.shape[0] > 1 else k.shape[1] * k.shape[2],
+                             v.stride(0) if v.shape[0] > 1 else v.shape[1] * v.shape[2]])
 
 
 def _bias_args(bias, bias_stride, q, batch, hq, max_q, max_k):
@@ -94,8 +108,9 @@ def va_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   workspace: Optional[torch.Tensor] = None):
     """Forward.  Returns (out [Tq, Hq, d] in q's dtype, lse [Hq, Tq] float32)."""
     lib = _lib.load()
-    for n, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
-                 ("cu_seqlens_k", cu_seqlens_k)):
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_dev(n, t, q.device, rows=True)
+    for n, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
         _need_dev(n, t, q.device)
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be [tokens, heads, head_dim]")
@@ -114,7 +129,7 @@ def va_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     bptr, bstr = _bias_args(bias, bias_stride, q, batch, hq, int(max_seqlen_q), int(max_seqlen_k))
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
     _need_dev("out", out, q.device)
@@ -129,7 +144,7 @@ def va_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _need_dev("workspace", workspace, q.device)
     st = lib.va_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
                            cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
-                           int(bool(causal)), bptr, bstr, out.data_ptr(), lse.data_ptr(),
+                           int(bool(causal)), bptr, bstr, _row_strides(q, k, v), out.data_ptr(), lse.data_ptr(),
                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                            batch, tq, tk, hq, hkv, d, dt, _stream(q.device))
     _raise(st, lib)
@@ -235,8 +250,10 @@ def va_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch
     (elements of pairs in key blocks a causal mask skips are left as they are).
     """
     lib = _lib.load()
-    for n, t in (("dout", dout), ("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse),
-                 ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _need_dev(n, t, q.device, rows=True)
+    for n, t in (("dout", dout), ("out", out), ("lse", lse), ("cu_seqlens_q", cu_seqlens_q),
+                 ("cu_seqlens_k", cu_seqlens_k)):
         _need_dev(n, t, q.device)
     if q.dim() != 3 or k.shape != v.shape or dout.shape != q.shape or out.shape != q.shape:
         raise ValueError("shape mismatch among dout, q, k, v, out")
@@ -290,7 +307,7 @@ def va_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch
     st = lib.va_varlen_bwd(dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                            out.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
                            cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
-                           int(bool(causal)), bptr, bstr, dq.data_ptr(), dk.data_ptr(),
+                           int(bool(causal)), bptr, bstr, _row_strides(q, k, v), dq.data_ptr(), dk.data_ptr(),
                            dv.data_ptr(), dbptr, dbstr, workspace.data_ptr(),
                            workspace.numel() * workspace.element_size(), batch, tq, tk, hq, hkv,
                            d, dt, gdt, _stream(q.device))

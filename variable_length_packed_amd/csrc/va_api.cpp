@@ -64,6 +64,28 @@ va_status check_common(const Common& c, float scale, const void* bias, const int
   return VA_OK;
 }
 
+// Token strides of q, k, v (elements): the caller's, or the contiguous ones.
+// Rows are read with 16-byte loads at 32-bit byte offsets inside a sequence.
+va_status row_strides(const Common& c, const void* q, const void* k, const void* v, const int64_t* rs,
+                      int64_t out[3]) {
+  const int64_t dense[3] = {(int64_t)c.hq * c.d, (int64_t)c.hkv * c.d, (int64_t)c.hkv * c.d};
+  const int elt = c.dtype == VA_F32 ? 4 : 2;
+  for (int i = 0; i < 3; ++i) {
+    out[i] = rs ? rs[i] : dense[i];
+    if (out[i] < dense[i])
+      return fail(VA_ERR_INVALID, "qkv_row_stride[%d] = %lld is below heads * head_dim = %lld", i,
+                  (long long)out[i], (long long)dense[i]);
+    if ((out[i] * elt) % 16 != 0)
+      return fail(VA_ERR_INVALID, "qkv_row_stride[%d] must keep rows 16-byte aligned", i);
+    const int64_t rows = i == 0 ? c.max_q : c.max_k;
+    if (rows * out[i] * elt >= ((int64_t)1 << 31))
+      return fail(VA_ERR_UNSUPPORTED, "max_seqlen * qkv_row_stride[%d] spans 2 GiB or more", i);
+  }
+  if ((((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v)) % 16 != 0)
+    return fail(VA_ERR_INVALID, "q, k and v must be 16-byte aligned");
+  return VA_OK;
+}
+
 // ---------------------------------------------------------------------------
 // Workspace.  Every pass gets a work plan (a header, the unit list and the
 // split-tile list) and, when some tile can be split, float32 partial-result
@@ -255,7 +277,8 @@ size_t va_varlen_fwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
 va_status va_varlen_fwd(const void* q, const void* k, const void* v,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                         int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
-                        int causal, const void* bias, const int64_t* bias_stride, void* out,
+                        int causal, const void* bias, const int64_t* bias_stride,
+                        const int64_t* qkv_row_stride, void* out,
                         float* lse, void* workspace, size_t workspace_bytes, int32_t batch,
                         int32_t total_q, int32_t total_k, int32_t num_heads_q,
                         int32_t num_heads_kv, int32_t head_dim, va_dtype dtype,
@@ -266,6 +289,9 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
   Common c{batch, total_q, total_k, num_heads_q, num_heads_kv, head_dim, max_seqlen_q,
            max_seqlen_k, causal, dtype};
   va_status s = check_common(c, softmax_scale, bias, bias_stride);
+  if (s != VA_OK) return s;
+  int64_t rs[3];
+  s = row_strides(c, q, k, v, qkv_row_stride, rs);
   if (s != VA_OK) return s;
   if (((uintptr_t)workspace) % kAlign != 0)
     return fail(VA_ERR_INVALID, "workspace must be 256-byte aligned");
@@ -290,6 +316,7 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
                  ((uintptr_t)bias) % (4 * elt) == 0;
   }
   a.out = out; a.lse = lse;
+  a.q_rs = rs[0]; a.k_rs = rs[1]; a.v_rs = rs[2];
   a.batch = batch; a.total_q = total_q; a.total_k = total_k;
   a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = num_heads_q / num_heads_kv; a.d = head_dim;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
@@ -330,7 +357,8 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
                         const void* out, const float* lse, const int32_t* cu_seqlens_q,
                         const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
                         float softmax_scale, int causal, const void* bias,
-                        const int64_t* bias_stride, void* dq, void* dk, void* dv, float* dbias,
+                        const int64_t* bias_stride, const int64_t* qkv_row_stride, void* dq,
+                        void* dk, void* dv, float* dbias,
                         const int64_t* dbias_stride, void* workspace,
                         size_t workspace_bytes, int32_t batch, int32_t total_q, int32_t total_k,
                         int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
@@ -342,6 +370,9 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
   Common c{batch, total_q, total_k, num_heads_q, num_heads_kv, head_dim, max_seqlen_q,
            max_seqlen_k, causal, dtype};
   va_status s = check_common(c, softmax_scale, bias, bias_stride);
+  if (s != VA_OK) return s;
+  int64_t rs[3];
+  s = row_strides(c, q, k, v, qkv_row_stride, rs);
   if (s != VA_OK) return s;
   if (grad_dtype != VA_F32 && grad_dtype != VA_BF16 && grad_dtype != VA_F16)
     return fail(VA_ERR_UNSUPPORTED, "unknown grad_dtype %d", (int)grad_dtype);
@@ -393,6 +424,7 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
                  ((uintptr_t)bias) % (4 * elt) == 0;
   }
   a.dq = dq; a.dk = dk; a.dv = dv;
+  a.q_rs = rs[0]; a.k_rs = rs[1]; a.v_rs = rs[2];
   a.batch = batch; a.total_q = total_q; a.total_k = total_k;
   a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = n_rep; a.d = head_dim;
   a.scale = softmax_scale;

@@ -252,8 +252,11 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
   const int hh = lane >> 5, r32 = lane & 31;
 
   const int total_items = uniform(a.plan_k.hdr[1]) * a.hkv;
-  const size_t qstride = (size_t)a.hq * D, kstride = (size_t)a.hkv * D;
-  const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
+  // token strides (elements): Q, K, V as the caller lays them out; dO, dK, dV dense
+  const size_t qstride = (size_t)a.q_rs, dostride = (size_t)a.hq * D;
+  const size_t kstride = (size_t)a.k_rs, vstride = (size_t)a.v_rs, gstride = (size_t)a.hkv * D;
+  const int qrow_bytes = (int)(qstride * ELT), dorow_bytes = (int)(dostride * ELT);
+  const int krow_bytes = (int)(kstride * ELT), vrow_bytes = (int)(vstride * ELT);
   const int hpw = a.n_rep;  // every query head of the group
 
   int ticket = 0;  // thread 0: ticket of the item after the current one
@@ -279,11 +282,12 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     const int kj = wk0 + r32;        // this lane's key (columns of the score tile)
     const bool wave_keys = wk0 < Lk;
 
-    const size_t koff = (size_t)k0 * kstride + (size_t)g * D;
-    const int64_t kbytes = Lk > 0 ? (int64_t)(Lk - 1) * krow_bytes + D * ELT : 0;
     RowFrag<H16, D> kf, vf;
-    kf.load(make_rsrc((const T*)a.k + koff, kbytes), krow_bytes, kj, hh);
-    vf.load(make_rsrc((const T*)a.v + koff, kbytes), krow_bytes, kj, hh);
+    kf.load(make_rsrc((const T*)a.k + (size_t)k0 * kstride + (size_t)g * D,
+                      Lk > 0 ? (int64_t)(Lk - 1) * krow_bytes + D * ELT : 0), krow_bytes, kj, hh);
+    vf.load(make_rsrc((const T*)a.v + (size_t)k0 * vstride + (size_t)g * D,
+                      Lk > 0 ? (int64_t)(Lk - 1) * vrow_bytes + D * ELT : 0), vrow_bytes, kj, hh);
+    const size_t koff = (size_t)k0 * gstride + (size_t)g * D;  // this tile's dK / dV rows
     f32x16_t dk[DT], dv[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) { dk[i] = (f32x16_t){}; dv[i] = (f32x16_t){}; }
@@ -319,10 +323,10 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
       const int r = rn.x, n = rn.y;
       const int h = h_first + r;
       const int qb = qs + n * BMQ;
-      const size_t qoff = (size_t)q0 * qstride + (size_t)h * D;
-      const int64_t qbytes = Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0;
-      sq.load(make_rsrc((const T*)a.q + qoff, qbytes), qrow_bytes, qb);
-      sd.load(make_rsrc((const T*)a.dout + qoff, qbytes), qrow_bytes, qb);
+      sq.load(make_rsrc((const T*)a.q + (size_t)q0 * qstride + (size_t)h * D,
+                        Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0), qrow_bytes, qb);
+      sd.load(make_rsrc((const T*)a.dout + (size_t)q0 * dostride + (size_t)h * D,
+                        Lq > 0 ? (int64_t)(Lq - 1) * dorow_bytes + D * ELT : 0), dorow_bytes, qb);
       if (tid < BMQ) {
         const int i = qb + tid;
         pl = INFINITY;  // rows past the sequence: P = exp2(x - inf) = 0
@@ -485,8 +489,8 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     // into its slot; the merge kernel undoes the layout.
     if (slot < 0) {
       const int gelt = a.grad_bf16 ? 2 : 4;
-      const int krow = (int)kstride * gelt;
-      const size_t base = (koff + (size_t)max(wk0, 0) * kstride) * gelt;
+      const int krow = (int)gstride * gelt;
+      const size_t base = (koff + (size_t)max(wk0, 0) * gstride) * gelt;
       const int64_t nbytes = Lk > wk0 ? (int64_t)(Lk - wk0 - 1) * krow + D * gelt : 0;
       const rsrc_t rk = make_rsrc((const uint8_t*)a.dk + base, nbytes);
       const rsrc_t rv = make_rsrc((const uint8_t*)a.dv + base, nbytes);
@@ -612,8 +616,11 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   const int hh = lane >> 5, r32 = lane & 31;
 
   const int total_items = uniform(a.plan_q.hdr[1]) * a.hq;
-  const size_t qstride = (size_t)a.hq * D, kstride = (size_t)a.hkv * D;
-  const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
+  // token strides (elements): Q, K, V as the caller lays them out; dO and dQ dense
+  const size_t qstride = (size_t)a.q_rs, dostride = (size_t)a.hq * D;
+  const size_t kstride = (size_t)a.k_rs, vstride = (size_t)a.v_rs;
+  const int qrow_bytes = (int)(qstride * ELT), dorow_bytes = (int)(dostride * ELT);
+  const int krow_bytes = (int)(kstride * ELT), vrow_bytes = (int)(vstride * ELT);
   const int gelt = a.grad_bf16 ? 2 : 4;
 
   int ticket = 0;  // thread 0: ticket of the item after the current one
@@ -648,11 +655,12 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     const int n_plain = CAUSAL ? max(r1 - BMQ_DQ + off + 1, 0) / BN : kv_hi / BN;
     const int kv_end = min(kv_hi, n1 * BN);  // keys this unit may read
 
-    const size_t qoff = (size_t)q0 * qstride + (size_t)h * D;
-    const int64_t qbytes = Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0;
+    const size_t qoff = (size_t)q0 * dostride + (size_t)h * D;  // dO and dQ rows
     RowFrag<H16, D> qf, of;
-    qf.load(make_rsrc((const T*)a.q + qoff, qbytes), qrow_bytes, rq, hh);
-    of.load(make_rsrc((const T*)a.dout + qoff, qbytes), qrow_bytes, rq, hh);
+    qf.load(make_rsrc((const T*)a.q + (size_t)q0 * qstride + (size_t)h * D,
+                      Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0), qrow_bytes, rq, hh);
+    of.load(make_rsrc((const T*)a.dout + qoff, Lq > 0 ? (int64_t)(Lq - 1) * dorow_bytes + D * ELT : 0),
+            dorow_bytes, rq, hh);
     float lse2 = 0.f, dsum = 0.f;
     if (row_ok) {
       const float l = a.lse[(size_t)h * a.total_q + q0 + rq];
@@ -663,10 +671,10 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < DT; ++i) acc[i] = (f32x16_t){};
 
-    const size_t koff = (size_t)k0 * kstride + (size_t)g * D;
-    const int64_t kbytes = kv_end > 0 ? (int64_t)(kv_end - 1) * krow_bytes + D * ELT : 0;
-    const rsrc_t kres = make_rsrc((const T*)a.k + koff, kbytes);
-    const rsrc_t vres = make_rsrc((const T*)a.v + koff, kbytes);
+    const rsrc_t kres = make_rsrc((const T*)a.k + (size_t)k0 * kstride + (size_t)g * D,
+                                  kv_end > 0 ? (int64_t)(kv_end - 1) * krow_bytes + D * ELT : 0);
+    const rsrc_t vres = make_rsrc((const T*)a.v + (size_t)k0 * vstride + (size_t)g * D,
+                                  kv_end > 0 ? (int64_t)(kv_end - 1) * vrow_bytes + D * ELT : 0);
     // this (sequence, head)'s bias view (element (r, c) at r*bs2 + c*bs3), ending after the
     // last element a valid (row, key) reads; rows before the sequence read 0, keys past
     // it are masked
@@ -687,7 +695,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
       const int buf = (n - n0) & 1;
       if (n + 1 < n1) {
         sk.load(kres, krow_bytes, kb + BN);
-        sv.load(vres, krow_bytes, kb + BN);
+        sv.load(vres, vrow_bytes, kb + BN);
       }
       if (wave_on && kb < wave_hi) {
         float dsv[16 * NS];
@@ -776,7 +784,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
 
     if (n1 > n0) {
       sk.load(kres, krow_bytes, n0 * BN);
-      sv.load(vres, krow_bytes, n0 * BN);
+      sv.load(vres, vrow_bytes, n0 * BN);
       sk.store(sm.kn[0], sm.kt[0]);
       sv.store(sm.vn[0], nullptr);
     }
@@ -793,7 +801,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
 
     if (slot < 0) {
       // rows < 0 fall outside the resource: their stores are dropped
-      const int dq_row_bytes = (int)qstride * gelt;
+      const int dq_row_bytes = (int)dostride * gelt;
       const rsrc_t dqres = make_rsrc((uint8_t*)a.dq + qoff * gelt,
                                      Lq > 0 ? (int64_t)(Lq - 1) * dq_row_bytes + D * gelt : 0);
 #pragma unroll

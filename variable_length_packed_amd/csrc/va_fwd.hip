@@ -138,8 +138,10 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
   const T* __restrict__ kg = (const T*)a.k;
   const T* __restrict__ vg = (const T*)a.v;
   T* __restrict__ og = (T*)a.out;
-  const size_t qstride = (size_t)a.hq * D;
-  const size_t kstride = (size_t)a.hkv * D;
+  // token strides (elements): Q, K and V as the caller lays them out (a fused
+  // QKV projection interleaves them), O dense
+  const size_t qstride = (size_t)a.q_rs, ostride = (size_t)a.hq * D;
+  const size_t kstride = (size_t)a.k_rs, vstride = (size_t)a.v_rs;
 
   int ticket = 0;  // thread 0: ticket of the item after the current one
   if (tid == 0) {
@@ -184,15 +186,16 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
 
     // ---- resources: this sequence's rows of Q/O for head h and of K/V for head g
     constexpr int ELT = (int)sizeof(T);
-    const int qrow_bytes = (int)(qstride * ELT), krow_bytes = (int)(kstride * ELT);
-    const size_t qoff = (size_t)q0 * qstride + (size_t)h * D;
-    const int64_t qbytes = Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0;
-    const rsrc_t qres = make_rsrc(qg + qoff, qbytes);
-    const rsrc_t ores = make_rsrc(og + qoff, qbytes);
-    const size_t koff = (size_t)k0 * kstride + (size_t)g * D;
-    const int64_t kbytes = kv_end > 0 ? (int64_t)(kv_end - 1) * krow_bytes + D * ELT : 0;
-    const rsrc_t kres = make_rsrc(kg + koff, kbytes);
-    const rsrc_t vres = make_rsrc(vg + koff, kbytes);
+    const int qrow_bytes = (int)(qstride * ELT), orow_bytes = (int)(ostride * ELT);
+    const int krow_bytes = (int)(kstride * ELT), vrow_bytes = (int)(vstride * ELT);
+    const rsrc_t qres = make_rsrc(qg + (size_t)q0 * qstride + (size_t)h * D,
+                                  Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0);
+    const rsrc_t ores = make_rsrc(og + (size_t)q0 * ostride + (size_t)h * D,
+                                  Lq > 0 ? (int64_t)(Lq - 1) * orow_bytes + D * ELT : 0);
+    const rsrc_t kres = make_rsrc(kg + (size_t)k0 * kstride + (size_t)g * D,
+                                  kv_end > 0 ? (int64_t)(kv_end - 1) * krow_bytes + D * ELT : 0);
+    const rsrc_t vres = make_rsrc(vg + (size_t)k0 * vstride + (size_t)g * D,
+                                  kv_end > 0 ? (int64_t)(kv_end - 1) * vrow_bytes + D * ELT : 0);
 
     // ---- Q fragments (B operand of S^T = K Q^T); rows < 0 read as zero
     u32x4_t qf4[QT][H16 ? QF : 1];
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       const int kb = kb0 + n * BN;
       const int kbuf = (n + 1) & 1, vbuf = n & 1;
       ld.load_k(kres, krow_bytes, kb + 2 * BN);  // past the last block every row reads as zero
-      ld.load_v(vres, krow_bytes, kb + BN);
+      ld.load_v(vres, vrow_bytes, kb + BN);
       u32x4_t kfr[KFN];
       read_k(kbuf, kfr);
       u32x4_t vf[NCH][DT];
@@ -564,7 +567,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     {
       Loader<H16, D> ld1;  // K(1) in flight with K(0) and V(0)
       ld.load_k(kres, krow_bytes, kb0);
-      ld.load_v(vres, krow_bytes, kb0);
+      ld.load_v(vres, vrow_bytes, kb0);
       ld1.load_k(kres, krow_bytes, kb0 + BN);
       ld.store_k(sm, 0);
       ld.store_v(sm, 0);
@@ -581,7 +584,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       constexpr bool MASK = decltype(mask_tag)::value;
       const int kb = kb0 + n * BN;
       ld.load_k(kres, krow_bytes, kb + 2 * BN);  // past the last block every row reads as zero
-      ld.load_v(vres, krow_bytes, kb + BN);
+      ld.load_v(vres, vrow_bytes, kb + BN);
       f32x16_t s_nxt[QT][NS];
       if constexpr (!MASK) {
         // every wave with rows in the sequence sees all of block n; S of
@@ -673,10 +676,10 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
             const float o2 = acc[qt][dt][4 * a4 + 2] * inv_l, o3 = acc[qt][dt][4 * a4 + 3] * inv_l;
             // rows < 0 fall outside the resource: the store is dropped
             if constexpr (H16) {
-              buf_store8((u32x2_t){pack16<H16>(o0, o1), pack16<H16>(o2, o3)}, ores, rq[qt] * qrow_bytes + d0 * 2);
+              buf_store8((u32x2_t){pack16<H16>(o0, o1), pack16<H16>(o2, o3)}, ores, rq[qt] * orow_bytes + d0 * 2);
             } else {
               buf_store16((u32x4_t){__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2),
-                                    __float_as_uint(o3)}, ores, rq[qt] * qrow_bytes + d0 * 4);
+                                    __float_as_uint(o3)}, ores, rq[qt] * orow_bytes + d0 * 4);
             }
           }
         if (rq[qt] >= 0 && hh == 0) a.lse[(size_t)h * a.total_q + q0 + rq[qt]] = lse2 * kLn2;

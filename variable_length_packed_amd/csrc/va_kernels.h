@@ -55,6 +55,7 @@ struct FwdArgs {
   int64_t bs0, bs1, bs2, bs3;
   void* out;
   float* lse;
+  int64_t q_rs, k_rs, v_rs;  // token strides of q, k, v (elements); out is dense
   Plan plan;
   float* part_o;    // [slot][hq][BM][d]  normalised partial outputs of split tiles
   float* part_lse;  // [slot][hq][BM]     their base-2 log-sum-exp
@@ -80,6 +81,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
+  int64_t q_rs, k_rs, v_rs;  // token strides of q, k, v (elements); dout, out and grads dense
   float* dsum;     // workspace [hq, total_q]: rowsum(dO * O)
   Plan plan_k;     // dK/dV pass: key tiles
   Plan plan_q;     // dQ pass: query tiles
