@@ -196,23 +196,27 @@ size_t bwd_workspace(int batch, int total_q, int total_k, int max_q, int max_k, 
          round_up(dbias_slot_bytes(hq) * K.slot_cap);
 }
 
-// Decode steps: 32-row blocks of (new token, query head) pairs per (sequence,
-// KV head), and key chunks sized so the grid holds about kKvWaves waves (at
-// least 256 keys per chunk, so the partial results of a chunk stay a few
-// percent of the K/V bytes it reads).
+// Decode steps: row blocks of `rows` = min(32, n_rep * max_seqlen_q) (new
+// token, query head) pairs, and key chunks sized so the grid holds about
+// kKvWaves waves (at least 256 keys per chunk, so the partial results of a
+// chunk stay a few percent of the K/V bytes it reads).  The planner lists the
+// (sequence, row block, chunk) triples with work; `cap` bounds that list:
+// from max_seqlen_q when it is a bound the caller promises (paged caches),
+// from total_q when it is only a hint (the packed forward's short-query path).
 constexpr int64_t kKvWaves = 8192;
 struct KvLayout {
-  int rblocks = 1, rows = 1, chunk = 1, nchunk = 1;
+  int rows = 1, chunk = 1, nchunk = 1, cap = 1;
   size_t plan_bytes = 0, part_o_bytes = 0, part_lse_bytes = 0;
   size_t total() const { return plan_bytes + part_o_bytes + part_lse_bytes; }
 };
-KvLayout kv_layout(int batch, int max_q, int max_k, int hq, int hkv, int d) {
+KvLayout kv_layout(int batch, int max_q, int max_k, int hq, int hkv, int d, int64_t total_q = -1) {
   KvLayout L;
-  const int64_t R = (int64_t)max_q * (hq / hkv);
-  L.rblocks = (int)((R + 31) / 32);
+  const int n_rep = hq / hkv;
+  const int64_t R = (int64_t)max_q * n_rep;
   L.rows = (int)(R < 32 ? R : 32);
+  const int64_t rb_hint = (R + L.rows - 1) / L.rows;  // row blocks of a sequence at the hint
   const int kb = va::kv_block_n(d);
-  const int64_t blocks = (int64_t)batch * hkv * L.rblocks;
+  const int64_t blocks = (int64_t)batch * hkv * rb_hint;
   const int64_t want = (kKvWaves + blocks - 1) / blocks;  // chunks wanted per row block
   const int64_t steps = ((int64_t)max_k + kb - 1) / kb;
   int64_t cs = (steps + want - 1) / want;
@@ -220,14 +224,28 @@ KvLayout kv_layout(int batch, int max_q, int max_k, int hq, int hkv, int d) {
   L.chunk = (int)(cs * kb);
   L.nchunk = (int)(((int64_t)max_k + L.chunk - 1) / L.chunk);
   if (L.nchunk < 1) L.nchunk = 1;
+  const int64_t row_blocks = total_q < 0 ? (int64_t)batch * rb_hint
+                                         : (total_q * n_rep + L.rows - 1) / L.rows + batch;
+  L.cap = (int)(row_blocks * L.nchunk);
+  L.plan_bytes = round_up(256) + round_up((size_t)L.cap * sizeof(va::KvChunk));
   if (L.nchunk > 1) {
-    const size_t slots = (size_t)blocks * L.nchunk;
+    const size_t slots = (size_t)L.cap * hkv;
     L.part_o_bytes = round_up(slots * L.rows * d * sizeof(float));
     L.part_lse_bytes = round_up(slots * L.rows * sizeof(float));
   }
-  // the planner's header and chunk list (at most nchunk entries per sequence)
-  L.plan_bytes = round_up(256) + round_up((size_t)batch * L.nchunk * sizeof(va::KvChunk));
   return L;
+}
+
+// The packed forward's short-query path: with 16-bit inputs, no bias and at
+// most 32 (new token, query head) rows per KV head and sequence (by the
+// max_seqlen_q hint) -- decode steps, beams, short drafts over contiguous
+// K/V -- the decode kernels run instead of 128-row query tiles.  They read
+// K/V through cu_seqlens_k and the token strides; every result is the same
+// up to rounding order, and sequences longer than the hints still get every
+// row and key (more row blocks, longer chunks).
+constexpr int64_t kShortQueryRows = 32;
+bool short_query(va_dtype dtype, int max_q, int n_rep) {
+  return dtype != VA_F32 && (int64_t)max_q * n_rep <= kShortQueryRows;
 }
 
 bool kv_args_ok(int32_t batch, int32_t max_q, int32_t max_k, int32_t hq, int32_t hkv, int32_t d,
@@ -271,7 +289,13 @@ size_t va_varlen_fwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
       num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0 ||
       (head_dim != 64 && head_dim != 128) || (dtype != VA_F32 && dtype != VA_BF16 && dtype != VA_F16))
     return 0;
-  return fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, dtype != VA_F32);
+  size_t n = fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, dtype != VA_F32);
+  if (short_query(dtype, max_seqlen_q, num_heads_q / num_heads_kv)) {
+    const size_t m = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
+                               total_q).total();
+    if (m > n) n = m;
+  }
+  return n;
 }
 
 va_status va_varlen_fwd(const void* q, const void* k, const void* v,
@@ -299,6 +323,36 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
   const size_t need = fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16);
   if (workspace_bytes < need)
     return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+
+  hipStream_t st = (hipStream_t)stream;
+  if (!bias && short_query(dtype, max_seqlen_q, num_heads_q / num_heads_kv)) {
+    const KvLayout L = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
+                                 total_q);
+    if (workspace_bytes < L.total())
+      return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, L.total());
+    va::KvArgs a{};
+    a.q = q; a.k_cache = k; a.v_cache = v;
+    a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+    a.q_rs = rs[0]; a.k_rs = rs[1]; a.v_rs = rs[2];
+    a.total_k = total_k;
+    a.out = out; a.lse = lse;
+    char* w = (char*)workspace;
+    a.plan = (int32_t*)w;
+    a.chunks = (va::KvChunk*)(w + round_up(256));
+    a.part_o = L.part_o_bytes > 0 ? (float*)(w + L.plan_bytes) : nullptr;
+    a.part_lse = L.part_lse_bytes > 0 ? (float*)(w + L.plan_bytes + L.part_o_bytes) : nullptr;
+    a.batch = batch; a.total_q = total_q;
+    a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = num_heads_q / num_heads_kv; a.d = head_dim;
+    a.num_pages = 1;
+    a.max_k = max_seqlen_k;
+    a.rows = L.rows; a.chunk = L.chunk; a.nchunk = L.nchunk; a.cap = L.cap;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.causal = causal;
+    a.h16 = elem_code(dtype);
+    const hipError_t e = va::launch_kvcache(a, st);
+    if (e != hipSuccess) return hip_fail(e, "short-query forward launch");
+    return VA_OK;
+  }
 
   va::FwdArgs a{};
   a.q = q; a.k = k; a.v = v;
@@ -331,7 +385,6 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
   va::PlanSet ps{};
   ps.p[0] = plan_args(a.plan, L, cu_seqlens_q, cu_seqlens_k, total_q, total_k, batch,
                       va::fwd_block_m(), va::fwd_block_n(bf16, head_dim), 0, causal);
-  hipStream_t st = (hipStream_t)stream;
   hipError_t e = va::launch_plan(ps, 1, st);
   if (e != hipSuccess) return hip_fail(e, "forward plan launch");
   e = va::launch_fwd(a, (int64_t)L.unit_cap * num_heads_q, st);
@@ -531,7 +584,9 @@ va_status va_kvcache_fwd(const void* q, const void* k_cache, const void* v_cache
   a.num_pages = num_pages;
   const int64_t reach = (int64_t)block_table_stride * page_size;
   a.max_k = (int)(reach < max_seqlen_k ? reach : max_seqlen_k);
-  a.rblocks = L.rblocks; a.rows = L.rows; a.chunk = L.chunk; a.nchunk = L.nchunk;
+  a.rows = L.rows; a.chunk = L.chunk; a.nchunk = L.nchunk; a.cap = L.cap;
+  a.q_rs = (int64_t)num_heads_q * head_dim;
+  a.k_rs = a.v_rs = (int64_t)num_heads_kv * head_dim;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.causal = causal;
   a.h16 = elem_code(dtype);

@@ -128,22 +128,28 @@ hipError_t launch_bwd(const BwdArgs& a, const PlanSet& ps, int64_t max_q_items, 
 // Decode steps against a paged KV cache.  A work item (one wave) is one
 // (sequence, KV head, row block, key chunk): 32 rows = (new token, query
 // head of the KV head's group) pairs, keys [chunk * c, chunk * (c + 1)).
-// A planner kernel lists the (sequence, chunk) pairs that have work; items
-// are (list entry, row block, KV head), KV heads fastest.  A sequence with
-// more than one chunk writes float32 partials to slot
-// ((b * hkv + g) * rblocks + rb) * nchunk + c, [slot][rows][d] and
-// [slot][rows], and the merge kernel combines its chunks in order.
+// A planner kernel lists the (sequence, row block, chunk) triples that have
+// work; items are (list entry, KV head), KV heads fastest.  A row block with
+// more than one chunk writes float32 partials to slot entry * hkv + g,
+// [slot][rows][d] and [slot][rows], and the merge kernel combines its chunks
+// in order.
 // ---------------------------------------------------------------------------
 struct KvChunk {
-  int32_t b, c, q0, q1, lk, pad0, pad1, pad2;  // sequence, chunk, its query rows, its cached keys
+  int32_t b, rb, c;      // sequence, 32-row block, key chunk
+  int32_t q0, q1;        // the sequence's query rows
+  int32_t lk, k0;        // its key count and first key row (ragged mode)
+  int32_t chunk;         // keys per chunk of this sequence
 };
 struct KvArgs {
-  const void* q;             // [total_q, hq, d]
-  const void* k_cache;       // [num_pages, page_size, hkv, d]
+  const void* q;             // [total_q, hq, d], token stride q_rs
+  const void* k_cache;       // paged: [num_pages, page_size, hkv, d]; ragged: [total_k, hkv, d]
   const void* v_cache;
   const int32_t* cu_q;       // [batch + 1]
-  const int32_t* seqlens_k;  // [batch]
-  const int32_t* block_table;  // [batch][bt_stride]
+  const int32_t* seqlens_k;  // paged: [batch]
+  const int32_t* block_table;  // paged: [batch][bt_stride]
+  const int32_t* cu_k;       // ragged (no table): [batch + 1] rows of k_cache / v_cache
+  int64_t q_rs, k_rs, v_rs;  // token strides (elements); out is dense
+  int32_t total_k;           // ragged: rows of k_cache / v_cache
   void* out;                 // [total_q, hq, d]
   float* lse;                // [hq, total_q]
   float* part_o;
@@ -152,9 +158,10 @@ struct KvArgs {
   KvChunk* chunks;           // [batch * nchunk] at most
   int32_t batch, total_q, hq, hkv, n_rep, d;
   int32_t bt_stride, page_shift, num_pages;
-  int32_t max_k;             // keys of a sequence are capped here (max_seqlen_k and the table's reach)
-  int32_t rblocks, rows;     // 32-row blocks per (sequence, KV head); partial rows per slot
-  int32_t chunk, nchunk;     // keys per item (a multiple of the step), chunks per row block
+  int32_t max_k;             // paged: keys of a sequence are capped here (max_seqlen_k and the table's reach)
+  int32_t rows;              // partial rows per slot
+  int32_t chunk, nchunk;     // keys per chunk (a multiple of the step); most chunks of a row block
+  int32_t cap;               // most list entries (and partial slots per KV head)
   float scale_log2;
   int32_t causal;
   int32_t h16;               // 1 bfloat16, 2 float16

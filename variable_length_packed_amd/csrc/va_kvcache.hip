@@ -24,6 +24,9 @@
 //   LSE, and a merge kernel combines a sequence's chunks in chunk order
 //   (deterministic).
 //
+// The same kernels serve packed (ragged) K/V without a page table: key j of
+// sequence b is then row cu_k[b] + j, read through the token strides.
+//
 // Semantics (the packed forward's): bottom-right causal alignment, so query
 // i of Lq sees keys j <= i + Lk - Lq; a row with no visible key gives O = 0
 // and LSE = -inf.
@@ -45,8 +48,33 @@ struct KvShape {
   static constexpr int DT = D / 32;    // 32-wide tiles of head_dim in O^T
 };
 
-template <int H16, int D, bool CAUSAL, bool BIGPAGE>
+// Key addressing of the decode kernel.
+enum KvMode { kPagedSmall = 0, kPagedBig = 1, kRagged = 2 };
+
+// A sequence's key count and the first row of its keys (ragged mode).  Paged
+// lengths are clamped to max_k (the table's reach); ragged ones only to the
+// rows of K and V, since max_seqlen_k is a hint there.
+__device__ __forceinline__ int kv_len(const KvArgs& a, int b, int& k0) {
+  if (a.cu_k) {
+    int k1;
+    seq_bounds(a.cu_k, b, a.total_k, k0, k1);
+    return k1 - k0;
+  }
+  k0 = 0;
+  return min(max(a.seqlens_k[b], 0), a.max_k);
+}
+
+// Keys per chunk of a sequence of Lk keys: `chunk`, or a multiple of it for
+// a sequence longer than nchunk chunks (a ragged sequence past the hint), so
+// no sequence has more chunks than the partial slots hold.
+__device__ __forceinline__ int kv_chunk_of(const KvArgs& a, int Lk) {
+  const int64_t cap = (int64_t)a.chunk * a.nchunk;
+  return Lk <= cap ? a.chunk : a.chunk * (int)((Lk + cap - 1) / cap);
+}
+
+template <int H16, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
+  constexpr bool BIGPAGE = MODE == kPagedBig, RAGGED = MODE == kRagged;
   using SH = KvShape<D>;
   constexpr int KB = SH::KB, NS = SH::NS, VP = SH::VP, KS = SH::KS, DT = SH::DT;
   __shared__ uint16_t sk_all[4][KB * VP];
@@ -59,44 +87,43 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
   uint16_t* sk = sk_all[wid];
   uint16_t* sv = sv_all[wid];
 
-  // ---- items: (chunk of the planner's list, row block, KV head), KV heads
-  // fastest, so the waves of a workgroup read the same keys of neighbouring
-  // heads (adjacent in each cache row) at the same time.  The list holds
-  // only real chunks, so a static round robin gives every wave nearly the
-  // same work; a wave prefetches its next item's entry during the current one.
-  // Waves never synchronise: each runs its items alone.
-  const int RB = a.rblocks;
-  const int per_chunk = RB * a.hkv;
-  const int n_items = uniform(a.plan[0]) * per_chunk;
+  // ---- items: (entry of the planner's list, KV head), KV heads fastest, so
+  // the waves of a workgroup read the same keys of neighbouring heads
+  // (adjacent in each cache row) at the same time.  An entry is one
+  // (sequence, 32-row block, key chunk) with work, so a static round robin
+  // gives every wave nearly the same work; a wave prefetches its next item's
+  // entry during the current one.  Waves never synchronise: each runs its
+  // items alone.
+  const int n_items = uniform(a.plan[0]) * a.hkv;
   const int n_waves = (int)gridDim.x * 4;
   auto entry = [&](int it) {
-    return it < n_items ? a.chunks[it / per_chunk] : (KvChunk){0, 0, 0, 0, 0, 0, 0, 0};
+    return it < n_items ? a.chunks[it / a.hkv] : (KvChunk){0, 0, 0, 0, 0, 0, 0, 1};
   };
   KvChunk nxt = entry((int)blockIdx.x * 4 + wid);
   for (int item = (int)blockIdx.x * 4 + wid; item < n_items; item += n_waves) {
   const KvChunk ent = nxt;
   nxt = entry(item + n_waves);
   const int g = item % a.hkv;
-  const int rb = (item / a.hkv) % RB;
-  const int b = uniform(ent.b), c = uniform(ent.c);
-  const int q0 = uniform(ent.q0), q1 = uniform(ent.q1), Lk = uniform(ent.lk);
-  const size_t slot = (((size_t)b * a.hkv + g) * RB + rb) * a.nchunk + c;  // partial slot of this chunk
+  const int b = uniform(ent.b), rb = uniform(ent.rb), c = uniform(ent.c);
+  const int q0 = uniform(ent.q0), q1 = uniform(ent.q1), Lk = uniform(ent.lk), k0 = uniform(ent.k0);
+  const int chunk = uniform(ent.chunk);
+  const size_t slot = (size_t)item;  // partial slot: (entry, KV head)
   const int Lq = q1 - q0;
-  if (32 * rb >= Lq * a.n_rep) continue;  // no rows in this block
-  const int nch = max(1, (Lk + a.chunk - 1) / a.chunk);
+  const int nch = max(1, (Lk + chunk - 1) / chunk);
   const int off = Lk - Lq;
 
-  // this lane's row: new token qpos, query head h
-  const int r = 32 * rb + r32;
+  // this lane's row: new token qpos, query head h.  A row block is a.rows
+  // (<= 32) rows; lanes past it compute a column that is never stored.
+  const int r = rb * a.rows + r32;
   const int qpos = r / a.n_rep;
   const int h = g * a.n_rep + (r - qpos * a.n_rep);
-  const bool row_ok = qpos < Lq;
+  const bool row_ok = r32 < a.rows && qpos < Lq;
   // keys of the chunk that some row of the block sees, and the steps that
   // every valid row of the block sees in full
-  const int qpos_first = (32 * rb) / a.n_rep;
-  const int qpos_last = min(Lq - 1, (32 * rb + 31) / a.n_rep);
-  const int kbeg = c * a.chunk;
-  int kend = min(Lk, kbeg + a.chunk);
+  const int qpos_first = (rb * a.rows) / a.n_rep;
+  const int qpos_last = min(Lq - 1, (rb * a.rows + a.rows - 1) / a.n_rep);
+  const int kbeg = c * chunk;
+  int kend = min(Lk, kbeg + chunk);
   if (CAUSAL) kend = min(kend, qpos_last + off + 1);
   const int nsteps = kend > kbeg ? (kend - kbeg + KB - 1) / KB : 0;
   int plain_end = kend;
@@ -106,12 +133,12 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
 
   // ---- Q fragments (B operand of S^T = K Q^T); rows past the sequence read 0
   constexpr int ELT = 2;
-  const size_t qrow = (size_t)a.hq * D;
+  const size_t qrow = (size_t)a.q_rs;
   const rsrc_t qres = make_rsrc((const uint16_t*)a.q + (size_t)q0 * qrow, (int64_t)Lq * qrow * ELT);
   u32x4_t qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qf[ks] = buf_load16(qres, ((qpos * a.hq + h) * D + 16 * ks + 8 * hh) * ELT);
+    qf[ks] = buf_load16(qres, (int)((qpos * qrow + h * D + 16 * ks + 8 * hh) * ELT));
 
   // ---- cache rows.  Loads are coalesced: in each 16-byte load instruction LPR
   // consecutive lanes read one key's row of this KV head (D * 2 bytes), so the
@@ -124,17 +151,19 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
   const int lrow = lane / LPR, lcol = (lane % LPR) * 8;
   const uint16_t* __restrict__ kc = (const uint16_t*)a.k_cache;
   const uint16_t* __restrict__ vc = (const uint16_t*)a.v_cache;
-  const int32_t* __restrict__ bt = a.block_table + (size_t)b * a.bt_stride;
+  const int32_t* __restrict__ bt = RAGGED ? nullptr : a.block_table + (size_t)b * a.bt_stride;
   const int pmask = (1 << a.page_shift) - 1;
   // key of load i of step n (clamped to the chunk's last key)
   auto key_of = [&](int n, int i) { return min(kbeg + n * KB + RPI * i + lrow, kend - 1); };
   // pages of the next step to load, fetched a step ahead: with pages of at
   // least KB keys a step lies in one page (steps start at multiples of KB),
   // so one uniform lookup per step; otherwise one per load and lane
-  constexpr int NPG = BIGPAGE ? 1 : NI;
+  constexpr int NPG = BIGPAGE || RAGGED ? 1 : NI;
   int pg[NPG];
   auto fetch_pages = [&](int n) __attribute__((always_inline)) {
-    if constexpr (BIGPAGE) {
+    if constexpr (RAGGED) {
+      pg[0] = 0;
+    } else if constexpr (BIGPAGE) {
       pg[0] = bt[uniform(kbeg + n * KB) >> a.page_shift];
     } else {
 #pragma unroll
@@ -145,11 +174,15 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
   auto load_kv = [&](int n) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int page = min(max(pg[BIGPAGE ? 0 : i], 0), a.num_pages - 1);
-      const int64_t row = ((int64_t)page << a.page_shift) + (key_of(n, i) & pmask);
-      const int64_t o = (row * a.hkv + g) * D + lcol;
-      kr[i] = __builtin_nontemporal_load((const u32x4_t*)(kc + o));
-      vr[i] = __builtin_nontemporal_load((const u32x4_t*)(vc + o));
+      int64_t row;
+      if constexpr (RAGGED) {
+        row = (int64_t)k0 + key_of(n, i);
+      } else {
+        const int page = min(max(pg[BIGPAGE ? 0 : i], 0), a.num_pages - 1);
+        row = ((int64_t)page << a.page_shift) + (key_of(n, i) & pmask);
+      }
+      kr[i] = __builtin_nontemporal_load((const u32x4_t*)(kc + row * a.k_rs + g * D + lcol));
+      vr[i] = __builtin_nontemporal_load((const u32x4_t*)(vc + row * a.v_rs + g * D + lcol));
     }
   };
 
@@ -247,19 +280,20 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
   const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse2 = l_tot > 0.f ? m_run + __builtin_log2f(l_tot) : -INFINITY;
   if (nch == 1) {
-    const rsrc_t ores = make_rsrc((uint16_t*)a.out + (size_t)q0 * qrow, (int64_t)Lq * qrow * ELT);
+    if (row_ok) {
+      uint16_t* po = (uint16_t*)a.out + ((size_t)(q0 + qpos) * a.hq + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const int d0 = 32 * dt + 8 * a4 + 4 * hh;
-        const float o0 = acc[dt][4 * a4 + 0] * inv_l, o1 = acc[dt][4 * a4 + 1] * inv_l;
-        const float o2 = acc[dt][4 * a4 + 2] * inv_l, o3 = acc[dt][4 * a4 + 3] * inv_l;
-        // rows past the sequence fall outside the resource: the store is dropped
-        buf_store8((u32x2_t){pack16<H16>(o0, o1), pack16<H16>(o2, o3)}, ores, ((qpos * a.hq + h) * D + d0) * ELT);
-      }
-    if (row_ok && hh == 0) a.lse[(size_t)h * a.total_q + q0 + qpos] = lse2 * kLn2;
-  } else if (row_ok && r32 < a.rows) {
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int d0 = 32 * dt + 8 * a4 + 4 * hh;
+          const float o0 = acc[dt][4 * a4 + 0] * inv_l, o1 = acc[dt][4 * a4 + 1] * inv_l;
+          const float o2 = acc[dt][4 * a4 + 2] * inv_l, o3 = acc[dt][4 * a4 + 3] * inv_l;
+          *(u32x2_t*)(po + d0) = (u32x2_t){pack16<H16>(o0, o1), pack16<H16>(o2, o3)};
+        }
+      if (hh == 0) a.lse[(size_t)h * a.total_q + q0 + qpos] = lse2 * kLn2;
+    }
+  } else if (row_ok) {
     float* po = a.part_o + (slot * a.rows + r32) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -274,11 +308,14 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
   }
 }
 
-// The planner: one workgroup lists every (sequence, chunk) pair that has
-// work, in sequence order, with the sequence's bounds (clamped as in the
-// decode kernel), and stores the count in plan[0].  A sequence with new
-// tokens has max(1, ceil(Lk / chunk)) chunks (an empty cache still owes its
-// rows O = 0 and LSE = -inf); one without has none.
+// The planner: one workgroup lists every (sequence, row block, key chunk)
+// with work, in that order (chunks fastest), with the sequence's bounds
+// (clamped as the decode kernel needs them), and stores the count in
+// plan[0].  A sequence with Lq new tokens has ceil(Lq * n_rep / rows) row
+// blocks of max(1, ceil(Lk / chunk)) chunks each (an empty cache still owes
+// its rows O = 0 and LSE = -inf); one without new tokens has none.  The
+// list never outgrows a.cap entries (the host's bound); entries past it are
+// dropped, which only bad metadata can cause.
 constexpr int kPlanThreads = 1024;
 __global__ __launch_bounds__(kPlanThreads) void kv_plan_kernel(KvArgs a) {
   __shared__ int scan[kPlanThreads];
@@ -288,12 +325,15 @@ __global__ __launch_bounds__(kPlanThreads) void kv_plan_kernel(KvArgs a) {
   __syncthreads();
   for (int b0 = 0; b0 < a.batch; b0 += kPlanThreads) {
     const int b = b0 + tid;
-    int q0 = 0, q1 = 0, lk = 0, cnt = 0;
+    int q0 = 0, q1 = 0, lk = 0, k0 = 0, ch = 1, nch = 0, nrb = 0;
     if (b < a.batch) {
       seq_bounds(a.cu_q, b, a.total_q, q0, q1);
-      lk = min(max(a.seqlens_k[b], 0), a.max_k);
-      cnt = q1 > q0 ? max(1, (lk + a.chunk - 1) / a.chunk) : 0;
+      lk = kv_len(a, b, k0);
+      ch = kv_chunk_of(a, lk);
+      nch = max(1, (lk + ch - 1) / ch);
+      nrb = (int)(((int64_t)(q1 - q0) * a.n_rep + a.rows - 1) / a.rows);
     }
+    const int cnt = nrb * nch;
     // inclusive scan of the counts (Hillis-Steele over the workgroup)
     scan[tid] = cnt;
     __syncthreads();
@@ -304,68 +344,70 @@ __global__ __launch_bounds__(kPlanThreads) void kv_plan_kernel(KvArgs a) {
       __syncthreads();
     }
     const int base = s_base + scan[tid] - cnt;
-    for (int c = 0; c < cnt; ++c) a.chunks[base + c] = (KvChunk){b, c, q0, q1, lk, 0, 0, 0};
+    for (int e = 0; e < cnt; ++e)
+      if (base + e < a.cap) a.chunks[base + e] = (KvChunk){b, e / nch, e % nch, q0, q1, lk, k0, ch};
     __syncthreads();
     if (tid == kPlanThreads - 1) s_base += scan[tid];
     __syncthreads();
   }
-  if (tid == 0) a.plan[0] = s_base;
+  if (tid == 0) a.plan[0] = min(s_base, a.cap);
 }
 
 // Combines the chunks of every row block whose sequence has more than one:
 // LSE = log2 sum_c 2^LSE_c and O = sum_c 2^(LSE_c - LSE) O_c, in chunk order.
-// A workgroup is one (sequence, KV head, row block); eight threads per row.
+// Work items are (list entry of chunk 0 of a row block, KV head); the row
+// block's chunks are the entries that follow it.  Eight threads per row.
 template <int H16, int D>
 __global__ __launch_bounds__(KNT) void kv_merge_kernel(KvArgs a) {
   constexpr int TPR = 8, SEG = D / TPR;
-  const int item = (int)blockIdx.x;  // (b * hkv + g) * rblocks + rb
-  const int rb = item % a.rblocks;
-  const int g = (item / a.rblocks) % a.hkv;
-  const int b = item / a.rblocks / a.hkv;
-  int q0, q1;
-  seq_bounds(a.cu_q, b, a.total_q, q0, q1);
-  const int Lq = q1 - q0;
-  const int Lk = min(max(a.seqlens_k[b], 0), a.max_k);
-  const int nch = max(1, (Lk + a.chunk - 1) / a.chunk);
-  if (nch == 1) return;
+  const int n_items = uniform(a.plan[0]) * a.hkv;
   const int row = threadIdx.x / TPR, seg = threadIdx.x % TPR;
-  const int r = 32 * rb + row;
-  const int qpos = r / a.n_rep;
-  if (qpos >= Lq || row >= a.rows) return;
-  const int h = g * a.n_rep + (r - qpos * a.n_rep);
-  const size_t slot0 = (size_t)item * a.nchunk;
-  float mx = -INFINITY;
-  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.part_lse[(slot0 + c) * a.rows + row]);
-  f32x4_t acc[SEG / 4];
+  for (int item = (int)blockIdx.x; item < n_items; item += (int)gridDim.x) {
+    const int e0 = item / a.hkv, g = item % a.hkv;
+    const KvChunk ent = a.chunks[e0];
+    const int rb = uniform(ent.rb), c = uniform(ent.c);
+    const int q0 = uniform(ent.q0), Lq = uniform(ent.q1) - q0;
+    const int nch = max(1, (uniform(ent.lk) + uniform(ent.chunk) - 1) / uniform(ent.chunk));
+    if (c != 0 || nch == 1 || e0 + nch > a.cap) continue;
+    const int r = rb * a.rows + row;
+    const int qpos = r / a.n_rep;
+    if (qpos >= Lq || row >= a.rows) continue;
+    const int h = g * a.n_rep + (r - qpos * a.n_rep);
+    float mx = -INFINITY;
+    for (int cc = 0; cc < nch; ++cc)
+      mx = fmaxf(mx, a.part_lse[((size_t)(e0 + cc) * a.hkv + g) * a.rows + row]);
+    f32x4_t acc[SEG / 4];
 #pragma unroll
-  for (int e = 0; e < SEG / 4; ++e) acc[e] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (mx != -INFINITY) {
-    for (int c = 0; c < nch; ++c) {
-      const size_t sl = slot0 + c;
-      const float w = fast_exp2(a.part_lse[sl * a.rows + row] - mx);
-      wsum += w;
-      const f32x4_t* src = (const f32x4_t*)(a.part_o + (sl * a.rows + row) * D + seg * SEG);
+    for (int e = 0; e < SEG / 4; ++e) acc[e] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (mx != -INFINITY) {
+      for (int cc = 0; cc < nch; ++cc) {
+        const size_t sl = (size_t)(e0 + cc) * a.hkv + g;
+        const float w = fast_exp2(a.part_lse[sl * a.rows + row] - mx);
+        wsum += w;
+        const f32x4_t* src = (const f32x4_t*)(a.part_o + (sl * a.rows + row) * D + seg * SEG);
 #pragma unroll
-      for (int e = 0; e < SEG / 4; ++e) acc[e] += w * src[e];
+        for (int e = 0; e < SEG / 4; ++e) acc[e] += w * src[e];
+      }
     }
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  uint16_t* dst = (uint16_t*)a.out + ((size_t)(q0 + qpos) * a.hq + h) * D + seg * SEG;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    uint16_t* dst = (uint16_t*)a.out + ((size_t)(q0 + qpos) * a.hq + h) * D + seg * SEG;
 #pragma unroll
-  for (int e = 0; e < SEG / 4; ++e) {
-    const f32x4_t x = acc[e] * inv;
-    *(u32x2_t*)(dst + 4 * e) = (u32x2_t){pack16<H16>(x[0], x[1]), pack16<H16>(x[2], x[3])};
+    for (int e = 0; e < SEG / 4; ++e) {
+      const f32x4_t x = acc[e] * inv;
+      *(u32x2_t*)(dst + 4 * e) = (u32x2_t){pack16<H16>(x[0], x[1]), pack16<H16>(x[2], x[3])};
+    }
+    if (seg == 0)
+      a.lse[(size_t)h * a.total_q + q0 + qpos] = wsum > 0.f ? (mx + __builtin_log2f(wsum)) * kLn2 : -INFINITY;
   }
-  if (seg == 0)
-    a.lse[(size_t)h * a.total_q + q0 + qpos] = wsum > 0.f ? (mx + __builtin_log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 template <int H16, int D, bool CAUSAL>
 hipError_t launch_kv_t(const KvArgs& a, hipStream_t st) {
-  const int64_t items = (int64_t)a.batch * a.hkv * a.rblocks * a.nchunk;
-  auto kern = (1 << a.page_shift) >= KvShape<D>::KB ? kv_decode_kernel<H16, D, CAUSAL, true>
-                                                    : kv_decode_kernel<H16, D, CAUSAL, false>;
+  const int64_t items = (int64_t)a.cap * a.hkv;
+  auto kern = a.cu_k ? kv_decode_kernel<H16, D, CAUSAL, kRagged>
+             : (1 << a.page_shift) >= KvShape<D>::KB ? kv_decode_kernel<H16, D, CAUSAL, kPagedBig>
+                                                     : kv_decode_kernel<H16, D, CAUSAL, kPagedSmall>;
   const int grid = resident_grid((const void*)kern, KNT, (items + 3) / 4);
   if (grid <= 0) return hipErrorInvalidConfiguration;
   timing_before(st, "kvcache_plan");
@@ -378,8 +420,10 @@ hipError_t launch_kv_t(const KvArgs& a, hipStream_t st) {
   timing_after(st);
   e = hipGetLastError();
   if (e != hipSuccess || a.nchunk <= 1) return e;
+  int64_t mg = (int64_t)a.cap * a.hkv;
+  if (mg > 8192) mg = 8192;
   timing_before(st, "kvcache_merge");
-  hipLaunchKernelGGL((kv_merge_kernel<H16, D>), dim3((unsigned)(items / a.nchunk)), dim3(KNT), 0, st, a);
+  hipLaunchKernelGGL((kv_merge_kernel<H16, D>), dim3((unsigned)mg), dim3(KNT), 0, st, a);
   timing_after(st);
   return hipGetLastError();
 }
