@@ -126,8 +126,15 @@ typedef void* va_stream;
  * {64, 128}, an unknown dtype, a bias view spanning 2 GiB or more inside one
  * (sequence, head), or max_seqlen * row stride reaching 2 GiB (the kernels
  * address one sequence's rows with 32-bit byte offsets); VA_ERR_WORKSPACE for
- * too small a workspace; VA_ERR_HIP if a launch fails.  A bias with contiguous keys (bias_stride[3] = 1), strides that are
- * multiples of 4 and a base aligned to 4 elements is read 4 keys per load.
+ * too small a workspace; VA_ERR_HIP if a launch fails.  A bias with
+ * contiguous keys (bias_stride[3] = 1), strides that are multiples of 4 and a
+ * base aligned to 4 elements is read 4 keys per load.
+ * Short queries: with bf16 or float16 inputs, no bias, and max_seqlen_q <= 16
+ * (or <= 32 with max_seqlen_q * num_heads_q / num_heads_kv <= 128) -- decode
+ * steps, beams and drafts over contiguous K/V -- the call runs the decode
+ * kernels of include/va_kvcache.h (K/V read through cu_seqlens_k) instead of
+ * 128-row query tiles; results agree up to rounding order, and the hints
+ * still only size the work.
  */
 va_status va_varlen_fwd(const void* q, const void* k, const void* v,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

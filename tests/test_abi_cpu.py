@@ -308,18 +308,20 @@ def test_kvcache_workspace_size(lib):
     assert f(2, 1, 128, 8, 2, 128, F32) == 0         # not a decode dtype
     assert f(2, 1, 128, 8, 3, 128, BF16) == 0
 
-    def plan(entries):  # planner header + a 32-byte entry per (sequence, row block, chunk)
-        return 256 + _r(entries * 32)
+    def plan(entries, split=False):
+        # planner header, a 32-byte entry per (sequence, row block, chunk), and the merge
+        # list (an int per row block with several chunks: at most entries / 2)
+        return 256 + _r(entries * 32) + _r(max(entries // 2 if split else 0, 1) * 4)
     # chunks of at least 256 keys: a cache that fits one chunk needs no partials
     assert f(2, 1, 256, 8, 2, 128, BF16) == plan(2)
     assert f(2, 1, 0, 8, 2, 128, F16) == plan(2)
     # 4 KV heads x 2 sequences = 8 row blocks of n_rep * max_q = 4 rows want 1024 chunks
     # each: 512 keys split into two of 256; a partial slot per (entry, KV head)
     slots = 2 * 2 * 4
-    assert f(2, 1, 512, 16, 4, 128, BF16) == plan(2 * 2) + _r(slots * 4 * 128 * 4) + _r(slots * 4 * 4)
+    assert f(2, 1, 512, 16, 4, 128, BF16) == plan(2 * 2, True) + _r(slots * 4 * 128 * 4) + _r(slots * 4 * 4)
     # 12 new tokens x 4 heads per KV head = 48 rows: two row blocks of 32 rows per sequence
     slots = 2 * 2 * 2 * 4
-    assert f(2, 12, 512, 16, 4, 64, F16) == plan(2 * 2 * 2) + _r(slots * 32 * 64 * 4) + _r(slots * 32 * 4)
+    assert f(2, 12, 512, 16, 4, 64, F16) == plan(2 * 2 * 2, True) + _r(slots * 32 * 64 * 4) + _r(slots * 32 * 4)
     # a large batch keeps whole caches in one chunk when that already gives 8192 waves
     assert f(8192, 1, 4000, 8, 1, 128, BF16) == plan(8192)
 
@@ -333,9 +335,14 @@ def test_short_query_forward_workspace(lib):
     # blocks want 4 chunks each -> chunks of 256 keys, 4 per row block; the work list holds
     # (256 * 4 / 4 + 256) * 4 entries, each with a partial slot per KV head
     cap = (256 * 4 // 4 + 256) * 4
-    want = 256 + _r(cap * 32) + _r(cap * 8 * 4 * 128 * 4) + _r(cap * 8 * 4 * 4)
+    want = 256 + _r(cap * 32) + _r(cap // 2 * 4) + _r(cap * 8 * 4 * 128 * 4) + _r(cap * 8 * 4 * 4)
     assert f(256, 256, 256 * 1024, 1, 1024, 32, 8, 128, BF16) == want
     assert f(256, 256, 256 * 1024, 1, 1024, 32, 8, 128, F16) == want
-    # float32 and more than 32 rows keep the 128-row tiles' (much smaller) workspace
+    # float32, more than 32 tokens, or 17..32 tokens with more than 128 rows per KV head
+    # keep the 128-row tiles' (much smaller) workspace
     assert f(256, 256, 256 * 1024, 1, 1024, 32, 8, 128, F32) < want // 100
-    assert f(256, 256 * 9, 256 * 1024, 9, 1024, 32, 8, 128, BF16) < want // 100
+    assert f(256, 256 * 48, 256 * 1024, 48, 1024, 16, 16, 64, BF16) < want // 100
+    assert f(256, 256 * 20, 256 * 1024, 20, 1024, 32, 4, 128, BF16) < want // 100
+    # 16 tokens with 8 heads per KV head (128 rows) and 24 tokens with 4 (96 rows) do not
+    assert f(256, 256 * 16, 256 * 1024, 16, 1024, 32, 4, 128, BF16) > want // 100
+    assert f(256, 256 * 24, 256 * 1024, 24, 1024, 16, 4, 128, BF16) > want // 100

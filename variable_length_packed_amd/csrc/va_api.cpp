@@ -205,7 +205,7 @@ size_t bwd_workspace(int batch, int total_q, int total_k, int max_q, int max_k, 
 // from total_q when it is only a hint (the packed forward's short-query path).
 constexpr int64_t kKvWaves = 8192;
 struct KvLayout {
-  int rows = 1, chunk = 1, nchunk = 1, cap = 1;
+  int rows = 1, chunk = 1, nchunk = 1, cap = 1, cap_merge = 0;
   size_t plan_bytes = 0, part_o_bytes = 0, part_lse_bytes = 0;
   size_t total() const { return plan_bytes + part_o_bytes + part_lse_bytes; }
 };
@@ -227,7 +227,9 @@ KvLayout kv_layout(int batch, int max_q, int max_k, int hq, int hkv, int d, int6
   const int64_t row_blocks = total_q < 0 ? (int64_t)batch * rb_hint
                                          : (total_q * n_rep + L.rows - 1) / L.rows + batch;
   L.cap = (int)(row_blocks * L.nchunk);
-  L.plan_bytes = round_up(256) + round_up((size_t)L.cap * sizeof(va::KvChunk));
+  L.cap_merge = L.nchunk > 1 ? L.cap / 2 : 0;  // a merged row block has >= 2 entries
+  L.plan_bytes = round_up(256) + round_up((size_t)L.cap * sizeof(va::KvChunk)) +
+                 round_up((size_t)(L.cap_merge > 0 ? L.cap_merge : 1) * sizeof(int32_t));
   if (L.nchunk > 1) {
     const size_t slots = (size_t)L.cap * hkv;
     L.part_o_bytes = round_up(slots * L.rows * d * sizeof(float));
@@ -236,16 +238,24 @@ KvLayout kv_layout(int batch, int max_q, int max_k, int hq, int hkv, int d, int6
   return L;
 }
 
-// The packed forward's short-query path: with 16-bit inputs, no bias and at
-// most 32 (new token, query head) rows per KV head and sequence (by the
-// max_seqlen_q hint) -- decode steps, beams, short drafts over contiguous
-// K/V -- the decode kernels run instead of 128-row query tiles.  They read
-// K/V through cu_seqlens_k and the token strides; every result is the same
-// up to rounding order, and sequences longer than the hints still get every
-// row and key (more row blocks, longer chunks).
-constexpr int64_t kShortQueryRows = 32;
+// The packed forward's short-query path: with 16-bit inputs, no bias and
+// few new tokens per sequence (by the max_seqlen_q hint) -- decode steps,
+// beams, drafts, short chunks over contiguous K/V -- the decode kernels run
+// instead of 128-row query tiles, which such rows would mostly leave empty.
+// Measured on MI355X (one call, 64 sequences of 2,048-4,096 keys): 16 tokens
+// x 8 query heads per KV head 64 against 112 us, 8 x 16 199 against 738 us,
+// 32 x 4 106 against 118 us; the tiles win from 48 tokens (41 against 48 us)
+// and at 64 x 2 (129 against 194 us).  Hence: at most 16 tokens, or at most
+// 32 with at most 128 (token, head) rows per KV head.  The decode kernels read
+// K/V through cu_seqlens_k and the token strides; every result is the same up
+// to rounding order, and sequences longer than the hints still get every row
+// and key (more row blocks, longer chunks).
+constexpr int kShortQueryTokens = 16, kShortQueryTokensMax = 32;
+constexpr int64_t kShortQueryRows = 128;
 bool short_query(va_dtype dtype, int max_q, int n_rep) {
-  return dtype != VA_F32 && (int64_t)max_q * n_rep <= kShortQueryRows;
+  return dtype != VA_F32 &&
+         (max_q <= kShortQueryTokens ||
+          (max_q <= kShortQueryTokensMax && (int64_t)max_q * n_rep <= kShortQueryRows));
 }
 
 bool kv_args_ok(int32_t batch, int32_t max_q, int32_t max_k, int32_t hq, int32_t hkv, int32_t d,
@@ -339,13 +349,14 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
     char* w = (char*)workspace;
     a.plan = (int32_t*)w;
     a.chunks = (va::KvChunk*)(w + round_up(256));
+    a.merges = (int32_t*)(w + round_up(256) + round_up((size_t)L.cap * sizeof(va::KvChunk)));
     a.part_o = L.part_o_bytes > 0 ? (float*)(w + L.plan_bytes) : nullptr;
     a.part_lse = L.part_lse_bytes > 0 ? (float*)(w + L.plan_bytes + L.part_o_bytes) : nullptr;
     a.batch = batch; a.total_q = total_q;
     a.hq = num_heads_q; a.hkv = num_heads_kv; a.n_rep = num_heads_q / num_heads_kv; a.d = head_dim;
     a.num_pages = 1;
     a.max_k = max_seqlen_k;
-    a.rows = L.rows; a.chunk = L.chunk; a.nchunk = L.nchunk; a.cap = L.cap;
+    a.rows = L.rows; a.chunk = L.chunk; a.nchunk = L.nchunk; a.cap = L.cap; a.cap_merge = L.cap_merge;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.causal = causal;
     a.h16 = elem_code(dtype);
@@ -573,6 +584,7 @@ va_status va_kvcache_fwd(const void* q, const void* k_cache, const void* v_cache
   char* w = (char*)workspace;
   a.plan = (int32_t*)w;
   a.chunks = (va::KvChunk*)(w + round_up(256));
+  a.merges = (int32_t*)(w + round_up(256) + round_up((size_t)L.cap * sizeof(va::KvChunk)));
   a.part_o = L.part_o_bytes > 0 ? (float*)(w + L.plan_bytes) : nullptr;
   a.part_lse = L.part_lse_bytes > 0 ? (float*)(w + L.plan_bytes + L.part_o_bytes) : nullptr;
   a.batch = batch; a.total_q = total_q;
@@ -584,7 +596,7 @@ va_status va_kvcache_fwd(const void* q, const void* k_cache, const void* v_cache
   a.num_pages = num_pages;
   const int64_t reach = (int64_t)block_table_stride * page_size;
   a.max_k = (int)(reach < max_seqlen_k ? reach : max_seqlen_k);
-  a.rows = L.rows; a.chunk = L.chunk; a.nchunk = L.nchunk; a.cap = L.cap;
+  a.rows = L.rows; a.chunk = L.chunk; a.nchunk = L.nchunk; a.cap = L.cap; a.cap_merge = L.cap_merge;
   a.q_rs = (int64_t)num_heads_q * head_dim;
   a.k_rs = a.v_rs = (int64_t)num_heads_kv * head_dim;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;

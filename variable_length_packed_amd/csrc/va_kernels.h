@@ -154,14 +154,16 @@ struct KvArgs {
   float* lse;                // [hq, total_q]
   float* part_o;
   float* part_lse;
-  int32_t* plan;             // [0] = entries in `chunks` (written by the planner)
-  KvChunk* chunks;           // [batch * nchunk] at most
+  int32_t* plan;             // [0] entries in `chunks`, [1] in `merges` (written by the planner)
+  KvChunk* chunks;           // [cap]
+  int32_t* merges;           // [cap_merge] list entry of chunk 0 of each row block with several chunks
   int32_t batch, total_q, hq, hkv, n_rep, d;
   int32_t bt_stride, page_shift, num_pages;
   int32_t max_k;             // paged: keys of a sequence are capped here (max_seqlen_k and the table's reach)
   int32_t rows;              // partial rows per slot
   int32_t chunk, nchunk;     // keys per chunk (a multiple of the step); most chunks of a row block
   int32_t cap;               // most list entries (and partial slots per KV head)
+  int32_t cap_merge;         // most row blocks with several chunks (cap / 2)
   float scale_log2;
   int32_t causal;
   int32_t h16;               // 1 bfloat16, 2 float16

@@ -318,10 +318,10 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
 // dropped, which only bad metadata can cause.
 constexpr int kPlanThreads = 1024;
 __global__ __launch_bounds__(kPlanThreads) void kv_plan_kernel(KvArgs a) {
-  __shared__ int scan[kPlanThreads];
-  __shared__ int s_base;
+  __shared__ int scan[kPlanThreads], mscan[kPlanThreads];
+  __shared__ int s_base, s_mbase;
   const int tid = threadIdx.x;
-  if (tid == 0) s_base = 0;
+  if (tid == 0) s_base = s_mbase = 0;
   __syncthreads();
   for (int b0 = 0; b0 < a.batch; b0 += kPlanThreads) {
     const int b = b0 + tid;
@@ -333,42 +333,54 @@ __global__ __launch_bounds__(kPlanThreads) void kv_plan_kernel(KvArgs a) {
       nch = max(1, (lk + ch - 1) / ch);
       nrb = (int)(((int64_t)(q1 - q0) * a.n_rep + a.rows - 1) / a.rows);
     }
-    const int cnt = nrb * nch;
-    // inclusive scan of the counts (Hillis-Steele over the workgroup)
+    const int cnt = nrb * nch;                // list entries of the sequence
+    const int mcnt = nch > 1 ? nrb : 0;        // its row blocks that need a merge
+    // inclusive scans of both counts (Hillis-Steele over the workgroup)
     scan[tid] = cnt;
+    mscan[tid] = mcnt;
     __syncthreads();
     for (int o = 1; o < kPlanThreads; o <<= 1) {
-      const int add = tid >= o ? scan[tid - o] : 0;
+      const int add = tid >= o ? scan[tid - o] : 0, madd = tid >= o ? mscan[tid - o] : 0;
       __syncthreads();
       scan[tid] += add;
+      mscan[tid] += madd;
       __syncthreads();
     }
-    const int base = s_base + scan[tid] - cnt;
+    const int base = s_base + scan[tid] - cnt, mbase = s_mbase + mscan[tid] - mcnt;
     for (int e = 0; e < cnt; ++e)
       if (base + e < a.cap) a.chunks[base + e] = (KvChunk){b, e / nch, e % nch, q0, q1, lk, k0, ch};
+    for (int r = 0; r < mcnt; ++r)
+      if (mbase + r < a.cap_merge) a.merges[mbase + r] = base + r * nch;  // entry of chunk 0
     __syncthreads();
-    if (tid == kPlanThreads - 1) s_base += scan[tid];
+    if (tid == kPlanThreads - 1) {
+      s_base += scan[tid];
+      s_mbase += mscan[tid];
+    }
     __syncthreads();
   }
-  if (tid == 0) a.plan[0] = min(s_base, a.cap);
+  if (tid == 0) {
+    a.plan[0] = min(s_base, a.cap);
+    a.plan[1] = min(s_mbase, a.cap_merge);
+  }
 }
 
-// Combines the chunks of every row block whose sequence has more than one:
+// Combines the chunks of every row block that has more than one:
 // LSE = log2 sum_c 2^LSE_c and O = sum_c 2^(LSE_c - LSE) O_c, in chunk order.
-// Work items are (list entry of chunk 0 of a row block, KV head); the row
-// block's chunks are the entries that follow it.  Eight threads per row.
+// Work items are (row block of the planner's merge list, KV head); the list
+// holds the entry of the block's chunk 0, and its other chunks are the
+// entries that follow it.  Eight threads per row.
 template <int H16, int D>
 __global__ __launch_bounds__(KNT) void kv_merge_kernel(KvArgs a) {
   constexpr int TPR = 8, SEG = D / TPR;
-  const int n_items = uniform(a.plan[0]) * a.hkv;
+  const int n_items = uniform(a.plan[1]) * a.hkv;
   const int row = threadIdx.x / TPR, seg = threadIdx.x % TPR;
   for (int item = (int)blockIdx.x; item < n_items; item += (int)gridDim.x) {
-    const int e0 = item / a.hkv, g = item % a.hkv;
+    const int e0 = uniform(a.merges[item / a.hkv]), g = item % a.hkv;
     const KvChunk ent = a.chunks[e0];
-    const int rb = uniform(ent.rb), c = uniform(ent.c);
+    const int rb = uniform(ent.rb);
     const int q0 = uniform(ent.q0), Lq = uniform(ent.q1) - q0;
     const int nch = max(1, (uniform(ent.lk) + uniform(ent.chunk) - 1) / uniform(ent.chunk));
-    if (c != 0 || nch == 1 || e0 + nch > a.cap) continue;
+    if (nch == 1 || e0 + nch > a.cap) continue;
     const int r = rb * a.rows + row;
     const int qpos = r / a.n_rep;
     if (qpos >= Lq || row >= a.rows) continue;
@@ -420,8 +432,9 @@ hipError_t launch_kv_t(const KvArgs& a, hipStream_t st) {
   timing_after(st);
   e = hipGetLastError();
   if (e != hipSuccess || a.nchunk <= 1) return e;
-  int64_t mg = (int64_t)a.cap * a.hkv;
-  if (mg > 8192) mg = 8192;
+  int64_t mg = (int64_t)a.cap_merge * a.hkv;
+  if (mg > 2048) mg = 2048;
+  if (mg < 1) mg = 1;
   timing_before(st, "kvcache_merge");
   hipLaunchKernelGGL((kv_merge_kernel<H16, D>), dim3((unsigned)mg), dim3(KNT), 0, st, a);
   timing_after(st);
