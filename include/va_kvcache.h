@@ -24,12 +24,13 @@
  * every key); a row that sees no key (an empty cache) gets O = 0 and
  * LSE = -inf.  Query head h reads KV head h / (Hq / Hkv).
  *
- * How.  One wave per (sequence, KV head, 32 rows of (new token, query head),
- * chunk of keys): every K/V byte of a KV head is read once for all the query
- * heads of its group; long caches are split over chunks whose partial
- * results a last kernel merges in chunk order (deterministic).  A first
- * one-workgroup kernel lists the chunks that have work.  The step is bound
- * by HBM bandwidth (K and V read once).
+ * How.  One wave per (sequence, KV head, block of up to 32 rows of (new
+ * token, query head), chunk of keys): every K/V byte of a KV head is read
+ * once per row block for all the query heads of its group; long caches are
+ * split over chunks whose partial results a last kernel merges in chunk order
+ * (deterministic).  A first one-workgroup kernel lists the (sequence, row
+ * block, chunk) triples that have work, from the true lengths.  The step is
+ * bound by HBM bandwidth (K and V read once).
  *
  * Memory safety against bad metadata: a sequence's length is clamped to
  * [0, min(max_seqlen_k, block_table_stride * page_size)], page indices to
@@ -53,9 +54,9 @@ extern "C" {
 
 /*
  * Bytes of device workspace va_kvcache_fwd needs: the work list (a planner
- * kernel lists the (sequence, key chunk) pairs that have work, so the waves
- * share them evenly) and, when caches can be longer than one chunk, float32
- * partial results.  The split of long caches into chunks, and so this size,
+ * kernel lists the (sequence, row block, key chunk) triples that have work,
+ * so the waves share them evenly) and, when caches can be longer than one
+ * chunk, float32 partial results.  The split of long caches into chunks, and so this size,
  * depends only on these arguments.  Returns 0 for arguments the call would
  * reject.
  */
@@ -65,7 +66,9 @@ size_t va_kvcache_fwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_
 
 /*
  * Decode-step attention against a paged cache (layout above).
- *   max_seqlen_q      >= every Lq (a bound; sizes the row blocks), > 0
+ *   max_seqlen_q      >= every Lq (a bound; sizes the row blocks and the work
+ *                     list: rows of a longer sequence past the list are not
+ *                     computed), > 0
  *   max_seqlen_k      >= every seqlens_k[b] (a bound; sizes the chunks), >= 0
  *   block_table_stride int32 entries per block-table row; must cover
  *                     max_seqlen_k: stride * page_size >= max_seqlen_k
