@@ -88,7 +88,7 @@ extern "C" {
 typedef enum {
   VA_OK = 0,
   VA_ERR_INVALID = 1,     /* null pointer, zero/negative size, Hq % Hkv != 0, bad stride */
-  VA_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, unknown dtype, bf16 grads of fp32 inputs */
+  VA_ERR_UNSUPPORTED = 2, /* head_dim not supported, unknown dtype, bf16 grads of fp32 inputs */
   VA_ERR_WORKSPACE = 3,   /* workspace smaller than va_varlen_{fwd,bwd}_workspace_size() */
   VA_ERR_HIP = 4          /* the HIP runtime reported an error; text in va_last_error() */
 } va_status;
@@ -117,13 +117,13 @@ typedef void* va_stream;
  *   qkv_row_stride     NULL or HOST int64[3] token strides of q, k, v (above)
  *   workspace          device scratch of at least va_varlen_fwd_workspace_size()
  *                      bytes, 256-byte aligned
- *   head_dim           64 or 128
+ *   head_dim           32, 64, 96 or 128 (multiples of the 32-wide MFMA output tile)
  * Returns VA_ERR_INVALID for a NULL required pointer, exactly one of
  * bias/bias_stride NULL, batch/total/heads/head_dim <= 0, Hq % Hkv != 0,
  * max_seqlen <= 0, a negative stride, a scale that is not finite and > 0, a
  * misaligned workspace, a row stride below num_heads * head_dim or rows or
  * bases of q/k/v not 16-byte aligned; VA_ERR_UNSUPPORTED for head_dim not in
- * {64, 128}, an unknown dtype, a bias view spanning 2 GiB or more inside one
+ * {32, 64, 96, 128}, an unknown dtype, a bias view spanning 2 GiB or more inside one
  * (sequence, head), or max_seqlen * row stride reaching 2 GiB (the kernels
  * address one sequence's rows with 32-bit byte offsets); VA_ERR_WORKSPACE for
  * too small a workspace; VA_ERR_HIP if a launch fails.  A bias with

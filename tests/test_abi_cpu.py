@@ -91,8 +91,9 @@ def _fwd(lib, **kw):
     (dict(bias=P, bstr=(1, -1, 1, 1)), INVALID),
     (dict(ws=None), INVALID),
     (dict(ws=0x100040), INVALID),      # misaligned workspace
-    (dict(d=96), UNSUPPORTED),
+    (dict(d=80), UNSUPPORTED),
     (dict(d=256), UNSUPPORTED),
+    (dict(d=16), UNSUPPORTED),
     (dict(dt=7), UNSUPPORTED),
     (dict(dt=3), UNSUPPORTED),
     (dict(wsb=16), WORKSPACE),
@@ -129,7 +130,7 @@ def _bwd(lib, **kw):
     (dict(ws=0x100010), INVALID),      # misaligned workspace
     (dict(tq=0), INVALID),
     (dict(hq=3, hkv=2), INVALID),
-    (dict(d=32), UNSUPPORTED),
+    (dict(d=48), UNSUPPORTED),
     (dict(dt=F32, gdt=BF16), UNSUPPORTED),
     (dict(dt=BF16, gdt=F16), UNSUPPORTED),     # 16-bit gradients only in the input's format
     (dict(dt=F16, gdt=BF16), UNSUPPORTED),
@@ -164,7 +165,8 @@ def test_fwd_workspace_size(lib):
     assert f(0, 16, 16, 8, 8, 4, 2, 64, BF16) == 0
     assert f(2, 16, 16, 0, 8, 4, 2, 64, BF16) == 0
     assert f(2, 16, 16, 8, 8, 4, 3, 64, BF16) == 0
-    assert f(2, 16, 16, 8, 8, 4, 2, 96, BF16) == 0
+    assert f(2, 16, 16, 8, 8, 4, 2, 80, BF16) == 0
+    assert f(2, 16, 16, 8, 8, 4, 2, 96, BF16) > 0 and f(2, 16, 16, 8, 8, 4, 2, 32, F32) > 0
     # no tile can see more than 1024 keys: only the plan (<= total/128 + batch units)
     assert f(2, 16, 16, 8, 8, 4, 2, 64, BF16) == _plan_bytes(2, 0)
     assert f(20, 10459, 10459, 1024, 1024, 14, 2, 64, BF16) == _plan_bytes(10459 // 128 + 20, 0)
@@ -183,7 +185,8 @@ def test_bwd_workspace_size(lib):
     f = lib.va_varlen_bwd_workspace_size
     assert f(0, 16, 16, 8, 8, 4, 2, 64, BF16, F32) == 0
     assert f(2, 16, 16, 8, 8, 4, 3, 64, BF16, F32) == 0
-    assert f(2, 16, 16, 8, 8, 4, 2, 96, BF16, F32) == 0
+    assert f(2, 16, 16, 8, 8, 4, 2, 80, BF16, F32) == 0
+    assert f(2, 16, 16, 8, 8, 4, 2, 96, BF16, F32) > 0
     assert f(2, 16, 16, 8, 8, 4, 2, 64, F32, BF16) == 0
     assert f(2, 16, 16, 8, 8, 4, 2, 64, BF16, F16) == 0
     # float16 plans exactly as bf16 (same 64-key steps, same unit sizes)

@@ -131,7 +131,7 @@ def test_python_errors_on_gpu_tensors():
     with pytest.raises(ValueError):  # zero-length batch (empty cu_seqlens)
         va.va_varlen_fwd(inp["q"], inp["k"], inp["v"], inp["cu_q"][:1], inp["cu_k"][:1], 5, 5)
     with pytest.raises(ValueError):  # unsupported head dim
-        q = torch.zeros(12, 2, 96, dtype=torch.bfloat16, device=_gpu.DEV)
+        q = torch.zeros(12, 2, 80, dtype=torch.bfloat16, device=_gpu.DEV)
         va.va_varlen_fwd(q, q, q, inp["cu_q"], inp["cu_k"], 7, 7)
     with pytest.raises(ValueError):  # non-contiguous input
         va.va_varlen_fwd(inp["q"].transpose(0, 1), inp["k"], inp["v"], inp["cu_q"], inp["cu_k"], 7, 7)

@@ -30,6 +30,11 @@ va_status fail(va_status s, const char* fmt, ...) {
   return s;
 }
 
+// Head dims of the packed forward and backward (multiples of the 32-wide
+// MFMA output tile); the decode kernels take 64 and 128.
+bool varlen_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+bool decode_head_dim(int d) { return d == 64 || d == 128; }
+
 struct Common {
   int batch, total_q, total_k, hq, hkv, d, max_q, max_k;
   int causal;
@@ -57,7 +62,8 @@ va_status check_common(const Common& c, float scale, const void* bias, const int
       if (bstride[i] < 0) return fail(VA_ERR_INVALID, "bias_stride[%d] is negative", i);
   if (c.dtype != VA_F32 && c.dtype != VA_BF16 && c.dtype != VA_F16)
     return fail(VA_ERR_UNSUPPORTED, "unknown dtype %d", (int)c.dtype);
-  if (c.d != 64 && c.d != 128) return fail(VA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", c.d);
+  if (!varlen_head_dim(c.d))
+    return fail(VA_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64, 96 or 128)", c.d);
   if ((int64_t)c.total_q * c.hq * c.d >= ((int64_t)1 << 40) ||
       (int64_t)c.total_k * c.hkv * c.d >= ((int64_t)1 << 40))
     return fail(VA_ERR_UNSUPPORTED, "tensor too large");
@@ -252,8 +258,8 @@ KvLayout kv_layout(int batch, int max_q, int max_k, int hq, int hkv, int d, int6
 // and key (more row blocks, longer chunks).
 constexpr int kShortQueryTokens = 16, kShortQueryTokensMax = 32;
 constexpr int64_t kShortQueryRows = 128;
-bool short_query(va_dtype dtype, int max_q, int n_rep) {
-  return dtype != VA_F32 &&
+bool short_query(va_dtype dtype, int d, int max_q, int n_rep) {
+  return dtype != VA_F32 && decode_head_dim(d) &&
          (max_q <= kShortQueryTokens ||
           (max_q <= kShortQueryTokensMax && (int64_t)max_q * n_rep <= kShortQueryRows));
 }
@@ -261,7 +267,7 @@ bool short_query(va_dtype dtype, int max_q, int n_rep) {
 bool kv_args_ok(int32_t batch, int32_t max_q, int32_t max_k, int32_t hq, int32_t hkv, int32_t d,
                 va_dtype dtype) {
   return batch > 0 && max_q > 0 && max_k >= 0 && hq > 0 && hkv > 0 && hq % hkv == 0 &&
-         (d == 64 || d == 128) && (dtype == VA_BF16 || dtype == VA_F16) &&
+         decode_head_dim(d) && (dtype == VA_BF16 || dtype == VA_F16) &&
          (int64_t)max_q * hq * d * 2 < ((int64_t)1 << 31);
 }
 
@@ -297,10 +303,10 @@ size_t va_varlen_fwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
                                     va_dtype dtype) {
   if (batch <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 ||
       num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0 ||
-      (head_dim != 64 && head_dim != 128) || (dtype != VA_F32 && dtype != VA_BF16 && dtype != VA_F16))
+      !varlen_head_dim(head_dim) || (dtype != VA_F32 && dtype != VA_BF16 && dtype != VA_F16))
     return 0;
   size_t n = fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, dtype != VA_F32);
-  if (short_query(dtype, max_seqlen_q, num_heads_q / num_heads_kv)) {
+  if (short_query(dtype, head_dim, max_seqlen_q, num_heads_q / num_heads_kv)) {
     const size_t m = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
                                total_q).total();
     if (m > n) n = m;
@@ -335,7 +341,7 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
     return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
 
   hipStream_t st = (hipStream_t)stream;
-  if (!bias && short_query(dtype, max_seqlen_q, num_heads_q / num_heads_kv)) {
+  if (!bias && short_query(dtype, head_dim, max_seqlen_q, num_heads_q / num_heads_kv)) {
     const KvLayout L = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
                                  total_q);
     if (workspace_bytes < L.total())
@@ -409,7 +415,7 @@ size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
                                     va_dtype dtype, va_dtype grad_dtype) {
   if (batch <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 ||
       num_heads_q <= 0 || num_heads_kv <= 0 ||
-      num_heads_q % num_heads_kv != 0 || (head_dim != 64 && head_dim != 128) ||
+      num_heads_q % num_heads_kv != 0 || !varlen_head_dim(head_dim) ||
       (dtype != VA_F32 && dtype != VA_BF16 && dtype != VA_F16) ||
       (grad_dtype != VA_F32 && grad_dtype != dtype))
     return 0;
@@ -567,8 +573,8 @@ va_status va_kvcache_fwd(const void* q, const void* k_cache, const void* v_cache
     return fail(VA_ERR_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned");
   if (dtype != VA_BF16 && dtype != VA_F16)
     return fail(VA_ERR_UNSUPPORTED, "decode steps take bf16 or float16 (got dtype %d)", (int)dtype);
-  if (head_dim != 64 && head_dim != 128)
-    return fail(VA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (!decode_head_dim(head_dim))
+    return fail(VA_ERR_UNSUPPORTED, "head_dim %d not supported in decode steps (64 or 128)", head_dim);
   if (!kv_args_ok(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, dtype))
     return fail(VA_ERR_UNSUPPORTED, "max_seqlen_q * num_heads_q * head_dim * 2 must be < 2^31");
   const KvLayout L = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);

@@ -72,14 +72,13 @@ struct Stager {
   static constexpr int TPT = (PAIRS + NT - 1) / NT;      // tasks per thread
   static constexpr int NP = D + 16 / (int)sizeof(T);     // row pitch (elements)
   static constexpr int TP = ROWS + 16 / (int)sizeof(T);  // transposed pitch
-  static_assert(PAIRS % NT == 0 || PAIRS < NT, "stager tasks");
   u32x4_t r[2 * TPT];
 
   __device__ __forceinline__ void load(rsrc_t res, int row_bytes, int row0) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int u = threadIdx.x + i * NT;
-      if (PAIRS < NT && u >= PAIRS) continue;
+      if (PAIRS % NT != 0 && u >= PAIRS) continue;  // a partial last round
       const int c = u % CH, p = u / CH;
 #pragma unroll
       for (int e = 0; e < 2; ++e) r[2 * i + e] = buf_load16(res, (row0 + 2 * p + e) * row_bytes + c * 16);
@@ -90,7 +89,7 @@ struct Stager {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int u = threadIdx.x + i * NT;
-      if (PAIRS < NT && u >= PAIRS) continue;
+      if (PAIRS % NT != 0 && u >= PAIRS) continue;  // a partial last round
       const int c = u % CH, p = u / CH;
       *(u32x4_t*)(dn + (2 * p) * NP + c * EPV) = r[2 * i];
       *(u32x4_t*)(dn + (2 * p + 1) * NP + c * EPV) = r[2 * i + 1];
@@ -178,6 +177,16 @@ __device__ __forceinline__ void pack8(const float* v, u32x4_t& hi, u32x4_t* lo) 
 // ---------------------------------------------------------------- preprocess
 // One launch: workgroups 0 and 1 build the dK/dV and dQ work plans while the
 // others compute D = rowsum(dO * O) for every (query row, head).
+// Threads per (token, head) row of the D pass: one per 16-byte piece, padded
+// to a power of two so the row's sum is a butterfly inside an aligned group.
+template <int H16, int D>
+constexpr int dsum_tpr() {
+  constexpr int n = D / (H16 ? 8 : 4);
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
 template <int H16, int D>
 __global__ __launch_bounds__(plan::PT) void plan_dsum_kernel(BwdArgs a, PlanSet ps) {
   __shared__ plan::PlanShared sh;
@@ -187,12 +196,13 @@ __global__ __launch_bounds__(plan::PT) void plan_dsum_kernel(BwdArgs a, PlanSet 
   }
   using T = elem_t<H16>;
   constexpr int EPV = 16 / sizeof(T);
-  constexpr int TPR = D / EPV;  // threads per (token, head) row
+  constexpr int TPR = dsum_tpr<H16, D>();  // threads per (token, head) row; the first D / EPV load
+  static_assert(plan::PT % TPR == 0, "rows must not straddle workgroups");
   const int64_t rows = (int64_t)a.total_q * a.hq;
   const int64_t row = ((int64_t)(blockIdx.x - 2) * plan::PT + threadIdx.x) / TPR;
   const int c = threadIdx.x % TPR;
   float s = 0.f;
-  if (row < rows) {
+  if (row < rows && c < D / EPV) {
     const T* o = (const T*)a.out + row * D + c * EPV;
     const T* g = (const T*)a.dout + row * D + c * EPV;
     if constexpr (H16) {
@@ -233,7 +243,7 @@ struct DkdvSmem {
 };
 
 template <int H16, int D>
-constexpr int dkdv_min_blocks() { return D == 64 ? 2 : 1; }
+constexpr int dkdv_min_blocks() { return D <= 64 ? 2 : 1; }
 
 template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
 __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(BwdArgs a) {
@@ -588,7 +598,7 @@ __global__ __launch_bounds__(NT) void dkdv_merge_kernel(BwdArgs a) {
 template <int H16, int D>
 struct DqSmem {
   using T = elem_t<H16>;
-  static constexpr int BN = (H16 && D == 64) ? 64 : 32;
+  static constexpr int BN = (H16 && D <= 64) ? 64 : 32;
   using St = Stager<H16, BN, D, true>;
   using Sv = Stager<H16, BN, D, false>;
   T kn[2][BN * St::NP];
@@ -882,8 +892,7 @@ template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
 hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, int64_t k_items,
                         hipStream_t st) {
   {
-    constexpr int EPV = H16 ? 8 : 4;
-    const int64_t threads = (int64_t)a.total_q * a.hq * (D / EPV);
+    const int64_t threads = (int64_t)a.total_q * a.hq * dsum_tpr<H16, D>();
     const int64_t grid = 2 + (threads + plan::PT - 1) / plan::PT;
     timing_before(st, "bwd_plan_dsum");
     hipLaunchKernelGGL((plan_dsum_kernel<H16, D>), dim3((unsigned)grid), dim3(plan::PT), 0, st, a, ps);
@@ -948,20 +957,27 @@ int bwd_block_q() { return BMQ_DQ; }
 int bwd_block_k() { return BNK; }
 int bwd_dkdv_block_q() { return BMQ; }
 int bwd_dq_block_n(bool bf16, int d) {
-  if (bf16) return d == 64 ? DqSmem<true, 64>::BN : DqSmem<true, 128>::BN;
-  return d == 64 ? DqSmem<false, 64>::BN : DqSmem<false, 128>::BN;
+  if (bf16) return d <= 64 ? DqSmem<1, 64>::BN : DqSmem<1, 128>::BN;
+  return DqSmem<0, 64>::BN;
+}
+
+template <int H16>
+static hipError_t launch_bwd_h(const BwdArgs& a, const PlanSet& ps, int64_t q_items, int64_t k_items,
+                               hipStream_t st) {
+  switch (a.d) {
+    case 32: return launch_bwd_d<H16, 32>(a, ps, q_items, k_items, st);
+    case 64: return launch_bwd_d<H16, 64>(a, ps, q_items, k_items, st);
+    case 96: return launch_bwd_d<H16, 96>(a, ps, q_items, k_items, st);
+    case 128: return launch_bwd_d<H16, 128>(a, ps, q_items, k_items, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, const PlanSet& ps, int64_t q_items, int64_t k_items,
                       hipStream_t st) {
-  if (a.bf16 == 2)
-    return a.d == 64 ? launch_bwd_d<2, 64>(a, ps, q_items, k_items, st)
-                     : launch_bwd_d<2, 128>(a, ps, q_items, k_items, st);
-  if (a.bf16)
-    return a.d == 64 ? launch_bwd_d<1, 64>(a, ps, q_items, k_items, st)
-                     : launch_bwd_d<1, 128>(a, ps, q_items, k_items, st);
-  return a.d == 64 ? launch_bwd_d<0, 64>(a, ps, q_items, k_items, st)
-                   : launch_bwd_d<0, 128>(a, ps, q_items, k_items, st);
+  if (a.bf16 == 2) return launch_bwd_h<2>(a, ps, q_items, k_items, st);
+  if (a.bf16) return launch_bwd_h<1>(a, ps, q_items, k_items, st);
+  return launch_bwd_h<0>(a, ps, q_items, k_items, st);
 }
 
 }  // namespace va

@@ -106,10 +106,10 @@ struct WaveTiles {
 template <int H16, int D>
 constexpr int block_m() { return 4 * 32 * WaveTiles<H16, D>::value; }
 
-// d = 64: two workgroups per CU (256 registers per lane); d = 128: one, with
-// the accumulators free to use the whole 512-entry register file.
+// d <= 64: two workgroups per CU (256 registers per lane); d = 96, 128: one,
+// with the accumulators free to use the whole 512-entry register file.
 template <int H16, int D>
-constexpr int min_blocks() { return D == 64 ? 2 : 1; }
+constexpr int min_blocks() { return D <= 64 ? 2 : 1; }
 
 template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
 __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs a) {
@@ -477,8 +477,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     // on neither.  The row sums add the bf16-rounded P that the PV MFMAs use.
     constexpr int NCH = 2 * NS;  // 16-key chunks per block
     auto step_fast = [&](int n, f32x16_t (&sc)[QT][NS], f32x16_t (&sn)[QT][NS]) __attribute__((always_inline)) {
-      if constexpr (QT == 1 && H16 && !HAS_BIAS) {
-      static_assert(QF % NCH == 0, "whole k-steps per round");
+      if constexpr (QT == 1 && H16 && !HAS_BIAS && QF % NCH == 0) {
       constexpr int KPR = QF / NCH;  // S k-steps per round
       const int kb = kb0 + n * BN;
       const int kbuf = (n + 1) & 1, vbuf = n & 1;
@@ -637,7 +636,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     // unmasked blocks, then the (at most a few) masked ones: two loops, so the
     // accumulators never merge from two code paths inside a loop
     int j = 0;
-    if constexpr (H16 && !HAS_BIAS && QT == 1) {
+    if constexpr (H16 && !HAS_BIAS && QT == 1 && QF % NCH == 0) {
       f32x16_t s_alt[QT][NS];
       for (; j + 1 < j_plain; j += 2) {
         step_fast(j, s_cur, s_alt);
@@ -791,14 +790,25 @@ static hipError_t launch_fwd_d(const FwdArgs& a, int64_t grid, hipStream_t st) {
 
 int fwd_block_m() { return block_m<true, 64>(); }
 int fwd_block_n(bool bf16, int d) {
-  if (bf16) return d == 64 ? BlockN<true, 64>::value : BlockN<true, 128>::value;
-  return d == 64 ? BlockN<false, 64>::value : BlockN<false, 128>::value;
+  (void)d;  // keys per block depend only on the element size
+  return bf16 ? BlockN<1, 64>::value : BlockN<0, 64>::value;
+}
+
+template <int H16>
+static hipError_t launch_fwd_h(const FwdArgs& a, int64_t grid, hipStream_t st) {
+  switch (a.d) {
+    case 32: return launch_fwd_d<H16, 32>(a, grid, st);
+    case 64: return launch_fwd_d<H16, 64>(a, grid, st);
+    case 96: return launch_fwd_d<H16, 96>(a, grid, st);
+    case 128: return launch_fwd_d<H16, 128>(a, grid, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int64_t grid, hipStream_t st) {
-  if (a.bf16 == 2) return a.d == 64 ? launch_fwd_d<2, 64>(a, grid, st) : launch_fwd_d<2, 128>(a, grid, st);
-  if (a.bf16) return a.d == 64 ? launch_fwd_d<1, 64>(a, grid, st) : launch_fwd_d<1, 128>(a, grid, st);
-  return a.d == 64 ? launch_fwd_d<0, 64>(a, grid, st) : launch_fwd_d<0, 128>(a, grid, st);
+  if (a.bf16 == 2) return launch_fwd_h<2>(a, grid, st);
+  if (a.bf16) return launch_fwd_h<1>(a, grid, st);
+  return launch_fwd_h<0>(a, grid, st);
 }
 
 }  // namespace va
