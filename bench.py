@@ -33,7 +33,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import config, count, padding_mask  # noqa: E402
+from workloads import config, count, make_case, padding_mask  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_F32_TFLOPS = 157.3     # dense fp32 MFMA
@@ -115,9 +115,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="3", help="config id for the step (default 3)")
-    ap.add_argument("--sections", default="qwen,packing,bias,decode",
+    ap.add_argument("--sections", default="qwen,packing,bias,decode,variants",
                     help="comma list of the sections to run besides the main step "
-                         "(qwen, packing, bias, decode; default all)")
+                         "(qwen, packing, bias, decode, variants; default all)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 3 device-to-device copies of MIB MiB (a kernel of known HBM "
                          "traffic, to scale hardware byte counters against)")
@@ -146,7 +146,7 @@ def main() -> int:
 
     secs = {t for t in args.sections.split(",") if t}
     ms_fwd2 = tf2 = w2 = None
-    packing = bias_grad = kvcache_decode = None
+    packing = bias_grad = kvcache_decode = variants = None
 
     w = config(int(args.workload), with_dout=True)
     x = dev_inputs(w)
@@ -373,6 +373,45 @@ def main() -> int:
         }
         del kv
 
+    # the main step's lengths under other input kinds: float16, Q/K/V read in place from
+    # one fused projection output, and head_dim 32 / 96 (same heads and lengths)
+    if "variants" in secs:
+        variants = {"workload": "config-3 lengths (16 seqs logU[128,2048], T=9687), 14/2 heads, causal, "
+                                "fwd+bwd step, fp32 grads", "steps": {}}
+        for vname, vdt, vd, fused in (("f16", "f16", 64, False), ("bf16 fused qkv", "bf16", 64, True),
+                                      ("bf16 d32", "bf16", 32, False), ("bf16 d96", "bf16", 96, False)):
+            wv = make_case(3, w.lens_q, hq=w.hq, hkv=w.hkv, d=vd, causal=True, dtype=vdt, with_dout=True)
+            tdv = torch.float16 if vdt == "f16" else torch.bfloat16
+            tv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(tdv)
+            qv, kv_, vv, dov = tv(wv.q), tv(wv.k), tv(wv.v), tv(wv.dout)
+            if fused:
+                qkv = torch.cat([qv, kv_, vv], dim=1).contiguous()
+                qv, kv_, vv = qkv[:, :wv.hq], qkv[:, wv.hq:wv.hq + wv.hkv], qkv[:, wv.hq + wv.hkv:]
+            cqv = torch.from_numpy(wv.cu_q).to(dev)
+            ov = torch.empty((wv.total_q, wv.hq, vd), dtype=tdv, device=dev)
+            lv = torch.empty((wv.hq, wv.total_q), dtype=torch.float32, device=dev)
+            gq = torch.empty((wv.total_q, wv.hq, vd), dtype=torch.float32, device=dev)
+            gk = torch.empty((wv.total_k, wv.hkv, vd), dtype=torch.float32, device=dev)
+            gv = torch.empty_like(gk)
+            wfv = torch.empty(va.va_varlen_fwd_workspace_size(wv.batch, wv.total_q, wv.total_k, wv.max_q,
+                                                              wv.max_k, wv.hq, wv.hkv, vd, tdv),
+                              dtype=torch.uint8, device=dev)
+            wbv = torch.empty(va.va_varlen_bwd_workspace_size(wv.batch, wv.total_q, wv.total_k, wv.max_q,
+                                                              wv.max_k, wv.hq, wv.hkv, vd, tdv, torch.float32),
+                              dtype=torch.uint8, device=dev)
+
+            def stepv():
+                va.va_varlen_fwd(qv, kv_, vv, cqv, cqv, wv.max_q, wv.max_k, wv.scale, True, out=ov, lse=lv,
+                                 workspace=wfv)
+                va.va_varlen_bwd(dov, qv, kv_, vv, ov, lv, cqv, cqv, wv.max_q, wv.max_k, wv.scale, True,
+                                 dq=gq, dk=gk, dv=gv, workspace=wbv)
+
+            for _ in range(3):
+                stepv()
+            msv = timed(stepv, args.steps)
+            flv = count.fwd_flops(wv) + count.bwd_flops(wv)
+            variants["steps"][vname] = {"ms": round(msv, 5), "tflops": round(flv / (msv * 1e-3) / 1e12, 2)}
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     props = torch.cuda.get_device_properties(dev)
     line = {
@@ -408,6 +447,7 @@ def main() -> int:
         "packing": packing,
         "bias_grad": bias_grad,
         "kvcache_decode": kvcache_decode,
+        "variants": variants,
         "roofline": roof,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
