@@ -492,6 +492,9 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
       return fail(VA_ERR_UNSUPPORTED, "a bias view spanning 2 GiB or more per sequence and head");
     a.bias_vec = a.bs3 == 1 && a.bs0 % 4 == 0 && a.bs1 % 4 == 0 && a.bs2 % 4 == 0 &&
                  ((uintptr_t)bias) % (4 * elt) == 0;
+    const int64_t ve = 16 / elt;  // elements per 16 bytes
+    a.bias_tile = a.bs3 == 1 && a.bs2 > 0 && a.bs0 % ve == 0 && a.bs1 % ve == 0 && a.bs2 % ve == 0 &&
+                  ((uintptr_t)bias) % 16 == 0;
   }
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.q_rs = rs[0]; a.k_rs = rs[1]; a.v_rs = rs[2];

@@ -245,11 +245,14 @@ struct DkdvSmem {
 template <int H16, int D>
 constexpr int dkdv_min_blocks() { return D <= 64 ? 2 : 1; }
 
-template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
+// BIAS: 0 none; 1 any layout (one element per load); 2 contiguous keys in 16-byte
+// aligned rows (the step's tile staged in LDS with Q and dO)
+template <int H16, int D, bool CAUSAL, int BIAS>
 __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(BwdArgs a) {
   using T = elem_t<H16>;
   using SM = DkdvSmem<H16, D>;
   using St = typename SM::St;
+  constexpr bool HAS_BIAS = BIAS != 0;
   constexpr int DT = D / 32;
   constexpr int ELT = (int)sizeof(T);
 
@@ -257,6 +260,15 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
   __shared__ int s_info[2][10];
   // per-key bias gradient sums [head of the group][key of the tile] (bias kernels only)
   __shared__ float db_acc[HAS_BIAS ? kDbiasMaxHeads * BNK : 1];
+  // a bias with contiguous keys and 16-byte aligned rows comes a step ahead, with
+  // Q and dO, as [BMQ rows][BNK keys] tiles (double-buffered), loaded straight
+  // into LDS: each wave load fills 64 x 16 consecutive bytes
+  constexpr bool btile = BIAS == 2;
+  constexpr int BTP = BNK;
+  constexpr int BCH = BNK * ELT / 16;     // 16-byte pieces per tile row
+  constexpr int BTT = BMQ * BCH / NT;     // per thread
+  static_assert(BMQ * BCH % NT == 0, "bias tile loads must tile the workgroup");
+  __shared__ __attribute__((aligned(16))) T bias_t[btile ? 2 * BMQ * BTP : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
   const int hh = lane >> 5, r32 = lane & 31;
@@ -281,7 +293,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     const int item = uniform(inf[0]);
     if (item >= total_items) break;
     const int unit = item / a.hkv;
-    const int g = item - unit * a.hkv;
+    const int g = uniform(item - unit * a.hkv);  // the division runs on the vector ALU
     const int b = uniform(inf[1]), t = uniform(inf[2]);
     const int u0 = uniform(inf[3]), u1 = uniform(inf[4]);
     const int k0 = uniform(inf[5]), k1 = uniform(inf[6]), q0 = uniform(inf[7]), q1 = uniform(inf[8]);
@@ -311,7 +323,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     const int nb = u1 - u0;
     const int nm = min(max(n_diag - u0, 0), nb);  // masked blocks of the unit (its first ones)
     const int k_masked = hpw * nm, k_total = hpw * nb;
-    const int h_first = g * a.n_rep;
+    const int h_first = uniform(g * a.n_rep);
     // block k of the unit is (head r, query block n): the masked blocks first
     // (heads outer), then the unmasked ones; next_of() gives block k from
     // block k - 1 (values only, so the cursor stays in scalar registers)
@@ -328,39 +340,65 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     };
 
     St sq, sd;
-    float pl = 0.f, pd = 0.f;  // staged lse2 / dsum of query tid (tid < BMQ)
-    auto issue = [&](int2 rn) {
-      const int r = rn.x, n = rn.y;
+    float pl = 0.f, pd = 0.f;  // staged LSE / dsum of query pi
+    int pi = 0;
+    // the bias view of head h (element (r, c) at r*bs2 + c*bs3) through a resource
+    // that ends after the last element a valid (row, key) reads, rounded up to a
+    // dword; rows past the sequence read 0 or are zeroed where used
+    auto bias_res = [&](int h) {
+      const int64_t last = ((int64_t)(Lq - 1) * a.bs2 + (int64_t)(Lk - 1) * a.bs3 + 1) * ELT;
+      return make_rsrc((const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1, (last + 3) & ~(int64_t)3);
+    };
+    auto issue = [&](int2 rn, int tbuf) {
+      const int r = uniform(rn.x), n = uniform(rn.y);
       const int h = h_first + r;
       const int qb = qs + n * BMQ;
+      if constexpr (HAS_BIAS) {
+        if constexpr (btile) {
+          const rsrc_t br = bias_res(h);
+#pragma unroll
+          for (int i = 0; i < BTT; ++i) {
+            const int u = tid + i * NT, row = u / BCH, ch = u % BCH;
+            const int64_t o = ((int64_t)(qb + row) * a.bs2 + kt0) * ELT + 16 * ch;
+            T* dst = bias_t + tbuf * BMQ * BTP + (i * NT + 64 * wid) * (16 / ELT);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (__attribute__((address_space(3))) void*)dst, 16,
+                                                     (int)(o < 0x7FFFFFF0 ? o : 0x7FFFFFF0), 0, 0, 0);
+          }
+        }
+      }
       sq.load(make_rsrc((const T*)a.q + (size_t)q0 * qstride + (size_t)h * D,
                         Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0), qrow_bytes, qb);
       sd.load(make_rsrc((const T*)a.dout + (size_t)q0 * dostride + (size_t)h * D,
                         Lq > 0 ? (int64_t)(Lq - 1) * dorow_bytes + D * ELT : 0), dorow_bytes, qb);
-      if (tid < BMQ) {
-        const int i = qb + tid;
-        pl = INFINITY;  // rows past the sequence: P = exp2(x - inf) = 0
-        pd = 0.f;
-        if (i < Lq) {
-          const float l = a.lse[(size_t)h * a.total_q + q0 + i];
-          pl = l == -INFINITY ? INFINITY : l * kLog2e;  // a row that sees nothing adds nothing
-          pd = a.dsum[(size_t)h * a.total_q + q0 + i];
-        }
+      // the raw LSE and dsum of query qb + tid % BMQ (rows past the sequence read 0);
+      // commit() converts them, so nothing here waits for the loads above
+      {
+        const size_t rb = (size_t)h * a.total_q + q0;
+        pi = qb + (tid & (BMQ - 1));
+        pl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.lse + rb, (int64_t)Lq * 4), pi * 4, 0, 0));
+        pd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.dsum + rb, (int64_t)Lq * 4), pi * 4, 0, 0));
       }
     };
     auto commit = [&](int buf) {
+      // the bias tile's direct loads were issued before Q and dO: wait for all of them
+      // so the barrier after this publishes the tile
+      if constexpr (btile) __builtin_amdgcn_s_waitcnt(kWaitVm0);
       sq.store(sm.qn[buf], sm.qt[buf]);
       sd.store(sm.dn[buf], sm.dt[buf]);
-      if (tid < BMQ) { sm.lse2[buf][tid] = pl; sm.dsum[buf][tid] = pd; }
+      if (tid < BMQ) {
+        // rows past the sequence get P = exp2(x - inf) = 0, and so does a row that sees nothing
+        sm.lse2[buf][tid] = pi < Lq && pl != -INFINITY ? pl * kLog2e : INFINITY;
+        sm.dsum[buf][tid] = pi < Lq ? pd : 0.f;
+      }
     };
 
     auto step = [&](auto mask_tag, int k, int2 rn, int2 rn_next) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int buf = k & 1;
-      const int r = rn.x, n = rn.y;
+      const int r = uniform(rn.x), n = uniform(rn.y);
       const int h = h_first + r;
       const int qb = qs + n * BMQ;
-      if (k + 1 < k_total) issue(rn_next);
+      if (k + 1 < k_total) issue(rn_next, buf ^ 1);
       // this wave's keys are seen by queries i >= wk0 - off
       const bool active = wave_keys && (!CAUSAL || qb + BMQ - 1 + off >= wk0);
       if (active) {
@@ -373,10 +411,12 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
         rsrc_t bres = make_rsrc(a.bias, 0);
         int brow = 0;
         if constexpr (HAS_BIAS) {
-          const int64_t last = ((int64_t)(Lq - 1) * a.bs2 + (int64_t)(Lk - 1) * a.bs3 + 1) * ELT;
-          bres = make_rsrc((const T*)a.bias + (int64_t)b * a.bs0 + (int64_t)h * a.bs1, (last + 3) & ~(int64_t)3);
-          brow = (int)(((int64_t)kj * a.bs3 + (int64_t)(qb + 4 * hh) * a.bs2) * ELT);
+          if constexpr (!btile) {
+            bres = bias_res(h);
+            brow = (int)(((int64_t)kj * a.bs3 + (int64_t)(qb + 4 * hh) * a.bs2) * ELT);
+          }
         }
+        const T* bt_lane = bias_t + (btile ? (buf * BMQ + 4 * hh) * BTP + 32 * wid + r32 : 0);  // staged tile
         // causal: key kj is visible to query qb + ql iff ql >= kj - off - qb
         const int thr = kj - off - qb - 4 * hh;
         float p[16], ds[16];
@@ -386,10 +426,15 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
           const int ql = cl + 4 * hh;
           float x = s[i] * a.scale_log2;
           if constexpr (HAS_BIAS) {
-            const int off = brow + cl * (int)a.bs2 * ELT;
             float bf;
-            if constexpr (H16) bf = lo16<H16>(__builtin_amdgcn_raw_buffer_load_b16(bres, off, 0, 0));
-            else bf = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bres, off, 0, 0));
+            if constexpr (btile) {
+              if constexpr (H16) bf = lo16<H16>((uint32_t)bt_lane[cl * BTP]);
+              else bf = bt_lane[cl * BTP];
+            } else {
+              const int off = brow + cl * (int)a.bs2 * ELT;
+              if constexpr (H16) bf = lo16<H16>(__builtin_amdgcn_raw_buffer_load_b16(bres, off, 0, 0));
+              else bf = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bres, off, 0, 0));
+            }
             x = __builtin_fmaf(qb + ql < Lq ? bf : 0.f, kLog2e, x);
           }
           float pv = fast_exp2(x - sm.lse2[buf][ql]);
@@ -457,7 +502,10 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
         for (int r = 0; r < (a.ds1 == 0 ? 1 : hpw); ++r) db_acc[r * BNK + 32 * wid + r32] = 0.f;
     }
     int2 rn = make_int2(0, u0);
-    if (k_total > 0) { issue(rn); commit(0); }
+    if (k_total > 0) { issue(rn, 0); commit(0); }
+    // every load so far (K and V fragments included) has landed: the steps below then
+    // wait only for their own prefetches
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     ItemInfo nxt;
     if (tid == 0) nxt = item_load(a.plan_k, (int)gridDim.x + ticket, a.hkv, total_items);
@@ -798,6 +846,9 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
       sk.store(sm.kn[0], sm.kt[0]);
       sv.store(sm.vn[0], nullptr);
     }
+    // every load so far (Q and dO fragments included) has landed: the steps below then
+    // wait only for their own prefetches
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     ItemInfo nxt;
     if (tid == 0) nxt = item_load(a.plan_q, (int)gridDim.x + ticket, a.hq, total_items);
@@ -901,7 +952,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    auto kern = dkdv_kernel<H16, D, CAUSAL, HAS_BIAS>;
+    auto kern = !HAS_BIAS ? dkdv_kernel<H16, D, CAUSAL, 0>
+                          : (a.bias_tile ? dkdv_kernel<H16, D, CAUSAL, 2> : dkdv_kernel<H16, D, CAUSAL, 1>);
     const int grid = resident_grid((const void*)kern, NT, k_items);
     if (grid <= 0) return hipErrorInvalidConfiguration;
     timing_before(st, H16 == 2 ? "bwd_dkdv_f16" : H16 ? "bwd_dkdv_bf16" : "bwd_dkdv_f32");

@@ -109,6 +109,11 @@ __device__ __forceinline__ uint32_t pack16_rt(float lo, float hi, int h16) {
 // setting for raw (unstructured) buffers on CDNA.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// s_waitcnt operand (gfx9 encoding) that waits for every vector memory load,
+// LDS-direct buffer loads included, and leaves the other counters alone:
+// vmcnt = 0 (bits 3:0 and 15:14), expcnt = 7 (bits 6:4), lgkmcnt = 15 (bits 11:8)
+constexpr int kWaitVm0 = 0x0F70;
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
