@@ -751,6 +751,18 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const int kb = n * BN;
       const int buf = (n - n0) & 1;
+      // a 16-bit bias with contiguous keys: this step's values are loaded before the
+      // next step's K/V prefetch, so waiting for them does not wait for the prefetch
+      // (vector loads retire in order); register e holds keys kb + 32(e/4) + 8(e%4)
+      // + 4hh .. +3.  (float32 keeps its loads in the step: its registers are full.)
+      constexpr bool EARLY = BIAS == 2 && H16 != 0;
+      u32x2_t braw[EARLY ? 4 * NS : 1];
+      if constexpr (EARLY) {
+        if (wave_on && kb < wave_hi) {
+#pragma unroll
+          for (int e = 0; e < 4 * NS; ++e) braw[e] = buf_load8(bres, boff + (kb + 32 * (e >> 2) + 8 * (e & 3)) * ELT);
+        }
+      }
       if (n + 1 < n1) {
         sk.load(kres, krow_bytes, kb + BN);
         sv.load(vres, vrow_bytes, kb + BN);
@@ -772,7 +784,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
               if constexpr (H16) {
                 u32x2_t x;
                 if constexpr (BIAS == 2) {
-                  x = buf_load8(bres, boff + key * ELT);
+                  x = braw[4 * st + j];
                 } else {
                   uint32_t e[4];
 #pragma unroll
