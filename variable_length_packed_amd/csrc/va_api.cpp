@@ -385,6 +385,9 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
     // vector bias loads: contiguous keys, every 4-key group aligned to its own size
     a.bias_vec = a.bs3 == 1 && a.bs0 % 4 == 0 && a.bs1 % 4 == 0 && a.bs2 % 4 == 0 &&
                  ((uintptr_t)bias) % (4 * elt) == 0;
+    // 16-bit, whole 16-byte pieces of a row: the forward stages the bias through LDS
+    a.bias_tile = elt == 2 && a.bs3 == 1 && a.bs0 % 8 == 0 && a.bs1 % 8 == 0 && a.bs2 % 8 == 0 &&
+                  ((uintptr_t)bias) % 16 == 0;
   }
   a.out = out; a.lse = lse;
   a.q_rs = rs[0]; a.k_rs = rs[1]; a.v_rs = rs[2];

@@ -111,7 +111,10 @@ constexpr int block_m() { return 4 * 32 * WaveTiles<H16, D>::value; }
 template <int H16, int D>
 constexpr int min_blocks() { return D <= 64 ? 2 : 1; }
 
-template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
+// BIAS: 0 none; 1 loaded per step (vector loads for contiguous keys, else one
+// element per load); 2 (16-bit only) contiguous keys in 16-byte aligned rows, the
+// tile of a block staged in LDS a block ahead
+template <int H16, int D, bool CAUSAL, int BIAS>
 __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs a) {
   using T = typename std::conditional<(H16 != 0), uint16_t, float>::type;
   using S = FwdSmem<H16, D>;
@@ -125,6 +128,17 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
 
   __shared__ S sm;
   __shared__ int s_info[2][10];
+  // 16-bit bias with contiguous keys: the [BM rows][BN keys] tile of a block, loaded
+  // a block ahead straight into LDS (double-buffered).  Row r keeps its 16-byte
+  // piece c (keys 8c .. 8c+7) in slot c ^ (r % 8), so the 32 rows a wave reads at
+  // once spread over the banks.
+  constexpr bool HAS_BIAS = BIAS != 0;
+  constexpr bool BTILE = BIAS == 2;
+  static_assert(!BTILE || H16 != 0, "the staged bias tile is 16-bit");
+  constexpr int BPR = BN * 2 / 16;  // 16-byte pieces per tile row
+  static_assert(!BTILE || BPR == 8, "the slot swizzle assumes 8 pieces per row");
+  static_assert(!BTILE || BM * BPR % NT == 0, "bias tile loads must tile the workgroup");
+  __shared__ __attribute__((aligned(16))) uint16_t fbias[BTILE ? 2 * BM * BN : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,6 +253,23 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) boff[qt] = (int)(((int64_t)rq[qt] * a.bs2 + 4 * hh * a.bs3) * ELT);
     }
+    constexpr bool btile = BTILE;
+    // loads block kb's bias tile into buffer tb: wave load i fills 64 consecutive
+    // slots (8 rows); slot s of tile row r takes piece s ^ (r % 8)
+    auto bias_dma = [&](int kb, int tb) __attribute__((always_inline)) {
+      if constexpr (BTILE) {
+#pragma unroll
+        for (int i = 0; i < BM * BPR / NT; ++i) {
+          const int u = (i * (NT / 64) + wid) * 64 + lane;  // slot index in the tile
+          const int row = u / BPR, piece = (u % BPR) ^ (row & 7);
+          const int64_t o = ((int64_t)(r1 - BM + row) * a.bs2 + kb + 8 * piece) * 2;
+          uint16_t* dst = fbias + tb * BM * BN + (i * (NT / 64) + wid) * 64 * 8;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (__attribute__((address_space(3))) void*)dst, 16,
+                                                   (int)(o < 0 ? 0x7FFFFFF0 : (o < 0x7FFFFFF0 ? o : 0x7FFFFFF0)),
+                                                   0, 0, 0);
+        }
+      }
+    };
 
     Loader<H16, D> ld;
 
@@ -333,7 +364,21 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
         const unsigned span = (unsigned)max(hi_row[qt] + 1, 0);  // kj <= hi_row (none if < 0)
         float bv[HAS_BIAS ? NS : 1][16];
         if constexpr (HAS_BIAS) {
-          if (a.bias_vec) {
+          if constexpr (BTILE) {
+            // this lane's row of the staged tile: piece 4st + j, its half hh
+            const int row = WR * wid + 32 * qt + r32;
+            const uint16_t* rp = fbias + ((kb - kb0) / BN & 1) * BM * BN + row * BN + 4 * hh;
+#pragma unroll
+            for (int st = 0; st < NS; ++st)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const u32x2_t x = *(const u32x2_t*)(rp + 8 * ((4 * st + j) ^ (row & 7)));
+                bv[st][4 * j + 0] = lo16<H16>(x[0]);
+                bv[st][4 * j + 1] = hi16<H16>(x[0]);
+                bv[st][4 * j + 2] = lo16<H16>(x[1]);
+                bv[st][4 * j + 3] = hi16<H16>(x[1]);
+              }
+          } else if (a.bias_vec) {
             // registers 4j .. 4j+3 of a score tile are 4 consecutive keys: one 8-byte
             // (bf16) or 16-byte (f32) load each; keys past the sequence are masked
             // below, rows outside it are never stored
@@ -565,6 +610,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     auto active = [&](int j) { return j < nb && wave_on && kb0 + j * BN < wave_hi; };
     {
       Loader<H16, D> ld1;  // K(1) in flight with K(0) and V(0)
+      if (btile) bias_dma(kb0, 0);
       ld.load_k(kres, krow_bytes, kb0);
       ld.load_v(vres, vrow_bytes, kb0);
       ld1.load_k(kres, krow_bytes, kb0 + BN);
@@ -572,6 +618,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       ld.store_v(sm, 0);
       ld1.store_k(sm, 1);
     }
+    if (btile) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the bias tile, loaded straight into LDS
     __syncthreads();
     f32x16_t s_cur[QT][NS];
     if (active(0)) qk(0, s_cur);
@@ -582,6 +629,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     auto step = [&](auto mask_tag, int n) {  // n: block index inside the unit
       constexpr bool MASK = decltype(mask_tag)::value;
       const int kb = kb0 + n * BN;
+      if (btile && n + 1 < nb) bias_dma(kb + BN, (n + 1) & 1);  // before the K/V prefetch
       ld.load_k(kres, krow_bytes, kb + 2 * BN);  // past the last block every row reads as zero
       ld.load_v(vres, vrow_bytes, kb + BN);
       f32x16_t s_nxt[QT][NS];
@@ -627,6 +675,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       }
       ld.store_k(sm, n & 1);
       ld.store_v(sm, (n + 1) & 1);
+      if (btile) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // block n + 1's bias tile has landed
       __syncthreads();
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
@@ -762,7 +811,9 @@ __global__ __launch_bounds__(NT) void fwd_merge_kernel(FwdArgs a) {
 
 template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
 static hipError_t launch_fwd_t(const FwdArgs& a, int64_t items, hipStream_t st) {
-  auto kern = fwd_kernel<H16, D, CAUSAL, HAS_BIAS>;
+  auto kern = !HAS_BIAS ? fwd_kernel<H16, D, CAUSAL, 0>
+                        : (H16 && a.bias_tile ? fwd_kernel<H16, D, CAUSAL, (H16 ? 2 : 1)>
+                                              : fwd_kernel<H16, D, CAUSAL, 1>);
   const int grid = resident_grid((const void*)kern, NT, items);
   if (grid <= 0) return hipErrorInvalidConfiguration;
   timing_before(st, H16 == 2 ? "fwd_f16" : H16 ? "fwd_bf16" : "fwd_f32");

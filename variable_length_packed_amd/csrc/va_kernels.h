@@ -65,6 +65,7 @@ struct FwdArgs {
   int32_t causal;
   int32_t bf16;      // element kind: 0 float32, 1 bfloat16, 2 float16
   int32_t bias_vec;  // keys contiguous (bs3 = 1), 4-key groups aligned: vector bias loads
+  int32_t bias_tile;  // 16-bit bias, contiguous keys, 16-byte aligned rows: tiles staged in LDS
 };
 
 struct BwdArgs {
