@@ -308,6 +308,7 @@ def test_kvcache_validation(lib, kw, code):
 def test_kvcache_workspace_size(lib):
     f = lib.va_kvcache_fwd_workspace_size
     assert f(0, 1, 128, 8, 2, 128, BF16) == 0
+    assert f(2, 1, 128, 8, 2, 32, BF16) > 0 and f(2, 1, 128, 8, 2, 96, BF16) == 0  # head dims 32/64/128
     assert f(2, 1, 128, 8, 2, 128, F32) == 0         # not a decode dtype
     assert f(2, 1, 128, 8, 3, 128, BF16) == 0
 

@@ -1,7 +1,7 @@
 """GPU parity of decode steps against a paged KV cache (include/va_kvcache.h) with the oracle.
 
 Single-token steps and multi-token steps (beams, drafts), causal and not,
-GQA, MQA and MHA, head_dim 64 and 128, bf16 and float16, pages of 1 to 256
+GQA, MQA and MHA, head_dim 32, 64 and 128, bf16 and float16, pages of 1 to 256
 keys handed out in random order, empty caches, sequences with no new token,
 caches shorter than the new tokens (rows that see no key), caches long enough
 to split into tens of chunks, and the full decode workload the bench times
@@ -40,6 +40,13 @@ CASES = [
                              page_size=16)),
     ("long-split-d64-causal-draft", dict(seed=7, lens_q=[6, 1, 3], lens_k=[5000, 2, 9001], hq=12, hkv=3, d=64,
                                          dtype="f16", page_size=128)),
+    # head_dim 32: 64-key steps, so pages of 64 take one lookup per step and pages of 8 one per load
+    ("decode-gqa4-d32-p64", dict(seed=13, lens_q=[1] * 5, lens_k=[1, 63, 64, 3000, 0], hq=16, hkv=4, d=32,
+                                 dtype="bf16", page_size=64)),
+    ("draft3-mqa-d32-f16-p8-split", dict(seed=14, lens_q=[3, 1, 2], lens_k=[9000, 5, 700], hq=8, hkv=1, d=32,
+                                         dtype="f16", page_size=8)),
+    ("beam6-noncausal-d32-p16", dict(seed=15, lens_q=[6, 6], lens_k=[129, 2000], hq=4, hkv=2, d=32,
+                                     dtype="bf16", page_size=16, causal=False)),
 ]
 
 

@@ -35,6 +35,8 @@ CASES = [
                                causal=False, dtype="f16")),
     ("mha-tokens-0-and-1", dict(seed=104, lens_q=[1, 0, 1, 1], lens_k=[33, 50, 0, 2], hq=4, hkv=4, d=64,
                                 causal=True, dtype="bf16")),
+    ("draft5-gqa4-d32", dict(seed=108, lens_q=[5, 1, 2], lens_k=[3000, 64, 9], hq=8, hkv=2, d=32,
+                             causal=True, dtype="bf16")),
 ]
 
 

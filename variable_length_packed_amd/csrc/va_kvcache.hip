@@ -41,7 +41,9 @@ constexpr int KNT = 256;  // 4 independent waves per workgroup
 
 template <int D>
 struct KvShape {
-  static constexpr int KB = 4096 / D;  // keys per step: 8 KB of K and 8 KB of V per wave
+  // keys per step: 8 KB of K and 8 KB of V per wave (4 KB each at d = 32, where
+  // 128-key steps would leave no room for two workgroups per CU)
+  static constexpr int KB = D >= 64 ? 4096 / D : 64;
   static constexpr int NS = KB / 32;   // 32-key score tiles per step
   static constexpr int VP = D + 8;     // LDS row pitch of the staged V block (elements)
   static constexpr int KS = D / 16;    // MFMA k-steps over head_dim
@@ -448,11 +450,20 @@ hipError_t launch_kv_d(const KvArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int kv_block_n(int d) { return d == 64 ? KvShape<64>::KB : KvShape<128>::KB; }
+int kv_block_n(int d) { return d == 32 ? KvShape<32>::KB : d == 64 ? KvShape<64>::KB : KvShape<128>::KB; }
+
+template <int H16>
+hipError_t launch_kv_h(const KvArgs& a, hipStream_t st) {
+  switch (a.d) {
+    case 32: return launch_kv_d<H16, 32>(a, st);
+    case 64: return launch_kv_d<H16, 64>(a, st);
+    case 128: return launch_kv_d<H16, 128>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_kvcache(const KvArgs& a, hipStream_t st) {
-  if (a.h16 == 2) return a.d == 64 ? launch_kv_d<2, 64>(a, st) : launch_kv_d<2, 128>(a, st);
-  return a.d == 64 ? launch_kv_d<1, 64>(a, st) : launch_kv_d<1, 128>(a, st);
+  return a.h16 == 2 ? launch_kv_h<2>(a, st) : launch_kv_h<1>(a, st);
 }
 
 }  // namespace va
