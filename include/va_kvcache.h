@@ -73,7 +73,7 @@ size_t va_kvcache_fwd_workspace_size(int32_t batch, int32_t max_seqlen_q, int32_
  *   block_table_stride int32 entries per block-table row; must cover
  *                     max_seqlen_k: stride * page_size >= max_seqlen_k
  *   page_size         a power of two, 1 .. 2^20;  num_pages > 0
- *   dtype             VA_BF16 or VA_F16 (VA_F32: VA_ERR_UNSUPPORTED); head_dim 32, 64 or 128
+ *   dtype             VA_BF16 or VA_F16 (VA_F32: VA_ERR_UNSUPPORTED); head_dim 32, 64, 96 or 128
  *   workspace         device memory, 256-byte aligned, of at least the size above
  * Returns VA_ERR_INVALID for a NULL required pointer, a misaligned buffer,
  * a non-positive size, Hq % Hkv != 0, a bad page_size / num_pages / stride,

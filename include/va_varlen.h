@@ -129,8 +129,7 @@ typedef void* va_stream;
  * too small a workspace; VA_ERR_HIP if a launch fails.  A bias with
  * contiguous keys (bias_stride[3] = 1), strides that are multiples of 4 and a
  * base aligned to 4 elements is read 4 keys per load.
- * Short queries: with bf16 or float16 inputs, head_dim 32, 64 or 128, no bias,
- * and max_seqlen_q <= 16
+ * Short queries: with bf16 or float16 inputs, no bias, and max_seqlen_q <= 16
  * (or <= 32 with max_seqlen_q * num_heads_q / num_heads_kv <= 128) -- decode
  * steps, beams and drafts over contiguous K/V -- the call runs the decode
  * kernels of include/va_kvcache.h (K/V read through cu_seqlens_k) instead of

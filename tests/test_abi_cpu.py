@@ -297,7 +297,7 @@ def _kv(lib, **kw):
     (dict(ws=P + 64), INVALID),        # misaligned workspace
     (dict(wsb=16), WORKSPACE),
     (dict(dt=F32), UNSUPPORTED),
-    (dict(d=96), UNSUPPORTED),
+    (dict(d=80), UNSUPPORTED),
     (dict(mq=1 << 20, hq=64, hkv=8), UNSUPPORTED),  # a sequence's queries span 2^31 bytes
 ])
 def test_kvcache_validation(lib, kw, code):
@@ -308,7 +308,9 @@ def test_kvcache_validation(lib, kw, code):
 def test_kvcache_workspace_size(lib):
     f = lib.va_kvcache_fwd_workspace_size
     assert f(0, 1, 128, 8, 2, 128, BF16) == 0
-    assert f(2, 1, 128, 8, 2, 32, BF16) > 0 and f(2, 1, 128, 8, 2, 96, BF16) == 0  # head dims 32/64/128
+    for d in (32, 64, 96, 128):
+        assert f(2, 1, 128, 8, 2, d, BF16) > 0
+    assert f(2, 1, 128, 8, 2, 80, BF16) == 0 and f(2, 1, 128, 8, 2, 256, BF16) == 0
     assert f(2, 1, 128, 8, 2, 128, F32) == 0         # not a decode dtype
     assert f(2, 1, 128, 8, 3, 128, BF16) == 0
 

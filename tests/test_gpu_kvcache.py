@@ -1,7 +1,7 @@
 """GPU parity of decode steps against a paged KV cache (include/va_kvcache.h) with the oracle.
 
 Single-token steps and multi-token steps (beams, drafts), causal and not,
-GQA, MQA and MHA, head_dim 32, 64 and 128, bf16 and float16, pages of 1 to 256
+GQA, MQA and MHA, head_dim 32, 64, 96 and 128, bf16 and float16, pages of 1 to 256
 keys handed out in random order, empty caches, sequences with no new token,
 caches shorter than the new tokens (rows that see no key), caches long enough
 to split into tens of chunks, and the full decode workload the bench times
@@ -47,6 +47,14 @@ CASES = [
                                          dtype="f16", page_size=8)),
     ("beam6-noncausal-d32-p16", dict(seed=15, lens_q=[6, 6], lens_k=[129, 2000], hq=4, hkv=2, d=32,
                                      dtype="bf16", page_size=16, causal=False)),
+    # head_dim 96: 12 pieces per cache row, so some wave loads straddle two rows (and,
+    # with pages of 4 keys, two pages); 32-key steps
+    ("decode-gqa4-d96-p4", dict(seed=16, lens_q=[1] * 4, lens_k=[31, 32, 33, 2500], hq=16, hkv=4, d=96,
+                                dtype="bf16", page_size=4)),
+    ("draft2-mqa-d96-f16-p32-split", dict(seed=17, lens_q=[2, 2, 1], lens_k=[7000, 1, 300], hq=8, hkv=1, d=96,
+                                          dtype="f16", page_size=32)),
+    ("beam5-noncausal-d96-p128", dict(seed=18, lens_q=[5, 3], lens_k=[777, 40], hq=6, hkv=3, d=96,
+                                      dtype="bf16", page_size=128, causal=False)),
 ]
 
 

@@ -37,6 +37,8 @@ CASES = [
                                 causal=True, dtype="bf16")),
     ("draft5-gqa4-d32", dict(seed=108, lens_q=[5, 1, 2], lens_k=[3000, 64, 9], hq=8, hkv=2, d=32,
                              causal=True, dtype="bf16")),
+    ("decode-gqa2-d96-f16", dict(seed=109, lens_q=[1, 3, 1], lens_k=[4500, 35, 1], hq=8, hkv=4, d=96,
+                                 causal=True, dtype="f16")),
 ]
 
 

@@ -33,7 +33,7 @@ va_status fail(va_status s, const char* fmt, ...) {
 // Head dims of the packed forward and backward (multiples of the 32-wide
 // MFMA output tile); the decode kernels take 64 and 128.
 bool varlen_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
-bool decode_head_dim(int d) { return d == 32 || d == 64 || d == 128; }
+bool decode_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
 
 struct Common {
   int batch, total_q, total_k, hq, hkv, d, max_q, max_k;

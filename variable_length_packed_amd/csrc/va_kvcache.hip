@@ -41,9 +41,11 @@ constexpr int KNT = 256;  // 4 independent waves per workgroup
 
 template <int D>
 struct KvShape {
-  // keys per step: 8 KB of K and 8 KB of V per wave (4 KB each at d = 32, where
-  // 128-key steps would leave no room for two workgroups per CU)
-  static constexpr int KB = D >= 64 ? 4096 / D : 64;
+  // keys per step: 8 KB of K and 8 KB of V per wave at d = 64 and 128 (4 KB each
+  // at d = 32, where 128-key steps would leave no room for two workgroups per
+  // CU; 6 KB at d = 96, whose steps must stay whole 32-key tiles)
+  static constexpr int KB = D == 32 ? 64 : D == 96 ? 32 : 4096 / D;
+  static_assert(KB % 32 == 0 && KB * D / 8 % 64 == 0, "steps of whole tiles and whole wave loads");
   static constexpr int NS = KB / 32;   // 32-key score tiles per step
   static constexpr int VP = D + 8;     // LDS row pitch of the staged V block (elements)
   static constexpr int KS = D / 16;    // MFMA k-steps over head_dim
@@ -142,21 +144,23 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
   for (int ks = 0; ks < KS; ++ks)
     qf[ks] = buf_load16(qres, (int)((qpos * qrow + h * D + 16 * ks + 8 * hh) * ELT));
 
-  // ---- cache rows.  Loads are coalesced: in each 16-byte load instruction LPR
-  // consecutive lanes read one key's row of this KV head (D * 2 bytes), so the
-  // wave reads RPI whole rows per instruction and NI instructions per step for
-  // each of K and V.  Both go through the wave's LDS slices: K is read back in
-  // the MFMA operand layout, V through the transposing read.
-  constexpr int LPR = D / 8;     // lanes per row
-  constexpr int RPI = 64 / LPR;  // rows per load instruction
-  constexpr int NI = KB / RPI;   // load instructions per step and tensor
-  const int lrow = lane / LPR, lcol = (lane % LPR) * 8;
+  // ---- cache rows.  Loads are coalesced: a step's K (and V) block is KB rows of
+  // LPR 16-byte pieces (this KV head's D * 2 bytes of a key), and load
+  // instruction i reads pieces 64i .. 64i+63 in order, so consecutive lanes read
+  // consecutive pieces of one row and the wave reads 64 / LPR rows per
+  // instruction (a row may straddle two when LPR does not divide 64, d = 96).
+  // Both go through the wave's LDS slices: K is read back in the MFMA operand
+  // layout, V through the transposing read.
+  constexpr int LPR = D / 8;          // 16-byte pieces per row
+  constexpr int NI = KB * LPR / 64;   // load instructions per step and tensor
+  auto prow = [&](int i) { return (64 * i + lane) / LPR; };       // row of load i's piece
+  auto pcol = [&](int i) { return (64 * i + lane) % LPR * 8; };   // its first element
   const uint16_t* __restrict__ kc = (const uint16_t*)a.k_cache;
   const uint16_t* __restrict__ vc = (const uint16_t*)a.v_cache;
   const int32_t* __restrict__ bt = RAGGED ? nullptr : a.block_table + (size_t)b * a.bt_stride;
   const int pmask = (1 << a.page_shift) - 1;
   // key of load i of step n (clamped to the chunk's last key)
-  auto key_of = [&](int n, int i) { return min(kbeg + n * KB + RPI * i + lrow, kend - 1); };
+  auto key_of = [&](int n, int i) { return min(kbeg + n * KB + prow(i), kend - 1); };
   // pages of the next step to load, fetched a step ahead: with pages of at
   // least KB keys a step lies in one page (steps start at multiples of KB),
   // so one uniform lookup per step; otherwise one per load and lane
@@ -183,8 +187,8 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
         const int page = min(max(pg[BIGPAGE ? 0 : i], 0), a.num_pages - 1);
         row = ((int64_t)page << a.page_shift) + (key_of(n, i) & pmask);
       }
-      kr[i] = __builtin_nontemporal_load((const u32x4_t*)(kc + row * a.k_rs + g * D + lcol));
-      vr[i] = __builtin_nontemporal_load((const u32x4_t*)(vc + row * a.v_rs + g * D + lcol));
+      kr[i] = __builtin_nontemporal_load((const u32x4_t*)(kc + row * a.k_rs + g * D + pcol(i)));
+      vr[i] = __builtin_nontemporal_load((const u32x4_t*)(vc + row * a.v_rs + g * D + pcol(i)));
     }
   };
 
@@ -208,8 +212,8 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
     // them are done: one wave's LDS operations complete in order)
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      *(u32x4_t*)(sk + (RPI * i + lrow) * VP + lcol) = kr[i];
-      *(u32x4_t*)(sv + (RPI * i + lrow) * VP + lcol) = vr[i];
+      *(u32x4_t*)(sk + prow(i) * VP + pcol(i)) = kr[i];
+      *(u32x4_t*)(sv + prow(i) * VP + pcol(i)) = vr[i];
     }
     // the next step's K and V are in flight during all of this step's work
     // (their pages were fetched a step ago); then the pages of the step after
@@ -450,13 +454,16 @@ hipError_t launch_kv_d(const KvArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int kv_block_n(int d) { return d == 32 ? KvShape<32>::KB : d == 64 ? KvShape<64>::KB : KvShape<128>::KB; }
+int kv_block_n(int d) {
+  return d == 32 ? KvShape<32>::KB : d == 64 ? KvShape<64>::KB : d == 96 ? KvShape<96>::KB : KvShape<128>::KB;
+}
 
 template <int H16>
 hipError_t launch_kv_h(const KvArgs& a, hipStream_t st) {
   switch (a.d) {
     case 32: return launch_kv_d<H16, 32>(a, st);
     case 64: return launch_kv_d<H16, 64>(a, st);
+    case 96: return launch_kv_d<H16, 96>(a, st);
     case 128: return launch_kv_d<H16, 128>(a, st);
     default: return hipErrorInvalidValue;
   }
