@@ -374,12 +374,13 @@ def main() -> int:
         del kv
 
     # the main step's lengths under other input kinds: float16, Q/K/V read in place from
-    # one fused projection output, and head_dim 32 / 96 (same heads and lengths)
+    # one fused projection output, and head_dim 32 / 96 / 256 (same heads and lengths)
     if "variants" in secs:
         variants = {"workload": "config-3 lengths (16 seqs logU[128,2048], T=9687), 14/2 heads, causal, "
                                 "fwd+bwd step, fp32 grads", "steps": {}}
         for vname, vdt, vd, fused in (("f16", "f16", 64, False), ("bf16 fused qkv", "bf16", 64, True),
-                                      ("bf16 d32", "bf16", 32, False), ("bf16 d96", "bf16", 96, False)):
+                                      ("bf16 d32", "bf16", 32, False), ("bf16 d96", "bf16", 96, False),
+                                      ("bf16 d256", "bf16", 256, False)):
             wv = make_case(3, w.lens_q, hq=w.hq, hkv=w.hkv, d=vd, causal=True, dtype=vdt, with_dout=True)
             tdv = torch.float16 if vdt == "f16" else torch.bfloat16
             tv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(tdv)

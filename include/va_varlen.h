@@ -117,7 +117,7 @@ typedef void* va_stream;
  *   qkv_row_stride     NULL or HOST int64[3] token strides of q, k, v (above)
  *   workspace          device scratch of at least va_varlen_fwd_workspace_size()
  *                      bytes, 256-byte aligned
- *   head_dim           32, 64, 96 or 128 (multiples of the 32-wide MFMA output tile)
+ *   head_dim           32, 64, 96, 128 or 256 (multiples of the 32-wide MFMA output tile)
  * Returns VA_ERR_INVALID for a NULL required pointer, exactly one of
  * bias/bias_stride NULL, batch/total/heads/head_dim <= 0, Hq % Hkv != 0,
  * max_seqlen <= 0, a negative stride, a scale that is not finite and > 0, a
@@ -184,7 +184,8 @@ size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
  *                      elements of pairs in key blocks the causal mask skips
  *                      entirely are NOT written (zero the buffer first); per key
  *                      (t2 = 0): summed over rows, every (b, h, c < Lk) written,
- *                      with t1 > 0 and at most 32 query heads per KV head, or
+ *                      with t1 > 0 and at most 32 query heads per KV head (8 at
+ *                      head_dim 256), or
  *                      t1 = 0 (summed over heads too) with one KV head.  Other
  *                      layouts return VA_ERR_UNSUPPORTED.  Typically dbias_stride
  *                      equals bias_stride of a float32 buffer shaped like the bias.

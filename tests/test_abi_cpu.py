@@ -92,7 +92,7 @@ def _fwd(lib, **kw):
     (dict(ws=None), INVALID),
     (dict(ws=0x100040), INVALID),      # misaligned workspace
     (dict(d=80), UNSUPPORTED),
-    (dict(d=256), UNSUPPORTED),
+    (dict(d=512), UNSUPPORTED),
     (dict(d=16), UNSUPPORTED),
     (dict(dt=7), UNSUPPORTED),
     (dict(dt=3), UNSUPPORTED),
@@ -147,6 +147,7 @@ def _bwd(lib, **kw):
     (dict(bias=P, bstr=(64, 16, 4, 1), db=P, dbstr=(64, 0, 4, 1)), UNSUPPORTED),   # per pair, summed over heads
     (dict(bias=P, bstr=(16, 4, 0, 1), db=P, dbstr=(16, 0, 0, 1)), UNSUPPORTED),    # per key over heads, 2 KV heads
     (dict(bias=P, bstr=(16, 4, 0, 1), db=P, dbstr=(16, 4, 0, 1), hq=66, hkv=2), UNSUPPORTED),  # 33 heads per KV head
+    (dict(bias=P, bstr=(16, 4, 0, 1), db=P, dbstr=(16, 4, 0, 1), hq=18, hkv=2, d=256), UNSUPPORTED),  # 9 at d = 256
 ])
 def test_bwd_validation(lib, kw, code):
     assert _bwd(lib, **kw) == code

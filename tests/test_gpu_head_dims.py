@@ -1,7 +1,9 @@
-"""GPU parity with the oracle at head_dim 32 and 96 (the packed forward and backward).
+"""GPU parity with the oracle at head_dim 32, 96 and 256 (the packed forward and backward).
 
-The same kernels as at 64 and 128, instantiated for one and three 32-wide
-output tiles: float32, bf16 and float16; causal and not; GQA, MQA and MHA;
+The same kernels as at 64 and 128, instantiated for one, three and eight
+32-wide output tiles (at 256 with 32-key blocks in the forward and dQ pass,
+and with the dK/dV pass's registers spilled): float32, bf16 and float16;
+causal and not; GQA, MQA and MHA;
 cross-length; sequences long enough to split in every pass; per-key and
 per-pair biases with their gradients; 16-bit gradients; a fused QKV input.
 Tolerances as for the other shapes (``tests/_gpu.py``).
@@ -33,6 +35,12 @@ CASES = [
     ("d96-f32-causal-gqa", dict(seed=115, lens_q=[200, 37], hq=4, hkv=2, d=96, causal=True, dtype="f32")),
     ("d32-f16-short-rows", dict(seed=116, lens_q=[1, 4, 2], lens_k=[700, 40, 2000], hq=16, hkv=4, d=32,
                                 causal=True, dtype="f16")),
+    ("d256-bf16-gqa4-causal-split", dict(seed=120, lens_q=[300, 1100, 17], hq=8, hkv=2, d=256, causal=True,
+                                         dtype="bf16")),
+    ("d256-f32-noncausal-mqa", dict(seed=121, lens_q=[100, 37, 1], hq=2, hkv=1, d=256, causal=False,
+                                    dtype="f32")),
+    ("d256-f16-cross-mha", dict(seed=122, lens_q=[112, 5, 0], lens_k=[262, 40, 9], hq=4, hkv=4, d=256,
+                                causal=True, dtype="f16")),
 ]
 
 
@@ -55,6 +63,10 @@ BIAS = [
                              bias="per_key")),
     ("d96-bf16-per-pair-permuted", dict(seed=118, lens_q=[64, 200, 17], hq=4, hkv=2, d=96, causal=False,
                                         dtype="bf16", bias="per_pair", bias_layout="permuted")),
+    ("d256-bf16-per-key", dict(seed=123, lens_q=[37, 300], hq=8, hkv=2, d=256, causal=True, dtype="bf16",
+                               bias="per_key")),
+    ("d256-f16-per-pair", dict(seed=124, lens_q=[64, 150], hq=2, hkv=2, d=256, causal=False, dtype="f16",
+                               bias="per_pair")),
 ]
 
 

@@ -32,7 +32,7 @@ va_status fail(va_status s, const char* fmt, ...) {
 
 // Head dims of the packed forward and backward (multiples of the 32-wide
 // MFMA output tile); the decode kernels take 64 and 128.
-bool varlen_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+bool varlen_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128 || d == 256; }
 bool decode_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
 
 struct Common {
@@ -467,10 +467,11 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
         return fail(VA_ERR_UNSUPPORTED, "a per-pair bias gradient summed over heads is not supported");
       dbias_mode = 1;
     } else {  // per key: summed over rows (and over heads when t1 = 0)
-      if (t[1] == 0 ? num_heads_kv != 1 : n_rep_ > 32)
+      const int max_heads = head_dim <= 128 ? 32 : 8;  // the dK/dV pass's LDS accumulators
+      if (t[1] == 0 ? num_heads_kv != 1 : n_rep_ > max_heads)
         return fail(VA_ERR_UNSUPPORTED,
-                    "a per-key bias gradient needs a head stride with at most 32 query heads per "
-                    "KV head, or one KV head when summed over heads");
+                    "a per-key bias gradient needs a head stride with at most %d query heads per "
+                    "KV head (head_dim %d), or one KV head when summed over heads", max_heads, head_dim);
       dbias_mode = 2;
     }
   }

@@ -43,7 +43,10 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int BNK = 128;     // keys per dK/dV workgroup
-constexpr int kDbiasMaxHeads = 32;  // query heads per KV head with a per-key bias gradient
+// query heads per KV head with a per-key bias gradient (an LDS accumulator per
+// head; fewer at head_dim 256, whose Q/dO staging fills most of the LDS)
+template <int D>
+constexpr int dbias_max_heads() { return D <= 128 ? 32 : 8; }
 constexpr int BMQ_DQ = 128;  // query rows per dQ workgroup
 
 template <int H16>
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
   __shared__ SM sm;
   __shared__ int s_info[2][10];
   // per-key bias gradient sums [head of the group][key of the tile] (bias kernels only)
-  __shared__ float db_acc[HAS_BIAS ? kDbiasMaxHeads * BNK : 1];
+  __shared__ float db_acc[HAS_BIAS ? dbias_max_heads<D>() * BNK : 1];
   // a bias with contiguous keys and 16-byte aligned rows comes a step ahead, with
   // Q and dO, as [BMQ rows][BNK keys] tiles (double-buffered), loaded straight
   // into LDS: each wave load fills 64 x 16 consecutive bytes
@@ -964,8 +967,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    auto kern = !HAS_BIAS ? dkdv_kernel<H16, D, CAUSAL, 0>
-                          : (a.bias_tile ? dkdv_kernel<H16, D, CAUSAL, 2> : dkdv_kernel<H16, D, CAUSAL, 1>);
+    auto kern = dkdv_kernel<H16, D, CAUSAL, 0>;
+    if constexpr (HAS_BIAS) {
+      kern = dkdv_kernel<H16, D, CAUSAL, 1>;
+      if constexpr (D <= 128)  // at 256 the staged Q/dO leave no room for a bias tile
+        if (a.bias_tile) kern = dkdv_kernel<H16, D, CAUSAL, 2>;
+    }
     const int grid = resident_grid((const void*)kern, NT, k_items);
     if (grid <= 0) return hipErrorInvalidConfiguration;
     timing_before(st, H16 == 2 ? "bwd_dkdv_f16" : H16 ? "bwd_dkdv_bf16" : "bwd_dkdv_f32");
@@ -1033,6 +1040,7 @@ static hipError_t launch_bwd_h(const BwdArgs& a, const PlanSet& ps, int64_t q_it
     case 64: return launch_bwd_d<H16, 64>(a, ps, q_items, k_items, st);
     case 96: return launch_bwd_d<H16, 96>(a, ps, q_items, k_items, st);
     case 128: return launch_bwd_d<H16, 128>(a, ps, q_items, k_items, st);
+    case 256: return launch_bwd_d<H16, 256>(a, ps, q_items, k_items, st);
   }
   return hipErrorInvalidValue;
 }

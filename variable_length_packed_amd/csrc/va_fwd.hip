@@ -30,7 +30,7 @@ constexpr int NT = 256;  // threads per workgroup
 // keys per block: 64 for bf16 (two 32-key score tiles), 32 for f32 (LDS size)
 template <int H16, int D>
 struct BlockN {
-  static constexpr int value = H16 ? 64 : 32;
+  static constexpr int value = H16 && D <= 128 ? 64 : 32;
 };
 
 template <int H16, int D>
@@ -811,9 +811,13 @@ __global__ __launch_bounds__(NT) void fwd_merge_kernel(FwdArgs a) {
 
 template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
 static hipError_t launch_fwd_t(const FwdArgs& a, int64_t items, hipStream_t st) {
-  auto kern = !HAS_BIAS ? fwd_kernel<H16, D, CAUSAL, 0>
-                        : (H16 && a.bias_tile ? fwd_kernel<H16, D, CAUSAL, (H16 ? 2 : 1)>
-                                              : fwd_kernel<H16, D, CAUSAL, 1>);
+  auto kern = fwd_kernel<H16, D, CAUSAL, 0>;
+  if constexpr (HAS_BIAS) {
+    kern = fwd_kernel<H16, D, CAUSAL, 1>;
+    // the staged tile: 16-bit, 64-key blocks
+    if constexpr (H16 != 0 && BlockN<H16, D>::value == 64)
+      if (a.bias_tile) kern = fwd_kernel<H16, D, CAUSAL, 2>;
+  }
   const int grid = resident_grid((const void*)kern, NT, items);
   if (grid <= 0) return hipErrorInvalidConfiguration;
   timing_before(st, H16 == 2 ? "fwd_f16" : H16 ? "fwd_bf16" : "fwd_f32");
@@ -841,7 +845,8 @@ static hipError_t launch_fwd_d(const FwdArgs& a, int64_t grid, hipStream_t st) {
 
 int fwd_block_m() { return block_m<true, 64>(); }
 int fwd_block_n(bool bf16, int d) {
-  (void)d;  // keys per block depend only on the element size
+  // keys per block: by element size, and 32 at head_dim 256 (LDS)
+  if (d > 128) return bf16 ? BlockN<1, 256>::value : BlockN<0, 256>::value;
   return bf16 ? BlockN<1, 64>::value : BlockN<0, 64>::value;
 }
 
@@ -852,6 +857,7 @@ static hipError_t launch_fwd_h(const FwdArgs& a, int64_t grid, hipStream_t st) {
     case 64: return launch_fwd_d<H16, 64>(a, grid, st);
     case 96: return launch_fwd_d<H16, 96>(a, grid, st);
     case 128: return launch_fwd_d<H16, 128>(a, grid, st);
+    case 256: return launch_fwd_d<H16, 256>(a, grid, st);
   }
   return hipErrorInvalidValue;
 }
