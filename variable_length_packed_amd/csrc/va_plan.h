@@ -182,7 +182,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
   };
 
   // (1) partial slots each chunk candidate needs (a split tile of nch chunks
-  // takes nch slots); only lanes with a split tile join the reductions
+  // takes nch slots)
   if (tid < NCAND) sh.cnt[tid] = 0;
   __syncthreads();
   const int chunk0 = max(p.chunk, 1);
@@ -199,13 +199,16 @@ __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
         if (nch > 1) sl[j] += nch;
       }
     });
+    // a wave with a split tile (candidate 0 splits whatever a larger one does)
+    // sums each candidate with a butterfly of shuffles over all its lanes and
+    // adds it with one LDS atomic; the others skip the reduction
+    if (__builtin_amdgcn_ballot_w64(sl[0] > 0) != 0) {
 #pragma unroll
-    for (int j = 0; j < NCAND; ++j)
-      if (sl[j] > 0) {
-        const int v = (int)__builtin_amdgcn_wave_reduce_add_u32((unsigned)sl[j], 0);
-        const uint64_t m = __builtin_amdgcn_read_exec();
-        if ((int)(threadIdx.x & 63) == (int)__builtin_ctzll(m)) atomicAdd(&sh.cnt[j], v);
+      for (int j = 0; j < NCAND; ++j) {
+        const int v = wave_sum(sl[j]);
+        if ((threadIdx.x & 63) == 0 && v > 0) atomicAdd(&sh.cnt[j], v);
       }
+    }
   }
   __syncthreads();
   // the smallest chunk whose partial results fit the workspace (each split
