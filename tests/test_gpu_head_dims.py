@@ -2,7 +2,8 @@
 
 The same kernels as at 64 and 128, instantiated for one, three and eight
 32-wide output tiles (at 256 with 32-key blocks in the forward and dQ pass,
-and with the dK/dV pass's registers spilled): float32, bf16 and float16;
+and two dK/dV work items per unit, each with half of the dims): float32, bf16
+and float16;
 causal and not; GQA, MQA and MHA;
 cross-length; sequences long enough to split in every pass; per-key and
 per-pair biases with their gradients; 16-bit gradients; a fused QKV input.

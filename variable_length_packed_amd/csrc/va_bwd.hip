@@ -257,6 +257,10 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
   using St = typename SM::St;
   constexpr bool HAS_BIAS = BIAS != 0;
   constexpr int DT = D / 32;
+  // head_dim 256: each unit runs as two items, each accumulating dK and dV for
+  // half of the dims (S and dP computed in both), so the accumulators fit
+  constexpr int HS = D > 128 ? 2 : 1;  // items per unit and KV head
+  constexpr int DTO = DT / HS;         // 32-wide output tiles per item
   constexpr int ELT = (int)sizeof(T);
 
   __shared__ SM sm;
@@ -276,7 +280,8 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
   const int hh = lane >> 5, r32 = lane & 31;
 
-  const int total_items = uniform(a.plan_k.hdr[1]) * a.hkv;
+  const int per_unit = a.hkv * HS;
+  const int total_items = uniform(a.plan_k.hdr[1]) * per_unit;
   // token strides (elements): Q, K, V as the caller lays them out; dO, dK, dV dense
   const size_t qstride = (size_t)a.q_rs, dostride = (size_t)a.hq * D;
   const size_t kstride = (size_t)a.k_rs, vstride = (size_t)a.v_rs, gstride = (size_t)a.hkv * D;
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
   int ticket = 0;  // thread 0: ticket of the item after the current one
   if (tid == 0) {
     const int first = (int)blockIdx.x;
-    item_store(s_info[0], item_load(a.plan_k, first, a.hkv, total_items));
+    item_store(s_info[0], item_load(a.plan_k, first, per_unit, total_items));
     if (first < total_items) ticket = queue_take(a.plan_k.hdr);
   }
   __syncthreads();
@@ -295,8 +300,10 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     const int* inf = s_info[cur];
     const int item = uniform(inf[0]);
     if (item >= total_items) break;
-    const int unit = item / a.hkv;
-    const int g = uniform(item - unit * a.hkv);  // the division runs on the vector ALU
+    const int unit = item / per_unit;
+    const int rem = uniform(item - unit * per_unit);  // the division runs on the vector ALU
+    const int g = rem / HS;
+    const int hb = rem - g * HS;  // which half of the dims (head_dim 256)
     const int b = uniform(inf[1]), t = uniform(inf[2]);
     const int u0 = uniform(inf[3]), u1 = uniform(inf[4]);
     const int k0 = uniform(inf[5]), k1 = uniform(inf[6]), q0 = uniform(inf[7]), q1 = uniform(inf[8]);
@@ -313,9 +320,9 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     vf.load(make_rsrc((const T*)a.v + (size_t)k0 * vstride + (size_t)g * D,
                       Lk > 0 ? (int64_t)(Lk - 1) * vrow_bytes + D * ELT : 0), vrow_bytes, kj, hh);
     const size_t koff = (size_t)k0 * gstride + (size_t)g * D;  // this tile's dK / dV rows
-    f32x16_t dk[DT], dv[DT];
+    f32x16_t dk[DTO], dv[DTO];
 #pragma unroll
-    for (int i = 0; i < DT; ++i) { dk[i] = (f32x16_t){}; dv[i] = (f32x16_t){}; }
+    for (int i = 0; i < DTO; ++i) { dk[i] = (f32x16_t){}; dv[i] = (f32x16_t){}; }
 
     // query blocks that can see a key of the tile: i + off >= kt0 (causal);
     // this unit runs blocks [u0, u1) of them, for every head of the group
@@ -448,7 +455,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
         if constexpr (HAS_BIAS) {
           // bias gradient = dS (the bias enters the logits additively)
           if (a.dbias_mode == 1) {
-            if (kj < Lk) {
+            if (kj < Lk && hb == 0) {  // both halves hold the same dS
               float* db = a.dbias + (int64_t)b * a.ds0 + (int64_t)h * a.ds1 + (int64_t)kj * a.ds3;
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
@@ -472,8 +479,8 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
             pack8<H16>(&p[8 * c], pa, nullptr);
             pack8<H16>(&ds[8 * c], da, &da_lo);
 #pragma unroll
-            for (int dt_ = 0; dt_ < DT; ++dt_) {
-              const int d = 32 * dt_ + r32;
+            for (int dt_ = 0; dt_ < DTO; ++dt_) {
+              const int d = 32 * (dt_ + hb * DTO) + r32;
               const u32x4_t ob = tfrag<BMQ, St::TP>(sm.dt[buf], d, c, hh);
               const u32x4_t qb4 = tfrag<BMQ, St::TP>(sm.qt[buf], d, c, hh);
               dv[dt_] = mfma16<H16>(pa, ob, dv[dt_]);
@@ -486,9 +493,9 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
           for (int i = 0; i < 16; ++i) {
             const int ql = 8 * (i >> 2) + 4 * hh + (i & 3);
 #pragma unroll
-            for (int dt_ = 0; dt_ < DT; ++dt_) {
-              const float ob = sm.dn[buf][ql * St::NP + 32 * dt_ + r32];
-              const float qv = sm.qn[buf][ql * St::NP + 32 * dt_ + r32];
+            for (int dt_ = 0; dt_ < DTO; ++dt_) {
+              const float ob = sm.dn[buf][ql * St::NP + 32 * (dt_ + hb * DTO) + r32];
+              const float qv = sm.qn[buf][ql * St::NP + 32 * (dt_ + hb * DTO) + r32];
               dv[dt_] = mfma32_f32(p[i], ob, dv[dt_]);
               dk[dt_] = mfma32_f32(ds[i], qv, dk[dt_]);
             }
@@ -511,7 +518,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     ItemInfo nxt;
-    if (tid == 0) nxt = item_load(a.plan_k, (int)gridDim.x + ticket, a.hkv, total_items);
+    if (tid == 0) nxt = item_load(a.plan_k, (int)gridDim.x + ticket, per_unit, total_items);
     int k = 0;
     for (; k < k_masked; ++k) {
       const int2 nx = next_of(k + 1, rn);
@@ -529,7 +536,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     }
 
     if constexpr (HAS_BIAS) {
-      if (a.dbias_mode == 2 && hh == 0) {
+      if (a.dbias_mode == 2 && hh == 0 && hb == 0) {
         const int nacc = a.ds1 == 0 ? 1 : hpw;
         if (slot < 0) {
           if (kj < Lk)
@@ -557,10 +564,10 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
       const rsrc_t rv = make_rsrc((const uint8_t*)a.dv + base, nbytes);
       const int lane_off = 4 * hh * krow + r32 * gelt;
 #pragma unroll
-      for (int dt_ = 0; dt_ < DT; ++dt_)
+      for (int dt_ = 0; dt_ < DTO; ++dt_)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int off = lane_off + (8 * (i >> 2) + (i & 3)) * krow + 32 * dt_ * gelt;
+          const int off = lane_off + (8 * (i >> 2) + (i & 3)) * krow + 32 * (dt_ + hb * DTO) * gelt;
           const float kv = dk[dt_][i] * a.scale, vv = dv[dt_][i];
           if (a.grad_bf16) {
             buf_store2((uint16_t)(pack16<H16>(kv, 0.f) & 0xFFFF), rk, off);
@@ -574,10 +581,10 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
       float* pk = a.part_kv + ((size_t)slot * a.hkv + g) * 2 * BNK * D + (size_t)wid * 32 * D;
       float* pv = pk + BNK * D;
 #pragma unroll
-      for (int dt_ = 0; dt_ < DT; ++dt_)
+      for (int dt_ = 0; dt_ < DTO; ++dt_)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const int o = ((dt_ * 4 + i4) * 64 + lane) * 4;
+          const int o = (((dt_ + hb * DTO) * 4 + i4) * 64 + lane) * 4;
           *(f32x4_t*)(pk + o) = (f32x4_t){dk[dt_][4 * i4], dk[dt_][4 * i4 + 1], dk[dt_][4 * i4 + 2], dk[dt_][4 * i4 + 3]};
           *(f32x4_t*)(pv + o) = (f32x4_t){dv[dt_][4 * i4], dv[dt_][4 * i4 + 1], dv[dt_][4 * i4 + 2], dv[dt_][4 * i4 + 3]};
         }
@@ -973,7 +980,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
       if constexpr (D <= 128)  // at 256 the staged Q/dO leave no room for a bias tile
         if (a.bias_tile) kern = dkdv_kernel<H16, D, CAUSAL, 2>;
     }
-    const int grid = resident_grid((const void*)kern, NT, k_items);
+    const int grid = resident_grid((const void*)kern, NT, k_items * (D > 128 ? 2 : 1));  // two items per unit at 256
     if (grid <= 0) return hipErrorInvalidConfiguration;
     timing_before(st, H16 == 2 ? "bwd_dkdv_f16" : H16 ? "bwd_dkdv_bf16" : "bwd_dkdv_f32");
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
