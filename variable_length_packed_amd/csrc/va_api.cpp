@@ -497,7 +497,7 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
     a.bias_vec = a.bs3 == 1 && a.bs0 % 4 == 0 && a.bs1 % 4 == 0 && a.bs2 % 4 == 0 &&
                  ((uintptr_t)bias) % (4 * elt) == 0;
     const int64_t ve = 16 / elt;  // elements per 16 bytes
-    a.bias_tile = a.bs3 == 1 && a.bs2 > 0 && a.bs0 % ve == 0 && a.bs1 % ve == 0 && a.bs2 % ve == 0 &&
+    a.bias_tile = a.bs3 == 1 && a.bs0 % ve == 0 && a.bs1 % ve == 0 && a.bs2 % ve == 0 &&
                   ((uintptr_t)bias) % 16 == 0;
   }
   a.dq = dq; a.dk = dk; a.dv = dv;

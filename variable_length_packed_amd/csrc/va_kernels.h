@@ -103,7 +103,7 @@ struct BwdArgs {
   int32_t bf16;       // element kind: 0 float32, 1 bfloat16, 2 float16
   int32_t grad_bf16;  // gradients in float32 (0) or in the input's 16-bit kind (its code)
   int32_t bias_vec;  // keys contiguous (bs3 = 1), 4-key groups aligned: vector bias loads
-  int32_t bias_tile;  // a per-pair bias with contiguous keys and 16-byte aligned rows:
+  int32_t bias_tile;  // a bias with contiguous keys and 16-byte aligned rows (per pair or per key):
                       // staged through LDS a tile at a time by the dK/dV pass
 };
 
