@@ -123,12 +123,14 @@ typedef void* va_stream;
  * max_seqlen <= 0, a negative stride, a scale that is not finite and > 0, a
  * misaligned workspace, a row stride below num_heads * head_dim or rows or
  * bases of q/k/v not 16-byte aligned; VA_ERR_UNSUPPORTED for head_dim not in
- * {32, 64, 96, 128}, an unknown dtype, a bias view spanning 2 GiB or more inside one
+ * {32, 64, 96, 128, 256}, an unknown dtype, a bias view spanning 2 GiB or more inside one
  * (sequence, head), or max_seqlen * row stride reaching 2 GiB (the kernels
  * address one sequence's rows with 32-bit byte offsets); VA_ERR_WORKSPACE for
  * too small a workspace; VA_ERR_HIP if a launch fails.  A bias with
  * contiguous keys (bias_stride[3] = 1), strides that are multiples of 4 and a
- * base aligned to 4 elements is read 4 keys per load.
+ * base aligned to 4 elements is read 4 keys per load; a 16-bit one whose
+ * strides are multiples of 8 and whose base is 16-byte aligned is staged
+ * through LDS a block of keys at a time (results identical either way).
  * Short queries: with bf16 or float16 inputs, no bias, and max_seqlen_q <= 16
  * (or <= 32 with max_seqlen_q * num_heads_q / num_heads_kv <= 128) -- decode
  * steps, beams and drafts over contiguous K/V -- the call runs the decode
