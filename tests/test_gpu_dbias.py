@@ -6,7 +6,8 @@ head_dim 64 and 128, and sequences long enough that key tiles are split over
 several work units (their per-key sums then go through the merge).  The
 buffer is zeroed first (per-pair elements of key blocks the causal mask skips
 are not written; the oracle's gradient there is 0).  Tolerances as for the
-other gradients (``tests/_gpu.py``).
+other gradients (``tests/_gpu.py``).  The LDS-staged and the loaded bias paths
+are also checked against each other, bitwise.
 """
 
 import numpy as np
@@ -86,3 +87,33 @@ def test_autograd_bias_grad():
     _gpu.check("dbias (autograd)", _gpu.host(bias.grad).reshape(-1), ref, "f32", grad=True)
     dq_ref = oracle.backward(w.dout, w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, True, w.bias, w.bias_strides)[0]
     _gpu.check("dq (autograd)", _gpu.host(q.grad), dq_ref, "f32", grad=True)
+
+
+@pytest.mark.parametrize("kind,dtype", [("per_pair", "bf16"), ("per_key", "f16"), ("per_pair", "f32")])
+def test_staged_and_loaded_bias_paths_agree_bitwise(kind, dtype):
+    """A contiguous-key bias whose base is 16-byte aligned goes through the LDS-staged tiles
+    (16-bit forward and dK/dV) or vector loads; the same values one element off that
+    alignment are read element by element.  Both must give identical results."""
+    print(f"[case] bias paths {kind} {dtype}", flush=True)
+    w = make_case(80, [64, 300, 17, 129], hq=4, hkv=2, d=64, causal=kind == "per_key", dtype=dtype,
+                  bias=kind, with_dout=True, bias_std=0.5)
+    inp = _gpu.device_inputs(w)
+    dt = inp["q"].dtype
+    buf = torch.zeros(len(w.bias) + 1, dtype=dt, device=_gpu.DEV)
+    buf[1:] = inp["bias"]
+    shifted = buf[1:]  # same values; base 1 element past 16-byte alignment
+    assert inp["bias"].data_ptr() % 16 == 0 and shifted.data_ptr() % 16 != 0
+    res = []
+    for bias in (inp["bias"], shifted):
+        out, lse = va.va_varlen_fwd(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_k"], w.max_q, w.max_k,
+                                    w.scale, w.causal, bias, w.bias_strides)
+        db = torch.zeros(len(w.bias), dtype=torch.float32, device=_gpu.DEV)
+        grads = va.va_varlen_bwd(inp["dout"], inp["q"], inp["k"], inp["v"], out, lse, inp["cu_q"], inp["cu_k"],
+                                 w.max_q, w.max_k, w.scale, w.causal, bias, w.bias_strides, dbias=db,
+                                 dbias_stride=w.bias_strides)
+        torch.cuda.synchronize()
+        res.append([out, lse, *grads, db])
+    for name, a, b in zip(("out", "lse", "dq", "dk", "dv", "dbias"), *res):
+        assert torch.equal(a, b), name
+    o_ref, _ = oracle.forward(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal, w.bias, w.bias_strides)
+    _gpu.check("out", _gpu.host(res[0][0]), o_ref, w.dtype)
