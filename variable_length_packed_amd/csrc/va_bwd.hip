@@ -598,12 +598,11 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
 // tile, KV head); a thread owns 16-byte pieces of the partials' register
 // layout [dt][i/4][lane][4], i.e. 4 consecutive keys of one dim.
 template <int D>
-__global__ __launch_bounds__(NT) void dkdv_merge_kernel(BwdArgs a) {
+__device__ __forceinline__ void dkdv_merge_item(const BwdArgs& a, int it) {
   constexpr int DT = D / 32;
   constexpr int PIECES = DT * 4 * 64;       // 16-byte pieces per wave block
   constexpr int PPT = PIECES / NT;          // per thread
-  const int total = uniform(a.plan_k.hdr[2]) * a.hkv * 4;
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+  {
     const int w = it & 3, sg = it >> 2;
     const int si = sg / a.hkv, g = sg - si * a.hkv;
     const int4 sp = a.plan_k.splits[si];
@@ -921,14 +920,15 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
 // item is 32 rows of one (split tile, head); eight threads per row.
 constexpr int kMergeRows = 32;
 
+constexpr int kMergeSlabs = BMQ_DQ / kMergeRows;
+
 template <int D>
-__global__ __launch_bounds__(NT) void dq_merge_kernel(BwdArgs a) {
-  constexpr int SLABS = BMQ_DQ / kMergeRows;
+__device__ __forceinline__ void dq_merge_item(const BwdArgs& a, int it) {
+  constexpr int SLABS = kMergeSlabs;
   constexpr int TPR = NT / kMergeRows;
   constexpr int SEG = D / TPR;
-  const int total = uniform(a.plan_q.hdr[2]) * a.hq * SLABS;
   const int rs = threadIdx.x / TPR, seg = threadIdx.x % TPR;
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+  {
     const int slab = it % SLABS, sh = it / SLABS;
     const int si = sh / a.hq, h = sh - si * a.hq;
     const int4 sp = a.plan_q.splits[si];
@@ -937,7 +937,7 @@ __global__ __launch_bounds__(NT) void dq_merge_kernel(BwdArgs a) {
     seq_bounds(a.cu_q, b, a.total_q, q0, q1);
     const int row = slab * kMergeRows + rs;
     const int rq = (q1 - q0) - (t + 1) * BMQ_DQ + row;
-    if (rq < 0) continue;
+    if (rq < 0) return;
     f32x4_t acc[SEG / 4];
 #pragma unroll
     for (int e = 0; e < SEG / 4; ++e) acc[e] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -958,6 +958,19 @@ __global__ __launch_bounds__(NT) void dq_merge_kernel(BwdArgs a) {
       else
         ((f32x4_t*)((float*)a.dq + o))[e] = x;
     }
+  }
+}
+
+// Both merges in one launch after the dQ pass: first the dK/dV items (one
+// wave's 32 keys of a (split key tile, KV head)), then the dQ items (32 rows
+// of a (split query tile, head)); each sums its chunks in chunk order.
+template <int D>
+__global__ __launch_bounds__(NT) void bwd_merge_kernel(BwdArgs a) {
+  const int nkv = uniform(a.plan_k.hdr[2]) * a.hkv * 4;
+  const int total = nkv + uniform(a.plan_q.hdr[2]) * a.hq * kMergeSlabs;
+  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+    if (it < nkv) dkdv_merge_item<D>(a, it);
+    else dq_merge_item<D>(a, it - nkv);
   }
 }
 
@@ -987,15 +1000,6 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
     timing_after(st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.split_cap_k > 0) {
-      int64_t g = (int64_t)a.split_cap_k * a.hkv * 4;
-      if (g > 4096) g = 4096;
-      timing_before(st, "bwd_dkdv_merge");
-      hipLaunchKernelGGL(dkdv_merge_kernel<D>, dim3((unsigned)g), dim3(NT), 0, st, a);
-      timing_after(st);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
   }
   {
     auto kern = !HAS_BIAS ? dq_kernel<H16, D, CAUSAL, 0>
@@ -1007,13 +1011,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
     timing_after(st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.split_cap_q > 0) {
-      int64_t g = (int64_t)a.split_cap_q * a.hq * (BMQ_DQ / kMergeRows);
-      if (g > 4096) g = 4096;
-      timing_before(st, "bwd_dq_merge");
-      hipLaunchKernelGGL(dq_merge_kernel<D>, dim3((unsigned)g), dim3(NT), 0, st, a);
-      timing_after(st);
-    }
+  }
+  if (a.split_cap_k > 0 || a.split_cap_q > 0) {  // the split tiles' partial sums
+    int64_t g = (int64_t)a.split_cap_k * a.hkv * 4 + (int64_t)a.split_cap_q * a.hq * kMergeSlabs;
+    if (g > 4096) g = 4096;
+    timing_before(st, "bwd_merge");
+    hipLaunchKernelGGL(bwd_merge_kernel<D>, dim3((unsigned)g), dim3(NT), 0, st, a);
+    timing_after(st);
   }
   return hipGetLastError();
 }
