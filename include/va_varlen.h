@@ -114,6 +114,7 @@ typedef void* va_stream;
  *                      must be finite and > 0
  *   causal             0 or 1; 1 = bottom-right aligned causal mask
  *   bias, bias_stride  both NULL (no bias) or both non-NULL
+ *   out, lse           device outputs, layouts above
  *   qkv_row_stride     NULL or HOST int64[3] token strides of q, k, v (above)
  *   workspace          device scratch of at least va_varlen_fwd_workspace_size()
  *                      bytes, 256-byte aligned
@@ -143,8 +144,8 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
                         int32_t max_seqlen_q, int32_t max_seqlen_k,
                         float softmax_scale, int causal,
                         const void* bias, const int64_t* bias_stride,
-                        const int64_t* qkv_row_stride,
                         void* out, float* lse,
+                        const int64_t* qkv_row_stride,
                         void* workspace, size_t workspace_bytes,
                         int32_t batch, int32_t total_q, int32_t total_k,
                         int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
@@ -169,7 +170,8 @@ size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
  * the softmax from `lse` (the forward's own output) instead of storing it,
  * and optionally the bias gradient.
  *   dout, out          device, `dtype`, [total_q, num_heads_q, head_dim], contiguous
- *   q, k, v            as for the forward, with the same qkv_row_stride
+ *   q, k, v            as for the forward, with the same qkv_row_stride (passed
+ *                      after the gradient outputs)
  *   lse                device float32 [num_heads_q, total_q] from va_varlen_fwd
  *   dq                 [total_q, num_heads_q, head_dim] in grad_dtype
  *   dk, dv             [total_k, num_heads_kv, head_dim] in grad_dtype; the
@@ -182,15 +184,17 @@ size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
  *                      element b*t0 + h*t1 + r*t2 + c*t3 with dbias_stride = {t0,
  *                      t1, t2, t3} (HOST int64[4]); a stride of 0 sums over that
  *                      axis.  Supported: t0 > 0 (or batch 1) and t3 > 0;
- *                      per pair (t2 > 0): t1 > 0 (or one query head) -- the
- *                      elements of pairs in key blocks the causal mask skips
- *                      entirely are NOT written (zero the buffer first); per key
+ *                      per pair (t2 > 0): t1 > 0 (or one query head), every
+ *                      element of a valid pair (r < Lq_b, c < Lk_b) written,
+ *                      0 where the causal mask hides the pair; per key
  *                      (t2 = 0): summed over rows, every (b, h, c < Lk) written,
  *                      with t1 > 0 and at most 32 query heads per KV head (8 at
  *                      head_dim 256), or
  *                      t1 = 0 (summed over heads too) with one KV head.  Other
  *                      layouts return VA_ERR_UNSUPPORTED.  Typically dbias_stride
  *                      equals bias_stride of a float32 buffer shaped like the bias.
+ *                      Elements no valid pair addresses (rows or keys past a
+ *                      sequence's length in a padded grid) are left untouched.
  *   workspace          device scratch of at least va_varlen_bwd_workspace_size()
  *                      bytes, 256-byte aligned
  *   grad_dtype         VA_F32, or the input dtype when that is VA_BF16 or VA_F16
@@ -204,9 +208,9 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
                         int32_t max_seqlen_q, int32_t max_seqlen_k,
                         float softmax_scale, int causal,
                         const void* bias, const int64_t* bias_stride,
-                        const int64_t* qkv_row_stride,
                         void* dq, void* dk, void* dv,
                         float* dbias, const int64_t* dbias_stride,
+                        const int64_t* qkv_row_stride,
                         void* workspace, size_t workspace_bytes,
                         int32_t batch, int32_t total_q, int32_t total_k,
                         int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,

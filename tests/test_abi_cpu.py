@@ -67,7 +67,7 @@ def _fwd(lib, **kw):
     bstr = _lib.strides_arg(a["bstr"]) if a["bstr"] is not None else None
     rs = _lib.strides_arg(a["rs"]) if a["rs"] is not None else None
     return lib.va_varlen_fwd(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["mq"], a["mk"], a["scale"],
-                             a["causal"], a["bias"], bstr, rs, a["out"], a["lse"], a["ws"], a["wsb"],
+                             a["causal"], a["bias"], bstr, a["out"], a["lse"], rs, a["ws"], a["wsb"],
                              a["batch"], a["tq"], a["tk"], a["hq"], a["hkv"], a["d"], a["dt"], None)
 
 
@@ -119,8 +119,8 @@ def _bwd(lib, **kw):
     dbstr = _lib.strides_arg(a["dbstr"]) if a["dbstr"] is not None else None
     rs = _lib.strides_arg(a["rs"]) if a["rs"] is not None else None
     return lib.va_varlen_bwd(a["do"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
-                             a["mq"], a["mk"], a["scale"], a["causal"], a["bias"], bstr, rs, a["dq"],
-                             a["dk"], a["dv"], a["db"], dbstr, a["ws"], a["wsb"], a["batch"], a["tq"],
+                             a["mq"], a["mk"], a["scale"], a["causal"], a["bias"], bstr, a["dq"],
+                             a["dk"], a["dv"], a["db"], dbstr, rs, a["ws"], a["wsb"], a["batch"], a["tq"],
                              a["tk"], a["hq"], a["hkv"], a["d"], a["dt"], a["gdt"], None)
 
 

@@ -4,10 +4,11 @@ Per-pair and per-key biases, contiguous and permuted layouts, a head-shared
 per-key bias with one KV head, causal and not, cross-length, float32 and bf16,
 head_dim 64 and 128, and sequences long enough that key tiles are split over
 several work units (their per-key sums then go through the merge).  The
-buffer is zeroed first (per-pair elements of key blocks the causal mask skips
-are not written; the oracle's gradient there is 0).  Tolerances as for the
-other gradients (``tests/_gpu.py``).  The LDS-staged and the loaded bias paths
-are also checked against each other, bitwise.
+buffer is filled with NaN first: every element a valid (row, key) pair
+addresses must be overwritten -- 0 where the causal mask hides the pair, as
+the oracle's gradient is there -- and every other element left untouched.
+Tolerances as for the other gradients (``tests/_gpu.py``).  The LDS-staged and
+the loaded bias paths are also checked against each other, bitwise.
 """
 
 import numpy as np
@@ -29,6 +30,10 @@ CASES = [
                                          dtype="bf16", bias="per_pair", bias_layout="permuted")),
     ("pair-bf16-cross-d128", dict(seed=73, lens_q=[50, 112], lens_k=[90, 262], hq=8, hkv=2, d=128,
                                   causal=True, dtype="bf16", bias="per_pair")),
+    ("pair-bf16-causal-split", dict(seed=81, lens_q=[700, 33, 450], hq=4, hkv=2, d=64, causal=True,
+                                    dtype="bf16", bias="per_pair")),
+    ("pair-f32-causal-qgtk", dict(seed=82, lens_q=[90, 20, 300], lens_k=[50, 20, 140], hq=2, hkv=1, d=64,
+                                  causal=True, dtype="f32", bias="per_pair")),
     ("key-f32-gqa7", dict(seed=74, lens_q=[37, 300, 129, 64], hq=14, hkv=2, d=64, causal=True,
                           dtype="f32", bias="per_key")),
     ("key-bf16-split-long", dict(seed=75, lens_q=[1500, 33, 700], hq=14, hkv=2, d=64, causal=True,
@@ -40,10 +45,23 @@ CASES = [
 ]
 
 
-def _dbias(w):
+def _addressed(w):
+    """Elements of the bias buffer that some valid (b, h, r < Lq, c < Lk) reads."""
+    m = np.zeros(len(w.bias), dtype=bool)
+    s0, s1, s2, s3 = (int(x) for x in w.bias_strides)
+    for b in range(w.batch):
+        lq, lk = int(w.cu_q[b + 1] - w.cu_q[b]), int(w.cu_k[b + 1] - w.cu_k[b])
+        r = np.arange(lq, dtype=np.int64)[:, None]
+        c = np.arange(lk, dtype=np.int64)[None, :]
+        for h in range(w.hq):
+            m[(b * s0 + h * s1 + r * s2 + c * s3).ravel()] = True
+    return m
+
+
+def _dbias(w, fill=float("nan")):
     inp = _gpu.device_inputs(w)
     out, lse = _gpu.run_fwd(w, inp)
-    db = torch.zeros(len(w.bias), dtype=torch.float32, device=_gpu.DEV)
+    db = torch.full((len(w.bias),), fill, dtype=torch.float32, device=_gpu.DEV)
     va.va_varlen_bwd(inp["dout"], inp["q"], inp["k"], inp["v"], out, lse, inp["cu_q"], inp["cu_k"],
                      max(1, w.max_q), max(1, w.max_k), w.scale, w.causal, inp["bias"], w.bias_strides,
                      dbias=db, dbias_stride=w.bias_strides)
@@ -58,14 +76,17 @@ def test_bias_grad_parity(name, c):
     got = _dbias(w)
     ref = oracle.bias_grad(w.dout, w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal, w.bias,
                            w.bias_strides, len(w.bias))
-    _gpu.check("dbias", got, ref, w.dtype, grad=True, abs_tol=_gpu.grad_abs_tol(w.dtype, ref, False))
+    m = _addressed(w)
+    assert np.all(np.isnan(got[~m])), "an element no valid pair addresses was written"
+    assert np.all(np.isfinite(got[m])), "an element of a valid pair was not written"
+    _gpu.check("dbias", got[m], ref[m], w.dtype, grad=True, abs_tol=_gpu.grad_abs_tol(w.dtype, ref, False))
 
 
 def test_bias_grad_is_deterministic():
     print("[case] dbias determinism", flush=True)
     w = make_case(78, [1500, 33, 700], hq=14, hkv=2, d=64, causal=True, dtype="bf16", bias="per_key",
                   with_dout=True, bias_std=0.5)
-    a, b = _dbias(w), _dbias(w)
+    a, b = _dbias(w, 0.0), _dbias(w, 0.0)
     assert np.array_equal(a, b)
 
 

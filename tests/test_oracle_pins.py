@@ -530,3 +530,87 @@ def test_pins_pass_on_unmodified_oracle():
 @pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_planted_mistakes_are_caught(name, old, new):
     assert not _pins_pass(_mutant(old, new)), name
+
+
+# ---------------------------------------------------------------- per-sequence checkers
+# ``sequence_head_forward`` computes one (sequence, query head) on its own, apart from
+# ``forward()``: it finds the sequence's rows, the KV head of the query head and the
+# bias block itself.  It is pinned to the brute force (scalar loops, exactly rounded
+# sums) for every (b, h) of every tiny case, and must equal forward()'s slice bitwise.
+# ``sequence_group_backward`` is the per-(sequence, KV head) body of ``backward()``,
+# whose results the finite-difference and autograd pins above fix.
+
+
+def _seq_head_pins_pass(mod) -> bool:
+    try:
+        for c in TINY:
+            w = _case(c)
+            bo, bl = oracle.brute_forward(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal,
+                                          w.bias, w.bias_strides)
+            bo, bl = np.array(bo), np.array(bl)
+            for b in range(w.batch):
+                q0, q1 = w.cu_q[b], w.cu_q[b + 1]
+                for h in range(w.hq):
+                    o, l = mod.sequence_head_forward(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal,
+                                                     w.bias, w.bias_strides, b, h)
+                    if o.shape != (q1 - q0, w.d) or l.shape != (q1 - q0,):
+                        return False
+                    if np.max(np.abs(o - bo[q0:q1, h]), initial=0) > 1e-12:
+                        return False
+                    ref = bl[h, q0:q1]
+                    fin = np.isfinite(ref)
+                    if not np.array_equal(fin, np.isfinite(l)) or \
+                            np.max(np.abs(l[fin] - ref[fin]), initial=0) > 1e-12:
+                        return False
+    except Exception:
+        return False
+    return True
+
+
+def test_sequence_head_forward_matches_brute_force_everywhere():
+    assert _seq_head_pins_pass(oatt)
+
+
+def test_sequence_head_forward_equals_forward_slices_bitwise():
+    for c in TINY:
+        w = _case(c)
+        out, lse = _fwd(w)
+        for b in range(w.batch):
+            q0, q1 = w.cu_q[b], w.cu_q[b + 1]
+            for h in range(w.hq):
+                o, l = oracle.sequence_head_forward(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal,
+                                                    w.bias, w.bias_strides, b, h)
+                assert np.array_equal(o, out[q0:q1, h])
+                assert np.array_equal(l, lse[h, q0:q1])
+
+
+def test_sequence_group_backward_equals_backward_slices():
+    for c in GRAD_CASES + [dict(seed=46, lens_q=[3, 0, 5], lens_k=[2, 4, 5], hq=4, hkv=2, d=3, causal=True,
+                                bias="per_pair")]:
+        w = _case(c, with_dout=True)
+        dq, dk, dv = _bwd(w)
+        n_rep = w.hq // w.hkv
+        for b in range(w.batch):
+            q0, q1, k0, k1 = w.cu_q[b], w.cu_q[b + 1], w.cu_k[b], w.cu_k[b + 1]
+            for g in range(w.hkv):
+                a, bk, bv = oracle.sequence_group_backward(w.dout, w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale,
+                                                           w.causal, w.bias, w.bias_strides, b, g)
+                assert np.array_equal(a, dq[q0:q1, g * n_rep:(g + 1) * n_rep])
+                assert np.array_equal(bk, dk[k0:k1, g]) and np.array_equal(bv, dv[k0:k1, g])
+
+
+SEQ_HEAD_MUTATIONS = [
+    ("wrong GQA map", "g = h // n_rep\n    bb", "g = h % k.shape[1]\n    bb"),
+    ("KV head from the group size", "g = h // n_rep\n    bb", "g = min(h, k.shape[1] - 1)\n    bb"),
+    ("key rows from the query bounds", "k[k0:k1, g], v[k0:k1, g], scale, causal, bb)\n\n\ndef forward",
+     "k[q0:q1, g], v[q0:q1, g], scale, causal, bb)\n\n\ndef forward"),
+    ("bias of the KV head", "bb = bias_tile(bias, bias_strides, b, h, q1 - q0, k1 - k0)\n    return",
+     "bb = bias_tile(bias, bias_strides, b, g, q1 - q0, k1 - k0)\n    return"),
+    ("next sequence's bias", "bb = bias_tile(bias, bias_strides, b, h, q1 - q0, k1 - k0)\n    return",
+     "bb = bias_tile(bias, bias_strides, min(b + 1, len(cu_q) - 2), h, q1 - q0, k1 - k0)\n    return"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", SEQ_HEAD_MUTATIONS, ids=[m[0] for m in SEQ_HEAD_MUTATIONS])
+def test_sequence_head_forward_mistakes_are_caught(name, old, new):
+    assert not _seq_head_pins_pass(_mutant(old, new)), name

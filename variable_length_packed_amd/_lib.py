@@ -44,12 +44,17 @@ def load() -> ctypes.CDLL:
                           "`python -m variable_length_packed_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     lib.va_varlen_fwd.restype = ctypes.c_int
-    lib.va_varlen_fwd.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p, _i64p, _i64p,
-                                  _p, _p, _p, ctypes.c_size_t, _i32, _i32, _i32, _i32, _i32, _i32,
+    # q, k, v, cu_q, cu_k, max_q, max_k, scale, causal, bias, bias_stride, out, lse,
+    # qkv_row_stride, workspace, workspace_bytes, batch, total_q, total_k, hq, hkv, d, dtype, stream
+    lib.va_varlen_fwd.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p, _i64p, _p, _p,
+                                  _i64p, _p, ctypes.c_size_t, _i32, _i32, _i32, _i32, _i32, _i32,
                                   ctypes.c_int, _p]
     lib.va_varlen_bwd.restype = ctypes.c_int
+    # dout, q, k, v, out, lse, cu_q, cu_k, max_q, max_k, scale, causal, bias, bias_stride,
+    # dq, dk, dv, dbias, dbias_stride, qkv_row_stride, workspace, workspace_bytes, batch, total_q,
+    # total_k, hq, hkv, d, dtype, grad_dtype, stream
     lib.va_varlen_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p,
-                                  _i64p, _i64p, _p, _p, _p, _p, _i64p, _p, ctypes.c_size_t, _i32, _i32,
+                                  _i64p, _p, _p, _p, _p, _i64p, _i64p, _p, ctypes.c_size_t, _i32, _i32,
                                   _i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int, _p]
     lib.va_varlen_fwd_workspace_size.restype = ctypes.c_size_t
     lib.va_varlen_fwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,

@@ -144,7 +144,7 @@ def va_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _need_dev("workspace", workspace, q.device)
     st = lib.va_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
                            cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
-                           int(bool(causal)), bptr, bstr, _row_strides(q, k, v), out.data_ptr(), lse.data_ptr(),
+                           int(bool(causal)), bptr, bstr, out.data_ptr(), lse.data_ptr(), _row_strides(q, k, v),
                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                            batch, tq, tk, hq, hkv, d, dt, _stream(q.device))
     _raise(st, lib)
@@ -247,7 +247,8 @@ def va_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch
     With ``dbias`` (a float32 device tensor) and ``dbias_stride`` (4 element
     strides relative to ``dbias``'s first element; 0 sums over that axis), the
     bias gradient is written into ``dbias`` as include/va_varlen.h describes
-    (elements of pairs in key blocks a causal mask skips are left as they are).
+    (every element of a valid (row, key) pair, 0 where a causal mask hides it;
+    elements no valid pair addresses are left as they are).
     """
     lib = _lib.load()
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -307,8 +308,8 @@ def va_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch
     st = lib.va_varlen_bwd(dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                            out.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
                            cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
-                           int(bool(causal)), bptr, bstr, _row_strides(q, k, v), dq.data_ptr(), dk.data_ptr(),
-                           dv.data_ptr(), dbptr, dbstr, workspace.data_ptr(),
+                           int(bool(causal)), bptr, bstr, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dbptr,
+                           dbstr, _row_strides(q, k, v), workspace.data_ptr(),
                            workspace.numel() * workspace.element_size(), batch, tq, tk, hq, hkv,
                            d, dt, gdt, _stream(q.device))
     _raise(st, lib)
@@ -335,7 +336,9 @@ class _VarlenAttn(torch.autograd.Function):
         db, dbs = None, None
         if bias is not None and ctx.needs_input_grad[9]:
             # a dense float32 gradient shaped like the bias; its size-1 head or row axis
-            # (a head-shared or per-key bias) is summed over by a zero stride
+            # (a head-shared or per-key bias) is summed over by a zero stride.  Zeroed:
+            # grid elements past a sequence's length belong to no valid pair, so the
+            # library leaves them alone, and their gradient is 0
             db = torch.zeros(bias.shape, dtype=torch.float32, device=bias.device)
             dbs = list(db.stride())
             for ax in (1, 2):

@@ -31,7 +31,7 @@ va_status fail(va_status s, const char* fmt, ...) {
 }
 
 // Head dims of the packed forward and backward (multiples of the 32-wide
-// MFMA output tile); the decode kernels take 64 and 128.
+// MFMA output tile); the decode kernels take 32, 64, 96 and 128.
 bool varlen_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128 || d == 256; }
 bool decode_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
 
@@ -63,7 +63,7 @@ va_status check_common(const Common& c, float scale, const void* bias, const int
   if (c.dtype != VA_F32 && c.dtype != VA_BF16 && c.dtype != VA_F16)
     return fail(VA_ERR_UNSUPPORTED, "unknown dtype %d", (int)c.dtype);
   if (!varlen_head_dim(c.d))
-    return fail(VA_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64, 96 or 128)", c.d);
+    return fail(VA_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64, 96, 128 or 256)", c.d);
   if ((int64_t)c.total_q * c.hq * c.d >= ((int64_t)1 << 40) ||
       (int64_t)c.total_k * c.hkv * c.d >= ((int64_t)1 << 40))
     return fail(VA_ERR_UNSUPPORTED, "tensor too large");
@@ -165,14 +165,15 @@ va::PlanArgs plan_args(const va::Plan& plan, const PlanLayout& L, const int32_t*
   return a;
 }
 
-PlanLayout fwd_plan(int batch, int total_q, int max_k, int hq, int d, bool bf16) {
+// budget: bytes the partial results of split tiles may take
+PlanLayout fwd_plan(int batch, int total_q, int max_k, int hq, int d, bool bf16, size_t budget) {
   const int bm = va::fwd_block_m(), bn = va::fwd_block_n(bf16, d);
   return plan_layout(total_q, batch, bm, max_k, bn, kChunkKeys / bn,
-                     (size_t)hq * bm * (d + 1) * sizeof(float), kFwdPartBudget);
+                     (size_t)hq * bm * (d + 1) * sizeof(float), budget);
 }
 
-size_t fwd_workspace(int batch, int total_q, int max_k, int hq, int d, bool bf16) {
-  const PlanLayout L = fwd_plan(batch, total_q, max_k, hq, d, bf16);
+size_t fwd_workspace(int batch, int total_q, int max_k, int hq, int d, bool bf16, size_t budget) {
+  const PlanLayout L = fwd_plan(batch, total_q, max_k, hq, d, bf16, budget);
   return L.plan_bytes + round_up(L.slot_bytes * L.slot_cap);
 }
 
@@ -301,11 +302,38 @@ size_t va_varlen_fwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
                                     int32_t max_seqlen_q, int32_t max_seqlen_k,
                                     int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                                     va_dtype dtype) {
+  return va::varlen_fwd_need(batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv,
+                             head_dim, dtype, kFwdPartBudget);
+}
+
+va_status va_varlen_fwd(const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                        int causal, const void* bias, const int64_t* bias_stride, void* out,
+                        float* lse, const int64_t* qkv_row_stride, void* workspace,
+                        size_t workspace_bytes, int32_t batch,
+                        int32_t total_q, int32_t total_k, int32_t num_heads_q,
+                        int32_t num_heads_kv, int32_t head_dim, va_dtype dtype,
+                        va_stream stream) {
+  return va::varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
+                        bias, bias_stride, out, lse, qkv_row_stride, workspace, workspace_bytes, kFwdPartBudget,
+                        batch, total_q, total_k, num_heads_q, num_heads_kv, head_dim, dtype, stream);
+}
+
+}  // extern "C"
+
+namespace va {
+
+void set_error(const char* msg) { snprintf(g_err, sizeof(g_err), "%s", msg); }
+
+size_t varlen_fwd_need(int32_t batch, int32_t total_q, int32_t total_k, int32_t max_seqlen_q,
+                       int32_t max_seqlen_k, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                       va_dtype dtype, size_t part_budget) {
   if (batch <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0 ||
       num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0 ||
       !varlen_head_dim(head_dim) || (dtype != VA_F32 && dtype != VA_BF16 && dtype != VA_F16))
     return 0;
-  size_t n = fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, dtype != VA_F32);
+  size_t n = fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, dtype != VA_F32, part_budget);
   if (short_query(dtype, head_dim, max_seqlen_q, num_heads_q / num_heads_kv)) {
     const size_t m = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
                                total_q).total();
@@ -314,15 +342,12 @@ size_t va_varlen_fwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
   return n;
 }
 
-va_status va_varlen_fwd(const void* q, const void* k, const void* v,
-                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                        int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
-                        int causal, const void* bias, const int64_t* bias_stride,
-                        const int64_t* qkv_row_stride, void* out,
-                        float* lse, void* workspace, size_t workspace_bytes, int32_t batch,
-                        int32_t total_q, int32_t total_k, int32_t num_heads_q,
-                        int32_t num_heads_kv, int32_t head_dim, va_dtype dtype,
-                        va_stream stream) {
+va_status varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                     const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                     float softmax_scale, int causal, const void* bias, const int64_t* bias_stride, void* out,
+                     float* lse, const int64_t* qkv_row_stride, void* workspace, size_t workspace_bytes,
+                     size_t part_budget, int32_t batch, int32_t total_q, int32_t total_k, int32_t num_heads_q,
+                     int32_t num_heads_kv, int32_t head_dim, va_dtype dtype, va_stream stream) {
   g_err[0] = 0;
   if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse || !workspace)
     return fail(VA_ERR_INVALID, "a required pointer is NULL");
@@ -336,7 +361,7 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
   if (((uintptr_t)workspace) % kAlign != 0)
     return fail(VA_ERR_INVALID, "workspace must be 256-byte aligned");
   const bool bf16 = dtype != VA_F32;  // a 16-bit kind (bf16 or f16)
-  const size_t need = fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16);
+  const size_t need = fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16, part_budget);
   if (workspace_bytes < need)
     return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
 
@@ -396,7 +421,7 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.causal = causal;
   a.bf16 = elem_code(dtype);
-  const PlanLayout L = fwd_plan(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16);
+  const PlanLayout L = fwd_plan(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16, part_budget);
   char* w = (char*)workspace;
   const size_t used = carve_plan(w, L, a.plan);
   a.part_o = (float*)(w + used);
@@ -411,6 +436,10 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return VA_OK;
 }
+
+}  // namespace va
+
+extern "C" {
 
 size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t total_k,
                                     int32_t max_seqlen_q, int32_t max_seqlen_k,
@@ -430,9 +459,8 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
                         const void* out, const float* lse, const int32_t* cu_seqlens_q,
                         const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
                         float softmax_scale, int causal, const void* bias,
-                        const int64_t* bias_stride, const int64_t* qkv_row_stride, void* dq,
-                        void* dk, void* dv, float* dbias,
-                        const int64_t* dbias_stride, void* workspace,
+                        const int64_t* bias_stride, void* dq, void* dk, void* dv, float* dbias,
+                        const int64_t* dbias_stride, const int64_t* qkv_row_stride, void* workspace,
                         size_t workspace_bytes, int32_t batch, int32_t total_q, int32_t total_k,
                         int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                         va_dtype dtype, va_dtype grad_dtype, va_stream stream) {
@@ -581,7 +609,7 @@ va_status va_kvcache_fwd(const void* q, const void* k_cache, const void* v_cache
   if (dtype != VA_BF16 && dtype != VA_F16)
     return fail(VA_ERR_UNSUPPORTED, "decode steps take bf16 or float16 (got dtype %d)", (int)dtype);
   if (!decode_head_dim(head_dim))
-    return fail(VA_ERR_UNSUPPORTED, "head_dim %d not supported in decode steps (64 or 128)", head_dim);
+    return fail(VA_ERR_UNSUPPORTED, "head_dim %d not supported in decode steps (32, 64, 96 or 128)", head_dim);
   if (!kv_args_ok(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, dtype))
     return fail(VA_ERR_UNSUPPORTED, "max_seqlen_q * num_heads_q * head_dim * 2 must be < 2^31");
   const KvLayout L = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);

@@ -502,6 +502,17 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
           }
         }
       }
+      if constexpr (HAS_BIAS) {
+        // per-pair bias gradient of a query block that sees none of this wave's keys: 0
+        if (!active && a.dbias_mode == 1 && hb == 0 && kj < Lk) {
+          float* db = a.dbias + (int64_t)b * a.ds0 + (int64_t)h * a.ds1 + (int64_t)kj * a.ds3;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qi = qb + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if (qi < Lq) db[(int64_t)qi * a.ds2] = 0.f;
+          }
+        }
+      }
       if (k + 1 < k_total) commit(buf ^ 1);
       __syncthreads();
     };
@@ -510,6 +521,15 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
       // per-key bias gradient: each wave sums into its own 32 columns (no barrier needed)
       if (a.dbias_mode == 2 && hh == 0)
         for (int r = 0; r < (a.ds1 == 0 ? 1 : hpw); ++r) db_acc[r * BNK + 32 * wid + r32] = 0.f;
+      // per-pair bias gradient of the rows before the first query that sees the tile
+      // (causal): 0, written once per (tile, head) by the tile's first chunk, the two
+      // lane halves taking alternate rows
+      if (a.dbias_mode == 1 && hb == 0 && u0 == 0 && kj < Lk && qs > 0) {
+        for (int r = 0; r < hpw; ++r) {
+          float* db = a.dbias + (int64_t)b * a.ds0 + (int64_t)(h_first + r) * a.ds1 + (int64_t)kj * a.ds3;
+          for (int qi = hh; qi < min(qs, Lq); qi += 2) db[(int64_t)qi * a.ds2] = 0.f;
+        }
+      }
     }
     int2 rn = make_int2(0, u0);
     if (k_total > 0) { issue(rn, 0); commit(0); }

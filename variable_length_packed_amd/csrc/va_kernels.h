@@ -5,7 +5,24 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "va_varlen.h"
+
 namespace va {
+
+// The packed forward (va_varlen_fwd) with the bytes split tiles' partial
+// results may take from the workspace as an argument, and the workspace it
+// then needs (0 for arguments it would reject).
+va_status varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                     const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                     float softmax_scale, int causal, const void* bias, const int64_t* bias_stride, void* out,
+                     float* lse, const int64_t* qkv_row_stride, void* workspace, size_t workspace_bytes,
+                     size_t part_budget, int32_t batch, int32_t total_q, int32_t total_k, int32_t num_heads_q,
+                     int32_t num_heads_kv, int32_t head_dim, va_dtype dtype, va_stream stream);
+size_t varlen_fwd_need(int32_t batch, int32_t total_q, int32_t total_k, int32_t max_seqlen_q,
+                       int32_t max_seqlen_k, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                       va_dtype dtype, size_t part_budget);
+// Sets the calling thread's va_last_error() text.
+void set_error(const char* msg);
 
 // ---------------------------------------------------------------------------
 // Work plans.  A pass tiles one side of every sequence (query rows for the
