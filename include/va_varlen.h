@@ -217,6 +217,36 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
                         va_dtype dtype, va_dtype grad_dtype, va_stream stream);
 
 /*
+ * Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The same computation and arguments as va_varlen_fwd (results
+ * bitwise identical whenever both plan the same split tiles), without the
+ * workspace arguments: the work plan and the partial results of split tiles
+ * go to a fixed array of VA_NOALLOC_SCRATCH_BYTES in the library's own device
+ * memory, one per GPU, held until the process ends.  The call allocates and
+ * frees nothing.  Sizes whose work plan does not fit the array return
+ * VA_ERR_WORKSPACE (use va_varlen_fwd with a workspace); when the plan fits
+ * but the hints allow more split tiles than the rest of the array holds,
+ * tiles are split into longer chunks (or not at all), as for a workspace
+ * whose partial budget is exhausted.  Every call on one GPU shares that GPU's
+ * array: calls that may overlap on one GPU (several streams or threads) race
+ * and must be serialised by the caller.  Nothing in the array needs clearing
+ * between calls.
+ */
+#define VA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+va_status va_varlen_fwd_noalloc(const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                float softmax_scale, int causal,
+                                const void* bias, const int64_t* bias_stride,
+                                void* out, float* lse,
+                                const int64_t* qkv_row_stride,
+                                int32_t batch, int32_t total_q, int32_t total_k,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                va_dtype dtype, va_stream stream);
+
+/*
  * Measurement.  The metric of this library is non-padded attention TFLOP/s
  * per kernel against the MI355X roofline, so a caller can time each kernel a
  * call launches.  After va_timing_start(n), the calling thread's library

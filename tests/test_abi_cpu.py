@@ -353,3 +353,33 @@ def test_short_query_forward_workspace(lib):
     # 16 tokens with 8 heads per KV head (128 rows) and 24 tokens with 4 (96 rows) do not
     assert f(256, 256 * 16, 256 * 1024, 16, 1024, 32, 4, 128, BF16) > want // 100
     assert f(256, 256 * 24, 256 * 1024, 24, 1024, 16, 4, 128, BF16) > want // 100
+
+
+def _fwd_noalloc(lib, **kw):
+    a = dict(q=P, k=P, v=P, cq=P, ck=P, mq=8, mk=8, scale=0.125, causal=1, bias=None,
+             bstr=None, rs=None, out=P, lse=P, batch=2, tq=16, tk=16, hq=4, hkv=2, d=64, dt=BF16)
+    a.update(kw)
+    bstr = _lib.strides_arg(a["bstr"]) if a["bstr"] is not None else None
+    rs = _lib.strides_arg(a["rs"]) if a["rs"] is not None else None
+    return lib.va_varlen_fwd_noalloc(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["mq"], a["mk"], a["scale"],
+                                     a["causal"], a["bias"], bstr, a["out"], a["lse"], rs, a["batch"], a["tq"],
+                                     a["tk"], a["hq"], a["hkv"], a["d"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), INVALID),
+    (dict(tq=0), INVALID),
+    (dict(hq=6, hkv=4), INVALID),
+    (dict(mq=0), INVALID),
+    (dict(d=80), UNSUPPORTED),
+    (dict(dt=7), UNSUPPORTED),
+    # a work plan larger than the library's scratch array (2^20 sequences)
+    (dict(batch=1 << 20, tq=1 << 22, tk=1 << 22, mq=1 << 22, mk=1 << 22, hq=64, hkv=8), WORKSPACE),
+])
+def test_fwd_noalloc_validation(lib, kw, code):
+    """The allocation-free forward checks sizes on the host before it looks up its scratch array."""
+    assert _fwd_noalloc(lib, **kw) == code
+    msg = lib.va_last_error()
+    assert msg
+    if code == WORKSPACE:
+        assert b"allocation-free" in msg

@@ -15,7 +15,7 @@ VA_F32, VA_BF16, VA_F16 = 0, 1, 2
 EXPORTS = ("va_varlen_fwd", "va_varlen_bwd", "va_varlen_fwd_workspace_size",
            "va_varlen_bwd_workspace_size", "va_status_string", "va_last_error", "va_version",
            "va_timing_start", "va_timing_stop", "va_pack_metadata", "va_unpad", "va_pad",
-           "va_kvcache_fwd", "va_kvcache_fwd_workspace_size")
+           "va_kvcache_fwd", "va_kvcache_fwd_workspace_size", "va_varlen_fwd_noalloc")
 VA_PACK_MAX_TENSORS = 4
 
 
@@ -49,6 +49,10 @@ def load() -> ctypes.CDLL:
     lib.va_varlen_fwd.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p, _i64p, _p, _p,
                                   _i64p, _p, ctypes.c_size_t, _i32, _i32, _i32, _i32, _i32, _i32,
                                   ctypes.c_int, _p]
+    # the forward's arguments without the workspace pair
+    lib.va_varlen_fwd_noalloc.restype = ctypes.c_int
+    lib.va_varlen_fwd_noalloc.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p, _i64p, _p,
+                                          _p, _i64p, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p]
     lib.va_varlen_bwd.restype = ctypes.c_int
     # dout, q, k, v, out, lse, cu_q, cu_k, max_q, max_k, scale, causal, bias, bias_stride,
     # dq, dk, dv, dbias, dbias_stride, qkv_row_stride, workspace, workspace_bytes, batch, total_q,

@@ -349,7 +349,7 @@ va_status varlen_fwd(const void* q, const void* k, const void* v, const int32_t*
                      size_t part_budget, int32_t batch, int32_t total_q, int32_t total_k, int32_t num_heads_q,
                      int32_t num_heads_kv, int32_t head_dim, va_dtype dtype, va_stream stream) {
   g_err[0] = 0;
-  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse || !workspace)
+  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse)
     return fail(VA_ERR_INVALID, "a required pointer is NULL");
   Common c{batch, total_q, total_k, num_heads_q, num_heads_kv, head_dim, max_seqlen_q,
            max_seqlen_k, causal, dtype};
@@ -358,6 +358,7 @@ va_status varlen_fwd(const void* q, const void* k, const void* v, const int32_t*
   int64_t rs[3];
   s = row_strides(c, q, k, v, qkv_row_stride, rs);
   if (s != VA_OK) return s;
+  if (!workspace) return fail(VA_ERR_INVALID, "workspace is NULL");
   if (((uintptr_t)workspace) % kAlign != 0)
     return fail(VA_ERR_INVALID, "workspace must be 256-byte aligned");
   const bool bf16 = dtype != VA_F32;  // a 16-bit kind (bf16 or f16)
