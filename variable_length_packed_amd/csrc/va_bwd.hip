@@ -21,8 +21,8 @@
 // lane holds one query row and dS^T feeds the dQ^T contraction straight from
 // registers.
 //
-// Both take their units from the planner's list through an atomic queue,
-// heaviest first.
+// Both take their units from the planner's list, heaviest first, in the fixed
+// snake order of snake_item() (no atomics).
 //
 // No mask is needed for a key past the sequence (its K and V read as zero and
 // its dK/dV row is never stored; in dQ its zero K row adds nothing) or for a
@@ -289,12 +289,8 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
   const int krow_bytes = (int)(kstride * ELT), vrow_bytes = (int)(vstride * ELT);
   const int hpw = a.n_rep;  // every query head of the group
 
-  int ticket = 0;  // thread 0: ticket of the item after the current one
-  if (tid == 0) {
-    const int first = (int)blockIdx.x;
-    item_store(s_info[0], item_load(a.plan_k, first, per_unit, total_items));
-    if (first < total_items) ticket = queue_take(a.plan_k.hdr);
-  }
+  int kth = 0;  // items this workgroup has run
+  if (tid == 0) item_store(s_info[0], item_load(a.plan_k, (int)blockIdx.x, per_unit, total_items));
   __syncthreads();
   for (int cur = 0;; cur ^= 1) {
     const int* inf = s_info[cur];
@@ -538,7 +534,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     ItemInfo nxt;
-    if (tid == 0) nxt = item_load(a.plan_k, (int)gridDim.x + ticket, per_unit, total_items);
+    if (tid == 0) nxt = item_load(a.plan_k, snake_item(kth + 1, blockIdx.x, gridDim.x), per_unit, total_items);
     int k = 0;
     for (; k < k_masked; ++k) {
       const int2 nx = next_of(k + 1, rn);
@@ -550,10 +546,8 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
       step(std::integral_constant<bool, false>(), k, rn, nx);
       rn = nx;
     }
-    if (tid == 0) {
-      item_store(s_info[cur ^ 1], nxt);  // before the output stores
-      ticket = queue_take(a.plan_k.hdr);  // waited for in the next item's prologue
-    }
+    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
+    ++kth;
 
     if constexpr (HAS_BIAS) {
       if (a.dbias_mode == 2 && hh == 0 && hb == 0) {
@@ -710,12 +704,8 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   const int krow_bytes = (int)(kstride * ELT), vrow_bytes = (int)(vstride * ELT);
   const int gelt = a.grad_bf16 ? 2 : 4;
 
-  int ticket = 0;  // thread 0: ticket of the item after the current one
-  if (tid == 0) {
-    const int first = (int)blockIdx.x;
-    item_store(s_info[0], item_load(a.plan_q, first, a.hq, total_items));
-    if (first < total_items) ticket = queue_take(a.plan_q.hdr);
-  }
+  int kth = 0;  // items this workgroup has run
+  if (tid == 0) item_store(s_info[0], item_load(a.plan_q, (int)blockIdx.x, a.hq, total_items));
   __syncthreads();
   for (int cur = 0;; cur ^= 1) {
     const int* inf = s_info[cur];
@@ -892,14 +882,12 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     ItemInfo nxt;
-    if (tid == 0) nxt = item_load(a.plan_q, (int)gridDim.x + ticket, a.hq, total_items);
+    if (tid == 0) nxt = item_load(a.plan_q, snake_item(kth + 1, blockIdx.x, gridDim.x), a.hq, total_items);
     int n = n0;
     for (; n < min(n_plain, n1); ++n) step(std::integral_constant<bool, false>(), n);
     for (; n < n1; ++n) step(std::integral_constant<bool, true>(), n);
-    if (tid == 0) {
-      item_store(s_info[cur ^ 1], nxt);  // before the output stores
-      ticket = queue_take(a.plan_q.hdr);  // waited for in the next item's prologue
-    }
+    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
+    ++kth;
 
     if (slot < 0) {
       // rows < 0 fall outside the resource: their stores are dropped

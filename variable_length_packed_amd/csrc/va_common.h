@@ -174,24 +174,17 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Work queue.  A planner kernel writes, per pass, a list of work units sorted
-// by cost (heaviest first) and zeroes hdr[0]; the pass's persistent
-// workgroups then take items in list order, so the heavy units start first
-// and the light ones fill in behind them.  Workgroup w starts with item w;
-// later items are gridDim.x + a ticket from one device-scope atomic, taken
-// by thread 0 one item ahead (a workgroup takes a ticket only while it holds
-// a valid item, and tickets grow, so every valid item is run exactly once).
-// The atomic's address goes through a register the compiler must treat as
-// per-lane: a uniform address would be rewritten into a one-lane atomic plus
-// an immediate broadcast, i.e. a wait for the atomic's full round trip (which
-// also drains every store still in flight) at the point of the call.  This
-// way the wait happens where the ticket is first used.
+// Work assignment.  A planner kernel writes, per pass, the list of work units
+// sorted by cost (heaviest first); the pass's persistent workgroups then take
+// the items of that list in a fixed order: rounds of gridDim.x items, with
+// workgroup w taking position w of even rounds and position gridDim.x - 1 - w
+// of odd rounds (a snake over the sorted list, so a workgroup's heavy items
+// pair with light ones).  No atomics: on MI355X a device-scope atomic resolves
+// past the per-XCD L2, and one shared queue cursor taken per item cost more
+// (measured: 4-6 us of a 45 us forward, 24 us when items are short) than the
+// imbalance a dynamic queue removes.  The order depends on the list alone.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int queue_take(int* hdr) {  // the ticket; its item is gridDim.x + ticket
-  int z;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-  return __hip_atomic_fetch_add(hdr + z, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+__device__ __forceinline__ int snake_item(int k, int w, int g) { return k * g + ((k & 1) ? g - 1 - w : w); }
 
 // A work item and its unit's plan entries.  Thread 0 loads the entries of
 // the next item while the current item computes and publishes them in LDS

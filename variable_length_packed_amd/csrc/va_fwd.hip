@@ -157,12 +157,8 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
   const size_t qstride = (size_t)a.q_rs, ostride = (size_t)a.hq * D;
   const size_t kstride = (size_t)a.k_rs, vstride = (size_t)a.v_rs;
 
-  int ticket = 0;  // thread 0: ticket of the item after the current one
-  if (tid == 0) {
-    const int first = (int)blockIdx.x;
-    item_store(s_info[0], item_load(a.plan, first, a.hq, total_items));
-    if (first < total_items) ticket = queue_take(a.plan.hdr);
-  }
+  int kth = 0;  // items this workgroup has run
+  if (tid == 0) item_store(s_info[0], item_load(a.plan, (int)blockIdx.x, a.hq, total_items));
   __syncthreads();
   for (int cur = 0;; cur ^= 1) {
     const int* inf = s_info[cur];
@@ -624,7 +620,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     if (active(0)) qk(0, s_cur);
     __syncthreads();  // every wave has read K(0) before K(2) replaces it
     ItemInfo nxt;
-    if (tid == 0) nxt = item_load(a.plan, (int)gridDim.x + ticket, a.hq, total_items);
+    if (tid == 0) nxt = item_load(a.plan, snake_item(kth + 1, blockIdx.x, gridDim.x), a.hq, total_items);
 
     auto step = [&](auto mask_tag, int n) {  // n: block index inside the unit
       constexpr bool MASK = decltype(mask_tag)::value;
@@ -701,10 +697,8 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       for (; j < j_plain; ++j) step(std::integral_constant<bool, false>(), j);
     }
     for (; j < nb; ++j) step(std::integral_constant<bool, true>(), j);
-    if (tid == 0) {
-      item_store(s_info[cur ^ 1], nxt);  // before the output stores
-      ticket = queue_take(a.plan.hdr);  // waited for in the next item's prologue
-    }
+    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
+    ++kth;
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; a chunk of a split
     // tile stores O and the base-2 LSE in float32 to its slot instead

@@ -9,8 +9,8 @@
 // asked once per device with that device current and kept here.  Every call
 // on a GPU shares that GPU's copy: calls that may overlap on one GPU (other
 // streams, other threads) race on it.  Nothing in it needs clearing between
-// calls: the planner resets its queue cursor, and every partial result is
-// written before it is read.
+// calls: the planner rewrites the whole work plan, and every partial result
+// is written before it is read.
 #include <mutex>
 
 #include "va_kernels.h"

@@ -1,7 +1,7 @@
 // Planner: turns cu_seqlens into the sorted work-unit list of a pass (see
 // Plan in va_kernels.h).  One workgroup per plan, run right before the pass
-// on the same stream; it also zeroes the pass's queue cursor, so a call
-// needs no memset and no host read of device memory.
+// on the same stream; it rewrites the whole plan, so a call needs no memset
+// and no host read of device memory.
 //
 // Steps: (1) count, for the fixed chunk and for 2x, 4x, ... 32x it, the units,
 // partial slots and split tiles every tile needs, and take the smallest
@@ -10,8 +10,9 @@
 // the workspace gets coarser chunks, or none, rather than failing);
 // (2) histogram the units by step count and scan it from the largest count
 // down; (3) place every unit at its bin's cursor.
-// Within a bin the order is whatever the atomics give: the units of a bin
-// are independent, and a unit's results do not depend on its position.
+// Within a bin the order is whatever the LDS atomics give: the units of a
+// bin cost the same, and a unit's results depend neither on its position
+// nor on the workgroup that runs it.
 #include "va_plan.h"
 
 namespace va {
