@@ -9,11 +9,11 @@
 // dK/dV kernel: a work unit is 128 keys (32 per wave) of one sequence and KV
 // head; K and V stay in registers while the workgroup walks the 32-query
 // blocks that see those keys, for every query head of the GQA group, staging
-// Q and dO in LDS both as rows (for S and dP) and transposed (for the
-// contractions over queries).  A key tile seen by many query blocks is split
-// into units over ranges of query blocks; those write float32 partial sums
-// and a merge kernel adds them in chunk order, so results never depend on
-// scheduling.
+// Q and dO in LDS as rows: read as rows for S and dP, and with transposing LDS
+// reads for the contractions over queries.  A key tile seen by many query
+// blocks is split into units over ranges of query blocks; those write float32
+// partial sums that the dQ pass, after its own items, adds in chunk order, so
+// results never depend on scheduling.
 //
 // dQ kernel: shaped like the forward.  A unit is 128 query rows of one head
 // (or a range of key blocks of them, merged the same way); Q and dO stay in
@@ -52,70 +52,41 @@ constexpr int BMQ_DQ = 128;  // query rows per dQ workgroup
 template <int H16>
 using elem_t = typename std::conditional<(H16 != 0), uint16_t, float>::type;
 
-// Row r's position inside a transposed bf16 LDS row (bits 2 and 3 swapped so
-// the 8 k-slots of a lane half are contiguous), and the XOR swizzle of the
-// 16-byte chunks of transposed row d (spreads the transposing stores and the
-// fragment reads over the LDS banks).
-__device__ __forceinline__ int tpos(int r) {
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-template <int ROWS>
-__device__ __forceinline__ int tswz(int d) { return ((d >> 3) & (ROWS / 8 - 1)) << 3; }
-
 // Stages a [ROWS][D] block (rows row0 .. of a buffer resource; rows outside
-// read as zero) into LDS as rows ([ROWS][D + pad]) and, for bf16, transposed
-// ([D][ROWS + pad], swizzled).  Each thread owns pairs of consecutive rows of
-// one 16-byte chunk, so the transposed store can pair them.
-template <int H16, int ROWS, int D, bool TRANS>
+// read as zero) into LDS rows ([ROWS][D + pad]), one 16-byte piece per task,
+// consecutive threads along a row.  The 16-bit operands that contract over
+// the rows (dO^T and Q^T in dK/dV, K^T in dQ) are read from these rows with
+// transposing LDS reads (tr_frag), so no transposed copy is ever written.
+template <int H16, int ROWS, int D>
 struct Stager {
   using T = elem_t<H16>;
   static constexpr int EPV = 16 / sizeof(T);
-  static constexpr int CH = D / EPV;                     // 16-byte chunks per row
-  static constexpr int PAIRS = (ROWS / 2) * CH;          // tasks
-  static constexpr int TPT = (PAIRS + NT - 1) / NT;      // tasks per thread
-  static constexpr int NP = D + 16 / (int)sizeof(T);     // row pitch (elements)
-  static constexpr int TP = ROWS + 16 / (int)sizeof(T);  // transposed pitch
-  u32x4_t r[2 * TPT];
+  static constexpr int CH = D / EPV;                  // 16-byte pieces per row
+  static constexpr int TASKS = ROWS * CH;
+  static constexpr int TPT = (TASKS + NT - 1) / NT;   // pieces per thread
+  static constexpr int NP = D + 16 / (int)sizeof(T);  // row pitch (elements)
+  u32x4_t r[TPT];
 
   __device__ __forceinline__ void load(rsrc_t res, int row_bytes, int row0) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int u = threadIdx.x + i * NT;
-      if (PAIRS % NT != 0 && u >= PAIRS) continue;  // a partial last round
-      const int c = u % CH, p = u / CH;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) r[2 * i + e] = buf_load16(res, (row0 + 2 * p + e) * row_bytes + c * 16);
+      if (TASKS % NT != 0 && u >= TASKS) continue;  // a partial last round
+      const int c = u % CH, row = u / CH;
+      r[i] = buf_load16(res, (row0 + row) * row_bytes + c * 16);
     }
   }
 
-  __device__ __forceinline__ void store(T* __restrict__ dn, T* __restrict__ dt) {
+  __device__ __forceinline__ void store(T* __restrict__ dn) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int u = threadIdx.x + i * NT;
-      if (PAIRS % NT != 0 && u >= PAIRS) continue;  // a partial last round
-      const int c = u % CH, p = u / CH;
-      *(u32x4_t*)(dn + (2 * p) * NP + c * EPV) = r[2 * i];
-      *(u32x4_t*)(dn + (2 * p + 1) * NP + c * EPV) = r[2 * i + 1];
-      if constexpr (H16 && TRANS) {
-        const int pos = tpos(2 * p) ^ tswz<ROWS>(c * 8);  // rows c*8 .. c*8+7 share the swizzle
-        const u32x4_t a = r[2 * i], b = r[2 * i + 1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (a[e] & 0xFFFFu) | (b[e] << 16);
-          const uint32_t hi = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
-          *(uint32_t*)(dt + (c * 8 + 2 * e) * TP + pos) = lo;
-          *(uint32_t*)(dt + (c * 8 + 2 * e + 1) * TP + pos) = hi;
-        }
-      }
+      if (TASKS % NT != 0 && u >= TASKS) continue;  // a partial last round
+      const int c = u % CH, row = u / CH;
+      *(u32x4_t*)(dn + row * NP + c * EPV) = r[i];
     }
   }
 };
-
-// 16-byte fragment of transposed row d (k-slot chunk kc of lane half hh).
-template <int ROWS, int TP>
-__device__ __forceinline__ u32x4_t tfrag(const uint16_t* t, int d, int kc, int hh) {
-  return *(const u32x4_t*)(t + d * TP + ((16 * kc + 8 * hh) ^ tswz<ROWS>(d)));
-}
 
 // Register fragment of this lane's row for the "other" operand of a 32x32
 // MFMA contracting over head_dim: bf16 -> D/16 vectors of 8; f32 -> D/2
@@ -236,11 +207,9 @@ constexpr int BMQ = 32;  // queries per dK/dV block
 template <int H16, int D>
 struct DkdvSmem {
   using T = elem_t<H16>;
-  using St = Stager<H16, BMQ, D, true>;
+  using St = Stager<H16, BMQ, D>;
   T qn[2][BMQ * St::NP];
   T dn[2][BMQ * St::NP];
-  T qt[2][H16 ? D * St::TP : 1];
-  T dt[2][H16 ? D * St::TP : 1];
   float lse2[2][BMQ];
   float dsum[2][BMQ];
 };
@@ -389,8 +358,8 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
       // the bias tile's direct loads were issued before Q and dO: wait for all of them
       // so the barrier after this publishes the tile
       if constexpr (btile) __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      sq.store(sm.qn[buf], sm.qt[buf]);
-      sd.store(sm.dn[buf], sm.dt[buf]);
+      sq.store(sm.qn[buf]);
+      sd.store(sm.dn[buf]);
       if (tid < BMQ) {
         // rows past the sequence get P = exp2(x - inf) = 0, and so does a row that sees nothing
         sm.lse2[buf][tid] = pi < Lq && pl != -INFINITY ? pl * kLog2e : INFINITY;
@@ -476,9 +445,10 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
             pack8<H16>(&ds[8 * c], da, &da_lo);
 #pragma unroll
             for (int dt_ = 0; dt_ < DTO; ++dt_) {
-              const int d = 32 * (dt_ + hb * DTO) + r32;
-              const u32x4_t ob = tfrag<BMQ, St::TP>(sm.dt[buf], d, c, hh);
-              const u32x4_t qb4 = tfrag<BMQ, St::TP>(sm.qt[buf], d, c, hh);
+              // dims 32 (dt_ + hb DTO) + r32 of the queries of P's chunk c, from the rows
+              const int c0 = 32 * (dt_ + hb * DTO);
+              const u32x4_t ob = tr_frag(sm.dn[buf], St::NP, c, c0);
+              const u32x4_t qb4 = tr_frag(sm.qn[buf], St::NP, c, c0);
               dv[dt_] = mfma16<H16>(pa, ob, dv[dt_]);
               dk[dt_] = mfma16<H16>(da, qb4, dk[dt_]);
               dk[dt_] = mfma16<H16>(da_lo, qb4, dk[dt_]);
@@ -670,10 +640,9 @@ template <int H16, int D>
 struct DqSmem {
   using T = elem_t<H16>;
   static constexpr int BN = (H16 && D <= 64) ? 64 : 32;
-  using St = Stager<H16, BN, D, true>;
-  using Sv = Stager<H16, BN, D, false>;
+  using St = Stager<H16, BN, D>;
+  using Sv = Stager<H16, BN, D>;
   T kn[2][BN * St::NP];
-  T kt[2][H16 ? D * St::TP : 1];
   T vn[2][BN * St::NP];
 };
 
@@ -848,7 +817,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
             pack8<H16>(&dsv[8 * kc], pb, nullptr);
 #pragma unroll
             for (int dt_ = 0; dt_ < DT; ++dt_)
-              acc[dt_] = mfma16<H16>(tfrag<BN, St::TP>(sm.kt[buf], 32 * dt_ + r32, kc, hh), pb, acc[dt_]);
+              acc[dt_] = mfma16<H16>(tr_frag(sm.kn[buf], St::NP, kc, 32 * dt_), pb, acc[dt_]);
           }
         } else {
 #pragma unroll
@@ -865,8 +834,8 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
         }
       }
       if (n + 1 < n1) {
-        sk.store(sm.kn[buf ^ 1], sm.kt[buf ^ 1]);
-        sv.store(sm.vn[buf ^ 1], nullptr);
+        sk.store(sm.kn[buf ^ 1]);
+        sv.store(sm.vn[buf ^ 1]);
       }
       __syncthreads();
     };
@@ -874,8 +843,8 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     if (n1 > n0) {
       sk.load(kres, krow_bytes, n0 * BN);
       sv.load(vres, vrow_bytes, n0 * BN);
-      sk.store(sm.kn[0], sm.kt[0]);
-      sv.store(sm.vn[0], nullptr);
+      sk.store(sm.kn[0]);
+      sv.store(sm.vn[0]);
     }
     // every load so far (Q and dO fragments included) has landed: the steps below then
     // wait only for their own prefetches
@@ -921,6 +890,14 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
+  }
+  // then the merge slabs of split dK/dV tiles (the dK/dV pass has finished),
+  // continuing the same order: workgroups with fewer dQ items take more slabs
+  const int merge_items = uniform(a.plan_k.hdr[2]) * a.hkv * 4;
+  for (int k2 = kth;; ++k2) {
+    const int m = snake_item(k2, blockIdx.x, gridDim.x) - total_items;
+    if (m >= merge_items) break;
+    dkdv_merge_item<D>(a, m);
   }
 }
 
@@ -969,17 +946,13 @@ __device__ __forceinline__ void dq_merge_item(const BwdArgs& a, int it) {
   }
 }
 
-// Both merges in one launch after the dQ pass: first the dK/dV items (one
-// wave's 32 keys of a (split key tile, KV head)), then the dQ items (32 rows
-// of a (split query tile, head)); each sums its chunks in chunk order.
+// The dQ merge after the dQ pass: items of 32 rows of a (split query tile,
+// head), each summing its chunks in chunk order.  (Split dK/dV tiles are
+// merged inside the dQ pass, after its own items.)
 template <int D>
 __global__ __launch_bounds__(NT) void bwd_merge_kernel(BwdArgs a) {
-  const int nkv = uniform(a.plan_k.hdr[2]) * a.hkv * 4;
-  const int total = nkv + uniform(a.plan_q.hdr[2]) * a.hq * kMergeSlabs;
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
-    if (it < nkv) dkdv_merge_item<D>(a, it);
-    else dq_merge_item<D>(a, it - nkv);
-  }
+  const int total = uniform(a.plan_q.hdr[2]) * a.hq * kMergeSlabs;
+  for (int it = blockIdx.x; it < total; it += gridDim.x) dq_merge_item<D>(a, it);
 }
 
 template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
@@ -1020,8 +993,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.split_cap_k > 0 || a.split_cap_q > 0) {  // the split tiles' partial sums
-    int64_t g = (int64_t)a.split_cap_k * a.hkv * 4 + (int64_t)a.split_cap_q * a.hq * kMergeSlabs;
+  if (a.split_cap_q > 0) {  // the split dQ tiles' partial sums
+    int64_t g = (int64_t)a.split_cap_q * a.hq * kMergeSlabs;
     if (g > 4096) g = 4096;
     timing_before(st, "bwd_merge");
     hipLaunchKernelGGL(bwd_merge_kernel<D>, dim3((unsigned)g), dim3(NT), 0, st, a);

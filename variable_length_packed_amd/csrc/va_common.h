@@ -173,6 +173,20 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p));
 }
 
+// 16-bit MFMA operand holding, in lane l, 8 values of column c0 + l % 32 of a
+// row-major LDS tile (rows `pitch` elements apart): rows 16 kc + {4hh .. 4hh+3,
+// 8+4hh .. 8+4hh+3} (hh = l / 32) -- the k-slots a score tile's registers give
+// a 16-row chunk kc.  Two transposing reads of 4 rows each: in each group of
+// 16 lanes, lane s points at row s / 4 of the four, columns 4 (s % 4) .. +4 of
+// the group's 16.  The pitch must keep rows 8-byte aligned.
+__device__ __forceinline__ u32x4_t tr_frag(const uint16_t* tile, int pitch, int kc, int c0) {
+  const int lane = threadIdx.x & 63;
+  const uint16_t* p = tile + (16 * kc + 4 * (lane >> 5) + ((lane >> 2) & 3)) * pitch + c0 + 16 * ((lane >> 4) & 1) +
+                      4 * (lane & 3);
+  const u32x2_t lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * pitch);
+  return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+}
+
 // ---------------------------------------------------------------------------
 // Work assignment.  A planner kernel writes, per pass, the list of work units
 // sorted by cost (heaviest first); the pass's persistent workgroups then take
