@@ -211,7 +211,7 @@ struct DkdvSmem {
   T qn[2][BMQ * St::NP];
   T dn[2][BMQ * St::NP];
   float lse2[2][BMQ];
-  float dsum[2][BMQ];
+  float ndsum[2][BMQ];  // -D of each query (the dP accumulators start from it)
 };
 
 template <int H16, int D>
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
       if (tid < BMQ) {
         // rows past the sequence get P = exp2(x - inf) = 0, and so does a row that sees nothing
         sm.lse2[buf][tid] = pi < Lq && pl != -INFINITY ? pl * kLog2e : INFINITY;
-        sm.dsum[buf][tid] = pi < Lq ? pd : 0.f;
+        sm.ndsum[buf][tid] = pi < Lq ? -pd : 0.f;
       }
     };
 
@@ -377,9 +377,19 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
       // this wave's keys are seen by queries i >= wk0 - off
       const bool active = wave_keys && (!CAUSAL || qb + BMQ - 1 + off >= wk0);
       if (active) {
-        // S = Q K^T and dP = dO V^T: C[query][key], lane = key
+        // S = Q K^T and dP - D = dO V^T - D: C[query][key], lane = key.  Register i
+        // holds query 8 (i / 4) + 4 hh + i % 4, so the LSE and -D of a lane's 16 queries
+        // are four 16-byte LDS reads, and -D starts the dP accumulators.
+        f32x4_t lq[4], nd[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lq[j] = *(const f32x4_t*)&sm.lse2[buf][8 * j + 4 * hh];
+          nd[j] = *(const f32x4_t*)&sm.ndsum[buf][8 * j + 4 * hh];
+        }
+        const f32x16_t nd16 = {nd[0][0], nd[0][1], nd[0][2], nd[0][3], nd[1][0], nd[1][1], nd[1][2], nd[1][3],
+                               nd[2][0], nd[2][1], nd[2][2], nd[2][3], nd[3][0], nd[3][1], nd[3][2], nd[3][3]};
         f32x16_t s = mm_rows<H16, D>(&sm.qn[buf][r32 * St::NP], kf, (f32x16_t){}, hh);
-        f32x16_t dp = mm_rows<H16, D>(&sm.dn[buf][r32 * St::NP], vf, (f32x16_t){}, hh);
+        f32x16_t dp = mm_rows<H16, D>(&sm.dn[buf][r32 * St::NP], vf, nd16, hh);
         // the bias of head h through a resource that ends after the last element a valid
         // (row, key) reads (rounded up to a dword); rows past the sequence read 0 or are
         // zeroed below, so garbage never meets a row whose P must be 0
@@ -412,10 +422,10 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
             }
             x = __builtin_fmaf(qb + ql < Lq ? bf : 0.f, kLog2e, x);
           }
-          float pv = fast_exp2(x - sm.lse2[buf][ql]);
+          float pv = fast_exp2(x - lq[i >> 2][i & 3]);
           if constexpr (MASK) pv = cl >= thr ? pv : 0.f;
           p[i] = pv;
-          ds[i] = pv * (dp[i] - sm.dsum[buf][ql]);
+          ds[i] = pv * dp[i];
         }
         if constexpr (HAS_BIAS) {
           // bias gradient = dS (the bias enters the logits additively)
@@ -713,6 +723,9 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
       lse2 = l == -INFINITY ? INFINITY : l * kLog2e;  // a row that sees nothing adds nothing
       dsum = a.dsum[(size_t)h * a.total_q + q0 + rq];
     }
+    f32x16_t ndsum16;  // -D of this lane's row in every register: the dP^T accumulators start from it
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ndsum16[i] = -dsum;
     f32x16_t acc[DT];
 #pragma unroll
     for (int i = 0; i < DT; ++i) acc[i] = (f32x16_t){};
@@ -761,7 +774,9 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
         for (int st = 0; st < NS; ++st) {
           // S^T = K Q^T, dP^T = V dO^T: C[key][query], lane = query
           const f32x16_t s = mm_rows<H16, D>(&sm.kn[buf][(32 * st + r32) * St::NP], qf, (f32x16_t){}, hh);
-          const f32x16_t dp = mm_rows<H16, D>(&sm.vn[buf][(32 * st + r32) * St::NP], of, (f32x16_t){}, hh);
+          // dP^T - D (the no-bias kernels start the accumulators from -D, kept in registers)
+          const f32x16_t dp = mm_rows<H16, D>(&sm.vn[buf][(32 * st + r32) * St::NP], of,
+                                              HAS_BIAS ? (f32x16_t){} : ndsum16, hh);
           float bv[HAS_BIAS ? 16 : 1];
           if constexpr (HAS_BIAS) {
             // registers 4j .. 4j+3 are 4 consecutive keys: one load each when keys are
@@ -806,7 +821,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
             if constexpr (HAS_BIAS) x = __builtin_fmaf(bv[i], kLog2e, x);
             float pv = fast_exp2(x - lse2);
             if constexpr (MASK) pv = kj <= hi_row ? pv : 0.f;
-            dsv[16 * st + i] = pv * (dp[i] - dsum);
+            dsv[16 * st + i] = pv * (HAS_BIAS ? dp[i] - dsum : dp[i]);
           }
         }
         // dQ^T += K^T dS^T
