@@ -768,7 +768,81 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
         sk.load(kres, krow_bytes, kb + BN);
         sv.load(vres, vrow_bytes, kb + BN);
       }
-      if (wave_on && kb < wave_hi) {
+      // 16-bit, no bias, two 32-key score tiles per block: the tiles' MFMAs and the
+      // vector work of the softmax gradient in an explicit order -- the fragments of
+      // tile 1 are read under tile 0's MFMAs, tile 1's MFMAs run under tile 0's
+      // exponentials, and the dQ MFMAs of tile 0's keys under tile 1's
+      constexpr bool FAST = H16 && !HAS_BIAS && NS == 2;
+      if (FAST && wave_on && kb < wave_hi) {
+        constexpr int KS = D / 16;  // k-steps over head_dim
+        const T* kr = &sm.kn[buf][r32 * St::NP + 8 * hh];
+        const T* vr = &sm.vn[buf][r32 * St::NP + 8 * hh];
+        u32x4_t kf[2][KS], vf[2][KS];
+        f32x16_t s2[2] = {(f32x16_t){}, (f32x16_t){}}, dp2[2] = {ndsum16, ndsum16};
+        float dsv[32];
+        u32x4_t pbs[4];
+        // softmax gradient of tile st (lane = query, registers = keys), packed for dQ
+        auto grad = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kj = kb + 32 * st + 8 * (i >> 2) + (i & 3) + 4 * hh;
+            float pv = fast_exp2(__builtin_fmaf(s2[st][i], a.scale_log2, -lse2));
+            if constexpr (MASK) pv = kj <= hi_row ? pv : 0.f;
+            dsv[16 * st + i] = pv * dp2[st][i];
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c) pack8<H16>(&dsv[16 * st + 8 * c], pbs[2 * st + c], nullptr);
+        };
+        auto dq_mma = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+          for (int dt_ = 0; dt_ < DT; ++dt_)
+            acc[dt_] = mfma16<H16>(tr_frag(sm.kn[buf], St::NP, kc, 32 * dt_), pbs[kc], acc[dt_]);
+        };
+        // tile 0's fragments
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          kf[0][ks] = *(const u32x4_t*)(kr + 16 * ks);
+          vf[0][ks] = *(const u32x4_t*)(vr + 16 * ks);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // tile 0's S^T and dP^T - D, tile 1's fragments read under them
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s2[0] = mfma16<H16>(kf[0][ks], qf.b[ks], s2[0]);
+          kf[1][ks] = *(const u32x4_t*)(kr + 32 * St::NP + 16 * ks);
+          dp2[0] = mfma16<H16>(vf[0][ks], of.b[ks], dp2[0]);
+          vf[1][ks] = *(const u32x4_t*)(vr + 32 * St::NP + 16 * ks);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // tile 1's MFMAs, each with a share of tile 0's vector work
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s2[1] = mfma16<H16>(kf[1][ks], qf.b[ks], s2[1]);
+          dp2[1] = mfma16<H16>(vf[1][ks], of.b[ks], dp2[1]);
+        }
+        grad(0);
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);  // exponentials
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // other vector work
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // tile 0's dQ MFMAs under tile 1's vector work
+        dq_mma(0);
+        dq_mma(1);
+        grad(1);
+#pragma unroll
+        for (int i = 0; i < 2 * DT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // transposing reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);  // exponentials
+          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // other vector work
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dq_mma(2);
+        dq_mma(3);
+      } else if (wave_on && kb < wave_hi) {
         float dsv[16 * NS];
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
