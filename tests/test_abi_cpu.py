@@ -157,8 +157,11 @@ def _r(x):
     return (x + 255) // 256 * 256
 
 
-def _plan_bytes(units, splits):
-    return 256 + 2 * _r(16 * units) + _r(4 * units) + _r(16 * max(splits, 1))
+def _plan_bytes(units, splits, heads):
+    """Header, units and bounds (16 bytes per unit), slot and split index (4 each),
+    split list (16 per split) and per (split, head) counts of chunks left (4 each)."""
+    return 256 + 2 * _r(16 * units) + 2 * _r(4 * units) + _r(16 * max(splits, 1)) + \
+        _r(4 * max(splits, 1) * heads)
 
 
 def test_fwd_workspace_size(lib):
@@ -169,17 +172,17 @@ def test_fwd_workspace_size(lib):
     assert f(2, 16, 16, 8, 8, 4, 2, 80, BF16) == 0
     assert f(2, 16, 16, 8, 8, 4, 2, 96, BF16) > 0 and f(2, 16, 16, 8, 8, 4, 2, 32, F32) > 0
     # no tile can see more than 1024 keys: only the plan (<= total/128 + batch units)
-    assert f(2, 16, 16, 8, 8, 4, 2, 64, BF16) == _plan_bytes(2, 0)
-    assert f(20, 10459, 10459, 1024, 1024, 14, 2, 64, BF16) == _plan_bytes(10459 // 128 + 20, 0)
+    assert f(2, 16, 16, 8, 8, 4, 2, 64, BF16) == _plan_bytes(2, 0, 4)
+    assert f(20, 10459, 10459, 1024, 1024, 14, 2, 64, BF16) == _plan_bytes(10459 // 128 + 20, 0, 14)
     # longer keys: partial slots of hq * 128 rows * (d + 1) floats, two per tile at most
     tiles = 9687 // 128 + 16
     slot = 14 * 128 * 65 * 4
     slots = min(2 * tiles, (64 << 20) // slot)
     assert f(16, 9687, 9687, 2048, 2048, 14, 2, 64, BF16) == \
-        _plan_bytes(tiles + slots, slots // 2) + _r(slots * slot)
+        _plan_bytes(tiles + slots, slots // 2, 14) + _r(slots * slot)
     assert f(16, 9687, 9687, 2048, 2048, 14, 2, 64, F16) == f(16, 9687, 9687, 2048, 2048, 14, 2, 64, BF16)
     # float32 steps are 32 keys, so the same 1024-key chunk is 32 steps
-    assert f(2, 16, 16, 1024, 1024, 4, 2, 64, F32) == _plan_bytes(2, 0)
+    assert f(2, 16, 16, 1024, 1024, 4, 2, 64, F32) == _plan_bytes(2, 0, 4)
 
 
 def test_bwd_workspace_size(lib):
@@ -194,12 +197,13 @@ def test_bwd_workspace_size(lib):
     assert f(2, 16, 16, 416, 8, 4, 2, 64, F16, F16) == f(2, 16, 16, 416, 8, 4, 2, 64, BF16, BF16)
     # short sequences: D = rowsum(dO * O) and the two plans (dK/dV and dQ)
     n = f(2, 16, 16, 8, 8, 4, 4, 64, BF16, F32)
-    assert n == _r(4 * 16 * 4) + 2 * _plan_bytes(2, 0)  # no partial slots (per-key bias sums: none)
+    # dK/dV plan (its split tiles are merged by the dQ pass: no counts) + dQ plan
+    assert n == _r(4 * 16 * 4) + _plan_bytes(2, 0, 0) + _plan_bytes(2, 0, 4)  # no partial slots (per-key bias sums: none)
     # GQA 4/2: a dK/dV unit holds at most 768 (query row, head) pairs = 12 blocks of 32
     assert f(2, 16, 16, 384, 8, 4, 2, 64, BF16, F32) == n
     big = f(2, 16, 16, 416, 8, 4, 2, 64, BF16, F32)
     slots_k = 2 * 2  # two tiles, ceil(13 / 12) = 2 chunks each
-    assert big == _r(4 * 16 * 4) + _plan_bytes(2 + slots_k, slots_k // 2) + _plan_bytes(2, 0) + \
+    assert big == _r(4 * 16 * 4) + _plan_bytes(2 + slots_k, slots_k // 2, 0) + _plan_bytes(2, 0, 4) + \
         _r(slots_k * 2 * 2 * 128 * 64 * 4) + _r(slots_k * 4 * 128 * 4)  # + per-key bias sums per slot
 
 

@@ -111,13 +111,15 @@ constexpr size_t kDqPartBudget = (size_t)64 << 20;
 
 struct PlanLayout {
   int unit_cap = 0, slot_cap = 0, split_cap = 0, chunk = 1;
+  int heads = 0;           // work items per unit, each with its own count of chunks left
   size_t plan_bytes = 0;   // header + lists
   size_t slot_bytes = 0;   // bytes of one partial slot
 };
 
 PlanLayout plan_layout(int total_t, int batch, int tile, int max_other, int step, int chunk,
-                       size_t slot_bytes, size_t budget) {
+                       size_t slot_bytes, size_t budget, int heads) {
   PlanLayout L;
+  L.heads = heads;
   const int64_t tiles = (int64_t)total_t / tile + batch;
   const int64_t max_steps = ((int64_t)max_other + step - 1) / step;
   int64_t slots = 0;
@@ -132,8 +134,9 @@ PlanLayout plan_layout(int total_t, int batch, int tile, int max_other, int step
   L.unit_cap = (int)(tiles + slots);
   L.chunk = chunk;
   L.slot_bytes = slot_bytes;
-  L.plan_bytes = round_up(256) + 2 * round_up((size_t)L.unit_cap * 16) + round_up((size_t)L.unit_cap * 4) +
-                 round_up((size_t)(L.split_cap > 0 ? L.split_cap : 1) * 16);
+  L.plan_bytes = round_up(256) + 2 * round_up((size_t)L.unit_cap * 16) + 2 * round_up((size_t)L.unit_cap * 4) +
+                 round_up((size_t)(L.split_cap > 0 ? L.split_cap : 1) * 16) +
+                 round_up((size_t)(L.split_cap > 0 ? L.split_cap : 1) * heads * 4);
   return L;
 }
 
@@ -147,8 +150,12 @@ size_t carve_plan(char* p, const PlanLayout& L, va::Plan& plan) {
   o += round_up((size_t)L.unit_cap * 16);
   plan.slots = (int*)(p + o);
   o += round_up((size_t)L.unit_cap * 4);
+  plan.sidx = (int*)(p + o);
+  o += round_up((size_t)L.unit_cap * 4);
   plan.splits = (int4*)(p + o);
   o += round_up((size_t)(L.split_cap > 0 ? L.split_cap : 1) * 16);
+  plan.left = (int*)(p + o);
+  o += round_up((size_t)(L.split_cap > 0 ? L.split_cap : 1) * L.heads * 4);
   return o;
 }
 
@@ -162,6 +169,7 @@ va::PlanArgs plan_args(const va::Plan& plan, const PlanLayout& L, const int32_t*
   a.tile = tile; a.step = step; a.kside = kside; a.causal = causal;
   a.chunk = L.chunk;
   a.unit_cap = L.unit_cap; a.slot_cap = L.slot_cap; a.split_cap = L.split_cap;
+  a.heads = L.heads;
   return a;
 }
 
@@ -169,7 +177,7 @@ va::PlanArgs plan_args(const va::Plan& plan, const PlanLayout& L, const int32_t*
 PlanLayout fwd_plan(int batch, int total_q, int max_k, int hq, int d, bool bf16, size_t budget) {
   const int bm = va::fwd_block_m(), bn = va::fwd_block_n(bf16, d);
   return plan_layout(total_q, batch, bm, max_k, bn, kChunkKeys / bn,
-                     (size_t)hq * bm * (d + 1) * sizeof(float), budget);
+                     (size_t)hq * bm * (d + 1) * sizeof(float), budget, hq);
 }
 
 size_t fwd_workspace(int batch, int total_q, int max_k, int hq, int d, bool bf16, size_t budget) {
@@ -181,14 +189,15 @@ PlanLayout dkdv_plan(int batch, int total_k, int max_q, int hkv, int n_rep, int 
   const int bnk = va::bwd_block_k(), bmq = va::bwd_dkdv_block_q();
   int chunk = kDkdvUnitRows / (bmq * n_rep);
   if (chunk < 1) chunk = 1;
+  // (its split tiles are merged by the dQ pass after the dK/dV pass: no counts)
   return plan_layout(total_k, batch, bnk, max_q, bmq, chunk,
-                     (size_t)hkv * 2 * bnk * d * sizeof(float), kDkdvPartBudget);
+                     (size_t)hkv * 2 * bnk * d * sizeof(float), kDkdvPartBudget, 0);
 }
 
 PlanLayout dq_plan(int batch, int total_q, int max_k, int hq, int d, bool bf16) {
   const int bm = va::bwd_block_q(), bn = va::bwd_dq_block_n(bf16, d);
   return plan_layout(total_q, batch, bm, max_k, bn, kChunkKeys / bn,
-                     (size_t)hq * bm * d * sizeof(float), kDqPartBudget);
+                     (size_t)hq * bm * d * sizeof(float), kDqPartBudget, hq);
 }
 
 // per-key bias-gradient sums of one dK/dV partial slot: [Hkv][n_rep][128 keys] floats

@@ -16,7 +16,8 @@
 // results never depend on scheduling.
 //
 // dQ kernel: shaped like the forward.  A unit is 128 query rows of one head
-// (or a range of key blocks of them, merged the same way); Q and dO stay in
+// (or a range of key blocks of them, whose last chunk to finish adds the
+// chunks' float32 partial sums in chunk order); Q and dO stay in
 // registers; score tiles are computed transposed (keys x queries) so each
 // lane holds one query row and dS^T feeds the dQ^T contraction straight from
 // registers.
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
   constexpr int ELT = (int)sizeof(T);
 
   __shared__ SM sm;
-  __shared__ int s_info[2][10];
+  __shared__ int s_info[2][kItemInts];
   // per-key bias gradient sums [head of the group][key of the tile] (bias kernels only)
   __shared__ float db_acc[HAS_BIAS ? dbias_max_heads<D>() * BNK : 1];
   // a bias with contiguous keys and 16-byte aligned rows comes a step ahead, with
@@ -548,7 +549,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     // dim 32dt + r32.  Whole tiles: buffer stores whose resource ends at the
     // sequence's last key (rows past it are dropped).  A chunk of a split tile
     // stores the registers as they lie (16 bytes per lane, [dt][i/4][lane][4])
-    // into its slot; the merge kernel undoes the layout.
+    // into its slot; the merge in the dQ pass undoes the layout.
     if (slot < 0) {
       const int gelt = a.grad_bf16 ? 2 : 4;
       const int krow = (int)gstride * gelt;
@@ -670,7 +671,8 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   using Sv = typename SM::Sv;
 
   __shared__ SM sm;
-  __shared__ int s_info[2][10];
+  __shared__ int s_info[2][kItemInts];
+  __shared__ int s_last;  // this chunk of a split tile finished last
 
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
   const int hh = lane >> 5, r32 = lane & 31;
@@ -696,6 +698,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     const int n0 = uniform(inf[3]), n1 = uniform(inf[4]);
     const int q0 = uniform(inf[5]), q1 = uniform(inf[6]), k0 = uniform(inf[7]), k1 = uniform(inf[8]);
     const int slot = uniform(inf[9]);  // >= 0: a chunk of a split tile
+    const int si = uniform(inf[10]);   // that split tile
     const int Lq = q1 - q0, Lk = k1 - k0, off = Lk - Lq;
     const int g = h / a.n_rep;
     const int r1 = Lq - t * BMQ_DQ;
@@ -773,75 +776,77 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
       // tile 1 are read under tile 0's MFMAs, tile 1's MFMAs run under tile 0's
       // exponentials, and the dQ MFMAs of tile 0's keys under tile 1's
       constexpr bool FAST = H16 && !HAS_BIAS && NS == 2;
-      if (FAST && wave_on && kb < wave_hi) {
-        constexpr int KS = D / 16;  // k-steps over head_dim
-        const T* kr = &sm.kn[buf][r32 * St::NP + 8 * hh];
-        const T* vr = &sm.vn[buf][r32 * St::NP + 8 * hh];
-        u32x4_t kf[2][KS], vf[2][KS];
-        f32x16_t s2[2] = {(f32x16_t){}, (f32x16_t){}}, dp2[2] = {ndsum16, ndsum16};
-        float dsv[32];
-        u32x4_t pbs[4];
-        // softmax gradient of tile st (lane = query, registers = keys), packed for dQ
-        auto grad = [&](int st) __attribute__((always_inline)) {
+      if constexpr (FAST) {
+        if (wave_on && kb < wave_hi) {
+          constexpr int KS = D / 16;  // k-steps over head_dim
+          const T* kr = &sm.kn[buf][r32 * St::NP + 8 * hh];
+          const T* vr = &sm.vn[buf][r32 * St::NP + 8 * hh];
+          u32x4_t kf[2][KS], vf[2][KS];
+          f32x16_t s2[2] = {(f32x16_t){}, (f32x16_t){}}, dp2[2] = {ndsum16, ndsum16};
+          float dsv[32];
+          u32x4_t pbs[4];
+          // softmax gradient of tile st (lane = query, registers = keys), packed for dQ
+          auto grad = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kj = kb + 32 * st + 8 * (i >> 2) + (i & 3) + 4 * hh;
-            float pv = fast_exp2(__builtin_fmaf(s2[st][i], a.scale_log2, -lse2));
-            if constexpr (MASK) pv = kj <= hi_row ? pv : 0.f;
-            dsv[16 * st + i] = pv * dp2[st][i];
+            for (int i = 0; i < 16; ++i) {
+              const int kj = kb + 32 * st + 8 * (i >> 2) + (i & 3) + 4 * hh;
+              float pv = fast_exp2(__builtin_fmaf(s2[st][i], a.scale_log2, -lse2));
+              if constexpr (MASK) pv = kj <= hi_row ? pv : 0.f;
+              dsv[16 * st + i] = pv * dp2[st][i];
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) pack8<H16>(&dsv[16 * st + 8 * c], pbs[2 * st + c], nullptr);
+          };
+          auto dq_mma = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+            for (int dt_ = 0; dt_ < DT; ++dt_)
+              acc[dt_] = mfma16<H16>(tr_frag(sm.kn[buf], St::NP, kc, 32 * dt_), pbs[kc], acc[dt_]);
+          };
+          // tile 0's fragments
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            kf[0][ks] = *(const u32x4_t*)(kr + 16 * ks);
+            vf[0][ks] = *(const u32x4_t*)(vr + 16 * ks);
           }
+          __builtin_amdgcn_sched_barrier(0);
+          // tile 0's S^T and dP^T - D, tile 1's fragments read under them
 #pragma unroll
-          for (int c = 0; c < 2; ++c) pack8<H16>(&dsv[16 * st + 8 * c], pbs[2 * st + c], nullptr);
-        };
-        auto dq_mma = [&](int kc) __attribute__((always_inline)) {
+          for (int ks = 0; ks < KS; ++ks) {
+            s2[0] = mfma16<H16>(kf[0][ks], qf.b[ks], s2[0]);
+            kf[1][ks] = *(const u32x4_t*)(kr + 32 * St::NP + 16 * ks);
+            dp2[0] = mfma16<H16>(vf[0][ks], of.b[ks], dp2[0]);
+            vf[1][ks] = *(const u32x4_t*)(vr + 32 * St::NP + 16 * ks);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // tile 1's MFMAs, each with a share of tile 0's vector work
 #pragma unroll
-          for (int dt_ = 0; dt_ < DT; ++dt_)
-            acc[dt_] = mfma16<H16>(tr_frag(sm.kn[buf], St::NP, kc, 32 * dt_), pbs[kc], acc[dt_]);
-        };
-        // tile 0's fragments
+          for (int ks = 0; ks < KS; ++ks) {
+            s2[1] = mfma16<H16>(kf[1][ks], qf.b[ks], s2[1]);
+            dp2[1] = mfma16<H16>(vf[1][ks], of.b[ks], dp2[1]);
+          }
+          grad(0);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          kf[0][ks] = *(const u32x4_t*)(kr + 16 * ks);
-          vf[0][ks] = *(const u32x4_t*)(vr + 16 * ks);
+          for (int i = 0; i < 2 * KS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);  // exponentials
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // other vector work
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          // tile 0's dQ MFMAs under tile 1's vector work
+          dq_mma(0);
+          dq_mma(1);
+          grad(1);
+#pragma unroll
+          for (int i = 0; i < 2 * DT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // transposing reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);  // exponentials
+            __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // other vector work
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          dq_mma(2);
+          dq_mma(3);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // tile 0's S^T and dP^T - D, tile 1's fragments read under them
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s2[0] = mfma16<H16>(kf[0][ks], qf.b[ks], s2[0]);
-          kf[1][ks] = *(const u32x4_t*)(kr + 32 * St::NP + 16 * ks);
-          dp2[0] = mfma16<H16>(vf[0][ks], of.b[ks], dp2[0]);
-          vf[1][ks] = *(const u32x4_t*)(vr + 32 * St::NP + 16 * ks);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // tile 1's MFMAs, each with a share of tile 0's vector work
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s2[1] = mfma16<H16>(kf[1][ks], qf.b[ks], s2[1]);
-          dp2[1] = mfma16<H16>(vf[1][ks], of.b[ks], dp2[1]);
-        }
-        grad(0);
-#pragma unroll
-        for (int i = 0; i < 2 * KS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x400, 2, 0);  // exponentials
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // other vector work
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // tile 0's dQ MFMAs under tile 1's vector work
-        dq_mma(0);
-        dq_mma(1);
-        grad(1);
-#pragma unroll
-        for (int i = 0; i < 2 * DT; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // transposing reads
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);  // exponentials
-          __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // other vector work
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        dq_mma(2);
-        dq_mma(3);
       } else if (wave_on && kb < wave_hi) {
         float dsv[16 * NS];
 #pragma unroll
@@ -947,7 +952,10 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
     ++kth;
 
-    if (slot < 0) {
+    // dQ = scale * acc.  A chunk of a split tile stores acc in float32 to its
+    // slot instead, and the chunk that finishes last sums the tile's chunks in
+    // chunk order, its own from registers (the same values it stored).
+    auto write_dq = [&]() __attribute__((always_inline)) {
       // rows < 0 fall outside the resource: their stores are dropped
       const int dq_row_bytes = (int)dostride * gelt;
       const rsrc_t dqres = make_rsrc((uint8_t*)a.dq + qoff * gelt,
@@ -966,17 +974,63 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
                                   __float_as_uint(o3)}, dqres, rq * dq_row_bytes + d0 * 4);
           }
         }
+    };
+    if (slot < 0) {
+      write_dq();
     } else {
+      constexpr int SLOT_Q = BMQ_DQ * D;  // floats of one (slot, head) block
       const int rl = rq - (r1 - BMQ_DQ);  // 0 .. BMQ_DQ-1
-      float* pq = a.part_q + ((size_t)slot * a.hq + h) * BMQ_DQ * D + (size_t)rl * D;
+      const rsrc_t pres = make_rsrc(a.part_q + ((size_t)slot * a.hq + h) * SLOT_Q, (int64_t)SLOT_Q * 4);
 #pragma unroll
       for (int dt_ = 0; dt_ < DT; ++dt_)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          const int d0 = 32 * dt_ + 8 * a4 + 4 * hh;
-          *(f32x4_t*)(pq + d0) = (f32x4_t){acc[dt_][4 * a4], acc[dt_][4 * a4 + 1], acc[dt_][4 * a4 + 2],
-                                           acc[dt_][4 * a4 + 3]};
+          const f32x4_t o = {acc[dt_][4 * a4], acc[dt_][4 * a4 + 1], acc[dt_][4 * a4 + 2], acc[dt_][4 * a4 + 3]};
+          buf_store16_dev(as_u32x4(o), pres, (rl * D + 32 * dt_ + 8 * a4 + 4 * hh) * 4);
         }
+      if (split_done_last(&a.plan_q.left[si * a.hq + h], &s_last)) {
+        const int4 sp = a.plan_q.splits[si];
+        const int sb = uniform(sp.z), nch = uniform(sp.w), me = slot - sb;  // first slot, chunks, this chunk
+        constexpr int G = DT < 2 ? DT : 2;  // output tiles summed per pass (bounds the registers)
+#pragma unroll
+        for (int g0 = 0; g0 < DT; g0 += G) {
+          f32x4_t sum[G][4];
+#pragma unroll
+          for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) sum[j][a4] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+          for (int c = 0; c < nch; ++c) {
+            f32x4_t oc[G][4];
+            if (c == me) {
+#pragma unroll
+              for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4)
+                  oc[j][a4] = (f32x4_t){acc[g0 + j][4 * a4], acc[g0 + j][4 * a4 + 1], acc[g0 + j][4 * a4 + 2],
+                                        acc[g0 + j][4 * a4 + 3]};
+            } else {
+              const rsrc_t cres =
+                  make_rsrc(a.part_q + ((size_t)(sb + c) * a.hq + h) * SLOT_Q, (int64_t)SLOT_Q * 4);
+#pragma unroll
+              for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4)
+                  oc[j][a4] = buf_load16_dev(cres, (rl * D + 32 * (g0 + j) + 8 * a4 + 4 * hh) * 4);
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+              for (int a4 = 0; a4 < 4; ++a4) sum[j][a4] += oc[j][a4];
+          }
+#pragma unroll
+          for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[g0 + j][4 * a4 + e] = sum[j][a4][e];
+        }
+        write_dq();
+      }
     }
     __syncthreads();
   }
@@ -988,60 +1042,6 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     if (m >= merge_items) break;
     dkdv_merge_item<D>(a, m);
   }
-}
-
-// Sums the chunks of split dQ tiles in chunk order (deterministic).  A work
-// item is 32 rows of one (split tile, head); eight threads per row.
-constexpr int kMergeRows = 32;
-
-constexpr int kMergeSlabs = BMQ_DQ / kMergeRows;
-
-template <int D>
-__device__ __forceinline__ void dq_merge_item(const BwdArgs& a, int it) {
-  constexpr int SLABS = kMergeSlabs;
-  constexpr int TPR = NT / kMergeRows;
-  constexpr int SEG = D / TPR;
-  const int rs = threadIdx.x / TPR, seg = threadIdx.x % TPR;
-  {
-    const int slab = it % SLABS, sh = it / SLABS;
-    const int si = sh / a.hq, h = sh - si * a.hq;
-    const int4 sp = a.plan_q.splits[si];
-    const int b = uniform(sp.x), t = uniform(sp.y), sb = uniform(sp.z), nch = uniform(sp.w);
-    int q0, q1;
-    seq_bounds(a.cu_q, b, a.total_q, q0, q1);
-    const int row = slab * kMergeRows + rs;
-    const int rq = (q1 - q0) - (t + 1) * BMQ_DQ + row;
-    if (rq < 0) return;
-    f32x4_t acc[SEG / 4];
-#pragma unroll
-    for (int e = 0; e < SEG / 4; ++e) acc[e] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int c = 0; c < nch; ++c) {
-      const f32x4_t* src =
-          (const f32x4_t*)(a.part_q + (((size_t)(sb + c) * a.hq + h) * BMQ_DQ + row) * D + seg * SEG);
-#pragma unroll
-      for (int e = 0; e < SEG / 4; ++e) acc[e] += src[e];
-    }
-    const size_t o = ((size_t)(q0 + rq) * a.hq + h) * D + seg * SEG;
-#pragma unroll
-    for (int e = 0; e < SEG / 4; ++e) {
-      const f32x4_t x = acc[e] * a.scale;
-      if (a.grad_bf16)
-        ((u32x2_t*)((uint16_t*)a.dq + o))[e] = (u32x2_t){pack16_rt(x[0], x[1], a.grad_bf16),
-                                                        pack16_rt(x[2], x[3], a.grad_bf16)};
-      else
-        ((f32x4_t*)((float*)a.dq + o))[e] = x;
-    }
-  }
-}
-
-// The dQ merge after the dQ pass: items of 32 rows of a (split query tile,
-// head), each summing its chunks in chunk order.  (Split dK/dV tiles are
-// merged inside the dQ pass, after its own items.)
-template <int D>
-__global__ __launch_bounds__(NT) void bwd_merge_kernel(BwdArgs a) {
-  const int total = uniform(a.plan_q.hdr[2]) * a.hq * kMergeSlabs;
-  for (int it = blockIdx.x; it < total; it += gridDim.x) dq_merge_item<D>(a, it);
 }
 
 template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
@@ -1080,16 +1080,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
     timing_after(st);
     e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
-  if (a.split_cap_q > 0) {  // the split dQ tiles' partial sums
-    int64_t g = (int64_t)a.split_cap_q * a.hq * kMergeSlabs;
-    if (g > 4096) g = 4096;
-    timing_before(st, "bwd_merge");
-    hipLaunchKernelGGL(bwd_merge_kernel<D>, dim3((unsigned)g), dim3(NT), 0, st, a);
-    timing_after(st);
-  }
-  return hipGetLastError();
+  return e;
 }
 
 template <int H16, int D>

@@ -187,6 +187,46 @@ __device__ __forceinline__ u32x4_t tr_frag(const uint16_t* tile, int pitch, int 
   return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Partial results of split tiles are written by one workgroup and merged by
+// another, possibly on another XCD (each XCD has its own L2).  They are
+// written and read with device-coherent accesses (cache policy sc1, as for
+// agent-scope atomics: past the per-CU cache, coherent across the L2s), so
+// handing them over needs no writeback or invalidation of whole caches.
+constexpr int kDevCoherent = 16;  // buffer cache-policy bit sc1
+__device__ __forceinline__ void buf_store16_dev(u32x4_t v, rsrc_t r, int byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, kDevCoherent);
+}
+__device__ __forceinline__ f32x4_t buf_load16_dev(rsrc_t r, int byte_off) {
+  const u32x4_t u = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kDevCoherent);
+  return (f32x4_t){__uint_as_float(u[0]), __uint_as_float(u[1]), __uint_as_float(u[2]), __uint_as_float(u[3])};
+}
+__device__ __forceinline__ u32x4_t as_u32x4(f32x4_t v) {
+  return (u32x4_t){__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+}
+__device__ __forceinline__ void st_dev(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by a whole workgroup when a chunk of a split tile has stored its
+// partial results (device-coherent); `left` counts the tile's chunks still
+// running (the planner sets it to the chunk count).  True, in every thread,
+// for the chunk that finishes last, which then merges the tile's chunks in
+// chunk order, so the result does not depend on which chunk that
+// is.  Every thread waits for its stores to complete before the count goes
+// down, so the last chunk, which reads (device-coherent) after it, sees them
+// all.  Nothing waits on another workgroup.
+__device__ __forceinline__ bool split_done_last(int* left, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_flag = __hip_atomic_fetch_add(left, -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1;
+  __syncthreads();
+  return *s_flag != 0;
+}
+
 // ---------------------------------------------------------------------------
 // Work assignment.  A planner kernel writes, per pass, the list of work units
 // sorted by cost (heaviest first); the pass's persistent workgroups then take
@@ -204,8 +244,10 @@ __device__ __forceinline__ int snake_item(int k, int w, int g) { return k * g + 
 // the next item while the current item computes and publishes them in LDS
 // (double-buffered by item parity) before the current item's output stores,
 // so an item starts without a dependent chain of global loads.
+constexpr int kItemInts = 11;
 struct ItemInfo {
-  int v[10];  // item, sequence, tile, first step, end step, tiled start/end, other start/end, slot
+  int v[kItemInts];  // item, sequence, tile, first step, end step, tiled start/end, other start/end,
+                     // slot, split index
 };
 template <typename PlanT>
 __device__ __forceinline__ ItemInfo item_load(const PlanT& pl, int item, int per_unit, int total_items) {
@@ -217,12 +259,13 @@ __device__ __forceinline__ ItemInfo item_load(const PlanT& pl, int item, int per
     r.v[1] = un.x; r.v[2] = un.y; r.v[3] = un.z; r.v[4] = un.w;
     r.v[5] = bd.x; r.v[6] = bd.y; r.v[7] = bd.z; r.v[8] = bd.w;
     r.v[9] = pl.slots[unit];
+    r.v[10] = pl.sidx[unit];
   }
   return r;
 }
 __device__ __forceinline__ void item_store(int* dst, const ItemInfo& r) {
 #pragma unroll
-  for (int i = 0; i < 10; ++i) dst[i] = r.v[i];
+  for (int i = 0; i < kItemInts; ++i) dst[i] = r.v[i];
 }
 
 }  // namespace va

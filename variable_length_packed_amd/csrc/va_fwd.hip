@@ -127,7 +127,8 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
   constexpr int WR = 32 * QT;                 // rows per wave
 
   __shared__ S sm;
-  __shared__ int s_info[2][10];
+  __shared__ int s_info[2][kItemInts];
+  __shared__ int s_last;  // this chunk of a split tile finished last
   // 16-bit bias with contiguous keys: the [BM rows][BN keys] tile of a block, loaded
   // a block ahead straight into LDS (double-buffered).  Row r keeps its 16-byte
   // piece c (keys 8c .. 8c+7) in slot c ^ (r % 8), so the 32 rows a wave reads at
@@ -170,6 +171,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     const int n0 = uniform(inf[3]), n1 = uniform(inf[4]);
     const int q0 = uniform(inf[5]), q1 = uniform(inf[6]), k0 = uniform(inf[7]), k1 = uniform(inf[8]);
     const int slot = uniform(inf[9]);  // >= 0: a chunk of a split tile
+    const int si = uniform(inf[10]);   // that split tile
     const int Lq = q1 - q0, Lk = k1 - k0;
     const int off = Lk - Lq;
     const int g = h / a.n_rep;
@@ -700,104 +702,121 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
     ++kth;
 
-    // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2; a chunk of a split
-    // tile stores O and the base-2 LSE in float32 to its slot instead
+    // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.  A chunk of a split
+    // tile stores O and the base-2 LSE in float32 to its slot instead, and the
+    // chunk that finishes last merges the tile's chunks in chunk order, per row
+    // LSE = log2 sum_c 2^LSE_c and O = sum_c 2^(LSE_c - LSE) O_c, taking its
+    // own O and LSE from registers (the same values it stored), so the result
+    // does not depend on which chunk that is.
     const int row_base = r1 - BM;  // tile row 0
+    float inv_v[QT], lse_v[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       const float l_tot = l_run[qt] + xor32(l_run[qt]);
-      const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      const float lse2 = l_tot > 0.f ? m_run[qt] + __builtin_log2f(l_tot) : -INFINITY;
-      if (slot < 0) {
+      inv_v[qt] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      lse_v[qt] = l_tot > 0.f ? m_run[qt] + __builtin_log2f(l_tot) : -INFINITY;
+    }
+    // O = acc * inv_l and the LSE of the rows >= 0
+    auto write_out = [&](int qt, float inv_l, float lse2) __attribute__((always_inline)) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int a4 = 0; a4 < 4; ++a4) {
-            const int d0 = 32 * dt + 8 * a4 + 4 * hh;
-            const float o0 = acc[qt][dt][4 * a4 + 0] * inv_l, o1 = acc[qt][dt][4 * a4 + 1] * inv_l;
-            const float o2 = acc[qt][dt][4 * a4 + 2] * inv_l, o3 = acc[qt][dt][4 * a4 + 3] * inv_l;
-            // rows < 0 fall outside the resource: the store is dropped
-            if constexpr (H16) {
-              buf_store8((u32x2_t){pack16<H16>(o0, o1), pack16<H16>(o2, o3)}, ores, rq[qt] * orow_bytes + d0 * 2);
-            } else {
-              buf_store16((u32x4_t){__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2),
-                                    __float_as_uint(o3)}, ores, rq[qt] * orow_bytes + d0 * 4);
-            }
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int d0 = 32 * dt + 8 * a4 + 4 * hh;
+          const float o0 = acc[qt][dt][4 * a4 + 0] * inv_l, o1 = acc[qt][dt][4 * a4 + 1] * inv_l;
+          const float o2 = acc[qt][dt][4 * a4 + 2] * inv_l, o3 = acc[qt][dt][4 * a4 + 3] * inv_l;
+          // rows < 0 fall outside the resource: the store is dropped
+          if constexpr (H16) {
+            buf_store8((u32x2_t){pack16<H16>(o0, o1), pack16<H16>(o2, o3)}, ores, rq[qt] * orow_bytes + d0 * 2);
+          } else {
+            buf_store16((u32x4_t){__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2),
+                                  __float_as_uint(o3)}, ores, rq[qt] * orow_bytes + d0 * 4);
           }
-        if (rq[qt] >= 0 && hh == 0) a.lse[(size_t)h * a.total_q + q0 + rq[qt]] = lse2 * kLn2;
-      } else {
+        }
+      if (rq[qt] >= 0 && hh == 0) a.lse[(size_t)h * a.total_q + q0 + rq[qt]] = lse2 * kLn2;
+    };
+    if (slot < 0) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) write_out(qt, inv_v[qt], lse_v[qt]);
+    } else {
+      constexpr int SLOT_O = BM * D;  // floats of one (slot, head) block of O
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
         const int rl = rq[qt] - row_base;  // 0 .. BM-1
-        float* po = a.part_o + ((size_t)slot * a.hq + h) * BM * D + (size_t)rl * D;
+        const rsrc_t pres = make_rsrc(a.part_o + ((size_t)slot * a.hq + h) * SLOT_O, (int64_t)SLOT_O * 4);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int a4 = 0; a4 < 4; ++a4) {
-            const int d0 = 32 * dt + 8 * a4 + 4 * hh;
-            *(f32x4_t*)(po + d0) = (f32x4_t){acc[qt][dt][4 * a4 + 0] * inv_l, acc[qt][dt][4 * a4 + 1] * inv_l,
-                                             acc[qt][dt][4 * a4 + 2] * inv_l, acc[qt][dt][4 * a4 + 3] * inv_l};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[qt][dt][4 * a4 + e] *= inv_v[qt];
+            const f32x4_t o = {acc[qt][dt][4 * a4], acc[qt][dt][4 * a4 + 1], acc[qt][dt][4 * a4 + 2],
+                               acc[qt][dt][4 * a4 + 3]};
+            buf_store16_dev(as_u32x4(o), pres, (rl * D + 32 * dt + 8 * a4 + 4 * hh) * 4);
           }
-        if (hh == 0) a.part_lse[((size_t)slot * a.hq + h) * BM + rl] = lse2;
+        if (hh == 0) st_dev(&a.part_lse[((size_t)slot * a.hq + h) * BM + rl], lse_v[qt]);
+      }
+      if (split_done_last(&a.plan.left[si * a.hq + h], &s_last)) {
+        const int4 sp = a.plan.splits[si];
+        const int sb = uniform(sp.z), nch = uniform(sp.w), me = slot - sb;  // first slot, chunks, this chunk
+        constexpr int G = DT < 2 ? DT : 2;  // output tiles merged per pass (bounds the registers)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+          const int rl = rq[qt] - row_base;
+          const float* pl = a.part_lse + ((size_t)sb * a.hq + h) * BM + rl;  // chunk c: + c * hq * BM
+          float mx = lse_v[qt];
+          for (int c = 0; c < nch; ++c)
+            if (c != me) mx = fmaxf(mx, ld_dev(pl + (size_t)c * a.hq * BM));
+          float wsum = 0.f;
+#pragma unroll
+          for (int g0 = 0; g0 < DT; g0 += G) {
+            f32x4_t mo[G][4];
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+              for (int a4 = 0; a4 < 4; ++a4) mo[j][a4] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            for (int c = 0; c < nch; ++c) {
+              f32x4_t oc[G][4];
+              float lc;
+              if (c == me) {
+                lc = lse_v[qt];
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+#pragma unroll
+                  for (int a4 = 0; a4 < 4; ++a4)
+                    oc[j][a4] = (f32x4_t){acc[qt][g0 + j][4 * a4], acc[qt][g0 + j][4 * a4 + 1],
+                                          acc[qt][g0 + j][4 * a4 + 2], acc[qt][g0 + j][4 * a4 + 3]};
+              } else {
+                lc = ld_dev(pl + (size_t)c * a.hq * BM);
+                const rsrc_t cres =
+                    make_rsrc(a.part_o + ((size_t)(sb + c) * a.hq + h) * SLOT_O, (int64_t)SLOT_O * 4);
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+#pragma unroll
+                  for (int a4 = 0; a4 < 4; ++a4)
+                    oc[j][a4] = buf_load16_dev(cres, (rl * D + 32 * (g0 + j) + 8 * a4 + 4 * hh) * 4);
+              }
+              const float w = mx == -INFINITY ? 0.f : fast_exp2(lc - mx);
+              if (g0 == 0) wsum += w;
+#pragma unroll
+              for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) mo[j][a4] += w * oc[j][a4];
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+              for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[qt][g0 + j][4 * a4 + e] = mo[j][a4][e];
+          }
+          inv_v[qt] = wsum > 0.f ? 1.f / wsum : 0.f;
+          lse_v[qt] = wsum > 0.f ? mx + __builtin_log2f(wsum) : -INFINITY;
+          write_out(qt, inv_v[qt], lse_v[qt]);
+        }
       }
     }
     __syncthreads();
-  }
-}
-
-// Merges the chunks of split tiles: per query row, LSE = log2 sum_c 2^LSE_c
-// and O = sum_c 2^(LSE_c - LSE) O_c, summed in chunk order (deterministic).
-// A work item is 32 rows of one (split tile, head); eight threads per row.
-constexpr int kMergeRows = 32;
-
-template <int H16, int D>
-__global__ __launch_bounds__(NT) void fwd_merge_kernel(FwdArgs a) {
-  using T = typename std::conditional<(H16 != 0), uint16_t, float>::type;
-  constexpr int BM = block_m<H16, D>();
-  constexpr int SLABS = BM / kMergeRows;
-  constexpr int TPR = NT / kMergeRows;  // threads per row
-  constexpr int SEG = D / TPR;          // dims per thread
-  const int total = uniform(a.plan.hdr[2]) * a.hq * SLABS;
-  const int rs = threadIdx.x / TPR, seg = threadIdx.x % TPR;
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
-    const int slab = it % SLABS, sh = it / SLABS;
-    const int si = sh / a.hq, h = sh - si * a.hq;
-    const int4 sp = a.plan.splits[si];
-    const int b = uniform(sp.x), t = uniform(sp.y), sb = uniform(sp.z), nch = uniform(sp.w);
-    int q0, q1;
-    seq_bounds(a.cu_q, b, a.total_q, q0, q1);
-    const int row = slab * kMergeRows + rs;         // row inside the tile
-    const int rq = (q1 - q0) - (t + 1) * BM + row;  // row inside the sequence
-    if (rq < 0) continue;
-    const size_t pi0 = (size_t)sb * a.hq + h;       // slot of chunk c: pi0 + c * hq
-    float mx = -INFINITY;
-#pragma unroll 4
-    for (int c = 0; c < nch; ++c) mx = fmaxf(mx, a.part_lse[(pi0 + (size_t)c * a.hq) * BM + row]);
-    f32x4_t acc[SEG / 4];
-#pragma unroll
-    for (int e = 0; e < SEG / 4; ++e) acc[e] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    if (mx != -INFINITY) {
-#pragma unroll 4
-      for (int c = 0; c < nch; ++c) {
-        const size_t pi = pi0 + (size_t)c * a.hq;
-        const float w = fast_exp2(a.part_lse[pi * BM + row] - mx);
-        wsum += w;
-        const f32x4_t* src = (const f32x4_t*)(a.part_o + (pi * BM + row) * D + seg * SEG);
-#pragma unroll
-        for (int e = 0; e < SEG / 4; ++e) acc[e] += w * src[e];
-      }
-    }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    T* dst = (T*)a.out + ((size_t)(q0 + rq) * a.hq + h) * D + seg * SEG;
-#pragma unroll
-    for (int e = 0; e < SEG / 4; ++e) {
-      const f32x4_t x = acc[e] * inv;
-      if constexpr (H16)
-        *(u32x2_t*)(dst + 4 * e) = (u32x2_t){pack16<H16>(x[0], x[1]), pack16<H16>(x[2], x[3])};
-      else
-        *(f32x4_t*)(dst + 4 * e) = x;
-    }
-    if (seg == 0)
-      a.lse[(size_t)h * a.total_q + q0 + rq] = wsum > 0.f ? (mx + __builtin_log2f(wsum)) * kLn2 : -INFINITY;
   }
 }
 
@@ -816,13 +835,6 @@ static hipError_t launch_fwd_t(const FwdArgs& a, int64_t items, hipStream_t st) 
   if (grid <= 0) return hipErrorInvalidConfiguration;
   timing_before(st, H16 == 2 ? "fwd_f16" : H16 ? "fwd_bf16" : "fwd_f32");
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, a);
-  timing_after(st);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.split_cap <= 0) return e;
-  int64_t mg = (int64_t)a.split_cap * a.hq * (block_m<H16, D>() / kMergeRows);
-  if (mg > 4096) mg = 4096;
-  timing_before(st, "fwd_merge");
-  hipLaunchKernelGGL((fwd_merge_kernel<H16, D>), dim3((unsigned)mg), dim3(NT), 0, st, a);
   timing_after(st);
   return hipGetLastError();
 }

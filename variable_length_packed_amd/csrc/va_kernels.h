@@ -29,8 +29,8 @@ void set_error(const char* msg);
 // forward and dQ, key rows for dK/dV) and walks the other side in steps (key
 // blocks, or query blocks).  A tile with more steps than `chunk` is split
 // into nch = ceil(steps / chunk) units of near-equal step ranges; each unit
-// of a split tile writes float32 partial results to its own slot and a merge
-// kernel combines the nch slots in chunk order.  The split rule depends only
+// of a split tile writes float32 partial results to its own slot, and the
+// unit that finishes last combines the nch slots in chunk order.  The split rule depends only
 // on the tile's own sequence, so a sequence's results never depend on the
 // rest of the batch.  Units are listed by step count, largest first.
 // ---------------------------------------------------------------------------
@@ -39,7 +39,10 @@ struct Plan {
   int4* units;     // [unit_cap] {sequence, tile, first step, end step}
   int4* bounds;    // [unit_cap] the sequence's rows: {tiled start, end, other start, end}
   int* slots;      // [unit_cap] partial slot of a chunk of a split tile, or -1
+  int* sidx;       // [unit_cap] index of that split tile in `splits`, or -1
   int4* splits;    // [split_cap] {sequence, tile, first slot, chunks}
+  int* left;       // [split_cap][heads] chunks of the split tile still to finish, per item
+                   // head (set by the planner)
 };
 
 struct PlanArgs {
@@ -54,6 +57,7 @@ struct PlanArgs {
   int32_t causal;
   int32_t chunk;   // most steps per unit
   int32_t unit_cap, slot_cap, split_cap;
+  int32_t heads;   // work items (heads) per unit, each counting its chunks in `left`
 };
 
 struct PlanSet {

@@ -246,7 +246,10 @@ __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
     if (nch > 1) {
       sp = atomicAdd(&sh.split_ctr, 1);
       sb = atomicAdd(&sh.slot_ctr, nch);
-      if (sp < p.split_cap) p.plan.splits[sp] = make_int4(b, t, sb, nch);
+      if (sp < p.split_cap) {
+        p.plan.splits[sp] = make_int4(b, t, sb, nch);
+        for (int h = 0; h < p.heads; ++h) p.plan.left[sp * p.heads + h] = nch;
+      }
     }
     const int q = s / nch, r = s - q * nch;
     int pos_hi = r > 0 ? atomicAdd(&sh.bins[min(q + 1, NBIN - 1)], r) : 0;
@@ -259,6 +262,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
         p.plan.units[pos] = make_int4(b, t, n0, n1);
         p.plan.bounds[pos] = bd;
         p.plan.slots[pos] = nch > 1 ? sb + c : -1;
+        p.plan.sidx[pos] = sp;
       }
     }
   });
