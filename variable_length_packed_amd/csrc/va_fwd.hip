@@ -705,9 +705,9 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.  A chunk of a split
     // tile stores O and the base-2 LSE in float32 to its slot instead, and the
     // chunk that finishes last merges the tile's chunks in chunk order, per row
-    // LSE = log2 sum_c 2^LSE_c and O = sum_c 2^(LSE_c - LSE) O_c, taking its
-    // own O and LSE from registers (the same values it stored), so the result
-    // does not depend on which chunk that is.
+    // LSE = log2 sum_c 2^LSE_c and O = sum_c 2^(LSE_c - LSE) O_c (accumulated
+    // with a running max), taking its own O and LSE from registers (the same
+    // values it stored), so the result does not depend on which chunk that is.
     const int row_base = r1 - BM;  // tile row 0
     float inv_v[QT], lse_v[QT];
 #pragma unroll
@@ -759,15 +759,15 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       if (split_done_last(&a.plan.left[si * a.hq + h], &s_last)) {
         const int4 sp = a.plan.splits[si];
         const int sb = uniform(sp.z), nch = uniform(sp.w), me = slot - sb;  // first slot, chunks, this chunk
-        constexpr int G = DT < 2 ? DT : 2;  // output tiles merged per pass (bounds the registers)
+        // chunks in order with a running max (each chunk's LSE and O are loaded
+        // together, so a chunk costs one round trip); at head dim 256 the output
+        // tiles go two at a time to bound the registers
+        constexpr int G = D <= 128 ? DT : 2;
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
           const int rl = rq[qt] - row_base;
           const float* pl = a.part_lse + ((size_t)sb * a.hq + h) * BM + rl;  // chunk c: + c * hq * BM
-          float mx = lse_v[qt];
-          for (int c = 0; c < nch; ++c)
-            if (c != me) mx = fmaxf(mx, ld_dev(pl + (size_t)c * a.hq * BM));
-          float wsum = 0.f;
+          float mx = -INFINITY, wsum = 0.f;
 #pragma unroll
           for (int g0 = 0; g0 < DT; g0 += G) {
             f32x4_t mo[G][4];
@@ -775,6 +775,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
             for (int j = 0; j < G; ++j)
 #pragma unroll
               for (int a4 = 0; a4 < 4; ++a4) mo[j][a4] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            float m_run_c = -INFINITY, w_run = 0.f;
             for (int c = 0; c < nch; ++c) {
               f32x4_t oc[G][4];
               float lc;
@@ -796,12 +797,15 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
                   for (int a4 = 0; a4 < 4; ++a4)
                     oc[j][a4] = buf_load16_dev(cres, (rl * D + 32 * (g0 + j) + 8 * a4 + 4 * hh) * 4);
               }
-              const float w = mx == -INFINITY ? 0.f : fast_exp2(lc - mx);
-              if (g0 == 0) wsum += w;
+              const float m_new = fmaxf(m_run_c, lc);
+              const float a_old = m_run_c == -INFINITY ? 0.f : fast_exp2(m_run_c - m_new);
+              const float a_c = lc == -INFINITY ? 0.f : fast_exp2(lc - m_new);
+              w_run = w_run * a_old + a_c;
 #pragma unroll
               for (int j = 0; j < G; ++j)
 #pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) mo[j][a4] += w * oc[j][a4];
+                for (int a4 = 0; a4 < 4; ++a4) mo[j][a4] = mo[j][a4] * a_old + a_c * oc[j][a4];
+              m_run_c = m_new;
             }
 #pragma unroll
             for (int j = 0; j < G; ++j)
@@ -809,6 +813,8 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
               for (int a4 = 0; a4 < 4; ++a4)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[qt][g0 + j][4 * a4 + e] = mo[j][a4][e];
+            mx = m_run_c;
+            wsum = w_run;
           }
           inv_v[qt] = wsum > 0.f ? 1.f / wsum : 0.f;
           lse_v[qt] = wsum > 0.f ? mx + __builtin_log2f(wsum) : -INFINITY;
