@@ -519,13 +519,31 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     // matrix unit and the vector unit of the SIMD both have work that waits
     // on neither.  The row sums add the bf16-rounded P that the PV MFMAs use.
     constexpr int NCH = 2 * NS;  // 16-key chunks per block
-    auto step_fast = [&](int n, f32x16_t (&sc)[QT][NS], f32x16_t (&sn)[QT][NS]) __attribute__((always_inline)) {
+    // MASK: a block on the diagonal (or past a row's last key): the scores of
+    // invisible keys become -inf before the row max, and a wave none of whose
+    // rows sees the block skips the arithmetic (its later blocks are invisible
+    // too, so the S it would compute is never used).
+    auto step_fast = [&](auto mask_tag, int n, f32x16_t (&sc)[QT][NS], f32x16_t (&sn)[QT][NS])
+                         __attribute__((always_inline)) {
       if constexpr (QT == 1 && H16 && !HAS_BIAS && QF % NCH == 0) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       constexpr int KPR = QF / NCH;  // S k-steps per round
       const int kb = kb0 + n * BN;
       const int kbuf = (n + 1) & 1, vbuf = n & 1;
       ld.load_k(kres, krow_bytes, kb + 2 * BN);  // past the last block every row reads as zero
       ld.load_v(vres, vrow_bytes, kb + BN);
+      if (!MASK || (wave_on && kb < wave_hi)) {
+      if constexpr (MASK) {
+        const int lo_rel = -kb - 4 * hh;                         // c_i >= lo_rel  <=>  key >= 0
+        const unsigned span = (unsigned)max(hi_row[0] + 1, 0);  // key <= hi_row
+#pragma unroll
+        for (int st = 0; st < NS; ++st)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ci = 32 * st + 8 * (i >> 2) + (i & 3);
+            sc[0][st][i] = ((unsigned)(ci - lo_rel) < span) ? sc[0][st][i] : -INFINITY;
+          }
+      }
       u32x4_t kfr[KFN];
       read_k(kbuf, kfr);
       u32x4_t vf[NCH][DT];
@@ -595,6 +613,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       }
       __builtin_amdgcn_sched_barrier(0);
       l_run[0] += ps0 + ps1;
+      }
       ld.store_k(sm, n & 1);
       ld.store_v(sm, (n + 1) & 1);
       __syncthreads();
@@ -685,20 +704,30 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     int j = 0;
     if constexpr (H16 && !HAS_BIAS && QT == 1 && QF % NCH == 0) {
       f32x16_t s_alt[QT][NS];
+      const std::integral_constant<bool, false> plain;
+      const std::integral_constant<bool, true> masked;
       for (; j + 1 < j_plain; j += 2) {
-        step_fast(j, s_cur, s_alt);
-        step_fast(j + 1, s_alt, s_cur);
+        step_fast(plain, j, s_cur, s_alt);
+        step_fast(plain, j + 1, s_alt, s_cur);
       }
       if (j < j_plain) {
-        step_fast(j, s_cur, s_alt);
+        step_fast(plain, j, s_cur, s_alt);
 #pragma unroll
         for (int st = 0; st < NS; ++st) s_cur[0][st] = s_alt[0][st];
         ++j;
       }
+      for (; j + 1 < nb; j += 2) {
+        step_fast(masked, j, s_cur, s_alt);
+        step_fast(masked, j + 1, s_alt, s_cur);
+      }
+      if (j < nb) {
+        step_fast(masked, j, s_cur, s_alt);
+        ++j;
+      }
     } else {
       for (; j < j_plain; ++j) step(std::integral_constant<bool, false>(), j);
+      for (; j < nb; ++j) step(std::integral_constant<bool, true>(), j);
     }
-    for (; j < nb; ++j) step(std::integral_constant<bool, true>(), j);
     if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
     ++kth;
 
