@@ -22,8 +22,9 @@
 // lane holds one query row and dS^T feeds the dQ^T contraction straight from
 // registers.
 //
-// Both take their units from the planner's list, heaviest first, in the fixed
-// snake order of snake_item() (no atomics).
+// Both take their units from the planner's list, heaviest first: workgroup w
+// starts with item w and takes each later item from the list's cursor near
+// the end of its current one (NextItem).
 //
 // No mask is needed for a key past the sequence (its K and V read as zero and
 // its dK/dV row is never stored; in dQ its zero K row adds nothing) or for a
@@ -514,20 +515,24 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     // wait only for their own prefetches
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    ItemInfo nxt;
-    if (tid == 0) nxt = item_load(a.plan_k, snake_item(kth + 1, blockIdx.x, gridDim.x), per_unit, total_items);
+    // the next item: a ticket taken at the start of this item's second-to-last
+    // step, its plan entries loaded during the last (thread 0)
+    NextItem<Plan> next_item{a.plan_k, per_unit, total_items};
     int k = 0;
     for (; k < k_masked; ++k) {
       const int2 nx = next_of(k + 1, rn);
+      next_item.at(k, k_total);
       step(std::integral_constant<bool, true>(), k, rn, nx);
       rn = nx;
     }
     for (; k < k_total; ++k) {
       const int2 nx = next_of(k + 1, rn);
+      next_item.at(k, k_total);
       step(std::integral_constant<bool, false>(), k, rn, nx);
       rn = nx;
     }
-    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
+    next_item.at(k_total, k_total);  // an item without steps
+    if (tid == 0) item_store(s_info[cur ^ 1], next_item.info);  // before the output stores
     ++kth;
 
     if constexpr (HAS_BIAS) {
@@ -944,12 +949,18 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     // wait only for their own prefetches
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    ItemInfo nxt;
-    if (tid == 0) nxt = item_load(a.plan_q, snake_item(kth + 1, blockIdx.x, gridDim.x), a.hq, total_items);
+    NextItem<Plan> next_item{a.plan_q, a.hq, total_items};
     int n = n0;
-    for (; n < min(n_plain, n1); ++n) step(std::integral_constant<bool, false>(), n);
-    for (; n < n1; ++n) step(std::integral_constant<bool, true>(), n);
-    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
+    for (; n < min(n_plain, n1); ++n) {
+      next_item.at(n - n0, n1 - n0);
+      step(std::integral_constant<bool, false>(), n);
+    }
+    for (; n < n1; ++n) {
+      next_item.at(n - n0, n1 - n0);
+      step(std::integral_constant<bool, true>(), n);
+    }
+    next_item.at(n1 - n0, n1 - n0);  // an item without steps
+    if (tid == 0) item_store(s_info[cur ^ 1], next_item.info);  // before the output stores
     ++kth;
 
     // dQ = scale * acc.  A chunk of a split tile stores acc in float32 to its
@@ -1035,13 +1046,9 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     __syncthreads();
   }
   // then the merge slabs of split dK/dV tiles (the dK/dV pass has finished),
-  // continuing the same order: workgroups with fewer dQ items take more slabs
+  // round robin over the workgroups
   const int merge_items = uniform(a.plan_k.hdr[2]) * a.hkv * 4;
-  for (int k2 = kth;; ++k2) {
-    const int m = snake_item(k2, blockIdx.x, gridDim.x) - total_items;
-    if (m >= merge_items) break;
-    dkdv_merge_item<D>(a, m);
-  }
+  for (int m = blockIdx.x; m < merge_items; m += gridDim.x) dkdv_merge_item<D>(a, m);
 }
 
 template <int H16, int D, bool CAUSAL, bool HAS_BIAS>

@@ -229,16 +229,14 @@ __device__ __forceinline__ bool split_done_last(int* left, int* s_flag) {
 
 // ---------------------------------------------------------------------------
 // Work assignment.  A planner kernel writes, per pass, the list of work units
-// sorted by cost (heaviest first); the pass's persistent workgroups then take
-// the items of that list in a fixed order: rounds of gridDim.x items, with
-// workgroup w taking position w of even rounds and position gridDim.x - 1 - w
-// of odd rounds (a snake over the sorted list, so a workgroup's heavy items
-// pair with light ones).  No atomics: on MI355X a device-scope atomic resolves
-// past the per-XCD L2, and one shared queue cursor taken per item cost more
-// (measured: 4-6 us of a 45 us forward, 24 us when items are short) than the
-// imbalance a dynamic queue removes.  The order depends on the list alone.
+// sorted by cost (heaviest first) and zeroes the list's cursor (hdr[0]).  The
+// pass's persistent workgroups start with item w = blockIdx.x; every later
+// item is taken from the cursor: a workgroup takes its ticket at the start of
+// the second-to-last step of its current item and loads the ticket's plan
+// entries during the last, so the workgroups that finish first take the next
+// (heaviest remaining) items and neither round trip delays a step.  Results
+// never depend on which workgroup ran an item.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int snake_item(int k, int w, int g) { return k * g + ((k & 1) ? g - 1 - w : w); }
 
 // A work item and its unit's plan entries.  Thread 0 loads the entries of
 // the next item while the current item computes and publishes them in LDS
@@ -267,5 +265,29 @@ __device__ __forceinline__ void item_store(int* dst, const ItemInfo& r) {
 #pragma unroll
   for (int i = 0; i < kItemInts; ++i) dst[i] = r.v[i];
 }
+
+// The next item of a workgroup (thread 0's copy): at(n, steps) is called
+// before step n of the current item's `steps` (and once with n = steps after
+// them); it takes the ticket at n >= steps - 2 and loads the item at
+// n >= steps - 1.  Items are numbered gridDim.x + ticket.
+template <typename PlanT>
+struct NextItem {
+  const PlanT& pl;
+  int per_unit, total_items;
+  ItemInfo info;
+  int ticket = 0;
+  bool asked = false, have = false;
+  __device__ __forceinline__ void at(int n, int steps) {
+    if (threadIdx.x != 0) return;
+    if (!asked && n >= steps - 2) {
+      ticket = __hip_atomic_fetch_add(&pl.hdr[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asked = true;
+    }
+    if (asked && !have && n >= steps - 1) {
+      info = item_load(pl, (int)gridDim.x + ticket, per_unit, total_items);
+      have = true;
+    }
+  }
+};
 
 }  // namespace va

@@ -640,8 +640,10 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     f32x16_t s_cur[QT][NS];
     if (active(0)) qk(0, s_cur);
     __syncthreads();  // every wave has read K(0) before K(2) replaces it
-    ItemInfo nxt;
-    if (tid == 0) nxt = item_load(a.plan, snake_item(kth + 1, blockIdx.x, gridDim.x), a.hq, total_items);
+    // the next item: a ticket taken at the start of this item's second-to-last
+    // block, its plan entries loaded during the last (thread 0)
+    NextItem<Plan> next_item{a.plan, a.hq, total_items};
+    auto fetch_next = [&](int n) __attribute__((always_inline)) { next_item.at(n, nb); };
 
     auto step = [&](auto mask_tag, int n) {  // n: block index inside the unit
       constexpr bool MASK = decltype(mask_tag)::value;
@@ -707,28 +709,41 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       const std::integral_constant<bool, false> plain;
       const std::integral_constant<bool, true> masked;
       for (; j + 1 < j_plain; j += 2) {
+        fetch_next(j);
         step_fast(plain, j, s_cur, s_alt);
+        fetch_next(j + 1);
         step_fast(plain, j + 1, s_alt, s_cur);
       }
       if (j < j_plain) {
+        fetch_next(j);
         step_fast(plain, j, s_cur, s_alt);
 #pragma unroll
         for (int st = 0; st < NS; ++st) s_cur[0][st] = s_alt[0][st];
         ++j;
       }
       for (; j + 1 < nb; j += 2) {
+        fetch_next(j);
         step_fast(masked, j, s_cur, s_alt);
+        fetch_next(j + 1);
         step_fast(masked, j + 1, s_alt, s_cur);
       }
       if (j < nb) {
+        fetch_next(j);
         step_fast(masked, j, s_cur, s_alt);
         ++j;
       }
     } else {
-      for (; j < j_plain; ++j) step(std::integral_constant<bool, false>(), j);
-      for (; j < nb; ++j) step(std::integral_constant<bool, true>(), j);
+      for (; j < j_plain; ++j) {
+        fetch_next(j);
+        step(std::integral_constant<bool, false>(), j);
+      }
+      for (; j < nb; ++j) {
+        fetch_next(j);
+        step(std::integral_constant<bool, true>(), j);
+      }
     }
-    if (tid == 0) item_store(s_info[cur ^ 1], nxt);  // before the output stores
+    fetch_next(nb);  // an item without blocks
+    if (tid == 0) item_store(s_info[cur ^ 1], next_item.info);  // before the output stores
     ++kth;
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.  A chunk of a split
