@@ -1,8 +1,11 @@
 """Helpers for GPU tests: run a workload through the C ABI and compare with the oracle.
 
 Tolerances (per output tensor, over all valid elements, computed in float64):
-float32 runs: max-abs <= 1e-5 on O and LSE; gradients max-abs <= 1e-5 * max(1, max|ref|)
-(accumulations of up to thousands of float32 terms).  bf16 runs: max-abs <= 2e-2 and
+float32 runs: max-abs <= 1e-5 on O and LSE; gradients max-abs <= 1e-5 * max(1, max|ref|):
+the absolute 1e-5 while every gradient of the tensor stays within +-1, scaled by the
+largest gradient beyond that, because each gradient is a float32 sum over up to thousands
+of query rows (or keys) whose rounding error grows with the magnitude of the sum (float32
+unit roundoff 6e-8 per addition); measured dK error 2.0e-6 at max|dK| 4.9.  bf16 runs: max-abs <= 2e-2 and
 relative L2 <= 5e-3 on every tensor (gradients stored float32).  On shapes other than
 the five named workloads, a bf16 gradient's max-abs bound is max(2e-2, 2^-8 * max|ref|):
 the kernels round P and dS to bf16 (relative error <= 2^-9 per term) before the
