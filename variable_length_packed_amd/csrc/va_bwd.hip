@@ -492,7 +492,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
         }
       }
       if (k + 1 < k_total) commit(buf ^ 1);
-      __syncthreads();
+      lds_barrier();
     };
 
     if constexpr (HAS_BIAS) {
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     // every load so far (K and V fragments included) has landed: the steps below then
     // wait only for their own prefetches
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
+    lds_barrier();
     // the next item: a ticket taken at the start of this item's second-to-last
     // step, its plan entries loaded during the last (thread 0)
     NextItem<Plan> next_item{a.plan_k, per_unit, total_items};
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
           *(f32x4_t*)(pv + o) = (f32x4_t){dv[dt_][4 * i4], dv[dt_][4 * i4 + 1], dv[dt_][4 * i4 + 2], dv[dt_][4 * i4 + 3]};
         }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -936,7 +936,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
         sk.store(sm.kn[buf ^ 1]);
         sv.store(sm.vn[buf ^ 1]);
       }
-      __syncthreads();
+      lds_barrier();
     };
 
     if (n1 > n0) {
@@ -948,7 +948,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     // every load so far (Q and dO fragments included) has landed: the steps below then
     // wait only for their own prefetches
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
+    lds_barrier();
     NextItem<Plan> next_item{a.plan_q, a.hq, total_items};
     int n = n0;
     for (; n < min(n_plain, n1); ++n) {
@@ -1043,7 +1043,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
         write_dq();
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   // then the merge slabs of split dK/dV tiles (the dK/dV pass has finished),
   // round robin over the workgroups

@@ -114,6 +114,17 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // vmcnt = 0 (bits 3:0 and 15:14), expcnt = 7 (bits 6:4), lgkmcnt = 15 (bits 11:8)
 constexpr int kWaitVm0 = 0x0F70;
 
+// A workgroup barrier that orders LDS accesses only.  Unlike __syncthreads it
+// does not wait for the global loads and stores in flight (the next block's
+// prefetch, the plan entries of the next item, the output stores of the item
+// before).  LDS-direct buffer loads count as global loads: a barrier that
+// publishes their data is preceded by an explicit wait (kWaitVm0).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);

@@ -616,7 +616,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       }
       ld.store_k(sm, n & 1);
       ld.store_v(sm, (n + 1) & 1);
-      __syncthreads();
+      lds_barrier();
       }
     };
 
@@ -636,10 +636,10 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       ld1.store_k(sm, 1);
     }
     if (btile) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the bias tile, loaded straight into LDS
-    __syncthreads();
+    lds_barrier();
     f32x16_t s_cur[QT][NS];
     if (active(0)) qk(0, s_cur);
-    __syncthreads();  // every wave has read K(0) before K(2) replaces it
+    lds_barrier();  // every wave has read K(0) before K(2) replaces it
     // the next item: a ticket taken at the start of this item's second-to-last
     // block, its plan entries loaded during the last (thread 0)
     NextItem<Plan> next_item{a.plan, a.hq, total_items};
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       ld.store_k(sm, n & 1);
       ld.store_v(sm, (n + 1) & 1);
       if (btile) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // block n + 1's bias tile has landed
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
@@ -866,7 +866,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
