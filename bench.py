@@ -77,25 +77,76 @@ def measured_traffic(kernel: str, workload: str):
     return None if e is None else e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, min_seconds: float = 10.0, max_reps: int = 10):
-    """The fp64 oracle (forward + backward of every sequence) timed on the host cores."""
-    import oracle  # test infrastructure: only this leg of the bench uses it
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    flops = count.fwd_flops(w) + count.bwd_flops(w)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal, w.bias, w.bias_strides)
-        oracle.backward(w.dout, w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal, w.bias,
-                        w.bias_strides)
-        reps += 1
+# ---------------------------------------------------------------- CPU oracle leg
+# The oracle (test infrastructure; only this leg of the bench runs it) does
+# the step one (sequence, KV head) unit at a time: the forward of the unit's
+# query heads and the backward of the group.  Units run in a pool of worker
+# processes, one per core this process may use (within the host's stated CPU
+# share), each with BLAS held to one thread; each worker rebuilds the seeded
+# workload itself.
+
+_W = None  # the worker's workload
+
+
+def _oracle_init(cfg_id: int) -> None:
+    global _W
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    _W = config(cfg_id, with_dout=True)
+
+
+def _oracle_unit(b: int, g: int):
+    """Forward (out, lse) of the query heads of KV head g and the group's backward, sequence b."""
+    import oracle  # test infrastructure: only the bench's CPU leg uses it
+    w = _W
+    t0 = time.perf_counter()
+    n_rep = w.hq // w.hkv
+    fw = [oracle.sequence_head_forward(w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale, w.causal, w.bias,
+                                       w.bias_strides, b, h)
+          for h in range(g * n_rep, (g + 1) * n_rep)]
+    dq, dk, dv = oracle.sequence_group_backward(w.dout, w.q, w.k, w.v, w.cu_q, w.cu_k, w.scale,
+                                                w.causal, w.bias, w.bias_strides, b, g)
+    return b, g, fw, dq, dk, dv, time.perf_counter() - t0
+
+
+def cpu_baseline(cfg_id: int, w, one_worker_seconds: float = 8.0):
+    """The fp64 oracle timed on the host cores over the whole step's workload, plus the
+    same units on one worker (a bounded sample).  Returns (baseline dict, oracle outputs)."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    from threadpoolctl import threadpool_limits
+    # one worker per core this process may run on, within the host's CPU share when the
+    # environment states one (OMP_NUM_THREADS)
+    cores = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        cores = min(cores, int(share))
+    units = [(b, g) for b in range(w.batch) for g in range(w.hkv)]
+    # heaviest first (pairs of the sequence), so the pool's tail is short
+    units.sort(key=lambda u: -count.visible_pairs(int(w.lens_q[u[0]]), int(w.lens_k[u[0]]), w.causal))
+    ctx = mp.get_context("spawn")  # no fork of a process that holds the GPU
+    with ProcessPoolExecutor(max_workers=cores, mp_context=ctx, initializer=_oracle_init,
+                             initargs=(cfg_id,)) as ex:
+        list(ex.map(abs, range(cores)))  # workers up and their workload built before the clock
+        t0 = time.perf_counter()
+        res = list(ex.map(_oracle_unit, *zip(*units)))
         el = time.perf_counter() - t0
-        if el >= min_seconds or reps >= max_reps:
-            break
-    rate = flops * reps / el / 1e12
+    flops = count.fwd_flops(w) + count.bwd_flops(w)
+    # one worker, in this process, BLAS at one thread: the lightest units first, until the
+    # sample's time is spent; its rate is FLOPs done / time
+    global _W
+    _W = w
+    done, t1 = 0, time.perf_counter()
+    with threadpool_limits(1):
+        for b, g in reversed(units):
+            _oracle_unit(b, g)
+            done += 1
+            if time.perf_counter() - t1 >= one_worker_seconds:
+                break
+    el1 = time.perf_counter() - t1
+    sample = list(reversed(units))[:done]
+    pairs = lambda us: sum(count.visible_pairs(int(w.lens_q[b]), int(w.lens_k[b]), w.causal) for b, _ in us)
+    flops1 = flops * pairs(sample) / pairs(units)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -103,16 +154,48 @@ def cpu_baseline(w, min_seconds: float = 10.0, max_reps: int = 10):
             model = m.group(1).strip() if m else ""
     except OSError:
         pass
-    return {"value": rate, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the whole workload, forward + backward, {reps} time(s), {el:.1f} s, "
-                      f"numpy float64 with {threads} BLAS threads on {model or 'the host CPU'}"}
+    base = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole step's workload once (forward + backward of {len(units)} (sequence, KV "
+                      f"head) units) in {el:.2f} s on a pool of {cores} worker processes, numpy float64, "
+                      f"BLAS at 1 thread each, on {model or 'the host CPU'}",
+            "seconds": round(el, 3),
+            "one_worker": {"value": flops1 / el1 / 1e12, "unit": "TFLOP/s", "seconds": round(el1, 3),
+                           "units": done, "of_units": len(units)},
+            "cpu_model": model}
+    outs = {"out": np.zeros((w.total_q, w.hq, w.d)), "lse": np.full((w.hq, w.total_q), -np.inf),
+            "dq": np.zeros((w.total_q, w.hq, w.d)), "dk": np.zeros((w.total_k, w.hkv, w.d)),
+            "dv": np.zeros((w.total_k, w.hkv, w.d))}
+    n_rep = w.hq // w.hkv
+    for b, g, fw, dq, dk, dv, _ in res:
+        q0, q1, k0, k1 = w.cu_q[b], w.cu_q[b + 1], w.cu_k[b], w.cu_k[b + 1]
+        for r, (o, l) in enumerate(fw):
+            outs["out"][q0:q1, g * n_rep + r] = o
+            outs["lse"][g * n_rep + r, q0:q1] = l
+        outs["dq"][q0:q1, g * n_rep:(g + 1) * n_rep] = dq
+        outs["dk"][k0:k1, g] = dk
+        outs["dv"][k0:k1, g] = dv
+    return base, outs
+
+
+def parity(gpu: dict, ref: dict) -> dict:
+    """Per-tensor max |GPU - oracle| and relative L2 error over the rows both define."""
+    r = {}
+    for name, a in gpu.items():
+        x, y = np.asarray(a, dtype=np.float64), ref[name]
+        fin = np.isfinite(y)
+        d = np.where(fin, x - np.where(fin, y, 0.0), 0.0)
+        same_inf = bool(np.all(x[~fin] == y[~fin]))
+        r[name] = {"max_abs": float(np.abs(d).max()),
+                   "rel_l2": float(np.linalg.norm(d) / max(np.linalg.norm(np.where(fin, y, 0.0)), 1e-300)),
+                   "non_finite_match": same_inf}
+    return r
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="3", help="config id for the step (default 3)")
     ap.add_argument("--sections", default="qwen,packing,bias,decode,variants",
@@ -196,6 +279,20 @@ def main() -> int:
     ms_fwd = timed(fwd, args.steps)
     ms_bwd = timed(bwd, args.steps)
 
+    # cold caches: before each timed step a 512 MiB fill evicts the XCDs' L2s and the
+    # 256 MB Infinity Cache, so the step reads its inputs from HBM
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for ea, eb in evs:
+        scrub.fill_(1)
+        ea.record()
+        step()
+        eb.record()
+    torch.cuda.synchronize()
+    ms_cold = sum(ea.elapsed_time(eb) for ea, eb in evs) / len(evs)
+    del scrub
+
     # per-kernel HIP-event timing on the stream the kernels run on
     va.va_timing_start(64 * args.steps + 64)
     for _ in range(args.steps):
@@ -207,6 +304,9 @@ def main() -> int:
         fl = algorithmic_flops(w, name)
         kernels[name] = {"launches": n, "avg_ms": round(avg, 5),
                          "tflops": round(fl / (avg * 1e-3) / 1e12, 2) if fl else None}
+    # the step's outputs (the last step above), for the parity check against the oracle
+    gpu_res = {"out": out.float().cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy(),
+               "dk": dk.cpu().numpy(), "dv": dv.cpu().numpy()}
     timed_kernels = {k: v for k, v in kt.items() if algorithmic_flops(w, k) > 0}
     dom = max(timed_kernels.items(), key=lambda kv: kv[1][1])[0] if timed_kernels else None
     roof = None
@@ -413,7 +513,16 @@ def main() -> int:
             flv = count.fwd_flops(wv) + count.bwd_flops(wv)
             variants["steps"][vname] = {"ms": round(msv, 5), "tflops": round(flv / (msv * 1e-3) / 1e12, 2)}
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    cpu = par = None
+    if not args.no_cpu_baseline:
+        cpu, ref = cpu_baseline(int(args.workload), w)
+        tol = {"max_abs": 2e-2, "rel_l2": 5e-3} if w.dtype == "bf16" else {"max_abs": 1e-5, "rel_l2": None}
+        errs = parity(gpu_res, ref)
+        ok = all(e["max_abs"] <= tol["max_abs"] and (tol["rel_l2"] is None or e["rel_l2"] <= tol["rel_l2"])
+                 and e["non_finite_match"] for e in errs.values())
+        par = {"against": "the fp64 oracle on the whole step (every row, head and dim)",
+               "tensors": errs, "tolerance": tol, "pass": ok}
+        del ref
     props = torch.cuda.get_device_properties(dev)
     line = {
         "metric": "varlen attention TFLOP/s (non-padded FLOPs), fwd+bwd step, bf16 MFMA",
@@ -434,6 +543,10 @@ def main() -> int:
                    "visible_pairs_per_head": count.workload_pairs(w.lens_q, w.lens_k, True),
                    "parallelism": "single GPU"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "cold_cache": {"ms_per_step": round(ms_cold, 5),
+                       "tflops": round((flops_fwd + flops_bwd) / (ms_cold * 1e-3) / 1e12, 3),
+                       "how": "a 512 MiB fill before each timed step evicts the L2s and the Infinity Cache"},
+        "parity": par,
         "passes": {
             "fwd": {"ms": round(ms_fwd, 5), "tflops": round(flops_fwd / (ms_fwd * 1e-3) / 1e12, 2),
                     "pct_bf16_peak": round(100 * flops_fwd / (ms_fwd * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)},
