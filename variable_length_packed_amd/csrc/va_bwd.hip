@@ -216,6 +216,20 @@ struct DkdvSmem {
   float ndsum[2][BMQ];  // -D of each query (the dP accumulators start from it)
 };
 
+// The direct-staged layout (16-bit inputs without a bias, head_dim 64 or 128):
+// Q and dO blocks, and the raw LSE and dsum of their queries, load straight
+// into LDS two blocks ahead of the block computed, so three buffers; rows
+// unpadded in the swizzled order of swz().  The LSE and dsum are converted in
+// place (base 2, -D, rows past the sequence) once they have landed.
+template <int H16, int D>
+struct DkdvSmemDirect {
+  using T = elem_t<H16>;
+  __attribute__((aligned(16))) T qn[3][BMQ * D];
+  __attribute__((aligned(16))) T dn[3][BMQ * D];
+  __attribute__((aligned(16))) float lse2[3][BMQ];
+  __attribute__((aligned(16))) float ndsum[3][BMQ];
+};
+
 template <int H16, int D>
 constexpr int dkdv_min_blocks() { return D <= 64 ? 2 : 1; }
 
@@ -224,9 +238,10 @@ constexpr int dkdv_min_blocks() { return D <= 64 ? 2 : 1; }
 template <int H16, int D, bool CAUSAL, int BIAS>
 __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(BwdArgs a) {
   using T = elem_t<H16>;
-  using SM = DkdvSmem<H16, D>;
-  using St = typename SM::St;
   constexpr bool HAS_BIAS = BIAS != 0;
+  constexpr bool DIRECT = H16 != 0 && !HAS_BIAS && (D == 64 || D == 128);
+  using SM = typename std::conditional<DIRECT, DkdvSmemDirect<H16, D>, DkdvSmem<H16, D>>::type;
+  using St = Stager<H16, BMQ, D>;
   constexpr int DT = D / 32;
   // head_dim 256: each unit runs as two items, each accumulating dK and dV for
   // half of the dims (S and dP computed in both), so the accumulators fit
@@ -356,6 +371,58 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
         pd = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.dsum + rb, (int64_t)Lq * 4), pi * 4, 0, 0));
       }
     };
+    // direct staging: block rn's Q and dO rows into buffer b3 (wave w's load i fills
+    // slots (i * 4 + w) * 64 .. +63 of the tile: row = slot / PR, its piece
+    // (slot % PR) ^ (row % 8)), and the raw LSE (wave 0) and dsum (wave 1) of its
+    // queries; each wave issues NI_D loads per tensor, waves 0 and 1 one more
+    constexpr int PR = D * 2 / 16;      // 16-byte pieces per row
+    constexpr int NI_D = BMQ * PR / NT;  // loads per thread per tensor
+    static_assert(!DIRECT || BMQ * PR % NT == 0, "direct loads must tile the workgroup");
+    auto issue_direct = [&](int2 rn, int b3) {
+      if constexpr (DIRECT) {
+        const int r = uniform(rn.x), n = uniform(rn.y);
+        const int h = h_first + r;
+        const int qb = qs + n * BMQ;
+        const rsrc_t qres = make_rsrc((const T*)a.q + (size_t)q0 * qstride + (size_t)h * D,
+                                      Lq > 0 ? (int64_t)(Lq - 1) * qrow_bytes + D * ELT : 0);
+        const rsrc_t dres = make_rsrc((const T*)a.dout + (size_t)q0 * dostride + (size_t)h * D,
+                                      Lq > 0 ? (int64_t)(Lq - 1) * dorow_bytes + D * ELT : 0);
+#pragma unroll
+        for (int i = 0; i < NI_D; ++i) {
+          const int base = (i * (NT / 64) + wid) * 64;  // first slot of this wave's load
+          const int u = base + lane, row = u / PR, piece = (u % PR) ^ (row & 7);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              qres, (__attribute__((address_space(3))) void*)(sm.qn[b3] + base * 8), 16,
+              (qb + row) * qrow_bytes + piece * 16, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              dres, (__attribute__((address_space(3))) void*)(sm.dn[b3] + base * 8), 16,
+              (qb + row) * dorow_bytes + piece * 16, 0, 0, 0);
+        }
+        if (wid < 2) {
+          const size_t rb = (size_t)h * a.total_q + q0;
+          const rsrc_t res = make_rsrc((wid == 0 ? a.lse : a.dsum) + rb, (int64_t)Lq * 4);
+          float* dst = wid == 0 ? sm.lse2[b3] : sm.ndsum[b3];
+          if (lane < BMQ)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (__attribute__((address_space(3))) void*)dst, 4,
+                                                     (qb + lane) * 4, 0, 0, 0);
+        }
+      }
+    };
+    // once block rn's direct loads have landed: its LSE to base 2 (+inf for rows
+    // past the sequence or that see nothing, so their P is 0) and its dsum to -D
+    // (0 past the sequence), by the waves that loaded them
+    auto fixup_direct = [&](int2 rn, int b3) {
+      if constexpr (DIRECT) {
+        const int qb = qs + uniform(rn.y) * BMQ;
+        const int pi_ = qb + lane;
+        if (wid == 0 && lane < BMQ) {
+          const float l = sm.lse2[b3][lane];
+          sm.lse2[b3][lane] = pi_ < Lq && l != -INFINITY ? l * kLog2e : INFINITY;
+        } else if (wid == 1 && lane < BMQ) {
+          sm.ndsum[b3][lane] = pi_ < Lq ? -sm.ndsum[b3][lane] : 0.f;
+        }
+      }
+    };
     auto commit = [&](int buf) {
       // the bias tile's direct loads were issued before Q and dO: wait for all of them
       // so the barrier after this publishes the tile
@@ -369,13 +436,18 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
       }
     };
 
-    auto step = [&](auto mask_tag, int k, int2 rn, int2 rn_next) {
+    // rn, rn_next, rn_next2: blocks k, k + 1, k + 2
+    auto step = [&](auto mask_tag, int k, int2 rn, int2 rn_next, int2 rn_next2) {
       constexpr bool MASK = decltype(mask_tag)::value;
-      const int buf = k & 1;
+      const int buf = DIRECT ? k % 3 : k & 1;
       const int r = uniform(rn.x), n = uniform(rn.y);
       const int h = h_first + r;
       const int qb = qs + n * BMQ;
-      if (k + 1 < k_total) issue(rn_next, buf ^ 1);
+      if constexpr (DIRECT) {
+        if (k + 2 < k_total) issue_direct(rn_next2, (k + 2) % 3);
+      } else {
+        if (k + 1 < k_total) issue(rn_next, buf ^ 1);
+      }
       // this wave's keys are seen by queries i >= wk0 - off
       const bool active = wave_keys && (!CAUSAL || qb + BMQ - 1 + off >= wk0);
       if (active) {
@@ -390,8 +462,20 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
         }
         const f32x16_t nd16 = {nd[0][0], nd[0][1], nd[0][2], nd[0][3], nd[1][0], nd[1][1], nd[1][2], nd[1][3],
                                nd[2][0], nd[2][1], nd[2][2], nd[2][3], nd[3][0], nd[3][1], nd[3][2], nd[3][3]};
-        f32x16_t s = mm_rows<H16, D>(&sm.qn[buf][r32 * St::NP], kf, (f32x16_t){}, hh);
-        f32x16_t dp = mm_rows<H16, D>(&sm.dn[buf][r32 * St::NP], vf, nd16, hh);
+        f32x16_t s, dp;
+        if constexpr (DIRECT) {
+          s = (f32x16_t){};
+          dp = nd16;
+#pragma unroll
+          for (int ks = 0; ks < D / 16; ++ks) {
+            const int o = swz<D>(r32, 16 * ks + 8 * hh);
+            s = mfma16<H16>(*(const u32x4_t*)&sm.qn[buf][o], kf.b[ks], s);
+            dp = mfma16<H16>(*(const u32x4_t*)&sm.dn[buf][o], vf.b[ks], dp);
+          }
+        } else {
+          s = mm_rows<H16, D>(&sm.qn[buf][r32 * St::NP], kf, (f32x16_t){}, hh);
+          dp = mm_rows<H16, D>(&sm.dn[buf][r32 * St::NP], vf, nd16, hh);
+        }
         // the bias of head h through a resource that ends after the last element a valid
         // (row, key) reads (rounded up to a dword); rows past the sequence read 0 or are
         // zeroed below, so garbage never meets a row whose P must be 0
@@ -459,8 +543,14 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
             for (int dt_ = 0; dt_ < DTO; ++dt_) {
               // dims 32 (dt_ + hb DTO) + r32 of the queries of P's chunk c, from the rows
               const int c0 = 32 * (dt_ + hb * DTO);
-              const u32x4_t ob = tr_frag(sm.dn[buf], St::NP, c, c0);
-              const u32x4_t qb4 = tr_frag(sm.qn[buf], St::NP, c, c0);
+              u32x4_t ob, qb4;
+              if constexpr (DIRECT) {
+                ob = tr_frag_swz<D>(sm.dn[buf], c, c0);
+                qb4 = tr_frag_swz<D>(sm.qn[buf], c, c0);
+              } else {
+                ob = tr_frag(sm.dn[buf], St::NP, c, c0);
+                qb4 = tr_frag(sm.qn[buf], St::NP, c, c0);
+              }
               dv[dt_] = mfma16<H16>(pa, ob, dv[dt_]);
               dk[dt_] = mfma16<H16>(da, qb4, dk[dt_]);
               dk[dt_] = mfma16<H16>(da_lo, qb4, dk[dt_]);
@@ -491,7 +581,18 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
           }
         }
       }
-      if (k + 1 < k_total) commit(buf ^ 1);
+      if constexpr (DIRECT) {
+        // block k + 1's loads (issued a step ago) have landed; block k + 2's stay in flight
+        if (k + 2 < k_total) {
+          if (wid < 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * NI_D + 1));
+          else __builtin_amdgcn_s_waitcnt(wait_vm(2 * NI_D));
+        } else {
+          __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        }
+        if (k + 1 < k_total) fixup_direct(rn_next, (k + 1) % 3);
+      } else {
+        if (k + 1 < k_total) commit(buf ^ 1);
+      }
       lds_barrier();
     };
 
@@ -510,26 +611,42 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
       }
     }
     int2 rn = make_int2(0, u0);
-    if (k_total > 0) { issue(rn, 0); commit(0); }
-    // every load so far (K and V fragments included) has landed: the steps below then
-    // wait only for their own prefetches
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    int2 rn1 = next_of(1, rn);  // block k + 1
+    if constexpr (DIRECT) {
+      if (k_total > 0) issue_direct(rn, 0);
+      if (k_total > 1) issue_direct(rn1, 1);
+      // block 0 and every load before it (K and V fragments included) have landed
+      if (k_total > 1) {
+        if (wid < 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * NI_D + 1));
+        else __builtin_amdgcn_s_waitcnt(wait_vm(2 * NI_D));
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      }
+      if (k_total > 0) fixup_direct(rn, 0);
+    } else {
+      if (k_total > 0) { issue(rn, 0); commit(0); }
+      // every load so far (K and V fragments included) has landed: the steps below then
+      // wait only for their own prefetches
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
     lds_barrier();
     // the next item: a ticket taken at the start of this item's second-to-last
     // step, its plan entries loaded during the last (thread 0)
     NextItem<Plan> next_item{a.plan_k, per_unit, total_items};
     int k = 0;
     for (; k < k_masked; ++k) {
-      const int2 nx = next_of(k + 1, rn);
+      const int2 nx2 = next_of(k + 2, rn1);
       next_item.at(k, k_total);
-      step(std::integral_constant<bool, true>(), k, rn, nx);
-      rn = nx;
+      step(std::integral_constant<bool, true>(), k, rn, rn1, nx2);
+      rn = rn1;
+      rn1 = nx2;
     }
     for (; k < k_total; ++k) {
-      const int2 nx = next_of(k + 1, rn);
+      const int2 nx2 = next_of(k + 2, rn1);
       next_item.at(k, k_total);
-      step(std::integral_constant<bool, false>(), k, rn, nx);
-      rn = nx;
+      step(std::integral_constant<bool, false>(), k, rn, rn1, nx2);
+      rn = rn1;
+      rn1 = nx2;
     }
     next_item.at(k_total, k_total);  // an item without steps
     if (tid == 0) item_store(s_info[cur ^ 1], next_item.info);  // before the output stores

@@ -198,6 +198,29 @@ __device__ __forceinline__ u32x4_t tr_frag(const uint16_t* tile, int pitch, int 
   return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Tiles staged straight from memory into LDS (buffer loads with an LDS
+// destination write each wave's 64 x 16 bytes contiguously) keep their rows
+// unpadded: row r of D 16-bit elements holds its 16-byte piece p in slot
+// p ^ (r % 8), so eight rows read at the same column fall in different banks.
+// Element offset of (row r, column col), col a multiple of 4.
+template <int D>
+__device__ __forceinline__ int swz(int r, int col) {
+  return r * D + (((col >> 3) ^ (r & 7)) << 3) + (col & 7);
+}
+// tr_frag of such a tile (rows 16 kc + ..., columns c0 + l % 32).
+template <int D>
+__device__ __forceinline__ u32x4_t tr_frag_swz(const uint16_t* tile, int kc, int c0) {
+  const int lane = threadIdx.x & 63;
+  const uint16_t* p = tile + swz<D>(16 * kc + 4 * (lane >> 5) + ((lane >> 2) & 3),
+                                    c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  const u32x2_t lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * D);  // row + 8: the same slot order
+  return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+}
+
+// s_waitcnt operand that waits until at most n vector memory operations of
+// the wave are outstanding (n < 64), other counters untouched.
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
 // Partial results of split tiles are written by one workgroup and merged by
 // another, possibly on another XCD (each XCD has its own L2).  They are
 // written and read with device-coherent accesses (cache policy sc1, as for
