@@ -171,18 +171,20 @@ def test_fwd_workspace_size(lib):
     assert f(2, 16, 16, 8, 8, 4, 3, 64, BF16) == 0
     assert f(2, 16, 16, 8, 8, 4, 2, 80, BF16) == 0
     assert f(2, 16, 16, 8, 8, 4, 2, 96, BF16) > 0 and f(2, 16, 16, 8, 8, 4, 2, 32, F32) > 0
-    # no tile can see more than 1024 keys: only the plan (<= total/128 + batch units)
+    # no tile sees more than 2048 keys: only the plan (<= total/128 + batch units)
     assert f(2, 16, 16, 8, 8, 4, 2, 64, BF16) == _plan_bytes(2, 0, 4)
     assert f(20, 10459, 10459, 1024, 1024, 14, 2, 64, BF16) == _plan_bytes(10459 // 128 + 20, 0, 14)
-    # longer keys: partial slots of hq * 128 rows * (d + 1) floats, two per tile at most
+    assert f(16, 9687, 9687, 2048, 2048, 14, 2, 64, BF16) == _plan_bytes(9687 // 128 + 16, 0, 14)
+    # longer keys (up to 4096: 64 steps, two 2048-key chunks): partial slots of
+    # hq * 128 rows * (d + 1) floats, two per tile at most
     tiles = 9687 // 128 + 16
     slot = 14 * 128 * 65 * 4
     slots = min(2 * tiles, (64 << 20) // slot)
-    assert f(16, 9687, 9687, 2048, 2048, 14, 2, 64, BF16) == \
+    assert f(16, 9687, 9687, 4096, 4096, 14, 2, 64, BF16) == \
         _plan_bytes(tiles + slots, slots // 2, 14) + _r(slots * slot)
-    assert f(16, 9687, 9687, 2048, 2048, 14, 2, 64, F16) == f(16, 9687, 9687, 2048, 2048, 14, 2, 64, BF16)
-    # float32 steps are 32 keys, so the same 1024-key chunk is 32 steps
-    assert f(2, 16, 16, 1024, 1024, 4, 2, 64, F32) == _plan_bytes(2, 0, 4)
+    assert f(16, 9687, 9687, 4096, 4096, 14, 2, 64, F16) == f(16, 9687, 9687, 4096, 4096, 14, 2, 64, BF16)
+    # float32 steps are 32 keys, so the same 2048-key chunk is 64 steps
+    assert f(2, 16, 16, 2048, 2048, 4, 2, 64, F32) == _plan_bytes(2, 0, 4)
 
 
 def test_bwd_workspace_size(lib):
@@ -199,10 +201,10 @@ def test_bwd_workspace_size(lib):
     n = f(2, 16, 16, 8, 8, 4, 4, 64, BF16, F32)
     # dK/dV plan (its split tiles are merged by the dQ pass: no counts) + dQ plan
     assert n == _r(4 * 16 * 4) + _plan_bytes(2, 0, 0) + _plan_bytes(2, 0, 4)  # no partial slots (per-key bias sums: none)
-    # GQA 4/2: a dK/dV unit holds at most 768 (query row, head) pairs = 12 blocks of 32
-    assert f(2, 16, 16, 384, 8, 4, 2, 64, BF16, F32) == n
-    big = f(2, 16, 16, 416, 8, 4, 2, 64, BF16, F32)
-    slots_k = 2 * 2  # two tiles, ceil(13 / 12) = 2 chunks each
+    # GQA 4/2: a dK/dV unit holds at most 1536 (query row, head) pairs = 24 blocks of 32
+    assert f(2, 16, 16, 768, 8, 4, 2, 64, BF16, F32) == n
+    big = f(2, 16, 16, 800, 8, 4, 2, 64, BF16, F32)
+    slots_k = 2 * 2  # two tiles, ceil(25 / 24) = 2 chunks each
     assert big == _r(4 * 16 * 4) + _plan_bytes(2 + slots_k, slots_k // 2, 0) + _plan_bytes(2, 0, 4) + \
         _r(slots_k * 2 * 2 * 128 * 64 * 4) + _r(slots_k * 4 * 128 * 4)  # + per-key bias sums per slot
 

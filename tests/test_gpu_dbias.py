@@ -30,7 +30,7 @@ CASES = [
                                          dtype="bf16", bias="per_pair", bias_layout="permuted")),
     ("pair-bf16-cross-d128", dict(seed=73, lens_q=[50, 112], lens_k=[90, 262], hq=8, hkv=2, d=128,
                                   causal=True, dtype="bf16", bias="per_pair")),
-    ("pair-bf16-causal-split", dict(seed=81, lens_q=[700, 33, 450], hq=4, hkv=2, d=64, causal=True,
+    ("pair-bf16-causal-split", dict(seed=81, lens_q=[700, 33, 450], hq=4, hkv=1, d=64, causal=True,
                                     dtype="bf16", bias="per_pair")),
     ("pair-f32-causal-qgtk", dict(seed=82, lens_q=[90, 20, 300], lens_k=[50, 20, 140], hq=2, hkv=1, d=64,
                                   causal=True, dtype="f32", bias="per_pair")),

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 
 CASES = [
     ("gqa7-causal-ragged", dict(seed=81, lens_q=[37, 300, 129, 64, 1, 5], hq=14, hkv=2, d=64, causal=True)),
-    ("gqa7-causal-split", dict(seed=82, lens_q=[1500, 33, 700], hq=14, hkv=2, d=64, causal=True)),
+    ("gqa7-causal-split", dict(seed=82, lens_q=[2600, 33, 700], hq=14, hkv=2, d=64, causal=True)),
     ("mqa-noncausal", dict(seed=83, lens_q=[200, 17, 64], hq=8, hkv=1, d=64, causal=False)),
     ("cross-d128", dict(seed=84, lens_q=[112, 50, 0], lens_k=[262, 90, 7], hq=32, hkv=8, d=128, causal=True)),
     ("d128-noncausal-long", dict(seed=85, lens_q=[900, 3], hq=4, hkv=2, d=128, causal=False)),

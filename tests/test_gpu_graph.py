@@ -56,7 +56,7 @@ def test_fwd_bwd_step_replays(short):
         w = make_case(131, [1, 4, 2, 3], lens_k=[900, 40, 3000, 5], hq=16, hkv=4, d=64, causal=True,
                       dtype="bf16", with_dout=True)
     else:  # split tiles in every pass
-        w = make_case(132, [37, 300, 1500, 129], hq=14, hkv=2, d=64, causal=True, dtype="bf16", with_dout=True)
+        w = make_case(132, [37, 300, 2600, 129], hq=14, hkv=2, d=64, causal=True, dtype="bf16", with_dout=True)
     names = ("out", "lse", "dq", "dk", "dv")
     inp = _gpu.device_inputs(w)
     b = _alloc_step(w, inp)

@@ -25,9 +25,9 @@ pytestmark = pytest.mark.gpu
 DEV = _gpu.DEV
 
 CASES = [
-    ("d32-bf16-gqa7-causal-split", dict(seed=111, lens_q=[37, 300, 129, 1500, 5], hq=14, hkv=2, d=32,
+    ("d32-bf16-gqa7-causal-split", dict(seed=111, lens_q=[37, 300, 129, 2600, 5], hq=14, hkv=2, d=32,
                                         causal=True, dtype="bf16")),
-    ("d96-bf16-gqa4-causal-split", dict(seed=112, lens_q=[1500, 64, 1], hq=8, hkv=2, d=96, causal=True,
+    ("d96-bf16-gqa4-causal-split", dict(seed=112, lens_q=[2600, 64, 1], hq=8, hkv=2, d=96, causal=True,
                                         dtype="bf16")),
     ("d96-f16-cross-mqa", dict(seed=113, lens_q=[112, 50, 0], lens_k=[262, 90, 7], hq=8, hkv=1, d=96,
                                causal=True, dtype="f16")),
@@ -36,7 +36,7 @@ CASES = [
     ("d96-f32-causal-gqa", dict(seed=115, lens_q=[200, 37], hq=4, hkv=2, d=96, causal=True, dtype="f32")),
     ("d32-f16-short-rows", dict(seed=116, lens_q=[1, 4, 2], lens_k=[700, 40, 2000], hq=16, hkv=4, d=32,
                                 causal=True, dtype="f16")),
-    ("d256-bf16-gqa4-causal-split", dict(seed=120, lens_q=[300, 1100, 17], hq=8, hkv=2, d=256, causal=True,
+    ("d256-bf16-gqa4-causal-split", dict(seed=120, lens_q=[300, 2200, 17], hq=8, hkv=2, d=256, causal=True,
                                          dtype="bf16")),
     ("d256-f32-noncausal-mqa", dict(seed=121, lens_q=[100, 37, 1], hq=2, hkv=1, d=256, causal=False,
                                     dtype="f32")),

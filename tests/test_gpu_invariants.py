@@ -19,7 +19,7 @@ from . import _gpu
 
 pytestmark = pytest.mark.gpu
 
-LENS = [37, 300, 129, 64, 1500, 5]  # 1500: split work units in every pass
+LENS = [37, 300, 129, 64, 2600, 5]  # 2600: split work units in every pass
 
 
 def _run_all(w):
@@ -30,7 +30,7 @@ def _run_all(w):
     return [x.detach().clone() for x in (out, lse, dq, dk, dv)]
 
 
-LENS_BIAS = [37, 300, 129, 64, 1000, 5]  # keeps the per-pair bias grid at 1024 x 1024
+LENS_BIAS = [37, 300, 129, 64, 1000, 5]  # keeps the per-pair bias grid at 1024 x 1024 (dK/dV split)
 
 
 def _case(seed, lens_q, lens_k=None, bias=False, dtype="bf16"):

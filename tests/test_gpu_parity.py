@@ -54,11 +54,11 @@ for dt in ("f32", "bf16"):
                                             hkv=2, d=64, causal=False, dtype=dt, with_dout=True,
                                             bias="per_pair", bias_std=0.5)))
     # tiles long enough to be split into several work units (forward and dQ:
-    # more than 1024 keys; dK/dV: more than 768 query-row x head pairs),
-    # merged by the merge kernels
+    # more than 2048 keys; dK/dV: more than 1536 query-row x head pairs),
+    # merged by the chunk that finishes last (forward, dQ) and by the dQ pass (dK/dV)
     CASES.append((f"split-long-{dt}", dict(seed=46, lens_q=[1500, 40, 2100], hq=4, hkv=1, d=64,
                                            causal=True, dtype=dt, with_dout=True)))
-    CASES.append((f"split-cross-bias-{dt}", dict(seed=47, lens_q=[300, 1100], lens_k=[1300, 2000],
+    CASES.append((f"split-cross-bias-{dt}", dict(seed=47, lens_q=[300, 1700], lens_k=[1300, 2600],
                                                  hq=2, hkv=2, d=64, causal=False, dtype=dt,
                                                  with_dout=True, bias="per_pair", bias_std=0.5)))
     CASES.append((f"split-decode-d128-{dt}", dict(seed=48, lens_q=[1, 3, 1200], lens_k=[3000, 1500, 2500],

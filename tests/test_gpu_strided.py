@@ -42,7 +42,7 @@ def _run(w, q, k, v, inp, dbias=None):
 
 
 FUSED = [
-    ("bf16-gqa7-causal-split", dict(seed=91, lens_q=[37, 300, 129, 1500, 5], hq=14, hkv=2, d=64, causal=True,
+    ("bf16-gqa7-causal-split", dict(seed=91, lens_q=[37, 300, 129, 2600, 5], hq=14, hkv=2, d=64, causal=True,
                                     dtype="bf16")),
     ("f32-d128-noncausal", dict(seed=92, lens_q=[100, 260, 1], hq=4, hkv=4, d=128, causal=False, dtype="f32")),
     ("f16-mqa-per-key-bias", dict(seed=93, lens_q=[64, 200, 17], hq=8, hkv=1, d=64, causal=True, dtype="f16",

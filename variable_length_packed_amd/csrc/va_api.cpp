@@ -103,8 +103,8 @@ va_status row_strides(const Common& c, const void* q, const void* k, const void*
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-constexpr int kChunkKeys = 1024;      // forward / dQ: most keys per unit
-constexpr int kDkdvUnitRows = 768;    // dK/dV: most (query row, head) pairs per unit
+constexpr int kChunkKeys = 2048;      // forward / dQ: most keys per unit
+constexpr int kDkdvUnitRows = 1536;   // dK/dV: most (query row, head) pairs per unit
 constexpr size_t kFwdPartBudget = (size_t)64 << 20;
 constexpr size_t kDkdvPartBudget = (size_t)128 << 20;
 constexpr size_t kDqPartBudget = (size_t)64 << 20;
