@@ -250,7 +250,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
   constexpr int ELT = (int)sizeof(T);
 
   __shared__ SM sm;
-  __shared__ int s_info[2][kItemInts];
+  __shared__ __attribute__((aligned(16))) int s_info[2][kItemInts];
   // per-key bias gradient sums [head of the group][key of the tile] (bias kernels only)
   __shared__ float db_acc[HAS_BIAS ? dbias_max_heads<D>() * BNK : 1];
   // a bias with contiguous keys and 16-byte aligned rows comes a step ahead, with
@@ -280,16 +280,17 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
   __syncthreads();
   for (int cur = 0;; cur ^= 1) {
     const int* inf = s_info[cur];
-    const int item = uniform(inf[0]);
+    const int item = uniform(inf[kInfItem]);
     if (item >= total_items) break;
     const int unit = item / per_unit;
     const int rem = uniform(item - unit * per_unit);  // the division runs on the vector ALU
     const int g = rem / HS;
     const int hb = rem - g * HS;  // which half of the dims (head_dim 256)
-    const int b = uniform(inf[1]), t = uniform(inf[2]);
-    const int u0 = uniform(inf[3]), u1 = uniform(inf[4]);
-    const int k0 = uniform(inf[5]), k1 = uniform(inf[6]), q0 = uniform(inf[7]), q1 = uniform(inf[8]);
-    const int slot = uniform(inf[9]);  // >= 0: a chunk of a split tile
+    const int b = uniform(inf[kInfUnit]), t = uniform(inf[kInfUnit + 1]);
+    const int u0 = uniform(inf[kInfUnit + 2]), u1 = uniform(inf[kInfUnit + 3]);
+    const int k0 = uniform(inf[kInfRows]), k1 = uniform(inf[kInfRows + 1]), q0 = uniform(inf[kInfRows + 2]),
+              q1 = uniform(inf[kInfRows + 3]);
+    const int slot = uniform(inf[kInfSlot]);  // >= 0: a chunk of a split tile
     const int Lq = q1 - q0, Lk = k1 - k0, off = Lk - Lq;
     const int kt0 = t * BNK;
     const int wk0 = kt0 + 32 * wid;  // first key of this wave
@@ -632,7 +633,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     lds_barrier();
     // the next item: a ticket taken at the start of this item's second-to-last
     // step, its plan entries loaded during the last (thread 0)
-    NextItem<Plan> next_item{a.plan_k, per_unit, total_items};
+    NextItem<Plan> next_item{a.plan_k, per_unit, total_items, s_info[cur ^ 1]};
     int k = 0;
     for (; k < k_masked; ++k) {
       const int2 nx2 = next_of(k + 2, rn1);
@@ -648,8 +649,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
       rn = rn1;
       rn1 = nx2;
     }
-    next_item.at(k_total, k_total);  // an item without steps
-    if (tid == 0) item_store(s_info[cur ^ 1], next_item.info);  // before the output stores
+    next_item.finish(k_total);
     ++kth;
 
     if constexpr (HAS_BIAS) {
@@ -769,6 +769,11 @@ __device__ __forceinline__ void dkdv_merge_item(const BwdArgs& a, int it) {
 }
 
 // ---------------------------------------------------------------- dQ
+// Two workgroups per CU (256 registers per lane) up to head_dim 128; one at 256,
+// whose accumulators and Q/dO fragments alone take about that many.
+template <int D>
+constexpr int dq_min_blocks() { return D <= 128 ? 2 : 1; }
+
 template <int H16, int D>
 struct DqSmem {
   using T = elem_t<H16>;
@@ -781,7 +786,7 @@ struct DqSmem {
 
 // BIAS: 0 none; 1 any layout (one element per load); 2 contiguous keys (four per load)
 template <int H16, int D, bool CAUSAL, int BIAS>
-__global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, (dq_min_blocks<D>())) void dq_kernel(BwdArgs a) {
   constexpr bool HAS_BIAS = BIAS != 0;
   using T = elem_t<H16>;
   using SM = DqSmem<H16, D>;
@@ -793,7 +798,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   using Sv = typename SM::Sv;
 
   __shared__ SM sm;
-  __shared__ int s_info[2][kItemInts];
+  __shared__ __attribute__((aligned(16))) int s_info[2][kItemInts];
   __shared__ int s_last;  // this chunk of a split tile finished last
 
   const int tid = threadIdx.x, lane = tid & 63, wid = uniform(tid >> 6);
@@ -812,15 +817,16 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
   __syncthreads();
   for (int cur = 0;; cur ^= 1) {
     const int* inf = s_info[cur];
-    const int item = uniform(inf[0]);
+    const int item = uniform(inf[kInfItem]);
     if (item >= total_items) break;
     const int unit = item / a.hq;
     const int h = item - unit * a.hq;
-    const int b = uniform(inf[1]), t = uniform(inf[2]);
-    const int n0 = uniform(inf[3]), n1 = uniform(inf[4]);
-    const int q0 = uniform(inf[5]), q1 = uniform(inf[6]), k0 = uniform(inf[7]), k1 = uniform(inf[8]);
-    const int slot = uniform(inf[9]);  // >= 0: a chunk of a split tile
-    const int si = uniform(inf[10]);   // that split tile
+    const int b = uniform(inf[kInfUnit]), t = uniform(inf[kInfUnit + 1]);
+    const int n0 = uniform(inf[kInfUnit + 2]), n1 = uniform(inf[kInfUnit + 3]);
+    const int q0 = uniform(inf[kInfRows]), q1 = uniform(inf[kInfRows + 1]), k0 = uniform(inf[kInfRows + 2]),
+              k1 = uniform(inf[kInfRows + 3]);
+    const int slot = uniform(inf[kInfSlot]);  // >= 0: a chunk of a split tile
+    const int si = uniform(inf[kInfSplit]);  // that split tile
     const int Lq = q1 - q0, Lk = k1 - k0, off = Lk - Lq;
     const int g = h / a.n_rep;
     const int r1 = Lq - t * BMQ_DQ;
@@ -1066,7 +1072,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
     // wait only for their own prefetches
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     lds_barrier();
-    NextItem<Plan> next_item{a.plan_q, a.hq, total_items};
+    NextItem<Plan> next_item{a.plan_q, a.hq, total_items, s_info[cur ^ 1]};
     int n = n0;
     for (; n < min(n_plain, n1); ++n) {
       next_item.at(n - n0, n1 - n0);
@@ -1076,8 +1082,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
       next_item.at(n - n0, n1 - n0);
       step(std::integral_constant<bool, true>(), n);
     }
-    next_item.at(n1 - n0, n1 - n0);  // an item without steps
-    if (tid == 0) item_store(s_info[cur ^ 1], next_item.info);  // before the output stores
+    next_item.finish(n1 - n0);
     ++kth;
 
     // dQ = scale * acc.  A chunk of a split tile stores acc in float32 to its
@@ -1119,7 +1124,7 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
       if (split_done_last(&a.plan_q.left[si * a.hq + h], &s_last)) {
         const int4 sp = a.plan_q.splits[si];
         const int sb = uniform(sp.z), nch = uniform(sp.w), me = slot - sb;  // first slot, chunks, this chunk
-        constexpr int G = DT < 2 ? DT : 2;  // output tiles summed per pass (bounds the registers)
+        constexpr int G = D <= 128 ? DT : 1;  // output tiles summed per pass (bounds the registers)
 #pragma unroll
         for (int g0 = 0; g0 < DT; g0 += G) {
           f32x4_t sum[G][4];
@@ -1128,14 +1133,13 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) sum[j][a4] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
           for (int c = 0; c < nch; ++c) {
-            f32x4_t oc[G][4];
             if (c == me) {
 #pragma unroll
               for (int j = 0; j < G; ++j)
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4)
-                  oc[j][a4] = (f32x4_t){acc[g0 + j][4 * a4], acc[g0 + j][4 * a4 + 1], acc[g0 + j][4 * a4 + 2],
-                                        acc[g0 + j][4 * a4 + 3]};
+                  sum[j][a4] += (f32x4_t){acc[g0 + j][4 * a4], acc[g0 + j][4 * a4 + 1], acc[g0 + j][4 * a4 + 2],
+                                          acc[g0 + j][4 * a4 + 3]};
             } else {
               const rsrc_t cres =
                   make_rsrc(a.part_q + ((size_t)(sb + c) * a.hq + h) * SLOT_Q, (int64_t)SLOT_Q * 4);
@@ -1143,12 +1147,8 @@ __global__ __launch_bounds__(NT, 2) void dq_kernel(BwdArgs a) {
               for (int j = 0; j < G; ++j)
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4)
-                  oc[j][a4] = buf_load16_dev(cres, (rl * D + 32 * (g0 + j) + 8 * a4 + 4 * hh) * 4);
+                  sum[j][a4] += buf_load16_dev(cres, (rl * D + 32 * (g0 + j) + 8 * a4 + 4 * hh) * 4);
             }
-#pragma unroll
-            for (int j = 0; j < G; ++j)
-#pragma unroll
-              for (int a4 = 0; a4 < 4; ++a4) sum[j][a4] += oc[j][a4];
           }
 #pragma unroll
           for (int j = 0; j < G; ++j)

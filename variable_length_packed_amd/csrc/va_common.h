@@ -217,6 +217,18 @@ __device__ __forceinline__ u32x4_t tr_frag_swz(const uint16_t* tile, int kc, int
   return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
 }
 
+// One lane's 16 (or 4) bytes from global memory straight into LDS (a buffer
+// load with an LDS destination; the lanes of the wave that run it write
+// consecutive pieces from `lds`).  Counts as a vector memory load.
+__device__ __forceinline__ void lds_load_direct16(const void* src, void* lds) {
+  const rsrc_t r = make_rsrc(src, 16);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, 0, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load_direct4(const void* src, void* lds) {
+  const rsrc_t r = make_rsrc(src, 4);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, 0, 0, 0, 0);
+}
+
 // s_waitcnt operand that waits until at most n vector memory operations of
 // the wave are outstanding (n < 64), other counters untouched.
 constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
@@ -276,22 +288,26 @@ __device__ __forceinline__ bool split_done_last(int* left, int* s_flag) {
 // the next item while the current item computes and publishes them in LDS
 // (double-buffered by item parity) before the current item's output stores,
 // so an item starts without a dependent chain of global loads.
-constexpr int kItemInts = 11;
+// The entries of a work item as the kernels keep them in LDS (ints, 16-byte
+// aligned groups): [0] the item, [4..7] its unit {sequence, tile, first step,
+// end step}, [8..11] the sequence's rows {tiled start, end, other start, end},
+// [12] partial slot, [13] split index.
+constexpr int kInfItem = 0, kInfUnit = 4, kInfRows = 8, kInfSlot = 12, kInfSplit = 13;
+constexpr int kItemInts = 16;
 struct ItemInfo {
-  int v[kItemInts];  // item, sequence, tile, first step, end step, tiled start/end, other start/end,
-                     // slot, split index
+  int v[kItemInts];
 };
 template <typename PlanT>
 __device__ __forceinline__ ItemInfo item_load(const PlanT& pl, int item, int per_unit, int total_items) {
   ItemInfo r;
-  r.v[0] = item;
+  r.v[kInfItem] = item;
   if (item < total_items) {
     const int unit = item / per_unit;
     const int4 un = pl.units[unit], bd = pl.bounds[unit];
-    r.v[1] = un.x; r.v[2] = un.y; r.v[3] = un.z; r.v[4] = un.w;
-    r.v[5] = bd.x; r.v[6] = bd.y; r.v[7] = bd.z; r.v[8] = bd.w;
-    r.v[9] = pl.slots[unit];
-    r.v[10] = pl.sidx[unit];
+    r.v[kInfUnit + 0] = un.x; r.v[kInfUnit + 1] = un.y; r.v[kInfUnit + 2] = un.z; r.v[kInfUnit + 3] = un.w;
+    r.v[kInfRows + 0] = bd.x; r.v[kInfRows + 1] = bd.y; r.v[kInfRows + 2] = bd.z; r.v[kInfRows + 3] = bd.w;
+    r.v[kInfSlot] = pl.slots[unit];
+    r.v[kInfSplit] = pl.sidx[unit];
   }
   return r;
 }
@@ -300,15 +316,18 @@ __device__ __forceinline__ void item_store(int* dst, const ItemInfo& r) {
   for (int i = 0; i < kItemInts; ++i) dst[i] = r.v[i];
 }
 
-// The next item of a workgroup (thread 0's copy): at(n, steps) is called
-// before step n of the current item's `steps` (and once with n = steps after
-// them); it takes the ticket at n >= steps - 2 and loads the item at
-// n >= steps - 1.  Items are numbered gridDim.x + ticket.
+// The next item of a workgroup, taken by thread 0: at(n, steps) is called
+// before step n of the current item's `steps`; it takes the ticket at
+// n >= steps - 2 and at n >= steps - 1 loads the item's plan entries
+// straight into the LDS entries `dst` (buffer loads with an LDS destination,
+// so no registers hold them across the steps).  finish(steps), after the
+// steps, waits for those loads; the item's closing barrier publishes them.
+// Items are numbered gridDim.x + ticket.
 template <typename PlanT>
 struct NextItem {
   const PlanT& pl;
   int per_unit, total_items;
-  ItemInfo info;
+  int* dst;
   int ticket = 0;
   bool asked = false, have = false;
   __device__ __forceinline__ void at(int n, int steps) {
@@ -318,9 +337,21 @@ struct NextItem {
       asked = true;
     }
     if (asked && !have && n >= steps - 1) {
-      info = item_load(pl, (int)gridDim.x + ticket, per_unit, total_items);
+      const int item = (int)gridDim.x + ticket;
+      dst[kInfItem] = item;
+      if (item < total_items) {
+        const int unit = item / per_unit;
+        lds_load_direct16(pl.units + unit, dst + kInfUnit);
+        lds_load_direct16(pl.bounds + unit, dst + kInfRows);
+        lds_load_direct4(pl.slots + unit, dst + kInfSlot);
+        lds_load_direct4(pl.sidx + unit, dst + kInfSplit);
+      }
       have = true;
     }
+  }
+  __device__ __forceinline__ void finish(int steps) {
+    at(steps, steps);
+    if ((threadIdx.x >> 6) == 0) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // thread 0's wave
   }
 };
 

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
   constexpr int WR = 32 * QT;                 // rows per wave
 
   __shared__ S sm;
-  __shared__ int s_info[2][kItemInts];
+  __shared__ __attribute__((aligned(16))) int s_info[2][kItemInts];
   __shared__ int s_last;  // this chunk of a split tile finished last
   // 16-bit bias with contiguous keys: the [BM rows][BN keys] tile of a block, loaded
   // a block ahead straight into LDS (double-buffered).  Row r keeps its 16-byte
@@ -163,15 +163,16 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
   __syncthreads();
   for (int cur = 0;; cur ^= 1) {
     const int* inf = s_info[cur];
-    const int item = uniform(inf[0]);
+    const int item = uniform(inf[kInfItem]);
     if (item >= total_items) break;
     const int unit = item / a.hq;
     const int h = item - unit * a.hq;
-    const int b = uniform(inf[1]), t = uniform(inf[2]);
-    const int n0 = uniform(inf[3]), n1 = uniform(inf[4]);
-    const int q0 = uniform(inf[5]), q1 = uniform(inf[6]), k0 = uniform(inf[7]), k1 = uniform(inf[8]);
-    const int slot = uniform(inf[9]);  // >= 0: a chunk of a split tile
-    const int si = uniform(inf[10]);   // that split tile
+    const int b = uniform(inf[kInfUnit]), t = uniform(inf[kInfUnit + 1]);
+    const int n0 = uniform(inf[kInfUnit + 2]), n1 = uniform(inf[kInfUnit + 3]);
+    const int q0 = uniform(inf[kInfRows]), q1 = uniform(inf[kInfRows + 1]), k0 = uniform(inf[kInfRows + 2]),
+              k1 = uniform(inf[kInfRows + 3]);
+    const int slot = uniform(inf[kInfSlot]);  // >= 0: a chunk of a split tile
+    const int si = uniform(inf[kInfSplit]);  // that split tile
     const int Lq = q1 - q0, Lk = k1 - k0;
     const int off = Lk - Lq;
     const int g = h / a.n_rep;
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     lds_barrier();  // every wave has read K(0) before K(2) replaces it
     // the next item: a ticket taken at the start of this item's second-to-last
     // block, its plan entries loaded during the last (thread 0)
-    NextItem<Plan> next_item{a.plan, a.hq, total_items};
+    NextItem<Plan> next_item{a.plan, a.hq, total_items, s_info[cur ^ 1]};
     auto fetch_next = [&](int n) __attribute__((always_inline)) { next_item.at(n, nb); };
 
     auto step = [&](auto mask_tag, int n) {  // n: block index inside the unit
@@ -721,16 +722,25 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
         for (int st = 0; st < NS; ++st) s_cur[0][st] = s_alt[0][st];
         ++j;
       }
-      for (; j + 1 < nb; j += 2) {
-        fetch_next(j);
-        step_fast(masked, j, s_cur, s_alt);
-        fetch_next(j + 1);
-        step_fast(masked, j + 1, s_alt, s_cur);
-      }
-      if (j < nb) {
-        fetch_next(j);
-        step_fast(masked, j, s_cur, s_alt);
-        ++j;
+      if constexpr (D <= 128) {
+        for (; j + 1 < nb; j += 2) {
+          fetch_next(j);
+          step_fast(masked, j, s_cur, s_alt);
+          fetch_next(j + 1);
+          step_fast(masked, j + 1, s_alt, s_cur);
+        }
+        if (j < nb) {
+          fetch_next(j);
+          step_fast(masked, j, s_cur, s_alt);
+          ++j;
+        }
+      } else {
+        // head_dim 256: the generic masked step (a second copy of the round
+        // schedule would not fit the register file)
+        for (; j < nb; ++j) {
+          fetch_next(j);
+          step(masked, j);
+        }
       }
     } else {
       for (; j < j_plain; ++j) {
@@ -742,8 +752,7 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
         step(std::integral_constant<bool, true>(), j);
       }
     }
-    fetch_next(nb);  // an item without blocks
-    if (tid == 0) item_store(s_info[cur ^ 1], next_item.info);  // before the output stores
+    next_item.finish(nb);
     ++kth;
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2.  A chunk of a split
@@ -805,8 +814,8 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
         const int sb = uniform(sp.z), nch = uniform(sp.w), me = slot - sb;  // first slot, chunks, this chunk
         // chunks in order with a running max (each chunk's LSE and O are loaded
         // together, so a chunk costs one round trip); at head dim 256 the output
-        // tiles go two at a time to bound the registers
-        constexpr int G = D <= 128 ? DT : 2;
+        // tiles go one at a time to bound the registers
+        constexpr int G = D <= 128 ? DT : 1;
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
           const int rl = rq[qt] - row_base;
@@ -821,34 +830,30 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
               for (int a4 = 0; a4 < 4; ++a4) mo[j][a4] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
             float m_run_c = -INFINITY, w_run = 0.f;
             for (int c = 0; c < nch; ++c) {
-              f32x4_t oc[G][4];
-              float lc;
-              if (c == me) {
-                lc = lse_v[qt];
+              const bool own = c == me;
+              const float lc = own ? lse_v[qt] : ld_dev(pl + (size_t)c * a.hq * BM);
+              const float m_new = fmaxf(m_run_c, lc);
+              const float a_old = m_run_c == -INFINITY ? 0.f : fast_exp2(m_run_c - m_new);
+              const float a_c = lc == -INFINITY ? 0.f : fast_exp2(lc - m_new);
+              w_run = w_run * a_old + a_c;
+              if (own) {
 #pragma unroll
                 for (int j = 0; j < G; ++j)
 #pragma unroll
                   for (int a4 = 0; a4 < 4; ++a4)
-                    oc[j][a4] = (f32x4_t){acc[qt][g0 + j][4 * a4], acc[qt][g0 + j][4 * a4 + 1],
-                                          acc[qt][g0 + j][4 * a4 + 2], acc[qt][g0 + j][4 * a4 + 3]};
+                    mo[j][a4] = mo[j][a4] * a_old +
+                                a_c * (f32x4_t){acc[qt][g0 + j][4 * a4], acc[qt][g0 + j][4 * a4 + 1],
+                                                acc[qt][g0 + j][4 * a4 + 2], acc[qt][g0 + j][4 * a4 + 3]};
               } else {
-                lc = ld_dev(pl + (size_t)c * a.hq * BM);
                 const rsrc_t cres =
                     make_rsrc(a.part_o + ((size_t)(sb + c) * a.hq + h) * SLOT_O, (int64_t)SLOT_O * 4);
 #pragma unroll
                 for (int j = 0; j < G; ++j)
 #pragma unroll
                   for (int a4 = 0; a4 < 4; ++a4)
-                    oc[j][a4] = buf_load16_dev(cres, (rl * D + 32 * (g0 + j) + 8 * a4 + 4 * hh) * 4);
+                    mo[j][a4] = mo[j][a4] * a_old +
+                                a_c * buf_load16_dev(cres, (rl * D + 32 * (g0 + j) + 8 * a4 + 4 * hh) * 4);
               }
-              const float m_new = fmaxf(m_run_c, lc);
-              const float a_old = m_run_c == -INFINITY ? 0.f : fast_exp2(m_run_c - m_new);
-              const float a_c = lc == -INFINITY ? 0.f : fast_exp2(lc - m_new);
-              w_run = w_run * a_old + a_c;
-#pragma unroll
-              for (int j = 0; j < G; ++j)
-#pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) mo[j][a4] = mo[j][a4] * a_old + a_c * oc[j][a4];
               m_run_c = m_new;
             }
 #pragma unroll
