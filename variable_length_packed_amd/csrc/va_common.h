@@ -228,6 +228,14 @@ __device__ __forceinline__ void lds_load_direct4(const void* src, void* lds) {
   const rsrc_t r = make_rsrc(src, 4);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, 0, 0, 0, 0);
 }
+// The same from a resource over a whole array (kernel-argument base, so the
+// resource sits in scalar registers) at byte offset off.
+__device__ __forceinline__ void lds_load_direct16_at(rsrc_t r, int off, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load_direct4_at(rsrc_t r, int off, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
+}
 
 // s_waitcnt operand that waits until at most n vector memory operations of
 // the wave are outstanding (n < 64), other counters untouched.
@@ -340,11 +348,11 @@ struct NextItem {
       const int item = (int)gridDim.x + ticket;
       dst[kInfItem] = item;
       if (item < total_items) {
-        const int unit = item / per_unit;
-        lds_load_direct16(pl.units + unit, dst + kInfUnit);
-        lds_load_direct16(pl.bounds + unit, dst + kInfRows);
-        lds_load_direct4(pl.slots + unit, dst + kInfSlot);
-        lds_load_direct4(pl.sidx + unit, dst + kInfSplit);
+        const int unit = item / per_unit, units = total_items / per_unit;
+        lds_load_direct16_at(make_rsrc(pl.units, (int64_t)units * 16), unit * 16, dst + kInfUnit);
+        lds_load_direct16_at(make_rsrc(pl.bounds, (int64_t)units * 16), unit * 16, dst + kInfRows);
+        lds_load_direct4_at(make_rsrc(pl.slots, (int64_t)units * 4), unit * 4, dst + kInfSlot);
+        lds_load_direct4_at(make_rsrc(pl.sidx, (int64_t)units * 4), unit * 4, dst + kInfSplit);
       }
       have = true;
     }

@@ -40,7 +40,9 @@ struct FwdSmem {
   // K and V blocks: [BN][D] row-major as in memory, row pitch padded by 16
   // bytes.  bf16 V^T fragments come from transposing LDS reads.
   static constexpr int KP = D + 16 / (int)sizeof(T);
-  static constexpr int VP = KP;
+  // V rows: the pitch that keeps the transposing V^T reads of a wave on
+  // distinct banks (head_dim a multiple of 64: 64 bytes of padding; 32, 96: none)
+  static constexpr int VP = H16 ? D + (D % 64 == 0 ? 32 : 0) : KP;
   T k[2][BN * KP];
   T v[2][BN * VP];
 };
@@ -524,13 +526,14 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
     // invisible keys become -inf before the row max, and a wave none of whose
     // rows sees the block skips the arithmetic (its later blocks are invisible
     // too, so the S it would compute is never used).
-    auto step_fast = [&](auto mask_tag, int n, f32x16_t (&sc)[QT][NS], f32x16_t (&sn)[QT][NS])
+    // par: n & 1 (a literal where the caller knows it, so the buffer offsets fold)
+    auto step_fast = [&](auto mask_tag, int n, int par, f32x16_t (&sc)[QT][NS], f32x16_t (&sn)[QT][NS])
                          __attribute__((always_inline)) {
       if constexpr (QT == 1 && H16 && !HAS_BIAS && QF % NCH == 0) {
       constexpr bool MASK = decltype(mask_tag)::value;
       constexpr int KPR = QF / NCH;  // S k-steps per round
       const int kb = kb0 + n * BN;
-      const int kbuf = (n + 1) & 1, vbuf = n & 1;
+      const int kbuf = par ^ 1, vbuf = par;
       ld.load_k(kres, krow_bytes, kb + 2 * BN);  // past the last block every row reads as zero
       ld.load_v(vres, vrow_bytes, kb + BN);
       if (!MASK || (wave_on && kb < wave_hi)) {
@@ -615,8 +618,8 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       __builtin_amdgcn_sched_barrier(0);
       l_run[0] += ps0 + ps1;
       }
-      ld.store_k(sm, n & 1);
-      ld.store_v(sm, (n + 1) & 1);
+      ld.store_k(sm, par);
+      ld.store_v(sm, par ^ 1);
       lds_barrier();
       }
     };
@@ -709,15 +712,16 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       f32x16_t s_alt[QT][NS];
       const std::integral_constant<bool, false> plain;
       const std::integral_constant<bool, true> masked;
+      // j is even here and in the single step after the pairs
       for (; j + 1 < j_plain; j += 2) {
         fetch_next(j);
-        step_fast(plain, j, s_cur, s_alt);
+        step_fast(plain, j, 0, s_cur, s_alt);
         fetch_next(j + 1);
-        step_fast(plain, j + 1, s_alt, s_cur);
+        step_fast(plain, j + 1, 1, s_alt, s_cur);
       }
       if (j < j_plain) {
         fetch_next(j);
-        step_fast(plain, j, s_cur, s_alt);
+        step_fast(plain, j, 0, s_cur, s_alt);
 #pragma unroll
         for (int st = 0; st < NS; ++st) s_cur[0][st] = s_alt[0][st];
         ++j;
@@ -725,13 +729,13 @@ __global__ __launch_bounds__(NT, (min_blocks<H16, D>())) void fwd_kernel(FwdArgs
       if constexpr (D <= 128) {
         for (; j + 1 < nb; j += 2) {
           fetch_next(j);
-          step_fast(masked, j, s_cur, s_alt);
+          step_fast(masked, j, j & 1, s_cur, s_alt);
           fetch_next(j + 1);
-          step_fast(masked, j + 1, s_alt, s_cur);
+          step_fast(masked, j + 1, (j + 1) & 1, s_alt, s_cur);
         }
         if (j < nb) {
           fetch_next(j);
-          step_fast(masked, j, s_cur, s_alt);
+          step_fast(masked, j, j & 1, s_cur, s_alt);
           ++j;
         }
       } else {

@@ -35,7 +35,7 @@ void set_error(const char* msg);
 // rest of the batch.  Units are listed by step count, largest first.
 // ---------------------------------------------------------------------------
 struct Plan {
-  int* hdr;        // [0] unused (written 0), [1] units, [2] split tiles
+  int* hdr;        // [0] work cursor (written 0), [1] units, [2] split tiles
   int4* units;     // [unit_cap] {sequence, tile, first step, end step}
   int4* bounds;    // [unit_cap] the sequence's rows: {tiled start, end, other start, end}
   int* slots;      // [unit_cap] partial slot of a chunk of a split tile, or -1
