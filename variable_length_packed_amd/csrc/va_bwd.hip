@@ -88,6 +88,16 @@ struct Stager {
       *(u32x4_t*)(dn + row * NP + c * EPV) = r[i];
     }
   }
+  // the same rows unpadded, in the swizzled order of swz()
+  __device__ __forceinline__ void store_swz(T* __restrict__ dn) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int u = threadIdx.x + i * NT;
+      if (TASKS % NT != 0 && u >= TASKS) continue;
+      const int c = u % CH, row = u / CH;
+      *(u32x4_t*)(dn + swz<D>(row, c * EPV)) = r[i];
+    }
+  }
 };
 
 // Register fragment of this lane's row for the "other" operand of a 32x32
@@ -374,7 +384,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
     };
     // direct staging: block rn's Q and dO rows into buffer b3 (wave w's load i fills
     // slots (i * 4 + w) * 64 .. +63 of the tile: row = slot / PR, its piece
-    // (slot % PR) ^ (row % 8)), and the raw LSE (wave 0) and dsum (wave 1) of its
+    // (slot % PR) ^ swz_key(row)), and the raw LSE (wave 0) and dsum (wave 1) of its
     // queries; each wave issues NI_D loads per tensor, waves 0 and 1 one more
     constexpr int PR = D * 2 / 16;      // 16-byte pieces per row
     constexpr int NI_D = BMQ * PR / NT;  // loads per thread per tensor
@@ -391,7 +401,7 @@ __global__ __launch_bounds__(NT, (dkdv_min_blocks<H16, D>())) void dkdv_kernel(B
 #pragma unroll
         for (int i = 0; i < NI_D; ++i) {
           const int base = (i * (NT / 64) + wid) * 64;  // first slot of this wave's load
-          const int u = base + lane, row = u / PR, piece = (u % PR) ^ (row & 7);
+          const int u = base + lane, row = u / PR, piece = (u % PR) ^ swz_key<D>(row);
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               qres, (__attribute__((address_space(3))) void*)(sm.qn[b3] + base * 8), 16,
               (qb + row) * qrow_bytes + piece * 16, 0, 0, 0);
@@ -792,6 +802,11 @@ __global__ __launch_bounds__(NT, (dq_min_blocks<D>())) void dq_kernel(BwdArgs a)
   using SM = DqSmem<H16, D>;
   constexpr int BN = SM::BN;
   constexpr int NS = BN / 32;
+  // 16-bit, no bias, two 32-key score tiles per block: the explicit-order step (FAST);
+  // at head_dim 64 its K tiles are staged swizzled, conflict-free for both the row
+  // reads of S and the transposing reads of dQ += dS K
+  constexpr bool FAST = H16 && !HAS_BIAS && NS == 2;
+  constexpr bool KSWZ = FAST && D == 64;
   constexpr int DT = D / 32;
   constexpr int ELT = (int)sizeof(T);
   using St = typename SM::St;
@@ -899,15 +914,18 @@ __global__ __launch_bounds__(NT, (dq_min_blocks<D>())) void dq_kernel(BwdArgs a)
         sk.load(kres, krow_bytes, kb + BN);
         sv.load(vres, vrow_bytes, kb + BN);
       }
-      // 16-bit, no bias, two 32-key score tiles per block: the tiles' MFMAs and the
-      // vector work of the softmax gradient in an explicit order -- the fragments of
-      // tile 1 are read under tile 0's MFMAs, tile 1's MFMAs run under tile 0's
-      // exponentials, and the dQ MFMAs of tile 0's keys under tile 1's
-      constexpr bool FAST = H16 && !HAS_BIAS && NS == 2;
+      // FAST: the tiles' MFMAs and the vector work of the softmax gradient in an
+      // explicit order -- the fragments of tile 1 are read under tile 0's MFMAs, tile
+      // 1's MFMAs run under tile 0's exponentials, and the dQ MFMAs of tile 0's keys
+      // under tile 1's
       if constexpr (FAST) {
         if (wave_on && kb < wave_hi) {
           constexpr int KS = D / 16;  // k-steps over head_dim
-          const T* kr = &sm.kn[buf][r32 * St::NP + 8 * hh];
+          // K rows: swizzled (head_dim 64) or padded; row r32 (+32 for tile 1), piece 2 ks + hh
+          auto kfrag = [&](int row, int ks) __attribute__((always_inline)) {
+            if constexpr (KSWZ) return *(const u32x4_t*)&sm.kn[buf][swz<D>(row, 16 * ks + 8 * hh)];
+            else return *(const u32x4_t*)&sm.kn[buf][row * St::NP + 16 * ks + 8 * hh];
+          };
           const T* vr = &sm.vn[buf][r32 * St::NP + 8 * hh];
           u32x4_t kf[2][KS], vf[2][KS];
           f32x16_t s2[2] = {(f32x16_t){}, (f32x16_t){}}, dp2[2] = {ndsum16, ndsum16};
@@ -927,13 +945,17 @@ __global__ __launch_bounds__(NT, (dq_min_blocks<D>())) void dq_kernel(BwdArgs a)
           };
           auto dq_mma = [&](int kc) __attribute__((always_inline)) {
 #pragma unroll
-            for (int dt_ = 0; dt_ < DT; ++dt_)
-              acc[dt_] = mfma16<H16>(tr_frag(sm.kn[buf], St::NP, kc, 32 * dt_), pbs[kc], acc[dt_]);
+            for (int dt_ = 0; dt_ < DT; ++dt_) {
+              u32x4_t kt;
+              if constexpr (KSWZ) kt = tr_frag_swz<D>(sm.kn[buf], kc, 32 * dt_);
+              else kt = tr_frag(sm.kn[buf], St::NP, kc, 32 * dt_);
+              acc[dt_] = mfma16<H16>(kt, pbs[kc], acc[dt_]);
+            }
           };
           // tile 0's fragments
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            kf[0][ks] = *(const u32x4_t*)(kr + 16 * ks);
+            kf[0][ks] = kfrag(r32, ks);
             vf[0][ks] = *(const u32x4_t*)(vr + 16 * ks);
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -941,7 +963,7 @@ __global__ __launch_bounds__(NT, (dq_min_blocks<D>())) void dq_kernel(BwdArgs a)
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             s2[0] = mfma16<H16>(kf[0][ks], qf.b[ks], s2[0]);
-            kf[1][ks] = *(const u32x4_t*)(kr + 32 * St::NP + 16 * ks);
+            kf[1][ks] = kfrag(32 + r32, ks);
             dp2[0] = mfma16<H16>(vf[0][ks], of.b[ks], dp2[0]);
             vf[1][ks] = *(const u32x4_t*)(vr + 32 * St::NP + 16 * ks);
           }
@@ -1056,7 +1078,8 @@ __global__ __launch_bounds__(NT, (dq_min_blocks<D>())) void dq_kernel(BwdArgs a)
         }
       }
       if (n + 1 < n1) {
-        sk.store(sm.kn[buf ^ 1]);
+        if constexpr (KSWZ) sk.store_swz(sm.kn[buf ^ 1]);
+        else sk.store(sm.kn[buf ^ 1]);
         sv.store(sm.vn[buf ^ 1]);
       }
       lds_barrier();
@@ -1065,7 +1088,8 @@ __global__ __launch_bounds__(NT, (dq_min_blocks<D>())) void dq_kernel(BwdArgs a)
     if (n1 > n0) {
       sk.load(kres, krow_bytes, n0 * BN);
       sv.load(vres, vrow_bytes, n0 * BN);
-      sk.store(sm.kn[0]);
+      if constexpr (KSWZ) sk.store_swz(sm.kn[0]);
+      else sk.store(sm.kn[0]);
       sv.store(sm.vn[0]);
     }
     // every load so far (Q and dO fragments included) has landed: the steps below then

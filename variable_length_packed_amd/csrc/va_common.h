@@ -201,19 +201,32 @@ __device__ __forceinline__ u32x4_t tr_frag(const uint16_t* tile, int pitch, int 
 // Tiles staged straight from memory into LDS (buffer loads with an LDS
 // destination write each wave's 64 x 16 bytes contiguously) keep their rows
 // unpadded: row r of D 16-bit elements holds its 16-byte piece p in slot
-// p ^ (r % 8), so eight rows read at the same column fall in different banks.
+// p ^ swz_key(r).  The LDS has 64 four-byte banks, so a 128-byte row (D = 64)
+// covers half of them (odd rows the other half) and a 256-byte row (D = 128)
+// all of them.  The key keeps both read patterns free of bank conflicts:
+//  - 16-byte row reads (16 lanes at a time: rows r0 .. r0+15, one piece):
+//    the key is a bijection over the rows that share a bank half;
+//  - transposing 8-byte reads (32 lanes at a time: rows r0 .. r0+3, r0 a
+//    multiple of 4, pieces 4m .. 4m+3): rows of one bank half land in
+//    different aligned groups of four slots.
+template <int D>
+__device__ __forceinline__ int swz_key(int r) {
+  static_assert(D == 64 || D == 128, "swizzled tiles have 8 or 16 pieces per row");
+  if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
 // Element offset of (row r, column col), col a multiple of 4.
 template <int D>
 __device__ __forceinline__ int swz(int r, int col) {
-  return r * D + (((col >> 3) ^ (r & 7)) << 3) + (col & 7);
+  return r * D + (((col >> 3) ^ swz_key<D>(r)) << 3) + (col & 7);
 }
 // tr_frag of such a tile (rows 16 kc + ..., columns c0 + l % 32).
 template <int D>
 __device__ __forceinline__ u32x4_t tr_frag_swz(const uint16_t* tile, int kc, int c0) {
   const int lane = threadIdx.x & 63;
-  const uint16_t* p = tile + swz<D>(16 * kc + 4 * (lane >> 5) + ((lane >> 2) & 3),
-                                    c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-  const u32x2_t lo = lds_read_tr16(p), hi = lds_read_tr16(p + 8 * D);  // row + 8: the same slot order
+  const int row = 16 * kc + 4 * (lane >> 5) + ((lane >> 2) & 3);
+  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const u32x2_t lo = lds_read_tr16(tile + swz<D>(row, col)), hi = lds_read_tr16(tile + swz<D>(row + 8, col));
   return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
 }
 
