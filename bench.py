@@ -480,7 +480,7 @@ def main() -> int:
                                 "fwd+bwd step, fp32 grads", "steps": {}}
         for vname, vdt, vd, fused in (("f16", "f16", 64, False), ("bf16 fused qkv", "bf16", 64, True),
                                       ("bf16 d32", "bf16", 32, False), ("bf16 d96", "bf16", 96, False),
-                                      ("bf16 d256", "bf16", 256, False)):
+                                      ("bf16 d128", "bf16", 128, False), ("bf16 d256", "bf16", 256, False)):
             wv = make_case(3, w.lens_q, hq=w.hq, hkv=w.hkv, d=vd, causal=True, dtype=vdt, with_dout=True)
             tdv = torch.float16 if vdt == "f16" else torch.bfloat16
             tv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(tdv)
