@@ -47,7 +47,13 @@ struct KvShape {
   static constexpr int KB = D == 32 ? 64 : D == 96 ? 32 : 4096 / D;
   static_assert(KB % 32 == 0 && KB * D / 8 % 64 == 0, "steps of whole tiles and whole wave loads");
   static constexpr int NS = KB / 32;   // 32-key score tiles per step
-  static constexpr int VP = D + 8;     // LDS row pitch of the staged V block (elements)
+  // LDS row pitches (elements) of the staged K and V blocks: K is read by rows
+  // (16-byte reads, conflict-free at D + 8), V by transposing 8-byte reads, whose
+  // 32 lanes at a time touch four consecutive rows and are conflict-free on the 64
+  // banks at pitch D for d = 32 and 96 and D + 32 for d = 128; at d = 64 the
+  // conflict-free pitch (96) would not leave room for two workgroups per CU
+  static constexpr int KP = D + 8;
+  static constexpr int VP = D == 32 || D == 96 ? D : D == 128 ? D + 32 : D + 8;
   static constexpr int KS = D / 16;    // MFMA k-steps over head_dim
   static constexpr int DT = D / 32;    // 32-wide tiles of head_dim in O^T
 };
@@ -80,8 +86,8 @@ template <int H16, int D, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
   constexpr bool BIGPAGE = MODE == kPagedBig, RAGGED = MODE == kRagged;
   using SH = KvShape<D>;
-  constexpr int KB = SH::KB, NS = SH::NS, VP = SH::VP, KS = SH::KS, DT = SH::DT;
-  __shared__ uint16_t sk_all[4][KB * VP];
+  constexpr int KB = SH::KB, NS = SH::NS, KP = SH::KP, VP = SH::VP, KS = SH::KS, DT = SH::DT;
+  __shared__ uint16_t sk_all[4][KB * KP];
   __shared__ uint16_t sv_all[4][KB * VP];
 
   const int lane = threadIdx.x & 63;
@@ -212,7 +218,7 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
     // them are done: one wave's LDS operations complete in order)
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      *(u32x4_t*)(sk + prow(i) * VP + pcol(i)) = kr[i];
+      *(u32x4_t*)(sk + prow(i) * KP + pcol(i)) = kr[i];
       *(u32x4_t*)(sv + prow(i) * VP + pcol(i)) = vr[i];
     }
     // the next step's K and V are in flight during all of this step's work
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
       s[st] = (f32x16_t){};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const u32x4_t kf = *(const u32x4_t*)(sk + (32 * st + r32) * VP + 16 * ks + 8 * hh);
+        const u32x4_t kf = *(const u32x4_t*)(sk + (32 * st + r32) * KP + 16 * ks + 8 * hh);
         s[st] = mfma16<H16>(kf, qf[ks], s[st]);
       }
     }
