@@ -444,8 +444,10 @@ def main() -> int:
                          dtype=torch.uint8, device=dev)
         sc_k = 1.0 / float(np.sqrt(shk["d"]))
 
+        cu_dec, sk_dec, bt_dec = kv["cu"], kv["sk"], kv["btd"]
+
         def decode():
-            va.kvcache_fwd(kv["q"], kv["kc"], kv["vc"], kv["cu"], kv["sk"], kv["btd"], 1, mk, sc_k, True,
+            va.kvcache_fwd(kv["q"], kv["kc"], kv["vc"], cu_dec, sk_dec, bt_dec, 1, mk, sc_k, True,
                            out=ok, lse=lk, workspace=wk)
 
         for _ in range(3):
@@ -471,7 +473,28 @@ def main() -> int:
                          "algorithmic_bytes": kv_bytes + io_bytes,
                          "traffic": measured_traffic("kvcache_bf16", "decode")},
         }
+        # the same step with float32 Q, caches and output (the float32 MFMA kernel): twice the bytes
+        q32, kc32, vc32 = kv["q"].float(), kv["kc"].float(), kv["vc"].float()
         del kv
+        o32 = torch.empty_like(q32)
+
+        def decode32():
+            va.kvcache_fwd(q32, kc32, vc32, cu_dec, sk_dec, bt_dec, 1, mk, sc_k, True, out=o32, lse=lk, workspace=wk)
+
+        for _ in range(3):
+            decode32()
+        ms32 = timed(decode32, args.steps)
+        va.va_timing_start(8 * args.steps + 8)
+        for _ in range(args.steps):
+            decode32()
+        kt32 = va.va_timing_stop()
+        k32_ms = kt32["kvcache_f32"][1] / kt32["kvcache_f32"][0]
+        b32 = 2 * kv_bytes + 2 * io_bytes - lk.numel() * 4
+        kvcache_decode["float32"] = {"ms_per_step": round(ms32, 5), "kernel_ms": round(k32_ms, 5),
+                                     "algorithmic_bytes": b32,
+                                     "kernel_GB_s": round(b32 / (k32_ms * 1e-3) / 1e9, 1),
+                                     "frac_hbm": round(b32 / (k32_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        del q32, kc32, vc32, o32
 
     # the main step's lengths under other input kinds: float16, Q/K/V read in place from
     # one fused projection output, and head_dim 32 / 96 / 256 (same heads and lengths)

@@ -303,9 +303,10 @@ def _kv(lib, **kw):
     (dict(ws=None), INVALID),
     (dict(ws=P + 64), INVALID),        # misaligned workspace
     (dict(wsb=16), WORKSPACE),
-    (dict(dt=F32), UNSUPPORTED),
+    (dict(dt=7), UNSUPPORTED),
     (dict(d=80), UNSUPPORTED),
     (dict(mq=1 << 20, hq=64, hkv=8), UNSUPPORTED),  # a sequence's queries span 2^31 bytes
+    (dict(mq=1 << 16, hq=64, hkv=8, dt=F32), UNSUPPORTED),  # 2^31 bytes in float32 (2^30 in bf16)
 ])
 def test_kvcache_validation(lib, kw, code):
     assert _kv(lib, **kw) == code
@@ -318,7 +319,10 @@ def test_kvcache_workspace_size(lib):
     for d in (32, 64, 96, 128):
         assert f(2, 1, 128, 8, 2, d, BF16) > 0
     assert f(2, 1, 128, 8, 2, 80, BF16) == 0 and f(2, 1, 128, 8, 2, 256, BF16) == 0
-    assert f(2, 1, 128, 8, 2, 128, F32) == 0         # not a decode dtype
+    # float32 steps use the same work list and float32 partials: the same size
+    assert f(2, 1, 128, 8, 2, 128, F32) == f(2, 1, 128, 8, 2, 128, BF16) > 0
+    assert f(2, 1, 128, 8, 2, 128, 5) == 0             # not a dtype
+    assert f(2, 1 << 16, 128, 64, 8, 128, BF16) > 0 and f(2, 1 << 16, 128, 64, 8, 128, F32) == 0
     assert f(2, 1, 128, 8, 3, 128, BF16) == 0
 
     def plan(entries, split=False):

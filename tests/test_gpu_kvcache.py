@@ -1,7 +1,7 @@
 """GPU parity of decode steps against a paged KV cache (include/va_kvcache.h) with the oracle.
 
 Single-token steps and multi-token steps (beams, drafts), causal and not,
-GQA, MQA and MHA, head_dim 32, 64, 96 and 128, bf16 and float16, pages of 1 to 256
+GQA, MQA and MHA, head_dim 32, 64, 96 and 128, bf16, float16 and float32, pages of 1 to 256
 keys handed out in random order, empty caches, sequences with no new token,
 caches shorter than the new tokens (rows that see no key), caches long enough
 to split into tens of chunks, and the full decode workload the bench times
@@ -23,7 +23,7 @@ from . import _gpu
 pytestmark = pytest.mark.gpu
 
 DEV = _gpu.DEV
-_DT = {"bf16": torch.bfloat16, "f16": torch.float16}
+_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 CASES = [
     ("decode-gqa4-d128-p16", dict(seed=1, lens_q=[1] * 6, lens_k=[1, 17, 300, 1000, 4000, 0], hq=32, hkv=8,
@@ -55,6 +55,16 @@ CASES = [
                                           dtype="f16", page_size=32)),
     ("beam5-noncausal-d96-p128", dict(seed=18, lens_q=[5, 3], lens_k=[777, 40], hq=6, hkv=3, d=96,
                                       dtype="bf16", page_size=128, causal=False)),
+    # float32 caches (the float32 MFMA kernel, 32-key steps): every head dim, pages smaller
+    # and larger than a step, split caches merged, beams without a mask
+    ("decode-gqa4-d128-f32-p16-split", dict(seed=21, lens_q=[1] * 5, lens_k=[1, 17, 300, 4000, 0], hq=32, hkv=8,
+                                            d=128, dtype="f32", page_size=16)),
+    ("draft3-mqa-d64-f32-p8-split", dict(seed=22, lens_q=[3, 1, 2], lens_k=[9000, 5, 700], hq=8, hkv=1, d=64,
+                                         dtype="f32", page_size=8)),
+    ("beam5-noncausal-d32-f32-p64", dict(seed=23, lens_q=[5, 3], lens_k=[777, 40], hq=6, hkv=3, d=32,
+                                         dtype="f32", page_size=64, causal=False)),
+    ("decode-gqa4-d96-f32-p4", dict(seed=24, lens_q=[1] * 4, lens_k=[31, 32, 33, 2500], hq=16, hkv=4, d=96,
+                                    dtype="f32", page_size=4)),
 ]
 
 

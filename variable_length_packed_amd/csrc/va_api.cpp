@@ -277,8 +277,8 @@ bool short_query(va_dtype dtype, int d, int max_q, int n_rep) {
 bool kv_args_ok(int32_t batch, int32_t max_q, int32_t max_k, int32_t hq, int32_t hkv, int32_t d,
                 va_dtype dtype) {
   return batch > 0 && max_q > 0 && max_k >= 0 && hq > 0 && hkv > 0 && hq % hkv == 0 &&
-         decode_head_dim(d) && (dtype == VA_BF16 || dtype == VA_F16) &&
-         (int64_t)max_q * hq * d * 2 < ((int64_t)1 << 31);
+         decode_head_dim(d) && (dtype == VA_BF16 || dtype == VA_F16 || dtype == VA_F32) &&
+         (int64_t)max_q * hq * d * (dtype == VA_F32 ? 4 : 2) < ((int64_t)1 << 31);
 }
 
 // kernel element code: 0 float32, 1 bfloat16, 2 float16
@@ -616,12 +616,12 @@ va_status va_kvcache_fwd(const void* q, const void* k_cache, const void* v_cache
     return fail(VA_ERR_INVALID, "softmax_scale must be finite and > 0");
   if ((((uintptr_t)q) | ((uintptr_t)k_cache) | ((uintptr_t)v_cache) | ((uintptr_t)out)) % 16 != 0)
     return fail(VA_ERR_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned");
-  if (dtype != VA_BF16 && dtype != VA_F16)
-    return fail(VA_ERR_UNSUPPORTED, "decode steps take bf16 or float16 (got dtype %d)", (int)dtype);
+  if (dtype != VA_BF16 && dtype != VA_F16 && dtype != VA_F32)
+    return fail(VA_ERR_UNSUPPORTED, "decode steps take bf16, float16 or float32 (got dtype %d)", (int)dtype);
   if (!decode_head_dim(head_dim))
     return fail(VA_ERR_UNSUPPORTED, "head_dim %d not supported in decode steps (32, 64, 96 or 128)", head_dim);
   if (!kv_args_ok(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim, dtype))
-    return fail(VA_ERR_UNSUPPORTED, "max_seqlen_q * num_heads_q * head_dim * 2 must be < 2^31");
+    return fail(VA_ERR_UNSUPPORTED, "max_seqlen_q * num_heads_q * head_dim * element size must be < 2^31");
   const KvLayout L = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim);
   const size_t need = L.total();
   if (!workspace) return fail(VA_ERR_INVALID, "workspace is NULL");

@@ -320,6 +320,224 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
   }
 }
 
+// The float32 decode kernel: the same items, paging, chunks and online softmax
+// as kv_decode_kernel, on the float32 MFMA (32x32x2, two k-slots a lane).
+//  - Q: lane l keeps dims 8G + 4hh + j of its row (k-slot (G, j)) in
+//    registers; K rows are staged in the wave's LDS slice and read 16 bytes
+//    at a time (dims 8G + 4hh .. +3 of key r32), so the two k-slots of one
+//    MFMA are dims 8G + j and 8G + 4 + j for K and Q alike.
+//  - P never leaves registers: register i of a score tile holds key
+//    8(i/4) + 4hh + i%4 of the lane's row, which is the B operand of
+//    O^T += V^T P^T with those two keys as k-slots; the A operand is one V
+//    element per lane (dim 32 dt + r32 of that key) read from the V slice.
+//  - 32-key steps; LDS pitches d + 4 (K: sixteen 16-byte row reads at a time
+//    touch 64 distinct banks) and d + 8 (V: the two rows an element read
+//    touches, k and k + 4, fall in opposite bank halves).  At d = 96 and 128
+//    a workgroup's slices need more than half of the LDS and the staging
+//    registers more than half of the register file: one workgroup per CU.
+template <int D>
+struct KvShapeF32 {
+  static constexpr int KB = 32;
+  static constexpr int KP = D + 4, VP = D + 8;
+  static constexpr int G8 = D / 8;   // 8-dim groups of Q (4 k-slot pairs each)
+  static constexpr int DT = D / 32;
+  static constexpr int LPR = D / 4;  // 16-byte pieces per row
+  static constexpr int NI = KB * LPR / 64;
+  static_assert(KB * LPR % 64 == 0, "whole wave loads");
+};
+template <int D>
+constexpr int kv_f32_blocks() { return D <= 64 ? 2 : 1; }
+
+template <int D, bool CAUSAL, int MODE>
+__global__ __launch_bounds__(KNT, (kv_f32_blocks<D>())) void kv_decode_f32_kernel(KvArgs a) {
+  constexpr bool BIGPAGE = MODE == kPagedBig, RAGGED = MODE == kRagged;
+  using SH = KvShapeF32<D>;
+  constexpr int KB = SH::KB, KP = SH::KP, VP = SH::VP, G8 = SH::G8, DT = SH::DT, LPR = SH::LPR, NI = SH::NI;
+  __shared__ __attribute__((aligned(16))) float sk_all[4][KB * KP];
+  __shared__ __attribute__((aligned(16))) float sv_all[4][KB * VP];
+
+  const int lane = threadIdx.x & 63;
+  const int wid = uniform(threadIdx.x >> 6);
+  const int hh = lane >> 5;
+  const int r32 = lane & 31;
+  float* sk = sk_all[wid];
+  float* sv = sv_all[wid];
+
+  const int n_items = uniform(a.plan[0]) * a.hkv;
+  const int n_waves = (int)gridDim.x * 4;
+  auto entry = [&](int it) {
+    return it < n_items ? a.chunks[it / a.hkv] : (KvChunk){0, 0, 0, 0, 0, 0, 0, 1};
+  };
+  KvChunk nxt = entry((int)blockIdx.x * 4 + wid);
+  for (int item = (int)blockIdx.x * 4 + wid; item < n_items; item += n_waves) {
+  const KvChunk ent = nxt;
+  nxt = entry(item + n_waves);
+  const int g = item % a.hkv;
+  const int b = uniform(ent.b), rb = uniform(ent.rb), c = uniform(ent.c);
+  const int q0 = uniform(ent.q0), q1 = uniform(ent.q1), Lk = uniform(ent.lk), k0 = uniform(ent.k0);
+  const int chunk = uniform(ent.chunk);
+  const size_t slot = (size_t)item;
+  const int Lq = q1 - q0;
+  const int nch = max(1, (Lk + chunk - 1) / chunk);
+  const int off = Lk - Lq;
+
+  const int r = rb * a.rows + r32;
+  const int qpos = r / a.n_rep;
+  const int h = g * a.n_rep + (r - qpos * a.n_rep);
+  const bool row_ok = r32 < a.rows && qpos < Lq;
+  const int qpos_first = (rb * a.rows) / a.n_rep;
+  const int qpos_last = min(Lq - 1, (rb * a.rows + a.rows - 1) / a.n_rep);
+  const int kbeg = c * chunk;
+  int kend = min(Lk, kbeg + chunk);
+  if (CAUSAL) kend = min(kend, qpos_last + off + 1);
+  const int nsteps = kend > kbeg ? (kend - kbeg + KB - 1) / KB : 0;
+  int plain_end = kend;
+  if (CAUSAL) plain_end = min(plain_end, qpos_first + off + 1);
+  const int nplain = plain_end > kbeg ? (plain_end - kbeg) / KB : 0;
+  const int hi = !row_ok ? -1 : (CAUSAL ? min(kend - 1, qpos + off) : kend - 1);
+
+  // ---- Q (the B operand of S^T = K Q^T); rows past the sequence read 0
+  const size_t qrow = (size_t)a.q_rs;
+  const rsrc_t qres = make_rsrc((const float*)a.q + (size_t)q0 * qrow, (int64_t)Lq * qrow * 4);
+  float qf[4 * G8];
+#pragma unroll
+  for (int G = 0; G < G8; ++G) {
+    const u32x4_t z = buf_load16(qres, (int)((qpos * qrow + h * D + 8 * G + 4 * hh) * 4));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qf[4 * G + j] = __uint_as_float(z[j]);
+  }
+
+  // ---- cache rows: coalesced 16-byte pieces, load i covering pieces 64i .. 64i+63
+  auto prow = [&](int i) { return (64 * i + lane) / LPR; };
+  auto pcol = [&](int i) { return (64 * i + lane) % LPR * 4; };
+  const float* __restrict__ kc = (const float*)a.k_cache;
+  const float* __restrict__ vc = (const float*)a.v_cache;
+  const int32_t* __restrict__ bt = RAGGED ? nullptr : a.block_table + (size_t)b * a.bt_stride;
+  const int pmask = (1 << a.page_shift) - 1;
+  auto key_of = [&](int n, int i) { return min(kbeg + n * KB + prow(i), kend - 1); };
+  constexpr int NPG = BIGPAGE || RAGGED ? 1 : NI;
+  int pg[NPG];
+  auto fetch_pages = [&](int n) __attribute__((always_inline)) {
+    if constexpr (RAGGED) {
+      pg[0] = 0;
+    } else if constexpr (BIGPAGE) {
+      pg[0] = bt[uniform(kbeg + n * KB) >> a.page_shift];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) pg[i] = bt[key_of(n, i) >> a.page_shift];
+    }
+  };
+  u32x4_t kr[NI], vr[NI];
+  auto load_kv = [&](int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      int64_t row;
+      if constexpr (RAGGED) {
+        row = (int64_t)k0 + key_of(n, i);
+      } else {
+        const int page = min(max(pg[BIGPAGE ? 0 : i], 0), a.num_pages - 1);
+        row = ((int64_t)page << a.page_shift) + (key_of(n, i) & pmask);
+      }
+      kr[i] = __builtin_nontemporal_load((const u32x4_t*)(kc + row * a.k_rs + g * D + pcol(i)));
+      vr[i] = __builtin_nontemporal_load((const u32x4_t*)(vc + row * a.v_rs + g * D + pcol(i)));
+    }
+  };
+
+  f32x16_t acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x16_t){};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (nsteps > 0) {
+    fetch_pages(0);
+    load_kv(0);
+  }
+  if (nsteps > 1) fetch_pages(1);
+  for (int n = 0; n < nsteps; ++n) {
+    // K(n), V(n) into the wave's slices (its earlier reads of them are done:
+    // one wave's LDS operations complete in order)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      *(u32x4_t*)(sk + prow(i) * KP + pcol(i)) = kr[i];
+      *(u32x4_t*)(sv + prow(i) * VP + pcol(i)) = vr[i];
+    }
+    if (n + 1 < nsteps) load_kv(n + 1);
+    if (n + 2 < nsteps) fetch_pages(n + 2);
+    // S^T = K Q^T
+    f32x16_t s = (f32x16_t){};
+#pragma unroll
+    for (int G = 0; G < G8; ++G) {
+      const f32x4_t ka = *(const f32x4_t*)(sk + r32 * KP + 8 * G + 4 * hh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s = mfma32_f32(ka[j], qf[4 * G + j], s);
+    }
+    // ---- online softmax (base 2); masked steps test every key against the row's last
+    const int kb = kbeg + n * KB;
+    const bool masked = n >= nplain;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = s[i] * a.scale_log2;
+      if (masked) {
+        const int kj = kb + 8 * (i >> 2) + 4 * hh + (i & 3);
+        v = kj <= hi ? v : -INFINITY;
+      }
+      s[i] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = fmaxf(mx, xor32(mx));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);  // 0 while m_run is -inf
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+    // ---- P and O^T += V^T P^T, two keys (k-slots) per MFMA
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(s[i] - m_use);
+      l_run += p;
+      const int key = 8 * (i >> 2) + 4 * hh + (i & 3);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32_f32(sv[key * VP + 32 * dt + r32], p, acc[dt]);
+    }
+  }
+
+  // ---- epilogue: O = acc / l and LSE, or this chunk's partials
+  const float l_tot = l_run + xor32(l_run);
+  const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse2 = l_tot > 0.f ? m_run + __builtin_log2f(l_tot) : -INFINITY;
+  if (nch == 1) {
+    if (row_ok) {
+      float* po = (float*)a.out + ((size_t)(q0 + qpos) * a.hq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int d0 = 32 * dt + 8 * a4 + 4 * hh;
+          *(f32x4_t*)(po + d0) = (f32x4_t){acc[dt][4 * a4 + 0] * inv_l, acc[dt][4 * a4 + 1] * inv_l,
+                                           acc[dt][4 * a4 + 2] * inv_l, acc[dt][4 * a4 + 3] * inv_l};
+        }
+      if (hh == 0) a.lse[(size_t)h * a.total_q + q0 + qpos] = lse2 * kLn2;
+    }
+  } else if (row_ok) {
+    float* po = a.part_o + (slot * a.rows + r32) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = 32 * dt + 8 * a4 + 4 * hh;
+        *(f32x4_t*)(po + d0) = (f32x4_t){acc[dt][4 * a4 + 0] * inv_l, acc[dt][4 * a4 + 1] * inv_l,
+                                         acc[dt][4 * a4 + 2] * inv_l, acc[dt][4 * a4 + 3] * inv_l};
+      }
+    if (hh == 0) a.part_lse[slot * a.rows + r32] = lse2;
+  }
+  }
+}
+
 // The planner: one workgroup lists every (sequence, row block, key chunk)
 // with work, in that order (chunks fastest), with the sequence's bounds
 // (clamped as the decode kernel needs them), and stores the count in
@@ -415,11 +633,15 @@ __global__ __launch_bounds__(KNT) void kv_merge_kernel(KvArgs a) {
       }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    uint16_t* dst = (uint16_t*)a.out + ((size_t)(q0 + qpos) * a.hq + h) * D + seg * SEG;
+    const size_t o0 = ((size_t)(q0 + qpos) * a.hq + h) * D + seg * SEG;
 #pragma unroll
     for (int e = 0; e < SEG / 4; ++e) {
       const f32x4_t x = acc[e] * inv;
-      *(u32x2_t*)(dst + 4 * e) = (u32x2_t){pack16<H16>(x[0], x[1]), pack16<H16>(x[2], x[3])};
+      if constexpr (H16) {
+        *(u32x2_t*)((uint16_t*)a.out + o0 + 4 * e) = (u32x2_t){pack16<H16>(x[0], x[1]), pack16<H16>(x[2], x[3])};
+      } else {
+        *(f32x4_t*)((float*)a.out + o0 + 4 * e) = x;
+      }
     }
     if (seg == 0)
       a.lse[(size_t)h * a.total_q + q0 + qpos] = wsum > 0.f ? (mx + __builtin_log2f(wsum)) * kLn2 : -INFINITY;
@@ -429,9 +651,16 @@ __global__ __launch_bounds__(KNT) void kv_merge_kernel(KvArgs a) {
 template <int H16, int D, bool CAUSAL>
 hipError_t launch_kv_t(const KvArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.cap * a.hkv;
-  auto kern = a.cu_k ? kv_decode_kernel<H16, D, CAUSAL, kRagged>
-             : (1 << a.page_shift) >= KvShape<D>::KB ? kv_decode_kernel<H16, D, CAUSAL, kPagedBig>
-                                                     : kv_decode_kernel<H16, D, CAUSAL, kPagedSmall>;
+  void (*kern)(KvArgs);
+  if constexpr (H16 != 0) {
+    kern = a.cu_k ? kv_decode_kernel<H16, D, CAUSAL, kRagged>
+           : (1 << a.page_shift) >= KvShape<D>::KB ? kv_decode_kernel<H16, D, CAUSAL, kPagedBig>
+                                                   : kv_decode_kernel<H16, D, CAUSAL, kPagedSmall>;
+  } else {
+    kern = a.cu_k ? kv_decode_f32_kernel<D, CAUSAL, kRagged>
+           : (1 << a.page_shift) >= KvShapeF32<D>::KB ? kv_decode_f32_kernel<D, CAUSAL, kPagedBig>
+                                                      : kv_decode_f32_kernel<D, CAUSAL, kPagedSmall>;
+  }
   const int grid = resident_grid((const void*)kern, KNT, (items + 3) / 4);
   if (grid <= 0) return hipErrorInvalidConfiguration;
   timing_before(st, "kvcache_plan");
@@ -439,7 +668,7 @@ hipError_t launch_kv_t(const KvArgs& a, hipStream_t st) {
   timing_after(st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  timing_before(st, H16 == 2 ? "kvcache_f16" : "kvcache_bf16");
+  timing_before(st, H16 == 2 ? "kvcache_f16" : H16 ? "kvcache_bf16" : "kvcache_f32");
   hipLaunchKernelGGL(kern, dim3(grid), dim3(KNT), 0, st, a);
   timing_after(st);
   e = hipGetLastError();
@@ -476,6 +705,7 @@ hipError_t launch_kv_h(const KvArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_kvcache(const KvArgs& a, hipStream_t st) {
+  if (a.h16 == 0) return launch_kv_h<0>(a, st);
   return a.h16 == 2 ? launch_kv_h<2>(a, st) : launch_kv_h<1>(a, st);
 }
 
