@@ -1,12 +1,12 @@
 """GPU parity of the packed forward's short-query path with the oracle.
 
-With 16-bit inputs, no bias and few new tokens per sequence by the
+Without a bias and with few new tokens per sequence by the
 max_seqlen_q hint (at most 16, or 32 with at most 128 (token, query head) rows
 per KV head), va_varlen_fwd runs the decode kernels over contiguous (or
 strided) K/V read through cu_seqlens_k: decode steps and short drafts without
 a page table.  Checked: single-token steps over
 ragged caches (empty, short, split over tens of chunks), drafts of up to 8
-tokens with 4 heads per KV head (32 rows), non-causal, MQA, float16, K and V
+tokens with 4 heads per KV head (32 rows), non-causal, MQA, float16, float32, K and V
 interleaved in one buffer, hints smaller than the true lengths (more row
 blocks and longer chunks, same results), bitwise determinism, and the backward
 run on the forward's O and LSE.
@@ -39,6 +39,13 @@ CASES = [
                              causal=True, dtype="bf16")),
     ("decode-gqa2-d96-f16", dict(seed=109, lens_q=[1, 3, 1], lens_k=[4500, 35, 1], hq=8, hkv=4, d=96,
                                  causal=True, dtype="f16")),
+    # float32: the float32 decode kernel
+    ("decode-gqa4-d128-f32", dict(seed=110, lens_q=[1] * 5, lens_k=[1, 17, 3000, 0, 9000], hq=32, hkv=8,
+                                  d=128, causal=True, dtype="f32")),
+    ("draft6-gqa2-d64-f32-noncausal", dict(seed=111, lens_q=[6, 2, 1], lens_k=[700, 4100, 3], hq=8, hkv=4, d=64,
+                                           causal=False, dtype="f32")),
+    ("draft4-mqa-d32-f32", dict(seed=112, lens_q=[4, 1], lens_k=[2500, 31], hq=8, hkv=1, d=32,
+                                causal=True, dtype="f32")),
 ]
 
 

@@ -254,7 +254,7 @@ KvLayout kv_layout(int batch, int max_q, int max_k, int hq, int hkv, int d, int6
   return L;
 }
 
-// The packed forward's short-query path: with 16-bit inputs, no bias and
+// The packed forward's short-query path: without a bias and with
 // few new tokens per sequence (by the max_seqlen_q hint) -- decode steps,
 // beams, drafts, short chunks over contiguous K/V -- the decode kernels run
 // instead of 128-row query tiles, which such rows would mostly leave empty.
@@ -269,7 +269,8 @@ KvLayout kv_layout(int batch, int max_q, int max_k, int hq, int hkv, int d, int6
 constexpr int kShortQueryTokens = 16, kShortQueryTokensMax = 32;
 constexpr int64_t kShortQueryRows = 128;
 bool short_query(va_dtype dtype, int d, int max_q, int n_rep) {
-  return dtype != VA_F32 && decode_head_dim(d) &&
+  (void)dtype;  // 16-bit and float32 alike (float32 runs the float32 decode kernel)
+  return decode_head_dim(d) &&
          (max_q <= kShortQueryTokens ||
           (max_q <= kShortQueryTokensMax && (int64_t)max_q * n_rep <= kShortQueryRows));
 }
