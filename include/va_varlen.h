@@ -132,12 +132,14 @@ typedef void* va_stream;
  * base aligned to 4 elements is read 4 keys per load; a 16-bit one whose
  * strides are multiples of 8 and whose base is 16-byte aligned is staged
  * through LDS a block of keys at a time (results identical either way).
- * Short queries: with bf16 or float16 inputs, no bias, and max_seqlen_q <= 16
- * (or <= 32 with max_seqlen_q * num_heads_q / num_heads_kv <= 128) -- decode
- * steps, beams and drafts over contiguous K/V -- the call runs the decode
- * kernels of include/va_kvcache.h (K/V read through cu_seqlens_k) instead of
- * 128-row query tiles; results agree up to rounding order, and the hints
- * still only size the work.
+ * Short queries: with max_seqlen_q <= 16 (or <= 32 with
+ * max_seqlen_q * num_heads_q / num_heads_kv <= 128) -- decode steps, beams and
+ * drafts over contiguous K/V -- the call runs the decode kernels of
+ * include/va_kvcache.h (K/V read through cu_seqlens_k; any dtype; a bias read
+ * per element, or four keys at a time under the vector-load conditions above,
+ * when its view over one sequence and KV group of heads spans less than 2 GiB)
+ * instead of 128-row query tiles; results agree up to rounding order, and the
+ * hints still only size the work.
  */
 va_status va_varlen_fwd(const void* q, const void* k, const void* v,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

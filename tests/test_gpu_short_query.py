@@ -1,12 +1,13 @@
 """GPU parity of the packed forward's short-query path with the oracle.
 
-Without a bias and with few new tokens per sequence by the
+With few new tokens per sequence by the
 max_seqlen_q hint (at most 16, or 32 with at most 128 (token, query head) rows
 per KV head), va_varlen_fwd runs the decode kernels over contiguous (or
 strided) K/V read through cu_seqlens_k: decode steps and short drafts without
 a page table.  Checked: single-token steps over
 ragged caches (empty, short, split over tens of chunks), drafts of up to 8
-tokens with 4 heads per KV head (32 rows), non-causal, MQA, float16, float32, K and V
+tokens with 4 heads per KV head (32 rows), non-causal, MQA, float16, float32,
+an additive bias per key or per pair (contiguous, permuted, head-shared), K and V
 interleaved in one buffer, hints smaller than the true lengths (more row
 blocks and longer chunks, same results), bitwise determinism, and the backward
 run on the forward's O and LSE.
@@ -46,6 +47,21 @@ CASES = [
                                            causal=False, dtype="f32")),
     ("draft4-mqa-d32-f32", dict(seed=112, lens_q=[4, 1], lens_k=[2500, 31], hq=8, hkv=1, d=32,
                                 causal=True, dtype="f32")),
+    # an additive bias (GiGL "Approach": per sequence, through a strided view) on the decode
+    # kernels: per key (row stride 0), per pair, a permuted view (no unit key stride: one
+    # element per load) and a head-shared grid
+    ("decode-gqa4-d128-bf16-bias-key", dict(seed=113, lens_q=[1] * 4, lens_k=[1, 300, 3000, 9000], hq=32, hkv=8,
+                                            d=128, causal=True, dtype="bf16", bias="per_key")),
+    ("draft6-gqa2-d64-f16-bias-pair", dict(seed=114, lens_q=[6, 2, 1], lens_k=[700, 4100, 3], hq=8, hkv=4,
+                                           d=64, causal=True, dtype="f16", bias="per_pair", bias_std=0.5)),
+    ("draft3-mqa-d64-bf16-bias-permuted", dict(seed=115, lens_q=[3, 1], lens_k=[1300, 40], hq=8, hkv=1, d=64,
+                                               causal=False, dtype="bf16", bias="per_pair",
+                                               bias_layout="permuted")),
+    ("draft4-gqa4-d128-f32-bias-pair", dict(seed=116, lens_q=[4, 1, 2], lens_k=[2500, 31, 5000], hq=16, hkv=4,
+                                            d=128, causal=True, dtype="f32", bias="per_pair", bias_std=0.5)),
+    ("decode-d96-f32-bias-head-shared", dict(seed=117, lens_q=[1, 2], lens_k=[777, 3000], hq=8, hkv=2, d=96,
+                                             causal=True, dtype="f32", bias="per_pair",
+                                             bias_layout="head_shared")),
 ]
 
 
@@ -103,3 +119,17 @@ def test_short_query_lse_feeds_the_backward():
     for nm, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), g_ref):
         _gpu.check(nm, _gpu.host(got), ref, "bf16", grad=True, abs_tol=_gpu.grad_abs_tol("bf16", ref, False))
     np.testing.assert_array_equal(np.isneginf(_gpu.host(lse)), np.zeros_like(_gpu.host(lse), dtype=bool))
+
+
+@pytest.mark.parametrize("dtype,kernel", [("bf16", "kvcache_bf16"), ("f32", "kvcache_f32")])
+def test_bias_calls_take_the_decode_kernels(dtype, kernel):
+    """A short-query call with a bias runs the decode kernels (not the 128-row tiles)."""
+    print(f"[case] short query with a bias: kernel names ({dtype})", flush=True)
+    w = make_case(118, [2, 1], lens_k=[600, 90], hq=8, hkv=2, d=64, causal=True, dtype=dtype,
+                  bias="per_pair")
+    inp = _gpu.device_inputs(w)
+    torch.cuda.synchronize()
+    va.va_timing_start(64)
+    _gpu.run_fwd(w, inp)
+    names = set(va.va_timing_stop())
+    assert kernel in names and not any(n.startswith("fwd_") for n in names), names

@@ -377,7 +377,18 @@ va_status varlen_fwd(const void* q, const void* k, const void* v, const int32_t*
     return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
 
   hipStream_t st = (hipStream_t)stream;
-  if (!bias && short_query(dtype, head_dim, max_seqlen_q, num_heads_q / num_heads_kv)) {
+  // a bias reaches the decode kernels through one resource per (sequence, KV group):
+  // every offset inside it must be a 32-bit byte offset
+  bool short_bias_ok = true;
+  if (bias) {
+    const int64_t elt = bf16 ? 2 : 4;
+    const int64_t span = ((int64_t)(num_heads_q / num_heads_kv - 1) * bias_stride[1] +
+                          (int64_t)max_seqlen_q * bias_stride[2] + ((int64_t)max_seqlen_k + 64) * bias_stride[3] + 8) *
+                         elt;
+    short_bias_ok = bias_stride[0] >= 0 && bias_stride[1] >= 0 && bias_stride[2] >= 0 && bias_stride[3] >= 0 &&
+                    span < ((int64_t)1 << 31);
+  }
+  if (short_bias_ok && short_query(dtype, head_dim, max_seqlen_q, num_heads_q / num_heads_kv)) {
     const KvLayout L = kv_layout(batch, max_seqlen_q, max_seqlen_k, num_heads_q, num_heads_kv, head_dim,
                                  total_q);
     if (workspace_bytes < L.total())
@@ -402,6 +413,14 @@ va_status varlen_fwd(const void* q, const void* k, const void* v, const int32_t*
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.causal = causal;
     a.h16 = elem_code(dtype);
+    if (bias) {
+      const int elt = bf16 ? 2 : 4;
+      a.bias = bias;
+      a.bs0 = bias_stride[0]; a.bs1 = bias_stride[1]; a.bs2 = bias_stride[2]; a.bs3 = bias_stride[3];
+      // four keys per load: contiguous keys, every 4-key group aligned to its own size
+      a.bias_vec = a.bs3 == 1 && a.bs0 % 4 == 0 && a.bs1 % 4 == 0 && a.bs2 % 4 == 0 &&
+                   ((uintptr_t)bias) % (4 * elt) == 0;
+    }
     const hipError_t e = va::launch_kvcache(a, st);
     if (e != hipSuccess) return hip_fail(e, "short-query forward launch");
     return VA_OK;

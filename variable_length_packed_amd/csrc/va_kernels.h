@@ -190,7 +190,12 @@ struct KvArgs {
   int32_t cap_merge;         // most row blocks with several chunks (cap / 2)
   float scale_log2;
   int32_t causal;
-  int32_t h16;               // 1 bfloat16, 2 float16
+  int32_t h16;               // 0 float32, 1 bfloat16, 2 float16
+  // additive bias (the packed forward's short-query path only; nullptr otherwise):
+  // element (b, h, r, c) at b*bs0 + h*bs1 + r*bs2 + c*bs3, in the input dtype
+  const void* bias;
+  int64_t bs0, bs1, bs2, bs3;
+  int32_t bias_vec;          // bs3 == 1 and every 4-key group aligned: 4 keys per load
 };
 int kv_block_n(int d);  // keys per step of the decode kernel
 hipError_t launch_kvcache(const KvArgs& a, hipStream_t st);

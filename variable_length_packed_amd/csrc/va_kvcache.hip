@@ -82,7 +82,58 @@ __device__ __forceinline__ int kv_chunk_of(const KvArgs& a, int Lk) {
   return Lk <= cap ? a.chunk : a.chunk * (int)((Lk + cap - 1) / cap);
 }
 
-template <int H16, int D, bool CAUSAL, int MODE>
+// The additive bias of the packed forward's short-query path (BIAS; ragged K/V
+// only): this lane's (row, key) element b*bs0 + h*bs1 + qpos*bs2 + key*bs3,
+// through a resource over the KV group's heads of the sequence that ends after
+// the last element a valid (head, row, key) reads; rows past the sequence are
+// never stored and keys past it are masked, whatever they read.
+template <int H16, int NS>
+struct KvBias {
+  static constexpr int ELT = H16 ? 2 : 4;
+  rsrc_t res;
+  int off = 0;  // this lane's head, row and key half, bytes
+  float v[NS][16];
+  __device__ __forceinline__ void init(const KvArgs& a, int b, int g, int h, int qpos, int hh, int Lq, int Lk) {
+    const int h0 = g * a.n_rep;
+    const int64_t last = Lq > 0 && Lk > 0
+                             ? ((int64_t)(a.n_rep - 1) * a.bs1 + (int64_t)(Lq - 1) * a.bs2 + (int64_t)(Lk - 1) * a.bs3 + 1) * ELT
+                             : 0;
+    res = make_rsrc((const uint8_t*)a.bias + ((int64_t)b * a.bs0 + (int64_t)h0 * a.bs1) * ELT, (last + 3) & ~(int64_t)3);
+    off = (int)(((int64_t)(h - h0) * a.bs1 + (int64_t)qpos * a.bs2 + (int64_t)(4 * hh) * a.bs3) * ELT);
+  }
+  // the values of keys kb + 32 st + 8 (i / 4) + 4 hh + i % 4 (register i of tile st):
+  // four consecutive keys per load when bias_vec, else one element per load
+  __device__ __forceinline__ void load(const KvArgs& a, int kb) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (a.bias_vec) {
+          const int o = off + (kb + 32 * st + 8 * j) * ELT;
+          if constexpr (H16) {
+            const u32x2_t x = buf_load8(res, o);
+            v[st][4 * j + 0] = lo16<H16>(x[0]);
+            v[st][4 * j + 1] = hi16<H16>(x[0]);
+            v[st][4 * j + 2] = lo16<H16>(x[1]);
+            v[st][4 * j + 3] = hi16<H16>(x[1]);
+          } else {
+            const u32x4_t x = buf_load16(res, o);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[st][4 * j + e] = __uint_as_float(x[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int o = off + (int)((int64_t)(kb + 32 * st + 8 * j + e) * a.bs3 * ELT);
+            if constexpr (H16) v[st][4 * j + e] = lo16<H16>(__builtin_amdgcn_raw_buffer_load_b16(res, o, 0, 0));
+            else v[st][4 * j + e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(res, o, 0, 0));
+          }
+        }
+      }
+  }
+};
+
+template <int H16, int D, bool CAUSAL, int MODE, bool BIAS = false>
 __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
   constexpr bool BIGPAGE = MODE == kPagedBig, RAGGED = MODE == kRagged;
   using SH = KvShape<D>;
@@ -140,6 +191,8 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
   if (CAUSAL) plain_end = min(plain_end, qpos_first + off + 1);
   const int nplain = plain_end > kbeg ? (plain_end - kbeg) / KB : 0;
   const int hi = !row_ok ? -1 : (CAUSAL ? min(kend - 1, qpos + off) : kend - 1);
+  KvBias<H16, NS> bias;
+  if constexpr (BIAS) bias.init(a, b, g, h, qpos, hh, Lq, Lk);
 
   // ---- Q fragments (B operand of S^T = K Q^T); rows past the sequence read 0
   constexpr int ELT = 2;
@@ -225,6 +278,7 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
     // (their pages were fetched a step ago); then the pages of the step after
     if (n + 1 < nsteps) load_kv(n + 1);
     if (n + 2 < nsteps) fetch_pages(n + 2);
+    if constexpr (BIAS) bias.load(a, kbeg + n * KB);
     // S^T = K Q^T, K fragments from LDS
     f32x16_t s[NS];
 #pragma unroll
@@ -246,6 +300,7 @@ __global__ __launch_bounds__(KNT, 2) void kv_decode_kernel(KvArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float v = s[st][i] * a.scale_log2;
+        if constexpr (BIAS) v = __builtin_fmaf(bias.v[st][i], kLog2e, v);
         if (masked) {
           const int kj = kb + 32 * st + 8 * (i >> 2) + 4 * hh + (i & 3);
           v = kj <= hi ? v : -INFINITY;
@@ -348,7 +403,7 @@ struct KvShapeF32 {
 template <int D>
 constexpr int kv_f32_blocks() { return D <= 64 ? 2 : 1; }
 
-template <int D, bool CAUSAL, int MODE>
+template <int D, bool CAUSAL, int MODE, bool BIAS = false>
 __global__ __launch_bounds__(KNT, (kv_f32_blocks<D>())) void kv_decode_f32_kernel(KvArgs a) {
   constexpr bool BIGPAGE = MODE == kPagedBig, RAGGED = MODE == kRagged;
   using SH = KvShapeF32<D>;
@@ -395,6 +450,8 @@ __global__ __launch_bounds__(KNT, (kv_f32_blocks<D>())) void kv_decode_f32_kerne
   if (CAUSAL) plain_end = min(plain_end, qpos_first + off + 1);
   const int nplain = plain_end > kbeg ? (plain_end - kbeg) / KB : 0;
   const int hi = !row_ok ? -1 : (CAUSAL ? min(kend - 1, qpos + off) : kend - 1);
+  KvBias<0, 1> bias;
+  if constexpr (BIAS) bias.init(a, b, g, h, qpos, hh, Lq, Lk);
 
   // ---- Q (the B operand of S^T = K Q^T); rows past the sequence read 0
   const size_t qrow = (size_t)a.q_rs;
@@ -463,6 +520,7 @@ __global__ __launch_bounds__(KNT, (kv_f32_blocks<D>())) void kv_decode_f32_kerne
     }
     if (n + 1 < nsteps) load_kv(n + 1);
     if (n + 2 < nsteps) fetch_pages(n + 2);
+    if constexpr (BIAS) bias.load(a, kbeg + n * KB);
     // S^T = K Q^T
     f32x16_t s = (f32x16_t){};
 #pragma unroll
@@ -478,6 +536,7 @@ __global__ __launch_bounds__(KNT, (kv_f32_blocks<D>())) void kv_decode_f32_kerne
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float v = s[i] * a.scale_log2;
+      if constexpr (BIAS) v = __builtin_fmaf(bias.v[0][i], kLog2e, v);
       if (masked) {
         const int kj = kb + 8 * (i >> 2) + 4 * hh + (i & 3);
         v = kj <= hi ? v : -INFINITY;
@@ -652,7 +711,11 @@ template <int H16, int D, bool CAUSAL>
 hipError_t launch_kv_t(const KvArgs& a, hipStream_t st) {
   const int64_t items = (int64_t)a.cap * a.hkv;
   void (*kern)(KvArgs);
-  if constexpr (H16 != 0) {
+  if (a.bias) {
+    // the packed forward's short-query path (ragged K/V) with an additive bias
+    if constexpr (H16 != 0) kern = kv_decode_kernel<H16, D, CAUSAL, kRagged, true>;
+    else kern = kv_decode_f32_kernel<D, CAUSAL, kRagged, true>;
+  } else if constexpr (H16 != 0) {
     kern = a.cu_k ? kv_decode_kernel<H16, D, CAUSAL, kRagged>
            : (1 << a.page_shift) >= KvShape<D>::KB ? kv_decode_kernel<H16, D, CAUSAL, kPagedBig>
                                                    : kv_decode_kernel<H16, D, CAUSAL, kPagedSmall>;
