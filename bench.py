@@ -198,9 +198,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="3", help="config id for the step (default 3)")
-    ap.add_argument("--sections", default="qwen,packing,bias,decode,variants",
+    ap.add_argument("--sections", default="graph,qwen,packing,bias,decode,variants",
                     help="comma list of the sections to run besides the main step "
-                         "(qwen, packing, bias, decode, variants; default all)")
+                         "(graph, qwen, packing, bias, decode, variants; default all)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 3 device-to-device copies of MIB MiB (a kernel of known HBM "
                          "traffic, to scale hardware byte counters against)")
@@ -292,6 +292,29 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_cold = sum(ea.elapsed_time(eb) for ea, eb in evs) / len(evs)
     del scrub
+
+    # the same step captured once in a HIP graph and replayed (the library only enqueues
+    # kernels, so a caller can capture whole steps): the step without host launch costs
+    graph_step = None
+    if "graph" in secs:
+        step()
+        torch.cuda.synchronize()
+        eager_dq = dq.clone()
+        gr = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(gr, stream=side):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        ms_graph = timed(gr.replay, args.steps)
+        graph_step = {"ms_per_step": round(ms_graph, 5),
+                      "tflops": round((flops_fwd + flops_bwd) / (ms_graph * 1e-3) / 1e12, 3),
+                      "bitwise_equal_to_eager": bool(torch.equal(dq, eager_dq))}
+        del gr
 
     # per-kernel HIP-event timing on the stream the kernels run on
     va.va_timing_start(64 * args.steps + 64)
@@ -585,6 +608,7 @@ def main() -> int:
         "bias_grad": bias_grad,
         "kvcache_decode": kvcache_decode,
         "variants": variants,
+        "graph_step": graph_step,
         "roofline": roof,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
