@@ -219,6 +219,54 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
                         va_dtype dtype, va_dtype grad_dtype, va_stream stream);
 
 /*
+ * One plan for a forward and its backward.  The work plans of both passes
+ * depend only on cu_seqlens and the sizes (TorchEasyRec intro: one set of
+ * cumulative boundaries per packed batch), so the forward's planner launch can
+ * build the backward's plans as well:
+ *
+ * va_varlen_fwd_bwdplan: va_varlen_fwd, and in the same planner launch the
+ *   dK/dV and dQ work plans of va_varlen_bwd for the same cu_seqlens and sizes,
+ *   written into bwd_workspace (device memory, 256-byte aligned, at least
+ *   va_varlen_bwd_workspace_size bytes for these sizes; the caller keeps it
+ *   for the backward).  Results of the forward are those of va_varlen_fwd.
+ *   Errors: those of va_varlen_fwd; VA_ERR_INVALID for a NULL or misaligned
+ *   bwd_workspace; VA_ERR_WORKSPACE if bwd_workspace_bytes is too small.
+ * va_varlen_bwd_planned: va_varlen_bwd that takes its work plans from
+ *   `workspace` as the forward left them (it builds none: the preprocessing
+ *   launch only computes D = rowsum(dO * O)).  The caller guarantees that the
+ *   last call that wrote `workspace` was a va_varlen_fwd_bwdplan with the same
+ *   cu_seqlens, max_seqlen, sizes and causal flag on the same stream (or one
+ *   ordered before it); the backward consumes the plans, so each forward
+ *   feeds one backward.  Results are bitwise those of va_varlen_bwd.  Errors:
+ *   those of va_varlen_bwd.
+ */
+va_status va_varlen_fwd_bwdplan(const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                float softmax_scale, int causal,
+                                const void* bias, const int64_t* bias_stride,
+                                void* out, float* lse,
+                                const int64_t* qkv_row_stride,
+                                void* workspace, size_t workspace_bytes,
+                                void* bwd_workspace, size_t bwd_workspace_bytes,
+                                int32_t batch, int32_t total_q, int32_t total_k,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                va_dtype dtype, va_stream stream);
+va_status va_varlen_bwd_planned(const void* dout, const void* q, const void* k, const void* v,
+                                const void* out, const float* lse,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                float softmax_scale, int causal,
+                                const void* bias, const int64_t* bias_stride,
+                                void* dq, void* dk, void* dv,
+                                float* dbias, const int64_t* dbias_stride,
+                                const int64_t* qkv_row_stride,
+                                void* workspace, size_t workspace_bytes,
+                                int32_t batch, int32_t total_q, int32_t total_k,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                va_dtype dtype, va_dtype grad_dtype, va_stream stream);
+
+/*
  * Allocation-free forward, for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation.  The same computation and arguments as va_varlen_fwd (results

@@ -110,6 +110,38 @@ def test_fwd_validation(lib, kw, code):
     assert lib.va_last_error()
 
 
+def _fwd_bwdplan(lib, bws, bwsb, **kw):
+    a = dict(q=P, k=P, v=P, cq=P, ck=P, mq=8, mk=8, scale=0.125, causal=1, bias=None,
+             bstr=None, rs=None, out=P, lse=P, ws=0x100000, wsb=1 << 30, batch=2, tq=16, tk=16, hq=4,
+             hkv=2, d=64, dt=BF16)
+    a.update(kw)
+    return lib.va_varlen_fwd_bwdplan(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["mq"], a["mk"],
+                                     a["scale"], a["causal"], None, None, a["out"], a["lse"], None,
+                                     a["ws"], a["wsb"], bws, bwsb, a["batch"], a["tq"], a["tk"], a["hq"],
+                                     a["hkv"], a["d"], a["dt"], None)
+
+
+@pytest.mark.parametrize("bws,bwsb,kw,code", [
+    (None, 1 << 30, {}, INVALID),             # no backward workspace
+    (0x200040, 1 << 30, {}, INVALID),         # misaligned
+    (0x200000, 16, {}, WORKSPACE),            # too small for the backward's sizes
+    (0x200000, 1 << 30, dict(q=None), INVALID),  # the forward's own checks still apply
+    (0x200000, 1 << 30, dict(d=80), UNSUPPORTED),
+])
+def test_fwd_bwdplan_validation(lib, bws, bwsb, kw, code):
+    assert _fwd_bwdplan(lib, bws, bwsb, **kw) == code
+    assert lib.va_last_error()
+
+
+def test_bwd_planned_validation(lib):
+    """The planned backward runs the backward's argument checks."""
+    args = [P, P, P, P, P, P, P, P, 8, 8, 0.125, 1, None, None, P, P, P, None, None, None,
+            0x100000, 16, 2, 16, 16, 4, 2, 64, BF16, F32, None]
+    assert lib.va_varlen_bwd_planned(*args) == WORKSPACE
+    args[20] = None
+    assert lib.va_varlen_bwd_planned(*args) == INVALID
+
+
 def _bwd(lib, **kw):
     a = dict(do=P, q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, mq=8, mk=8, scale=0.125, causal=1,
              bias=None, bstr=None, rs=None, dq=P, dk=P, dv=P, db=None, dbstr=None, ws=0x100000,

@@ -15,7 +15,8 @@ VA_F32, VA_BF16, VA_F16 = 0, 1, 2
 EXPORTS = ("va_varlen_fwd", "va_varlen_bwd", "va_varlen_fwd_workspace_size",
            "va_varlen_bwd_workspace_size", "va_status_string", "va_last_error", "va_version",
            "va_timing_start", "va_timing_stop", "va_pack_metadata", "va_unpad", "va_pad",
-           "va_kvcache_fwd", "va_kvcache_fwd_workspace_size", "va_varlen_fwd_noalloc")
+           "va_kvcache_fwd", "va_kvcache_fwd_workspace_size", "va_varlen_fwd_noalloc",
+           "va_varlen_fwd_bwdplan", "va_varlen_bwd_planned")
 VA_PACK_MAX_TENSORS = 4
 
 
@@ -49,6 +50,11 @@ def load() -> ctypes.CDLL:
     lib.va_varlen_fwd.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p, _i64p, _p, _p,
                                   _i64p, _p, ctypes.c_size_t, _i32, _i32, _i32, _i32, _i32, _i32,
                                   ctypes.c_int, _p]
+    # the forward's arguments plus the backward's workspace pair after its own
+    lib.va_varlen_fwd_bwdplan.restype = ctypes.c_int
+    lib.va_varlen_fwd_bwdplan.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p, _i64p, _p,
+                                          _p, _i64p, _p, ctypes.c_size_t, _p, ctypes.c_size_t, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, ctypes.c_int, _p]
     # the forward's arguments without the workspace pair
     lib.va_varlen_fwd_noalloc.restype = ctypes.c_int
     lib.va_varlen_fwd_noalloc.argtypes = [_p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p, _i64p, _p,
@@ -60,6 +66,8 @@ def load() -> ctypes.CDLL:
     lib.va_varlen_bwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _f, ctypes.c_int, _p,
                                   _i64p, _p, _p, _p, _p, _i64p, _i64p, _p, ctypes.c_size_t, _i32, _i32,
                                   _i32, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int, _p]
+    lib.va_varlen_bwd_planned.restype = ctypes.c_int
+    lib.va_varlen_bwd_planned.argtypes = list(lib.va_varlen_bwd.argtypes)
     lib.va_varlen_fwd_workspace_size.restype = ctypes.c_size_t
     lib.va_varlen_fwd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                  ctypes.c_int]

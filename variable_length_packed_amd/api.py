@@ -105,8 +105,13 @@ def va_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   bias: Optional[torch.Tensor] = None,
                   bias_stride: Optional[Sequence[int]] = None,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None):
-    """Forward.  Returns (out [Tq, Hq, d] in q's dtype, lse [Hq, Tq] float32)."""
+                  workspace: Optional[torch.Tensor] = None,
+                  bwd_workspace: Optional[torch.Tensor] = None):
+    """Forward.  Returns (out [Tq, Hq, d] in q's dtype, lse [Hq, Tq] float32).
+
+    With ``bwd_workspace`` (a uint8 device buffer of va_varlen_bwd_workspace_size bytes),
+    the forward's planner launch also builds the backward's work plans in it
+    (va_varlen_fwd_bwdplan); pass the same buffer to va_varlen_bwd with planned=True."""
     lib = _lib.load()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _need_dev(n, t, q.device, rows=True)
@@ -142,11 +147,23 @@ def va_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
     _need_dev("workspace", workspace, q.device)
-    st = lib.va_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
-                           cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
-                           int(bool(causal)), bptr, bstr, out.data_ptr(), lse.data_ptr(), _row_strides(q, k, v),
-                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                           batch, tq, tk, hq, hkv, d, dt, _stream(q.device))
+    if bwd_workspace is None:
+        st = lib.va_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+                               cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
+                               int(bool(causal)), bptr, bstr, out.data_ptr(), lse.data_ptr(),
+                               _row_strides(q, k, v), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(),
+                               batch, tq, tk, hq, hkv, d, dt, _stream(q.device))
+    else:
+        _need_dev("bwd_workspace", bwd_workspace, q.device)
+        st = lib.va_varlen_fwd_bwdplan(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_seqlens_q.data_ptr(),
+                                       cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
+                                       int(bool(causal)), bptr, bstr, out.data_ptr(), lse.data_ptr(),
+                                       _row_strides(q, k, v), workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(),
+                                       bwd_workspace.data_ptr(),
+                                       bwd_workspace.numel() * bwd_workspace.element_size(),
+                                       batch, tq, tk, hq, hkv, d, dt, _stream(q.device))
     _raise(st, lib)
     return out, lse
 
@@ -241,8 +258,12 @@ def va_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch
                   dv: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None,
                   dbias: Optional[torch.Tensor] = None,
-                  dbias_stride: Optional[Sequence[int]] = None):
+                  dbias_stride: Optional[Sequence[int]] = None,
+                  planned: bool = False):
     """Backward.  Returns (dq, dk, dv) in ``grad_dtype``.
+
+    ``planned``: ``workspace`` holds the work plans a va_varlen_fwd(..., bwd_workspace=workspace)
+    of the same batch built (va_varlen_bwd_planned); each such forward feeds one backward.
 
     With ``dbias`` (a float32 device tensor) and ``dbias_stride`` (4 element
     strides relative to ``dbias``'s first element; 0 sums over that axis), the
@@ -305,13 +326,16 @@ def va_varlen_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch
     if workspace is None:
         workspace = torch.empty(max(int(need), 1), dtype=torch.uint8, device=q.device)
     _need_dev("workspace", workspace, q.device)
-    st = lib.va_varlen_bwd(dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                           out.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
-                           cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
-                           int(bool(causal)), bptr, bstr, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dbptr,
-                           dbstr, _row_strides(q, k, v), workspace.data_ptr(),
-                           workspace.numel() * workspace.element_size(), batch, tq, tk, hq, hkv,
-                           d, dt, gdt, _stream(q.device))
+    if planned and workspace is None:
+        raise ValueError("planned=True needs the workspace the forward built the plans in")
+    fn = lib.va_varlen_bwd_planned if planned else lib.va_varlen_bwd
+    st = fn(dout.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+            out.data_ptr(), lse.data_ptr(), cu_seqlens_q.data_ptr(),
+            cu_seqlens_k.data_ptr(), int(max_seqlen_q), int(max_seqlen_k), scale,
+            int(bool(causal)), bptr, bstr, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dbptr,
+            dbstr, _row_strides(q, k, v), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), batch, tq, tk, hq, hkv,
+            d, dt, gdt, _stream(q.device))
     _raise(st, lib)
     return dq, dk, dv
 

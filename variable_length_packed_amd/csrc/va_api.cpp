@@ -212,6 +212,25 @@ size_t bwd_workspace(int batch, int total_q, int total_k, int max_q, int max_k, 
          round_up(dbias_slot_bytes(hq) * K.slot_cap);
 }
 
+// The backward's two work plans inside its workspace, at the places va_varlen_bwd
+// uses (after the D buffer): the dK/dV plan over key tiles, then the dQ plan.
+struct BwdPlans {
+  PlanLayout K, Q;
+  va::Plan pk, pq;
+  size_t end = 0;  // bytes from the workspace start to the end of the plans
+};
+BwdPlans bwd_plans(char* w, int batch, int total_q, int total_k, int max_q, int max_k, int hq, int hkv, int d,
+                   bool bf16) {
+  BwdPlans r;
+  r.K = dkdv_plan(batch, total_k, max_q, hkv, hq / hkv, d);
+  r.Q = dq_plan(batch, total_q, max_k, hq, d, bf16);
+  size_t o = round_up((size_t)hq * total_q * sizeof(float));
+  o += carve_plan(w + o, r.K, r.pk);
+  o += carve_plan(w + o, r.Q, r.pq);
+  r.end = o;
+  return r;
+}
+
 // Decode steps: row blocks of `rows` = min(32, n_rep * max_seqlen_q) (new
 // token, query head) pairs, and key chunks sized so the grid holds about
 // kKvWaves waves (at least 256 keys per chunk, so the partial results of a
@@ -330,6 +349,24 @@ va_status va_varlen_fwd(const void* q, const void* k, const void* v,
                         batch, total_q, total_k, num_heads_q, num_heads_kv, head_dim, dtype, stream);
 }
 
+va_status va_varlen_fwd_bwdplan(const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int32_t max_seqlen_q, int32_t max_seqlen_k, float softmax_scale,
+                                int causal, const void* bias, const int64_t* bias_stride, void* out,
+                                float* lse, const int64_t* qkv_row_stride, void* workspace,
+                                size_t workspace_bytes, void* bwd_workspace, size_t bwd_workspace_bytes,
+                                int32_t batch, int32_t total_q, int32_t total_k, int32_t num_heads_q,
+                                int32_t num_heads_kv, int32_t head_dim, va_dtype dtype, va_stream stream) {
+  if (!bwd_workspace) {
+    g_err[0] = 0;
+    return fail(VA_ERR_INVALID, "bwd_workspace is NULL");
+  }
+  return va::varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, softmax_scale, causal,
+                        bias, bias_stride, out, lse, qkv_row_stride, workspace, workspace_bytes, kFwdPartBudget,
+                        batch, total_q, total_k, num_heads_q, num_heads_kv, head_dim, dtype, stream,
+                        bwd_workspace, bwd_workspace_bytes);
+}
+
 }  // extern "C"
 
 namespace va {
@@ -357,7 +394,8 @@ va_status varlen_fwd(const void* q, const void* k, const void* v, const int32_t*
                      float softmax_scale, int causal, const void* bias, const int64_t* bias_stride, void* out,
                      float* lse, const int64_t* qkv_row_stride, void* workspace, size_t workspace_bytes,
                      size_t part_budget, int32_t batch, int32_t total_q, int32_t total_k, int32_t num_heads_q,
-                     int32_t num_heads_kv, int32_t head_dim, va_dtype dtype, va_stream stream) {
+                     int32_t num_heads_kv, int32_t head_dim, va_dtype dtype, va_stream stream,
+                     void* bwd_ws, size_t bwd_ws_bytes) {
   g_err[0] = 0;
   if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out || !lse)
     return fail(VA_ERR_INVALID, "a required pointer is NULL");
@@ -375,6 +413,22 @@ va_status varlen_fwd(const void* q, const void* k, const void* v, const int32_t*
   const size_t need = fwd_workspace(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16, part_budget);
   if (workspace_bytes < need)
     return fail(VA_ERR_WORKSPACE, "workspace of %zu bytes < %zu required", workspace_bytes, need);
+  // the backward's plans, built by this call's planner launch (va_varlen_fwd_bwdplan)
+  va::PlanArgs bwd_pk{}, bwd_pq{};
+  if (bwd_ws) {
+    if (((uintptr_t)bwd_ws) % kAlign != 0)
+      return fail(VA_ERR_INVALID, "bwd_workspace must be 256-byte aligned");
+    const size_t bneed = bwd_workspace(batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q,
+                                       num_heads_kv, head_dim, bf16);
+    if (bwd_ws_bytes < bneed)
+      return fail(VA_ERR_WORKSPACE, "bwd_workspace of %zu bytes < %zu required", bwd_ws_bytes, bneed);
+    const BwdPlans B = bwd_plans((char*)bwd_ws, batch, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                                 num_heads_q, num_heads_kv, head_dim, bf16);
+    bwd_pk = plan_args(B.pk, B.K, cu_seqlens_k, cu_seqlens_q, total_k, total_q, batch, va::bwd_block_k(),
+                       va::bwd_dkdv_block_q(), 1, causal);
+    bwd_pq = plan_args(B.pq, B.Q, cu_seqlens_q, cu_seqlens_k, total_q, total_k, batch, va::bwd_block_q(),
+                       va::bwd_dq_block_n(bf16, head_dim), 0, causal);
+  }
 
   hipStream_t st = (hipStream_t)stream;
   // a bias reaches the decode kernels through one resource per (sequence, KV group):
@@ -421,6 +475,13 @@ va_status varlen_fwd(const void* q, const void* k, const void* v, const int32_t*
       a.bias_vec = a.bs3 == 1 && a.bs0 % 4 == 0 && a.bs1 % 4 == 0 && a.bs2 % 4 == 0 &&
                    ((uintptr_t)bias) % (4 * elt) == 0;
     }
+    if (bwd_ws) {
+      va::PlanSet pb{};
+      pb.p[0] = bwd_pk;
+      pb.p[1] = bwd_pq;
+      const hipError_t eb = va::launch_plan(pb, 2, st);
+      if (eb != hipSuccess) return hip_fail(eb, "backward plan launch");
+    }
     const hipError_t e = va::launch_kvcache(a, st);
     if (e != hipSuccess) return hip_fail(e, "short-query forward launch");
     return VA_OK;
@@ -460,7 +521,9 @@ va_status varlen_fwd(const void* q, const void* k, const void* v, const int32_t*
   va::PlanSet ps{};
   ps.p[0] = plan_args(a.plan, L, cu_seqlens_q, cu_seqlens_k, total_q, total_k, batch,
                       va::fwd_block_m(), va::fwd_block_n(bf16, head_dim), 0, causal);
-  hipError_t e = va::launch_plan(ps, 1, st);
+  ps.p[1] = bwd_pk;
+  ps.p[2] = bwd_pq;
+  hipError_t e = va::launch_plan(ps, bwd_ws ? 3 : 1, st);
   if (e != hipSuccess) return hip_fail(e, "forward plan launch");
   e = va::launch_fwd(a, (int64_t)L.unit_cap * num_heads_q, st);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
@@ -485,15 +548,19 @@ size_t va_varlen_bwd_workspace_size(int32_t batch, int32_t total_q, int32_t tota
                        num_heads_kv, head_dim, dtype != VA_F32);
 }
 
-va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const void* v,
-                        const void* out, const float* lse, const int32_t* cu_seqlens_q,
-                        const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                        float softmax_scale, int causal, const void* bias,
-                        const int64_t* bias_stride, void* dq, void* dk, void* dv, float* dbias,
-                        const int64_t* dbias_stride, const int64_t* qkv_row_stride, void* workspace,
-                        size_t workspace_bytes, int32_t batch, int32_t total_q, int32_t total_k,
-                        int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
-                        va_dtype dtype, va_dtype grad_dtype, va_stream stream) {
+}  // extern "C"
+
+// The backward; `planned`: the workspace already holds the work plans, built by the
+// forward of the same call shape (va_varlen_fwd_bwdplan).
+static va_status varlen_bwd(const void* dout, const void* q, const void* k, const void* v,
+                            const void* out, const float* lse, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            float softmax_scale, int causal, const void* bias,
+                            const int64_t* bias_stride, void* dq, void* dk, void* dv, float* dbias,
+                            const int64_t* dbias_stride, const int64_t* qkv_row_stride, void* workspace,
+                            size_t workspace_bytes, int32_t batch, int32_t total_q, int32_t total_k,
+                            int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                            va_dtype dtype, va_dtype grad_dtype, va_stream stream, bool planned) {
   g_err[0] = 0;
   if (!dout || !q || !k || !v || !out || !lse || !cu_seqlens_q || !cu_seqlens_k || !dq || !dk ||
       !dv || !workspace)
@@ -568,13 +635,15 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
   a.bf16 = elem_code(dtype);
   a.grad_bf16 = grad_dtype == VA_F32 ? 0 : elem_code(grad_dtype);
 
-  const PlanLayout K = dkdv_plan(batch, total_k, max_seqlen_q, num_heads_kv, n_rep, head_dim);
-  const PlanLayout Q = dq_plan(batch, total_q, max_seqlen_k, num_heads_q, head_dim, bf16);
   char* w = (char*)workspace;
+  const BwdPlans B = bwd_plans(w, batch, total_q, total_k, max_seqlen_q, max_seqlen_k, num_heads_q,
+                               num_heads_kv, head_dim, bf16);
+  const PlanLayout& K = B.K;
+  const PlanLayout& Q = B.Q;
   a.dsum = (float*)w;
-  size_t o = round_up((size_t)num_heads_q * total_q * sizeof(float));
-  o += carve_plan(w + o, K, a.plan_k);
-  o += carve_plan(w + o, Q, a.plan_q);
+  a.plan_k = B.pk;
+  a.plan_q = B.pq;
+  size_t o = B.end;
   a.part_kv = (float*)(w + o);
   o += round_up(K.slot_bytes * K.slot_cap);
   a.part_q = (float*)(w + o);
@@ -591,10 +660,43 @@ va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const vo
                       va::bwd_block_k(), va::bwd_dkdv_block_q(), 1, causal);
   ps.p[1] = plan_args(a.plan_q, Q, cu_seqlens_q, cu_seqlens_k, total_q, total_k, batch,
                       va::bwd_block_q(), va::bwd_dq_block_n(bf16, head_dim), 0, causal);
+  ps.nplans = planned ? 0 : 2;
   hipError_t e = va::launch_bwd(a, ps, (int64_t)Q.unit_cap * num_heads_q,
                                 (int64_t)K.unit_cap * num_heads_kv, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return VA_OK;
+}
+
+extern "C" {
+
+va_status va_varlen_bwd(const void* dout, const void* q, const void* k, const void* v,
+                        const void* out, const float* lse, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                        float softmax_scale, int causal, const void* bias,
+                        const int64_t* bias_stride, void* dq, void* dk, void* dv, float* dbias,
+                        const int64_t* dbias_stride, const int64_t* qkv_row_stride, void* workspace,
+                        size_t workspace_bytes, int32_t batch, int32_t total_q, int32_t total_k,
+                        int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                        va_dtype dtype, va_dtype grad_dtype, va_stream stream) {
+  return varlen_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    softmax_scale, causal, bias, bias_stride, dq, dk, dv, dbias, dbias_stride, qkv_row_stride,
+                    workspace, workspace_bytes, batch, total_q, total_k, num_heads_q, num_heads_kv, head_dim,
+                    dtype, grad_dtype, stream, false);
+}
+
+va_status va_varlen_bwd_planned(const void* dout, const void* q, const void* k, const void* v,
+                                const void* out, const float* lse, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                float softmax_scale, int causal, const void* bias,
+                                const int64_t* bias_stride, void* dq, void* dk, void* dv, float* dbias,
+                                const int64_t* dbias_stride, const int64_t* qkv_row_stride, void* workspace,
+                                size_t workspace_bytes, int32_t batch, int32_t total_q, int32_t total_k,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                va_dtype dtype, va_dtype grad_dtype, va_stream stream) {
+  return varlen_bwd(dout, q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    softmax_scale, causal, bias, bias_stride, dq, dk, dv, dbias, dbias_stride, qkv_row_stride,
+                    workspace, workspace_bytes, batch, total_q, total_k, num_heads_q, num_heads_kv, head_dim,
+                    dtype, grad_dtype, stream, true);
 }
 
 // ---------------------------------------------------------------------------

@@ -162,7 +162,8 @@ __device__ __forceinline__ void pack8(const float* v, u32x4_t& hi, u32x4_t* lo) 
 
 // ---------------------------------------------------------------- preprocess
 // One launch: workgroups 0 and 1 build the dK/dV and dQ work plans while the
-// others compute D = rowsum(dO * O) for every (query row, head).
+// others compute D = rowsum(dO * O) for every (query row, head); with plans
+// the forward already built (va_varlen_bwd_planned), every workgroup computes D.
 // Threads per (token, head) row of the D pass: one per 16-byte piece, padded
 // to a power of two so the row's sum is a butterfly inside an aligned group.
 template <int H16, int D>
@@ -176,7 +177,8 @@ constexpr int dsum_tpr() {
 template <int H16, int D>
 __global__ __launch_bounds__(plan::PT) void plan_dsum_kernel(BwdArgs a, PlanSet ps) {
   __shared__ plan::PlanShared sh;
-  if (blockIdx.x < 2) {
+  const int np = ps.nplans;  // 2, or 0 when the forward built the plans
+  if ((int)blockIdx.x < np) {
     plan::plan_body(ps.p[blockIdx.x], sh);
     return;
   }
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(plan::PT) void plan_dsum_kernel(BwdArgs a, PlanSet 
   constexpr int TPR = dsum_tpr<H16, D>();  // threads per (token, head) row; the first D / EPV load
   static_assert(plan::PT % TPR == 0, "rows must not straddle workgroups");
   const int64_t rows = (int64_t)a.total_q * a.hq;
-  const int64_t row = ((int64_t)(blockIdx.x - 2) * plan::PT + threadIdx.x) / TPR;
+  const int64_t row = ((int64_t)((int)blockIdx.x - np) * plan::PT + threadIdx.x) / TPR;
   const int c = threadIdx.x % TPR;
   float s = 0.f;
   if (row < rows && c < D / EPV) {
@@ -1197,7 +1199,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, in
                         hipStream_t st) {
   {
     const int64_t threads = (int64_t)a.total_q * a.hq * dsum_tpr<H16, D>();
-    const int64_t grid = 2 + (threads + plan::PT - 1) / plan::PT;
+    const int64_t grid = ps.nplans + (threads + plan::PT - 1) / plan::PT;
     timing_before(st, "bwd_plan_dsum");
     hipLaunchKernelGGL((plan_dsum_kernel<H16, D>), dim3((unsigned)grid), dim3(plan::PT), 0, st, a, ps);
     timing_after(st);

@@ -11,13 +11,16 @@ namespace va {
 
 // The packed forward (va_varlen_fwd) with the bytes split tiles' partial
 // results may take from the workspace as an argument, and the workspace it
-// then needs (0 for arguments it would reject).
+// then needs (0 for arguments it would reject).  With bwd_workspace, the
+// planner launch also builds the backward's two work plans in it
+// (va_varlen_fwd_bwdplan).
 va_status varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                      const int32_t* cu_seqlens_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
                      float softmax_scale, int causal, const void* bias, const int64_t* bias_stride, void* out,
                      float* lse, const int64_t* qkv_row_stride, void* workspace, size_t workspace_bytes,
                      size_t part_budget, int32_t batch, int32_t total_q, int32_t total_k, int32_t num_heads_q,
-                     int32_t num_heads_kv, int32_t head_dim, va_dtype dtype, va_stream stream);
+                     int32_t num_heads_kv, int32_t head_dim, va_dtype dtype, va_stream stream,
+                     void* bwd_workspace = nullptr, size_t bwd_workspace_bytes = 0);
 size_t varlen_fwd_need(int32_t batch, int32_t total_q, int32_t total_k, int32_t max_seqlen_q,
                        int32_t max_seqlen_k, int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
                        va_dtype dtype, size_t part_budget);
@@ -61,7 +64,8 @@ struct PlanArgs {
 };
 
 struct PlanSet {
-  PlanArgs p[2];
+  PlanArgs p[3];
+  int32_t nplans;  // plan_dsum_kernel: its first nplans workgroups build p[0 .. nplans)
 };
 
 hipError_t launch_plan(const PlanSet& s, int nplans, hipStream_t st);
