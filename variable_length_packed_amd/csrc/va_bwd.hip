@@ -174,6 +174,13 @@ constexpr int dsum_tpr() {
   return p;
 }
 
+// D pass: the rows are cut into DSUM_WG equal contiguous ranges, one per
+// workgroup (one workgroup per CU: no CU gets a second round while others
+// idle); a group of TPR threads takes every GPW-th row of its range, DSUM_R
+// rows at a time with all their loads issued before the first sum.
+constexpr int DSUM_R = 4;
+constexpr int DSUM_WG = 256;
+
 template <int H16, int D>
 __global__ __launch_bounds__(plan::PT) void plan_dsum_kernel(BwdArgs a, PlanSet ps) {
   __shared__ plan::PlanShared sh;
@@ -183,35 +190,56 @@ __global__ __launch_bounds__(plan::PT) void plan_dsum_kernel(BwdArgs a, PlanSet 
     return;
   }
   using T = elem_t<H16>;
+  using V = std::conditional_t<H16 != 0, u32x4_t, f32x4_t>;  // float vectors are loaded as such
   constexpr int EPV = 16 / sizeof(T);
   constexpr int TPR = dsum_tpr<H16, D>();  // threads per (token, head) row; the first D / EPV load
+  constexpr int GPW = plan::PT / TPR;      // row groups per workgroup
   static_assert(plan::PT % TPR == 0, "rows must not straddle workgroups");
+  // rows are numbered head-major (r = h * total_q + t), so the groups of a wave
+  // take consecutive tokens of one head and their D stores are contiguous
   const int64_t rows = (int64_t)a.total_q * a.hq;
-  const int64_t row = ((int64_t)((int)blockIdx.x - np) * plan::PT + threadIdx.x) / TPR;
+  const int64_t nwg = (int64_t)gridDim.x - np, w = (int64_t)blockIdx.x - np;
+  const int64_t lo = rows * w / nwg, hi = rows * (w + 1) / nwg;
   const int c = threadIdx.x % TPR;
-  float s = 0.f;
-  if (row < rows && c < D / EPV) {
-    const T* o = (const T*)a.out + row * D + c * EPV;
-    const T* g = (const T*)a.dout + row * D + c * EPV;
-    if constexpr (H16) {
-      const u32x4_t x = *(const u32x4_t*)o, y = *(const u32x4_t*)g;
+  const bool small = rows < ((int64_t)1 << 31);  // uniform: 32-bit division where the count allows
+  for (int64_t r0 = lo + threadIdx.x / TPR; r0 < hi; r0 += (int64_t)GPW * DSUM_R) {
+    V x[DSUM_R], y[DSUM_R];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s = __builtin_fmaf(lo16<H16>(x[e]), lo16<H16>(y[e]), s);
-        s = __builtin_fmaf(hi16<H16>(x[e]), hi16<H16>(y[e]), s);
+    for (int j = 0; j < DSUM_R; ++j) {
+      const int64_t r = r0 + (int64_t)j * GPW;
+      if (r < hi && c < D / EPV) {
+        int64_t t, h;
+        if (small) {
+          t = (uint32_t)r % (uint32_t)a.total_q;
+          h = (uint32_t)r / (uint32_t)a.total_q;
+        } else {
+          t = r % a.total_q;
+          h = r / a.total_q;
+        }
+        const int64_t e = (t * a.hq + h) * D + c * EPV;
+        x[j] = *(const V*)((const T*)a.out + e);
+        y[j] = *(const V*)((const T*)a.dout + e);
       }
-    } else {
-      // float vectors are loaded as such (no bit casts of vector elements)
-      const f32x4_t x = *(const f32x4_t*)o, y = *(const f32x4_t*)g;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s = __builtin_fmaf(x[e], y[e], s);
     }
-  }
 #pragma unroll
-  for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  if (row < rows && c == 0) {
-    const int t = (int)(row / a.hq), h = (int)(row % a.hq);
-    a.dsum[(size_t)h * a.total_q + t] = s;
+    for (int j = 0; j < DSUM_R; ++j) {
+      const int64_t r = r0 + (int64_t)j * GPW;
+      float s = 0.f;
+      if (r < hi && c < D / EPV) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (H16) {
+            s = __builtin_fmaf(lo16<H16>(x[j][e]), lo16<H16>(y[j][e]), s);
+            s = __builtin_fmaf(hi16<H16>(x[j][e]), hi16<H16>(y[j][e]), s);
+          } else {
+            s = __builtin_fmaf(x[j][e], y[j][e], s);
+          }
+        }
+      }
+#pragma unroll
+      for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+      if (r < hi && c == 0) a.dsum[r] = s;  // D is [Hq][total_q]: element h * total_q + t = r
+    }
   }
 }
 
@@ -1198,8 +1226,9 @@ template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
 hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, int64_t k_items,
                         hipStream_t st) {
   {
-    const int64_t threads = (int64_t)a.total_q * a.hq * dsum_tpr<H16, D>();
-    const int64_t grid = ps.nplans + (threads + plan::PT - 1) / plan::PT;
+    // D workgroups: DSUM_WG, or fewer when there are fewer rows than row groups in that many
+    const int64_t rows = (int64_t)a.total_q * a.hq, gpw = plan::PT / dsum_tpr<H16, D>();
+    const int64_t grid = ps.nplans + std::min<int64_t>(DSUM_WG, (rows + gpw - 1) / gpw);
     timing_before(st, "bwd_plan_dsum");
     hipLaunchKernelGGL((plan_dsum_kernel<H16, D>), dim3((unsigned)grid), dim3(plan::PT), 0, st, a, ps);
     timing_after(st);
