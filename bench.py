@@ -270,7 +270,23 @@ def main() -> int:
                          w.max_q, w.max_k, w.scale, w.causal, x["bias"], bstr,
                          grad_dtype=torch.float32, dq=dq, dk=dk, dv=dv, workspace=ws, planned=True)
 
-    def timed(fn, k):
+    def settle(fn, ms=80.0):
+        """Runs fn untimed for about `ms` of GPU time.  After an idle gap (host work between
+        sections) the clocks drop, and they take about 40 ms of sustained work to come back,
+        so each section's figure is taken in the same settled state as the step's."""
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        for _ in range(min(5000, int(ms / max(a.elapsed_time(b), 1e-3)))):
+            fn()
+        torch.cuda.synchronize()
+
+    def timed(fn, k, settle_first=True):
+        if settle_first:
+            settle(fn)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
@@ -283,9 +299,38 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ms_step = timed(step, args.steps)
+    ms_step = timed(step, args.steps, settle_first=False)  # after exactly the W warmup steps
     flops_fwd, flops_bwd = count.fwd_flops(w), count.bwd_flops(w)
     value = (flops_fwd + flops_bwd) / (ms_step * 1e-3) / 1e12
+    # per-kernel HIP-event timing on the stream the kernels run on, right after the timed
+    # steps (the same clock state as they ran in)
+    va.va_timing_start(64 * args.steps + 64)
+    for _ in range(args.steps):
+        step()
+    kt = va.va_timing_stop()
+    kernels = {}
+    for name, (n, tot) in kt.items():
+        avg = tot / max(n, 1)
+        fl = algorithmic_flops(w, name)
+        kernels[name] = {"launches": n, "avg_ms": round(avg, 5),
+                         "tflops": round(fl / (avg * 1e-3) / 1e12, 2) if fl else None}
+    # the step's outputs (the last step above), for the parity check against the oracle
+    gpu_res = {"out": out.float().cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy(),
+               "dk": dk.cpu().numpy(), "dv": dv.cpu().numpy()}
+    timed_kernels = {k: v for k, v in kt.items() if algorithmic_flops(w, k) > 0}
+    dom = max(timed_kernels.items(), key=lambda kv: kv[1][1])[0] if timed_kernels else None
+    roof = None
+    if dom is not None:
+        n, tot = kt[dom]
+        avg_s = tot / n * 1e-3
+        fl = algorithmic_flops(w, dom)
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        ach = fl / avg_s / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "traffic": measured_traffic(dom, f"config{args.workload}"),
+                "algorithmic_flops_per_launch": fl, "avg_launch_ms": round(tot / n, 5)}
+
     ms_fwd = timed(fwd, args.steps)
     ms_bwd = timed(bwd, args.steps)
 
@@ -294,6 +339,7 @@ def main() -> int:
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    settle(step)
     for ea, eb in evs:
         scrub.fill_(1)
         ea.record()
@@ -342,34 +388,6 @@ def main() -> int:
                       "tflops": round((flops_fwd + flops_bwd) / (ms_sh * 1e-3) / 1e12, 3),
                       "bitwise_equal_to_step": bool(same)}
         del plain
-
-    # per-kernel HIP-event timing on the stream the kernels run on
-    va.va_timing_start(64 * args.steps + 64)
-    for _ in range(args.steps):
-        step()
-    kt = va.va_timing_stop()
-    kernels = {}
-    for name, (n, tot) in kt.items():
-        avg = tot / max(n, 1)
-        fl = algorithmic_flops(w, name)
-        kernels[name] = {"launches": n, "avg_ms": round(avg, 5),
-                         "tflops": round(fl / (avg * 1e-3) / 1e12, 2) if fl else None}
-    # the step's outputs (the last step above), for the parity check against the oracle
-    gpu_res = {"out": out.float().cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy(),
-               "dk": dk.cpu().numpy(), "dv": dv.cpu().numpy()}
-    timed_kernels = {k: v for k, v in kt.items() if algorithmic_flops(w, k) > 0}
-    dom = max(timed_kernels.items(), key=lambda kv: kv[1][1])[0] if timed_kernels else None
-    roof = None
-    if dom is not None:
-        n, tot = kt[dom]
-        avg_s = tot / n * 1e-3
-        fl = algorithmic_flops(w, dom)
-        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-        ach = fl / avg_s / 1e12
-        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                "traffic": measured_traffic(dom, f"config{args.workload}"),
-                "algorithmic_flops_per_launch": fl, "avg_launch_ms": round(tot / n, 5)}
 
     # the Qwen2.5-0.5B-shaped forward (20 sequences U[64, 1024]) as a second forward figure
     if "qwen" in secs:
