@@ -174,9 +174,9 @@ constexpr int dsum_tpr() {
   return p;
 }
 
-// D pass: the rows are cut into DSUM_WG equal contiguous ranges, one per
-// workgroup (one workgroup per CU: no CU gets a second round while others
-// idle); a group of TPR threads takes every GPW-th row of its range, DSUM_R
+// D pass: the rows are cut into equal contiguous ranges, one per workgroup,
+// and with the planners the launch holds DSUM_WG workgroups (one per CU: no
+// CU gets a second round while others idle); a group of TPR threads takes every GPW-th row of its range, DSUM_R
 // rows at a time with all their loads issued before the first sum.
 constexpr int DSUM_R = 4;
 constexpr int DSUM_WG = 256;
@@ -1226,9 +1226,10 @@ template <int H16, int D, bool CAUSAL, bool HAS_BIAS>
 hipError_t launch_bwd_t(const BwdArgs& a, const PlanSet& ps, int64_t q_items, int64_t k_items,
                         hipStream_t st) {
   {
-    // D workgroups: DSUM_WG, or fewer when there are fewer rows than row groups in that many
+    // D workgroups: DSUM_WG less the planners (the launch then fits one round of
+    // one workgroup per CU), or fewer when there are fewer rows than row groups
     const int64_t rows = (int64_t)a.total_q * a.hq, gpw = plan::PT / dsum_tpr<H16, D>();
-    const int64_t grid = ps.nplans + std::min<int64_t>(DSUM_WG, (rows + gpw - 1) / gpw);
+    const int64_t grid = ps.nplans + std::min<int64_t>(DSUM_WG - ps.nplans, (rows + gpw - 1) / gpw);
     timing_before(st, "bwd_plan_dsum");
     hipLaunchKernelGGL((plan_dsum_kernel<H16, D>), dim3((unsigned)grid), dim3(plan::PT), 0, st, a, ps);
     timing_after(st);

@@ -141,12 +141,6 @@ __device__ void for_each_tile(const PlanArgs& p, PlanShared& sh, F&& f) {
   }
 }
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
 __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
   static_assert(2 * PT == MAXB, "two sequences per thread");
   static_assert(2 * PT == NBIN, "two bins per thread");
@@ -200,13 +194,23 @@ __device__ __forceinline__ void plan_body(const PlanArgs& p, PlanShared& sh) {
       }
     });
     // a wave with a split tile (candidate 0 splits whatever a larger one does)
-    // sums each candidate with a butterfly of shuffles over all its lanes and
-    // adds it with one LDS atomic; the others skip the reduction
+    // sums every candidate with a butterfly of shuffles over all its lanes, the
+    // candidates' shuffles of one distance issued together so their round trips
+    // overlap, and lane 0 adds each sum with one LDS atomic; the other waves
+    // skip the reduction
     if (__builtin_amdgcn_ballot_w64(sl[0] > 0) != 0) {
 #pragma unroll
-      for (int j = 0; j < NCAND; ++j) {
-        const int v = wave_sum(sl[j]);
-        if ((threadIdx.x & 63) == 0 && v > 0) atomicAdd(&sh.cnt[j], v);
+      for (int o = 32; o > 0; o >>= 1) {
+        int t[NCAND];
+#pragma unroll
+        for (int j = 0; j < NCAND; ++j) t[j] = __shfl_xor(sl[j], o, 64);
+#pragma unroll
+        for (int j = 0; j < NCAND; ++j) sl[j] += t[j];
+      }
+      if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int j = 0; j < NCAND; ++j)
+          if (sl[j] > 0) atomicAdd(&sh.cnt[j], sl[j]);
       }
     }
   }
