@@ -5,7 +5,8 @@ The plans are a pure function of cu_seqlens and the sizes, and each unit's resul
 neither on its place in the list nor on the workgroup that runs it, so the planned pair
 must give bitwise the outputs of va_varlen_fwd / va_varlen_bwd (which the parity tests
 compare with the oracle).  Cases: long sequences whose tiles split (merges), GQA, both
-head dims, float32 and float16, a bias with its gradient, and a forward that takes the
+head dims, float32 and float16, per-key and per-pair (permuted) biases with their gradients,
+and a forward that takes the
 short-query kernels; one buffer reused over calls, with an unrelated backward between a
 forward and its planned backward.
 """
@@ -33,6 +34,9 @@ CASES = [
                               d=64, causal=True, dtype="bf16", with_dout=True)),
     ("bias-per-key-bf16", dict(seed=76, lens_q=[1300, 17, 400], hq=4, hkv=4, d=64, causal=False,
                                dtype="bf16", bias="per_key", with_dout=True)),
+    ("bias-per-pair-permuted-bf16", dict(seed=77, lens_q=[700, 33, 260], hq=4, hkv=2, d=64, causal=True,
+                                         dtype="bf16", bias="per_pair", bias_layout="permuted",
+                                         with_dout=True)),
 ]
 
 
