@@ -6,9 +6,8 @@ neither on its place in the list nor on the workgroup that runs it, so the plann
 must give bitwise the outputs of va_varlen_fwd / va_varlen_bwd (which the parity tests
 compare with the oracle).  Cases: long sequences whose tiles split (merges), GQA, both
 head dims, float32 and float16, per-key and per-pair (permuted) biases with their gradients,
-and a forward that takes the
-short-query kernels; one buffer reused over calls, with an unrelated backward between a
-forward and its planned backward.
+and a forward that takes the short-query kernels; one buffer reused over calls, with an
+unrelated backward between a forward and its planned backward.
 """
 
 import pytest
